@@ -1,0 +1,178 @@
+"""ctypes front end of the CPU oracle (``libsla2_oracle.so``).
+
+TEST INFRASTRUCTURE ONLY: used by ``tests/``, ``__graft_entry__.smoke()`` and
+the CPU-baseline leg of ``bench.py``.  The GPU library and its Python binding
+never import this module.  Arrays are numpy: Q/K/V [B,H,N,d] as float32 or as
+uint16 bf16 bit patterns; Wq/Wk [w_heads,d,d] float32; alpha [H] float32.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "sla2_oracle.c")
+_LIB = os.path.join(_HERE, "libsla2_oracle.so")
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc (plain -O2, no fast-math)."""
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + ".tmp"
+        subprocess.check_call(["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-pthread",
+                               "-Wall", "-o", tmp, _SRC, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+class Problem(C.Structure):
+    _fields_ = [("B", C.c_int32), ("H", C.c_int32), ("N", C.c_int32), ("d", C.c_int32),
+                ("bq", C.c_int32), ("bkv", C.c_int32), ("topk_frac", C.c_float),
+                ("w_heads", C.c_int32), ("dtype", C.c_int32)]
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            build()
+        L = C.CDLL(_LIB)
+        P = C.POINTER(Problem)
+        vp, ip, dp = C.c_void_p, C.c_void_p, C.c_void_p
+        L.orc_topk.argtypes = [P]
+        L.orc_num_blocks.argtypes = [C.c_int, C.c_int]
+        L.orc_route.argtypes = [P, vp, vp, vp, vp, ip, C.c_int, ip, vp, dp, dp, C.c_int]
+        L.orc_forward.argtypes = [P, vp, vp, vp, ip, vp, ip, C.c_int, dp, C.c_int]
+        L.orc_forward_fp8.argtypes = [P, vp, vp, vp, ip, vp, ip, C.c_int, C.c_int, dp, C.c_int]
+        L.orc_quant_fp8.argtypes = [P, vp, vp, C.c_long, vp, vp, vp, vp, vp]
+        L.orc_e4m3_encode.argtypes = [C.c_float]
+        L.orc_e4m3_encode.restype = C.c_uint8
+        L.orc_e4m3_decode.argtypes = [C.c_uint8]
+        L.orc_e4m3_decode.restype = C.c_float
+        L.orc_bf16_encode.argtypes = [C.c_float]
+        L.orc_bf16_encode.restype = C.c_uint16
+        _lib = L
+    return _lib
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data
+
+
+def problem(B, H, N, d, bq, bkv, frac, w_heads=1, dtype="f32") -> Problem:
+    return Problem(B, H, N, d, bq, bkv, float(frac), w_heads, 0 if dtype == "f32" else 1)
+
+
+def problem_of(x) -> Problem:
+    """Problem for an ``inputs.Inputs`` bundle."""
+    w = x.wl
+    return problem(w.B, w.H, w.N, w.d, w.bq, w.bkv, w.topk_frac, x.wq.shape[0], w.dtype)
+
+
+def _arr(a, dtype):
+    return np.ascontiguousarray(a, dtype=dtype)
+
+
+def _qkv(p: Problem, a):
+    return _arr(a, np.float32 if p.dtype == 0 else np.uint16)
+
+
+def topk(p: Problem) -> int:
+    return lib().orc_topk(C.byref(p))
+
+
+def num_blocks(n: int, b: int) -> int:
+    return lib().orc_num_blocks(n, b)
+
+
+def route(p: Problem, q, k, wq, wk, heads=None, nthreads=0, want_scores=False):
+    """Router (pool -> project -> score -> top-k) for the listed heads.
+
+    Returns (idx [B,H,Tq,k] int32 ascending, mask [B,H,Tq,Tkv] uint8,
+    gap_rel [B,H,Tq] float64, scores or None).  Rows of unlisted heads are
+    left at -1 / 0 / nan."""
+    L = lib()
+    B, H, N = p.B, p.H, p.N
+    Tq, Tkv = num_blocks(N, p.bq), num_blocks(N, p.bkv)
+    kk = topk(p)
+    heads = np.arange(B * H, dtype=np.int32) if heads is None else np.asarray(heads, np.int32)
+    q, k = _qkv(p, q), _qkv(p, k)
+    wq, wk = _arr(wq, np.float32), _arr(wk, np.float32)
+    idx = np.full((B, H, Tq, kk), -1, np.int32)
+    mask = np.zeros((B, H, Tq, Tkv), np.uint8)
+    gap = np.full((B, H, Tq), np.nan)
+    sc = np.full((B, H, Tq, Tkv), np.nan) if want_scores else None
+    L.orc_route(C.byref(p), _ptr(q), _ptr(k), _ptr(wq), _ptr(wk), _ptr(heads), len(heads),
+                _ptr(idx), _ptr(mask), _ptr(gap), _ptr(sc), nthreads)
+    return idx, mask, gap, sc
+
+
+def forward(p: Problem, q, k, v, idx, alpha, blocks, nthreads=0, variant="exact",
+            quantize=True):
+    """Forward for the query blocks ``blocks`` (list of (bh, i)).
+
+    Returns out [n_blocks, bq, d] float64 (rows past N are 0)."""
+    L = lib()
+    blocks = np.ascontiguousarray(np.asarray(blocks, np.int32).reshape(-1, 2))
+    out = np.zeros((blocks.shape[0], p.bq, p.d))
+    q, k, v = _qkv(p, q), _qkv(p, k), _qkv(p, v)
+    idx = _arr(idx, np.int32)
+    alpha = _arr(alpha, np.float32)
+    if variant == "exact":
+        rc = L.orc_forward(C.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(idx), _ptr(alpha),
+                           _ptr(blocks), blocks.shape[0], _ptr(out), nthreads)
+    else:
+        rc = L.orc_forward_fp8(C.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(idx), _ptr(alpha),
+                               _ptr(blocks), blocks.shape[0], 1 if quantize else 0,
+                               _ptr(out), nthreads)
+    if rc != 0:
+        raise ValueError("oracle: bad block list")
+    return out
+
+
+def all_blocks(p: Problem):
+    Tq = num_blocks(p.N, p.bq)
+    return [(bh, i) for bh in range(p.B * p.H) for i in range(Tq)]
+
+
+def forward_full(p: Problem, q, k, v, idx, alpha, nthreads=0, variant="exact",
+                 quantize=True):
+    """Whole output [B,H,N,d] float64 (small problems only)."""
+    out = forward(p, q, k, v, idx, alpha, all_blocks(p), nthreads, variant, quantize)
+    Tq = num_blocks(p.N, p.bq)
+    o = out.reshape(p.B, p.H, Tq * p.bq, p.d)[:, :, : p.N]
+    return np.ascontiguousarray(o)
+
+
+def quant_fp8(p: Problem, q, k, bh):
+    """Low-bit inputs of one head: (qhat [N,d] u8, khat [N,d] u8, sq [Tq],
+    sk [Tkv], mu [d])."""
+    L = lib()
+    Tq, Tkv = num_blocks(p.N, p.bq), num_blocks(p.N, p.bkv)
+    qh = np.zeros((p.N, p.d), np.uint8)
+    kh = np.zeros((p.N, p.d), np.uint8)
+    sq = np.zeros(Tq, np.float32)
+    sk = np.zeros(Tkv, np.float32)
+    mu = np.zeros(p.d, np.float32)
+    q, k = _qkv(p, q), _qkv(p, k)
+    L.orc_quant_fp8(C.byref(p), _ptr(q), _ptr(k), bh, _ptr(qh), _ptr(kh), _ptr(sq),
+                    _ptr(sk), _ptr(mu))
+    return qh, kh, sq, sk, mu
+
+
+def e4m3_encode(x: float) -> int:
+    return int(lib().orc_e4m3_encode(float(x)))
+
+
+def e4m3_decode(c: int) -> float:
+    return float(lib().orc_e4m3_decode(int(c)))
+
+
+def bf16_encode(x: float) -> int:
+    return int(lib().orc_bf16_encode(float(x)))

@@ -1,0 +1,651 @@
+/*
+ * sla2_oracle.c -- plain, slow CPU reference of the SLA2 forward pass.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the bench's
+ * CPU-baseline leg may load this library.  The GPU library never links,
+ * includes or calls it, and it shares no source with the GPU path.
+ *
+ * All floating point is fp64 (inputs converted exactly from fp32 / bf16),
+ * except where a float decides an integer code in the low-bit variant: there
+ * the code is decided in fp32, the precision the GPU kernel uses (see
+ * orc_quant_fp8 and the P quantisation in orc_forward_fp8).
+ *
+ * Sources (the pages; section names as printed on them):
+ *  [SLA2-zh] "SLA2 深度解读" (jefxiong.cn): 04 (P = softmax(QK^T/sqrt d),
+ *            P1 = P.M, alpha = P1 1, O = alpha O_s + (1-alpha) O_l),
+ *            05 (pool, proj_q / proj_k, P_c, hard Top-k, b_q=128, b_kv=64),
+ *            07 (low-bit Q/K and P, K column-mean smoothing, online softmax
+ *            over mask-hit blocks only), 08 (what runs for hit / missed blocks).
+ *  [SLA-zh]  "SLA: Beyond Sparsity ..." notes (papernotes.org), key design 3
+ *            (H_i, Z_i, O_i^l = phi(Q_i) H_i / phi(Q_i) Z_i) and key design 4
+ *            (per-block h_j = phi(K_j)^T V_j and z_j, H_i += h_j).
+ *  [SLA2-en] gist.science explainer, section 2A (O = alpha O_s + (1-alpha) O_l,
+ *            both branches row-normalised).
+ *
+ * Readings where the pages are silent (each is listed in the design doc):
+ *  - router score is the plain product proj_q(Qbar) . proj_k(Kbar), no 1/sqrt(d)
+ *    and no softmax (both are monotone per row and cannot change a hard top-k);
+ *  - proj(x) = x W, no bias; W is [w_heads][d][d] row-major, w_heads in {1,H};
+ *  - k = clamp(ceil(frac * T_kv - 1e-6), 0, T_kv); ties broken by lower index;
+ *  - tokens beyond N in a ragged last block are excluded everywhere (means
+ *    divide by the valid count, no logit, no phi term);
+ *  - phi = elu + 1 elementwise on raw Q and K;
+ *  - empty selected set -> O_s = 0; empty unselected set -> O_l = 0;
+ *  - alpha is per head;
+ *  - low bit: OCP fp8 e4m3 (max 448), RNE, saturating; per-block absmax
+ *    scales (Q: b_q tokens, K: b_kv tokens); K smoothed by its mean over the N
+ *    valid tokens (sparse-branch QK^T only); P quantised as e4m3(256 P~)/256
+ *    with P~ = exp(l - running max) and the row sum taken over the quantised
+ *    values; V stays bf16; tiles visited in ascending KV-block order.
+ */
+#include <math.h>
+#include <pthread.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#include <unistd.h>
+
+typedef struct {
+    int32_t B, H, N, d;
+    int32_t bq, bkv;
+    float topk_frac;
+    int32_t w_heads;
+    int32_t dtype; /* 0: Q,K,V are float32; 1: Q,K,V are bf16 bit patterns */
+} orc_problem;
+
+/* ------------------------------------------------------------------ */
+/* small helpers                                                       */
+/* ------------------------------------------------------------------ */
+static int ceil_div(int a, int b) { return (a + b - 1) / b; }
+
+int orc_num_blocks(int n, int b) { return ceil_div(n, b); }
+
+/* step 5 reading: k = clamp(ceil(frac * T_kv - 1e-6), 0, T_kv) */
+int orc_topk(const orc_problem* p) {
+    int tkv = ceil_div(p->N, p->bkv);
+    double k = ceil((double)p->topk_frac * (double)tkv - 1e-6);
+    if (k < 0) k = 0;
+    if (k > tkv) k = tkv;
+    return (int)k;
+}
+
+static double bf16_to_double(uint16_t b) {
+    uint32_t u = (uint32_t)b << 16;
+    float f;
+    memcpy(&f, &u, 4);
+    return (double)f;
+}
+
+/* element (bh, t, c) of a [B*H][N][d] input */
+static double elem(const orc_problem* p, const void* X, long bh, long t, long c) {
+    size_t off = ((size_t)bh * p->N + t) * p->d + c;
+    if (p->dtype == 0) return (double)((const float*)X)[off];
+    return bf16_to_double(((const uint16_t*)X)[off]);
+}
+
+/* phi = elu + 1: x + 1 for x > 0, exp(x) otherwise */
+static double phi(double x) { return x > 0.0 ? x + 1.0 : exp(x); }
+
+/* ------------------------------------------------------------------ */
+/* OCP fp8 E4M3 (bias 7, no infinities, S.1111.111 = NaN, max 448)      */
+/* ------------------------------------------------------------------ */
+float orc_e4m3_decode(uint8_t c) {
+    int s = c >> 7, e = (c >> 3) & 15, m = c & 7;
+    float v;
+    if (e == 15 && m == 7) return NAN;
+    if (e == 0) v = ldexpf((float)m, -9);          /* subnormal: m/8 * 2^-6 */
+    else v = ldexpf((float)(8 + m), e - 10);       /* (1 + m/8) * 2^(e-7)   */
+    return s ? -v : v;
+}
+
+/* Round-to-nearest-even onto the e4m3 grid, saturating at +-448.
+ * Works on the exact value of the fp32 input: the grid spacing in the binade
+ * [2^e, 2^(e+1)) is 2^(e-3) for e >= -6, and 2^-9 below 2^-6. */
+uint8_t orc_e4m3_encode(float x) {
+    if (isnan(x)) return 0x7F;
+    uint8_t sign = signbit(x) ? 0x80 : 0x00;
+    double a = fabs((double)x);
+    if (a >= 448.0) return sign | 0x7E;
+    int e;
+    frexp(a, &e);             /* a = f * 2^e, f in [0.5,1) -> binade 2^(e-1) */
+    int be = e - 1;
+    if (be < -6) be = -6;     /* subnormal range shares the 2^-9 spacing */
+    double q = ldexp(1.0, be - 3);
+    double n = a / q;         /* exact: scaling by a power of two */
+    double r = floor(n);
+    double frac = n - r;
+    if (frac > 0.5 || (frac == 0.5 && fmod(r, 2.0) != 0.0)) r += 1.0;
+    double v = r * q;
+    if (v > 448.0) v = 448.0;
+    /* encode v exactly */
+    if (v == 0.0) return sign;
+    int ve;
+    double vf = frexp(v, &ve);           /* v = vf * 2^ve */
+    int E = ve - 1 + 7;                  /* biased exponent of 1.m form */
+    if (E <= 0) {                        /* subnormal: v = m * 2^-9 */
+        int m = (int)llround(v / ldexp(1.0, -9));
+        return sign | (uint8_t)m;
+    }
+    int m = (int)llround((vf * 2.0 - 1.0) * 8.0);
+    return sign | (uint8_t)((E << 3) | m);
+}
+
+/* fp32 -> bf16 bits, round to nearest even (finite inputs) */
+uint16_t orc_bf16_encode(float x) {
+    uint32_t u;
+    memcpy(&u, &x, 4);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+/* ------------------------------------------------------------------ */
+/* a tiny work pool                                                    */
+/* ------------------------------------------------------------------ */
+typedef void (*work_fn)(void* ctx, long item);
+typedef struct {
+    work_fn fn;
+    void* ctx;
+    long n;
+    long next;
+    pthread_mutex_t mu;
+} pool_t;
+
+static void* pool_worker(void* arg) {
+    pool_t* P = (pool_t*)arg;
+    for (;;) {
+        pthread_mutex_lock(&P->mu);
+        long it = P->next++;
+        pthread_mutex_unlock(&P->mu);
+        if (it >= P->n) break;
+        P->fn(P->ctx, it);
+    }
+    return NULL;
+}
+
+static int resolve_threads(int nthreads) {
+    if (nthreads > 0) return nthreads;
+    long n = sysconf(_SC_NPROCESSORS_ONLN);
+    return n > 0 ? (int)n : 1;
+}
+
+static void run_pool(work_fn fn, void* ctx, long n, int nthreads) {
+    pool_t P = {fn, ctx, n, 0, PTHREAD_MUTEX_INITIALIZER};
+    int nt = resolve_threads(nthreads);
+    if (nt > n) nt = (int)n;
+    if (nt <= 1) {
+        for (long i = 0; i < n; ++i) fn(ctx, i);
+        return;
+    }
+    pthread_t* th = (pthread_t*)malloc(sizeof(pthread_t) * nt);
+    for (int i = 0; i < nt; ++i) pthread_create(&th[i], NULL, pool_worker, &P);
+    for (int i = 0; i < nt; ++i) pthread_join(th[i], NULL);
+    free(th);
+}
+
+/* ------------------------------------------------------------------ */
+/* Router: pool -> project -> score -> hard top-k  ([SLA2-zh] 05)      */
+/* ------------------------------------------------------------------ */
+typedef struct {
+    double s;
+    int j;
+} scored_t;
+
+static int cmp_scored(const void* a, const void* b) {
+    const scored_t* x = (const scored_t*)a;
+    const scored_t* y = (const scored_t*)b;
+    if (x->s > y->s) return -1; /* larger score first */
+    if (x->s < y->s) return 1;
+    return x->j - y->j;         /* equal scores: lower index first */
+}
+
+typedef struct {
+    const orc_problem* p;
+    const void *Q, *K;
+    const float *Wq, *Wk;
+    const int32_t* heads;
+    int32_t* idx;
+    uint8_t* mask;
+    double* gap_rel;
+    double* scores; /* optional [B*H][Tq][Tkv] */
+} route_ctx;
+
+/* mean of the valid rows of block `blk` (size bs) of head bh, in fp64 */
+static void pool_block(const orc_problem* p, const void* X, long bh, int blk, int bs,
+                       double* out) {
+    int d = p->d;
+    int t0 = blk * bs;
+    int n = p->N - t0 < bs ? p->N - t0 : bs;
+    for (int c = 0; c < d; ++c) out[c] = 0.0;
+    for (int t = t0; t < t0 + n; ++t)
+        for (int c = 0; c < d; ++c) out[c] += elem(p, X, bh, t, c);
+    for (int c = 0; c < d; ++c) out[c] /= (double)n;
+}
+
+/* y = x W  with W [d][d] row-major (W[c][e]) */
+static void project(int d, const double* x, const float* W, double* y) {
+    for (int e = 0; e < d; ++e) y[e] = 0.0;
+    for (int c = 0; c < d; ++c)
+        for (int e = 0; e < d; ++e) y[e] += x[c] * (double)W[(size_t)c * d + e];
+}
+
+static void route_head(void* vctx, long item) {
+    route_ctx* C = (route_ctx*)vctx;
+    const orc_problem* p = C->p;
+    long bh = C->heads[item];
+    int h = (int)(bh % p->H);
+    int d = p->d;
+    int Tq = ceil_div(p->N, p->bq), Tkv = ceil_div(p->N, p->bkv);
+    int k = orc_topk(p);
+    const float* Wq = C->Wq + (p->w_heads == 1 ? 0 : (size_t)h * d * d);
+    const float* Wk = C->Wk + (p->w_heads == 1 ? 0 : (size_t)h * d * d);
+
+    double* bar = (double*)malloc(sizeof(double) * d);
+    double* qt = (double*)malloc(sizeof(double) * (size_t)Tq * d);
+    double* kt = (double*)malloc(sizeof(double) * (size_t)Tkv * d);
+    scored_t* row = (scored_t*)malloc(sizeof(scored_t) * Tkv);
+
+    /* step 2 (pool) and step 3 (project) */
+    for (int i = 0; i < Tq; ++i) {
+        pool_block(p, C->Q, bh, i, p->bq, bar);
+        project(d, bar, Wq, qt + (size_t)i * d);
+    }
+    for (int j = 0; j < Tkv; ++j) {
+        pool_block(p, C->K, bh, j, p->bkv, bar);
+        project(d, bar, Wk, kt + (size_t)j * d);
+    }
+    for (int i = 0; i < Tq; ++i) {
+        /* step 4: compressed score row P_c[i, :] */
+        double smax = 0.0;
+        for (int j = 0; j < Tkv; ++j) {
+            double s = 0.0;
+            for (int e = 0; e < d; ++e) s += qt[(size_t)i * d + e] * kt[(size_t)j * d + e];
+            row[j].s = s;
+            row[j].j = j;
+            if (fabs(s) > smax) smax = fabs(s);
+            if (C->scores) C->scores[((size_t)bh * Tq + i) * Tkv + j] = s;
+        }
+        /* step 5: hard top-k, ties to the lower index */
+        qsort(row, Tkv, sizeof(scored_t), cmp_scored);
+        uint8_t* mrow = C->mask ? C->mask + ((size_t)bh * Tq + i) * Tkv : NULL;
+        if (mrow) memset(mrow, 0, Tkv);
+        for (int r = 0; r < k; ++r)
+            if (mrow) mrow[row[r].j] = 1;
+        /* emit selected indices ascending */
+        if (C->idx) {
+            int32_t* irow = C->idx + ((size_t)bh * Tq + i) * k;
+            int w = 0;
+            /* a mask-ordered walk gives ascending order */
+            uint8_t* tmp = (uint8_t*)calloc(Tkv, 1);
+            for (int r = 0; r < k; ++r) tmp[row[r].j] = 1;
+            for (int j = 0; j < Tkv; ++j)
+                if (tmp[j]) irow[w++] = j;
+            free(tmp);
+        }
+        /* step 10: margin between the k-th and (k+1)-th scores */
+        if (C->gap_rel) {
+            double g = 1.0;
+            if (k > 0 && k < Tkv) {
+                double gap = row[k - 1].s - row[k].s;
+                g = smax > 0.0 ? gap / smax : 0.0;
+            }
+            C->gap_rel[(size_t)bh * Tq + i] = g;
+        }
+    }
+    free(bar);
+    free(qt);
+    free(kt);
+    free(row);
+}
+
+/* Route the listed heads (bh = b*H + h).  idx: [B*H][Tq][k] (ascending),
+ * mask: [B*H][Tq][Tkv] (0/1), gap_rel: [B*H][Tq], scores: optional.
+ * Returns k. */
+int orc_route(const orc_problem* p, const void* Q, const void* K, const float* Wq,
+              const float* Wk, const int32_t* heads, int n_heads, int32_t* idx,
+              uint8_t* mask, double* gap_rel, double* scores, int nthreads) {
+    route_ctx C = {p, Q, K, Wq, Wk, heads, idx, mask, gap_rel, scores};
+    run_pool(route_head, &C, n_heads, nthreads);
+    return orc_topk(p);
+}
+
+/* ------------------------------------------------------------------ */
+/* Per-KV-block linear summaries  ([SLA-zh] key design 4)              */
+/*   h_j = sum_{u in block j} phi(K_u)^T V_u   (d x d)                  */
+/*   z_j = sum_{u in block j} phi(K_u)          (d)                     */
+/* ------------------------------------------------------------------ */
+typedef struct {
+    const orc_problem* p;
+    const void *K, *V;
+    long bh;
+    double* h; /* [Tkv][d][d] */
+    double* z; /* [Tkv][d] */
+} summ_ctx;
+
+static void summary_block(void* vctx, long j) {
+    summ_ctx* S = (summ_ctx*)vctx;
+    const orc_problem* p = S->p;
+    int d = p->d;
+    double* h = S->h + (size_t)j * d * d;
+    double* z = S->z + (size_t)j * d;
+    double* pk = (double*)malloc(sizeof(double) * d);
+    double* vv = (double*)malloc(sizeof(double) * d);
+    memset(h, 0, sizeof(double) * d * d);
+    memset(z, 0, sizeof(double) * d);
+    int t0 = (int)j * p->bkv;
+    int n = p->N - t0 < p->bkv ? p->N - t0 : p->bkv;
+    for (int u = t0; u < t0 + n; ++u) {
+        for (int c = 0; c < d; ++c) pk[c] = phi(elem(p, S->K, S->bh, u, c));
+        for (int e = 0; e < d; ++e) vv[e] = elem(p, S->V, S->bh, u, e);
+        for (int c = 0; c < d; ++c) {
+            z[c] += pk[c];
+            for (int e = 0; e < d; ++e) h[(size_t)c * d + e] += pk[c] * vv[e];
+        }
+    }
+    free(pk);
+    free(vv);
+}
+
+/* ------------------------------------------------------------------ */
+/* low-bit inputs of one head (fp32 decisions, as the kernel takes them) */
+/* ------------------------------------------------------------------ */
+typedef struct {
+    uint8_t* qh; /* [N][d] e4m3 codes */
+    uint8_t* kh; /* [N][d] */
+    float* sq;   /* [Tq] */
+    float* sk;   /* [Tkv] */
+    float* mu;   /* [d] */
+} quant_t;
+
+static float elemf(const orc_problem* p, const void* X, long bh, long t, long c) {
+    return (float)elem(p, X, bh, t, c); /* exact: fp32 or bf16 inputs */
+}
+
+static void quant_head(const orc_problem* p, const void* Q, const void* K, long bh,
+                       quant_t* o) {
+    int d = p->d, N = p->N;
+    int Tq = ceil_div(N, p->bq), Tkv = ceil_div(N, p->bkv);
+    /* K channel mean over the N valid tokens (column-mean smoothing,
+       [SLA2-zh] 07): summed in fp64, rounded once to fp32 */
+    for (int c = 0; c < d; ++c) {
+        double s = 0.0;
+        for (int t = 0; t < N; ++t) s += elem(p, K, bh, t, c);
+        o->mu[c] = (float)(s / (double)N);
+    }
+    for (int j = 0; j < Tkv; ++j) {
+        int t0 = j * p->bkv, n = N - t0 < p->bkv ? N - t0 : p->bkv;
+        float amax = 0.0f;
+        for (int t = t0; t < t0 + n; ++t)
+            for (int c = 0; c < d; ++c) {
+                float ks = elemf(p, K, bh, t, c) - o->mu[c];
+                if (fabsf(ks) > amax) amax = fabsf(ks);
+            }
+        float s = amax > 0.0f ? amax / 448.0f : 1.0f;
+        o->sk[j] = s;
+        for (int t = t0; t < t0 + n; ++t)
+            for (int c = 0; c < d; ++c) {
+                float ks = elemf(p, K, bh, t, c) - o->mu[c];
+                o->kh[(size_t)t * d + c] = orc_e4m3_encode(ks / s);
+            }
+    }
+    for (int i = 0; i < Tq; ++i) {
+        int t0 = i * p->bq, n = N - t0 < p->bq ? N - t0 : p->bq;
+        float amax = 0.0f;
+        for (int t = t0; t < t0 + n; ++t)
+            for (int c = 0; c < d; ++c) {
+                float x = elemf(p, Q, bh, t, c);
+                if (fabsf(x) > amax) amax = fabsf(x);
+            }
+        float s = amax > 0.0f ? amax / 448.0f : 1.0f;
+        o->sq[i] = s;
+        for (int t = t0; t < t0 + n; ++t)
+            for (int c = 0; c < d; ++c)
+                o->qh[(size_t)t * d + c] = orc_e4m3_encode(elemf(p, Q, bh, t, c) / s);
+    }
+}
+
+/* Quantised inputs of head bh (step a4 of the low-bit variant). */
+void orc_quant_fp8(const orc_problem* p, const void* Q, const void* K, long bh,
+                   uint8_t* qhat, uint8_t* khat, float* sq, float* sk, float* mu) {
+    quant_t o = {qhat, khat, sq, sk, mu};
+    quant_head(p, Q, K, bh, &o);
+}
+
+/* ------------------------------------------------------------------ */
+/* Forward for a list of query blocks                                  */
+/* ------------------------------------------------------------------ */
+typedef struct {
+    const orc_problem* p;
+    const void *Q, *K, *V;
+    const int32_t* idx;
+    const float* alpha;
+    const int32_t* blocks; /* pairs (bh, i) */
+    double* out;           /* [n_blocks][bq][d] */
+    long bh;               /* head being processed */
+    const long* items;     /* block-list positions belonging to this head */
+    const double *h, *z;   /* this head's per-block summaries (or NULL) */
+    int variant;           /* 0: bf16/fp32 sparse branch, 1: low bit */
+    int quantize;          /* low bit: 1 = e4m3, 0 = identity quantiser */
+    const quant_t* qt;     /* this head's quantised inputs (low bit) */
+} fwd_ctx;
+
+/* Sparse branch, exact: O_s[t] = softmax(l) V over the selected tokens
+   ([SLA2-zh] 04 and 08), as a two-pass max-subtracted softmax. */
+static void sparse_exact(const fwd_ctx* F, int i, const int32_t* sel, int k, int t,
+                         double* os, double* lbuf) {
+    const orc_problem* p = F->p;
+    int d = p->d;
+    double inv = 1.0 / sqrt((double)d);
+    for (int e = 0; e < d; ++e) os[e] = 0.0;
+    if (k == 0) return;
+    long nu = 0;
+    double m = -INFINITY;
+    for (int r = 0; r < k; ++r) {
+        int t0 = sel[r] * p->bkv, n = p->N - t0 < p->bkv ? p->N - t0 : p->bkv;
+        for (int u = t0; u < t0 + n; ++u) {
+            double s = 0.0;
+            for (int c = 0; c < d; ++c) s += elem(p, F->Q, F->bh, t, c) * elem(p, F->K, F->bh, u, c);
+            s *= inv;
+            lbuf[nu++] = s;
+            if (s > m) m = s;
+        }
+    }
+    double l = 0.0;
+    nu = 0;
+    for (int r = 0; r < k; ++r) {
+        int t0 = sel[r] * p->bkv, n = p->N - t0 < p->bkv ? p->N - t0 : p->bkv;
+        for (int u = t0; u < t0 + n; ++u) {
+            double w = exp(lbuf[nu++] - m);
+            l += w;
+            for (int e = 0; e < d; ++e) os[e] += w * elem(p, F->V, F->bh, u, e);
+        }
+    }
+    for (int e = 0; e < d; ++e) os[e] /= l;
+    (void)i;
+}
+
+/* Sparse branch, low bit ([SLA2-zh] 07): quantised Q^K^T with per-block
+   scales, online softmax over the selected tiles in ascending order, P
+   quantised per tile against the running max, V unquantised. */
+static void sparse_lowbit(const fwd_ctx* F, int i, const int32_t* sel, int k, int t,
+                          double* os, double* lbuf) {
+    const orc_problem* p = F->p;
+    int d = p->d;
+    double inv = 1.0 / sqrt((double)d);
+    const quant_t* Qt = F->qt;
+    for (int e = 0; e < d; ++e) os[e] = 0.0;
+    if (k == 0) return;
+    double m = -INFINITY, l = 0.0;
+    for (int r = 0; r < k; ++r) {
+        int j = sel[r];
+        int t0 = j * p->bkv, n = p->N - t0 < p->bkv ? p->N - t0 : p->bkv;
+        double sc = (double)Qt->sq[i] * (double)Qt->sk[j] * inv;
+        double mt = -INFINITY;
+        for (int u = t0; u < t0 + n; ++u) {
+            double s = 0.0;
+            for (int c = 0; c < d; ++c) {
+                double a, b;
+                if (F->quantize) {
+                    a = orc_e4m3_decode(Qt->qh[(size_t)t * d + c]);
+                    b = orc_e4m3_decode(Qt->kh[(size_t)u * d + c]);
+                } else { /* identity quantiser: x / s exactly */
+                    a = elem(p, F->Q, F->bh, t, c) / (double)Qt->sq[i];
+                    b = (elem(p, F->K, F->bh, u, c) - (double)Qt->mu[c]) / (double)Qt->sk[j];
+                }
+                s += a * b;
+            }
+            s *= sc;
+            lbuf[u - t0] = s;
+            if (s > mt) mt = s;
+        }
+        double mn = mt > m ? mt : m;
+        double resc = (m == -INFINITY) ? 0.0 : exp(m - mn);
+        l *= resc;
+        for (int e = 0; e < d; ++e) os[e] *= resc;
+        for (int u = t0; u < t0 + n; ++u) {
+            double pt = exp(lbuf[u - t0] - mn);
+            double ph;
+            if (F->quantize) {
+                float f = (float)(256.0 * pt);
+                ph = (double)orc_e4m3_decode(orc_e4m3_encode(f)) / 256.0;
+            } else {
+                ph = pt;
+            }
+            l += ph;
+            for (int e = 0; e < d; ++e) os[e] += ph * elem(p, F->V, F->bh, u, e);
+        }
+        m = mn;
+    }
+    for (int e = 0; e < d; ++e) os[e] /= l;
+}
+
+static void forward_block(void* vctx, long it) {
+    const fwd_ctx* F = (const fwd_ctx*)vctx;
+    const orc_problem* p = F->p;
+    long pos = F->items[it];
+    int i = F->blocks[2 * pos + 1];
+    int d = p->d, Tq = ceil_div(p->N, p->bq), Tkv = ceil_div(p->N, p->bkv);
+    int k = orc_topk(p);
+    int h = (int)(F->bh % p->H);
+    double a = (double)F->alpha[h];
+    const int32_t* sel = F->idx + ((size_t)F->bh * Tq + i) * k;
+    double* out = F->out + (size_t)pos * p->bq * d;
+    memset(out, 0, sizeof(double) * (size_t)p->bq * d);
+
+    /* unselected set, H_i and Z_i ([SLA-zh] key design 3) */
+    uint8_t* hit = (uint8_t*)calloc(Tkv, 1);
+    for (int r = 0; r < k; ++r) hit[sel[r]] = 1;
+    int n_unsel = Tkv - k;
+    double* Hi = (double*)calloc((size_t)d * d, sizeof(double));
+    double* Zi = (double*)calloc(d, sizeof(double));
+    if (n_unsel > 0) {
+        for (int j = 0; j < Tkv; ++j) {
+            if (hit[j]) continue;
+            const double* hj = F->h + (size_t)j * d * d;
+            const double* zj = F->z + (size_t)j * d;
+            for (size_t x = 0; x < (size_t)d * d; ++x) Hi[x] += hj[x];
+            for (int c = 0; c < d; ++c) Zi[c] += zj[c];
+        }
+    }
+    double* os = (double*)malloc(sizeof(double) * d);
+    double* pq = (double*)malloc(sizeof(double) * d);
+    double* lbuf = (double*)malloc(sizeof(double) * ((size_t)k * p->bkv + 1));
+    int t0 = i * p->bq, nq = p->N - t0 < p->bq ? p->N - t0 : p->bq;
+    for (int t = t0; t < t0 + nq; ++t) {
+        double* o = out + (size_t)(t - t0) * d;
+        /* step 6: sparse branch */
+        if (F->variant == 0) sparse_exact(F, i, sel, k, t, os, lbuf);
+        else sparse_lowbit(F, i, sel, k, t, os, lbuf);
+        /* step 7: linear branch O_l = phi(q) H_i / (phi(q) . Z_i) */
+        for (int c = 0; c < d; ++c) pq[c] = phi(elem(p, F->Q, F->bh, t, c));
+        if (n_unsel > 0) {
+            double den = 0.0;
+            for (int c = 0; c < d; ++c) den += pq[c] * Zi[c];
+            for (int e = 0; e < d; ++e) {
+                double num = 0.0;
+                for (int c = 0; c < d; ++c) num += pq[c] * Hi[(size_t)c * d + e];
+                /* step 8: combine */
+                o[e] = a * os[e] + (1.0 - a) * (num / den);
+            }
+        } else {
+            for (int e = 0; e < d; ++e) o[e] = a * os[e];
+        }
+    }
+    free(hit);
+    free(Hi);
+    free(Zi);
+    free(os);
+    free(pq);
+    free(lbuf);
+}
+
+static int forward_common(const orc_problem* p, const void* Q, const void* K, const void* V,
+                          const int32_t* idx, const float* alpha, const int32_t* blocks,
+                          int n_blocks, double* out, int nthreads, int variant,
+                          int quantize) {
+    int d = p->d, Tq = ceil_div(p->N, p->bq), Tkv = ceil_div(p->N, p->bkv);
+    int k = orc_topk(p);
+    long nbh = (long)p->B * p->H;
+    /* process heads one at a time: the per-block summaries of a head are
+       large (T_kv * d * d doubles) */
+    long* items = (long*)malloc(sizeof(long) * (n_blocks > 0 ? n_blocks : 1));
+    for (long bh = 0; bh < nbh; ++bh) {
+        long n_it = 0;
+        for (long b = 0; b < n_blocks; ++b)
+            if (blocks[2 * b] == bh) {
+                if (blocks[2 * b + 1] < 0 || blocks[2 * b + 1] >= Tq) {
+                    free(items);
+                    return -1;
+                }
+                items[n_it++] = b;
+            }
+        if (n_it == 0) continue;
+        double *h = NULL, *z = NULL;
+        if (k < Tkv) {
+            h = (double*)malloc(sizeof(double) * (size_t)Tkv * d * d);
+            z = (double*)malloc(sizeof(double) * (size_t)Tkv * d);
+            summ_ctx S = {p, K, V, bh, h, z};
+            run_pool(summary_block, &S, Tkv, nthreads);
+        }
+        quant_t qt = {0};
+        if (variant == 1) {
+            qt.qh = (uint8_t*)malloc((size_t)p->N * d);
+            qt.kh = (uint8_t*)malloc((size_t)p->N * d);
+            qt.sq = (float*)malloc(sizeof(float) * Tq);
+            qt.sk = (float*)malloc(sizeof(float) * Tkv);
+            qt.mu = (float*)malloc(sizeof(float) * d);
+            quant_head(p, Q, K, bh, &qt);
+        }
+        fwd_ctx F = {p, Q, K, V, idx, alpha, blocks, out, bh, items, h, z,
+                     variant, quantize, &qt};
+        run_pool(forward_block, &F, n_it, nthreads);
+        free(h);
+        free(z);
+        if (variant == 1) {
+            free(qt.qh);
+            free(qt.kh);
+            free(qt.sq);
+            free(qt.sk);
+            free(qt.mu);
+        }
+    }
+    free(items);
+    return 0;
+}
+
+/* Forward (exact sparse branch) for the listed query blocks.
+ * blocks: n_blocks pairs (bh, i); out: [n_blocks][bq][d] fp64, rows past
+ * the valid tokens of a ragged block are 0.  idx: the router's
+ * [B*H][Tq][k] ascending selection.  Returns 0, or -1 on a bad block. */
+int orc_forward(const orc_problem* p, const void* Q, const void* K, const void* V,
+                const int32_t* idx, const float* alpha, const int32_t* blocks,
+                int n_blocks, double* out, int nthreads) {
+    return forward_common(p, Q, K, V, idx, alpha, blocks, n_blocks, out, nthreads, 0, 1);
+}
+
+/* Forward with the low-bit sparse branch (quantize=1: e4m3; 0: identity). */
+int orc_forward_fp8(const orc_problem* p, const void* Q, const void* K, const void* V,
+                    const int32_t* idx, const float* alpha, const int32_t* blocks,
+                    int n_blocks, int quantize, double* out, int nthreads) {
+    return forward_common(p, Q, K, V, idx, alpha, blocks, n_blocks, out, nthreads, 1,
+                          quantize);
+}

@@ -1,0 +1,93 @@
+"""The oracle's pins must catch plausible mistakes.
+
+Each case plants one mistake in a temporary copy of the oracle's C source
+(a dropped term, a wrong sign or index, a transposed operand, a wrong tie
+rule), builds it with gcc, and runs the pins of ``test_oracle_pins`` against
+it: at least one pin has to fail.  Runs on the CPU only.
+"""
+import importlib.util
+import os
+import subprocess
+
+import pytest
+
+from tests import test_oracle_pins as pins
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SRC = os.path.join(ROOT, "oracle", "sla2_oracle.c")
+
+MUTANTS = {
+    "combine_weight": ("(1.0 - a) * (num / den)", "a * (num / den)"),
+    "linear_over_selected": ("if (hit[j]) continue;", "if (!hit[j]) continue;"),
+    "phi_without_plus_one": ("x > 0.0 ? x + 1.0 : exp(x)", "x > 0.0 ? x : exp(x)"),
+    "no_softmax_scale": ("double inv = 1.0 / sqrt((double)d);\n    for (int e = 0; e < d; ++e) os[e] = 0.0;\n    if (k == 0) return;\n    long nu",
+                         "double inv = 1.0;\n    for (int e = 0; e < d; ++e) os[e] = 0.0;\n    if (k == 0) return;\n    long nu"),
+    "projection_transposed": ("(double)W[(size_t)c * d + e]", "(double)W[(size_t)e * d + c]"),
+    "pool_divides_by_block_size": ("out[c] /= (double)n;", "out[c] /= (double)bs;"),
+    "ties_to_higher_index": ("return x->j - y->j;", "return y->j - x->j;"),
+    "sparse_not_normalised": ("    for (int e = 0; e < d; ++e) os[e] /= l;\n    (void)i;", "    (void)i;"),
+    "k_rounds_down": ("ceil((double)p->topk_frac", "floor((double)p->topk_frac"),
+    "e4m3_ties_to_odd": ("fmod(r, 2.0) != 0.0", "fmod(r, 2.0) == 0.0"),
+    "lowbit_no_rescale": ("double resc = (m == -INFINITY) ? 0.0 : exp(m - mn);",
+                          "double resc = (m == -INFINITY) ? 0.0 : 1.0;"),
+    "no_k_smoothing": ("o->mu[c] = (float)(s / (double)N);", "o->mu[c] = 0.0f;"),
+    "denominator_without_phi_q": ("den += pq[c] * Zi[c];", "den += Zi[c];"),
+    "alpha_of_wrong_head": ("double a = (double)F->alpha[h];", "double a = (double)F->alpha[0];"),
+    "numerator_transposed_H": ("num += pq[c] * Hi[(size_t)c * d + e];", "num += pq[c] * Hi[(size_t)e * d + c];"),
+}
+
+# pins to run against a mutant (function, args after the oracle module)
+PINS = [
+    (pins.test_e4m3_encode_vs_torch_rne, ()),
+    (pins.test_topk_count_table, ()),
+    (pins.test_router_planted_scores, (True,)),
+    (pins.test_router_projection_orientation, ("q",)),
+    (pins.test_router_ties_go_to_lower_index, ()),
+    (pins.test_all_blocks_alpha1_is_dense_attention, ("f32", 700, 64, 128)),
+    (pins.test_row_mass_identity, ()),
+    (pins.test_no_blocks_alpha0_is_linear_attention, ("f32", 700, 64)),
+    (pins.test_linear_branch_over_unselected_blocks, ()),
+    (pins.test_combine_is_alpha_mix_of_the_two_branches, ()),
+    (pins.test_lowbit_identity_quantiser_equals_exact, ("bf16",)),
+    (pins.test_lowbit_quantised_inputs, ()),
+    (pins.test_lowbit_error_is_small, ()),
+]
+
+
+def _load_mutant(tmp_path, name, find, repl):
+    src = open(SRC).read()
+    assert src.count(find) == 1, f"mutation anchor for {name} not unique"
+    mdir = tmp_path / name
+    mdir.mkdir()
+    c = mdir / "sla2_oracle.c"
+    c.write_text(src.replace(find, repl))
+    so = mdir / "libsla2_oracle.so"
+    subprocess.check_call(["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-pthread", "-w",
+                           "-o", str(so), str(c), "-lm"])
+    spec = importlib.util.spec_from_file_location(f"oracle_mut_{name}",
+                                                  os.path.join(ROOT, "oracle", "oracle.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    mod._LIB = str(so)
+    mod._lib = None
+    return mod
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_pins_catch_mutant(tmp_path, name):
+    find, repl = MUTANTS[name]
+    mod = _load_mutant(tmp_path, name, find, repl)
+    caught = []
+    for fn, args in PINS:
+        try:
+            fn(mod, *args)
+        except AssertionError:
+            caught.append(fn.__name__)
+    assert caught, f"no pin caught the planted mistake {name!r}"
+
+
+def test_unmutated_copy_passes(tmp_path):
+    mod = _load_mutant(tmp_path, "none", "int orc_num_blocks(int n, int b)",
+                       "int orc_num_blocks(int n, int b)")
+    for fn, args in PINS:
+        fn(mod, *args)

@@ -1,0 +1,439 @@
+"""Pins of the CPU oracle against what the pages and the mathematics fix.
+
+Every check here compares the oracle with something other than itself:
+library routines (torch SDPA, torch's fp8 / bf16 casts, torch elu), closed
+forms the pages state, planted inputs whose answer is known by construction,
+and invariants.  Sources are the SLA2 pages: "SLA2 深度解读" sections 04
+(decomposition, alpha = P1 1, combine), 05 (router), 07 (low bit); the SLA
+notes' key design 3 (linear branch) and 4 (block summaries).
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from sparse_linear_attention_amd import inputs as I
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# --------------------------------------------------------------------------
+# helpers: independent references (library routines, brute force)
+# --------------------------------------------------------------------------
+def as_f64(x, dtype):
+    if dtype == "bf16":
+        return I.bf16_bits_to_f32(x).astype(np.float64)
+    return np.asarray(x, np.float64)
+
+
+def dense_attention(q, k, v):
+    """softmax(q k^T / sqrt(d)) v via torch's SDPA on the CPU in float64."""
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a))
+    return torch.nn.functional.scaled_dot_product_attention(t(q), t(k), t(v)).numpy()
+
+
+def phi_torch(x):
+    return (torch.nn.functional.elu(torch.from_numpy(x)) + 1.0).numpy()
+
+
+def linear_quadratic(q, k, v, keep):
+    """Linear attention in its quadratic form: sum_u (phi(q).phi(k_u)) v_u /
+    sum_u phi(q).phi(k_u), over the tokens u with keep[t, u] true."""
+    a = phi_torch(q) @ phi_torch(k).T
+    a = a * keep
+    return (a @ v) / a.sum(axis=1, keepdims=True)
+
+
+def token_mask(mask_row_blocks, N, bq, bkv):
+    """Expand a [Tq, Tkv] block mask to [N, N] tokens."""
+    m = np.repeat(np.repeat(mask_row_blocks, bq, axis=0), bkv, axis=1)
+    return m[:N, :N].astype(bool)
+
+
+def small(dtype="f32", N=700, d=64, bq=128, bkv=64, H=2, frac=0.25, seed=3, alpha=None):
+    wl = I.Workload("t", 1, H, N, d, bq, bkv, frac, dtype, "centroids", seed=seed,
+                    alpha=alpha or ())
+    return I.make_inputs(wl)
+
+
+# --------------------------------------------------------------------------
+# codecs
+# --------------------------------------------------------------------------
+def test_e4m3_decode_all_codes_vs_torch(orc):
+    codes = torch.arange(256, dtype=torch.uint8)
+    ref = codes.view(torch.float8_e4m3fn).float().numpy()
+    mine = np.array([orc.e4m3_decode(c) for c in range(256)], np.float32)
+    nan = np.isnan(ref)
+    assert (np.isnan(mine) == nan).all()
+    assert nan.sum() == 2  # S.1111.111
+    assert np.array_equal(mine[~nan], ref[~nan])
+    assert mine[0x7E] == 448.0 and mine[0x01] == 2.0 ** -9
+
+
+def test_e4m3_encode_vs_torch_rne(orc):
+    rng = np.random.default_rng(0)
+    vals = np.concatenate([
+        rng.uniform(-448, 448, 4000), rng.normal(0, 1, 4000),
+        rng.normal(0, 1e-2, 2000), rng.uniform(-2 ** -6, 2 ** -6, 2000),
+    ]).astype(np.float32)
+    # every midpoint between neighbouring codes (ties to even) and the codes
+    pos = np.array(sorted({orc.e4m3_decode(c) for c in range(0x7F)}), np.float64)
+    mids = ((pos[1:] + pos[:-1]) / 2).astype(np.float32)
+    vals = np.concatenate([vals, pos.astype(np.float32), mids, -mids])
+    ref = torch.from_numpy(vals).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    mine = np.array([orc.e4m3_encode(v) for v in vals], np.uint8)
+    # torch maps -0 results to 0x80 as well; compare bit patterns directly
+    assert np.array_equal(mine, ref)
+
+
+def test_e4m3_encode_saturates(orc):
+    assert orc.e4m3_encode(448.0) == 0x7E
+    assert orc.e4m3_encode(460.0) == 0x7E
+    assert orc.e4m3_encode(1e6) == 0x7E
+    assert orc.e4m3_encode(-1e30) == 0xFE
+    assert orc.e4m3_encode(float("nan")) == 0x7F
+
+
+def test_bf16_encode_vs_torch(orc):
+    rng = np.random.default_rng(1)
+    v = np.concatenate([rng.normal(0, 3, 3000), rng.normal(0, 1e-3, 1000)]).astype(np.float32)
+    ref = torch.from_numpy(v).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    mine = np.array([orc.bf16_encode(x) for x in v], np.uint16)
+    assert np.array_equal(mine, ref)
+    assert np.array_equal(I.round_to_bf16_bits(v), ref)
+
+
+# --------------------------------------------------------------------------
+# router
+# --------------------------------------------------------------------------
+def test_topk_count_table(orc):
+    g = json.load(open(os.path.join(GOLD, "topk_counts.json")))
+    for c in g["cases"]:
+        N = c["tkv"] * 64
+        p = orc.problem(1, 1, N, 64, 64, 64, c["frac"])
+        assert orc.topk(p) == c["k"], c
+
+
+def _planted_router(orc, ragged):
+    """Q/K built so that the scores are known: K block j is c_j e_{b_j},
+    Q block i is sum_j a_ij e_{b_j} (W = I), so S_ij = a_ij c_j."""
+    rng = np.random.default_rng(7)
+    d, bq, bkv = 64, 64, 64
+    N = 8 * 64 - (50 if ragged else 0)
+    Tq, Tkv = -(-N // bq), -(-N // bkv)
+    b = rng.permutation(d)[:Tkv]
+    c = rng.uniform(0.5, 2.0, Tkv)
+    a = rng.normal(0, 1, (Tq, Tkv))
+    q = np.zeros((1, 1, N, d), np.float32)
+    k = np.zeros((1, 1, N, d), np.float32)
+    for j in range(Tkv):
+        rows = slice(j * bkv, min(N, (j + 1) * bkv))
+        n = rows.stop - rows.start
+        # a zero-mean perturbation so the block mean (not any single row) is c_j e_b
+        pert = rng.normal(0, 0.3, (n, d))
+        pert -= pert.mean(axis=0, keepdims=True)
+        k[0, 0, rows] = pert
+        k[0, 0, rows, b[j]] += c[j]
+    for i in range(Tq):
+        rows = slice(i * bq, min(N, (i + 1) * bq))
+        blk = np.zeros((rows.stop - rows.start, d), np.float32)
+        blk[:, b] = a[i]
+        q[0, 0, rows] = blk
+    eye = np.eye(d, dtype=np.float32)[None]
+    S = a * c[None, :]
+    return q, k, eye, S, N
+
+
+@pytest.mark.parametrize("ragged", [False, True])
+def test_router_planted_scores(orc, ragged):
+    q, k, eye, S, N = _planted_router(orc, ragged)
+    p = orc.problem(1, 1, N, 64, 64, 64, 3 / 8)
+    idx, mask, gap, sc = orc.route(p, q, k, eye, eye, want_scores=True)
+    kk = orc.topk(p)
+    assert np.allclose(sc[0, 0], S, rtol=1e-6, atol=1e-6)
+    for i in range(S.shape[0]):
+        want = np.sort(np.argsort(-S[i], kind="stable")[:kk])
+        assert np.array_equal(idx[0, 0, i], want)
+        assert mask[0, 0, i].sum() == kk and mask[0, 0, i][want].all()
+
+
+@pytest.mark.parametrize("which", ["q", "k"])
+def test_router_projection_orientation(orc, which):
+    """Qbar = e_a, Kbar = e_b; one projection is a random A, the other I.
+    proj(x) = x W gives S = A[a, b] (A on Q) or A[b, a] (A on K)."""
+    rng = np.random.default_rng(11)
+    d, Tq, Tkv = 32, 4, 8
+    N = Tkv * 64
+    A = rng.normal(0, 1, (d, d)).astype(np.float32)
+    a_ch = rng.permutation(d)[:Tq]
+    b_ch = rng.permutation(d)[:Tkv]
+    q = np.zeros((1, 1, N, d), np.float32)
+    k = np.zeros((1, 1, N, d), np.float32)
+    for i in range(Tq):
+        q[0, 0, i * 128:(i + 1) * 128, a_ch[i]] = 1.0
+    for j in range(Tkv):
+        k[0, 0, j * 64:(j + 1) * 64, b_ch[j]] = 1.0
+    eye = np.eye(d, dtype=np.float32)
+    wq, wk = (A, eye) if which == "q" else (eye, A)
+    p = orc.problem(1, 1, N, d, 128, 64, 0.25)
+    _, _, _, sc = orc.route(p, q, k, wq[None], wk[None], want_scores=True)
+    want = A[np.ix_(a_ch, b_ch)] if which == "q" else A[np.ix_(b_ch, a_ch)].T
+    assert np.allclose(sc[0, 0], want, rtol=1e-6, atol=1e-6)
+
+
+def test_router_per_head_projections(orc):
+    x = small(H=3)
+    rng = np.random.default_rng(5)
+    wq = rng.normal(0, 0.1, (3, 64, 64)).astype(np.float32)
+    wk = rng.normal(0, 0.1, (3, 64, 64)).astype(np.float32)
+    p = orc.problem(1, 3, x.wl.N, 64, 128, 64, 0.25, w_heads=3)
+    idx, _, _, sc = orc.route(p, x.q, x.k, wq, wk, want_scores=True)
+    for h in range(3):
+        p1 = orc.problem(1, 1, x.wl.N, 64, 128, 64, 0.25, w_heads=1)
+        i1, _, _, s1 = orc.route(p1, x.q[:, h:h + 1], x.k[:, h:h + 1], wq[h:h + 1],
+                                 wk[h:h + 1], want_scores=True)
+        assert np.array_equal(s1[0, 0], sc[0, h]) and np.array_equal(i1[0, 0], idx[0, h])
+
+
+def test_router_identity_projection_is_sla1_ranking(orc):
+    """With proj_q = proj_k = I the router reduces to SLA v1's pooled map
+    softmax(pool(Q) pool(K)^T / sqrt d) ('SLA2 深度解读' 05; SLA notes, key
+    design 2); its per-row ranking is computed here with torch.softmax."""
+    x = small(N=1024, d=64, bq=64, bkv=64, frac=0.25, seed=9)
+    d = 64
+    eye = np.eye(d, dtype=np.float32)[None]
+    p = orc.problem_of(x)
+    idx, _, _, _ = orc.route(p, x.q, x.k, eye, eye)
+    kk = orc.topk(p)
+    for h in range(2):
+        qb = torch.from_numpy(x.q[0, h].astype(np.float64)).reshape(16, 64, d).mean(1)
+        kb = torch.from_numpy(x.k[0, h].astype(np.float64)).reshape(16, 64, d).mean(1)
+        pc = torch.softmax(qb @ kb.T / math.sqrt(d), dim=-1).numpy()
+        for i in range(16):
+            order = sorted(range(16), key=lambda j: (-pc[i, j], j))
+            assert np.array_equal(idx[0, h, i], np.sort(order[:kk]))
+
+
+def test_router_invariants(orc):
+    x = small(N=1000, frac=0.3)
+    p = orc.problem_of(x)
+    idx, mask, gap, sc = orc.route(p, x.q, x.k, x.wq, x.wk, want_scores=True)
+    kk = orc.topk(p)
+    Tq, Tkv = x.wl.Tq, x.wl.Tkv
+    assert (mask.sum(-1) == kk).all()
+    assert (np.diff(idx, axis=-1) > 0).all()
+    rebuilt = np.zeros_like(mask)
+    np.put_along_axis(rebuilt, idx.astype(np.int64), 1, axis=-1)
+    assert np.array_equal(rebuilt, mask)
+    assert (gap > 1e-12).all()
+    # selection = the k largest scores of the row
+    for h in range(2):
+        for i in range(Tq):
+            thr = np.sort(sc[0, h, i])[::-1][kk - 1]
+            assert (sc[0, h, i][mask[0, h, i] == 1] >= thr).all()
+            assert (sc[0, h, i][mask[0, h, i] == 0] <= thr).all()
+
+
+def test_router_positive_rescale_of_a_query_block(orc):
+    x = small(N=1024, frac=0.25)
+    p = orc.problem_of(x)
+    idx0, _, _, _ = orc.route(p, x.q, x.k, x.wq, x.wk)
+    q2 = x.q.copy()
+    q2[:, :, 128:256] *= 3.0  # query block 1 (bq = 128)
+    idx1, _, _, _ = orc.route(p, q2, x.k, x.wq, x.wk)
+    assert np.array_equal(idx0, idx1)
+
+
+def test_router_kv_block_permutation(orc):
+    x = small(N=1024, frac=0.25, bq=128, bkv=64)
+    p = orc.problem_of(x)
+    perm = np.random.default_rng(2).permutation(16)
+    k2 = x.k.reshape(1, 2, 16, 64, 64)[:, :, perm].reshape(x.k.shape)
+    _, m0, _, _ = orc.route(p, x.q, x.k, x.wq, x.wk)
+    _, m1, _, _ = orc.route(p, x.q, k2, x.wq, x.wk)
+    assert np.array_equal(m1, m0[..., perm])
+
+
+def test_router_ties_go_to_lower_index(orc):
+    """K = K_base without noise makes KV blocks 2m and 2m+1 identical."""
+    wl = I.TINY.with_(k_noise=0.0, topk_frac=5 / 16)  # k = 5: odd, splits a pair
+    x = I.make_inputs(wl)
+    assert np.array_equal(x.k[0, 0, 0:64], x.k[0, 0, 64:128])
+    p = orc.problem_of(x)
+    idx, mask, gap, sc = orc.route(p, x.q, x.k, x.wq, x.wk, want_scores=True)
+    assert (sc[..., 0::2] == sc[..., 1::2]).all()
+    split = 0
+    for row in mask.reshape(-1, 16):
+        for m in range(8):
+            if row[2 * m] != row[2 * m + 1]:
+                split += 1
+                assert row[2 * m] == 1 and row[2 * m + 1] == 0
+    assert split == mask.reshape(-1, 16).shape[0]  # every row splits one pair
+    assert (gap == 0).all()
+
+
+# --------------------------------------------------------------------------
+# sparse branch
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("dtype,N,d,bq", [("f32", 700, 64, 128), ("bf16", 513, 128, 64),
+                                          ("f32", 64, 32, 64), ("f32", 1, 64, 64)])
+def test_all_blocks_alpha1_is_dense_attention(orc, dtype, N, d, bq):
+    """k = T_kv and alpha = 1: the sparse branch is full softmax attention
+    ('SLA2 深度解读' 04, P = softmax(QK^T/sqrt d))."""
+    x = small(dtype=dtype, N=N, d=d, bq=bq, frac=1.0, alpha=(1.0, 1.0))
+    p = orc.problem_of(x)
+    idx, _, _, _ = orc.route(p, x.q, x.k, x.wq, x.wk)
+    o = orc.forward_full(p, x.q, x.k, x.v, idx, x.alpha)
+    for h in range(2):
+        ref = dense_attention(as_f64(x.q[0, h], dtype), as_f64(x.k[0, h], dtype),
+                              as_f64(x.v[0, h], dtype))
+        assert np.abs(o[0, h] - ref).max() < 1e-12
+
+
+def test_row_mass_identity(orc):
+    """alpha_t = (P.M) 1 from the dense P gives alpha_t O_s[t] = ((P.M) V)[t]
+    ('SLA2 深度解读' 04: P1 V = alpha (P_s V))."""
+    x = small(N=640, frac=0.3, alpha=(1.0, 1.0))
+    p = orc.problem_of(x)
+    idx, mask, _, _ = orc.route(p, x.q, x.k, x.wq, x.wk)
+    os_ = orc.forward_full(p, x.q, x.k, x.v, idx, x.alpha)  # alpha = 1 -> O = O_s
+    N, d = x.wl.N, x.wl.d
+    for h in range(2):
+        q, k, v = (a[0, h].astype(np.float64) for a in (x.q, x.k, x.v))
+        s = q @ k.T / math.sqrt(d)
+        P = torch.softmax(torch.from_numpy(s), -1).numpy()
+        M = token_mask(mask[0, h], N, x.wl.bq, x.wl.bkv)
+        P1 = P * M
+        a = P1.sum(1, keepdims=True)
+        assert np.abs(a * os_[0, h] - P1 @ v).max() < 1e-12
+
+
+def test_constant_v_gives_constant_output(orc):
+    x = small(N=600, frac=0.4)
+    v = np.full_like(x.v, 0.75)
+    p = orc.problem_of(x)
+    idx, _, _, _ = orc.route(p, x.q, x.k, x.wq, x.wk)
+    for alpha in ([1.0, 1.0], [0.0, 0.0], [0.3, 0.8]):
+        o = orc.forward_full(p, x.q, x.k, v, idx, np.array(alpha, np.float32))
+        assert np.abs(o - 0.75).max() < 1e-12
+
+
+# --------------------------------------------------------------------------
+# linear branch
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("dtype,N,d", [("f32", 700, 64), ("bf16", 300, 128)])
+def test_no_blocks_alpha0_is_linear_attention(orc, dtype, N, d):
+    """k = 0 and alpha = 0: pure linear attention with phi = elu + 1 (SLA
+    notes, key design 3), checked against its quadratic form."""
+    x = small(dtype=dtype, N=N, d=d, frac=0.0, alpha=(0.0, 0.0))
+    p = orc.problem_of(x)
+    assert orc.topk(p) == 0
+    idx, _, _, _ = orc.route(p, x.q, x.k, x.wq, x.wk)
+    o = orc.forward_full(p, x.q, x.k, x.v, idx, x.alpha)
+    for h in range(2):
+        q, k, v = (as_f64(a[0, h], dtype) for a in (x.q, x.k, x.v))
+        ref = linear_quadratic(q, k, v, np.ones((N, N)))
+        assert np.abs(o[0, h] - ref).max() < 1e-11
+
+
+def test_linear_branch_over_unselected_blocks(orc):
+    """alpha = 0 at an intermediate k: O = linear attention over the tokens of
+    the unselected blocks only (the blocks with M_c = 0)."""
+    x = small(N=700, frac=0.3, alpha=(0.0, 0.0))
+    p = orc.problem_of(x)
+    idx, mask, _, _ = orc.route(p, x.q, x.k, x.wq, x.wk)
+    o = orc.forward_full(p, x.q, x.k, x.v, idx, x.alpha)
+    for h in range(2):
+        q, k, v = (a[0, h].astype(np.float64) for a in (x.q, x.k, x.v))
+        keep = ~token_mask(mask[0, h], x.wl.N, x.wl.bq, x.wl.bkv)
+        ref = linear_quadratic(q, k, v, keep)
+        assert np.abs(o[0, h] - ref).max() < 1e-11
+
+
+def test_all_selected_linear_branch_is_zero(orc):
+    x = small(N=300, frac=1.0, alpha=(0.0, 0.0))
+    p = orc.problem_of(x)
+    idx, _, _, _ = orc.route(p, x.q, x.k, x.wq, x.wk)
+    o = orc.forward_full(p, x.q, x.k, x.v, idx, x.alpha)
+    assert np.abs(o).max() == 0.0
+
+
+# --------------------------------------------------------------------------
+# combine
+# --------------------------------------------------------------------------
+def test_combine_is_alpha_mix_of_the_two_branches(orc):
+    """O = alpha O_s + (1 - alpha) O_l with O_s = O(alpha=1), O_l = O(alpha=0)."""
+    x = small(N=700, frac=0.3)
+    p = orc.problem_of(x)
+    idx, _, _, _ = orc.route(p, x.q, x.k, x.wq, x.wk)
+    os_ = orc.forward_full(p, x.q, x.k, x.v, idx, np.ones(2, np.float32))
+    ol = orc.forward_full(p, x.q, x.k, x.v, idx, np.zeros(2, np.float32))
+    al = np.array([0.3, 0.85], np.float32)
+    o = orc.forward_full(p, x.q, x.k, x.v, idx, al)
+    a = al.astype(np.float64)[None, :, None, None]
+    assert np.abs(o - (a * os_ + (1 - a) * ol)).max() < 1e-13
+
+
+# --------------------------------------------------------------------------
+# low-bit variant
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_lowbit_identity_quantiser_equals_exact(orc, dtype):
+    """Smoothing K by its mean shifts every logit of a row by q.mu/sqrt d;
+    softmax is shift invariant, so with the quantiser replaced by the
+    identity the low-bit path must equal the exact one."""
+    x = small(dtype=dtype, N=700, d=64, frac=0.3)
+    p = orc.problem_of(x)
+    idx, _, _, _ = orc.route(p, x.q, x.k, x.wq, x.wk)
+    o = orc.forward_full(p, x.q, x.k, x.v, idx, x.alpha)
+    o8 = orc.forward_full(p, x.q, x.k, x.v, idx, x.alpha, variant="fp8", quantize=False)
+    assert np.abs(o - o8).max() < 1e-12
+
+
+def test_lowbit_quantised_inputs(orc):
+    x = small(dtype="bf16", N=700, d=64, frac=0.3)
+    p = orc.problem_of(x)
+    N, d = x.wl.N, x.wl.d
+    qh, kh, sq, sk, mu = orc.quant_fp8(p, x.q, x.k, 1)
+    q = I.bf16_bits_to_f32(x.q[0, 1]).astype(np.float64)
+    k = I.bf16_bits_to_f32(x.k[0, 1]).astype(np.float64)
+    assert np.allclose(mu, k.mean(0), rtol=0, atol=1e-6)
+    dec = torch.from_numpy(qh).view(torch.float8_e4m3fn).double().numpy()
+    deck = torch.from_numpy(kh).view(torch.float8_e4m3fn).double().numpy()
+    for i in range(x.wl.Tq):
+        r = slice(i * 128, min(N, (i + 1) * 128))
+        assert np.abs(dec[r]).max() == 448.0
+        # e4m3 keeps 4 significant bits: relative error <= 2^-4 (normals)
+        err = np.abs(dec[r] * sq[i] - q[r])
+        assert (err <= np.abs(q[r]) * 2 ** -4 + sq[i] * 2 ** -10 + 1e-12).all()
+    for j in range(x.wl.Tkv):
+        r = slice(j * 64, min(N, (j + 1) * 64))
+        ks = k[r] - mu.astype(np.float64)
+        assert np.abs(deck[r]).max() == 448.0
+        err = np.abs(deck[r] * sk[j] - ks)
+        assert (err <= np.abs(ks) * 2 ** -4 * 1.0001 + sk[j] * 2 ** -10 + 1e-9).all()
+
+
+def test_lowbit_error_is_small(orc):
+    """Reported, not a parity gate: the quantised path stays near the exact one."""
+    x = small(dtype="bf16", N=1024, d=128, frac=0.25)
+    p = orc.problem_of(x)
+    idx, _, _, _ = orc.route(p, x.q, x.k, x.wq, x.wk)
+    o = orc.forward_full(p, x.q, x.k, x.v, idx, x.alpha)
+    o8 = orc.forward_full(p, x.q, x.k, x.v, idx, x.alpha, variant="fp8")
+    assert np.abs(o - o8).max() < 0.1
+
+
+# --------------------------------------------------------------------------
+# workload generator sanity (shapes and statistics stated for the workloads)
+# --------------------------------------------------------------------------
+def test_tiny_workload_statistics():
+    x = I.make_inputs(I.TINY)
+    assert x.q.shape == (1, 2, 1024, 64) and x.q.dtype == np.float32
+    assert list(x.alpha) == [pytest.approx(0.7), pytest.approx(0.4)]
+    # Q - K within a token is the difference of two N(0, 0.3) noises
+    assert abs((x.q - x.k).std() - 0.3 * math.sqrt(2)) < 0.01
+    assert abs(x.wq.std() - 1 / math.sqrt(64)) < 0.01
