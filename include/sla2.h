@@ -1,0 +1,187 @@
+/*
+ * sla2.h -- C ABI of libsla2.so, the SLA2 sparse-linear attention forward
+ * pass for AMD MI355X (gfx950).
+ *
+ * What is computed (sources are the SLA2 pages; section names as printed):
+ *   router   Qbar = pool(Q), Kbar = pool(K) (block means), P_c =
+ *            proj_q(Qbar) proj_k(Kbar)^T, M_c = Top-k(k%, P_c) per row
+ *            ["SLA2 深度解读" 05, "Learnable Router 到底学什么"];
+ *   sparse   FlashAttention-style online softmax of Q K^T / sqrt(d) over the
+ *            selected KV blocks only, O_s row-normalised
+ *            ["SLA2 深度解读" 04 and 08];
+ *   linear   O_l = phi(Q_i) H_i / (phi(Q_i) Z_i) with H_i, Z_i summed over the
+ *            unselected blocks, phi = elu + 1
+ *            ["SLA: Beyond Sparsity ..." notes, key design 3 and 4];
+ *   combine  O = alpha O_s + (1 - alpha) O_l ["SLA2 深度解读" 04; gist.science
+ *            explainer, section 2A];
+ *   low bit  Q, K quantised to fp8 e4m3 with per-block scales, K smoothed by
+ *            its channel mean, P quantised before P V ["SLA2 深度解读" 07].
+ *
+ * Conventions (all entry points):
+ *  - Q, K, V, O, topk_idx, block_mask, alpha, Wq, Wk and ws are DEVICE
+ *    pointers owned by the caller.  The library never allocates, frees or
+ *    synchronises device memory; all work is enqueued on `stream` (a
+ *    hipStream_t; NULL = the default stream) in call order.
+ *  - Q, K, V, O are [B, H, N, d] contiguous, d innermost.  Q, K, V share one
+ *    dtype (problem.dtype); O is always fp32.
+ *  - Every argument is validated on the host before anything is launched; on
+ *    any error nothing is launched and no output is written.
+ *  - Returned codes: SLA2_OK; SLA2_EINVAL (null or misaligned pointer,
+ *    B/H/N <= 0, topk_frac outside [0,1] or NaN, w_heads not in {1,H});
+ *    SLA2_EUNSUPPORTED (a valid but unbuilt combination: d not in {64,128},
+ *    bq not in {64,128}, bkv != 64, phi other than elu+1, fp8 with fp32
+ *    inputs, more than 65535 heads or a number of blocks outside the limits
+ *    below); SLA2_EWORKSPACE (ws_bytes smaller than sla2_workspace_bytes);
+ *    SLA2_EHIP (a HIP launch error, reported right after the launch;
+ *    asynchronous faults surface at the caller's next synchronisation).
+ *  - Device-resident values are not inspected: Q, K, V must be finite, alpha
+ *    values should lie in [0,1], and for the bf16 paths |V| < 65504 (V is
+ *    carried in fp16 inside the kernels).
+ *  - Pointers must be 16-byte aligned (ws: 256-byte aligned).
+ *  - Calls on one stream are ordered; the library keeps no state between calls
+ *    (except the optional timing records below), so concurrent calls on
+ *    different streams with different workspaces are safe.
+ */
+#ifndef SLA2_H
+#define SLA2_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    SLA2_OK = 0,
+    SLA2_EINVAL = 1,
+    SLA2_EUNSUPPORTED = 2,
+    SLA2_EWORKSPACE = 3,
+    SLA2_EHIP = 4
+} sla2_status;
+
+typedef enum { SLA2_F32 = 0, SLA2_BF16 = 1 } sla2_dtype;
+
+/* feature map of the linear branch: elu(x) + 1, elementwise on raw Q and K */
+typedef enum { SLA2_PHI_ELU1 = 0 } sla2_phi;
+
+/* operations, for sla2_workspace_bytes */
+typedef enum { SLA2_OP_ROUTE = 0, SLA2_OP_FORWARD = 1, SLA2_OP_FORWARD_FP8 = 2 } sla2_op;
+
+typedef struct {
+    int32_t B, H, N, d;  /* batch, heads, tokens, head dim (64 or 128)       */
+    int32_t bq, bkv;     /* query / KV block sizes: bq in {64,128}, bkv = 64   */
+    float topk_frac;     /* k% as a fraction in [0,1]; see sla2_topk           */
+    int32_t w_heads;     /* 1: one Wq/Wk pair for all heads; H: one per head    */
+    int32_t phi;         /* sla2_phi                                            */
+    int32_t dtype;       /* sla2_dtype of Q, K, V                               */
+} sla2_problem;
+
+/* T_q = ceil(N / bq) and T_kv = ceil(N / bkv).  The last block of each kind
+ * may be ragged; tokens past N are excluded from every mean, logit and sum. */
+int32_t sla2_num_q_blocks(const sla2_problem* p);
+int32_t sla2_num_kv_blocks(const sla2_problem* p);
+
+/* Number of KV blocks kept per query block ("SLA2 深度解读" 05 gives k% only):
+ * k = clamp(ceil(topk_frac * T_kv - 1e-6), 0, T_kv).  Returns -1 if the
+ * problem is invalid. */
+int32_t sla2_topk(const sla2_problem* p);
+
+/* Bytes of device workspace an operation needs (0 if the problem is
+ * invalid).  Limits: T_kv <= 7680. */
+size_t sla2_workspace_bytes(const sla2_problem* p, int32_t op);
+
+/* Validate a problem for an operation without launching anything. */
+sla2_status sla2_check(const sla2_problem* p, int32_t op);
+
+const char* sla2_status_str(int32_t status);
+
+/*
+ * sla2_route -- the block router ("SLA2 深度解读" 05).
+ *   Qbar_i = mean of the valid rows of query block i, Kbar_j likewise;
+ *   qt_i = Qbar_i Wq[h'], kt_j = Kbar_j Wk[h'] (h' = 0 if w_heads == 1,
+ *   else h; W row-major [d][d], proj(x) = x W, no bias);
+ *   S_ij = qt_i . kt_j (plain product: a 1/sqrt(d) scale or a softmax would
+ *   not change a per-row top-k); the k largest S_ij of each row are
+ *   selected, ties going to the lower block index.  All router arithmetic is
+ *   fp64, so the selection does not depend on fp32 rounding.
+ * In : Q, K [B,H,N,d] (dtype); Wq, Wk [w_heads,d,d] fp32.
+ * Out: topk_idx [B,H,T_q,k] int32, each row ascending (may be NULL if k = 0);
+ *      block_mask [B,H,T_q,T_kv] uint8 0/1, or NULL if not wanted.
+ * ws : sla2_workspace_bytes(p, SLA2_OP_ROUTE) bytes.
+ */
+sla2_status sla2_route(const sla2_problem* p, const void* Q, const void* K,
+                       const float* Wq, const float* Wk, int32_t* topk_idx,
+                       uint8_t* block_mask, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * sla2_forward -- sparse branch + linear branch + combine.
+ *   O_s: softmax(Q_t K_u^T / sqrt(d)) V over the tokens u of the selected
+ *        blocks ("SLA2 深度解读" 04, 08); O_s = 0 when k = 0.
+ *   O_l: phi(Q_t) H_i / (phi(Q_t) . Z_i), H_i = sum over unselected blocks of
+ *        h_j = phi(K_j)^T V_j, Z_i = sum of z_j = colsum phi(K_j) (SLA notes,
+ *        key design 3 and 4); evaluated as (total - selected); O_l = 0 when
+ *        k = T_kv.
+ *   O   = alpha_h O_s + (1 - alpha_h) O_l, written for the N valid rows.
+ * In : Q, K, V [B,H,N,d]; topk_idx [B,H,T_q,k] from sla2_route (ascending,
+ *      values in [0,T_kv), not checked on the device); alpha [H] fp32.
+ * Out: O [B,H,N,d] fp32.
+ * ws : sla2_workspace_bytes(p, SLA2_OP_FORWARD) bytes.
+ * Precision: fp32 inputs are computed in fp32 throughout (vector ALU), and
+ * so are bf16 inputs with bq = 64.  bf16 inputs with bq = 128: Q K^T
+ * on bf16 matrix cores with fp32 accumulation, P rounded to fp16 for P V
+ * (V converted to fp16, exact for |V| < 65504 apart from fp16 subnormals),
+ * phi(K) and V in fp16 for the block summaries, fp32 everywhere else.
+ */
+sla2_status sla2_forward(const sla2_problem* p, const void* Q, const void* K,
+                         const void* V, const int32_t* topk_idx, const float* alpha,
+                         float* O, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * sla2_forward_fp8 -- as sla2_forward, with the low-bit sparse branch
+ * ("SLA2 深度解读" 07).  Requires dtype == SLA2_BF16 and bq == 128.
+ *   mu = mean of K over the N valid tokens (per head, per channel; summed in
+ *   fp64, rounded to fp32); K' = K - mu (fp32);
+ *   s_K(j) = max|K'| over KV block j / 448, s_Q(i) = max|Q| over query block
+ *   i / 448 (1 if the maximum is 0); Khat = e4m3(K' / s_K), Qhat = e4m3(Q /
+ *   s_Q) (OCP e4m3, round to nearest even, saturating at 448);
+ *   logits = (Qhat Khat^T) s_Q s_K / sqrt(d) on fp8 matrix cores;
+ *   online softmax over the selected blocks in ascending block order, with
+ *   P~ = exp(logit - running max) quantised as e4m3(256 P~) / 256 before
+ *   P V (V unquantised, fp16) and the row sum taken over the quantised
+ *   values.  Router and linear branch are those of sla2_forward.
+ * ws : sla2_workspace_bytes(p, SLA2_OP_FORWARD_FP8) bytes.
+ */
+sla2_status sla2_forward_fp8(const sla2_problem* p, const void* Q, const void* K,
+                             const void* V, const int32_t* topk_idx, const float* alpha,
+                             float* O, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * sla2_quantize_fp8 -- the low-bit inputs alone (the quantisation step that
+ * sla2_forward_fp8 runs first), for inspection.  Requires dtype == SLA2_BF16.
+ * Out (device): Qhat [B,H,T_q*bq,d] and Khat [B,H,T_kv*bkv,d] e4m3 codes
+ * (rows past N are 0), s_Q [B,H,T_q], s_K [B,H,T_kv], mu [B,H,d] fp32.
+ * ws : sla2_workspace_bytes(p, SLA2_OP_FORWARD_FP8) bytes.
+ */
+sla2_status sla2_quantize_fp8(const sla2_problem* p, const void* Q, const void* K,
+                              uint8_t* Qhat, uint8_t* Khat, float* sQ, float* sK,
+                              float* mu, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Kernel timing (diagnostics, host-side state).  sla2_timing_start(n) makes
+ * the library bracket each of its next n kernel launches with a pair of
+ * hipEvents on the launch stream (the events are created here, not device
+ * memory).  sla2_timing_stop() waits for those events and reports, per
+ * kernel kind, the summed duration in ms and the launch count, then stops
+ * recording.  Not thread-safe; meant for benchmarks.
+ */
+sla2_status sla2_timing_start(int32_t max_launches);
+sla2_status sla2_timing_stop(float* total_ms, int32_t* launches, int32_t n_kinds);
+int32_t sla2_kernel_kinds(void);
+const char* sla2_kernel_name(int32_t kind);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SLA2_H */

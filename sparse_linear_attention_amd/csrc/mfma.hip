@@ -1,0 +1,468 @@
+// bf16 forward path on the CDNA4 matrix cores.
+//
+// 1) summaries_mfma: one pass over K and V.  Per KV block j of 64 tokens it
+//    writes V_j^T and phi(K_j)^T in fp16, block-transposed ([d][64]) with the
+//    token order permuted inside each group of 16 (positions = token index
+//    with bits 2 and 3 swapped), the per-block z_j = colsum phi(K_j), and
+//    accumulates h = sum_j phi(K_j)^T V_j on the matrix cores into per-chunk
+//    partials (reduced in a fixed order afterwards).  Linear-branch block
+//    summaries: SLA notes, key design 4 (h_j = phi(K_j)^T V_j, z_j).
+// 2) fused_mfma: per (head, query block of 128) a work-group of 4 waves; wave
+//    w owns queries 32w..32w+31.  For every selected KV block (ascending):
+//      S^T = K_j Q^T            (bf16 MFMA 32x32x16, fp32 accumulate)
+//      online softmax on S^T    (each lane holds one query's column)
+//      O^T += V_j^T P^T         (fp16 MFMA; P rounded to fp16)
+//      G^T += V_j^T phi(K_j)    (fp16 MFMA; the selected part of h)
+//    Epilogue: H^T = h_tot^T - G^T, Z = z_tot - sum z_j, O_l^T = H^T phi(Q)^T
+//    (fp16 MFMA) / (phi(Q) . Z), O = alpha O_s + (1 - alpha) O_l.
+//    Sparse branch: "SLA2 深度解读" 04 and 08 (only mask-hit blocks run QK
+//    and PV); linear branch: SLA notes key design 3 (H_i, Z_i, O_l);
+//    combine: "SLA2 深度解读" 04.
+//
+// Operand layouts of v_mfma_f32_32x32x16_{bf16,f16}: A (32 x 16) lane l holds
+// row l%32 and k = 8*(l/32)+[0..7]; B (16 x 32) lane l holds column l%32 and
+// the same k; C (32 x 32) lane l holds column l%32 and rows
+// 8*(r/4) + 4*(l/32) + r%4, r = 0..15.  Only the C layout is relied on for
+// meaning (P^T is fed straight from the S^T accumulators); the k order inside
+// an instruction only has to agree between A and B, which holds because both
+// operands are loaded with the same position rule.
+#include "sla2_internal.h"
+
+namespace sla2 {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+__device__ inline f32x16 mfma_bf16(bf16x8 a, bf16x8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+__device__ inline f32x16 mfma_f16(f16x8 a, f16x8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+
+__device__ inline float bf16_lo(unsigned w) { return __uint_as_float(w << 16); }
+__device__ inline float bf16_hi(unsigned w) { return __uint_as_float(w & 0xffff0000u); }
+
+__device__ inline float phi_fast(float x) { return x > 0.0f ? x + 1.0f : __expf(x); }
+
+// token u of a 64-block -> its position in the transposed layouts
+__device__ inline int perm_pos(int u) {
+    return (u & ~12) | ((u >> 1) & 4) | ((u << 1) & 8);
+}
+
+__device__ inline f32x16 zero16() {
+    f32x16 z;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) z[i] = 0.0f;
+    return z;
+}
+
+// ---------------------------------------------------------------------------
+// block summaries
+// ---------------------------------------------------------------------------
+constexpr int kTPitch = 64 * 2 + 16;  // bytes per row of a [d][64] fp16 tile in LDS
+
+template <int D>
+__global__ __launch_bounds__(256) void summaries_mfma_kernel(
+    const uint16_t* __restrict__ K, const uint16_t* __restrict__ V, uint16_t* __restrict__ vt,
+    uint16_t* __restrict__ pkt, float* __restrict__ zb, float* __restrict__ hpart,
+    float* __restrict__ zpart, int N, int Tkv, int nch) {
+    constexpr int NT = D / 32;
+    constexpr int TPW = NT * NT / 4;  // h^T tiles per wave
+    __shared__ __attribute__((aligned(16))) char sV[D * kTPitch];
+    __shared__ __attribute__((aligned(16))) char sP[D * kTPitch];
+    // wave index as a scalar: conditions on it must be wave-uniform branches
+    // (matrix instructions ignore EXEC, so they may never sit under a lane mask)
+    const int t = threadIdx.x, lane = t & 63, l32 = lane & 31, hl = lane >> 5;
+    const int w = __builtin_amdgcn_readfirstlane(t >> 6);
+    const int chunk = blockIdx.x;
+    const long bh = blockIdx.y;
+    const int j0 = chunk * kSummBlocksPerChunk;
+    const int j1 = min(Tkv, j0 + kSummBlocksPerChunk);
+    const uint16_t* Kh = K + (size_t)bh * N * D;
+    const uint16_t* Vh = V + (size_t)bh * N * D;
+    const int nt_w = w % NT;       // this wave's n-tile (phi(K) channels)
+    const int mt_w0 = w / NT;      // first m-tile (V channels)
+    constexpr int MT_STEP = 4 / NT;
+
+    f32x16 acc[TPW];
+#pragma unroll
+    for (int s = 0; s < TPW; ++s) acc[s] = zero16();
+    float zacc = 0.0f;  // thread t < D: channel t
+
+    for (int j = j0; j < j1; ++j) {
+        __syncthreads();
+        // load 64 tokens x D channels; lane -> token, wave + pass -> channel group
+        constexpr int CG = D / 8;
+#pragma unroll
+        for (int pass = 0; pass < CG / 4; ++pass) {
+            const int cg = w + 4 * pass;
+            const int u = lane;
+            const int tok = j * 64 + u;
+            uint4 kv = make_uint4(0, 0, 0, 0), vv = make_uint4(0, 0, 0, 0);
+            const bool ok = tok < N;
+            if (ok) {
+                kv = *reinterpret_cast<const uint4*>(Kh + (size_t)tok * D + cg * 8);
+                vv = *reinterpret_cast<const uint4*>(Vh + (size_t)tok * D + cg * 8);
+            }
+            const unsigned kw[4] = {kv.x, kv.y, kv.z, kv.w};
+            const unsigned vw[4] = {vv.x, vv.y, vv.z, vv.w};
+            const int pos = perm_pos(u);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float kf = (e & 1) ? bf16_hi(kw[e >> 1]) : bf16_lo(kw[e >> 1]);
+                const float vf = (e & 1) ? bf16_hi(vw[e >> 1]) : bf16_lo(vw[e >> 1]);
+                const _Float16 ph = ok ? (_Float16)phi_fast(kf) : (_Float16)0.0f;
+                const _Float16 vh = ok ? (_Float16)vf : (_Float16)0.0f;
+                const int c = cg * 8 + e;
+                *reinterpret_cast<_Float16*>(sP + c * kTPitch + pos * 2) = ph;
+                *reinterpret_cast<_Float16*>(sV + c * kTPitch + pos * 2) = vh;
+            }
+        }
+        __syncthreads();
+        // write the transposed tiles (contiguous D*64 fp16 each) and z_j
+        uint16_t* gv = vt + ((size_t)bh * Tkv + j) * D * 64;
+        uint16_t* gp = pkt + ((size_t)bh * Tkv + j) * D * 64;
+        for (int x = t; x < D * 8; x += 256) {
+            const int row = x >> 3, c16 = x & 7;
+            *reinterpret_cast<uint4*>(gv + row * 64 + c16 * 8) =
+                *reinterpret_cast<const uint4*>(sV + row * kTPitch + c16 * 16);
+            *reinterpret_cast<uint4*>(gp + row * 64 + c16 * 8) =
+                *reinterpret_cast<const uint4*>(sP + row * kTPitch + c16 * 16);
+        }
+        if (t < D) {
+            float z = 0.0f;
+            const _Float16* rowp = reinterpret_cast<const _Float16*>(sP + t * kTPitch);
+            for (int p = 0; p < 64; ++p) z += (float)rowp[p];
+            zb[((size_t)bh * Tkv + j) * D + t] = z;
+            zacc += z;
+        }
+        // h^T (V channels x phi(K) channels) += V_j^T phi(K_j)
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            const f16x8 b = *reinterpret_cast<const f16x8*>(sP + (32 * nt_w + l32) * kTPitch +
+                                                            (16 * ks + 8 * hl) * 2);
+#pragma unroll
+            for (int s = 0; s < TPW; ++s) {
+                const int mt = mt_w0 + s * MT_STEP;
+                const f16x8 a = *reinterpret_cast<const f16x8*>(sV + (32 * mt + l32) * kTPitch +
+                                                                (16 * ks + 8 * hl) * 2);
+                acc[s] = mfma_f16(a, b, acc[s]);
+            }
+        }
+    }
+    // partial h[c][e]: c = phi(K) channel (C column), e = V channel (C row)
+    float* hp = hpart + ((size_t)bh * nch + chunk) * D * D;
+#pragma unroll
+    for (int s = 0; s < TPW; ++s) {
+        const int mt = mt_w0 + s * MT_STEP;
+        const int c = 32 * nt_w + l32;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int e = 32 * mt + 8 * (r >> 2) + 4 * hl + (r & 3);
+            hp[(size_t)c * D + e] = acc[s][r];
+        }
+    }
+    if (t < D) zpart[((size_t)bh * nch + chunk) * D + t] = zacc;
+}
+
+// ---------------------------------------------------------------------------
+// fused sparse + linear + combine
+// ---------------------------------------------------------------------------
+template <int D>
+struct FusedSmem {
+    static constexpr int kKPitch = D * 2 + 16;              // K tile row (bf16)
+    static constexpr int kK = 64 * kKPitch;                 // K tile
+    static constexpr int kT = D * kTPitch;                  // V^T or phi(K)^T tile
+    static constexpr int kHPitch = D * 2 + 16;              // H^T row (fp16)
+    static constexpr int kTiles = kK + 2 * kT;
+    static constexpr int kEpi = D * kHPitch + D * 4;        // H^T + Z
+    static constexpr int kBytes = kTiles > kEpi ? kTiles : kEpi;
+};
+
+// lazy-rescale threshold (log2 units): P~ stays <= 2^8 between rescales
+constexpr float kRescaleThr = 8.0f;
+
+template <int D>
+__global__ __launch_bounds__(256, 2) void fused_mfma_kernel(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+    const uint16_t* __restrict__ vt, const uint16_t* __restrict__ pkt,
+    const float* __restrict__ zb, const int32_t* __restrict__ idx,
+    const float* __restrict__ alpha, const float* __restrict__ htot,
+    const float* __restrict__ ztot, float* __restrict__ O, int N, int Tq, int Tkv, int k,
+    int H) {
+    using SM = FusedSmem<D>;
+    constexpr int NT = D / 32;       // 32-wide tiles along d
+    constexpr int KS = D / 16;       // k-steps of Q K^T
+    __shared__ __attribute__((aligned(16))) char smem[SM::kBytes];
+    char* sK = smem;
+    char* sV = smem + SM::kK;
+    char* sP = sV + SM::kT;
+
+    // wave index as a scalar: conditions on it must be wave-uniform branches
+    // (matrix instructions ignore EXEC, so they may never sit under a lane mask)
+    const int t = threadIdx.x, lane = t & 63, l32 = lane & 31, hl = lane >> 5;
+    const int w = __builtin_amdgcn_readfirstlane(t >> 6);
+    const long bh = blockIdx.y;
+    const int qb = blockIdx.x;
+    const int tq = qb * 128 + 32 * w + l32;  // this lane's query
+    const bool valid_q = tq < N;
+    const bool need_lin = k < Tkv;
+    // G^T tiles: wave w accumulates every m-tile (V channels) of n-tile
+    // w % NT (phi(K) channels); with D = 64 two waves share an n-tile.
+    const int nt_w = w % NT;
+    const float c_log2 = 1.4426950408889634f / sqrtf((float)D);
+
+    // Q^T fragments (B operand): lane holds Q[tq][16ks + 8hl .. +8]
+    bf16x8 qf[KS];
+    {
+        const uint16_t* qrow = Q + ((size_t)bh * N + (valid_q ? tq : 0)) * D;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            uint4 v = make_uint4(0, 0, 0, 0);
+            if (valid_q) v = *reinterpret_cast<const uint4*>(qrow + 16 * ks + 8 * hl);
+            qf[ks] = __builtin_bit_cast(bf16x8, v);
+        }
+    }
+
+    f32x16 o[NT], g[NT];
+#pragma unroll
+    for (int i = 0; i < NT; ++i) {
+        o[i] = zero16();
+        g[i] = zero16();
+    }
+    float m_ref = -INFINITY;  // log2-domain reference max of this query
+    float l_part = 0.0f;      // row sum over this lane's half of the tokens
+    float zsel0 = 0.0f, zsel1 = 0.0f;
+
+    const int32_t* sel = idx + ((size_t)bh * Tq + qb) * k;
+    const uint16_t* Kh = K + (size_t)bh * N * D;
+
+    for (int r = 0; r < k; ++r) {
+        const int j = sel[r];
+        __syncthreads();
+        // ---- stage K_j (bf16 rows), V_j^T and phi(K_j)^T (fp16) in LDS
+        constexpr int KCH = 64 * D / 8;  // 16-byte chunks of the K tile
+#pragma unroll
+        for (int x = t; x < KCH; x += 256) {
+            const int row = x / (D / 8), cg = x % (D / 8);
+            const int tok = j * 64 + row;
+            uint4 v = make_uint4(0, 0, 0, 0);
+            if (tok < N) v = *reinterpret_cast<const uint4*>(Kh + (size_t)tok * D + cg * 8);
+            *reinterpret_cast<uint4*>(sK + row * SM::kKPitch + cg * 16) = v;
+        }
+        const uint16_t* gv = vt + ((size_t)bh * Tkv + j) * D * 64;
+        const uint16_t* gp = pkt + ((size_t)bh * Tkv + j) * D * 64;
+#pragma unroll
+        for (int x = t; x < D * 8; x += 256) {
+            const int row = x >> 3, c16 = x & 7;
+            *reinterpret_cast<uint4*>(sV + row * kTPitch + c16 * 16) =
+                *reinterpret_cast<const uint4*>(gv + row * 64 + c16 * 8);
+            if (need_lin)
+                *reinterpret_cast<uint4*>(sP + row * kTPitch + c16 * 16) =
+                    *reinterpret_cast<const uint4*>(gp + row * 64 + c16 * 8);
+        }
+        if (need_lin && w == 0) {
+            const float* z = zb + ((size_t)bh * Tkv + j) * D;
+            if (D == 128) {
+                const float2 zz = *reinterpret_cast<const float2*>(z + 2 * lane);
+                zsel0 += zz.x;
+                zsel1 += zz.y;
+            } else {
+                zsel0 += z[lane];
+            }
+        }
+        __syncthreads();
+
+        // ---- S^T = K_j Q^T (two 32-row tiles of KV)
+        f32x16 s[2] = {zero16(), zero16()};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+            for (int mt = 0; mt < 2; ++mt) {
+                const bf16x8 a = *reinterpret_cast<const bf16x8*>(
+                    sK + (32 * mt + l32) * SM::kKPitch + (16 * ks + 8 * hl) * 2);
+                s[mt] = mfma_bf16(a, qf[ks], s[mt]);
+            }
+        }
+        // ragged last KV block: tokens >= N get no logit
+        if (j * 64 + 64 > N) {
+#pragma unroll
+            for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int kvi = 32 * mt + 8 * (i >> 2) + 4 * hl + (i & 3);
+                    if (j * 64 + kvi >= N) s[mt][i] = -INFINITY;
+                }
+        }
+        // ---- online softmax (log2 domain)
+        float mx = -INFINITY;
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[mt][i]);
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float xmax = mx * c_log2;
+        const bool need = xmax > m_ref + kRescaleThr;
+        if (__ballot(need)) {
+            const float nref = need ? xmax : m_ref;
+            const float f = __builtin_amdgcn_exp2f(m_ref - nref);
+            l_part *= f;
+#pragma unroll
+            for (int i = 0; i < NT; ++i)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) o[i][e] *= f;
+            m_ref = nref;
+        }
+        f16x8 pf[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float x = s[q >> 1][8 * (q & 1) + e];
+                pf[q][e] = (_Float16)__builtin_amdgcn_exp2f(fmaf(x, c_log2, -m_ref));
+            }
+        }
+        // row sum over the fp16-rounded values (what P V actually uses)
+        const f16x2 ones = {(_Float16)1.0f, (_Float16)1.0f};
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+            for (int e = 0; e < 8; e += 2) {
+                const f16x2 pr = {pf[q][e], pf[q][e + 1]};
+                l_part = __builtin_amdgcn_fdot2(pr, ones, l_part, false);
+            }
+        // ---- O^T += V^T P^T and G^T += V^T phi(K)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            f16x8 bk;
+            if (need_lin)
+                bk = *reinterpret_cast<const f16x8*>(sP + (32 * nt_w + l32) * kTPitch +
+                                                     (16 * q + 8 * hl) * 2);
+#pragma unroll
+            for (int mt = 0; mt < NT; ++mt) {
+                const f16x8 a = *reinterpret_cast<const f16x8*>(sV + (32 * mt + l32) * kTPitch +
+                                                                (16 * q + 8 * hl) * 2);
+                o[mt] = mfma_f16(a, pf[q], o[mt]);
+                if (need_lin) g[mt] = mfma_f16(a, bk, g[mt]);
+            }
+        }
+    }
+
+    // ---- epilogue
+    const float l_tot = l_part + __shfl_xor(l_part, 32);
+    const float inv_l = (k > 0) ? 1.0f / l_tot : 0.0f;
+    const float a_h = alpha[bh % H];
+    f32x16 ol[NT];
+#pragma unroll
+    for (int i = 0; i < NT; ++i) ol[i] = zero16();
+    float inv_den = 0.0f;
+    if (need_lin) {
+        __syncthreads();
+        char* sH = smem;                               // [D][kHPitch] fp16, H^T[e][c]
+        float* sZ = reinterpret_cast<float*>(smem + D * SM::kHPitch);
+        const float* hT = htot + (size_t)bh * D * D;   // h[c][e]
+        if (w < NT) {
+            const int c = 32 * nt_w + l32;
+#pragma unroll
+            for (int mt = 0; mt < NT; ++mt)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int e = 32 * mt + 8 * (i >> 2) + 4 * hl + (i & 3);
+                    const float hv = hT[(size_t)c * D + e] - g[mt][i];
+                    *reinterpret_cast<_Float16*>(sH + e * SM::kHPitch + c * 2) = (_Float16)hv;
+                }
+        }
+        if (w == 0) {
+            const float* zT = ztot + (size_t)bh * D;
+            if (D == 128) {
+                sZ[2 * lane] = zT[2 * lane] - zsel0;
+                sZ[2 * lane + 1] = zT[2 * lane + 1] - zsel1;
+            } else {
+                sZ[lane] = zT[lane] - zsel0;
+            }
+        }
+        __syncthreads();
+        // phi(Q)^T fragments and the denominator phi(q) . Z
+        f16x8 pq[KS];
+        float den = 0.0f;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float x = (float)qf[ks][e];
+                const float p = x > 0.0f ? x + 1.0f : __expf(x);
+                pq[ks][e] = (_Float16)p;
+                den = fmaf(p, sZ[16 * ks + 8 * hl + e], den);
+            }
+        }
+        den += __shfl_xor(den, 32);
+        inv_den = 1.0f / den;
+        // O_l^T = H^T phi(Q)^T
+#pragma unroll
+        for (int mt = 0; mt < NT; ++mt)
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                const f16x8 a = *reinterpret_cast<const f16x8*>(
+                    sH + (32 * mt + l32) * SM::kHPitch + (16 * ks + 8 * hl) * 2);
+                ol[mt] = mfma_f16(a, pq[ks], ol[mt]);
+            }
+    }
+    if (valid_q) {
+        float* orow = O + ((size_t)bh * N + tq) * D;
+#pragma unroll
+        for (int mt = 0; mt < NT; ++mt)
+#pragma unroll
+            for (int i4 = 0; i4 < 4; ++i4) {
+                const int e = 32 * mt + 8 * i4 + 4 * hl;
+                float4 v;
+                v.x = a_h * (o[mt][4 * i4 + 0] * inv_l) + (1.0f - a_h) * (ol[mt][4 * i4 + 0] * inv_den);
+                v.y = a_h * (o[mt][4 * i4 + 1] * inv_l) + (1.0f - a_h) * (ol[mt][4 * i4 + 1] * inv_den);
+                v.z = a_h * (o[mt][4 * i4 + 2] * inv_l) + (1.0f - a_h) * (ol[mt][4 * i4 + 2] * inv_den);
+                v.w = a_h * (o[mt][4 * i4 + 3] * inv_l) + (1.0f - a_h) * (ol[mt][4 * i4 + 3] * inv_den);
+                *reinterpret_cast<float4*>(orow + e) = v;
+            }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_summaries_mfma(const Dims& D, const void* K, const void* V,
+                                 const FwdWS& ws, hipStream_t s) {
+    const int nch = summ_chunks(D);
+    dim3 g(nch, (unsigned)D.BH);
+    timing_before(s, K_SUMM_MFMA);
+    if (D.d == 128)
+        summaries_mfma_kernel<128><<<g, 256, 0, s>>>((const uint16_t*)K, (const uint16_t*)V,
+                                                     ws.vt, ws.pkt, ws.zb, ws.hpart, ws.zpart,
+                                                     D.N, D.Tkv, nch);
+    else
+        summaries_mfma_kernel<64><<<g, 256, 0, s>>>((const uint16_t*)K, (const uint16_t*)V,
+                                                    ws.vt, ws.pkt, ws.zb, ws.hpart, ws.zpart,
+                                                    D.N, D.Tkv, nch);
+    timing_after(s, K_SUMM_MFMA);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    return launch_summaries_reduce(D, ws, s);
+}
+
+hipError_t launch_fused_mfma(const Dims& D, const void* Q, const void* K, const int32_t* idx,
+                             const float* alpha, float* O, const FwdWS& ws, hipStream_t s) {
+    dim3 g(D.Tq, (unsigned)D.BH);
+    timing_before(s, K_FUSED_MFMA);
+    if (D.d == 128)
+        fused_mfma_kernel<128><<<g, 256, 0, s>>>(
+            (const uint16_t*)Q, (const uint16_t*)K, ws.vt, ws.pkt, ws.zb, idx, alpha, ws.htot,
+            ws.ztot, O, D.N, D.Tq, D.Tkv, D.k, D.H);
+    else
+        fused_mfma_kernel<64><<<g, 256, 0, s>>>(
+            (const uint16_t*)Q, (const uint16_t*)K, ws.vt, ws.pkt, ws.zb, idx, alpha, ws.htot,
+            ws.ztot, O, D.N, D.Tq, D.Tkv, D.k, D.H);
+    timing_after(s, K_FUSED_MFMA);
+    return hipGetLastError();
+}
+
+}  // namespace sla2

@@ -1,0 +1,303 @@
+// Router kernels: block mean-pool + projection, compressed score, hard top-k
+// ("SLA2 深度解读" section 05: Qbar = pool(Q), Kbar = pool(K),
+// P_c = proj_q(Qbar) proj_k(Kbar)^T, M_c = Top-k(k%, P_c)).
+//
+// All arithmetic is fp64.  Block sums of <= 128 bf16 values are exact in
+// fp64, so the pooled means do not depend on summation order; the scores
+// are exact to fp64 rounding, which keeps the selection identical to any
+// other fp64 evaluation unless two scores of a row lie within ~1e-15
+// relative of each other at the k-th place.
+#include "sla2_internal.h"
+
+namespace sla2 {
+namespace {
+
+__device__ inline void load8(const float* __restrict__ p, float* o) {
+    const float4 a = *reinterpret_cast<const float4*>(p);
+    const float4 b = *reinterpret_cast<const float4*>(p + 4);
+    o[0] = a.x; o[1] = a.y; o[2] = a.z; o[3] = a.w;
+    o[4] = b.x; o[5] = b.y; o[6] = b.z; o[7] = b.w;
+}
+
+__device__ inline void load8(const uint16_t* __restrict__ p, float* o) {
+    const uint4 v = *reinterpret_cast<const uint4*>(p);
+    const unsigned w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        o[2 * i] = __uint_as_float(w[i] << 16);
+        o[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+}
+
+// One work-group per (head, block); blocks [0, Tq) are query blocks, the
+// rest KV blocks.  Output: proj(mean of the valid rows) in fp64.
+template <typename T>
+__global__ __launch_bounds__(256) void pool_project_kernel(
+    const T* __restrict__ Q, const T* __restrict__ K, const float* __restrict__ Wq,
+    const float* __restrict__ Wk, double* __restrict__ qt, double* __restrict__ kt, int N,
+    int d, int bq, int bkv, int Tq, int Tkv, int H, int w_heads) {
+    __shared__ double part[2048];  // [R][d], R * d == 2048
+    __shared__ double xbar[128];
+    const int blk = blockIdx.x;
+    const long bh = blockIdx.y;
+    const bool isq = blk < Tq;
+    const int j = isq ? blk : blk - Tq;
+    const int bs = isq ? bq : bkv;
+    const T* X = (isq ? Q : K) + (size_t)bh * N * d;
+    const int t0 = j * bs;
+    const int n = min(bs, N - t0);
+    const int groups = d >> 3;  // channel groups of 8
+    const int g = threadIdx.x % groups;
+    const int r = threadIdx.x / groups;
+    const int R = 256 / groups;
+
+    double s[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) s[e] = 0.0;
+    for (int row = r; row < n; row += R) {
+        float v[8];
+        load8(X + (size_t)(t0 + row) * d + g * 8, v);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) s[e] += (double)v[e];
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) part[r * d + g * 8 + e] = s[e];
+    __syncthreads();
+    if (threadIdx.x < d) {
+        const int c = threadIdx.x;
+        double acc = 0.0;
+        for (int rr = 0; rr < R; ++rr) acc += part[rr * d + c];
+        xbar[c] = acc / (double)n;
+    }
+    __syncthreads();
+    if (threadIdx.x < d) {
+        const int e = threadIdx.x;
+        const int h = (int)(bh % H);
+        const float* W = (isq ? Wq : Wk) + (w_heads == 1 ? 0 : (size_t)h * d * d);
+        double y = 0.0;
+        for (int c = 0; c < d; ++c) y = fma(xbar[c], (double)W[(size_t)c * d + e], y);
+        double* out = isq ? qt + ((size_t)bh * Tq + j) * d : kt + ((size_t)bh * Tkv + j) * d;
+        out[e] = y;
+    }
+}
+
+// S[bh][i][j] = qt[bh][i] . kt[bh][j]; 64x64 tile per work-group, 4x4 per thread.
+__global__ __launch_bounds__(256) void score_kernel(const double* __restrict__ qt,
+                                                    const double* __restrict__ kt,
+                                                    double* __restrict__ S, int Tq, int Tkv,
+                                                    int d) {
+    __shared__ double As[16][65];
+    __shared__ double Bs[16][65];
+    const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
+    const int i0 = blockIdx.y * 64, j0 = blockIdx.x * 64;
+    const long bh = blockIdx.z;
+    const double* A = qt + (size_t)bh * Tq * d;
+    const double* Bm = kt + (size_t)bh * Tkv * d;
+    double acc[4][4];
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int b = 0; b < 4; ++b) acc[a][b] = 0.0;
+    for (int k0 = 0; k0 < d; k0 += 16) {
+        for (int x = threadIdx.x; x < 1024; x += 256) {
+            const int row = x >> 4, kk = x & 15;
+            const int gi = i0 + row, gj = j0 + row;
+            As[kk][row] = gi < Tq ? A[(size_t)gi * d + k0 + kk] : 0.0;
+            Bs[kk][row] = gj < Tkv ? Bm[(size_t)gj * d + k0 + kk] : 0.0;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int kk = 0; kk < 16; ++kk) {
+            double a[4], b[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                a[q] = As[kk][ty + 16 * q];
+                b[q] = Bs[kk][tx + 16 * q];
+            }
+#pragma unroll
+            for (int p = 0; p < 4; ++p)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) acc[p][q] = fma(a[p], b[q], acc[p][q]);
+        }
+        __syncthreads();
+    }
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        const int i = i0 + ty + 16 * p;
+        if (i >= Tq) continue;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int j = j0 + tx + 16 * q;
+            if (j < Tkv) S[((size_t)bh * Tq + i) * Tkv + j] = acc[p][q];
+        }
+    }
+}
+
+// Order-preserving map of an fp64 score to an unsigned key (-0 -> +0 first).
+__device__ inline unsigned long long score_key(double v) {
+    if (v == 0.0) v = 0.0;
+    const unsigned long long u = (unsigned long long)__double_as_longlong(v);
+    return (u >> 63) ? ~u : (u | 0x8000000000000000ull);
+}
+
+// One work-group per score row: radix-select the k-th largest key, then keep
+// every larger key and the lowest-index keys equal to it; indices are emitted
+// ascending.  Deterministic (counts only, no order-dependent arithmetic).
+__global__ __launch_bounds__(256) void topk_kernel(const double* __restrict__ S, int Tq,
+                                                   int Tkv, int k, int32_t* __restrict__ idx,
+                                                   uint8_t* __restrict__ mask) {
+    extern __shared__ unsigned long long keys[];  // [Tkv]
+    __shared__ unsigned hist[256];
+    __shared__ unsigned long long s_prefix;
+    __shared__ int s_kr;
+    __shared__ int s_cnt[4];
+    const int t = threadIdx.x, lane = t & 63;
+    const int wid = __builtin_amdgcn_readfirstlane(t >> 6);
+    const size_t row = (size_t)blockIdx.y * Tq + blockIdx.x;
+    const double* srow = S + row * Tkv;
+    uint8_t* mrow = mask ? mask + row * Tkv : nullptr;
+    int32_t* irow = idx + row * k;
+
+    if (k == Tkv) {  // everything selected
+        for (int j = t; j < Tkv; j += 256) {
+            if (mrow) mrow[j] = 1;
+            irow[j] = j;
+        }
+        return;
+    }
+    for (int j = t; j < Tkv; j += 256) keys[j] = score_key(srow[j]);
+
+    unsigned long long prefix = 0, pmask = 0;
+    int kr = k;
+    for (int shift = 56; shift >= 0; shift -= 8) {
+        hist[t] = 0u;
+        __syncthreads();
+        for (int j = t; j < Tkv; j += 256) {
+            const unsigned long long key = keys[j];
+            if ((key & pmask) == prefix) atomicAdd(&hist[(unsigned)(key >> shift) & 255u], 1u);
+        }
+        __syncthreads();
+        if (wid == 0) {
+            unsigned c[4], tot = 0;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                c[q] = hist[255 - 4 * lane - q];
+                tot += c[q];
+            }
+            unsigned incl = tot;
+#pragma unroll
+            for (int off = 1; off < 64; off <<= 1) {
+                const unsigned o = __shfl_up(incl, off);
+                if (lane >= off) incl += o;
+            }
+            const unsigned excl = incl - tot;
+            if (excl < (unsigned)kr && (unsigned)kr <= incl) {
+                unsigned run = excl;
+                int digit = -1;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    if (digit < 0) {
+                        if (run + c[q] >= (unsigned)kr) {
+                            digit = 255 - 4 * lane - q;
+                            s_kr = kr - (int)run;
+                        } else {
+                            run += c[q];
+                        }
+                    }
+                }
+                s_prefix = prefix | ((unsigned long long)digit << shift);
+            }
+        }
+        __syncthreads();
+        prefix = s_prefix;
+        kr = s_kr;
+        pmask |= 255ull << shift;
+    }
+
+    const unsigned long long thr = prefix;
+    int eq_base = 0, out_base = 0;
+    for (int j0 = 0; j0 < Tkv; j0 += 256) {
+        const int j = j0 + t;
+        const unsigned long long key = j < Tkv ? keys[j] : 0ull;
+        const bool gt = j < Tkv && key > thr;
+        const bool eq = j < Tkv && key == thr;
+        const unsigned long long below = (1ull << lane) - 1ull;
+        const unsigned long long be = __ballot(eq);
+        const int eq_rank = __popcll(be & below);
+        __syncthreads();
+        if (lane == 0) s_cnt[wid] = __popcll(be);
+        __syncthreads();
+        int eq_before = eq_base, eq_total = 0;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            if (w < wid) eq_before += s_cnt[w];
+            eq_total += s_cnt[w];
+        }
+        const bool sel = gt || (eq && eq_before + eq_rank < kr);
+        const unsigned long long bs = __ballot(sel);
+        const int sel_rank = __popcll(bs & below);
+        __syncthreads();
+        if (lane == 0) s_cnt[wid] = __popcll(bs);
+        __syncthreads();
+        int sel_before = out_base, sel_total = 0;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            if (w < wid) sel_before += s_cnt[w];
+            sel_total += s_cnt[w];
+        }
+        if (j < Tkv) {
+            if (mrow) mrow[j] = sel ? 1 : 0;
+            if (sel) irow[sel_before + sel_rank] = j;
+        }
+        eq_base += eq_total;
+        out_base += sel_total;
+    }
+}
+
+__global__ void zero_mask_kernel(uint8_t* __restrict__ mask, size_t n) {
+    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+         i += (size_t)gridDim.x * blockDim.x)
+        mask[i] = 0;
+}
+
+}  // namespace
+
+hipError_t launch_route(const Dims& D, const void* Q, const void* K, const float* Wq,
+                        const float* Wk, int32_t* idx, uint8_t* mask, const RouteWS& ws,
+                        hipStream_t s) {
+    if (D.k == 0) {  // nothing is selected: only the mask (if wanted) is written
+        if (mask) {
+            const size_t n = (size_t)D.BH * D.Tq * D.Tkv;
+            timing_before(s, K_TOPK);
+            const size_t nb = (n + 255) / 256;
+            zero_mask_kernel<<<dim3((unsigned)(nb < 65535 ? nb : 65535)), 256, 0, s>>>(mask, n);
+            timing_after(s, K_TOPK);
+        }
+        return hipGetLastError();
+    }
+    dim3 g1(D.Tq + D.Tkv, (unsigned)D.BH);
+    timing_before(s, K_POOL_PROJECT);
+    if (D.dtype == SLA2_F32)
+        pool_project_kernel<float><<<g1, 256, 0, s>>>(
+            (const float*)Q, (const float*)K, Wq, Wk, ws.qt, ws.kt, D.N, D.d, D.bq, D.bkv, D.Tq,
+            D.Tkv, D.H, D.w_heads);
+    else
+        pool_project_kernel<uint16_t><<<g1, 256, 0, s>>>(
+            (const uint16_t*)Q, (const uint16_t*)K, Wq, Wk, ws.qt, ws.kt, D.N, D.d, D.bq, D.bkv,
+            D.Tq, D.Tkv, D.H, D.w_heads);
+    timing_after(s, K_POOL_PROJECT);
+
+    dim3 g2((D.Tkv + 63) / 64, (D.Tq + 63) / 64, (unsigned)D.BH);
+    timing_before(s, K_SCORE);
+    score_kernel<<<g2, 256, 0, s>>>(ws.qt, ws.kt, ws.S, D.Tq, D.Tkv, D.d);
+    timing_after(s, K_SCORE);
+
+    dim3 g3(D.Tq, (unsigned)D.BH);
+    timing_before(s, K_TOPK);
+    topk_kernel<<<g3, 256, sizeof(unsigned long long) * D.Tkv, s>>>(ws.S, D.Tq, D.Tkv, D.k,
+                                                                    idx, mask);
+    timing_after(s, K_TOPK);
+    return hipGetLastError();
+}
+
+}  // namespace sla2

@@ -1,0 +1,339 @@
+// Host side of libsla2: argument validation, block counts, workspace
+// layout, kernel sequencing and the optional kernel timing records.
+#include <math.h>
+#include <string.h>
+
+#include <vector>
+
+#include "sla2_internal.h"
+
+#define SLA2_API extern "C" __attribute__((visibility("default")))
+
+namespace sla2 {
+
+static constexpr int kMaxTkv = 7680;
+
+static bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+static int ceil_div(long a, long b) { return (int)((a + b - 1) / b); }
+
+// k = clamp(ceil(frac * T_kv - 1e-6), 0, T_kv)  (the pages give k% only)
+static int topk_of(float frac, int tkv) {
+    double k = ceil((double)frac * (double)tkv - 1e-6);
+    if (k < 0) k = 0;
+    if (k > tkv) k = tkv;
+    return (int)k;
+}
+
+static sla2_status make_dims(const sla2_problem* p, int op, Dims* D) {
+    if (!p) return SLA2_EINVAL;
+    if (p->B <= 0 || p->H <= 0 || p->N <= 0 || p->d <= 0 || p->bq <= 0 || p->bkv <= 0)
+        return SLA2_EINVAL;
+    if (!(p->topk_frac >= 0.0f && p->topk_frac <= 1.0f)) return SLA2_EINVAL;  // also NaN
+    if (p->w_heads != 1 && p->w_heads != p->H) return SLA2_EINVAL;
+    if (p->dtype != SLA2_F32 && p->dtype != SLA2_BF16) return SLA2_EINVAL;
+    if (op < SLA2_OP_ROUTE || op > SLA2_OP_FORWARD_FP8) return SLA2_EINVAL;
+    if (p->d != 64 && p->d != 128) return SLA2_EUNSUPPORTED;
+    if (p->bq != 64 && p->bq != 128) return SLA2_EUNSUPPORTED;
+    if (p->bkv != 64) return SLA2_EUNSUPPORTED;
+    if (p->phi != SLA2_PHI_ELU1) return SLA2_EUNSUPPORTED;
+    if (op == SLA2_OP_FORWARD_FP8 && (p->dtype != SLA2_BF16 || p->bq != 128))
+        return SLA2_EUNSUPPORTED;
+    long bh = (long)p->B * p->H;
+    if (bh > 65535) return SLA2_EUNSUPPORTED;
+    D->B = p->B;
+    D->H = p->H;
+    D->N = p->N;
+    D->d = p->d;
+    D->bq = p->bq;
+    D->bkv = p->bkv;
+    D->Tq = ceil_div(p->N, p->bq);
+    D->Tkv = ceil_div(p->N, p->bkv);
+    if (D->Tkv > kMaxTkv) return SLA2_EUNSUPPORTED;
+    D->k = topk_of(p->topk_frac, D->Tkv);
+    D->w_heads = p->w_heads;
+    D->dtype = p->dtype;
+    D->BH = bh;
+    return SLA2_OK;
+}
+
+// ---------------------------------------------------------------------------
+// workspace layout
+// ---------------------------------------------------------------------------
+template <typename T>
+static T* carve(char* base, size_t& off, size_t bytes) {
+    off = align256(off);
+    T* p = base ? reinterpret_cast<T*>(base + off) : nullptr;
+    off += bytes;
+    return p;
+}
+
+size_t layout_route(const Dims& D, char* base, RouteWS* ws) {
+    size_t off = 0;
+    RouteWS w;
+    w.qt = carve<double>(base, off, sizeof(double) * D.BH * D.Tq * D.d);
+    w.kt = carve<double>(base, off, sizeof(double) * D.BH * D.Tkv * D.d);
+    w.S = carve<double>(base, off, sizeof(double) * D.BH * D.Tq * D.Tkv);
+    if (ws) *ws = w;
+    return align256(off);
+}
+
+size_t layout_forward(const Dims& D, int op, char* base, FwdWS* ws) {
+    size_t off = 0;
+    FwdWS w;
+    memset(&w, 0, sizeof(w));
+    const size_t bh = (size_t)D.BH, d = D.d;
+    const int nch = summ_chunks(D);
+    if (D.dtype == SLA2_BF16) {
+        w.vt = carve<uint16_t>(base, off, 2 * bh * D.Tkv * d * 64);
+        w.pkt = carve<uint16_t>(base, off, 2 * bh * D.Tkv * d * 64);
+        w.zb = carve<float>(base, off, 4 * bh * D.Tkv * d);
+    }
+    w.hpart = carve<float>(base, off, 4 * bh * nch * d * d);
+    w.zpart = carve<float>(base, off, 4 * bh * nch * d);
+    w.htot = carve<float>(base, off, 4 * bh * d * d);
+    w.ztot = carve<float>(base, off, 4 * bh * d);
+    if (op == SLA2_OP_FORWARD_FP8) {
+        w.qhat = carve<uint8_t>(base, off, bh * (size_t)D.Tq * D.bq * d);
+        w.khat = carve<uint8_t>(base, off, bh * (size_t)D.Tkv * 64 * d);
+        w.sq = carve<float>(base, off, 4 * bh * D.Tq);
+        w.sk = carve<float>(base, off, 4 * bh * D.Tkv);
+        w.mu = carve<float>(base, off, 4 * bh * d);
+    }
+    if (ws) *ws = w;
+    return align256(off);
+}
+
+static size_t ws_bytes_of(const Dims& D, int op) {
+    if (op == SLA2_OP_ROUTE) return layout_route(D, nullptr, nullptr);
+    return layout_forward(D, op, nullptr, nullptr);
+}
+
+// ---------------------------------------------------------------------------
+// timing records
+// ---------------------------------------------------------------------------
+namespace {
+struct Rec {
+    hipEvent_t a, b;
+    int kind;
+};
+struct Timing {
+    bool on = false;
+    int max = 0;
+    int used = 0;
+    std::vector<Rec> recs;
+} g_timing;
+
+const char* kKindNames[K_NUM_KINDS] = {
+    "pool_project", "score",       "topk_select", "summaries_valu",
+    "summaries_reduce", "fused_valu", "summaries_mfma", "fused_mfma",
+    "quant_mean",   "quant_fp8",   "fused_fp8",
+};
+}  // namespace
+
+void timing_before(hipStream_t s, int kind) {
+    if (!g_timing.on || g_timing.used >= g_timing.max) return;
+    Rec& r = g_timing.recs[g_timing.used];
+    r.kind = kind;
+    (void)hipEventRecord(r.a, s);
+}
+
+void timing_after(hipStream_t s, int kind) {
+    (void)kind;
+    if (!g_timing.on || g_timing.used >= g_timing.max) return;
+    Rec& r = g_timing.recs[g_timing.used++];
+    (void)hipEventRecord(r.b, s);
+}
+
+}  // namespace sla2
+
+using namespace sla2;
+
+// ---------------------------------------------------------------------------
+// exported entry points
+// ---------------------------------------------------------------------------
+SLA2_API int32_t sla2_num_q_blocks(const sla2_problem* p) {
+    Dims D;
+    return make_dims(p, SLA2_OP_ROUTE, &D) == SLA2_OK ? D.Tq : -1;
+}
+
+SLA2_API int32_t sla2_num_kv_blocks(const sla2_problem* p) {
+    Dims D;
+    return make_dims(p, SLA2_OP_ROUTE, &D) == SLA2_OK ? D.Tkv : -1;
+}
+
+SLA2_API int32_t sla2_topk(const sla2_problem* p) {
+    Dims D;
+    return make_dims(p, SLA2_OP_ROUTE, &D) == SLA2_OK ? D.k : -1;
+}
+
+SLA2_API size_t sla2_workspace_bytes(const sla2_problem* p, int32_t op) {
+    Dims D;
+    if (make_dims(p, op, &D) != SLA2_OK) return 0;
+    return ws_bytes_of(D, op);
+}
+
+SLA2_API sla2_status sla2_check(const sla2_problem* p, int32_t op) {
+    Dims D;
+    return make_dims(p, op, &D);
+}
+
+SLA2_API const char* sla2_status_str(int32_t s) {
+    switch (s) {
+        case SLA2_OK: return "ok";
+        case SLA2_EINVAL: return "invalid argument";
+        case SLA2_EUNSUPPORTED: return "unsupported configuration";
+        case SLA2_EWORKSPACE: return "workspace too small";
+        case SLA2_EHIP: return "HIP launch error";
+        default: return "unknown status";
+    }
+}
+
+static sla2_status check_ws(const Dims& D, int op, void* ws, size_t ws_bytes) {
+    size_t need = ws_bytes_of(D, op);
+    if (need > 0 && (!ws || !aligned(ws, 256))) return SLA2_EINVAL;
+    if (ws_bytes < need) return SLA2_EWORKSPACE;
+    return SLA2_OK;
+}
+
+static bool ok_ptr(const void* p) { return p && aligned(p, 16); }
+
+SLA2_API sla2_status sla2_route(const sla2_problem* p, const void* Q, const void* K,
+                                const float* Wq, const float* Wk, int32_t* topk_idx,
+                                uint8_t* block_mask, void* ws, size_t ws_bytes,
+                                void* stream) {
+    Dims D;
+    sla2_status st = make_dims(p, SLA2_OP_ROUTE, &D);
+    if (st != SLA2_OK) return st;
+    if (!ok_ptr(Q) || !ok_ptr(K) || !ok_ptr(Wq) || !ok_ptr(Wk)) return SLA2_EINVAL;
+    if (D.k > 0 && !ok_ptr(topk_idx)) return SLA2_EINVAL;
+    if (block_mask && !aligned(block_mask, 16)) return SLA2_EINVAL;
+    if ((st = check_ws(D, SLA2_OP_ROUTE, ws, ws_bytes)) != SLA2_OK) return st;
+    RouteWS w;
+    layout_route(D, (char*)ws, &w);
+    hipError_t e = launch_route(D, Q, K, Wq, Wk, topk_idx, block_mask, w, (hipStream_t)stream);
+    return e == hipSuccess ? SLA2_OK : SLA2_EHIP;
+}
+
+static sla2_status forward_args(const sla2_problem* p, int op, const void* Q, const void* K,
+                                const void* V, const int32_t* idx, const float* alpha,
+                                float* O, void* ws, size_t ws_bytes, Dims* D, FwdWS* w) {
+    sla2_status st = make_dims(p, op, D);
+    if (st != SLA2_OK) return st;
+    if (!ok_ptr(Q) || !ok_ptr(K) || !ok_ptr(V) || !ok_ptr(alpha) || !ok_ptr(O))
+        return SLA2_EINVAL;
+    if (D->k > 0 && !ok_ptr(idx)) return SLA2_EINVAL;
+    if ((st = check_ws(*D, op, ws, ws_bytes)) != SLA2_OK) return st;
+    layout_forward(*D, op, (char*)ws, w);
+    return SLA2_OK;
+}
+
+SLA2_API sla2_status sla2_forward(const sla2_problem* p, const void* Q, const void* K,
+                                  const void* V, const int32_t* topk_idx, const float* alpha,
+                                  float* O, void* ws, size_t ws_bytes, void* stream) {
+    Dims D;
+    FwdWS w;
+    sla2_status st = forward_args(p, SLA2_OP_FORWARD, Q, K, V, topk_idx, alpha, O, ws,
+                                  ws_bytes, &D, &w);
+    if (st != SLA2_OK) return st;
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t e;
+    if (D.dtype == SLA2_F32 || D.bq != 128) {
+        e = launch_forward_valu(D, Q, K, V, topk_idx, alpha, O, w, s);
+    } else {
+        e = launch_summaries_mfma(D, K, V, w, s);
+        if (e == hipSuccess) e = launch_fused_mfma(D, Q, K, topk_idx, alpha, O, w, s);
+    }
+    return e == hipSuccess ? SLA2_OK : SLA2_EHIP;
+}
+
+SLA2_API sla2_status sla2_forward_fp8(const sla2_problem* p, const void* Q, const void* K,
+                                      const void* V, const int32_t* topk_idx,
+                                      const float* alpha, float* O, void* ws,
+                                      size_t ws_bytes, void* stream) {
+    Dims D;
+    FwdWS w;
+    sla2_status st = forward_args(p, SLA2_OP_FORWARD_FP8, Q, K, V, topk_idx, alpha, O, ws,
+                                  ws_bytes, &D, &w);
+    if (st != SLA2_OK) return st;
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t e = launch_quantize_fp8(D, Q, K, w, s);
+    if (e == hipSuccess) e = launch_summaries_mfma(D, K, V, w, s);
+    if (e == hipSuccess) e = launch_fused_fp8(D, Q, topk_idx, alpha, O, w, s);
+    return e == hipSuccess ? SLA2_OK : SLA2_EHIP;
+}
+
+SLA2_API sla2_status sla2_quantize_fp8(const sla2_problem* p, const void* Q, const void* K,
+                                       uint8_t* Qhat, uint8_t* Khat, float* sQ, float* sK,
+                                       float* mu, void* ws, size_t ws_bytes, void* stream) {
+    Dims D;
+    sla2_status st = make_dims(p, SLA2_OP_FORWARD_FP8, &D);
+    if (st != SLA2_OK) return st;
+    if (!ok_ptr(Q) || !ok_ptr(K) || !ok_ptr(Qhat) || !ok_ptr(Khat) || !ok_ptr(sQ) ||
+        !ok_ptr(sK) || !ok_ptr(mu))
+        return SLA2_EINVAL;
+    if ((st = check_ws(D, SLA2_OP_FORWARD_FP8, ws, ws_bytes)) != SLA2_OK) return st;
+    FwdWS w;
+    layout_forward(D, SLA2_OP_FORWARD_FP8, (char*)ws, &w);
+    w.qhat = Qhat;
+    w.khat = Khat;
+    w.sq = sQ;
+    w.sk = sK;
+    w.mu = mu;
+    hipError_t e = launch_quantize_fp8(D, Q, K, w, (hipStream_t)stream);
+    return e == hipSuccess ? SLA2_OK : SLA2_EHIP;
+}
+
+SLA2_API sla2_status sla2_timing_start(int32_t max_launches) {
+    if (max_launches <= 0) return SLA2_EINVAL;
+    if ((int)g_timing.recs.size() < max_launches) {
+        size_t old = g_timing.recs.size();
+        g_timing.recs.resize(max_launches);
+        for (size_t i = old; i < g_timing.recs.size(); ++i) {
+            if (hipEventCreate(&g_timing.recs[i].a) != hipSuccess ||
+                hipEventCreate(&g_timing.recs[i].b) != hipSuccess) {
+                g_timing.recs.resize(i);
+                return SLA2_EHIP;
+            }
+        }
+    }
+    g_timing.max = max_launches;
+    g_timing.used = 0;
+    g_timing.on = true;
+    return SLA2_OK;
+}
+
+SLA2_API sla2_status sla2_timing_stop(float* total_ms, int32_t* launches, int32_t n_kinds) {
+    if (!total_ms || !launches || n_kinds <= 0) return SLA2_EINVAL;
+    for (int i = 0; i < n_kinds; ++i) {
+        total_ms[i] = 0.0f;
+        launches[i] = 0;
+    }
+    sla2_status st = SLA2_OK;
+    for (int i = 0; i < g_timing.used; ++i) {
+        Rec& r = g_timing.recs[i];
+        if (hipEventSynchronize(r.b) != hipSuccess) {
+            st = SLA2_EHIP;
+            continue;
+        }
+        float ms = 0.0f;
+        if (hipEventElapsedTime(&ms, r.a, r.b) != hipSuccess) {
+            st = SLA2_EHIP;
+            continue;
+        }
+        if (r.kind >= 0 && r.kind < n_kinds) {
+            total_ms[r.kind] += ms;
+            launches[r.kind] += 1;
+        }
+    }
+    g_timing.on = false;
+    g_timing.used = 0;
+    return st;
+}
+
+SLA2_API int32_t sla2_kernel_kinds(void) { return K_NUM_KINDS; }
+
+SLA2_API const char* sla2_kernel_name(int32_t kind) {
+    if (kind < 0 || kind >= K_NUM_KINDS) return "";
+    return kKindNames[kind];
+}

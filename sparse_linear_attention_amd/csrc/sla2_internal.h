@@ -1,0 +1,111 @@
+// Internal declarations of libsla2: problem dimensions, workspace layout,
+// kernel launchers and the timing hooks.  Host and device code of the
+// library only.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "sla2.h"
+
+namespace sla2 {
+
+// kinds of kernels, for the timing records
+enum KernelKind {
+    K_POOL_PROJECT = 0,
+    K_SCORE,
+    K_TOPK,
+    K_SUMM_VALU,
+    K_SUMM_REDUCE,
+    K_FUSED_VALU,
+    K_SUMM_MFMA,
+    K_FUSED_MFMA,
+    K_QUANT_MEAN,
+    K_QUANT,
+    K_FUSED_FP8,
+    K_NUM_KINDS
+};
+
+struct Dims {
+    int B, H, N, d, bq, bkv;
+    int Tq, Tkv, k, w_heads;
+    int dtype;  // sla2_dtype
+    long BH;
+};
+
+// chunking of the token axis for the block-summary pass
+constexpr int kSummBlocksPerChunk = 16;  // KV blocks of 64 tokens per work-group
+inline int summ_chunks(const Dims& D) {
+    return (D.Tkv + kSummBlocksPerChunk - 1) / kSummBlocksPerChunk;
+}
+
+inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// ---------------------------------------------------------------------------
+// workspace layout.  Every region starts 256-byte aligned.
+// ---------------------------------------------------------------------------
+struct RouteWS {
+    double* qt;  // [BH][Tq][d]   projected pooled queries
+    double* kt;  // [BH][Tkv][d]  projected pooled keys
+    double* S;   // [BH][Tq][Tkv] compressed scores
+};
+
+struct FwdWS {
+    // bf16 path: block-transposed fp16 copies, kv order permuted inside each
+    // group of 16 (see the fused kernel), padding tokens are 0
+    uint16_t* vt;    // [BH][Tkv][d][64]  V^T      (fp16 bits)
+    uint16_t* pkt;   // [BH][Tkv][d][64]  phi(K)^T (fp16 bits)
+    float* zb;       // [BH][Tkv][d]      per-block z_j
+    float* hpart;    // [BH][chunks][d][d] partial h per chunk
+    float* zpart;    // [BH][chunks][d]
+    float* htot;     // [BH][d][d]        h_tot[c][e] = sum phi(K)[.,c] V[.,e]
+    float* ztot;     // [BH][d]
+    // low-bit inputs
+    uint8_t* qhat;   // [BH][Tq*bq][d]
+    uint8_t* khat;   // [BH][Tkv*64][d]
+    float* sq;       // [BH][Tq]
+    float* sk;       // [BH][Tkv]
+    float* mu;       // [BH][d]
+};
+
+// Lays out the workspace of `op` starting at `base` (may be null to size
+// only); returns the bytes needed.
+size_t layout_route(const Dims& D, char* base, RouteWS* ws);
+size_t layout_forward(const Dims& D, int op, char* base, FwdWS* ws);
+
+// ---------------------------------------------------------------------------
+// timing hooks (no-ops unless sla2_timing_start was called)
+// ---------------------------------------------------------------------------
+void timing_before(hipStream_t s, int kind);
+void timing_after(hipStream_t s, int kind);
+
+// ---------------------------------------------------------------------------
+// launchers (each returns hipGetLastError() after its launches)
+// ---------------------------------------------------------------------------
+hipError_t launch_route(const Dims& D, const void* Q, const void* K, const float* Wq,
+                        const float* Wk, int32_t* idx, uint8_t* mask, const RouteWS& ws,
+                        hipStream_t s);
+
+// fp32 path: VALU block summaries + VALU fused kernel
+hipError_t launch_forward_valu(const Dims& D, const void* Q, const void* K, const void* V,
+                               const int32_t* idx, const float* alpha, float* O,
+                               const FwdWS& ws, hipStream_t s);
+
+// deterministic reduction of the per-chunk summary partials
+hipError_t launch_summaries_reduce(const Dims& D, const FwdWS& ws, hipStream_t s);
+
+// bf16 path: MFMA block summaries + MFMA fused kernel (bq = 128)
+hipError_t launch_summaries_mfma(const Dims& D, const void* K, const void* V,
+                                 const FwdWS& ws, hipStream_t s);
+hipError_t launch_fused_mfma(const Dims& D, const void* Q, const void* K,
+                             const int32_t* idx, const float* alpha, float* O,
+                             const FwdWS& ws, hipStream_t s);
+
+// low bit
+hipError_t launch_quantize_fp8(const Dims& D, const void* Q, const void* K, const FwdWS& ws,
+                               hipStream_t s);
+hipError_t launch_fused_fp8(const Dims& D, const void* Q, const int32_t* idx,
+                            const float* alpha, float* O, const FwdWS& ws, hipStream_t s);
+
+}  // namespace sla2

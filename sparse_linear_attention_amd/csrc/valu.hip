@@ -1,0 +1,282 @@
+// fp32 forward path (vector ALU): linear-branch block summaries and a fused
+// sparse + linear + combine kernel.
+//
+// Sparse branch ("SLA2 深度解读" 04/08): online softmax of q.k/sqrt(d) over
+// the tokens of the selected KV blocks.  Linear branch (SLA notes, key
+// design 3/4): O_l = phi(q) H_i / (phi(q) . Z_i) with H_i = h_tot - sum over
+// selected blocks; the selected part is evaluated per token as
+// sum_u (phi(q) . phi(k_u)) v_u, which equals phi(q) (sum_u phi(k_u)^T v_u).
+// Combine: O = alpha O_s + (1 - alpha) O_l.
+#include "sla2_internal.h"
+
+namespace sla2 {
+namespace {
+
+__device__ inline float ld1(const float* p) { return *p; }
+__device__ inline float ld1(const uint16_t* p) { return __uint_as_float((unsigned)(*p) << 16); }
+
+__device__ inline float phi_f(float x) { return x > 0.0f ? x + 1.0f : expf(x); }
+
+// Per-chunk partial h[c][e] = sum_u phi(K_u)[c] V_u[e] and z[c] = sum_u phi(K_u)[c]
+// over the valid tokens of the chunk.  grid (chunks, BH), 256 threads.
+template <typename T>
+__global__ __launch_bounds__(256) void summaries_valu_kernel(
+    const T* __restrict__ K, const T* __restrict__ V, float* __restrict__ hpart,
+    float* __restrict__ zpart, int N, int d, int nch) {
+    __shared__ float pk[32 * 128];
+    __shared__ float vv[32 * 128];
+    const int chunk = blockIdx.x;
+    const long bh = blockIdx.y;
+    const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
+    const int SB = d >> 4;  // 8 or 4
+    const int t_begin = chunk * kSummBlocksPerChunk * 64;
+    const int t_end = min(N, t_begin + kSummBlocksPerChunk * 64);
+    const T* Kh = K + (size_t)bh * N * d;
+    const T* Vh = V + (size_t)bh * N * d;
+    float acc[8][8];
+    float z[8];
+#pragma unroll
+    for (int a = 0; a < 8; ++a) {
+        z[a] = 0.0f;
+#pragma unroll
+        for (int b = 0; b < 8; ++b) acc[a][b] = 0.0f;
+    }
+    for (int u0 = t_begin; u0 < t_end; u0 += 32) {
+        for (int x = threadIdx.x; x < 32 * d; x += 256) {
+            const int u = x / d, c = x % d;
+            const int t = u0 + u;
+            const bool ok = t < t_end;
+            pk[u * d + c] = ok ? phi_f(ld1(Kh + (size_t)t * d + c)) : 0.0f;
+            vv[u * d + c] = ok ? ld1(Vh + (size_t)t * d + c) : 0.0f;
+        }
+        __syncthreads();
+        for (int u = 0; u < 32; ++u) {
+            float a[8], b[8];
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                a[q] = q < SB ? pk[u * d + ty * SB + q] : 0.0f;
+                b[q] = q < SB ? vv[u * d + tx * SB + q] : 0.0f;
+            }
+#pragma unroll
+            for (int p = 0; p < 8; ++p) {
+                z[p] += a[p];
+#pragma unroll
+                for (int q = 0; q < 8; ++q) acc[p][q] = fmaf(a[p], b[q], acc[p][q]);
+            }
+        }
+        __syncthreads();
+    }
+    float* hp = hpart + ((size_t)bh * nch + chunk) * d * d;
+    for (int p = 0; p < SB; ++p)
+        for (int q = 0; q < SB; ++q) hp[(size_t)(ty * SB + p) * d + tx * SB + q] = acc[p][q];
+    if (tx == 0) {
+        float* zp = zpart + ((size_t)bh * nch + chunk) * d;
+        for (int p = 0; p < SB; ++p) zp[ty * SB + p] = z[p];
+    }
+}
+
+// h_tot = sum of the chunk partials in chunk order (deterministic).
+__global__ __launch_bounds__(256) void summaries_reduce_kernel(
+    const float* __restrict__ hpart, const float* __restrict__ zpart, float* __restrict__ htot,
+    float* __restrict__ ztot, int d, int nch) {
+    const long bh = blockIdx.y;
+    const int x = blockIdx.x * 256 + threadIdx.x;
+    const int dd = d * d;
+    if (x < dd) {
+        float s = 0.0f;
+        for (int c = 0; c < nch; ++c) s += hpart[((size_t)bh * nch + c) * dd + x];
+        htot[(size_t)bh * dd + x] = s;
+    }
+    if (blockIdx.x == 0 && threadIdx.x < d) {
+        float s = 0.0f;
+        for (int c = 0; c < nch; ++c) s += zpart[((size_t)bh * nch + c) * d + threadIdx.x];
+        ztot[(size_t)bh * d + threadIdx.x] = s;
+    }
+}
+
+// Fused sparse + linear + combine.  A work-group handles 32 query rows of one
+// query block; 8 threads per row, each owning d/8 channels.  KV tiles are
+// visited 32 tokens at a time.  grid (Tq * bq/32, BH), 256 threads.
+template <typename T>
+__global__ __launch_bounds__(256) void fused_valu_kernel(
+    const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
+    const int32_t* __restrict__ idx, const float* __restrict__ alpha,
+    const float* __restrict__ htot, const float* __restrict__ ztot, float* __restrict__ O,
+    int N, int d, int bq, int Tq, int Tkv, int k, int H) {
+    __shared__ float Kt[32 * 128];
+    __shared__ float Vt[32 * 128];
+    __shared__ float Pk[32 * 128];
+    const int per_blk = bq >> 5;
+    const int qb = blockIdx.x / per_blk;
+    const int row = threadIdx.x >> 3, sub = threadIdx.x & 7;
+    const int CS = d >> 3;  // 16 or 8
+    const int c0 = sub * CS;
+    const long bh = blockIdx.y;
+    const int tq = qb * bq + (blockIdx.x % per_blk) * 32 + row;
+    const bool valid_q = tq < N;
+    const T* Qh = Q + (size_t)bh * N * d;
+    const T* Kh = K + (size_t)bh * N * d;
+    const T* Vh = V + (size_t)bh * N * d;
+    const float inv_sqrt_d = 1.0f / sqrtf((float)d);
+
+    float q[16], pq[16], acc[16], corr[16];
+#pragma unroll
+    for (int c = 0; c < 16; ++c) {
+        const float x = (c < CS && valid_q) ? ld1(Qh + (size_t)tq * d + c0 + c) : 0.0f;
+        q[c] = x;
+        pq[c] = phi_f(x);
+        acc[c] = 0.0f;
+        corr[c] = 0.0f;
+    }
+    float m = -INFINITY, l = 0.0f, zc = 0.0f;
+    const int32_t* sel = idx + ((size_t)bh * Tq + qb) * k;
+
+    for (int r = 0; r < k; ++r) {
+        const int j = sel[r];
+        for (int half = 0; half < 2; ++half) {
+            const int u0 = j * 64 + half * 32;
+            const int nu = min(32, N - u0);
+            if (nu <= 0) break;
+            for (int x = threadIdx.x; x < 32 * d; x += 256) {
+                const int u = x / d, c = x % d;
+                const bool ok = u < nu;
+                const float kv = ok ? ld1(Kh + (size_t)(u0 + u) * d + c) : 0.0f;
+                Kt[u * d + c] = kv;
+                Pk[u * d + c] = ok ? phi_f(kv) : 0.0f;
+                Vt[u * d + c] = ok ? ld1(Vh + (size_t)(u0 + u) * d + c) : 0.0f;
+            }
+            __syncthreads();
+            float s[32];
+            float tmax = -INFINITY;
+#pragma unroll
+            for (int u = 0; u < 32; ++u) {
+                float sp = 0.0f, ap = 0.0f;
+#pragma unroll
+                for (int c = 0; c < 16; ++c) {
+                    if (c < CS) {
+                        sp = fmaf(q[c], Kt[u * d + c0 + c], sp);
+                        ap = fmaf(pq[c], Pk[u * d + c0 + c], ap);
+                    }
+                }
+                sp += __shfl_xor(sp, 1);
+                sp += __shfl_xor(sp, 2);
+                sp += __shfl_xor(sp, 4);
+                ap += __shfl_xor(ap, 1);
+                ap += __shfl_xor(ap, 2);
+                ap += __shfl_xor(ap, 4);
+                const bool ok = u < nu;
+                s[u] = ok ? sp * inv_sqrt_d : -INFINITY;
+                tmax = fmaxf(tmax, s[u]);
+                if (ok) {
+                    zc += ap;
+#pragma unroll
+                    for (int c = 0; c < 16; ++c)
+                        if (c < CS) corr[c] = fmaf(ap, Vt[u * d + c0 + c], corr[c]);
+                }
+            }
+            const float mn = fmaxf(m, tmax);
+            const float resc = (m == -INFINITY) ? 0.0f : expf(m - mn);
+            l *= resc;
+#pragma unroll
+            for (int c = 0; c < 16; ++c) acc[c] *= resc;
+#pragma unroll
+            for (int u = 0; u < 32; ++u) {
+                const float p = expf(s[u] - mn);
+                l += p;
+#pragma unroll
+                for (int c = 0; c < 16; ++c)
+                    if (c < CS) acc[c] = fmaf(p, Vt[u * d + c0 + c], acc[c]);
+            }
+            m = mn;
+            __syncthreads();
+        }
+    }
+
+    // linear branch: phi(q) (h_tot - selected) / (phi(q) . (z_tot - selected))
+    float ol[16];
+#pragma unroll
+    for (int c = 0; c < 16; ++c) ol[c] = 0.0f;
+    if (k < Tkv) {
+        const float* hT = htot + (size_t)bh * d * d;
+        const float* zT = ztot + (size_t)bh * d;
+        // full phi(q) of each row into LDS
+#pragma unroll
+        for (int c = 0; c < 16; ++c)
+            if (c < CS) Kt[row * d + c0 + c] = pq[c];
+        float den = 0.0f;
+#pragma unroll
+        for (int c = 0; c < 16; ++c)
+            if (c < CS) den = fmaf(pq[c], zT[c0 + c], den);
+        den += __shfl_xor(den, 1);
+        den += __shfl_xor(den, 2);
+        den += __shfl_xor(den, 4);
+        den -= zc;
+        float num[16];
+#pragma unroll
+        for (int c = 0; c < 16; ++c) num[c] = 0.0f;
+        for (int cb = 0; cb < d; cb += 32) {
+            __syncthreads();
+            for (int x = threadIdx.x; x < 32 * d; x += 256) Vt[x] = hT[(size_t)cb * d + x];
+            __syncthreads();
+            for (int cc = 0; cc < 32; ++cc) {
+                const float a = Kt[row * d + cb + cc];
+#pragma unroll
+                for (int c = 0; c < 16; ++c)
+                    if (c < CS) num[c] = fmaf(a, Vt[cc * d + c0 + c], num[c]);
+            }
+        }
+#pragma unroll
+        for (int c = 0; c < 16; ++c) ol[c] = (num[c] - corr[c]) / den;
+    }
+    if (valid_q) {
+        const float a = alpha[bh % H];
+        const float inv_l = (k > 0) ? 1.0f / l : 0.0f;
+        float* o = O + ((size_t)bh * N + tq) * d + c0;
+#pragma unroll
+        for (int c = 0; c < 16; ++c)
+            if (c < CS) o[c] = a * (acc[c] * inv_l) + (1.0f - a) * ol[c];
+    }
+}
+
+}  // namespace
+
+hipError_t launch_summaries_reduce(const Dims& D, const FwdWS& ws, hipStream_t s) {
+    const int nch = summ_chunks(D);
+    timing_before(s, K_SUMM_REDUCE);
+    summaries_reduce_kernel<<<dim3((D.d * D.d + 255) / 256, (unsigned)D.BH), 256, 0, s>>>(
+        ws.hpart, ws.zpart, ws.htot, ws.ztot, D.d, nch);
+    timing_after(s, K_SUMM_REDUCE);
+    return hipGetLastError();
+}
+
+hipError_t launch_forward_valu(const Dims& D, const void* Q, const void* K, const void* V,
+                               const int32_t* idx, const float* alpha, float* O,
+                               const FwdWS& ws, hipStream_t s) {
+    const int nch = summ_chunks(D);
+    if (D.k < D.Tkv) {
+        timing_before(s, K_SUMM_VALU);
+        if (D.dtype == SLA2_F32)
+            summaries_valu_kernel<float><<<dim3(nch, (unsigned)D.BH), 256, 0, s>>>(
+                (const float*)K, (const float*)V, ws.hpart, ws.zpart, D.N, D.d, nch);
+        else
+            summaries_valu_kernel<uint16_t><<<dim3(nch, (unsigned)D.BH), 256, 0, s>>>(
+                (const uint16_t*)K, (const uint16_t*)V, ws.hpart, ws.zpart, D.N, D.d, nch);
+        timing_after(s, K_SUMM_VALU);
+        hipError_t e = launch_summaries_reduce(D, ws, s);
+        if (e != hipSuccess) return e;
+    }
+    dim3 g(D.Tq * (D.bq / 32), (unsigned)D.BH);
+    timing_before(s, K_FUSED_VALU);
+    if (D.dtype == SLA2_F32)
+        fused_valu_kernel<float><<<g, 256, 0, s>>>(
+            (const float*)Q, (const float*)K, (const float*)V, idx, alpha, ws.htot, ws.ztot, O,
+            D.N, D.d, D.bq, D.Tq, D.Tkv, D.k, D.H);
+    else
+        fused_valu_kernel<uint16_t><<<g, 256, 0, s>>>(
+            (const uint16_t*)Q, (const uint16_t*)K, (const uint16_t*)V, idx, alpha, ws.htot,
+            ws.ztot, O, D.N, D.d, D.bq, D.Tq, D.Tkv, D.k, D.H);
+    timing_after(s, K_FUSED_VALU);
+    return hipGetLastError();
+}
+
+}  // namespace sla2

@@ -164,6 +164,7 @@ def _smooth_field(rng: np.random.Generator, grid, d: int) -> np.ndarray:
     f = f.reshape(-1, d)
     mu = f.mean(axis=0, dtype=np.float64)
     sd = f.std(axis=0, dtype=np.float64)
+    sd = np.where(sd > 0, sd, 1.0)  # a single-token field has no spread
     return ((f - mu) / sd).astype(np.float32)
 
 
@@ -193,7 +194,8 @@ def _smooth_inputs(wl: Workload, threads: int | None = None) -> Inputs:
     t = rs.integers(0, N, 65536)
     u = rs.integers(0, N, 65536)
     x = np.einsum("ij,ij->i", q0[t].astype(np.float64), k0[u].astype(np.float64)) / math.sqrt(d)
-    s = math.sqrt(3.0 / float(x.std()))
+    sx = float(x.std())
+    s = math.sqrt(3.0 / sx) if sx > 0 else 1.0
     del q0, k0
 
     store_bf16 = wl.dtype == "bf16"

@@ -1,0 +1,211 @@
+"""ctypes binding of libsla2.so (C ABI in include/sla2.h).
+
+Argument marshalling only: every step of the computation runs in the HIP
+library.  Tensors are torch tensors on the GPU (PyTorch supplies device memory
+and the stream); names follow the C entry points.  Loading fails loudly if the
+library has not been built.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libsla2.so")
+
+OK, EINVAL, EUNSUPPORTED, EWORKSPACE, EHIP = range(5)
+F32, BF16 = 0, 1
+PHI_ELU1 = 0
+OP_ROUTE, OP_FORWARD, OP_FORWARD_FP8 = 0, 1, 2
+
+
+class Problem(C.Structure):
+    _fields_ = [("B", C.c_int32), ("H", C.c_int32), ("N", C.c_int32), ("d", C.c_int32),
+                ("bq", C.c_int32), ("bkv", C.c_int32), ("topk_frac", C.c_float),
+                ("w_heads", C.c_int32), ("phi", C.c_int32), ("dtype", C.c_int32)]
+
+
+class SLA2Error(RuntimeError):
+    def __init__(self, status: int, what: str):
+        super().__init__(f"{what}: {status_str(status)} ({status})")
+        self.status = status
+
+
+_lib = None
+
+
+def lib():
+    """The loaded library; raises if it is missing (no fallback exists)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is not built; run sparse_linear_attention_amd/build.py "
+                "(or __graft_entry__.build()) first")
+        L = C.CDLL(LIB_PATH)
+        P = C.POINTER(Problem)
+        vp = C.c_void_p
+        L.sla2_num_q_blocks.argtypes = [P]
+        L.sla2_num_kv_blocks.argtypes = [P]
+        L.sla2_topk.argtypes = [P]
+        L.sla2_workspace_bytes.argtypes = [P, C.c_int32]
+        L.sla2_workspace_bytes.restype = C.c_size_t
+        L.sla2_check.argtypes = [P, C.c_int32]
+        L.sla2_status_str.argtypes = [C.c_int32]
+        L.sla2_status_str.restype = C.c_char_p
+        L.sla2_route.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, C.c_size_t, vp]
+        L.sla2_forward.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, C.c_size_t, vp]
+        L.sla2_forward_fp8.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, C.c_size_t, vp]
+        L.sla2_quantize_fp8.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, C.c_size_t, vp]
+        L.sla2_timing_start.argtypes = [C.c_int32]
+        L.sla2_timing_stop.argtypes = [vp, vp, C.c_int32]
+        L.sla2_kernel_name.argtypes = [C.c_int32]
+        L.sla2_kernel_name.restype = C.c_char_p
+        _lib = L
+    return _lib
+
+
+EXPORTS = ("sla2_num_q_blocks", "sla2_num_kv_blocks", "sla2_topk", "sla2_workspace_bytes",
+           "sla2_check", "sla2_status_str", "sla2_route", "sla2_forward", "sla2_forward_fp8",
+           "sla2_quantize_fp8", "sla2_timing_start", "sla2_timing_stop", "sla2_kernel_kinds",
+           "sla2_kernel_name")
+
+
+def problem(B, H, N, d, bq=128, bkv=64, topk_frac=0.03, w_heads=1, dtype=BF16,
+            phi=PHI_ELU1) -> Problem:
+    if isinstance(dtype, str):
+        dtype = F32 if dtype == "f32" else BF16
+    return Problem(B, H, N, d, bq, bkv, float(topk_frac), w_heads, phi, dtype)
+
+
+def status_str(s: int) -> str:
+    return lib().sla2_status_str(int(s)).decode()
+
+
+def num_q_blocks(p: Problem) -> int:
+    return lib().sla2_num_q_blocks(C.byref(p))
+
+
+def num_kv_blocks(p: Problem) -> int:
+    return lib().sla2_num_kv_blocks(C.byref(p))
+
+
+def topk(p: Problem) -> int:
+    return lib().sla2_topk(C.byref(p))
+
+
+def workspace_bytes(p: Problem, op: int) -> int:
+    return int(lib().sla2_workspace_bytes(C.byref(p), op))
+
+
+def check(p: Problem, op: int) -> int:
+    return int(lib().sla2_check(C.byref(p), op))
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    return t.data_ptr() if hasattr(t, "data_ptr") else int(t)
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _ws(ws):
+    if ws is None:
+        return None, 0
+    return ws.data_ptr(), ws.numel() * ws.element_size()
+
+
+def _raise(st, what):
+    if st != OK:
+        raise SLA2Error(st, what)
+
+
+def sla2_route(p, Q, K, Wq, Wk, topk_idx, block_mask=None, ws=None, stream=None):
+    wp, wb = _ws(ws)
+    _raise(lib().sla2_route(C.byref(p), _ptr(Q), _ptr(K), _ptr(Wq), _ptr(Wk), _ptr(topk_idx),
+                            _ptr(block_mask), wp, wb, _stream(stream)), "sla2_route")
+
+
+def sla2_forward(p, Q, K, V, topk_idx, alpha, O, ws=None, stream=None):
+    wp, wb = _ws(ws)
+    _raise(lib().sla2_forward(C.byref(p), _ptr(Q), _ptr(K), _ptr(V), _ptr(topk_idx),
+                              _ptr(alpha), _ptr(O), wp, wb, _stream(stream)), "sla2_forward")
+
+
+def sla2_forward_fp8(p, Q, K, V, topk_idx, alpha, O, ws=None, stream=None):
+    wp, wb = _ws(ws)
+    _raise(lib().sla2_forward_fp8(C.byref(p), _ptr(Q), _ptr(K), _ptr(V), _ptr(topk_idx),
+                                  _ptr(alpha), _ptr(O), wp, wb, _stream(stream)),
+           "sla2_forward_fp8")
+
+
+def sla2_quantize_fp8(p, Q, K, Qhat, Khat, sQ, sK, mu, ws=None, stream=None):
+    wp, wb = _ws(ws)
+    _raise(lib().sla2_quantize_fp8(C.byref(p), _ptr(Q), _ptr(K), _ptr(Qhat), _ptr(Khat),
+                                   _ptr(sQ), _ptr(sK), _ptr(mu), wp, wb, _stream(stream)),
+           "sla2_quantize_fp8")
+
+
+def kernel_names():
+    L = lib()
+    return [L.sla2_kernel_name(i).decode() for i in range(L.sla2_kernel_kinds())]
+
+
+def timing_start(max_launches: int = 4096):
+    _raise(lib().sla2_timing_start(max_launches), "sla2_timing_start")
+
+
+def timing_stop():
+    """Returns {kernel name: (total ms, launches)} for the recorded launches."""
+    import numpy as np
+    n = lib().sla2_kernel_kinds()
+    ms = np.zeros(n, np.float32)
+    cnt = np.zeros(n, np.int32)
+    _raise(lib().sla2_timing_stop(ms.ctypes.data, cnt.ctypes.data, n), "sla2_timing_stop")
+    return {name: (float(ms[i]), int(cnt[i])) for i, name in enumerate(kernel_names())
+            if cnt[i] > 0}
+
+
+# ---------------------------------------------------------------------------
+# convenience wrappers around the entry points (allocation with torch)
+# ---------------------------------------------------------------------------
+def workspace(p: Problem, op: int, device="cuda"):
+    import torch
+    n = workspace_bytes(p, op)
+    if n == 0:
+        st = check(p, op)
+        _raise(st if st != OK else EINVAL, "workspace_bytes")
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def route(p: Problem, Q, K, Wq, Wk, want_mask=True, ws=None, stream=None):
+    """Allocates outputs, runs sla2_route; returns (topk_idx, block_mask)."""
+    import torch
+    dev = Q.device
+    Tq, Tkv, k = num_q_blocks(p), num_kv_blocks(p), topk(p)
+    idx = torch.empty((p.B, p.H, Tq, max(k, 0)), dtype=torch.int32, device=dev)
+    mask = torch.empty((p.B, p.H, Tq, Tkv), dtype=torch.uint8, device=dev) if want_mask else None
+    if ws is None:
+        ws = workspace(p, OP_ROUTE, dev)
+    sla2_route(p, Q, K, Wq, Wk, idx if k > 0 else None, mask, ws, stream)
+    return idx, mask
+
+
+def forward(p: Problem, Q, K, V, topk_idx, alpha, fp8=False, ws=None, out=None, stream=None):
+    """Allocates O (fp32) and the workspace if not given; runs the forward."""
+    import torch
+    dev = Q.device
+    O = out if out is not None else torch.empty((p.B, p.H, p.N, p.d), dtype=torch.float32,
+                                                device=dev)
+    op = OP_FORWARD_FP8 if fp8 else OP_FORWARD
+    if ws is None:
+        ws = workspace(p, op, dev)
+    fn = sla2_forward_fp8 if fp8 else sla2_forward
+    fn(p, Q, K, V, topk_idx if topk(p) > 0 else None, alpha, O, ws, stream)
+    return O

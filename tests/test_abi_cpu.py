@@ -1,0 +1,128 @@
+"""Host-side checks of the C ABI (no GPU needed, nothing is launched).
+
+The library must load, export every entry point ``include/sla2.h`` declares,
+and reject invalid arguments on the host before touching the device.
+"""
+import ctypes as C
+import json
+import os
+import re
+
+import numpy as np
+import pytest
+
+from sparse_linear_attention_amd import sla2 as S
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sla2.h")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(sla2_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_symbol():
+    L = S.lib()
+    names = declared_functions()
+    assert len(names) >= 12
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(S.EXPORTS) == set(names)
+
+
+def test_oracle_library_loads(orc):
+    assert orc.topk(orc.problem(1, 1, 640, 64, 64, 64, 0.5)) == 5
+
+
+def p_ok(**kw):
+    base = dict(B=1, H=2, N=1000, d=128, bq=128, bkv=64, topk_frac=0.25, w_heads=1, dtype=S.BF16)
+    base.update(kw)
+    return S.problem(**base)
+
+
+def test_block_counts_and_k():
+    p = p_ok(N=75600, topk_frac=0.03)
+    assert S.num_q_blocks(p) == 591 and S.num_kv_blocks(p) == 1182 and S.topk(p) == 36
+    p = p_ok(N=32760, topk_frac=0.03)
+    assert S.num_q_blocks(p) == 256 and S.num_kv_blocks(p) == 512 and S.topk(p) == 16
+
+
+def test_topk_matches_oracle_table(orc):
+    g = json.load(open(os.path.join(ROOT, "tests", "golden", "topk_counts.json")))
+    for c in g["cases"]:
+        p = p_ok(N=c["tkv"] * 64, topk_frac=c["frac"])
+        assert S.topk(p) == c["k"]
+        assert S.topk(p) == orc.topk(orc.problem(1, 2, c["tkv"] * 64, 128, 128, 64, c["frac"]))
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(B=0), S.EINVAL), (dict(H=-1), S.EINVAL), (dict(N=0), S.EINVAL),
+    (dict(topk_frac=-0.1), S.EINVAL), (dict(topk_frac=1.5), S.EINVAL),
+    (dict(topk_frac=float("nan")), S.EINVAL), (dict(w_heads=3), S.EINVAL),
+    (dict(dtype=7), S.EINVAL), (dict(d=96), S.EUNSUPPORTED), (dict(bq=32), S.EUNSUPPORTED),
+    (dict(bkv=128), S.EUNSUPPORTED), (dict(N=7681 * 64), S.EUNSUPPORTED),
+])
+def test_check_rejects(kw, code):
+    assert S.check(p_ok(**kw), S.OP_ROUTE) == code
+    assert S.workspace_bytes(p_ok(**kw), S.OP_ROUTE) == 0
+    assert S.topk(p_ok(**kw)) == -1
+
+
+def test_fp8_needs_bf16_and_bq128():
+    assert S.check(p_ok(dtype=S.F32), S.OP_FORWARD_FP8) == S.EUNSUPPORTED
+    assert S.check(p_ok(bq=64), S.OP_FORWARD_FP8) == S.EUNSUPPORTED
+    assert S.check(p_ok(), S.OP_FORWARD_FP8) == S.OK
+    assert S.check(p_ok(phi=1), S.OP_FORWARD) == S.EUNSUPPORTED
+    assert S.check(p_ok(), 9) == S.EINVAL
+
+
+def test_workspace_sizes_grow_with_the_problem():
+    prev = {op: 0 for op in (S.OP_ROUTE, S.OP_FORWARD, S.OP_FORWARD_FP8)}
+    for N in (64, 1000, 5000, 32760, 75600):
+        for op in prev:
+            n = S.workspace_bytes(p_ok(N=N, H=40), op)
+            assert n > prev[op] and n % 256 == 0
+            prev[op] = n
+    assert S.workspace_bytes(p_ok(N=75600, H=40), S.OP_FORWARD_FP8) > S.workspace_bytes(
+        p_ok(N=75600, H=40), S.OP_FORWARD)
+
+
+def _call_route(p, ptrs):
+    L = S.lib()
+    return L.sla2_route(C.byref(p), *ptrs)
+
+
+def test_entry_points_validate_before_launching():
+    """Null / misaligned pointers and short workspaces are caught on the host."""
+    L = S.lib()
+    p = p_ok()
+    good = 0x100000  # never dereferenced: every call below fails validation
+    ws_need = S.workspace_bytes(p, S.OP_ROUTE)
+    # null Q
+    assert L.sla2_route(C.byref(p), None, good, good, good, good, None, good, ws_need, None) == S.EINVAL
+    # misaligned K
+    assert L.sla2_route(C.byref(p), good, good + 2, good, good, good, None, good, ws_need, None) == S.EINVAL
+    # workspace too small
+    assert L.sla2_route(C.byref(p), good, good, good, good, good, None, good, ws_need - 256, None) == S.EWORKSPACE
+    # misaligned workspace
+    assert L.sla2_route(C.byref(p), good, good, good, good, good, None, good + 16, ws_need, None) == S.EINVAL
+    fw = S.workspace_bytes(p, S.OP_FORWARD)
+    assert L.sla2_forward(C.byref(p), good, good, good, good, None, good, good, fw, None) == S.EINVAL
+    assert L.sla2_forward(C.byref(p), good, good, good, good, good, good, good, fw - 1, None) == S.EWORKSPACE
+    pf = p_ok(dtype=S.F32)
+    f8 = S.workspace_bytes(p, S.OP_FORWARD_FP8)
+    assert L.sla2_forward_fp8(C.byref(pf), good, good, good, good, good, good, good, f8, None) == S.EUNSUPPORTED
+    assert L.sla2_quantize_fp8(C.byref(p), good, good, None, good, good, good, good, good, f8, None) == S.EINVAL
+    # idx may be null only when k == 0
+    p0 = p_ok(topk_frac=0.0)
+    assert L.sla2_route(C.byref(p), good, good, good, good, None, None, good, ws_need, None) == S.EINVAL
+    assert S.topk(p0) == 0
+
+
+def test_status_strings():
+    for s in range(5):
+        assert S.status_str(s) and S.status_str(s) != "unknown status"
+    assert S.status_str(42) == "unknown status"
+    assert "fused_mfma" in S.kernel_names()
