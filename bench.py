@@ -1,0 +1,283 @@
+"""Benchmark of the SLA2 forward pass on one MI355X.
+
+A step is one pass of the whole hot path over one batch: the router
+(sla2_route: pool + projection + score + top-k) and the forward
+(sla2_forward: block summaries, sparse branch, linear branch, combine) on the
+Wan2.1-14B-720P attention shape (B=1, H=40, N=75600, d=128, bf16, b_q=128,
+b_kv=64, top-k 3 % = 36 of 1182 KV blocks), with inputs resident in HBM.
+
+Metric: dense-equivalent attention TOPS = 4 B H N^2 d / step time (the pages'
+kernel metric, "SLA2 深度解读" 01/13: TOPS of the attention kernel against
+FlashAttention2's dense work).  Prints ONE JSON line.
+
+Options: --steps K --warmup W; --gpus N (only 1: this build runs on one GPU);
+--no-cpu-baseline skips the oracle timing; --workload wan13b for the smaller
+shape; --fp8 times sla2_forward_fp8 as well; --copy-calibration runs only a
+plain 1 GiB device copy (used to scale rocprofv3 FETCH_SIZE / WRITE_SIZE).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16/fp16 matrix peak
+PEAK_FP8_TFLOPS = 5000.0
+PEAK_HBM_GBS = 8000.0
+COUNTERS = os.path.join(ROOT, "profiles", "fused_mfma_wan14b_counters.json")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_sha() -> str:
+    p = os.path.join(ROOT, "sparse_linear_attention_amd", "csrc", "mfma.hip")
+    return hashlib.sha256(open(p, "rb").read()).hexdigest()[:16]
+
+
+# --------------------------------------------------------------------------
+# work accounting (algorithmic: what the method must compute)
+# --------------------------------------------------------------------------
+def dense_equivalent_flop(B, H, N, d) -> float:
+    return 4.0 * B * H * N * N * d
+
+
+def sparse_flop(idx_host: np.ndarray, N: int, d: int, bq: int, bkv: int) -> float:
+    """4 d sum_i n_q(i) sum_{j in S_i} n_kv(j): Q K^T and P V over the
+    selected tokens only (valid-token counts for ragged blocks)."""
+    BH, Tq, k = idx_host.shape
+    Tkv = -(-N // bkv)
+    nkv = np.full(Tkv, bkv, np.int64)
+    nkv[-1] = N - (Tkv - 1) * bkv
+    nq = np.full(Tq, bq, np.int64)
+    nq[-1] = N - (Tq - 1) * bq
+    if k == 0:
+        return 0.0
+    sel_tokens = nkv[idx_host].sum(axis=-1)  # [BH, Tq]
+    return float(4 * d * (sel_tokens * nq[None, :]).sum())
+
+
+def linear_apply_flop(BH, N, d) -> float:
+    """phi(Q) H_i: 2 N d^2 per head (the linear branch's per-query work)."""
+    return 2.0 * BH * N * d * d
+
+
+def linear_summary_flop(BH, N, d) -> float:
+    """sum_j phi(K_j)^T V_j: 2 N d^2 per head."""
+    return 2.0 * BH * N * d * d
+
+
+# --------------------------------------------------------------------------
+def copy_calibration():
+    import torch
+    n = 1 << 30
+    x = torch.empty(n, dtype=torch.uint8, device="cuda")
+    y = torch.empty_like(x)
+    x.fill_(1)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": n, "launches": 3}))
+
+
+def cpu_baseline(x, dense_flop, budget_s=12.0):
+    """Times the oracle on a bounded sample of the same workload: whole heads
+    (router + forward of every query block of the head), one after another,
+    until about `budget_s` seconds of oracle time; the whole-job CPU time is
+    the mean time per head times the number of heads."""
+    from oracle import oracle as orc
+    threads = int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or (os.cpu_count() or 1)
+    threads = max(1, threads)
+    w = x.wl
+    p = orc.problem_of(x)
+    BH = w.B * w.H
+    times = []
+    while len(times) < BH and sum(times) < budget_s:
+        bh = len(times)
+        t0 = time.perf_counter()
+        idx, _, _, _ = orc.route(p, x.q, x.k, x.wq, x.wk, heads=[bh], nthreads=threads)
+        orc.forward(p, x.q, x.k, x.v, idx, x.alpha, [(bh, i) for i in range(w.Tq)],
+                    nthreads=threads)
+        times.append(time.perf_counter() - t0)
+    t_head = sum(times) / len(times)
+    t_job = BH * t_head
+    return {
+        "value": dense_flop / t_job / 1e12,
+        "unit": "TOPS",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": (f"{len(times)} of {BH} heads, each routed and then run through the forward "
+                   f"for all {w.Tq} query blocks ({sum(times):.1f} s, {t_head:.2f} s per head); "
+                   f"whole-job CPU time extrapolated as {BH} x per-head time = {t_job:.0f} s"),
+        "sample_seconds": sum(times),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="wan14b", choices=["wan14b", "wan13b"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--fp8", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py: this build runs on one GPU only (no sharding, no collectives); "
+              "run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    if args.copy_calibration:
+        copy_calibration()
+        return
+
+    from sparse_linear_attention_amd import inputs as I
+    from sparse_linear_attention_amd import sla2 as S
+
+    S.lib()
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    w = I.WORKLOADS[args.workload]
+    log(f"bench: generating {w.name} inputs")
+    x = I.make_inputs(w)
+
+    def t(a):
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(a).to(dev)
+
+    q, k, v, wq, wk, al = t(x.q), t(x.k), t(x.v), t(x.wq), t(x.wk), t(x.alpha)
+    p = S.problem(w.B, w.H, w.N, w.d, w.bq, w.bkv, w.topk_frac, 1, w.dtype)
+    Tq, Tkv, kk = S.num_q_blocks(p), S.num_kv_blocks(p), S.topk(p)
+    idx = torch.empty((w.B, w.H, Tq, kk), dtype=torch.int32, device=dev)
+    O = torch.empty((w.B, w.H, w.N, w.d), dtype=torch.float32, device=dev)
+    ws_r = S.workspace(p, S.OP_ROUTE)
+    ws_f = S.workspace(p, S.OP_FORWARD)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        S.sla2_route(p, q, k, wq, wk, idx, None, ws_r, stream)
+        S.sla2_forward(p, q, k, v, idx, al, O, ws_f, stream)
+
+    log("bench: warmup")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    idx_host = idx.cpu().numpy().reshape(w.B * w.H, Tq, kk)
+
+    # timed region: K steps between two synchronisations, HIP events on the
+    # launch stream around the whole region and around every kernel launch
+    S.timing_start(64 * args.steps + 64)
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    kernels = S.timing_stop()
+    ms_step = ev0.elapsed_time(ev1) / args.steps
+    log(f"bench: {ms_step:.3f} ms/step (wall {1e3 * t_wall / args.steps:.3f})")
+
+    BH = w.B * w.H
+    dense = dense_equivalent_flop(w.B, w.H, w.N, w.d)
+    fl_sparse = sparse_flop(idx_host, w.N, w.d, w.bq, w.bkv)
+    fl_apply = linear_apply_flop(BH, w.N, w.d)
+    stages = {name: ms / n for name, (ms, n) in kernels.items()}
+    fused_ms = stages.get("fused_mfma")
+    fwd_ms = sum(v for kname, v in stages.items()
+                 if kname in ("summaries_mfma", "summaries_reduce", "fused_mfma"))
+    route_ms = sum(v for kname, v in stages.items()
+                   if kname in ("pool_project", "score", "topk_select"))
+
+    achieved = (fl_sparse + fl_apply) / (fused_ms * 1e-3) / 1e12
+    traffic = None
+    if os.path.exists(COUNTERS):
+        cj = json.load(open(COUNTERS))
+        if cj.get("kernel_source_sha") == kernel_source_sha() and cj.get("workload") == w.name:
+            traffic = cj.get("hbm_bytes_per_launch")
+    roofline = {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS, "traffic": traffic,
+                "kernel": "fused_mfma", "algorithmic_flop_per_launch": fl_sparse + fl_apply,
+                "avg_launch_ms": fused_ms}
+
+    qk_bytes = 2.0 * BH * w.N * w.d * 2  # one read of Q and K (router), or K and V
+    out = {
+        "metric": "dense-equivalent attention TOPS at 97% sparsity (Wan-14B-720P shape), 1 GPU"
+        if w.name == "wan14b" else "dense-equivalent attention TOPS (Wan-1.3B-480P shape), 1 GPU",
+        "value": dense / (ms_step * 1e-3) / 1e12,
+        "unit": "TOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded smooth-field Q/K, N(0,1) V; Wan2.1 latent-grid shape)",
+        "config": {"workload": f"{w.name}: B={w.B} H={w.H} N={w.N} d={w.d} b_q={w.bq} "
+                               f"b_kv={w.bkv} top-k {kk} of {Tkv} KV blocks per query block",
+                   "B": w.B, "H": w.H, "N": w.N, "d": w.d, "bq": w.bq, "bkv": w.bkv,
+                   "topk": kk, "Tq": Tq, "Tkv": Tkv},
+        "roofline": roofline,
+        "stages_ms": stages,
+        "route_ms": route_ms,
+        "forward_ms": fwd_ms,
+        "forward_only_tops": dense / (fwd_ms * 1e-3) / 1e12 if fwd_ms else None,
+        "sparse_flop_per_step": fl_sparse,
+        "sparse_fraction_of_dense": fl_sparse / dense,
+        "router_hbm_gbs": qk_bytes / ((stages.get("pool_project", 0) or 1e-9) * 1e-3) / 1e9,
+        "summaries_hbm_gbs": qk_bytes / ((stages.get("summaries_mfma", 0) or 1e-9) * 1e-3) / 1e9,
+        "kernel_source_sha": kernel_source_sha(),
+    }
+
+    if args.fp8:
+        ws8 = S.workspace(p, S.OP_FORWARD_FP8)
+
+        def step8():
+            S.sla2_route(p, q, k, wq, wk, idx, None, ws_r, stream)
+            S.sla2_forward_fp8(p, q, k, v, idx, al, O, ws8, stream)
+
+        for _ in range(args.warmup):
+            step8()
+        torch.cuda.synchronize()
+        S.timing_start(64 * args.steps + 64)
+        ev0.record(stream)
+        for _ in range(args.steps):
+            step8()
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        k8 = S.timing_stop()
+        ms8 = ev0.elapsed_time(ev1) / args.steps
+        out["fp8"] = {"ms_per_step": ms8, "tops": dense / (ms8 * 1e-3) / 1e12,
+                      "stages_ms": {n_: ms_ / c_ for n_, (ms_, c_) in k8.items()}}
+
+    if not args.no_cpu_baseline:
+        log("bench: timing the CPU oracle on a sample")
+        out["cpu_baseline"] = cpu_baseline(x, dense)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

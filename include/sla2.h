@@ -35,8 +35,10 @@
  *    SLA2_EHIP (a HIP launch error, reported right after the launch;
  *    asynchronous faults surface at the caller's next synchronisation).
  *  - Device-resident values are not inspected: Q, K, V must be finite, alpha
- *    values should lie in [0,1], and for the bf16 paths |V| < 65504 (V is
- *    carried in fp16 inside the kernels).
+ *    values should lie in [0,1], for the bf16 paths |V| < 65504 (V is
+ *    carried in fp16 inside the kernels), and every logit |q.k|/sqrt(d) must
+ *    stay below 2^20 (the softmax exponent is evaluated as one fused
+ *    multiply-add of the logit against the running maximum).
  *  - Pointers must be 16-byte aligned (ws: 256-byte aligned).
  *  - Calls on one stream are ordered; the library keeps no state between calls
  *    (except the optional timing records below), so concurrent calls on

@@ -53,6 +53,21 @@ __device__ inline int perm_pos(int u) {
     return (u & ~12) | ((u >> 1) & 4) | ((u << 1) & 8);
 }
 
+// Work-groups are dispatched round-robin over the 8 XCDs (each with its own
+// L2).  The grid is laid out as heads x (8 ranges of ceil(Tq/8) query
+// blocks); dispatch index g runs on XCD g % 8, which this map gives query
+// blocks x*R .. x*R+R-1 of one head at a time: all XCDs work on the same head
+// together (its gathered KV tiles stay in the shared last-level cache) and
+// each XCD walks a contiguous range (neighbouring query blocks share some of
+// their selected KV blocks in its L2).  Returns false for the padding slots.
+__device__ inline bool head_major_map(int g, int Tq, long* bh, int* qb) {
+    const int R = (Tq + 7) >> 3;   // query blocks per XCD and head
+    const int x = g & 7, s = g >> 3;
+    *bh = s / R;
+    *qb = x * R + s % R;
+    return *qb < Tq;
+}
+
 __device__ inline f32x16 zero16() {
     f32x16 z;
 #pragma unroll
@@ -206,8 +221,9 @@ __global__ __launch_bounds__(256, 2) void fused_mfma_kernel(
     // (matrix instructions ignore EXEC, so they may never sit under a lane mask)
     const int t = threadIdx.x, lane = t & 63, l32 = lane & 31, hl = lane >> 5;
     const int w = __builtin_amdgcn_readfirstlane(t >> 6);
-    const long bh = blockIdx.y;
-    const int qb = blockIdx.x;
+    long bh;
+    int qb;
+    if (!head_major_map(blockIdx.x, Tq, &bh, &qb)) return;
     const int tq = qb * 128 + 32 * w + l32;  // this lane's query
     const bool valid_q = tq < N;
     const bool need_lin = k < Tkv;
@@ -428,6 +444,368 @@ __global__ __launch_bounds__(256, 2) void fused_mfma_kernel(
     }
 }
 
+
+// ---------------------------------------------------------------------------
+// fused kernel, d = 128: 8 waves = 4 query groups x 2 KV halves
+// ---------------------------------------------------------------------------
+// Wave w handles queries 32*(w%4) .. +31 of the block and KV rows
+// 32*(w/4) .. +31 of every selected tile, with its own online-softmax state;
+// the two KV halves are merged once at the end.  KV tiles arrive in three
+// LDS stages through asynchronous direct-to-LDS loads issued two tiles
+// ahead.  Stage layout (48 KB): K tile [64][256 B] with 16-byte chunk c of
+// row r stored at chunk c ^ (r & 15); V^T and phi(K)^T tiles [128][128 B]
+// with chunk c of row r at chunk c ^ ((r >> 1) & 7).  Both swizzles make the
+// 32-row fragment reads bank-conflict free.
+constexpr int kStageBytes = 49152;
+__shared__ __attribute__((aligned(16))) char g_st0[kStageBytes];
+__shared__ __attribute__((aligned(16))) char g_st1[kStageBytes];
+__shared__ __attribute__((aligned(16))) char g_st2[kStageBytes];
+
+template <int S>
+__device__ inline char* stage_ptr() {
+    return S == 0 ? g_st0 : (S == 1 ? g_st1 : g_st2);
+}
+
+#define SLA2_LDS(p) ((__attribute__((address_space(3))) void*)(p))
+
+// s_waitcnt with only the vector-memory count constrained (gfx9 encoding:
+// vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8)
+template <int N>
+__device__ inline void wait_vmcnt() {
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0070 | 0x0F00);
+}
+
+// Issues the direct-to-LDS loads of KV tile j into stage S: 2 (K) + 2 (V^T)
+// [+ 2 (phi(K)^T)] 16-byte loads per lane.
+template <int S, bool LIN>
+__device__ inline void issue_tile(const uint16_t* __restrict__ Kh, const uint16_t* __restrict__ vt_h,
+                                  const uint16_t* __restrict__ pkt_h, int j, int N, int w,
+                                  int lane) {
+    char* st = stage_ptr<S>();
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int u = 2 * w + i;                 // 1 KB piece of the tile
+        const int row = 4 * u + (lane >> 4);     // K: 4 rows per piece
+        const int lc = (lane & 15) ^ (row & 15);
+        const int tok = min(j * 64 + row, N - 1);
+        __builtin_amdgcn_global_load_lds(Kh + (size_t)tok * 128 + lc * 8,
+                                         SLA2_LDS(st + u * 1024), 16, 0, 0);
+    }
+    const size_t tbase = (size_t)j * 128 * 64;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int u = 2 * w + i;
+        const int row = 8 * u + (lane >> 3);     // V^T: 8 rows per piece
+        const int lc = (lane & 7) ^ ((row >> 1) & 7);
+        __builtin_amdgcn_global_load_lds(vt_h + tbase + row * 64 + lc * 8,
+                                         SLA2_LDS(st + 16384 + u * 1024), 16, 0, 0);
+        if (LIN)
+            __builtin_amdgcn_global_load_lds(pkt_h + tbase + row * 64 + lc * 8,
+                                             SLA2_LDS(st + 32768 + u * 1024), 16, 0, 0);
+    }
+}
+
+struct WaveState {
+    f32x16 o[4];   // O^T tiles (d rows 32mt.., this wave's 32 queries)
+    f32x16 g[4];   // G^T tiles (V channels 32mt.., phi(K) channels 32*qg..)
+    float m_ref;   // log2-domain reference max of this lane's query
+    float l_part;  // row-sum over this lane's rows of this KV half
+    float zsel;    // lanes 0..15: sum of z_j[16*w + lane] over the selected tiles
+    float zp[3];   // z_j of the tiles in flight, one per LDS stage
+};
+
+// One KV tile from stage S for wave (qg, kh).
+template <int S, bool LIN>
+__device__ inline void tile_compute(WaveState& W, const bf16x8 (&qf)[8], int j, int N, int kh,
+                                    int qg, int l32, int hl, float c_log2) {
+    const char* st = stage_ptr<S>();
+    // S^T = K_half Q^T
+    f32x16 s = zero16();
+    const int krow = 32 * kh + l32;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+        const int pc = (2 * ks + hl) ^ (krow & 15);
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(st + krow * 256 + pc * 16);
+        s = mfma_bf16(a, qf[ks], s);
+    }
+    if (j * 64 + 64 > N) {  // ragged last block (uniform branch)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int kvi = 32 * kh + 8 * (i >> 2) + 4 * hl + (i & 3);
+            if (j * 64 + kvi >= N) s[i] = -INFINITY;
+        }
+    }
+    float mx = s[0];
+#pragma unroll
+    for (int i = 1; i < 16; ++i) mx = fmaxf(mx, s[i]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float xmax = mx * c_log2;
+    const bool need = xmax > W.m_ref + kRescaleThr;
+    if (__ballot(need)) {
+        const float nref = need ? xmax : W.m_ref;
+        const float f = __builtin_amdgcn_exp2f(W.m_ref - nref);
+        W.l_part *= f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) W.o[i][e] *= f;
+        W.m_ref = nref;
+    }
+    // a KV half whose rows are all padding has no reference yet: P = 0
+    const float mref = W.m_ref == -INFINITY ? 0.0f : W.m_ref;
+    f16x8 pf[2];
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            pf[q][e] = (_Float16)__builtin_amdgcn_exp2f(fmaf(s[8 * q + e], c_log2, -mref));
+    const f16x2 ones = {(_Float16)1.0f, (_Float16)1.0f};
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+            const f16x2 pr = {pf[q][e], pf[q][e + 1]};
+            W.l_part = __builtin_amdgcn_fdot2(pr, ones, W.l_part, false);
+        }
+    // O^T += V^T P^T ; G^T += V^T phi(K)
+    const char* sv = st + 16384;
+    const char* sp = st + 32768;
+    const int crow = 32 * qg + l32;
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        const int c2 = 4 * kh + 2 * q + hl;  // 16-byte chunk of the positions
+        f16x8 bk;
+        if (LIN)
+            bk = *reinterpret_cast<const f16x8*>(sp + crow * 128 + (c2 ^ ((crow >> 1) & 7)) * 16);
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+            const int erow = 32 * mt + l32;
+            const f16x8 a = *reinterpret_cast<const f16x8*>(sv + erow * 128 +
+                                                            (c2 ^ ((erow >> 1) & 7)) * 16);
+            W.o[mt] = mfma_f16(a, pf[q], W.o[mt]);
+            if (LIN) W.g[mt] = mfma_f16(a, bk, W.g[mt]);
+        }
+    }
+}
+
+template <int S, int SN, bool LIN>
+__device__ inline void tile_step(WaveState& W, const bf16x8 (&qf)[8], const int32_t* sel, int r,
+                                 int k, const uint16_t* Kh, const uint16_t* vt_h,
+                                 const uint16_t* pkt_h, const float* zb_h, int N, int w,
+                                 int lane, int kh, int qg, int l32, int hl, float c_log2) {
+    // vector-memory operations per lane and tile, issued as one group: with
+    // the linear branch one z_j load, then the direct-to-LDS loads (2 K +
+    // 2 V^T [+ 2 phi(K)^T]).  Only tile r+1's group was issued after tile r's.
+    constexpr int PER_TILE = LIN ? 7 : 4;
+    if (r + 1 < k) wait_vmcnt<PER_TILE>();
+    else wait_vmcnt<0>();
+    __builtin_amdgcn_s_barrier();  // every wave's part of tile r is in LDS
+    if (LIN) W.zsel += W.zp[S];    // z_j of tile r (older than tile r's loads)
+    if (r + 2 < k) {
+        const int jn = sel[r + 2];
+        if (LIN) W.zp[SN] = (lane < 16) ? zb_h[(size_t)jn * 128 + 16 * w + lane] : 0.0f;
+        issue_tile<SN, LIN>(Kh, vt_h, pkt_h, jn, N, w, lane);
+    }
+    tile_compute<S, LIN>(W, qf, sel[r], N, kh, qg, l32, hl, c_log2);
+}
+
+template <bool LIN>
+__global__ __launch_bounds__(512) void fused_mfma_d128_kernel(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+    const uint16_t* __restrict__ vt, const uint16_t* __restrict__ pkt,
+    const float* __restrict__ zb, const int32_t* __restrict__ idx,
+    const float* __restrict__ alpha, const float* __restrict__ hfrag,
+    const float* __restrict__ ztot, float* __restrict__ O, int N, int Tq, int Tkv, int k,
+    int H) {
+    const int t = threadIdx.x, lane = t & 63, l32 = lane & 31, hl = lane >> 5;
+    const int w = __builtin_amdgcn_readfirstlane(t >> 6);
+    const int qg = w & 3, kh = w >> 2;
+    long bh;
+    int qb;
+    if (!head_major_map(blockIdx.x, Tq, &bh, &qb)) return;
+    const int tq = qb * 128 + 32 * qg + l32;
+    const bool valid_q = tq < N;
+    const float c_log2 = 1.4426950408889634f / sqrtf(128.0f);
+
+    bf16x8 qf[8];
+    {
+        const uint16_t* qrow = Q + ((size_t)bh * N + (valid_q ? tq : 0)) * 128;
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) {
+            uint4 v = make_uint4(0, 0, 0, 0);
+            if (valid_q) v = *reinterpret_cast<const uint4*>(qrow + 16 * ks + 8 * hl);
+            qf[ks] = __builtin_bit_cast(bf16x8, v);
+        }
+    }
+    WaveState W;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        W.o[i] = zero16();
+        W.g[i] = zero16();
+    }
+    W.m_ref = -INFINITY;
+    W.l_part = 0.0f;
+    W.zsel = 0.0f;
+
+    const int32_t* sel = idx + ((size_t)bh * Tq + qb) * k;
+    const float* zb_h = zb + (size_t)bh * Tkv * 128;
+    const uint16_t* Kh = K + (size_t)bh * N * 128;
+    const uint16_t* vt_h = vt + (size_t)bh * Tkv * 128 * 64;
+    const uint16_t* pkt_h = pkt + (size_t)bh * Tkv * 128 * 64;
+
+    W.zp[0] = W.zp[1] = W.zp[2] = 0.0f;
+    for (int r = 0; r < 2 && r < k; ++r) {  // the first two tile groups
+        if (LIN) W.zp[r] = (lane < 16) ? zb_h[(size_t)sel[r] * 128 + 16 * w + lane] : 0.0f;
+        if (r == 0) issue_tile<0, LIN>(Kh, vt_h, pkt_h, sel[0], N, w, lane);
+        else issue_tile<1, LIN>(Kh, vt_h, pkt_h, sel[1], N, w, lane);
+    }
+    for (int r = 0; r < k; r += 3) {
+        tile_step<0, 2, LIN>(W, qf, sel, r, k, Kh, vt_h, pkt_h, zb_h, N, w, lane, kh, qg, l32, hl, c_log2);
+        if (r + 1 < k)
+            tile_step<1, 0, LIN>(W, qf, sel, r + 1, k, Kh, vt_h, pkt_h, zb_h, N, w, lane, kh, qg, l32, hl, c_log2);
+        if (r + 2 < k)
+            tile_step<2, 1, LIN>(W, qf, sel, r + 2, k, Kh, vt_h, pkt_h, zb_h, N, w, lane, kh, qg, l32, hl, c_log2);
+    }
+    wait_vmcnt<0>();
+    __syncthreads();
+
+    // ---- merge the two KV halves of (O, m, l): wave (qg, kh) finishes the
+    // d rows 64*kh .. 64*kh+63 (m-tiles 2kh, 2kh+1) of its queries
+    const float l_half = W.l_part + __shfl_xor(W.l_part, 32);
+    float* xo = reinterpret_cast<float*>((w < 4 ? g_st0 : g_st1) + (w & 3) * 8192);
+    float* xm = reinterpret_cast<float*>(g_st2);  // [8 waves][64 lanes][2]
+    const int other = 1 - kh;
+    const int partner = qg + 4 * other;
+    // partner's rows out
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) xo[(s2 * 16 + i) * 64 + lane] = W.o[2 * other + s2][i];
+    xm[(w * 64 + lane) * 2 + 0] = W.m_ref;
+    xm[(w * 64 + lane) * 2 + 1] = l_half;
+    __syncthreads();
+    const float* po = reinterpret_cast<const float*>((partner < 4 ? g_st0 : g_st1) + (partner & 3) * 8192);
+    const float m_p = xm[(partner * 64 + lane) * 2 + 0];
+    const float l_p = xm[(partner * 64 + lane) * 2 + 1];
+    const float m_s = W.m_ref;
+    const float m_new = fmaxf(m_s, m_p);
+    const float f_s = m_s == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m_s - m_new);
+    const float f_p = m_p == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m_p - m_new);
+    const float l_all = l_half * f_s + l_p * f_p;
+    const float inv_l = (k > 0 && l_all > 0.0f) ? 1.0f / l_all : 0.0f;
+    f32x16 os[2];
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+            os[s2][i] = (W.o[2 * kh + s2][i] * f_s + po[(s2 * 16 + i) * 64 + lane] * f_p) * inv_l;
+
+    f32x16 ol[2] = {zero16(), zero16()};
+    float inv_den = 0.0f;
+    if (LIN) {
+        // ---- G halves: H^T[e][c] = h_tot[c][e] - G^T[e][c] for e in my rows,
+        // c in the n-tile of my query group
+        __syncthreads();
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) xo[(s2 * 16 + i) * 64 + lane] = W.g[2 * other + s2][i];
+        __syncthreads();
+        f32x16 gs[2];
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+                gs[s2][i] = W.g[2 * kh + s2][i] + po[(s2 * 16 + i) * 64 + lane];
+        __syncthreads();
+        // H^T as fp16 in g_st0, row e, 16-byte chunk c' at c' ^ (e & 15)
+        char* sH = g_st0;
+        float* sZ = reinterpret_cast<float*>(g_st1);
+        // this lane's 32 values of h_tot, stored contiguously in epilogue order
+        const float4* hf = reinterpret_cast<const float4*>(
+            hfrag + (size_t)bh * 128 * 128 + ((size_t)w * 64 + lane) * 32);
+        const int c = 32 * qg + l32;
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+            for (int i4 = 0; i4 < 4; ++i4) {
+                const float4 h4 = hf[s2 * 4 + i4];
+                const float hv[4] = {h4.x, h4.y, h4.z, h4.w};
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int i = 4 * i4 + j;
+                    const int e = 32 * (2 * kh + s2) + 8 * i4 + 4 * hl + j;
+                    const int chunk = (c >> 3) ^ (e & 15);
+                    *reinterpret_cast<_Float16*>(sH + e * 256 + chunk * 16 + (c & 7) * 2) =
+                        (_Float16)(hv[j] - gs[s2][i]);
+                }
+            }
+        // Z = z_tot - sum of the selected blocks' z_j (wave w holds channels 16w..)
+        if (lane < 16) sZ[16 * w + lane] = ztot[(size_t)bh * 128 + 16 * w + lane] - W.zsel;
+        __syncthreads();
+        f16x8 pq[8];
+        float den = 0.0f;
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float x = (float)qf[ks][e];
+                const float p = x > 0.0f ? x + 1.0f : __expf(x);
+                pq[ks][e] = (_Float16)p;
+                den = fmaf(p, sZ[16 * ks + 8 * hl + e], den);
+            }
+        den += __shfl_xor(den, 32);
+        inv_den = 1.0f / den;
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) {
+            const int erow = 32 * (2 * kh + s2) + l32;
+#pragma unroll
+            for (int ks = 0; ks < 8; ++ks) {
+                const int pc = (2 * ks + hl) ^ (erow & 15);
+                const f16x8 a = *reinterpret_cast<const f16x8*>(sH + erow * 256 + pc * 16);
+                ol[s2] = mfma_f16(a, pq[ks], ol[s2]);
+            }
+        }
+    }
+    // ---- output: stage the 128 x 128 fp32 tile in LDS (rows padded to 528 B;
+    // query rows 0..63 in stage 0, 64..127 in stage 1), then store whole rows
+    __syncthreads();  // all reads of the epilogue's LDS data are done
+    {
+        const float a_h = alpha[bh % H];
+        const int qrow = 32 * qg + l32;
+        char* sO = (qrow < 64 ? g_st0 : g_st1) + (qrow & 63) * 528;
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+            for (int i4 = 0; i4 < 4; ++i4) {
+                const int e = 32 * (2 * kh + s2) + 8 * i4 + 4 * hl;
+                float4 v;
+                v.x = a_h * os[s2][4 * i4 + 0] + (1.0f - a_h) * (ol[s2][4 * i4 + 0] * inv_den);
+                v.y = a_h * os[s2][4 * i4 + 1] + (1.0f - a_h) * (ol[s2][4 * i4 + 1] * inv_den);
+                v.z = a_h * os[s2][4 * i4 + 2] + (1.0f - a_h) * (ol[s2][4 * i4 + 2] * inv_den);
+                v.w = a_h * os[s2][4 * i4 + 3] + (1.0f - a_h) * (ol[s2][4 * i4 + 3] * inv_den);
+                *reinterpret_cast<float4*>(sO + e * 4) = v;
+            }
+    }
+    __syncthreads();
+    {
+        const int nvalid = min(128, N - qb * 128);
+        float* obase = O + ((size_t)bh * N + (size_t)qb * 128) * 128;
+        // 512 threads: 16 rows of 32 x 16 B per pass; a wave stores 2 whole rows
+#pragma unroll
+        for (int pass = 0; pass < 8; ++pass) {
+            const int row = pass * 16 + (t >> 5), c4 = t & 31;
+            if (row < nvalid) {
+                const char* src = (row < 64 ? g_st0 : g_st1) + (row & 63) * 528 + c4 * 16;
+                typedef float f32x4 __attribute__((ext_vector_type(4)));
+                const f32x4 v = *reinterpret_cast<const f32x4*>(src);
+                f32x4* dst = reinterpret_cast<f32x4*>(obase + (size_t)row * 128 + c4 * 4);
+                __builtin_nontemporal_store(v, dst);
+            }
+        }
+    }
+}
+
 }  // namespace
 
 hipError_t launch_summaries_mfma(const Dims& D, const void* K, const void* V,
@@ -451,11 +829,16 @@ hipError_t launch_summaries_mfma(const Dims& D, const void* K, const void* V,
 
 hipError_t launch_fused_mfma(const Dims& D, const void* Q, const void* K, const int32_t* idx,
                              const float* alpha, float* O, const FwdWS& ws, hipStream_t s) {
-    dim3 g(D.Tq, (unsigned)D.BH);
+    // one work-group per (head, query block), Tq padded to a multiple of 8
+    dim3 g((unsigned)(((D.Tq + 7) / 8) * 8 * D.BH), 1);
     timing_before(s, K_FUSED_MFMA);
-    if (D.d == 128)
-        fused_mfma_kernel<128><<<g, 256, 0, s>>>(
-            (const uint16_t*)Q, (const uint16_t*)K, ws.vt, ws.pkt, ws.zb, idx, alpha, ws.htot,
+    if (D.d == 128 && D.k < D.Tkv)
+        fused_mfma_d128_kernel<true><<<g, 512, 0, s>>>(
+            (const uint16_t*)Q, (const uint16_t*)K, ws.vt, ws.pkt, ws.zb, idx, alpha, ws.hfrag,
+            ws.ztot, O, D.N, D.Tq, D.Tkv, D.k, D.H);
+    else if (D.d == 128)
+        fused_mfma_d128_kernel<false><<<g, 512, 0, s>>>(
+            (const uint16_t*)Q, (const uint16_t*)K, ws.vt, ws.pkt, ws.zb, idx, alpha, ws.hfrag,
             ws.ztot, O, D.N, D.Tq, D.Tkv, D.k, D.H);
     else
         fused_mfma_kernel<64><<<g, 256, 0, s>>>(

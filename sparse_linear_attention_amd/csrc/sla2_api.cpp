@@ -92,6 +92,7 @@ size_t layout_forward(const Dims& D, int op, char* base, FwdWS* ws) {
     w.hpart = carve<float>(base, off, 4 * bh * nch * d * d);
     w.zpart = carve<float>(base, off, 4 * bh * nch * d);
     w.htot = carve<float>(base, off, 4 * bh * d * d);
+    if (D.dtype == SLA2_BF16) w.hfrag = carve<float>(base, off, 4 * bh * d * d);
     w.ztot = carve<float>(base, off, 4 * bh * d);
     if (op == SLA2_OP_FORWARD_FP8) {
         w.qhat = carve<uint8_t>(base, off, bh * (size_t)D.Tq * D.bq * d);

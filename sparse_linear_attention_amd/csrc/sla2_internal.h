@@ -60,6 +60,8 @@ struct FwdWS {
     float* hpart;    // [BH][chunks][d][d] partial h per chunk
     float* zpart;    // [BH][chunks][d]
     float* htot;     // [BH][d][d]        h_tot[c][e] = sum phi(K)[.,c] V[.,e]
+    float* hfrag;    // [BH][8 waves][64 lanes][32] h_tot in the fused kernel's
+                     // per-lane epilogue order (bf16 path, d = 128)
     float* ztot;     // [BH][d]
     // low-bit inputs
     uint8_t* qhat;   // [BH][Tq*bq][d]
