@@ -30,7 +30,7 @@
  *    B/H/N <= 0, topk_frac outside [0,1] or NaN, w_heads not in {1,H});
  *    SLA2_EUNSUPPORTED (a valid but unbuilt combination: d not in {64,128},
  *    bq not in {64,128}, bkv != 64, phi other than elu+1, fp8 with fp32
- *    inputs, more than 65535 heads or a number of blocks outside the limits
+ *    inputs or with bq or d other than 128, more than 65535 heads or a number of blocks outside the limits
  *    below); SLA2_EWORKSPACE (ws_bytes smaller than sla2_workspace_bytes);
  *    SLA2_EHIP (a HIP launch error, reported right after the launch;
  *    asynchronous faults surface at the caller's next synchronisation).
@@ -141,7 +141,8 @@ sla2_status sla2_forward(const sla2_problem* p, const void* Q, const void* K,
 
 /*
  * sla2_forward_fp8 -- as sla2_forward, with the low-bit sparse branch
- * ("SLA2 深度解读" 07).  Requires dtype == SLA2_BF16 and bq == 128.
+ * ("SLA2 深度解读" 07).  Requires dtype == SLA2_BF16, bq == 128 and d == 128
+ * (SLA2_EUNSUPPORTED otherwise).
  *   mu = mean of K over the N valid tokens (per head, per channel; summed in
  *   fp64, rounded to fp32); K' = K - mu (fp32);
  *   s_K(j) = max|K'| over KV block j / 448, s_Q(i) = max|Q| over query block
@@ -152,6 +153,11 @@ sla2_status sla2_forward(const sla2_problem* p, const void* Q, const void* K,
  *   P~ = exp(logit - running max) quantised as e4m3(256 P~) / 256 before
  *   P V (V unquantised, fp16) and the row sum taken over the quantised
  *   values.  Router and linear branch are those of sla2_forward.
+ *   The fp8 matrix cores do not sum their products exactly (the error of a
+ *   dot product reaches about 2^-15 of the sum of the absolute products), so
+ *   a P~ lying that close to an e4m3 rounding midpoint may take either
+ *   neighbouring code: results agree with an exact evaluation of the same
+ *   steps up to such flips.
  * ws : sla2_workspace_bytes(p, SLA2_OP_FORWARD_FP8) bytes.
  */
 sla2_status sla2_forward_fp8(const sla2_problem* p, const void* Q, const void* K,

@@ -49,7 +49,8 @@ def lib():
         L.orc_num_blocks.argtypes = [C.c_int, C.c_int]
         L.orc_route.argtypes = [P, vp, vp, vp, vp, ip, C.c_int, ip, vp, dp, dp, C.c_int]
         L.orc_forward.argtypes = [P, vp, vp, vp, ip, vp, ip, C.c_int, dp, C.c_int]
-        L.orc_forward_fp8.argtypes = [P, vp, vp, vp, ip, vp, ip, C.c_int, C.c_int, dp, C.c_int]
+        L.orc_forward_fp8.argtypes = [P, vp, vp, vp, ip, vp, ip, C.c_int, C.c_int, dp, dp,
+                                      C.c_double, C.c_int]
         L.orc_quant_fp8.argtypes = [P, vp, vp, C.c_long, vp, vp, vp, vp, vp]
         L.orc_e4m3_encode.argtypes = [C.c_float]
         L.orc_e4m3_encode.restype = C.c_uint8
@@ -114,10 +115,14 @@ def route(p: Problem, q, k, wq, wk, heads=None, nthreads=0, want_scores=False):
 
 
 def forward(p: Problem, q, k, v, idx, alpha, blocks, nthreads=0, variant="exact",
-            quantize=True):
+            quantize=True, acc_eps=None):
     """Forward for the query blocks ``blocks`` (list of (bh, i)).
 
-    Returns out [n_blocks, bq, d] float64 (rows past N are 0)."""
+    Returns out [n_blocks, bq, d] float64 (rows past N are 0).  With acc_eps
+    (low-bit variant) also returns the per-row bound [n_blocks, bq] on the
+    effect of the P-quantisation decisions that an implementation whose
+    quantised dot products carry a relative accumulation error up to
+    acc_eps * sum|q^ k^| may round the other way."""
     L = lib()
     blocks = np.ascontiguousarray(np.asarray(blocks, np.int32).reshape(-1, 2))
     out = np.zeros((blocks.shape[0], p.bq, p.d))
@@ -128,9 +133,13 @@ def forward(p: Problem, q, k, v, idx, alpha, blocks, nthreads=0, variant="exact"
         rc = L.orc_forward(C.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(idx), _ptr(alpha),
                            _ptr(blocks), blocks.shape[0], _ptr(out), nthreads)
     else:
+        bound = np.zeros((blocks.shape[0], p.bq)) if acc_eps is not None else None
         rc = L.orc_forward_fp8(C.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(idx), _ptr(alpha),
                                _ptr(blocks), blocks.shape[0], 1 if quantize else 0,
-                               _ptr(out), nthreads)
+                               _ptr(out), _ptr(bound), float(acc_eps or 0.0), nthreads)
+        if rc != 0:
+            raise ValueError("oracle: bad block list")
+        return (out, bound) if acc_eps is not None else out
     if rc != 0:
         raise ValueError("oracle: bad block list")
     return out

@@ -426,7 +426,26 @@ typedef struct {
     int variant;           /* 0: bf16/fp32 sparse branch, 1: low bit */
     int quantize;          /* low bit: 1 = e4m3, 0 = identity quantiser */
     const quant_t* qt;     /* this head's quantised inputs (low bit) */
+    double* bound;         /* low bit, optional: [n_blocks][bq] near-midpoint bound */
+    double acc_eps;        /* relative accumulation error assumed for the bound */
 } fwd_ctx;
+
+/* Ambiguous P-quantisation decisions.  A second implementation computes the
+ * same logits with its own dot-product accumulation and exp(); when it sums
+ * the products of a quantised dot product with a relative error of at most
+ * acc_eps * sum|q^ k^|, the logit l_u and the running maximum m can each move
+ * by that much (times the block scales), and 256 P~ = 256 exp(l_u - m) by the
+ * sum of the two in relative terms, plus a few fp32 rounding steps.  A
+ * decision whose input lies that close to an e4m3 rounding midpoint may be
+ * taken the other way; it is recorded so that the effect of the other code on
+ * the output row can be bounded. */
+#define ORC_MAX_AMBIG 8192
+
+typedef struct {
+    int u;       /* token */
+    double m;    /* running max (natural log units) when it was quantised */
+    double step; /* distance to the neighbouring code value (256-scaled) */
+} ambig_t;
 
 /* Sparse branch, exact: O_s[t] = softmax(l) V over the selected tokens
    ([SLA2-zh] 04 and 08), as a two-pass max-subtracted softmax. */
@@ -466,22 +485,47 @@ static void sparse_exact(const fwd_ctx* F, int i, const int32_t* sel, int k, int
 /* Sparse branch, low bit ([SLA2-zh] 07): quantised Q^K^T with per-block
    scales, online softmax over the selected tiles in ascending order, P
    quantised per tile against the running max, V unquantised. */
+/* distance from f (> 0) to the nearest e4m3 rounding midpoint, and the
+ * size of the code step across that midpoint */
+static void e4m3_midpoint(float f, double* dist, double* step) {
+    uint8_t c = orc_e4m3_encode(f);
+    double v = orc_e4m3_decode(c);
+    double best = INFINITY, st = 0.0;
+    if (c > 0) {
+        double lo = orc_e4m3_decode((uint8_t)(c - 1));
+        double d = fabs((double)f - 0.5 * (lo + v));
+        if (d < best) { best = d; st = v - lo; }
+    }
+    if (c < 0x7E) {
+        double hi = orc_e4m3_decode((uint8_t)(c + 1));
+        double d = fabs((double)f - 0.5 * (v + hi));
+        if (d < best) { best = d; st = hi - v; }
+    }
+    *dist = best;
+    *step = st;
+}
+
 static void sparse_lowbit(const fwd_ctx* F, int i, const int32_t* sel, int k, int t,
-                          double* os, double* lbuf) {
+                          double* os, double* lbuf, double* bound) {
     const orc_problem* p = F->p;
     int d = p->d;
     double inv = 1.0 / sqrt((double)d);
     const quant_t* Qt = F->qt;
     for (int e = 0; e < d; ++e) os[e] = 0.0;
+    if (bound) *bound = 0.0;
     if (k == 0) return;
+    ambig_t* amb = bound ? (ambig_t*)malloc(sizeof(ambig_t) * ORC_MAX_AMBIG) : NULL;
+    double abuf[512];
+    int n_amb = 0;
     double m = -INFINITY, l = 0.0;
+    double mA = 0.0; /* largest logit movement seen so far: bounds the max's */
     for (int r = 0; r < k; ++r) {
         int j = sel[r];
         int t0 = j * p->bkv, n = p->N - t0 < p->bkv ? p->N - t0 : p->bkv;
         double sc = (double)Qt->sq[i] * (double)Qt->sk[j] * inv;
         double mt = -INFINITY;
         for (int u = t0; u < t0 + n; ++u) {
-            double s = 0.0;
+            double s = 0.0, sa = 0.0;
             for (int c = 0; c < d; ++c) {
                 double a, b;
                 if (F->quantize) {
@@ -492,10 +536,13 @@ static void sparse_lowbit(const fwd_ctx* F, int i, const int32_t* sel, int k, in
                     b = (elem(p, F->K, F->bh, u, c) - (double)Qt->mu[c]) / (double)Qt->sk[j];
                 }
                 s += a * b;
+                sa += fabs(a * b);
             }
             s *= sc;
             lbuf[u - t0] = s;
+            abuf[u - t0] = F->acc_eps * sa * sc; /* how far l_u may move */
             if (s > mt) mt = s;
+            if (abuf[u - t0] > mA) mA = abuf[u - t0];
         }
         double mn = mt > m ? mt : m;
         double resc = (m == -INFINITY) ? 0.0 : exp(m - mn);
@@ -507,6 +554,21 @@ static void sparse_lowbit(const fwd_ctx* F, int i, const int32_t* sel, int k, in
             if (F->quantize) {
                 float f = (float)(256.0 * pt);
                 ph = (double)orc_e4m3_decode(orc_e4m3_encode(f)) / 256.0;
+                if (amb && f > 0.0f) {
+                    double dist, step;
+                    e4m3_midpoint(f, &dist, &step);
+                    /* relative movement of 256 P~: logit and max, then the
+                       fp32 rounding of the exponent argument (magnitude up
+                       to |m| + 8 in log2 units) and of exp2 itself */
+                    double win = abuf[u - t0] + mA +
+                                 ldexp(fabs(mn) * 1.4426950408889634 + 16.0, -21) + ldexp(1.0, -21);
+                    if (dist <= win * (double)f && n_amb < ORC_MAX_AMBIG) {
+                        amb[n_amb].u = u;
+                        amb[n_amb].m = mn;
+                        amb[n_amb].step = step;
+                        ++n_amb;
+                    }
+                }
             } else {
                 ph = pt;
             }
@@ -516,6 +578,23 @@ static void sparse_lowbit(const fwd_ctx* F, int i, const int32_t* sel, int k, in
         m = mn;
     }
     for (int e = 0; e < d; ++e) os[e] /= l;
+    if (amb) {
+        /* moving one ambiguous P^ by its code step changes O_s by at most
+           (step/256) e^(m_q - m) / l * max_e |V_u - O_s| (to first order; a
+           factor 2 covers the change of l) */
+        double b = 0.0;
+        for (int a = 0; a < n_amb; ++a) {
+            double wgt = amb[a].step / 256.0 * exp(amb[a].m - m) / l;
+            double dv = 0.0;
+            for (int e = 0; e < d; ++e) {
+                double x = fabs(elem(p, F->V, F->bh, amb[a].u, e) - os[e]);
+                if (x > dv) dv = x;
+            }
+            b += 2.0 * wgt * dv;
+        }
+        *bound = b;
+        free(amb);
+    }
 }
 
 static void forward_block(void* vctx, long it) {
@@ -553,8 +632,10 @@ static void forward_block(void* vctx, long it) {
     for (int t = t0; t < t0 + nq; ++t) {
         double* o = out + (size_t)(t - t0) * d;
         /* step 6: sparse branch */
+        double* bnd = F->bound ? F->bound + (size_t)pos * p->bq + (t - t0) : NULL;
         if (F->variant == 0) sparse_exact(F, i, sel, k, t, os, lbuf);
-        else sparse_lowbit(F, i, sel, k, t, os, lbuf);
+        else sparse_lowbit(F, i, sel, k, t, os, lbuf, bnd);
+        if (bnd) *bnd *= a; /* the combine scales O_s by alpha */
         /* step 7: linear branch O_l = phi(q) H_i / (phi(q) . Z_i) */
         for (int c = 0; c < d; ++c) pq[c] = phi(elem(p, F->Q, F->bh, t, c));
         if (n_unsel > 0) {
@@ -581,7 +662,7 @@ static void forward_block(void* vctx, long it) {
 static int forward_common(const orc_problem* p, const void* Q, const void* K, const void* V,
                           const int32_t* idx, const float* alpha, const int32_t* blocks,
                           int n_blocks, double* out, int nthreads, int variant,
-                          int quantize) {
+                          int quantize, double* bound, double acc_eps) {
     int d = p->d, Tq = ceil_div(p->N, p->bq), Tkv = ceil_div(p->N, p->bkv);
     int k = orc_topk(p);
     long nbh = (long)p->B * p->H;
@@ -616,7 +697,7 @@ static int forward_common(const orc_problem* p, const void* Q, const void* K, co
             quant_head(p, Q, K, bh, &qt);
         }
         fwd_ctx F = {p, Q, K, V, idx, alpha, blocks, out, bh, items, h, z,
-                     variant, quantize, &qt};
+                     variant, quantize, &qt, bound, acc_eps};
         run_pool(forward_block, &F, n_it, nthreads);
         free(h);
         free(z);
@@ -639,13 +720,21 @@ static int forward_common(const orc_problem* p, const void* Q, const void* K, co
 int orc_forward(const orc_problem* p, const void* Q, const void* K, const void* V,
                 const int32_t* idx, const float* alpha, const int32_t* blocks,
                 int n_blocks, double* out, int nthreads) {
-    return forward_common(p, Q, K, V, idx, alpha, blocks, n_blocks, out, nthreads, 0, 1);
+    return forward_common(p, Q, K, V, idx, alpha, blocks, n_blocks, out, nthreads, 0, 1, NULL,
+                          0.0);
 }
 
-/* Forward with the low-bit sparse branch (quantize=1: e4m3; 0: identity). */
+/* Forward with the low-bit sparse branch (quantize=1: e4m3; 0: identity).
+ * bound (optional, [n_blocks][bq]): per output row, a bound on how far the
+ * row can move if the P-quantisation decisions that an implementation with
+ * relative dot-product accumulation error acc_eps could take the other way
+ * are all flipped (0 for rows without such a decision). */
 int orc_forward_fp8(const orc_problem* p, const void* Q, const void* K, const void* V,
                     const int32_t* idx, const float* alpha, const int32_t* blocks,
-                    int n_blocks, int quantize, double* out, int nthreads) {
+                    int n_blocks, int quantize, double* out, double* bound, double acc_eps,
+                    int nthreads) {
+    if (bound) memset(bound, 0, sizeof(double) * (size_t)n_blocks * p->bq);
+    if (p->bkv > 512) return -2;
     return forward_common(p, Q, K, V, idx, alpha, blocks, n_blocks, out, nthreads, 1,
-                          quantize);
+                          quantize, bound, acc_eps);
 }

@@ -475,21 +475,49 @@ __device__ inline void wait_vmcnt() {
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0070 | 0x0F00);
 }
 
-// Issues the direct-to-LDS loads of KV tile j into stage S: 2 (K) + 2 (V^T)
-// [+ 2 (phi(K)^T)] 16-byte loads per lane.
-template <int S, bool LIN>
-__device__ inline void issue_tile(const uint16_t* __restrict__ Kh, const uint16_t* __restrict__ vt_h,
+// s_barrier without the memory fence of __syncthreads (which would also
+// wait for the prefetch in flight); the empty asm keeps the compiler from
+// moving memory accesses across it.  LDS writes that other waves read after
+// it must be complete first (wait_lgkm0).
+__device__ inline void wg_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+__device__ inline void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+// e4m3 x e4m3 -> fp32 matrix product (32x32x64); E8M0 scale 127 = 1.0
+__device__ inline f32x16 mfma_fp8(i32x8 a, i32x8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+}
+
+// Issues the direct-to-LDS loads of KV tile j into stage S: K (bf16: 2 per
+// lane) or Khat (e4m3: 1), V^T (2) and, with the linear branch, phi(K)^T (2).
+// The Khat tile uses rows of 128 B with the V^T swizzle.
+template <int S, bool LIN, bool LOWBIT>
+__device__ inline void issue_tile(const void* __restrict__ Kh, const uint16_t* __restrict__ vt_h,
                                   const uint16_t* __restrict__ pkt_h, int j, int N, int w,
                                   int lane) {
     char* st = stage_ptr<S>();
+    if (LOWBIT) {
+        const int row = 8 * w + (lane >> 3);
+        const int lc = (lane & 7) ^ ((row >> 1) & 7);
+        __builtin_amdgcn_global_load_lds(
+            reinterpret_cast<const uint8_t*>(Kh) + ((size_t)j * 64 + row) * 128 + lc * 16,
+            SLA2_LDS(st + w * 1024), 16, 0, 0);
+    } else {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const int u = 2 * w + i;                 // 1 KB piece of the tile
-        const int row = 4 * u + (lane >> 4);     // K: 4 rows per piece
-        const int lc = (lane & 15) ^ (row & 15);
-        const int tok = min(j * 64 + row, N - 1);
-        __builtin_amdgcn_global_load_lds(Kh + (size_t)tok * 128 + lc * 8,
-                                         SLA2_LDS(st + u * 1024), 16, 0, 0);
+        for (int i = 0; i < 2; ++i) {
+            const int u = 2 * w + i;                 // 1 KB piece of the tile
+            const int row = 4 * u + (lane >> 4);     // K: 4 rows per piece
+            const int lc = (lane & 15) ^ (row & 15);
+            const int tok = min(j * 64 + row, N - 1);
+            __builtin_amdgcn_global_load_lds(
+                reinterpret_cast<const uint16_t*>(Kh) + (size_t)tok * 128 + lc * 8,
+                SLA2_LDS(st + u * 1024), 16, 0, 0);
+        }
     }
     const size_t tbase = (size_t)j * 128 * 64;
 #pragma unroll
@@ -514,19 +542,38 @@ struct WaveState {
     float zp[3];   // z_j of the tiles in flight, one per LDS stage
 };
 
-// One KV tile from stage S for wave (qg, kh).
-template <int S, bool LIN>
-__device__ inline void tile_compute(WaveState& W, const bf16x8 (&qf)[8], int j, int N, int kh,
-                                    int qg, int l32, int hl, float c_log2) {
-    const char* st = stage_ptr<S>();
-    // S^T = K_half Q^T
+// Q operand of Q K^T for this lane: bf16 (8 k-steps of 16) or e4m3 (2 of 64)
+template <bool LOWBIT> struct QOperand;
+template <> struct QOperand<false> { bf16x8 f[8]; };
+template <> struct QOperand<true> { i32x8 f[2]; };
+
+// One KV tile from stage S for wave (qg, kh).  c_tile converts a raw
+// product to log2 units (1/sqrt(d) log2(e), times s_Q s_K for the low bit).
+template <int S, bool LIN, bool LOWBIT>
+__device__ inline void tile_compute(WaveState& W, const QOperand<LOWBIT>& Qo, int j, int N,
+                                    int w, int kh, int qg, int lane, int l32, int hl,
+                                    float c_tile) {
+    char* st = stage_ptr<S>();
     f32x16 s = zero16();
     const int krow = 32 * kh + l32;
+    if (LOWBIT) {  // S^T = Khat_half Qhat^T on the fp8 matrix cores
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
-        const int pc = (2 * ks + hl) ^ (krow & 15);
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(st + krow * 256 + pc * 16);
-        s = mfma_bf16(a, qf[ks], s);
+        for (int ks = 0; ks < 2; ++ks) {
+            const int c0 = 4 * ks + 2 * hl, sw = (krow >> 1) & 7;
+            const uint4 lo = *reinterpret_cast<const uint4*>(st + krow * 128 + ((c0) ^ sw) * 16);
+            const uint4 hi = *reinterpret_cast<const uint4*>(st + krow * 128 + ((c0 + 1) ^ sw) * 16);
+            i32x8 a;
+            a[0] = lo.x; a[1] = lo.y; a[2] = lo.z; a[3] = lo.w;
+            a[4] = hi.x; a[5] = hi.y; a[6] = hi.z; a[7] = hi.w;
+            s = mfma_fp8(a, reinterpret_cast<const i32x8*>(Qo.f)[ks], s);
+        }
+    } else {  // S^T = K_half Q^T
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) {
+            const int pc = (2 * ks + hl) ^ (krow & 15);
+            const bf16x8 a = *reinterpret_cast<const bf16x8*>(st + krow * 256 + pc * 16);
+            s = mfma_bf16(a, reinterpret_cast<const bf16x8*>(Qo.f)[ks], s);
+        }
     }
     if (j * 64 + 64 > N) {  // ragged last block (uniform branch)
 #pragma unroll
@@ -539,8 +586,17 @@ __device__ inline void tile_compute(WaveState& W, const bf16x8 (&qf)[8], int j, 
 #pragma unroll
     for (int i = 1; i < 16; ++i) mx = fmaxf(mx, s[i]);
     mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float xmax = mx * c_log2;
-    const bool need = xmax > W.m_ref + kRescaleThr;
+    if (LOWBIT) {
+        // P is quantised against the running maximum over whole tiles: the
+        // two KV halves of a query group exchange their maxima
+        float* xt = reinterpret_cast<float*>(st + 8192);  // [8 waves][64 lanes]
+        xt[w * 64 + lane] = mx;
+        wait_lgkm0();
+        wg_barrier();
+        mx = fmaxf(mx, xt[((w + 4) & 7) * 64 + lane]);
+    }
+    const float xmax = mx * c_tile;
+    const bool need = LOWBIT ? (xmax > W.m_ref) : (xmax > W.m_ref + kRescaleThr);
     if (__ballot(need)) {
         const float nref = need ? xmax : W.m_ref;
         const float f = __builtin_amdgcn_exp2f(W.m_ref - nref);
@@ -554,11 +610,28 @@ __device__ inline void tile_compute(WaveState& W, const bf16x8 (&qf)[8], int j, 
     // a KV half whose rows are all padding has no reference yet: P = 0
     const float mref = W.m_ref == -INFINITY ? 0.0f : W.m_ref;
     f16x8 pf[2];
+    if (LOWBIT) {
+        // 256 P~ rounded onto the e4m3 grid (P~ <= 1), carried exactly in fp16
+        const float bias = 8.0f - mref;
 #pragma unroll
-    for (int q = 0; q < 2; ++q)
+        for (int q = 0; q < 2; ++q)
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
-            pf[q][e] = (_Float16)__builtin_amdgcn_exp2f(fmaf(s[8 * q + e], c_log2, -mref));
+            for (int e = 0; e < 8; e += 2) {
+                const float p0 = __builtin_amdgcn_exp2f(fmaf(s[8 * q + e], c_tile, bias));
+                const float p1 = __builtin_amdgcn_exp2f(fmaf(s[8 * q + e + 1], c_tile, bias));
+                const int code = __builtin_amdgcn_cvt_pk_fp8_f32(fminf(p0, 448.0f),
+                                                                 fminf(p1, 448.0f), 0, false);
+                const auto back = __builtin_amdgcn_cvt_pk_f32_fp8(code, false);
+                pf[q][e] = (_Float16)back[0];
+                pf[q][e + 1] = (_Float16)back[1];
+            }
+    } else {
+#pragma unroll
+        for (int q = 0; q < 2; ++q)
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                pf[q][e] = (_Float16)__builtin_amdgcn_exp2f(fmaf(s[8 * q + e], c_tile, -mref));
+    }
     const f16x2 ones = {(_Float16)1.0f, (_Float16)1.0f};
 #pragma unroll
     for (int q = 0; q < 2; ++q)
@@ -588,34 +661,40 @@ __device__ inline void tile_compute(WaveState& W, const bf16x8 (&qf)[8], int j, 
     }
 }
 
-template <int S, int SN, bool LIN>
-__device__ inline void tile_step(WaveState& W, const bf16x8 (&qf)[8], const int32_t* sel, int r,
-                                 int k, const uint16_t* Kh, const uint16_t* vt_h,
-                                 const uint16_t* pkt_h, const float* zb_h, int N, int w,
-                                 int lane, int kh, int qg, int l32, int hl, float c_log2) {
+template <int S, int SN, bool LIN, bool LOWBIT>
+__device__ inline void tile_step(WaveState& W, const QOperand<LOWBIT>& Qo, const int32_t* sel,
+                                 int r, int k, const void* Kh, const uint16_t* vt_h,
+                                 const uint16_t* pkt_h, const float* zb_h, const float* sk_h,
+                                 int N, int w, int lane, int kh, int qg, int l32, int hl,
+                                 float c_base) {
     // vector-memory operations per lane and tile, issued as one group: with
-    // the linear branch one z_j load, then the direct-to-LDS loads (2 K +
-    // 2 V^T [+ 2 phi(K)^T]).  Only tile r+1's group was issued after tile r's.
-    constexpr int PER_TILE = LIN ? 7 : 4;
+    // the linear branch one z_j load, then the direct-to-LDS loads (K: 2 or
+    // Khat: 1, V^T: 2 [, phi(K)^T: 2]).  Only tile r+1's group was issued
+    // after tile r's.
+    constexpr int PER_TILE = (LOWBIT ? 1 : 2) + 2 + (LIN ? 3 : 0);
     if (r + 1 < k) wait_vmcnt<PER_TILE>();
     else wait_vmcnt<0>();
-    __builtin_amdgcn_s_barrier();  // every wave's part of tile r is in LDS
+    wg_barrier();  // every wave's part of tile r is in LDS
     if (LIN) W.zsel += W.zp[S];    // z_j of tile r (older than tile r's loads)
     if (r + 2 < k) {
         const int jn = sel[r + 2];
         if (LIN) W.zp[SN] = (lane < 16) ? zb_h[(size_t)jn * 128 + 16 * w + lane] : 0.0f;
-        issue_tile<SN, LIN>(Kh, vt_h, pkt_h, jn, N, w, lane);
+        issue_tile<SN, LIN, LOWBIT>(Kh, vt_h, pkt_h, jn, N, w, lane);
     }
-    tile_compute<S, LIN>(W, qf, sel[r], N, kh, qg, l32, hl, c_log2);
+    const int j = sel[r];
+    const float c_tile = LOWBIT ? c_base * sk_h[j] : c_base;
+    tile_compute<S, LIN, LOWBIT>(W, Qo, j, N, w, kh, qg, lane, l32, hl, c_tile);
 }
 
-template <bool LIN>
+template <bool LIN, bool LOWBIT>
 __global__ __launch_bounds__(512) void fused_mfma_d128_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ vt, const uint16_t* __restrict__ pkt,
     const float* __restrict__ zb, const int32_t* __restrict__ idx,
     const float* __restrict__ alpha, const float* __restrict__ hfrag,
-    const float* __restrict__ ztot, float* __restrict__ O, int N, int Tq, int Tkv, int k,
+    const float* __restrict__ ztot, const uint8_t* __restrict__ qhat,
+    const uint8_t* __restrict__ khat, const float* __restrict__ sq,
+    const float* __restrict__ sk, float* __restrict__ O, int N, int Tq, int Tkv, int k,
     int H) {
     const int t = threadIdx.x, lane = t & 63, l32 = lane & 31, hl = lane >> 5;
     const int w = __builtin_amdgcn_readfirstlane(t >> 6);
@@ -627,14 +706,29 @@ __global__ __launch_bounds__(512) void fused_mfma_d128_kernel(
     const bool valid_q = tq < N;
     const float c_log2 = 1.4426950408889634f / sqrtf(128.0f);
 
-    bf16x8 qf[8];
-    {
+    // Q operand: lane holds row tq, k-chunk 8*hl.. of every 16 (bf16) or
+    // 32*hl.. of every 64 (e4m3)
+    QOperand<LOWBIT> Qo;
+    float c_base = c_log2;
+    if (LOWBIT) {
+        const uint8_t* qrow = qhat + ((size_t)bh * Tq * 128 + (size_t)qb * 128 + 32 * qg + l32) * 128;
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            const uint4 lo = *reinterpret_cast<const uint4*>(qrow + 64 * ks + 32 * hl);
+            const uint4 hi = *reinterpret_cast<const uint4*>(qrow + 64 * ks + 32 * hl + 16);
+            i32x8 v;
+            v[0] = lo.x; v[1] = lo.y; v[2] = lo.z; v[3] = lo.w;
+            v[4] = hi.x; v[5] = hi.y; v[6] = hi.z; v[7] = hi.w;
+            reinterpret_cast<i32x8*>(Qo.f)[ks] = v;
+        }
+        c_base = c_log2 * sq[bh * Tq + qb];
+    } else {
         const uint16_t* qrow = Q + ((size_t)bh * N + (valid_q ? tq : 0)) * 128;
 #pragma unroll
         for (int ks = 0; ks < 8; ++ks) {
             uint4 v = make_uint4(0, 0, 0, 0);
             if (valid_q) v = *reinterpret_cast<const uint4*>(qrow + 16 * ks + 8 * hl);
-            qf[ks] = __builtin_bit_cast(bf16x8, v);
+            reinterpret_cast<bf16x8*>(Qo.f)[ks] = __builtin_bit_cast(bf16x8, v);
         }
     }
     WaveState W;
@@ -649,26 +743,30 @@ __global__ __launch_bounds__(512) void fused_mfma_d128_kernel(
 
     const int32_t* sel = idx + ((size_t)bh * Tq + qb) * k;
     const float* zb_h = zb + (size_t)bh * Tkv * 128;
-    const uint16_t* Kh = K + (size_t)bh * N * 128;
+    const float* sk_h = LOWBIT ? sk + (size_t)bh * Tkv : nullptr;
+    const void* Kh = LOWBIT ? (const void*)(khat + (size_t)bh * Tkv * 64 * 128)
+                            : (const void*)(K + (size_t)bh * N * 128);
     const uint16_t* vt_h = vt + (size_t)bh * Tkv * 128 * 64;
     const uint16_t* pkt_h = pkt + (size_t)bh * Tkv * 128 * 64;
 
     W.zp[0] = W.zp[1] = W.zp[2] = 0.0f;
     for (int r = 0; r < 2 && r < k; ++r) {  // the first two tile groups
         if (LIN) W.zp[r] = (lane < 16) ? zb_h[(size_t)sel[r] * 128 + 16 * w + lane] : 0.0f;
-        if (r == 0) issue_tile<0, LIN>(Kh, vt_h, pkt_h, sel[0], N, w, lane);
-        else issue_tile<1, LIN>(Kh, vt_h, pkt_h, sel[1], N, w, lane);
+        if (r == 0) issue_tile<0, LIN, LOWBIT>(Kh, vt_h, pkt_h, sel[0], N, w, lane);
+        else issue_tile<1, LIN, LOWBIT>(Kh, vt_h, pkt_h, sel[1], N, w, lane);
     }
     for (int r = 0; r < k; r += 3) {
-        tile_step<0, 2, LIN>(W, qf, sel, r, k, Kh, vt_h, pkt_h, zb_h, N, w, lane, kh, qg, l32, hl, c_log2);
+        tile_step<0, 2, LIN, LOWBIT>(W, Qo, sel, r, k, Kh, vt_h, pkt_h, zb_h, sk_h, N, w, lane,
+                                     kh, qg, l32, hl, c_base);
         if (r + 1 < k)
-            tile_step<1, 0, LIN>(W, qf, sel, r + 1, k, Kh, vt_h, pkt_h, zb_h, N, w, lane, kh, qg, l32, hl, c_log2);
+            tile_step<1, 0, LIN, LOWBIT>(W, Qo, sel, r + 1, k, Kh, vt_h, pkt_h, zb_h, sk_h, N, w,
+                                         lane, kh, qg, l32, hl, c_base);
         if (r + 2 < k)
-            tile_step<2, 1, LIN>(W, qf, sel, r + 2, k, Kh, vt_h, pkt_h, zb_h, N, w, lane, kh, qg, l32, hl, c_log2);
+            tile_step<2, 1, LIN, LOWBIT>(W, Qo, sel, r + 2, k, Kh, vt_h, pkt_h, zb_h, sk_h, N, w,
+                                         lane, kh, qg, l32, hl, c_base);
     }
     wait_vmcnt<0>();
     __syncthreads();
-
     // ---- merge the two KV halves of (O, m, l): wave (qg, kh) finishes the
     // d rows 64*kh .. 64*kh+63 (m-tiles 2kh, 2kh+1) of its queries
     const float l_half = W.l_part + __shfl_xor(W.l_part, 32);
@@ -743,13 +841,27 @@ __global__ __launch_bounds__(512) void fused_mfma_d128_kernel(
         // Z = z_tot - sum of the selected blocks' z_j (wave w holds channels 16w..)
         if (lane < 16) sZ[16 * w + lane] = ztot[(size_t)bh * 128 + 16 * w + lane] - W.zsel;
         __syncthreads();
+        // phi(Q)^T operand from the raw bf16 Q (registers on the bf16 path)
+        bf16x8 qraw[8];
+        if (LOWBIT) {
+            const uint16_t* qrow = Q + ((size_t)bh * N + (valid_q ? tq : 0)) * 128;
+#pragma unroll
+            for (int ks = 0; ks < 8; ++ks) {
+                uint4 v = make_uint4(0, 0, 0, 0);
+                if (valid_q) v = *reinterpret_cast<const uint4*>(qrow + 16 * ks + 8 * hl);
+                qraw[ks] = __builtin_bit_cast(bf16x8, v);
+            }
+        } else {
+#pragma unroll
+            for (int ks = 0; ks < 8; ++ks) qraw[ks] = reinterpret_cast<const bf16x8*>(Qo.f)[ks];
+        }
         f16x8 pq[8];
         float den = 0.0f;
 #pragma unroll
         for (int ks = 0; ks < 8; ++ks)
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                const float x = (float)qf[ks][e];
+                const float x = (float)qraw[ks][e];
                 const float p = x > 0.0f ? x + 1.0f : __expf(x);
                 pq[ks][e] = (_Float16)p;
                 den = fmaf(p, sZ[16 * ks + 8 * hl + e], den);
@@ -833,13 +945,13 @@ hipError_t launch_fused_mfma(const Dims& D, const void* Q, const void* K, const 
     dim3 g((unsigned)(((D.Tq + 7) / 8) * 8 * D.BH), 1);
     timing_before(s, K_FUSED_MFMA);
     if (D.d == 128 && D.k < D.Tkv)
-        fused_mfma_d128_kernel<true><<<g, 512, 0, s>>>(
+        fused_mfma_d128_kernel<true, false><<<g, 512, 0, s>>>(
             (const uint16_t*)Q, (const uint16_t*)K, ws.vt, ws.pkt, ws.zb, idx, alpha, ws.hfrag,
-            ws.ztot, O, D.N, D.Tq, D.Tkv, D.k, D.H);
+            ws.ztot, nullptr, nullptr, nullptr, nullptr, O, D.N, D.Tq, D.Tkv, D.k, D.H);
     else if (D.d == 128)
-        fused_mfma_d128_kernel<false><<<g, 512, 0, s>>>(
+        fused_mfma_d128_kernel<false, false><<<g, 512, 0, s>>>(
             (const uint16_t*)Q, (const uint16_t*)K, ws.vt, ws.pkt, ws.zb, idx, alpha, ws.hfrag,
-            ws.ztot, O, D.N, D.Tq, D.Tkv, D.k, D.H);
+            ws.ztot, nullptr, nullptr, nullptr, nullptr, O, D.N, D.Tq, D.Tkv, D.k, D.H);
     else
         fused_mfma_kernel<64><<<g, 256, 0, s>>>(
             (const uint16_t*)Q, (const uint16_t*)K, ws.vt, ws.pkt, ws.zb, idx, alpha, ws.htot,
@@ -848,4 +960,22 @@ hipError_t launch_fused_mfma(const Dims& D, const void* Q, const void* K, const 
     return hipGetLastError();
 }
 
+}  // namespace sla2
+
+namespace sla2 {
+hipError_t launch_fused_fp8(const Dims& D, const void* Q, const int32_t* idx, const float* alpha,
+                            float* O, const FwdWS& ws, hipStream_t s) {
+    dim3 g((unsigned)(((D.Tq + 7) / 8) * 8 * D.BH), 1);
+    timing_before(s, K_FUSED_FP8);
+    if (D.k < D.Tkv)
+        fused_mfma_d128_kernel<true, true><<<g, 512, 0, s>>>(
+            (const uint16_t*)Q, nullptr, ws.vt, ws.pkt, ws.zb, idx, alpha, ws.hfrag, ws.ztot,
+            ws.qhat, ws.khat, ws.sq, ws.sk, O, D.N, D.Tq, D.Tkv, D.k, D.H);
+    else
+        fused_mfma_d128_kernel<false, true><<<g, 512, 0, s>>>(
+            (const uint16_t*)Q, nullptr, ws.vt, ws.pkt, ws.zb, idx, alpha, ws.hfrag, ws.ztot,
+            ws.qhat, ws.khat, ws.sq, ws.sk, O, D.N, D.Tq, D.Tkv, D.k, D.H);
+    timing_after(s, K_FUSED_FP8);
+    return hipGetLastError();
+}
 }  // namespace sla2

@@ -37,7 +37,7 @@ static sla2_status make_dims(const sla2_problem* p, int op, Dims* D) {
     if (p->bq != 64 && p->bq != 128) return SLA2_EUNSUPPORTED;
     if (p->bkv != 64) return SLA2_EUNSUPPORTED;
     if (p->phi != SLA2_PHI_ELU1) return SLA2_EUNSUPPORTED;
-    if (op == SLA2_OP_FORWARD_FP8 && (p->dtype != SLA2_BF16 || p->bq != 128))
+    if (op == SLA2_OP_FORWARD_FP8 && (p->dtype != SLA2_BF16 || p->bq != 128 || p->d != 128))
         return SLA2_EUNSUPPORTED;
     long bh = (long)p->B * p->H;
     if (bh > 65535) return SLA2_EUNSUPPORTED;
@@ -100,6 +100,7 @@ size_t layout_forward(const Dims& D, int op, char* base, FwdWS* ws) {
         w.sq = carve<float>(base, off, 4 * bh * D.Tq);
         w.sk = carve<float>(base, off, 4 * bh * D.Tkv);
         w.mu = carve<float>(base, off, 4 * bh * d);
+        w.ksum = carve<double>(base, off, 8 * bh * ((D.N + 1023) / 1024) * d);
     }
     if (ws) *ws = w;
     return align256(off);

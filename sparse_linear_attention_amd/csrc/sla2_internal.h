@@ -69,6 +69,7 @@ struct FwdWS {
     float* sq;       // [BH][Tq]
     float* sk;       // [BH][Tkv]
     float* mu;       // [BH][d]
+    double* ksum;    // [BH][ceil(N/1024)][d] partial column sums of K
 };
 
 // Lays out the workspace of `op` starting at `base` (may be null to size

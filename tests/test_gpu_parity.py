@@ -70,19 +70,62 @@ def check_route(orc, x, idx, mask, heads=None):
     return oidx
 
 
+# Relative accumulation error of the e4m3 matrix-core dot products of the
+# low-bit logits, |computed - exact| <= FP8_ACC_EPS * sum |q^_c k^_c|.  The
+# gfx950 fp8 MFMA does not sum its 64 products exactly: over 2 x 2^19 dot
+# products of length 128 of absmax-scaled Gaussian codes (independent and
+# correlated rows; tests/probes/fp8_mfma_accuracy.hip) the largest error was
+# 2^-15.35 of sum|ab|, and only 6-10 % of the results were exact; 2^-14 leaves
+# a factor 2.6.  Uniformly random codes over all exponents reach 2^-11.9, a
+# dynamic range that absmax-scaled blocks do not have.
+FP8_ACC_EPS = 2.0 ** -14
+# Low-bit bulk agreement: 90 % of the rows within 3e-4, 99 % within 5e-3.
+FP8_BULK = (3e-4, 5e-3)
+
+
 def compare_blocks(orc, x, oidx, O, blocks, tol, variant="exact"):
+    """Element-wise comparison on whole query blocks.  For the low-bit
+    variant a row may also move by the oracle's per-row bound: a P value
+    whose 256 P~ lies closer to an e4m3 rounding midpoint than the logit
+    error of the matrix-core accumulation (FP8_ACC_EPS) can reach may be
+    rounded to either neighbouring code, and both are correct results; the
+    bound is the largest effect of such flips on the row (0 for rows without
+    such a decision).  On top of that the bulk of the rows must agree to
+    FP8_BULK, which no flip-free difference comes near."""
     op = orc.problem_of(x)
-    ref = orc.forward(op, x.q, x.k, x.v, oidx, x.alpha, blocks, variant=variant)
+    if variant == "fp8":
+        ref, bound = orc.forward(op, x.q, x.k, x.v, oidx, x.alpha, blocks, variant=variant,
+                                 acc_eps=FP8_ACC_EPS)
+    else:
+        ref, bound = orc.forward(op, x.q, x.k, x.v, oidx, x.alpha, blocks), None
     w = x.wl
     Oc = O.cpu().numpy().reshape(w.B * w.H, w.N, w.d)
-    worst = 0.0
+    errs, bnds = [], []
     for n, (bh, i) in enumerate(blocks):
         t0 = i * w.bq
         nv = min(w.bq, w.N - t0)
-        err = np.abs(Oc[bh, t0:t0 + nv] - ref[n, :nv]).max()
-        worst = max(worst, float(err))
-    say(f"  max-abs error over {len(blocks)} blocks: {worst:.3e} (tol {tol})")
-    assert np.isfinite(worst) and worst <= tol
+        err = np.abs(Oc[bh, t0:t0 + nv] - ref[n, :nv]).max(axis=1)
+        assert np.isfinite(err).all()
+        errs.append(err)
+        bnds.append(bound[n, :nv] if bound is not None else np.zeros(nv))
+    err, bnd = np.concatenate(errs), np.concatenate(bnds)
+    worst = float(err.max()) if err.size else 0.0
+    extra = ""
+    if bound is not None and err.size:
+        q = np.quantile(err, [0.5, 0.9, 0.99])
+        extra = (f"; rows {err.size}, with a flippable decision {int((bnd > 0).sum())}, "
+                 f"err quantiles 50/90/99% {q[0]:.1e}/{q[1]:.1e}/{q[2]:.1e}, "
+                 f"rows over 1e-4 {int((err > 1e-4).sum())}, over 1e-3 {int((err > 1e-3).sum())}, "
+                 f"over tol {int((err > tol).sum())}")
+    say(f"  max-abs error over {len(blocks)} blocks: {worst:.3e} (tol {tol}{extra})")
+    bad = np.flatnonzero(err > tol + bnd)
+    assert bad.size == 0, (int(bad[0]), float(err[bad[0]]), float(bnd[bad[0]]))
+    if bound is not None and err.size >= 100:
+        # Flips are rare and every other difference is fp32 rounding, so the
+        # bulk of the rows must agree far more tightly than tol: a wrong max,
+        # scale or tile order moves most rows by 1e-3 or more.
+        assert np.quantile(err, 0.9) <= FP8_BULK[0], np.quantile(err, 0.9)
+        assert np.quantile(err, 0.99) <= FP8_BULK[1], np.quantile(err, 0.99)
     return worst
 
 
@@ -223,3 +266,74 @@ def test_sparsity_sweep(orc, dev, frac):
     rng = np.random.default_rng(1)
     blocks = [(h, int(i)) for h in heads for i in {0, w.Tq - 1, *rng.choice(w.Tq, 3).tolist()}]
     compare_blocks(orc, x, full, O, blocks, TOL["bf16"])
+
+
+# --------------------------------------------------------------------------
+# low-bit sparse branch
+# --------------------------------------------------------------------------
+def quantize_gpu(x, dev):
+    p = problem_of(x)
+    q, k, _, _, _, _ = to_dev(x, dev)
+    w = x.wl
+    BH = w.B * w.H
+    qh = torch.empty((BH, w.Tq * w.bq, w.d), dtype=torch.uint8, device=dev)
+    kh = torch.empty((BH, w.Tkv * 64, w.d), dtype=torch.uint8, device=dev)
+    sq = torch.empty((BH, w.Tq), dtype=torch.float32, device=dev)
+    sk = torch.empty((BH, w.Tkv), dtype=torch.float32, device=dev)
+    mu = torch.empty((BH, w.d), dtype=torch.float32, device=dev)
+    S.sla2_quantize_fp8(p, q, k, qh, kh, sq, sk, mu, S.workspace(p, S.OP_FORWARD_FP8))
+    torch.cuda.synchronize()
+    return [t.cpu().numpy() for t in (qh, kh, sq, sk, mu)]
+
+
+@pytest.mark.parametrize("N,H", [(700, 2), (4100, 3), (75600, 1)])
+def test_quantized_inputs_match_oracle(orc, dev, N, H):
+    """Q/K codes, per-block scales and the K channel mean are bit-exact."""
+    w = wl(f"q{N}", "bf16", N, 128, 128, 0.03, H=H)
+    if N == 75600:
+        w = w.with_(grid=(21, 45, 80))
+    x = I.make_inputs(w)
+    qh, kh, sq, sk, mu = quantize_gpu(x, dev)
+    op = orc.problem_of(x)
+    for bh in range(w.B * w.H):
+        oqh, okh, osq, osk, omu = orc.quant_fp8(op, x.q, x.k, bh)
+        assert np.array_equal(mu[bh], omu)
+        assert np.array_equal(sq[bh], osq) and np.array_equal(sk[bh], osk)
+        assert np.array_equal(qh[bh, :N], oqh), int((qh[bh, :N] != oqh).sum())
+        assert np.array_equal(kh[bh, :N], okh), int((kh[bh, :N] != okh).sum())
+        assert not qh[bh, N:].any() and not kh[bh, N:].any()
+
+
+FP8_SMALL = [
+    wl("fp8-ragged", "bf16", 700, 128, 128, 0.25),
+    wl("fp8-tiles", "bf16", 4100, 128, 128, 0.05, H=3),
+    wl("fp8-dense", "bf16", 640, 128, 128, 1.0, alpha=(1.0, 1.0)),
+    wl("fp8-k0", "bf16", 900, 128, 128, 0.0),
+    wl("fp8-one-token", "bf16", 1, 128, 128, 1.0),
+    wl("fp8-alpha1", "bf16", 2000, 128, 128, 0.1, alpha=(1.0, 1.0)),
+]
+
+
+@pytest.mark.parametrize("w", FP8_SMALL, ids=[w.name for w in FP8_SMALL])
+def test_fp8_forward_parity(orc, dev, w):
+    say(f"case {w.name}: N={w.N} frac={w.topk_frac}")
+    x = I.make_inputs(w)
+    p, idx, mask, O = run_gpu(x, dev, fp8=True)
+    oidx = check_route(orc, x, idx, mask)
+    compare_blocks(orc, x, oidx, O, orc.all_blocks(orc.problem_of(x)), TOL["fp8"],
+                   variant="fp8")
+
+
+def test_fp8_wan14b_sampled(orc, dev):
+    w = I.WAN14B
+    x = I.make_inputs(w)
+    p, idx, mask, O = run_gpu(x, dev, fp8=True, want_mask=False)
+    assert torch.isfinite(O).all()
+    heads = [5, 31]
+    op = orc.problem_of(x)
+    oidx, _, _, _ = orc.route(op, x.q, x.k, x.wq, x.wk, heads=heads)
+    gi = idx.cpu().numpy().reshape(w.B * w.H, w.Tq, -1)
+    assert np.array_equal(gi[heads], oidx.reshape(w.B * w.H, w.Tq, -1)[heads])
+    rng = np.random.default_rng(3)
+    blocks = [(h, int(i)) for h in heads for i in {0, w.Tq - 1, *rng.choice(w.Tq, 4).tolist()}]
+    compare_blocks(orc, x, oidx, O, blocks, TOL["fp8"], variant="fp8")

@@ -31,6 +31,12 @@ MUTANTS = {
     "lowbit_no_rescale": ("double resc = (m == -INFINITY) ? 0.0 : exp(m - mn);",
                           "double resc = (m == -INFINITY) ? 0.0 : 1.0;"),
     "no_k_smoothing": ("o->mu[c] = (float)(s / (double)N);", "o->mu[c] = 0.0f;"),
+    "p_against_tile_max": ("double pt = exp(lbuf[u - t0] - mn);", "double pt = exp(lbuf[u - t0] - mt);"),
+    "p_not_scaled_by_256": ("float f = (float)(256.0 * pt);\n                ph = (double)orc_e4m3_decode(orc_e4m3_encode(f)) / 256.0;",
+                            "float f = (float)(pt);\n                ph = (double)orc_e4m3_decode(orc_e4m3_encode(f));"),
+    "flip_bound_ignores_rescale": ("double wgt = amb[a].step / 256.0 * exp(amb[a].m - m) / l;",
+                                   "double wgt = amb[a].step / 256.0 * exp(m - amb[a].m) / l * 0.25;"),
+    "flip_bound_window_narrow": ("double win = abuf[u - t0] + mA +", "double win = abuf[u - t0] +"),
     "denominator_without_phi_q": ("den += pq[c] * Zi[c];", "den += Zi[c];"),
     "alpha_of_wrong_head": ("double a = (double)F->alpha[h];", "double a = (double)F->alpha[0];"),
     "numerator_transposed_H": ("num += pq[c] * Hi[(size_t)c * d + e];", "num += pq[c] * Hi[(size_t)e * d + c];"),
@@ -51,6 +57,8 @@ PINS = [
     (pins.test_lowbit_identity_quantiser_equals_exact, ("bf16",)),
     (pins.test_lowbit_quantised_inputs, ()),
     (pins.test_lowbit_error_is_small, ()),
+    (pins.test_lowbit_single_tile_closed_form, ()),
+    (pins.test_lowbit_branch_and_flip_bound_brute_force, ()),
 ]
 
 

@@ -427,6 +427,116 @@ def test_lowbit_error_is_small(orc):
     assert np.abs(o - o8).max() < 0.1
 
 
+def _e4m3_values():
+    return torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).double().numpy()
+
+
+def _lowbit_rows_brute(orc, x, idx, eps):
+    """The low-bit sparse branch of every row, worked out with torch's
+    float8 cast (alpha = 1, so the output is O_s): logits from the decoded
+    codes, tiles in ascending order, 256 P~ against the running max rounded
+    to e4m3.  Also returns, per row, every decision whose input lies within
+    the accumulation window of a rounding midpoint, with its flipped code."""
+    w = x.wl
+    val = _e4m3_values()
+    p = orc.problem_of(x)
+    qh, kh, sq, sk, _ = orc.quant_fp8(p, x.q, x.k, 0)
+    V = I.bf16_bits_to_f32(x.v[0, 0]).astype(np.float64)
+    rows = []
+    for t in range(w.N):
+        i = t // w.bq
+        m, mA, rec = -np.inf, 0.0, []
+        for j in idx[0, 0, i]:
+            u = np.arange(j * w.bkv, min(w.N, (j + 1) * w.bkv))
+            prod = val[qh[t]][None, :] * val[kh[u]]
+            sc = float(sq[i]) * float(sk[j]) / math.sqrt(w.d)
+            lg = prod.sum(1) * sc
+            a = eps * np.abs(prod).sum(1) * sc
+            mA = max(mA, a.max())
+            mn = max(m, lg.max())
+            f = (256.0 * np.exp(lg - mn)).astype(np.float32)
+            code = torch.from_numpy(f).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+            for n in range(len(u)):
+                c, fv = int(code[n]), float(f[n])
+                alt = None
+                if fv > 0:
+                    win = a[n] + mA + 2.0 ** -21 * (abs(mn) / math.log(2) + 16) + 2.0 ** -21
+                    mids = []
+                    if c > 0:
+                        mids.append((abs(fv - (val[c] + val[c - 1]) / 2), c - 1))
+                    if c < 0x7E:
+                        mids.append((abs(fv - (val[c] + val[c + 1]) / 2), c + 1))
+                    dist, other = min(mids)
+                    if dist <= win * fv:
+                        alt = other
+                rec.append((int(u[n]), mn, c, alt))
+            m = mn
+        rows.append((rec, m))
+
+    def output(t, flip=()):
+        rec, mf = rows[t]
+        num, den = np.zeros(w.d), 0.0
+        for n, (u, mn, c, alt) in enumerate(rec):
+            c = alt if n in flip else c
+            ph = val[c] / 256.0 * math.exp(mn - mf)
+            num += ph * V[u]
+            den += ph
+        return num / den
+
+    return rows, output
+
+
+def test_lowbit_branch_and_flip_bound_brute_force(orc):
+    """Two tiles per row (k = 2 of 8), alpha = 1: the oracle's low-bit output
+    equals the float8-cast evaluation of the steps, and its per-row bound
+    covers flipping any one, and all, of the decisions that lie within the
+    accumulation window of an e4m3 midpoint (a wide window, 2^-8, so that
+    many rows have several)."""
+    wl = I.Workload("t", 1, 1, 256, 32, 64, 32, 0.25, "bf16", "smooth", seed=5,
+                    alpha=(1.0,))
+    x = I.make_inputs(wl)
+    p = orc.problem_of(x)
+    idx, _, _, _ = orc.route(p, x.q, x.k, x.wq, x.wk)
+    assert idx.shape[-1] == 2
+    eps = 2.0 ** -8
+    out, bound = orc.forward(p, x.q, x.k, x.v, idx, x.alpha, orc.all_blocks(p), variant="fp8",
+                             acc_eps=eps)
+    rows, output = _lowbit_rows_brute(orc, x, idx, eps)
+    n_flag = 0
+    for t in range(wl.N):
+        i, r = divmod(t, wl.bq)
+        o = output(t)
+        assert np.abs(out[i, r] - o).max() < 1e-12
+        flag = [n for n, e in enumerate(rows[t][0]) if e[3] is not None]
+        assert (bound[i, r] > 0) == bool(flag)
+        n_flag += len(flag)
+        for f in [[n] for n in flag] + ([flag] if len(flag) > 1 else []):
+            assert np.abs(output(t, set(f)) - o).max() <= bound[i, r] * (1 + 1e-9)
+    assert n_flag > 100
+
+
+def test_lowbit_single_tile_closed_form(orc):
+    """With one selected tile the running max is the row max: O_s is
+    sum e4m3(256 exp(l - max)) V / sum e4m3(...), with torch's cast."""
+    wl = I.Workload("t", 1, 1, 300, 32, 64, 64, 0.2, "bf16", "smooth", seed=2, alpha=(1.0,))
+    x = I.make_inputs(wl)
+    p = orc.problem_of(x)
+    idx, _, _, _ = orc.route(p, x.q, x.k, x.wq, x.wk)
+    assert idx.shape[-1] == 1
+    out = orc.forward(p, x.q, x.k, x.v, idx, x.alpha, orc.all_blocks(p), variant="fp8")
+    val = _e4m3_values()
+    qh, kh, sq, sk, _ = orc.quant_fp8(p, x.q, x.k, 0)
+    V = I.bf16_bits_to_f32(x.v[0, 0]).astype(np.float64)
+    for t in range(wl.N):
+        i = t // 64
+        j = int(idx[0, 0, i, 0])
+        u = np.arange(j * 64, min(wl.N, j * 64 + 64))
+        lg = (val[kh[u]] @ val[qh[t]]) * float(sq[i]) * float(sk[j]) / math.sqrt(32)
+        f = torch.from_numpy((256.0 * np.exp(lg - lg.max())).astype(np.float32))
+        ph = f.to(torch.float8_e4m3fn).double().numpy() / 256.0
+        assert np.abs(out[i, t % 64] - ph @ V[u] / ph.sum()).max() < 1e-12
+
+
 # --------------------------------------------------------------------------
 # workload generator sanity (shapes and statistics stated for the workloads)
 # --------------------------------------------------------------------------
