@@ -10,10 +10,15 @@ Metric: dense-equivalent attention TOPS = 4 B H N^2 d / step time (the pages'
 kernel metric, "SLA2 深度解读" 01/13: TOPS of the attention kernel against
 FlashAttention2's dense work).  Prints ONE JSON line.
 
-Options: --steps K --warmup W; --gpus N (only 1: this build runs on one GPU);
+Options: --steps K --warmup W; --gpus N (only 1: the path runs on one GPU);
 --no-cpu-baseline skips the oracle timing; --workload wan13b for the smaller
-shape; --fp8 times sla2_forward_fp8 as well; --copy-calibration runs only a
-plain 1 GiB device copy (used to scale rocprofv3 FETCH_SIZE / WRITE_SIZE).
+shape; --no-fp8 skips the extra timing of sla2_forward_fp8 (the low-bit
+sparse branch on the same inputs); --copy-calibration runs only a plain 1 GiB
+device copy (used to scale rocprofv3 FETCH_SIZE / WRITE_SIZE);
+--counters-summary FETCH WRITE COPY_FETCH COPY_WRITE turns four rocprofv3
+--pmc output folders (the bench, then the copy) into the per-launch HBM
+traffic of the fused kernel, written to profiles/ and read back by later
+runs while the kernel source is unchanged.
 """
 from __future__ import annotations
 
@@ -77,9 +82,13 @@ def linear_summary_flop(BH, N, d) -> float:
 
 
 # --------------------------------------------------------------------------
+COPY_BYTES = 1 << 30
+FUSED_KERNEL_RX = r"fused_mfma_d128_kernel<true, false>"
+
+
 def copy_calibration():
     import torch
-    n = 1 << 30
+    n = COPY_BYTES
     x = torch.empty(n, dtype=torch.uint8, device="cuda")
     y = torch.empty_like(x)
     x.fill_(1)
@@ -88,6 +97,55 @@ def copy_calibration():
         y.copy_(x)
     torch.cuda.synchronize()
     print(json.dumps({"copy_calibration_bytes": n, "launches": 3}))
+
+
+def _counter_means(folder, counter, name_rx):
+    """Mean per dispatch (KiB) of one counter over the dispatches whose kernel
+    name matches name_rx, from a rocprofv3 --pmc csv folder."""
+    import csv
+    import glob
+    import re
+    files = glob.glob(os.path.join(folder, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no counter_collection.csv under {folder}")
+    per = {}
+    names = set()
+    for f in files:
+        for r in csv.DictReader(open(f)):
+            if r["Counter_Name"] != counter or not re.search(name_rx, r["Kernel_Name"]):
+                continue
+            names.add(r["Kernel_Name"])
+            per[(f, r["Dispatch_Id"])] = per.get((f, r["Dispatch_Id"]), 0.0) + float(
+                r["Counter_Value"])
+    if not per:
+        raise SystemExit(f"{counter}: no dispatch of /{name_rx}/ in {folder}")
+    v = list(per.values())
+    return sum(v) / len(v), len(v), sorted(names)
+
+
+def counters_summary(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, workload):
+    fk, fn, names = _counter_means(fetch_dir, "FETCH_SIZE", FUSED_KERNEL_RX)
+    wk, wn, _ = _counter_means(write_dir, "WRITE_SIZE", FUSED_KERNEL_RX)
+    cf, _, _ = _counter_means(copy_fetch_dir, "FETCH_SIZE", "copyBuffer")
+    cw, _, _ = _counter_means(copy_write_dir, "WRITE_SIZE", "copyBuffer")
+    f_fac = COPY_BYTES / (cf * 1024.0)
+    w_fac = COPY_BYTES / (cw * 1024.0)
+    read_b = fk * 1024.0 * f_fac
+    write_b = wk * 1024.0 * w_fac
+    res = {
+        "kernel": names[0] if names else FUSED_KERNEL_RX,
+        "workload": workload,
+        "kernel_source_sha": kernel_source_sha(),
+        "fetch_kib_per_dispatch": fk, "fetch_dispatches": fn,
+        "write_kib_per_dispatch": wk, "write_dispatches": wn,
+        "copy_fetch_kib": cf, "copy_write_kib": cw,
+        "fetch_scale": f_fac, "write_scale": w_fac,
+        "hbm_read_bytes_per_launch": read_b, "hbm_write_bytes_per_launch": write_b,
+        "hbm_bytes_per_launch": read_b + write_b,
+    }
+    with open(COUNTERS, "w") as f:
+        json.dump(res, f, indent=1)
+    print(json.dumps(res, indent=1))
 
 
 def cpu_baseline(x, dense_flop, budget_s=12.0):
@@ -130,9 +188,14 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="wan14b", choices=["wan14b", "wan13b"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--fp8", action="store_true")
+    ap.add_argument("--no-fp8", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--counters-summary", nargs=4, metavar="DIR")
     args = ap.parse_args()
+
+    if args.counters_summary:
+        counters_summary(*args.counters_summary, workload=args.workload)
+        return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -250,7 +313,7 @@ def main():
         "kernel_source_sha": kernel_source_sha(),
     }
 
-    if args.fp8:
+    if not args.no_fp8:
         ws8 = S.workspace(p, S.OP_FORWARD_FP8)
 
         def step8():
@@ -268,8 +331,14 @@ def main():
         torch.cuda.synchronize()
         k8 = S.timing_stop()
         ms8 = ev0.elapsed_time(ev1) / args.steps
+        st8 = {n_: ms_ / c_ for n_, (ms_, c_) in k8.items()}
+        f8_ms = st8.get("fused_fp8")
+        # the low-bit kernel's work: Q K^T on the fp8 cores, P V and phi(Q) H
+        # on the fp16 ones; priced against the fp16 peak (the larger share)
         out["fp8"] = {"ms_per_step": ms8, "tops": dense / (ms8 * 1e-3) / 1e12,
-                      "stages_ms": {n_: ms_ / c_ for n_, (ms_, c_) in k8.items()}}
+                      "stages_ms": st8,
+                      "fused_fp8_tflops": (fl_sparse + fl_apply) / (f8_ms * 1e-3) / 1e12
+                      if f8_ms else None}
 
     if not args.no_cpu_baseline:
         log("bench: timing the CPU oracle on a sample")
