@@ -1,0 +1,452 @@
+// Fused sparse + linear + combine kernel for d = 128, b_q = 128, b_kv = 64
+// (bf16 inputs; with LOWBIT the Q K^T products run on the e4m3 matrix cores).
+//
+// One work-group of 4 waves per (head, query block); wave w owns queries
+// 32w .. 32w+31 of the block and all 64 keys of every selected KV tile, so
+// each wave carries a complete online-softmax state and no partial results
+// are merged across waves.  80 KB of LDS per work-group lets two work-groups
+// share a compute unit: one group's prologue and epilogue overlap the
+// other's tile loop.
+//
+// Per selected KV block j, in ascending order ("SLA2 深度解读" 04, 07, 08:
+// only mask-hit blocks run Q K^T and P V, online softmax over them):
+//   S^T = K_j Q^T                       bf16 MFMA (LOWBIT: Khat Qhat^T, e4m3,
+//                                       times s_Q s_K)
+//   online softmax on S^T               one query per lane column
+//   O^T += V_j^T P^T                    fp16 MFMA (LOWBIT: P on the e4m3 grid)
+//   G^T += V_j^T phi(K_j)               fp16 MFMA; phi(K_j) is evaluated from
+//                                       the K tile already in LDS, read
+//                                       transposed
+//   z   += colsum phi(K_j)
+// G starts at -h_tot^T and z at -z_tot, so at the end H_i^T = -G^T and
+// Z_i = -z: the linear branch's sums over the unselected blocks (SLA notes,
+// key designs 3 and 4: H_i, Z_i as the total minus the selected blocks).
+// Epilogue: O_l^T = H_i^T phi(Q)^T / (phi(Q) . Z_i), O = alpha O_s +
+// (1 - alpha) O_l ("SLA2 深度解读" 04).
+//
+// Tiles arrive by direct-to-LDS loads.  K tiles are issued two tiles ahead
+// (three stages; two with LOWBIT and the linear branch, whose K stage holds
+// both Khat and K), V^T tiles one tile ahead (two stages).  LDS layouts:
+//   K    [64 keys][256 B]   16-byte chunk c of row r at chunk c ^ (r & 15)
+//   Khat [64 keys][128 B]   chunk c of row r at chunk c ^ ((r >> 1) & 7)
+//   V^T  [128 ch][128 B]    chunk c of row r at chunk c ^ ((r >> 1) & 7)
+// V^T comes from the block summaries pass in fp16 with the keys of each
+// group of 16 stored at positions with bits 2 and 3 swapped, which makes the
+// k order of P^T (taken straight from the S^T accumulators) line up with it;
+// the transposed reads of K for phi(K) follow the same order.
+#include "cdna4.h"
+#include "sla2_internal.h"
+
+namespace sla2 {
+namespace {
+using namespace cdna4;
+
+constexpr int kLdsBytes = 80 * 1024;
+constexpr int kKRaw = 16384;  // K tile, bf16
+constexpr int kKHat = 8192;   // Khat tile, e4m3
+constexpr int kVT = 16384;    // V^T tile, fp16
+constexpr float kRescaleThr = 8.0f;
+
+__shared__ __attribute__((aligned(1024))) char s_lds[kLdsBytes];
+
+template <bool LIN, bool LOWBIT>
+struct Plan {
+    static constexpr bool kRaw = !LOWBIT || LIN;  // bf16 K staged (Q K^T or phi(K))
+    static constexpr int kRawOff = LOWBIT ? kKHat : 0;
+    static constexpr int kStage = (LOWBIT ? kKHat : 0) + (kRaw ? kKRaw : 0);
+    static constexpr int kStages = (LOWBIT && LIN) ? 2 : 3;
+    static constexpr int vOff = kStages * kStage;
+    static constexpr int nK = (LOWBIT ? 2 : 0) + (kRaw ? 4 : 0);  // loads per lane, K tile
+    static_assert(vOff + 2 * kVT <= kLdsBytes, "LDS budget");
+    static_assert(32768 + 512 <= kLdsBytes, "epilogue LDS");
+};
+
+template <bool LOWBIT> struct QOp;
+template <> struct QOp<false> { bf16x8 f[8]; };  // 8 k-steps of 16 channels
+template <> struct QOp<true> { i32x8 f[2]; };    // 2 k-steps of 64 channels
+
+// K tile j into one K stage: 1 KB pieces, piece u = 4i + w
+template <bool LIN, bool LOWBIT>
+__device__ inline void issue_k(char* kst, const uint16_t* K_h, const uint8_t* khat_h, int j,
+                               int N, int w, int lane) {
+    using P = Plan<LIN, LOWBIT>;
+    if (LOWBIT) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int u = 4 * i + w;
+            const int row = 8 * u + (lane >> 3);
+            const int lc = (lane & 7) ^ ((row >> 1) & 7);
+            __builtin_amdgcn_global_load_lds(khat_h + ((size_t)j * 64 + row) * 128 + lc * 16,
+                                             SLA2_LDS(kst + u * 1024), 16, 0, 0);
+        }
+    }
+    if (P::kRaw) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int u = 4 * i + w;
+            const int row = 4 * u + (lane >> 4);
+            const int lc = (lane & 15) ^ (row & 15);
+            const int tok = min(j * 64 + row, N - 1);  // padding rows: any valid row
+            __builtin_amdgcn_global_load_lds(K_h + (size_t)tok * 128 + lc * 8,
+                                             SLA2_LDS(kst + P::kRawOff + u * 1024), 16, 0, 0);
+        }
+    }
+}
+
+// V^T tile j into one V stage
+__device__ inline void issue_v(char* vst, const uint16_t* vt_h, int j, int w, int lane) {
+    const uint16_t* src = vt_h + (size_t)j * 128 * 64;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int u = 4 * i + w;
+        const int row = 8 * u + (lane >> 3);
+        const int lc = (lane & 7) ^ ((row >> 1) & 7);
+        __builtin_amdgcn_global_load_lds(src + row * 64 + lc * 8, SLA2_LDS(vst + u * 1024), 16,
+                                         0, 0);
+    }
+}
+
+template <bool LIN, bool LOWBIT>
+__global__ __launch_bounds__(256, 2) void fused128_kernel(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+    const uint16_t* __restrict__ vt, const int32_t* __restrict__ idx,
+    const float* __restrict__ alpha, const float* __restrict__ htot,
+    const float* __restrict__ ztot, const uint8_t* __restrict__ qhat,
+    const uint8_t* __restrict__ khat, const float* __restrict__ sq,
+    const float* __restrict__ sk, float* __restrict__ O, int N, int Tq, int Tkv, int k,
+    int H) {
+    using P = Plan<LIN, LOWBIT>;
+    const int t = threadIdx.x, lane = t & 63, l32 = lane & 31, hl = lane >> 5;
+    const int w = __builtin_amdgcn_readfirstlane(t >> 6);
+    long bh;
+    int qb;
+    if (!head_major_map(blockIdx.x, Tq, &bh, &qb)) return;
+    const int tq = qb * 128 + 32 * w + l32;
+    const bool valid_q = tq < N;
+    const float c_log2 = 1.4426950408889634f / sqrtf(128.0f);
+
+    // ---- Q operand (B of S^T = K Q^T): lane holds query tq
+    QOp<LOWBIT> Qo;
+    float c_base = c_log2;
+    if (LOWBIT) {
+        const uint8_t* qrow =
+            qhat + ((size_t)bh * Tq * 128 + (size_t)qb * 128 + 32 * w + l32) * 128;
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            const uint4 lo = *reinterpret_cast<const uint4*>(qrow + 64 * ks + 32 * hl);
+            const uint4 hi = *reinterpret_cast<const uint4*>(qrow + 64 * ks + 32 * hl + 16);
+            i32x8 v;
+            v[0] = lo.x; v[1] = lo.y; v[2] = lo.z; v[3] = lo.w;
+            v[4] = hi.x; v[5] = hi.y; v[6] = hi.z; v[7] = hi.w;
+            reinterpret_cast<i32x8*>(Qo.f)[ks] = v;
+        }
+        c_base = c_log2 * sq[bh * Tq + qb];
+    } else {
+        const uint16_t* qrow = Q + ((size_t)bh * N + (valid_q ? tq : 0)) * 128;
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) {
+            uint4 v = make_uint4(0, 0, 0, 0);
+            if (valid_q) v = *reinterpret_cast<const uint4*>(qrow + 16 * ks + 8 * hl);
+            reinterpret_cast<bf16x8*>(Qo.f)[ks] = __builtin_bit_cast(bf16x8, v);
+        }
+    }
+
+    // ---- accumulators: O^T (d rows 32mt.., my queries), G^T (d rows 32mt..,
+    // phi channels 32w + l32) starting at -h_tot^T, z starting at -z_tot
+    f32x16 o[4], g[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) o[i] = zero16();
+    float zacc = 0.0f;
+    if (LIN) {
+        const float* hrow = htot + (size_t)bh * 128 * 128 + (size_t)(32 * w + l32) * 128;
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+            for (int i4 = 0; i4 < 4; ++i4) {
+                const float4 v = *reinterpret_cast<const float4*>(hrow + 32 * mt + 8 * i4 + 4 * hl);
+                g[mt][4 * i4 + 0] = -v.x;
+                g[mt][4 * i4 + 1] = -v.y;
+                g[mt][4 * i4 + 2] = -v.z;
+                g[mt][4 * i4 + 3] = -v.w;
+            }
+        zacc = hl == 0 ? -ztot[bh * 128 + 32 * w + l32] : 0.0f;
+    }
+    float m_ref = -INFINITY, l_part = 0.0f;
+
+    const int32_t* sel = idx + ((size_t)bh * Tq + qb) * k;
+    const uint16_t* K_h = K + (size_t)bh * N * 128;
+    const uint8_t* khat_h = LOWBIT ? khat + (size_t)bh * Tkv * 64 * 128 : nullptr;
+    const uint16_t* vt_h = vt + (size_t)bh * Tkv * 128 * 64;
+    const float* sk_h = LOWBIT ? sk + (size_t)bh * Tkv : nullptr;
+    char* const kbase = s_lds;
+    char* const vbase = s_lds + P::vOff;
+    constexpr int DK = P::kStages - 1;  // K prefetch distance
+
+    // ---- prologue: K_0, V_0 [, K_1]
+    if (k > 0) {
+        issue_k<LIN, LOWBIT>(kbase, K_h, khat_h, sel[0], N, w, lane);
+        issue_v(vbase, vt_h, sel[0], w, lane);
+        if (DK == 2 && k > 1) issue_k<LIN, LOWBIT>(kbase + P::kStage, K_h, khat_h, sel[1], N, w, lane);
+    }
+
+    int kslot = 0;
+    for (int r = 0; r < k; ++r) {
+        // tile r's K and V^T have landed for this wave (loads issued after
+        // V_r, at most one K tile, may still be in flight) ...
+        if (DK == 2 && r + 1 < k) wait_vmcnt<P::nK>();
+        else wait_vmcnt<0>();
+        wg_barrier();  // ... and for every wave; all waves are done with tile r-1
+        if (r + 1 < k) issue_v(vbase + ((r + 1) & 1) * kVT, vt_h, sel[r + 1], w, lane);
+        if (r + DK < k) {
+            const int s2 = kslot + DK >= P::kStages ? kslot + DK - P::kStages : kslot + DK;
+            issue_k<LIN, LOWBIT>(kbase + s2 * P::kStage, K_h, khat_h, sel[r + DK], N, w, lane);
+        }
+        const int j = sel[r];
+        const char* kst = kbase + kslot * P::kStage;
+        const char* vst = vbase + (r & 1) * kVT;
+        kslot = kslot + 1 == P::kStages ? 0 : kslot + 1;
+        const float c_tile = LOWBIT ? c_base * sk_h[j] : c_base;
+
+        // S^T = K Q^T, two m-tiles of 32 keys
+        f32x16 s[2] = {zero16(), zero16()};
+        if (LOWBIT) {
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+                for (int mt = 0; mt < 2; ++mt) {
+                    const int kr = 32 * mt + l32, sw = (kr >> 1) & 7, c0 = 4 * ks + 2 * hl;
+                    const uint4 lo = *reinterpret_cast<const uint4*>(kst + kr * 128 + ((c0 ^ sw) << 4));
+                    const uint4 hi =
+                        *reinterpret_cast<const uint4*>(kst + kr * 128 + (((c0 + 1) ^ sw) << 4));
+                    i32x8 a;
+                    a[0] = lo.x; a[1] = lo.y; a[2] = lo.z; a[3] = lo.w;
+                    a[4] = hi.x; a[5] = hi.y; a[6] = hi.z; a[7] = hi.w;
+                    s[mt] = mfma_fp8(a, reinterpret_cast<const i32x8*>(Qo.f)[ks], s[mt]);
+                }
+        } else {
+#pragma unroll
+            for (int ks = 0; ks < 8; ++ks)
+#pragma unroll
+                for (int mt = 0; mt < 2; ++mt) {
+                    const int kr = 32 * mt + l32;
+                    const bf16x8 a = *reinterpret_cast<const bf16x8*>(
+                        kst + kr * 256 + (((2 * ks + hl) ^ (kr & 15)) << 4));
+                    s[mt] = mfma_bf16(a, reinterpret_cast<const bf16x8*>(Qo.f)[ks], s[mt]);
+                }
+        }
+        const bool ragged = j * 64 + 64 > N;
+        if (ragged) {
+#pragma unroll
+            for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+                for (int i = 0; i < 16; ++i)
+                    if (j * 64 + 32 * mt + 8 * (i >> 2) + 4 * hl + (i & 3) >= N) s[mt][i] = -INFINITY;
+        }
+
+        // online softmax (log2 units)
+        float mx = s[0][0];
+#pragma unroll
+        for (int i = 1; i < 16; ++i) mx = fmaxf(mx, s[0][i]);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[1][i]);
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float xmax = mx * c_tile;
+        const bool need = LOWBIT ? (xmax > m_ref) : (xmax > m_ref + kRescaleThr);
+        if (__ballot(need)) {
+            const float nref = need ? xmax : m_ref;
+            const float f = __builtin_amdgcn_exp2f(m_ref - nref);
+            l_part *= f;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) o[i][e] *= f;
+            m_ref = nref;
+        }
+        const float mref = m_ref == -INFINITY ? 0.0f : m_ref;
+        // P^T as the B operand of 4 k-steps of 16 keys: k-step kq takes rows
+        // 8(kq&1)..8(kq&1)+7 of m-tile kq>>1
+        f16x8 pf[4];
+        if (LOWBIT) {  // 256 P~ rounded onto the e4m3 grid, carried exactly in fp16
+            const float bias = 8.0f - mref;
+#pragma unroll
+            for (int kq = 0; kq < 4; ++kq)
+#pragma unroll
+                for (int e = 0; e < 8; e += 2) {
+                    const float x0 = s[kq >> 1][8 * (kq & 1) + e];
+                    const float x1 = s[kq >> 1][8 * (kq & 1) + e + 1];
+                    const float p0 = __builtin_amdgcn_exp2f(fmaf(x0, c_tile, bias));
+                    const float p1 = __builtin_amdgcn_exp2f(fmaf(x1, c_tile, bias));
+                    const int code = __builtin_amdgcn_cvt_pk_fp8_f32(fminf(p0, 448.0f),
+                                                                     fminf(p1, 448.0f), 0, false);
+                    const auto back = __builtin_amdgcn_cvt_pk_f32_fp8(code, false);
+                    pf[kq][e] = (_Float16)back[0];
+                    pf[kq][e + 1] = (_Float16)back[1];
+                }
+        } else {
+#pragma unroll
+            for (int kq = 0; kq < 4; ++kq)
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    pf[kq][e] = (_Float16)__builtin_amdgcn_exp2f(
+                        fmaf(s[kq >> 1][8 * (kq & 1) + e], c_tile, -mref));
+        }
+        const f16x2 ones = {(_Float16)1.0f, (_Float16)1.0f};
+#pragma unroll
+        for (int kq = 0; kq < 4; ++kq)
+#pragma unroll
+            for (int e = 0; e < 8; e += 2) {
+                const f16x2 pr = {pf[kq][e], pf[kq][e + 1]};
+                l_part = __builtin_amdgcn_fdot2(pr, ones, l_part, false);
+            }
+
+        // O^T += V^T P^T and G^T += V^T phi(K)
+        const char* kraw = kst + P::kRawOff;
+#pragma unroll
+        for (int kq = 0; kq < 4; ++kq) {
+            f16x8 phk;
+            if (LIN) {
+                // keys 16kq + 8a + 4hl + e (e = 0..3) of channel 32w + l32:
+                // source lane r of each 16-lane group reads row
+                // 16kq + 8a + 4hl + r/4, channels cb + 4(r%4) .. +3
+                const int r16 = lane & 15;
+                const int ch = 32 * w + 16 * ((lane >> 4) & 1) + 4 * (r16 & 3);
+#pragma unroll
+                for (int a = 0; a < 2; ++a) {
+                    const int row = 16 * kq + 8 * a + 4 * hl + (r16 >> 2);
+                    const s16x4 raw = lds_read_tr16(
+                        kraw + row * 256 + ((((ch >> 3) ^ (row & 15))) << 4) + ((ch & 7) << 1));
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        float ph = phi_fast(bf16_bits((unsigned short)raw[e]));
+                        if (ragged && j * 64 + 16 * kq + 8 * a + 4 * hl + e >= N) ph = 0.0f;
+                        zacc += ph;
+                        phk[4 * a + e] = (_Float16)ph;
+                    }
+                }
+            }
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt) {
+                const int erow = 32 * mt + l32;
+                const f16x8 a = *reinterpret_cast<const f16x8*>(
+                    vst + erow * 128 + (((2 * kq + hl) ^ ((erow >> 1) & 7)) << 4));
+                o[mt] = mfma_f16(a, pf[kq], o[mt]);
+                if (LIN) g[mt] = mfma_f16(a, phk, g[mt]);
+            }
+        }
+    }
+
+    // ---- epilogue
+    const float l_all = l_part + __shfl_xor(l_part, 32);
+    const float inv_l = (k > 0 && l_all > 0.0f) ? 1.0f / l_all : 0.0f;
+    f32x16 ol[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) ol[i] = zero16();
+    float inv_den = 0.0f;
+    if (LIN) {
+        wg_barrier();  // every wave is done with the tile stages
+        // H^T = -G^T as fp16, [128 d rows][256 B], chunk c' of row e at c' ^ (e & 15)
+        char* sH = s_lds;
+        float* sZ = reinterpret_cast<float*>(s_lds + 32768);
+        const int c = 32 * w + l32;
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int e = 32 * mt + 8 * (i >> 2) + 4 * hl + (i & 3);
+                *reinterpret_cast<_Float16*>(sH + e * 256 + (((c >> 3) ^ (e & 15)) << 4) +
+                                             ((c & 7) << 1)) = (_Float16)(-g[mt][i]);
+            }
+        const float zs = zacc + __shfl_xor(zacc, 32);
+        if (hl == 0) sZ[c] = -zs;
+        wait_lgkm0();
+        wg_barrier();
+        // phi(Q)^T operand from the raw bf16 Q (registers on the bf16 path)
+        bf16x8 qraw[8];
+        if (LOWBIT) {
+            const uint16_t* qrow = Q + ((size_t)bh * N + (valid_q ? tq : 0)) * 128;
+#pragma unroll
+            for (int ks = 0; ks < 8; ++ks) {
+                uint4 v = make_uint4(0, 0, 0, 0);
+                if (valid_q) v = *reinterpret_cast<const uint4*>(qrow + 16 * ks + 8 * hl);
+                qraw[ks] = __builtin_bit_cast(bf16x8, v);
+            }
+        } else {
+#pragma unroll
+            for (int ks = 0; ks < 8; ++ks) qraw[ks] = reinterpret_cast<const bf16x8*>(Qo.f)[ks];
+        }
+        f16x8 pq[8];
+        float den = 0.0f;
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) {
+            const float4 z0 = *reinterpret_cast<const float4*>(sZ + 16 * ks + 8 * hl);
+            const float4 z1 = *reinterpret_cast<const float4*>(sZ + 16 * ks + 8 * hl + 4);
+            const float zz[8] = {z0.x, z0.y, z0.z, z0.w, z1.x, z1.y, z1.z, z1.w};
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float p = phi_fast((float)qraw[ks][e]);
+                pq[ks][e] = (_Float16)p;
+                den = fmaf(p, zz[e], den);
+            }
+        }
+        den += __shfl_xor(den, 32);
+        inv_den = 1.0f / den;
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+            const int erow = 32 * mt + l32;
+#pragma unroll
+            for (int ks = 0; ks < 8; ++ks) {
+                const f16x8 a = *reinterpret_cast<const f16x8*>(
+                    sH + erow * 256 + (((2 * ks + hl) ^ (erow & 15)) << 4));
+                ol[mt] = mfma_f16(a, pq[ks], ol[mt]);
+            }
+        }
+    }
+    if (valid_q) {
+        const float a_h = alpha[bh % H];
+        float* orow = O + ((size_t)bh * N + tq) * 128;
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+            for (int i4 = 0; i4 < 4; ++i4) {
+                float4 v;
+                v.x = a_h * (o[mt][4 * i4 + 0] * inv_l) + (1.0f - a_h) * (ol[mt][4 * i4 + 0] * inv_den);
+                v.y = a_h * (o[mt][4 * i4 + 1] * inv_l) + (1.0f - a_h) * (ol[mt][4 * i4 + 1] * inv_den);
+                v.z = a_h * (o[mt][4 * i4 + 2] * inv_l) + (1.0f - a_h) * (ol[mt][4 * i4 + 2] * inv_den);
+                v.w = a_h * (o[mt][4 * i4 + 3] * inv_l) + (1.0f - a_h) * (ol[mt][4 * i4 + 3] * inv_den);
+                *reinterpret_cast<float4*>(orow + 32 * mt + 8 * i4 + 4 * hl) = v;
+            }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_fused128(const Dims& D, const void* Q, const void* K, const int32_t* idx,
+                           const float* alpha, float* O, const FwdWS& ws, bool lowbit,
+                           hipStream_t s) {
+    // one work-group per (head, query block), Tq padded to a multiple of 8
+    const dim3 g((unsigned)(((D.Tq + 7) / 8) * 8 * D.BH), 1);
+    const bool lin = D.k < D.Tkv;
+    const uint16_t* q = (const uint16_t*)Q;
+    const uint16_t* kk = (const uint16_t*)K;
+    timing_before(s, lowbit ? K_FUSED_FP8 : K_FUSED_MFMA);
+    if (!lowbit && lin)
+        fused128_kernel<true, false><<<g, 256, 0, s>>>(q, kk, ws.vt, idx, alpha, ws.htot, ws.ztot,
+                                                      nullptr, nullptr, nullptr, nullptr, O, D.N,
+                                                      D.Tq, D.Tkv, D.k, D.H);
+    else if (!lowbit)
+        fused128_kernel<false, false><<<g, 256, 0, s>>>(q, kk, ws.vt, idx, alpha, ws.htot,
+                                                       ws.ztot, nullptr, nullptr, nullptr,
+                                                       nullptr, O, D.N, D.Tq, D.Tkv, D.k, D.H);
+    else if (lin)
+        fused128_kernel<true, true><<<g, 256, 0, s>>>(q, kk, ws.vt, idx, alpha, ws.htot, ws.ztot,
+                                                     ws.qhat, ws.khat, ws.sq, ws.sk, O, D.N,
+                                                     D.Tq, D.Tkv, D.k, D.H);
+    else
+        fused128_kernel<false, true><<<g, 256, 0, s>>>(q, kk, ws.vt, idx, alpha, ws.htot,
+                                                      ws.ztot, ws.qhat, ws.khat, ws.sq, ws.sk, O,
+                                                      D.N, D.Tq, D.Tkv, D.k, D.H);
+    timing_after(s, lowbit ? K_FUSED_FP8 : K_FUSED_MFMA);
+    return hipGetLastError();
+}
+
+}  // namespace sla2

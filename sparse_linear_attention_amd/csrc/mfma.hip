@@ -943,6 +943,7 @@ hipError_t launch_fused_mfma(const Dims& D, const void* Q, const void* K, const 
                              const float* alpha, float* O, const FwdWS& ws, hipStream_t s) {
     // one work-group per (head, query block), Tq padded to a multiple of 8
     dim3 g((unsigned)(((D.Tq + 7) / 8) * 8 * D.BH), 1);
+    if (D.d == 128) return launch_fused128(D, Q, K, idx, alpha, O, ws, false, s);
     timing_before(s, K_FUSED_MFMA);
     if (D.d == 128 && D.k < D.Tkv)
         fused_mfma_d128_kernel<true, false><<<g, 512, 0, s>>>(

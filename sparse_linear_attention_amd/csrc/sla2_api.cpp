@@ -261,7 +261,7 @@ SLA2_API sla2_status sla2_forward_fp8(const sla2_problem* p, const void* Q, cons
     hipStream_t s = (hipStream_t)stream;
     hipError_t e = launch_quantize_fp8(D, Q, K, w, s);
     if (e == hipSuccess) e = launch_summaries_mfma(D, K, V, w, s);
-    if (e == hipSuccess) e = launch_fused_fp8(D, Q, topk_idx, alpha, O, w, s);
+    if (e == hipSuccess) e = launch_fused128(D, Q, K, topk_idx, alpha, O, w, true, s);
     return e == hipSuccess ? SLA2_OK : SLA2_EHIP;
 }
 

@@ -108,6 +108,10 @@ hipError_t launch_fused_mfma(const Dims& D, const void* Q, const void* K,
 // low bit
 hipError_t launch_quantize_fp8(const Dims& D, const void* Q, const void* K, const FwdWS& ws,
                                hipStream_t s);
+// d = 128, b_q = 128 fused kernel (bf16, or the low-bit Q K^T with lowbit)
+hipError_t launch_fused128(const Dims& D, const void* Q, const void* K, const int32_t* idx,
+                           const float* alpha, float* O, const FwdWS& ws, bool lowbit,
+                           hipStream_t s);
 hipError_t launch_fused_fp8(const Dims& D, const void* Q, const int32_t* idx,
                             const float* alpha, float* O, const FwdWS& ws, hipStream_t s);
 
