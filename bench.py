@@ -45,8 +45,11 @@ def log(*a):
 
 
 def kernel_source_sha() -> str:
-    p = os.path.join(ROOT, "sparse_linear_attention_amd", "csrc", "mfma.hip")
-    return hashlib.sha256(open(p, "rb").read()).hexdigest()[:16]
+    """Hash of the fused kernel's sources (counters are void once it changes)."""
+    h = hashlib.sha256()
+    for f in ("fused128.hip", "cdna4.h"):
+        h.update(open(os.path.join(ROOT, "sparse_linear_attention_amd", "csrc", f), "rb").read())
+    return h.hexdigest()[:16]
 
 
 # --------------------------------------------------------------------------
@@ -83,7 +86,7 @@ def linear_summary_flop(BH, N, d) -> float:
 
 # --------------------------------------------------------------------------
 COPY_BYTES = 1 << 30
-FUSED_KERNEL_RX = r"fused_mfma_d128_kernel<true, false>"
+FUSED_KERNEL_RX = r"fused128_kernel<true, false>"
 
 
 def copy_calibration():

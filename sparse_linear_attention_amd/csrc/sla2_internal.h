@@ -55,13 +55,11 @@ struct FwdWS {
     // bf16 path: block-transposed fp16 copies, kv order permuted inside each
     // group of 16 (see the fused kernel), padding tokens are 0
     uint16_t* vt;    // [BH][Tkv][d][64]  V^T      (fp16 bits)
-    uint16_t* pkt;   // [BH][Tkv][d][64]  phi(K)^T (fp16 bits)
-    float* zb;       // [BH][Tkv][d]      per-block z_j
+    uint16_t* pkt;   // [BH][Tkv][d][64]  phi(K)^T (fp16 bits; d = 64 only)
+    float* zb;       // [BH][Tkv][d]      per-block z_j (d = 64 only)
     float* hpart;    // [BH][chunks][d][d] partial h per chunk
     float* zpart;    // [BH][chunks][d]
     float* htot;     // [BH][d][d]        h_tot[c][e] = sum phi(K)[.,c] V[.,e]
-    float* hfrag;    // [BH][8 waves][64 lanes][32] h_tot in the fused kernel's
-                     // per-lane epilogue order (bf16 path, d = 128)
     float* ztot;     // [BH][d]
     // low-bit inputs
     uint8_t* qhat;   // [BH][Tq*bq][d]
@@ -112,7 +110,4 @@ hipError_t launch_quantize_fp8(const Dims& D, const void* Q, const void* K, cons
 hipError_t launch_fused128(const Dims& D, const void* Q, const void* K, const int32_t* idx,
                            const float* alpha, float* O, const FwdWS& ws, bool lowbit,
                            hipStream_t s);
-hipError_t launch_fused_fp8(const Dims& D, const void* Q, const int32_t* idx,
-                            const float* alpha, float* O, const FwdWS& ws, hipStream_t s);
-
 }  // namespace sla2

@@ -76,12 +76,9 @@ __global__ __launch_bounds__(256) void summaries_valu_kernel(
 }
 
 // h_tot = sum of the chunk partials in chunk order (deterministic).
-// Optionally also writes h_tot in the order the d = 128 fused kernel's
-// epilogue reads it: wave w = qg + 4*kh, lane = l32 + 32*hl, slot
-// s2*16 + i holds h[c = 32*qg + l32][e = 32*(2*kh + s2) + 8*(i/4) + 4*hl + i%4].
 __global__ __launch_bounds__(256) void summaries_reduce_kernel(
     const float* __restrict__ hpart, const float* __restrict__ zpart, float* __restrict__ htot,
-    float* __restrict__ ztot, float* __restrict__ hfrag, int d, int nch) {
+    float* __restrict__ ztot, int d, int nch) {
     const long bh = blockIdx.y;
     const int x = blockIdx.x * 256 + threadIdx.x;
     const int dd = d * d;
@@ -89,14 +86,6 @@ __global__ __launch_bounds__(256) void summaries_reduce_kernel(
         float s = 0.0f;
         for (int c = 0; c < nch; ++c) s += hpart[((size_t)bh * nch + c) * dd + x];
         htot[(size_t)bh * dd + x] = s;
-        if (hfrag) {  // d == 128
-            const int c = x >> 7, e = x & 127;
-            const int qg = c >> 5, l32 = c & 31;
-            const int kh = e >> 6, s2 = (e >> 5) & 1, r = e & 31;
-            const int hl = (r >> 2) & 1, i = ((r >> 3) << 2) | (r & 3);
-            const int wv = qg + 4 * kh, lane = l32 + 32 * hl;
-            hfrag[(size_t)bh * dd + ((size_t)wv * 64 + lane) * 32 + s2 * 16 + i] = s;
-        }
     }
     if (blockIdx.x == 0 && threadIdx.x < d) {
         float s = 0.0f;
@@ -255,7 +244,7 @@ hipError_t launch_summaries_reduce(const Dims& D, const FwdWS& ws, hipStream_t s
     const int nch = summ_chunks(D);
     timing_before(s, K_SUMM_REDUCE);
     summaries_reduce_kernel<<<dim3((D.d * D.d + 255) / 256, (unsigned)D.BH), 256, 0, s>>>(
-        ws.hpart, ws.zpart, ws.htot, ws.ztot, D.d == 128 ? ws.hfrag : nullptr, D.d, nch);
+        ws.hpart, ws.zpart, ws.htot, ws.ztot, D.d, nch);
     timing_after(s, K_SUMM_REDUCE);
     return hipGetLastError();
 }
