@@ -37,7 +37,7 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16/fp16 matrix peak
 PEAK_FP8_TFLOPS = 5000.0
 PEAK_HBM_GBS = 8000.0
-COUNTERS = os.path.join(ROOT, "profiles", "fused_mfma_wan14b_counters.json")
+COUNTERS = os.path.join(ROOT, "profiles", "fused128_bf16_wan14b_counters.json")
 
 
 def log(*a):

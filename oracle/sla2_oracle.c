@@ -22,7 +22,7 @@
  *  [SLA2-en] gist.science explainer, section 2A (O = alpha O_s + (1-alpha) O_l,
  *            both branches row-normalised).
  *
- * Readings where the pages are silent (each is listed in the design doc):
+ * Readings where the pages are silent or ambiguous:
  *  - router score is the plain product proj_q(Qbar) . proj_k(Kbar), no 1/sqrt(d)
  *    and no softmax (both are monotone per row and cannot change a hard top-k);
  *  - proj(x) = x W, no bias; W is [w_heads][d][d] row-major, w_heads in {1,H};

@@ -14,26 +14,28 @@
 //                                       times s_Q s_K)
 //   online softmax on S^T               one query per lane column
 //   O^T += V_j^T P^T                    fp16 MFMA (LOWBIT: P on the e4m3 grid)
-//   G^T += V_j^T phi(K_j)               fp16 MFMA; phi(K_j) is evaluated from
-//                                       the K tile already in LDS, read
-//                                       transposed
-//   z   += colsum phi(K_j)
+//   G^T += V_j^T phi(K_j)               fp16 MFMA; phi(K_j)^T comes from the
+//                                       block summaries pass, each wave loads
+//                                       its 32 channels straight into
+//                                       registers
+//   z   += z_j = colsum phi(K_j)        (also from the summaries pass)
 // G starts at -h_tot^T and z at -z_tot, so at the end H_i^T = -G^T and
 // Z_i = -z: the linear branch's sums over the unselected blocks (SLA notes,
 // key designs 3 and 4: H_i, Z_i as the total minus the selected blocks).
 // Epilogue: O_l^T = H_i^T phi(Q)^T / (phi(Q) . Z_i), O = alpha O_s +
 // (1 - alpha) O_l ("SLA2 深度解读" 04).
 //
-// Tiles arrive by direct-to-LDS loads.  K tiles are issued two tiles ahead
-// (three stages; two with LOWBIT and the linear branch, whose K stage holds
-// both Khat and K), V^T tiles one tile ahead (two stages).  LDS layouts:
+// K (or Khat) and V^T tiles arrive by direct-to-LDS loads, K two tiles
+// ahead (three stages), V^T one tile ahead (two stages); the phi(K)^T slice
+// and z_j of the next tile are loaded into registers once the current tile's
+// G^T products have been issued.  LDS layouts:
 //   K    [64 keys][256 B]   16-byte chunk c of row r at chunk c ^ (r & 15)
 //   Khat [64 keys][128 B]   chunk c of row r at chunk c ^ ((r >> 1) & 7)
 //   V^T  [128 ch][128 B]    chunk c of row r at chunk c ^ ((r >> 1) & 7)
 // V^T comes from the block summaries pass in fp16 with the keys of each
 // group of 16 stored at positions with bits 2 and 3 swapped, which makes the
 // k order of P^T (taken straight from the S^T accumulators) line up with it;
-// the transposed reads of K for phi(K) follow the same order.
+// phi(K)^T is stored the same way.
 #include "cdna4.h"
 #include "sla2_internal.h"
 
@@ -49,14 +51,12 @@ constexpr float kRescaleThr = 8.0f;
 
 __shared__ __attribute__((aligned(1024))) char s_lds[kLdsBytes];
 
-template <bool LIN, bool LOWBIT>
+template <bool LOWBIT>
 struct Plan {
-    static constexpr bool kRaw = !LOWBIT || LIN;  // bf16 K staged (Q K^T or phi(K))
-    static constexpr int kRawOff = LOWBIT ? kKHat : 0;
-    static constexpr int kStage = (LOWBIT ? kKHat : 0) + (kRaw ? kKRaw : 0);
-    static constexpr int kStages = (LOWBIT && LIN) ? 2 : 3;
+    static constexpr int kStage = LOWBIT ? kKHat : kKRaw;
+    static constexpr int kStages = 3;
     static constexpr int vOff = kStages * kStage;
-    static constexpr int nK = (LOWBIT ? 2 : 0) + (kRaw ? 4 : 0);  // loads per lane, K tile
+    static constexpr int nK = LOWBIT ? 2 : 4;  // loads per lane, K tile
     static_assert(vOff + 2 * kVT <= kLdsBytes, "LDS budget");
     static_assert(32768 + 512 <= kLdsBytes, "epilogue LDS");
 };
@@ -65,57 +65,66 @@ template <bool LOWBIT> struct QOp;
 template <> struct QOp<false> { bf16x8 f[8]; };  // 8 k-steps of 16 channels
 template <> struct QOp<true> { i32x8 f[2]; };    // 2 k-steps of 64 channels
 
-// K tile j into one K stage: 1 KB pieces, piece u = 4i + w
-template <bool LIN, bool LOWBIT>
-__device__ inline void issue_k(char* kst, const uint16_t* K_h, const uint8_t* khat_h, int j,
-                               int N, int w, int lane) {
-    using P = Plan<LIN, LOWBIT>;
-    if (LOWBIT) {
+// Tile loads.  A tile is moved in 1 KB pieces, piece u = 4i + w going to
+// byte u * 1024 of its LDS stage; the lane's 16 bytes of piece u sit at the
+// same per-lane byte offset (plus 4 KB per i) in every tile, so each load is
+// a uniform base plus one per-lane offset.
+__device__ inline void load_lds16(const char* src, uint32_t off, char* dst) {
+    __builtin_amdgcn_global_load_lds(src + off, SLA2_LDS(dst), 16, 0, 0);
+}
+
+// per-lane offsets: K rows are 256 B (16-byte chunk c of row r at c ^ (r & 15)),
+// Khat and V^T rows 128 B (chunk c of row r at c ^ ((r >> 1) & 7))
+__device__ inline uint32_t k_lane_off(int w, int lane) {
+    const int row = 4 * w + (lane >> 4);
+    return (uint32_t)(row * 256 + (((lane & 15) ^ (row & 15)) << 4));
+}
+__device__ inline uint32_t t_lane_off(int w, int lane) {
+    const int row = 8 * w + (lane >> 3);
+    return (uint32_t)(row * 128 + (((lane & 7) ^ ((row >> 1) & 7)) << 4));
+}
+
+// K (or Khat) tile j into one K stage
+template <bool LOWBIT>
+__device__ inline void issue_k(char* kst, const char* k_h, const char* khat_h, int j, int N,
+                               int w, int lane, uint32_t koff, uint32_t toff) {
+    if (LOWBIT) {  // Khat rows past N are stored (as zeros)
+        const char* src = khat_h + (size_t)j * 8192;
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int u = 4 * i + w;
-            const int row = 8 * u + (lane >> 3);
-            const int lc = (lane & 7) ^ ((row >> 1) & 7);
-            __builtin_amdgcn_global_load_lds(khat_h + ((size_t)j * 64 + row) * 128 + lc * 16,
-                                             SLA2_LDS(kst + u * 1024), 16, 0, 0);
-        }
-    }
-    if (P::kRaw) {
+        for (int i = 0; i < 2; ++i) load_lds16(src + 4096 * i, toff, kst + (4 * i + w) * 1024);
+    } else if (j * 64 + 64 <= N) {
+        const char* src = k_h + (size_t)j * 16384;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) load_lds16(src + 4096 * i, koff, kst + (4 * i + w) * 1024);
+    } else {  // ragged last block: padding rows read row N-1 (their logits are masked)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const int u = 4 * i + w;
-            const int row = 4 * u + (lane >> 4);
-            const int lc = (lane & 15) ^ (row & 15);
-            const int tok = min(j * 64 + row, N - 1);  // padding rows: any valid row
-            __builtin_amdgcn_global_load_lds(K_h + (size_t)tok * 128 + lc * 8,
-                                             SLA2_LDS(kst + P::kRawOff + u * 1024), 16, 0, 0);
+            const int row = 16 * i + 4 * w + (lane >> 4);
+            const int tok = min(j * 64 + row, N - 1);
+            const uint32_t off = (uint32_t)tok * 256 + (koff & 255);
+            load_lds16(k_h, off, kst + (4 * i + w) * 1024);
         }
     }
 }
 
 // V^T tile j into one V stage
-__device__ inline void issue_v(char* vst, const uint16_t* vt_h, int j, int w, int lane) {
-    const uint16_t* src = vt_h + (size_t)j * 128 * 64;
+__device__ inline void issue_v(char* vst, const char* vt_h, int j, int w, uint32_t toff) {
+    const char* src = vt_h + (size_t)j * 16384;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int u = 4 * i + w;
-        const int row = 8 * u + (lane >> 3);
-        const int lc = (lane & 7) ^ ((row >> 1) & 7);
-        __builtin_amdgcn_global_load_lds(src + row * 64 + lc * 8, SLA2_LDS(vst + u * 1024), 16,
-                                         0, 0);
-    }
+    for (int i = 0; i < 4; ++i) load_lds16(src + 4096 * i, toff, vst + (4 * i + w) * 1024);
 }
 
 template <bool LIN, bool LOWBIT>
 __global__ __launch_bounds__(256, 2) void fused128_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
-    const uint16_t* __restrict__ vt, const int32_t* __restrict__ idx,
+    const uint16_t* __restrict__ vt, const uint16_t* __restrict__ pkt,
+    const float* __restrict__ zb, const int32_t* __restrict__ idx,
     const float* __restrict__ alpha, const float* __restrict__ htot,
     const float* __restrict__ ztot, const uint8_t* __restrict__ qhat,
     const uint8_t* __restrict__ khat, const float* __restrict__ sq,
     const float* __restrict__ sk, float* __restrict__ O, int N, int Tq, int Tkv, int k,
     int H) {
-    using P = Plan<LIN, LOWBIT>;
+    using P = Plan<LOWBIT>;
     const int t = threadIdx.x, lane = t & 63, l32 = lane & 31, hl = lane >> 5;
     const int w = __builtin_amdgcn_readfirstlane(t >> 6);
     long bh;
@@ -174,32 +183,58 @@ __global__ __launch_bounds__(256, 2) void fused128_kernel(
     float m_ref = -INFINITY, l_part = 0.0f;
 
     const int32_t* sel = idx + ((size_t)bh * Tq + qb) * k;
-    const uint16_t* K_h = K + (size_t)bh * N * 128;
-    const uint8_t* khat_h = LOWBIT ? khat + (size_t)bh * Tkv * 64 * 128 : nullptr;
-    const uint16_t* vt_h = vt + (size_t)bh * Tkv * 128 * 64;
+    const char* k_h = reinterpret_cast<const char*>(K + (size_t)bh * N * 128);
+    const char* khat_h =
+        LOWBIT ? reinterpret_cast<const char*>(khat + (size_t)bh * Tkv * 64 * 128) : nullptr;
+    const char* vt_h = reinterpret_cast<const char*>(vt + (size_t)bh * Tkv * 128 * 64);
+    const uint32_t koff = k_lane_off(w, lane), toff = t_lane_off(w, lane);
+    // this wave's rows (phi channels 32w .. 32w+31) of the phi(K)^T tiles, and
+    // the matching z_j entries
+    const char* pk_h = reinterpret_cast<const char*>(pkt + (size_t)bh * Tkv * 128 * 64);
+    const uint32_t pkoff = (uint32_t)((32 * w + l32) * 128 + 16 * hl);
+    const char* zb_h = reinterpret_cast<const char*>(zb + (size_t)bh * Tkv * 128);
+    const uint32_t zoff = (uint32_t)(32 * w + l32) * 4;
     const float* sk_h = LOWBIT ? sk + (size_t)bh * Tkv : nullptr;
     char* const kbase = s_lds;
     char* const vbase = s_lds + P::vOff;
     constexpr int DK = P::kStages - 1;  // K prefetch distance
 
-    // ---- prologue: K_0, V_0 [, K_1]
+    // phi(K_j)^T as the B operand of 4 k-steps of 16 keys, and z_j
+    f16x8 pk[4];
+    float zj = 0.0f;
+    auto load_pk = [&](int j) {
+        const char* src = pk_h + (size_t)j * 16384;
+#pragma unroll
+        for (int kq = 0; kq < 4; ++kq)
+            pk[kq] = *reinterpret_cast<const f16x8*>(src + 32 * kq + pkoff);
+        const float z = *reinterpret_cast<const float*>(zb_h + (size_t)j * 512 + zoff);
+        zj = hl == 0 ? z : 0.0f;
+    };
+
+    // ---- prologue: K_0, V_0, K_1 [, phi(K_0)^T, z_0]
     if (k > 0) {
-        issue_k<LIN, LOWBIT>(kbase, K_h, khat_h, sel[0], N, w, lane);
-        issue_v(vbase, vt_h, sel[0], w, lane);
-        if (DK == 2 && k > 1) issue_k<LIN, LOWBIT>(kbase + P::kStage, K_h, khat_h, sel[1], N, w, lane);
+        issue_k<LOWBIT>(kbase, k_h, khat_h, sel[0], N, w, lane, koff, toff);
+        issue_v(vbase, vt_h, sel[0], w, toff);
+        if (k > 1) issue_k<LOWBIT>(kbase + P::kStage, k_h, khat_h, sel[1], N, w, lane, koff, toff);
+        asm volatile("" ::: "memory");
+        if (LIN) load_pk(sel[0]);
+        asm volatile("" ::: "memory");
     }
 
     int kslot = 0;
     for (int r = 0; r < k; ++r) {
         // tile r's K and V^T have landed for this wave (loads issued after
-        // V_r, at most one K tile, may still be in flight) ...
-        if (DK == 2 && r + 1 < k) wait_vmcnt<P::nK>();
+        // V_r: at most one K tile and the phi(K_r)^T slice, may still be in
+        // flight; the compiler waits for the latter before its use) ...
+        if (r + 1 < k) wait_vmcnt<P::nK + (LIN ? 5 : 0)>();
+        else if (LIN) wait_vmcnt<5>();
         else wait_vmcnt<0>();
         wg_barrier();  // ... and for every wave; all waves are done with tile r-1
-        if (r + 1 < k) issue_v(vbase + ((r + 1) & 1) * kVT, vt_h, sel[r + 1], w, lane);
+        if (r + 1 < k) issue_v(vbase + ((r + 1) & 1) * kVT, vt_h, sel[r + 1], w, toff);
         if (r + DK < k) {
             const int s2 = kslot + DK >= P::kStages ? kslot + DK - P::kStages : kslot + DK;
-            issue_k<LIN, LOWBIT>(kbase + s2 * P::kStage, K_h, khat_h, sel[r + DK], N, w, lane);
+            issue_k<LOWBIT>(kbase + s2 * P::kStage, k_h, khat_h, sel[r + DK], N, w, lane, koff,
+                            toff);
         }
         const int j = sel[r];
         const char* kst = kbase + kslot * P::kStage;
@@ -300,38 +335,23 @@ __global__ __launch_bounds__(256, 2) void fused128_kernel(
             }
 
         // O^T += V^T P^T and G^T += V^T phi(K)
-        const char* kraw = kst + P::kRawOff;
 #pragma unroll
-        for (int kq = 0; kq < 4; ++kq) {
-            f16x8 phk;
-            if (LIN) {
-                // keys 16kq + 8a + 4hl + e (e = 0..3) of channel 32w + l32:
-                // source lane r of each 16-lane group reads row
-                // 16kq + 8a + 4hl + r/4, channels cb + 4(r%4) .. +3
-                const int r16 = lane & 15;
-                const int ch = 32 * w + 16 * ((lane >> 4) & 1) + 4 * (r16 & 3);
-#pragma unroll
-                for (int a = 0; a < 2; ++a) {
-                    const int row = 16 * kq + 8 * a + 4 * hl + (r16 >> 2);
-                    const s16x4 raw = lds_read_tr16(
-                        kraw + row * 256 + ((((ch >> 3) ^ (row & 15))) << 4) + ((ch & 7) << 1));
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        float ph = phi_fast(bf16_bits((unsigned short)raw[e]));
-                        if (ragged && j * 64 + 16 * kq + 8 * a + 4 * hl + e >= N) ph = 0.0f;
-                        zacc += ph;
-                        phk[4 * a + e] = (_Float16)ph;
-                    }
-                }
-            }
+        for (int kq = 0; kq < 4; ++kq)
 #pragma unroll
             for (int mt = 0; mt < 4; ++mt) {
                 const int erow = 32 * mt + l32;
                 const f16x8 a = *reinterpret_cast<const f16x8*>(
                     vst + erow * 128 + (((2 * kq + hl) ^ ((erow >> 1) & 7)) << 4));
                 o[mt] = mfma_f16(a, pf[kq], o[mt]);
-                if (LIN) g[mt] = mfma_f16(a, phk, g[mt]);
+                if (LIN) g[mt] = mfma_f16(a, pk[kq], g[mt]);
             }
+        if (LIN) {
+            zacc += zj;
+            // the waits above count these loads as issued last in the
+            // iteration: keep the compiler from moving them
+            asm volatile("" ::: "memory");
+            if (r + 1 < k) load_pk(sel[r + 1]);
+            asm volatile("" ::: "memory");
         }
     }
 
@@ -428,23 +448,15 @@ hipError_t launch_fused128(const Dims& D, const void* Q, const void* K, const in
     const bool lin = D.k < D.Tkv;
     const uint16_t* q = (const uint16_t*)Q;
     const uint16_t* kk = (const uint16_t*)K;
+    const uint8_t* qh = lowbit ? ws.qhat : nullptr;
+    const uint8_t* kh = lowbit ? ws.khat : nullptr;
+    const float* sq = lowbit ? ws.sq : nullptr;
+    const float* sk = lowbit ? ws.sk : nullptr;
+    auto kern = lowbit ? (lin ? fused128_kernel<true, true> : fused128_kernel<false, true>)
+                       : (lin ? fused128_kernel<true, false> : fused128_kernel<false, false>);
     timing_before(s, lowbit ? K_FUSED_FP8 : K_FUSED_MFMA);
-    if (!lowbit && lin)
-        fused128_kernel<true, false><<<g, 256, 0, s>>>(q, kk, ws.vt, idx, alpha, ws.htot, ws.ztot,
-                                                      nullptr, nullptr, nullptr, nullptr, O, D.N,
-                                                      D.Tq, D.Tkv, D.k, D.H);
-    else if (!lowbit)
-        fused128_kernel<false, false><<<g, 256, 0, s>>>(q, kk, ws.vt, idx, alpha, ws.htot,
-                                                       ws.ztot, nullptr, nullptr, nullptr,
-                                                       nullptr, O, D.N, D.Tq, D.Tkv, D.k, D.H);
-    else if (lin)
-        fused128_kernel<true, true><<<g, 256, 0, s>>>(q, kk, ws.vt, idx, alpha, ws.htot, ws.ztot,
-                                                     ws.qhat, ws.khat, ws.sq, ws.sk, O, D.N,
-                                                     D.Tq, D.Tkv, D.k, D.H);
-    else
-        fused128_kernel<false, true><<<g, 256, 0, s>>>(q, kk, ws.vt, idx, alpha, ws.htot,
-                                                      ws.ztot, ws.qhat, ws.khat, ws.sq, ws.sk, O,
-                                                      D.N, D.Tq, D.Tkv, D.k, D.H);
+    kern<<<g, 256, 0, s>>>(q, kk, ws.vt, ws.pkt, ws.zb, idx, alpha, ws.htot, ws.ztot, qh, kh, sq,
+                           sk, O, D.N, D.Tq, D.Tkv, D.k, D.H);
     timing_after(s, lowbit ? K_FUSED_FP8 : K_FUSED_MFMA);
     return hipGetLastError();
 }

@@ -2,13 +2,13 @@
 // fused kernel for d = 64 (d = 128 has its own kernel, fused128.hip).
 //
 // 1) summaries_mfma: one pass over K and V.  Per KV block j of 64 tokens it
-//    writes V_j^T in fp16, block-transposed ([d][64]) with the token order
-//    permuted inside each group of 16 (positions = token index with bits 2
-//    and 3 swapped), and accumulates h = sum_j phi(K_j)^T V_j and
-//    z = sum_j colsum phi(K_j) on the matrix cores into per-chunk partials
-//    (reduced in a fixed order afterwards).  For d = 64 it also keeps
-//    phi(K_j)^T and z_j per block.  Linear-branch block summaries: SLA notes,
-//    key design 4 (h_j = phi(K_j)^T V_j, z_j).
+//    writes V_j^T and phi(K_j)^T in fp16, block-transposed ([d][64]) with the
+//    token order permuted inside each group of 16 (positions = token index
+//    with bits 2 and 3 swapped), and the per-block z_j = colsum phi(K_j); it
+//    accumulates h = sum_j phi(K_j)^T V_j and z = sum_j z_j on the matrix
+//    cores into per-chunk partials (reduced in a fixed order afterwards).
+//    Linear-branch block summaries: SLA notes, key design 4 (h_j =
+//    phi(K_j)^T V_j, z_j).
 // 2) fused_mfma (d = 64): per (head, query block of 128) a work-group of 4
 //    waves; wave w owns queries 32w..32w+31.  For every selected KV block
 //    (ascending):
@@ -51,9 +51,6 @@ __global__ __launch_bounds__(256) void summaries_mfma_kernel(
     const uint16_t* __restrict__ K, const uint16_t* __restrict__ V, uint16_t* __restrict__ vt,
     uint16_t* __restrict__ pkt, float* __restrict__ zb, float* __restrict__ hpart,
     float* __restrict__ zpart, int N, int Tkv, int nch) {
-    // phi(K)^T tiles and per-block z_j are kept only for the d = 64 kernel,
-    // which gathers them per tile; the d = 128 kernel evaluates phi(K) itself
-    constexpr bool PER_BLOCK = D == 64;
     constexpr int NT = D / 32;
     constexpr int TPW = NT * NT / 4;  // h^T tiles per wave
     __shared__ __attribute__((aligned(16))) char sV[D * kTPitch];
@@ -113,17 +110,15 @@ __global__ __launch_bounds__(256) void summaries_mfma_kernel(
             const int row = x >> 3, c16 = x & 7;
             *reinterpret_cast<uint4*>(gv + row * 64 + c16 * 8) =
                 *reinterpret_cast<const uint4*>(sV + row * kTPitch + c16 * 16);
-            if (PER_BLOCK) {
-                uint16_t* gp = pkt + ((size_t)bh * Tkv + j) * D * 64;
-                *reinterpret_cast<uint4*>(gp + row * 64 + c16 * 8) =
-                    *reinterpret_cast<const uint4*>(sP + row * kTPitch + c16 * 16);
-            }
+            uint16_t* gp = pkt + ((size_t)bh * Tkv + j) * D * 64;
+            *reinterpret_cast<uint4*>(gp + row * 64 + c16 * 8) =
+                *reinterpret_cast<const uint4*>(sP + row * kTPitch + c16 * 16);
         }
         if (t < D) {
             float z = 0.0f;
             const _Float16* rowp = reinterpret_cast<const _Float16*>(sP + t * kTPitch);
             for (int p = 0; p < 64; ++p) z += (float)rowp[p];
-            if (PER_BLOCK) zb[((size_t)bh * Tkv + j) * D + t] = z;
+            zb[((size_t)bh * Tkv + j) * D + t] = z;
             zacc += z;
         }
         // h^T (V channels x phi(K) channels) += V_j^T phi(K_j)

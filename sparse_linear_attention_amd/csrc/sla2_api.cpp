@@ -86,10 +86,8 @@ size_t layout_forward(const Dims& D, int op, char* base, FwdWS* ws) {
     const int nch = summ_chunks(D);
     if (D.dtype == SLA2_BF16) {
         w.vt = carve<uint16_t>(base, off, 2 * bh * D.Tkv * d * 64);
-        if (D.d == 64) {  // the d = 64 kernel gathers phi(K)^T and z_j per tile
-            w.pkt = carve<uint16_t>(base, off, 2 * bh * D.Tkv * d * 64);
-            w.zb = carve<float>(base, off, 4 * bh * D.Tkv * d);
-        }
+        w.pkt = carve<uint16_t>(base, off, 2 * bh * D.Tkv * d * 64);
+        w.zb = carve<float>(base, off, 4 * bh * D.Tkv * d);
     }
     w.hpart = carve<float>(base, off, 4 * bh * nch * d * d);
     w.zpart = carve<float>(base, off, 4 * bh * nch * d);

@@ -55,8 +55,8 @@ struct FwdWS {
     // bf16 path: block-transposed fp16 copies, kv order permuted inside each
     // group of 16 (see the fused kernel), padding tokens are 0
     uint16_t* vt;    // [BH][Tkv][d][64]  V^T      (fp16 bits)
-    uint16_t* pkt;   // [BH][Tkv][d][64]  phi(K)^T (fp16 bits; d = 64 only)
-    float* zb;       // [BH][Tkv][d]      per-block z_j (d = 64 only)
+    uint16_t* pkt;   // [BH][Tkv][d][64]  phi(K)^T (fp16 bits)
+    float* zb;       // [BH][Tkv][d]      per-block z_j
     float* hpart;    // [BH][chunks][d][d] partial h per chunk
     float* zpart;    // [BH][chunks][d]
     float* htot;     // [BH][d][d]        h_tot[c][e] = sum phi(K)[.,c] V[.,e]
