@@ -242,7 +242,44 @@ __global__ __launch_bounds__(256, 2) void fused128_kernel(
         kslot = kslot + 1 == P::kStages ? 0 : kslot + 1;
         const float c_tile = LOWBIT ? c_base * sk_h[j] : c_base;
 
-        // S^T = K Q^T, two m-tiles of 32 keys
+        const bool ragged = j * 64 + 64 > N;
+        const f16x2 ones = {(_Float16)1.0f, (_Float16)1.0f};
+        // O^T += V^T P^T and G^T += V^T phi(K) for k-step kq (16 keys); the
+        // V^T operand is read once for both products
+        auto pv_step = [&](int kq, const f16x8& pfk) {
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt) {
+                const int erow = 32 * mt + l32;
+                const f16x8 a = *reinterpret_cast<const f16x8*>(
+                    vst + erow * 128 + (((2 * kq + hl) ^ ((erow >> 1) & 7)) << 4));
+                o[mt] = mfma_f16(a, pfk, o[mt]);
+                if (LIN) g[mt] = mfma_f16(a, pk[kq], g[mt]);
+            }
+        };
+        // new running reference after a block of logits whose maximum (over
+        // this wave's column, both lane halves) is mx; rescales O and l
+        auto update_ref = [&](float mx) {
+            const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx),
+                                                             __float_as_uint(mx), false, false);
+            mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+            const float xmax = mx * c_tile;
+            const bool need = LOWBIT ? (xmax > m_ref) : (xmax > m_ref + kRescaleThr);
+            if (__ballot(need)) {
+                const float nref = need ? xmax : m_ref;
+                const float f = __builtin_amdgcn_exp2f(m_ref - nref);
+                l_part *= f;
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) o[i][e] *= f;
+                m_ref = nref;
+            }
+            return m_ref == -INFINITY ? 0.0f : m_ref;
+        };
+
+        // S^T = K Q^T over the whole tile (two m-tiles of 32 keys); the
+        // running maximum is updated once per tile (with LOWBIT the
+        // quantisation grid of P follows it)
         f32x16 s[2] = {zero16(), zero16()};
         if (LOWBIT) {
 #pragma unroll
@@ -269,82 +306,50 @@ __global__ __launch_bounds__(256, 2) void fused128_kernel(
                     s[mt] = mfma_bf16(a, reinterpret_cast<const bf16x8*>(Qo.f)[ks], s[mt]);
                 }
         }
-        const bool ragged = j * 64 + 64 > N;
         if (ragged) {
 #pragma unroll
             for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
                 for (int i = 0; i < 16; ++i)
-                    if (j * 64 + 32 * mt + 8 * (i >> 2) + 4 * hl + (i & 3) >= N) s[mt][i] = -INFINITY;
+                    if (j * 64 + 32 * mt + 8 * (i >> 2) + 4 * hl + (i & 3) >= N)
+                        s[mt][i] = -INFINITY;
         }
-
-        // online softmax (log2 units)
         float mx = s[0][0];
 #pragma unroll
         for (int i = 1; i < 16; ++i) mx = fmaxf(mx, s[0][i]);
 #pragma unroll
         for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[1][i]);
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float xmax = mx * c_tile;
-        const bool need = LOWBIT ? (xmax > m_ref) : (xmax > m_ref + kRescaleThr);
-        if (__ballot(need)) {
-            const float nref = need ? xmax : m_ref;
-            const float f = __builtin_amdgcn_exp2f(m_ref - nref);
-            l_part *= f;
+        const float mref = update_ref(mx);
+        // P^T as the B operand of k-step kq (16 keys) takes rows 8(kq&1)..
+        // 8(kq&1)+7 of m-tile kq>>1
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int e = 0; e < 16; ++e) o[i][e] *= f;
-            m_ref = nref;
-        }
-        const float mref = m_ref == -INFINITY ? 0.0f : m_ref;
-        // P^T as the B operand of 4 k-steps of 16 keys: k-step kq takes rows
-        // 8(kq&1)..8(kq&1)+7 of m-tile kq>>1
-        f16x8 pf[4];
-        if (LOWBIT) {  // 256 P~ rounded onto the e4m3 grid, carried exactly in fp16
-            const float bias = 8.0f - mref;
-#pragma unroll
-            for (int kq = 0; kq < 4; ++kq)
+        for (int kq = 0; kq < 4; ++kq) {
+            f16x8 pf;
+            if (LOWBIT) {  // 256 P~ rounded onto the e4m3 grid, carried exactly in fp16
+                const float bias = 8.0f - mref;
 #pragma unroll
                 for (int e = 0; e < 8; e += 2) {
-                    const float x0 = s[kq >> 1][8 * (kq & 1) + e];
-                    const float x1 = s[kq >> 1][8 * (kq & 1) + e + 1];
-                    const float p0 = __builtin_amdgcn_exp2f(fmaf(x0, c_tile, bias));
-                    const float p1 = __builtin_amdgcn_exp2f(fmaf(x1, c_tile, bias));
+                    const float p0 = __builtin_amdgcn_exp2f(fmaf(s[kq >> 1][8 * (kq & 1) + e], c_tile, bias));
+                    const float p1 = __builtin_amdgcn_exp2f(fmaf(s[kq >> 1][8 * (kq & 1) + e + 1], c_tile, bias));
                     const int code = __builtin_amdgcn_cvt_pk_fp8_f32(fminf(p0, 448.0f),
                                                                      fminf(p1, 448.0f), 0, false);
                     const auto back = __builtin_amdgcn_cvt_pk_f32_fp8(code, false);
-                    pf[kq][e] = (_Float16)back[0];
-                    pf[kq][e + 1] = (_Float16)back[1];
+                    pf[e] = (_Float16)back[0];
+                    pf[e + 1] = (_Float16)back[1];
                 }
-        } else {
-#pragma unroll
-            for (int kq = 0; kq < 4; ++kq)
+            } else {
 #pragma unroll
                 for (int e = 0; e < 8; ++e)
-                    pf[kq][e] = (_Float16)__builtin_amdgcn_exp2f(
+                    pf[e] = (_Float16)__builtin_amdgcn_exp2f(
                         fmaf(s[kq >> 1][8 * (kq & 1) + e], c_tile, -mref));
-        }
-        const f16x2 ones = {(_Float16)1.0f, (_Float16)1.0f};
-#pragma unroll
-        for (int kq = 0; kq < 4; ++kq)
+            }
 #pragma unroll
             for (int e = 0; e < 8; e += 2) {
-                const f16x2 pr = {pf[kq][e], pf[kq][e + 1]};
+                const f16x2 pr = {pf[e], pf[e + 1]};
                 l_part = __builtin_amdgcn_fdot2(pr, ones, l_part, false);
             }
-
-        // O^T += V^T P^T and G^T += V^T phi(K)
-#pragma unroll
-        for (int kq = 0; kq < 4; ++kq)
-#pragma unroll
-            for (int mt = 0; mt < 4; ++mt) {
-                const int erow = 32 * mt + l32;
-                const f16x8 a = *reinterpret_cast<const f16x8*>(
-                    vst + erow * 128 + (((2 * kq + hl) ^ ((erow >> 1) & 7)) << 4));
-                o[mt] = mfma_f16(a, pf[kq], o[mt]);
-                if (LIN) g[mt] = mfma_f16(a, pk[kq], g[mt]);
-            }
+            pv_step(kq, pf);
+        }
         if (LIN) {
             zacc += zj;
             // the waits above count these loads as issued last in the
