@@ -22,12 +22,15 @@
  *    pointers owned by the caller.  The library never allocates, frees or
  *    synchronises device memory; all work is enqueued on `stream` (a
  *    hipStream_t; NULL = the default stream) in call order.
- *  - Q, K, V, O are [B, H, N, d] contiguous, d innermost.  Q, K, V share one
- *    dtype (problem.dtype); O is always fp32.
+ *  - Q, K, V and O share one memory layout (problem.layout): [B, H, N, d]
+ *    (SLA2_LAYOUT_BHND) or [B, N, H, d] (SLA2_LAYOUT_BNHD, the token-major
+ *    layout of a DiT block's attention), contiguous, d innermost.  Q, K, V
+ *    share one dtype (problem.dtype); O is fp32 or bf16 (problem.out_dtype).
  *  - Every argument is validated on the host before anything is launched; on
  *    any error nothing is launched and no output is written.
  *  - Returned codes: SLA2_OK; SLA2_EINVAL (null or misaligned pointer,
- *    B/H/N <= 0, topk_frac outside [0,1] or NaN, w_heads not in {1,H});
+ *    B/H/N <= 0, topk_frac outside [0,1] or NaN, w_heads not in {1,H}, an
+ *    unknown layout, alpha mode or output dtype);
  *    SLA2_EUNSUPPORTED (a valid but unbuilt combination: d not in {64,128},
  *    bq not in {64,128}, bkv != 64, phi other than elu+1, fp8 with fp32
  *    inputs or with bq or d other than 128, more than 65535 heads or a number of blocks outside the limits
@@ -67,6 +70,14 @@ typedef enum { SLA2_F32 = 0, SLA2_BF16 = 1 } sla2_dtype;
 /* feature map of the linear branch: elu(x) + 1, elementwise on raw Q and K */
 typedef enum { SLA2_PHI_ELU1 = 0 } sla2_phi;
 
+/* memory layout of Q, K, V and O */
+typedef enum { SLA2_LAYOUT_BHND = 0, SLA2_LAYOUT_BNHD = 1 } sla2_layout;
+
+/* granularity of the combine weight alpha ("SLA2 深度解读" 08 gives alpha per
+ * query block in the algorithm and per query in the text): one value per head
+ * (alpha [H]) or one per head and query block (alpha [H][T_q]) */
+typedef enum { SLA2_ALPHA_PER_HEAD = 0, SLA2_ALPHA_PER_QBLOCK = 1 } sla2_alpha_mode;
+
 /* operations, for sla2_workspace_bytes */
 typedef enum { SLA2_OP_ROUTE = 0, SLA2_OP_FORWARD = 1, SLA2_OP_FORWARD_FP8 = 2 } sla2_op;
 
@@ -77,6 +88,9 @@ typedef struct {
     int32_t w_heads;     /* 1: one Wq/Wk pair for all heads; H: one per head    */
     int32_t phi;         /* sla2_phi                                            */
     int32_t dtype;       /* sla2_dtype of Q, K, V                               */
+    int32_t layout;      /* sla2_layout of Q, K, V and O                        */
+    int32_t alpha_mode;  /* sla2_alpha_mode                                     */
+    int32_t out_dtype;   /* sla2_dtype of O (SLA2_F32 or SLA2_BF16)             */
 } sla2_problem;
 
 /* T_q = ceil(N / bq) and T_kv = ceil(N / bkv).  The last block of each kind
@@ -99,7 +113,7 @@ sla2_status sla2_check(const sla2_problem* p, int32_t op);
 const char* sla2_status_str(int32_t status);
 
 /*
- * sla2_route -- the block router ("SLA2 深度解读" 05).
+ * sla2_route -- the block router ("SLA2 深度解读" 05).  Q, K in problem.layout.
  *   Qbar_i = mean of the valid rows of query block i, Kbar_j likewise;
  *   qt_i = Qbar_i Wq[h'], kt_j = Kbar_j Wk[h'] (h' = 0 if w_heads == 1,
  *   else h; W row-major [d][d], proj(x) = x W, no bias);
@@ -107,7 +121,7 @@ const char* sla2_status_str(int32_t status);
  *   not change a per-row top-k); the k largest S_ij of each row are
  *   selected, ties going to the lower block index.  All router arithmetic is
  *   fp64, so the selection does not depend on fp32 rounding.
- * In : Q, K [B,H,N,d] (dtype); Wq, Wk [w_heads,d,d] fp32.
+ * In : Q, K (dtype, problem.layout); Wq, Wk [w_heads,d,d] fp32.
  * Out: topk_idx [B,H,T_q,k] int32, each row ascending (may be NULL if k = 0);
  *      block_mask [B,H,T_q,T_kv] uint8 0/1, or NULL if not wanted.
  * ws : sla2_workspace_bytes(p, SLA2_OP_ROUTE) bytes.
@@ -124,10 +138,13 @@ sla2_status sla2_route(const sla2_problem* p, const void* Q, const void* K,
  *        h_j = phi(K_j)^T V_j, Z_i = sum of z_j = colsum phi(K_j) (SLA notes,
  *        key design 3 and 4); evaluated as (total - selected); O_l = 0 when
  *        k = T_kv.
- *   O   = alpha_h O_s + (1 - alpha_h) O_l, written for the N valid rows.
- * In : Q, K, V [B,H,N,d]; topk_idx [B,H,T_q,k] from sla2_route (ascending,
- *      values in [0,T_kv), not checked on the device); alpha [H] fp32.
- * Out: O [B,H,N,d] fp32.
+ *   O   = alpha O_s + (1 - alpha) O_l, written for the N valid rows; alpha is
+ *        that of the row's head (and query block, with SLA2_ALPHA_PER_QBLOCK).
+ * In : Q, K, V in problem.layout; topk_idx [B,H,T_q,k] from sla2_route
+ *      (ascending, values in [0,T_kv), not checked on the device); alpha fp32
+ *      [H] or [H][T_q] (problem.alpha_mode).
+ * Out: O in problem.layout, fp32 or bf16 (problem.out_dtype; bf16 is O
+ *      computed in fp32 and rounded to nearest even once).
  * ws : sla2_workspace_bytes(p, SLA2_OP_FORWARD) bytes.
  * Precision: fp32 inputs are computed in fp32 throughout (vector ALU), and
  * so are bf16 inputs with bq = 64.  bf16 inputs with bq = 128: Q K^T
@@ -137,7 +154,7 @@ sla2_status sla2_route(const sla2_problem* p, const void* Q, const void* K,
  */
 sla2_status sla2_forward(const sla2_problem* p, const void* Q, const void* K,
                          const void* V, const int32_t* topk_idx, const float* alpha,
-                         float* O, void* ws, size_t ws_bytes, void* stream);
+                         void* O, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * sla2_forward_fp8 -- as sla2_forward, with the low-bit sparse branch
@@ -162,12 +179,13 @@ sla2_status sla2_forward(const sla2_problem* p, const void* Q, const void* K,
  */
 sla2_status sla2_forward_fp8(const sla2_problem* p, const void* Q, const void* K,
                              const void* V, const int32_t* topk_idx, const float* alpha,
-                             float* O, void* ws, size_t ws_bytes, void* stream);
+                             void* O, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * sla2_quantize_fp8 -- the low-bit inputs alone (the quantisation step that
  * sla2_forward_fp8 runs first), for inspection.  Requires dtype == SLA2_BF16.
  * Out (device): Qhat [B,H,T_q*bq,d] and Khat [B,H,T_kv*bkv,d] e4m3 codes
+ * (always head-major, whatever the layout of Q and K)
  * (rows past N are 0), s_Q [B,H,T_q], s_K [B,H,T_kv], mu [B,H,d] fp32.
  * ws : sla2_workspace_bytes(p, SLA2_OP_FORWARD_FP8) bytes.
  */

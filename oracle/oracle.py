@@ -31,7 +31,7 @@ def build(force: bool = True) -> str:
 class Problem(C.Structure):
     _fields_ = [("B", C.c_int32), ("H", C.c_int32), ("N", C.c_int32), ("d", C.c_int32),
                 ("bq", C.c_int32), ("bkv", C.c_int32), ("topk_frac", C.c_float),
-                ("w_heads", C.c_int32), ("dtype", C.c_int32)]
+                ("w_heads", C.c_int32), ("dtype", C.c_int32), ("alpha_mode", C.c_int32)]
 
 
 _lib = None
@@ -66,8 +66,10 @@ def _ptr(a):
     return None if a is None else a.ctypes.data
 
 
-def problem(B, H, N, d, bq, bkv, frac, w_heads=1, dtype="f32") -> Problem:
-    return Problem(B, H, N, d, bq, bkv, float(frac), w_heads, 0 if dtype == "f32" else 1)
+def problem(B, H, N, d, bq, bkv, frac, w_heads=1, dtype="f32", alpha_mode=0) -> Problem:
+    """alpha_mode 0: alpha [H]; 1: alpha [H][T_q] (one per query block)."""
+    return Problem(B, H, N, d, bq, bkv, float(frac), w_heads, 0 if dtype == "f32" else 1,
+                   alpha_mode)
 
 
 def problem_of(x) -> Problem:

@@ -31,7 +31,8 @@
  *    divide by the valid count, no logit, no phi term);
  *  - phi = elu + 1 elementwise on raw Q and K;
  *  - empty selected set -> O_s = 0; empty unselected set -> O_l = 0;
- *  - alpha is per head;
+ *  - alpha is per head, or per head and query block (the algorithm's
+ *    granularity; alpha_mode 1);
  *  - low bit: OCP fp8 e4m3 (max 448), RNE, saturating; per-block absmax
  *    scales (Q: b_q tokens, K: b_kv tokens); K smoothed by its mean over the N
  *    valid tokens (sparse-branch QK^T only); P quantised as e4m3(256 P~)/256
@@ -51,6 +52,7 @@ typedef struct {
     float topk_frac;
     int32_t w_heads;
     int32_t dtype; /* 0: Q,K,V are float32; 1: Q,K,V are bf16 bit patterns */
+    int32_t alpha_mode; /* 0: alpha [H]; 1: alpha [H][T_q], one per query block */
 } orc_problem;
 
 /* ------------------------------------------------------------------ */
@@ -605,7 +607,8 @@ static void forward_block(void* vctx, long it) {
     int d = p->d, Tq = ceil_div(p->N, p->bq), Tkv = ceil_div(p->N, p->bkv);
     int k = orc_topk(p);
     int h = (int)(F->bh % p->H);
-    double a = (double)F->alpha[h];
+    /* step 8 weight: per head, or per head and query block */
+    double a = (double)(p->alpha_mode ? F->alpha[(size_t)h * Tq + i] : F->alpha[h]);
     const int32_t* sel = F->idx + ((size_t)F->bh * Tq + i) * k;
     double* out = F->out + (size_t)pos * p->bq * d;
     memset(out, 0, sizeof(double) * (size_t)p->bq * d);

@@ -21,18 +21,19 @@ __device__ inline float bf16_hi(unsigned w) { return __uint_as_float(w & 0xffff0
 
 // Column sums of K over chunks of 1024 tokens, in fp64.  grid (chunks, BH).
 __global__ __launch_bounds__(256) void ksum_kernel(const uint16_t* __restrict__ K,
-                                                   double* __restrict__ part, int N, int nch) {
+                                                   double* __restrict__ part, int N, int nch,
+                                                   int H, Strides st) {
     __shared__ double red[16][128];
     const long bh = blockIdx.y;
     const int chunk = blockIdx.x;
     const int g = threadIdx.x & 15, r = threadIdx.x >> 4;  // 16 channel groups x 16 rows
     const int t0 = chunk * kTokPerChunk, t1 = min(N, t0 + kTokPerChunk);
-    const uint16_t* Kh = K + (size_t)bh * N * 128;
+    const uint16_t* Kh = K + head_base(st, bh, H);
     double s[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) s[e] = 0.0;
     for (int t = t0 + r; t < t1; t += 16) {
-        const uint4 v = *reinterpret_cast<const uint4*>(Kh + (size_t)t * 128 + g * 8);
+        const uint4 v = *reinterpret_cast<const uint4*>(Kh + (size_t)t * st.t + g * 8);
         const unsigned w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -72,7 +73,7 @@ __device__ inline unsigned e4m3_pair(float a, float b) {
 __global__ __launch_bounds__(256) void quant_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const float* __restrict__ mu, uint8_t* __restrict__ qhat, uint8_t* __restrict__ khat,
-    float* __restrict__ sq, float* __restrict__ sk, int N, int Tq, int Tkv) {
+    float* __restrict__ sq, float* __restrict__ sk, int N, int Tq, int Tkv, int H, Strides st) {
     __shared__ float red[256];
     __shared__ float s_scale;
     const int blk = blockIdx.x;
@@ -82,7 +83,7 @@ __global__ __launch_bounds__(256) void quant_kernel(
     const int bs = isq ? 128 : 64;
     const int t0 = j * bs;
     const int n = min(bs, N - t0);
-    const uint16_t* X = (isq ? Q : K) + (size_t)bh * N * 128;
+    const uint16_t* X = (isq ? Q : K) + head_base(st, bh, H);
     const int g = threadIdx.x & 15, r = threadIdx.x >> 4;  // 16 groups x 16 rows
     float m8[8];
 #pragma unroll
@@ -91,7 +92,7 @@ __global__ __launch_bounds__(256) void quant_kernel(
     // pass 1: block absmax of Q or of K - mu
     float amax = 0.0f;
     for (int row = r; row < n; row += 16) {
-        const uint4 v = *reinterpret_cast<const uint4*>(X + (size_t)(t0 + row) * 128 + g * 8);
+        const uint4 v = *reinterpret_cast<const uint4*>(X + (size_t)(t0 + row) * st.t + g * 8);
         const unsigned w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -118,7 +119,7 @@ __global__ __launch_bounds__(256) void quant_kernel(
     for (int row = r; row < bs; row += 16) {
         uint2 codes = make_uint2(0, 0);
         if (row < n) {
-            const uint4 v = *reinterpret_cast<const uint4*>(X + (size_t)(t0 + row) * 128 + g * 8);
+            const uint4 v = *reinterpret_cast<const uint4*>(X + (size_t)(t0 + row) * st.t + g * 8);
             const unsigned w[4] = {v.x, v.y, v.z, v.w};
             unsigned pk[4];
 #pragma unroll
@@ -138,13 +139,14 @@ hipError_t launch_quantize_fp8(const Dims& D, const void* Q, const void* K, cons
                                hipStream_t s) {
     const int nch = (D.N + kTokPerChunk - 1) / kTokPerChunk;
     timing_before(s, K_QUANT_MEAN);
-    ksum_kernel<<<dim3(nch, (unsigned)D.BH), 256, 0, s>>>((const uint16_t*)K, ws.ksum, D.N, nch);
+    ksum_kernel<<<dim3(nch, (unsigned)D.BH), 256, 0, s>>>((const uint16_t*)K, ws.ksum, D.N, nch,
+                                                          D.H, D.st);
     kmean_kernel<<<dim3((unsigned)D.BH), 128, 0, s>>>(ws.ksum, ws.mu, D.N, nch);
     timing_after(s, K_QUANT_MEAN);
     timing_before(s, K_QUANT);
     quant_kernel<<<dim3(D.Tq + D.Tkv, (unsigned)D.BH), 256, 0, s>>>(
         (const uint16_t*)Q, (const uint16_t*)K, ws.mu, ws.qhat, ws.khat, ws.sq, ws.sk, D.N, D.Tq,
-        D.Tkv);
+        D.Tkv, D.H, D.st);
     timing_after(s, K_QUANT);
     return hipGetLastError();
 }

@@ -73,11 +73,13 @@ __device__ inline void load_lds16(const char* src, uint32_t off, char* dst) {
     __builtin_amdgcn_global_load_lds(src + off, SLA2_LDS(dst), 16, 0, 0);
 }
 
-// per-lane offsets: K rows are 256 B (16-byte chunk c of row r at c ^ (r & 15)),
-// Khat and V^T rows 128 B (chunk c of row r at c ^ ((r >> 1) & 7))
-__device__ inline uint32_t k_lane_off(int w, int lane) {
+// per-lane offsets: K rows are 256 B apart in LDS (16-byte chunk c of row r
+// at c ^ (r & 15)) and rp bytes apart in global memory (256 for [B,H,N,d],
+// 256 H for [B,N,H,d]); Khat and V^T rows are 128 B (chunk c of row r at
+// c ^ ((r >> 1) & 7))
+__device__ inline uint32_t k_lane_off(int w, int lane, uint32_t rp) {
     const int row = 4 * w + (lane >> 4);
-    return (uint32_t)(row * 256 + (((lane & 15) ^ (row & 15)) << 4));
+    return (uint32_t)row * rp + ((uint32_t)((lane & 15) ^ (row & 15)) << 4);
 }
 __device__ inline uint32_t t_lane_off(int w, int lane) {
     const int row = 8 * w + (lane >> 3);
@@ -87,21 +89,22 @@ __device__ inline uint32_t t_lane_off(int w, int lane) {
 // K (or Khat) tile j into one K stage
 template <bool LOWBIT>
 __device__ inline void issue_k(char* kst, const char* k_h, const char* khat_h, int j, int N,
-                               int w, int lane, uint32_t koff, uint32_t toff) {
+                               int w, int lane, uint32_t koff, uint32_t toff, uint32_t rp) {
     if (LOWBIT) {  // Khat rows past N are stored (as zeros)
         const char* src = khat_h + (size_t)j * 8192;
 #pragma unroll
         for (int i = 0; i < 2; ++i) load_lds16(src + 4096 * i, toff, kst + (4 * i + w) * 1024);
     } else if (j * 64 + 64 <= N) {
-        const char* src = k_h + (size_t)j * 16384;
+        const char* src = k_h + (size_t)j * 64 * rp;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) load_lds16(src + 4096 * i, koff, kst + (4 * i + w) * 1024);
+        for (int i = 0; i < 4; ++i)
+            load_lds16(src + (size_t)16 * rp * i, koff, kst + (4 * i + w) * 1024);
     } else {  // ragged last block: padding rows read row N-1 (their logits are masked)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int row = 16 * i + 4 * w + (lane >> 4);
             const int tok = min(j * 64 + row, N - 1);
-            const uint32_t off = (uint32_t)tok * 256 + (koff & 255);
+            const uint32_t off = (uint32_t)tok * rp + ((uint32_t)((lane & 15) ^ (row & 15)) << 4);
             load_lds16(k_h, off, kst + (4 * i + w) * 1024);
         }
     }
@@ -122,8 +125,8 @@ __global__ __launch_bounds__(256, 2) void fused128_kernel(
     const float* __restrict__ alpha, const float* __restrict__ htot,
     const float* __restrict__ ztot, const uint8_t* __restrict__ qhat,
     const uint8_t* __restrict__ khat, const float* __restrict__ sq,
-    const float* __restrict__ sk, float* __restrict__ O, int N, int Tq, int Tkv, int k,
-    int H) {
+    const float* __restrict__ sk, void* __restrict__ O, int N, int Tq, int Tkv, int k,
+    int H, Strides st, int alpha_qblock, int out_bf16) {
     using P = Plan<LOWBIT>;
     const int t = threadIdx.x, lane = t & 63, l32 = lane & 31, hl = lane >> 5;
     const int w = __builtin_amdgcn_readfirstlane(t >> 6);
@@ -151,7 +154,7 @@ __global__ __launch_bounds__(256, 2) void fused128_kernel(
         }
         c_base = c_log2 * sq[bh * Tq + qb];
     } else {
-        const uint16_t* qrow = Q + ((size_t)bh * N + (valid_q ? tq : 0)) * 128;
+        const uint16_t* qrow = Q + head_base(st, bh, H) + (size_t)(valid_q ? tq : 0) * st.t;
 #pragma unroll
         for (int ks = 0; ks < 8; ++ks) {
             uint4 v = make_uint4(0, 0, 0, 0);
@@ -183,11 +186,12 @@ __global__ __launch_bounds__(256, 2) void fused128_kernel(
     float m_ref = -INFINITY, l_part = 0.0f;
 
     const int32_t* sel = idx + ((size_t)bh * Tq + qb) * k;
-    const char* k_h = reinterpret_cast<const char*>(K + (size_t)bh * N * 128);
+    const char* k_h = reinterpret_cast<const char*>(K + head_base(st, bh, H));
+    const uint32_t rp = (uint32_t)st.t * 2;  // bytes between consecutive K rows
     const char* khat_h =
         LOWBIT ? reinterpret_cast<const char*>(khat + (size_t)bh * Tkv * 64 * 128) : nullptr;
     const char* vt_h = reinterpret_cast<const char*>(vt + (size_t)bh * Tkv * 128 * 64);
-    const uint32_t koff = k_lane_off(w, lane), toff = t_lane_off(w, lane);
+    const uint32_t koff = k_lane_off(w, lane, rp), toff = t_lane_off(w, lane);
     // this wave's rows (phi channels 32w .. 32w+31) of the phi(K)^T tiles, and
     // the matching z_j entries
     const char* pk_h = reinterpret_cast<const char*>(pkt + (size_t)bh * Tkv * 128 * 64);
@@ -213,9 +217,10 @@ __global__ __launch_bounds__(256, 2) void fused128_kernel(
 
     // ---- prologue: K_0, V_0, K_1 [, phi(K_0)^T, z_0]
     if (k > 0) {
-        issue_k<LOWBIT>(kbase, k_h, khat_h, sel[0], N, w, lane, koff, toff);
+        issue_k<LOWBIT>(kbase, k_h, khat_h, sel[0], N, w, lane, koff, toff, rp);
         issue_v(vbase, vt_h, sel[0], w, toff);
-        if (k > 1) issue_k<LOWBIT>(kbase + P::kStage, k_h, khat_h, sel[1], N, w, lane, koff, toff);
+        if (k > 1)
+            issue_k<LOWBIT>(kbase + P::kStage, k_h, khat_h, sel[1], N, w, lane, koff, toff, rp);
         asm volatile("" ::: "memory");
         if (LIN) load_pk(sel[0]);
         asm volatile("" ::: "memory");
@@ -234,7 +239,7 @@ __global__ __launch_bounds__(256, 2) void fused128_kernel(
         if (r + DK < k) {
             const int s2 = kslot + DK >= P::kStages ? kslot + DK - P::kStages : kslot + DK;
             issue_k<LOWBIT>(kbase + s2 * P::kStage, k_h, khat_h, sel[r + DK], N, w, lane, koff,
-                            toff);
+                            toff, rp);
         }
         const int j = sel[r];
         const char* kst = kbase + kslot * P::kStage;
@@ -388,7 +393,7 @@ __global__ __launch_bounds__(256, 2) void fused128_kernel(
         // phi(Q)^T operand from the raw bf16 Q (registers on the bf16 path)
         bf16x8 qraw[8];
         if (LOWBIT) {
-            const uint16_t* qrow = Q + ((size_t)bh * N + (valid_q ? tq : 0)) * 128;
+            const uint16_t* qrow = Q + head_base(st, bh, H) + (size_t)(valid_q ? tq : 0) * st.t;
 #pragma unroll
             for (int ks = 0; ks < 8; ++ks) {
                 uint4 v = make_uint4(0, 0, 0, 0);
@@ -427,18 +432,18 @@ __global__ __launch_bounds__(256, 2) void fused128_kernel(
         }
     }
     if (valid_q) {
-        const float a_h = alpha[bh % H];
-        float* orow = O + ((size_t)bh * N + tq) * 128;
+        const float a_h = alpha_of(alpha, bh, H, qb, Tq, alpha_qblock);
+        const size_t orow = head_base(st, bh, H) + (size_t)tq * st.t;
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
             for (int i4 = 0; i4 < 4; ++i4) {
-                float4 v;
-                v.x = a_h * (o[mt][4 * i4 + 0] * inv_l) + (1.0f - a_h) * (ol[mt][4 * i4 + 0] * inv_den);
-                v.y = a_h * (o[mt][4 * i4 + 1] * inv_l) + (1.0f - a_h) * (ol[mt][4 * i4 + 1] * inv_den);
-                v.z = a_h * (o[mt][4 * i4 + 2] * inv_l) + (1.0f - a_h) * (ol[mt][4 * i4 + 2] * inv_den);
-                v.w = a_h * (o[mt][4 * i4 + 3] * inv_l) + (1.0f - a_h) * (ol[mt][4 * i4 + 3] * inv_den);
-                *reinterpret_cast<float4*>(orow + 32 * mt + 8 * i4 + 4 * hl) = v;
+                float v[4];
+#pragma unroll
+                for (int c = 0; c < 4; ++c)
+                    v[c] = a_h * (o[mt][4 * i4 + c] * inv_l) +
+                           (1.0f - a_h) * (ol[mt][4 * i4 + c] * inv_den);
+                store_out4(O, orow + 32 * mt + 8 * i4 + 4 * hl, v[0], v[1], v[2], v[3], out_bf16);
             }
     }
 }
@@ -446,7 +451,7 @@ __global__ __launch_bounds__(256, 2) void fused128_kernel(
 }  // namespace
 
 hipError_t launch_fused128(const Dims& D, const void* Q, const void* K, const int32_t* idx,
-                           const float* alpha, float* O, const FwdWS& ws, bool lowbit,
+                           const float* alpha, void* O, const FwdWS& ws, bool lowbit,
                            hipStream_t s) {
     // one work-group per (head, query block), Tq padded to a multiple of 8
     const dim3 g((unsigned)(((D.Tq + 7) / 8) * 8 * D.BH), 1);
@@ -461,7 +466,7 @@ hipError_t launch_fused128(const Dims& D, const void* Q, const void* K, const in
                        : (lin ? fused128_kernel<true, false> : fused128_kernel<false, false>);
     timing_before(s, lowbit ? K_FUSED_FP8 : K_FUSED_MFMA);
     kern<<<g, 256, 0, s>>>(q, kk, ws.vt, ws.pkt, ws.zb, idx, alpha, ws.htot, ws.ztot, qh, kh, sq,
-                           sk, O, D.N, D.Tq, D.Tkv, D.k, D.H);
+                           sk, O, D.N, D.Tq, D.Tkv, D.k, D.H, D.st, D.alpha_qblock, D.out_bf16);
     timing_after(s, lowbit ? K_FUSED_FP8 : K_FUSED_MFMA);
     return hipGetLastError();
 }

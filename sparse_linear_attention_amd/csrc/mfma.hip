@@ -50,7 +50,7 @@ template <int D>
 __global__ __launch_bounds__(256) void summaries_mfma_kernel(
     const uint16_t* __restrict__ K, const uint16_t* __restrict__ V, uint16_t* __restrict__ vt,
     uint16_t* __restrict__ pkt, float* __restrict__ zb, float* __restrict__ hpart,
-    float* __restrict__ zpart, int N, int Tkv, int nch) {
+    float* __restrict__ zpart, int N, int Tkv, int nch, int H, Strides st) {
     constexpr int NT = D / 32;
     constexpr int TPW = NT * NT / 4;  // h^T tiles per wave
     __shared__ __attribute__((aligned(16))) char sV[D * kTPitch];
@@ -63,8 +63,8 @@ __global__ __launch_bounds__(256) void summaries_mfma_kernel(
     const long bh = blockIdx.y;
     const int j0 = chunk * kSummBlocksPerChunk;
     const int j1 = min(Tkv, j0 + kSummBlocksPerChunk);
-    const uint16_t* Kh = K + (size_t)bh * N * D;
-    const uint16_t* Vh = V + (size_t)bh * N * D;
+    const uint16_t* Kh = K + head_base(st, bh, H);
+    const uint16_t* Vh = V + head_base(st, bh, H);
     const int nt_w = w % NT;       // this wave's n-tile (phi(K) channels)
     const int mt_w0 = w / NT;      // first m-tile (V channels)
     constexpr int MT_STEP = 4 / NT;
@@ -86,8 +86,8 @@ __global__ __launch_bounds__(256) void summaries_mfma_kernel(
             uint4 kv = make_uint4(0, 0, 0, 0), vv = make_uint4(0, 0, 0, 0);
             const bool ok = tok < N;
             if (ok) {
-                kv = *reinterpret_cast<const uint4*>(Kh + (size_t)tok * D + cg * 8);
-                vv = *reinterpret_cast<const uint4*>(Vh + (size_t)tok * D + cg * 8);
+                kv = *reinterpret_cast<const uint4*>(Kh + (size_t)tok * st.t + cg * 8);
+                vv = *reinterpret_cast<const uint4*>(Vh + (size_t)tok * st.t + cg * 8);
             }
             const unsigned kw[4] = {kv.x, kv.y, kv.z, kv.w};
             const unsigned vw[4] = {vv.x, vv.y, vv.z, vv.w};
@@ -173,8 +173,8 @@ __global__ __launch_bounds__(256, 2) void fused_mfma_kernel(
     const uint16_t* __restrict__ vt, const uint16_t* __restrict__ pkt,
     const float* __restrict__ zb, const int32_t* __restrict__ idx,
     const float* __restrict__ alpha, const float* __restrict__ htot,
-    const float* __restrict__ ztot, float* __restrict__ O, int N, int Tq, int Tkv, int k,
-    int H) {
+    const float* __restrict__ ztot, void* __restrict__ O, int N, int Tq, int Tkv, int k,
+    int H, Strides st, int alpha_qblock, int out_bf16) {
     using SM = FusedSmem<D>;
     constexpr int NT = D / 32;       // 32-wide tiles along d
     constexpr int KS = D / 16;       // k-steps of Q K^T
@@ -201,7 +201,7 @@ __global__ __launch_bounds__(256, 2) void fused_mfma_kernel(
     // Q^T fragments (B operand): lane holds Q[tq][16ks + 8hl .. +8]
     bf16x8 qf[KS];
     {
-        const uint16_t* qrow = Q + ((size_t)bh * N + (valid_q ? tq : 0)) * D;
+        const uint16_t* qrow = Q + head_base(st, bh, H) + (size_t)(valid_q ? tq : 0) * st.t;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
             uint4 v = make_uint4(0, 0, 0, 0);
@@ -221,7 +221,7 @@ __global__ __launch_bounds__(256, 2) void fused_mfma_kernel(
     float zsel0 = 0.0f, zsel1 = 0.0f;
 
     const int32_t* sel = idx + ((size_t)bh * Tq + qb) * k;
-    const uint16_t* Kh = K + (size_t)bh * N * D;
+    const uint16_t* Kh = K + head_base(st, bh, H);
 
     for (int r = 0; r < k; ++r) {
         const int j = sel[r];
@@ -233,7 +233,7 @@ __global__ __launch_bounds__(256, 2) void fused_mfma_kernel(
             const int row = x / (D / 8), cg = x % (D / 8);
             const int tok = j * 64 + row;
             uint4 v = make_uint4(0, 0, 0, 0);
-            if (tok < N) v = *reinterpret_cast<const uint4*>(Kh + (size_t)tok * D + cg * 8);
+            if (tok < N) v = *reinterpret_cast<const uint4*>(Kh + (size_t)tok * st.t + cg * 8);
             *reinterpret_cast<uint4*>(sK + row * SM::kKPitch + cg * 16) = v;
         }
         const uint16_t* gv = vt + ((size_t)bh * Tkv + j) * D * 64;
@@ -337,7 +337,7 @@ __global__ __launch_bounds__(256, 2) void fused_mfma_kernel(
     // ---- epilogue
     const float l_tot = l_part + __shfl_xor(l_part, 32);
     const float inv_l = (k > 0) ? 1.0f / l_tot : 0.0f;
-    const float a_h = alpha[bh % H];
+    const float a_h = alpha_of(alpha, bh, H, qb, Tq, alpha_qblock);
     f32x16 ol[NT];
 #pragma unroll
     for (int i = 0; i < NT; ++i) ol[i] = zero16();
@@ -394,18 +394,18 @@ __global__ __launch_bounds__(256, 2) void fused_mfma_kernel(
             }
     }
     if (valid_q) {
-        float* orow = O + ((size_t)bh * N + tq) * D;
+        const size_t orow = head_base(st, bh, H) + (size_t)tq * st.t;
 #pragma unroll
         for (int mt = 0; mt < NT; ++mt)
 #pragma unroll
             for (int i4 = 0; i4 < 4; ++i4) {
                 const int e = 32 * mt + 8 * i4 + 4 * hl;
-                float4 v;
-                v.x = a_h * (o[mt][4 * i4 + 0] * inv_l) + (1.0f - a_h) * (ol[mt][4 * i4 + 0] * inv_den);
-                v.y = a_h * (o[mt][4 * i4 + 1] * inv_l) + (1.0f - a_h) * (ol[mt][4 * i4 + 1] * inv_den);
-                v.z = a_h * (o[mt][4 * i4 + 2] * inv_l) + (1.0f - a_h) * (ol[mt][4 * i4 + 2] * inv_den);
-                v.w = a_h * (o[mt][4 * i4 + 3] * inv_l) + (1.0f - a_h) * (ol[mt][4 * i4 + 3] * inv_den);
-                *reinterpret_cast<float4*>(orow + e) = v;
+                float v[4];
+#pragma unroll
+                for (int c = 0; c < 4; ++c)
+                    v[c] = a_h * (o[mt][4 * i4 + c] * inv_l) +
+                           (1.0f - a_h) * (ol[mt][4 * i4 + c] * inv_den);
+                store_out4(O, orow + e, v[0], v[1], v[2], v[3], out_bf16);
             }
     }
 }
@@ -421,11 +421,11 @@ hipError_t launch_summaries_mfma(const Dims& D, const void* K, const void* V,
     if (D.d == 128)
         summaries_mfma_kernel<128><<<g, 256, 0, s>>>((const uint16_t*)K, (const uint16_t*)V,
                                                      ws.vt, ws.pkt, ws.zb, ws.hpart, ws.zpart,
-                                                     D.N, D.Tkv, nch);
+                                                     D.N, D.Tkv, nch, D.H, D.st);
     else
         summaries_mfma_kernel<64><<<g, 256, 0, s>>>((const uint16_t*)K, (const uint16_t*)V,
                                                     ws.vt, ws.pkt, ws.zb, ws.hpart, ws.zpart,
-                                                    D.N, D.Tkv, nch);
+                                                    D.N, D.Tkv, nch, D.H, D.st);
     timing_after(s, K_SUMM_MFMA);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -433,14 +433,15 @@ hipError_t launch_summaries_mfma(const Dims& D, const void* K, const void* V,
 }
 
 hipError_t launch_fused_mfma(const Dims& D, const void* Q, const void* K, const int32_t* idx,
-                             const float* alpha, float* O, const FwdWS& ws, hipStream_t s) {
+                             const float* alpha, void* O, const FwdWS& ws, hipStream_t s) {
     if (D.d == 128) return launch_fused128(D, Q, K, idx, alpha, O, ws, false, s);
     // one work-group per (head, query block), Tq padded to a multiple of 8
     dim3 g((unsigned)(((D.Tq + 7) / 8) * 8 * D.BH), 1);
     timing_before(s, K_FUSED_MFMA);
     fused_mfma_kernel<64><<<g, 256, 0, s>>>((const uint16_t*)Q, (const uint16_t*)K, ws.vt,
                                              ws.pkt, ws.zb, idx, alpha, ws.htot, ws.ztot, O, D.N,
-                                             D.Tq, D.Tkv, D.k, D.H);
+                                             D.Tq, D.Tkv, D.k, D.H, D.st, D.alpha_qblock,
+                                             D.out_bf16);
     timing_after(s, K_FUSED_MFMA);
     return hipGetLastError();
 }

@@ -35,7 +35,7 @@ template <typename T>
 __global__ __launch_bounds__(256) void pool_project_kernel(
     const T* __restrict__ Q, const T* __restrict__ K, const float* __restrict__ Wq,
     const float* __restrict__ Wk, double* __restrict__ qt, double* __restrict__ kt, int N,
-    int d, int bq, int bkv, int Tq, int Tkv, int H, int w_heads) {
+    int d, int bq, int bkv, int Tq, int Tkv, int H, int w_heads, Strides st) {
     __shared__ double part[2048];  // [R][d], R * d == 2048
     __shared__ double xbar[128];
     const int blk = blockIdx.x;
@@ -43,7 +43,7 @@ __global__ __launch_bounds__(256) void pool_project_kernel(
     const bool isq = blk < Tq;
     const int j = isq ? blk : blk - Tq;
     const int bs = isq ? bq : bkv;
-    const T* X = (isq ? Q : K) + (size_t)bh * N * d;
+    const T* X = (isq ? Q : K) + head_base(st, bh, H);
     const int t0 = j * bs;
     const int n = min(bs, N - t0);
     const int groups = d >> 3;  // channel groups of 8
@@ -56,7 +56,7 @@ __global__ __launch_bounds__(256) void pool_project_kernel(
     for (int e = 0; e < 8; ++e) s[e] = 0.0;
     for (int row = r; row < n; row += R) {
         float v[8];
-        load8(X + (size_t)(t0 + row) * d + g * 8, v);
+        load8(X + (size_t)(t0 + row) * st.t + g * 8, v);
 #pragma unroll
         for (int e = 0; e < 8; ++e) s[e] += (double)v[e];
     }
@@ -280,11 +280,11 @@ hipError_t launch_route(const Dims& D, const void* Q, const void* K, const float
     if (D.dtype == SLA2_F32)
         pool_project_kernel<float><<<g1, 256, 0, s>>>(
             (const float*)Q, (const float*)K, Wq, Wk, ws.qt, ws.kt, D.N, D.d, D.bq, D.bkv, D.Tq,
-            D.Tkv, D.H, D.w_heads);
+            D.Tkv, D.H, D.w_heads, D.st);
     else
         pool_project_kernel<uint16_t><<<g1, 256, 0, s>>>(
             (const uint16_t*)Q, (const uint16_t*)K, Wq, Wk, ws.qt, ws.kt, D.N, D.d, D.bq, D.bkv,
-            D.Tq, D.Tkv, D.H, D.w_heads);
+            D.Tq, D.Tkv, D.H, D.w_heads, D.st);
     timing_after(s, K_POOL_PROJECT);
 
     dim3 g2((D.Tkv + 63) / 64, (D.Tq + 63) / 64, (unsigned)D.BH);

@@ -32,6 +32,10 @@ static sla2_status make_dims(const sla2_problem* p, int op, Dims* D) {
     if (!(p->topk_frac >= 0.0f && p->topk_frac <= 1.0f)) return SLA2_EINVAL;  // also NaN
     if (p->w_heads != 1 && p->w_heads != p->H) return SLA2_EINVAL;
     if (p->dtype != SLA2_F32 && p->dtype != SLA2_BF16) return SLA2_EINVAL;
+    if (p->layout != SLA2_LAYOUT_BHND && p->layout != SLA2_LAYOUT_BNHD) return SLA2_EINVAL;
+    if (p->alpha_mode != SLA2_ALPHA_PER_HEAD && p->alpha_mode != SLA2_ALPHA_PER_QBLOCK)
+        return SLA2_EINVAL;
+    if (p->out_dtype != SLA2_F32 && p->out_dtype != SLA2_BF16) return SLA2_EINVAL;
     if (op < SLA2_OP_ROUTE || op > SLA2_OP_FORWARD_FP8) return SLA2_EINVAL;
     if (p->d != 64 && p->d != 128) return SLA2_EUNSUPPORTED;
     if (p->bq != 64 && p->bq != 128) return SLA2_EUNSUPPORTED;
@@ -54,6 +58,18 @@ static sla2_status make_dims(const sla2_problem* p, int op, Dims* D) {
     D->w_heads = p->w_heads;
     D->dtype = p->dtype;
     D->BH = bh;
+    const long nd = (long)p->N * p->d;
+    if (p->layout == SLA2_LAYOUT_BHND) {
+        D->st.b = (long)p->H * nd;
+        D->st.h = nd;
+        D->st.t = p->d;
+    } else {
+        D->st.b = (long)p->H * nd;
+        D->st.h = p->d;
+        D->st.t = p->H * p->d;
+    }
+    D->alpha_qblock = p->alpha_mode == SLA2_ALPHA_PER_QBLOCK;
+    D->out_bf16 = p->out_dtype == SLA2_BF16;
     return SLA2_OK;
 }
 
@@ -218,7 +234,7 @@ SLA2_API sla2_status sla2_route(const sla2_problem* p, const void* Q, const void
 
 static sla2_status forward_args(const sla2_problem* p, int op, const void* Q, const void* K,
                                 const void* V, const int32_t* idx, const float* alpha,
-                                float* O, void* ws, size_t ws_bytes, Dims* D, FwdWS* w) {
+                                void* O, void* ws, size_t ws_bytes, Dims* D, FwdWS* w) {
     sla2_status st = make_dims(p, op, D);
     if (st != SLA2_OK) return st;
     if (!ok_ptr(Q) || !ok_ptr(K) || !ok_ptr(V) || !ok_ptr(alpha) || !ok_ptr(O))
@@ -231,7 +247,7 @@ static sla2_status forward_args(const sla2_problem* p, int op, const void* Q, co
 
 SLA2_API sla2_status sla2_forward(const sla2_problem* p, const void* Q, const void* K,
                                   const void* V, const int32_t* topk_idx, const float* alpha,
-                                  float* O, void* ws, size_t ws_bytes, void* stream) {
+                                  void* O, void* ws, size_t ws_bytes, void* stream) {
     Dims D;
     FwdWS w;
     sla2_status st = forward_args(p, SLA2_OP_FORWARD, Q, K, V, topk_idx, alpha, O, ws,
@@ -250,7 +266,7 @@ SLA2_API sla2_status sla2_forward(const sla2_problem* p, const void* Q, const vo
 
 SLA2_API sla2_status sla2_forward_fp8(const sla2_problem* p, const void* Q, const void* K,
                                       const void* V, const int32_t* topk_idx,
-                                      const float* alpha, float* O, void* ws,
+                                      const float* alpha, void* O, void* ws,
                                       size_t ws_bytes, void* stream) {
     Dims D;
     FwdWS w;

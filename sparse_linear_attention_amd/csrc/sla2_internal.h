@@ -27,12 +27,51 @@ enum KernelKind {
     K_NUM_KINDS
 };
 
+// Element strides of a Q/K/V/O tensor: batch, head, token (d innermost).
+// [B,H,N,d]: (H N d, N d, d); [B,N,H,d]: (N H d, d, H d).
+struct Strides {
+    long b, h;
+    int t;
+};
+
+// offset of row 0 of head bh (= b * H + h)
+__host__ __device__ inline long head_base(const Strides& s, long bh, int H) {
+    return (bh / H) * s.b + (bh % H) * s.h;
+}
+
 struct Dims {
     int B, H, N, d, bq, bkv;
     int Tq, Tkv, k, w_heads;
-    int dtype;  // sla2_dtype
+    int dtype;  // sla2_dtype of Q, K, V
     long BH;
+    Strides st;          // layout of Q, K, V and O
+    int alpha_qblock;    // alpha is [H][Tq] (else [H])
+    int out_bf16;        // O is bf16 (else fp32)
 };
+
+// Four consecutive outputs (element offset off, a multiple of 4) as fp32, or
+// rounded once to bf16 (nearest even).
+__device__ inline void store_out4(void* O, size_t off, float x, float y, float z, float w,
+                                  int out_bf16) {
+    if (out_bf16) {
+        typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+        bf16x4_t b;
+        b[0] = (__bf16)x;
+        b[1] = (__bf16)y;
+        b[2] = (__bf16)z;
+        b[3] = (__bf16)w;
+        *reinterpret_cast<bf16x4_t*>(static_cast<uint16_t*>(O) + off) = b;
+    } else {
+        *reinterpret_cast<float4*>(static_cast<float*>(O) + off) = make_float4(x, y, z, w);
+    }
+}
+
+// alpha of a row of head bh in query block qb
+__device__ inline float alpha_of(const float* alpha, long bh, int H, int qb, int Tq,
+                                 int per_qblock) {
+    const int h = (int)(bh % H);
+    return per_qblock ? alpha[(size_t)h * Tq + qb] : alpha[h];
+}
 
 // chunking of the token axis for the block-summary pass
 constexpr int kSummBlocksPerChunk = 16;  // KV blocks of 64 tokens per work-group
@@ -90,7 +129,7 @@ hipError_t launch_route(const Dims& D, const void* Q, const void* K, const float
 
 // fp32 path: VALU block summaries + VALU fused kernel
 hipError_t launch_forward_valu(const Dims& D, const void* Q, const void* K, const void* V,
-                               const int32_t* idx, const float* alpha, float* O,
+                               const int32_t* idx, const float* alpha, void* O,
                                const FwdWS& ws, hipStream_t s);
 
 // deterministic reduction of the per-chunk summary partials
@@ -100,7 +139,7 @@ hipError_t launch_summaries_reduce(const Dims& D, const FwdWS& ws, hipStream_t s
 hipError_t launch_summaries_mfma(const Dims& D, const void* K, const void* V,
                                  const FwdWS& ws, hipStream_t s);
 hipError_t launch_fused_mfma(const Dims& D, const void* Q, const void* K,
-                             const int32_t* idx, const float* alpha, float* O,
+                             const int32_t* idx, const float* alpha, void* O,
                              const FwdWS& ws, hipStream_t s);
 
 // low bit
@@ -108,6 +147,6 @@ hipError_t launch_quantize_fp8(const Dims& D, const void* Q, const void* K, cons
                                hipStream_t s);
 // d = 128, b_q = 128 fused kernel (bf16, or the low-bit Q K^T with lowbit)
 hipError_t launch_fused128(const Dims& D, const void* Q, const void* K, const int32_t* idx,
-                           const float* alpha, float* O, const FwdWS& ws, bool lowbit,
+                           const float* alpha, void* O, const FwdWS& ws, bool lowbit,
                            hipStream_t s);
 }  // namespace sla2

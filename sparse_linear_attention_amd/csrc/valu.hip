@@ -22,7 +22,7 @@ __device__ inline float phi_f(float x) { return x > 0.0f ? x + 1.0f : expf(x); }
 template <typename T>
 __global__ __launch_bounds__(256) void summaries_valu_kernel(
     const T* __restrict__ K, const T* __restrict__ V, float* __restrict__ hpart,
-    float* __restrict__ zpart, int N, int d, int nch) {
+    float* __restrict__ zpart, int N, int d, int nch, int H, Strides st) {
     __shared__ float pk[32 * 128];
     __shared__ float vv[32 * 128];
     const int chunk = blockIdx.x;
@@ -31,8 +31,8 @@ __global__ __launch_bounds__(256) void summaries_valu_kernel(
     const int SB = d >> 4;  // 8 or 4
     const int t_begin = chunk * kSummBlocksPerChunk * 64;
     const int t_end = min(N, t_begin + kSummBlocksPerChunk * 64);
-    const T* Kh = K + (size_t)bh * N * d;
-    const T* Vh = V + (size_t)bh * N * d;
+    const T* Kh = K + head_base(st, bh, H);
+    const T* Vh = V + head_base(st, bh, H);
     float acc[8][8];
     float z[8];
 #pragma unroll
@@ -46,8 +46,8 @@ __global__ __launch_bounds__(256) void summaries_valu_kernel(
             const int u = x / d, c = x % d;
             const int t = u0 + u;
             const bool ok = t < t_end;
-            pk[u * d + c] = ok ? phi_f(ld1(Kh + (size_t)t * d + c)) : 0.0f;
-            vv[u * d + c] = ok ? ld1(Vh + (size_t)t * d + c) : 0.0f;
+            pk[u * d + c] = ok ? phi_f(ld1(Kh + (size_t)t * st.t + c)) : 0.0f;
+            vv[u * d + c] = ok ? ld1(Vh + (size_t)t * st.t + c) : 0.0f;
         }
         __syncthreads();
         for (int u = 0; u < 32; ++u) {
@@ -101,8 +101,9 @@ template <typename T>
 __global__ __launch_bounds__(256) void fused_valu_kernel(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
     const int32_t* __restrict__ idx, const float* __restrict__ alpha,
-    const float* __restrict__ htot, const float* __restrict__ ztot, float* __restrict__ O,
-    int N, int d, int bq, int Tq, int Tkv, int k, int H) {
+    const float* __restrict__ htot, const float* __restrict__ ztot, void* __restrict__ O,
+    int N, int d, int bq, int Tq, int Tkv, int k, int H, Strides st, int alpha_qblock,
+    int out_bf16) {
     __shared__ float Kt[32 * 128];
     __shared__ float Vt[32 * 128];
     __shared__ float Pk[32 * 128];
@@ -114,15 +115,15 @@ __global__ __launch_bounds__(256) void fused_valu_kernel(
     const long bh = blockIdx.y;
     const int tq = qb * bq + (blockIdx.x % per_blk) * 32 + row;
     const bool valid_q = tq < N;
-    const T* Qh = Q + (size_t)bh * N * d;
-    const T* Kh = K + (size_t)bh * N * d;
-    const T* Vh = V + (size_t)bh * N * d;
+    const T* Qh = Q + head_base(st, bh, H);
+    const T* Kh = K + head_base(st, bh, H);
+    const T* Vh = V + head_base(st, bh, H);
     const float inv_sqrt_d = 1.0f / sqrtf((float)d);
 
     float q[16], pq[16], acc[16], corr[16];
 #pragma unroll
     for (int c = 0; c < 16; ++c) {
-        const float x = (c < CS && valid_q) ? ld1(Qh + (size_t)tq * d + c0 + c) : 0.0f;
+        const float x = (c < CS && valid_q) ? ld1(Qh + (size_t)tq * st.t + c0 + c) : 0.0f;
         q[c] = x;
         pq[c] = phi_f(x);
         acc[c] = 0.0f;
@@ -140,10 +141,10 @@ __global__ __launch_bounds__(256) void fused_valu_kernel(
             for (int x = threadIdx.x; x < 32 * d; x += 256) {
                 const int u = x / d, c = x % d;
                 const bool ok = u < nu;
-                const float kv = ok ? ld1(Kh + (size_t)(u0 + u) * d + c) : 0.0f;
+                const float kv = ok ? ld1(Kh + (size_t)(u0 + u) * st.t + c) : 0.0f;
                 Kt[u * d + c] = kv;
                 Pk[u * d + c] = ok ? phi_f(kv) : 0.0f;
-                Vt[u * d + c] = ok ? ld1(Vh + (size_t)(u0 + u) * d + c) : 0.0f;
+                Vt[u * d + c] = ok ? ld1(Vh + (size_t)(u0 + u) * st.t + c) : 0.0f;
             }
             __syncthreads();
             float s[32];
@@ -229,12 +230,15 @@ __global__ __launch_bounds__(256) void fused_valu_kernel(
         for (int c = 0; c < 16; ++c) ol[c] = (num[c] - corr[c]) / den;
     }
     if (valid_q) {
-        const float a = alpha[bh % H];
+        const float a = alpha_of(alpha, bh, H, qb, Tq, alpha_qblock);
         const float inv_l = (k > 0) ? 1.0f / l : 0.0f;
-        float* o = O + ((size_t)bh * N + tq) * d + c0;
+        const size_t o = head_base(st, bh, H) + (size_t)tq * st.t + c0;
+        float v[16];
 #pragma unroll
-        for (int c = 0; c < 16; ++c)
-            if (c < CS) o[c] = a * (acc[c] * inv_l) + (1.0f - a) * ol[c];
+        for (int c = 0; c < 16; ++c) v[c] = a * (acc[c] * inv_l) + (1.0f - a) * ol[c];
+#pragma unroll
+        for (int c = 0; c < 16; c += 4)
+            if (c < CS) store_out4(O, o + c, v[c], v[c + 1], v[c + 2], v[c + 3], out_bf16);
     }
 }
 
@@ -250,17 +254,18 @@ hipError_t launch_summaries_reduce(const Dims& D, const FwdWS& ws, hipStream_t s
 }
 
 hipError_t launch_forward_valu(const Dims& D, const void* Q, const void* K, const void* V,
-                               const int32_t* idx, const float* alpha, float* O,
+                               const int32_t* idx, const float* alpha, void* O,
                                const FwdWS& ws, hipStream_t s) {
     const int nch = summ_chunks(D);
     if (D.k < D.Tkv) {
         timing_before(s, K_SUMM_VALU);
         if (D.dtype == SLA2_F32)
             summaries_valu_kernel<float><<<dim3(nch, (unsigned)D.BH), 256, 0, s>>>(
-                (const float*)K, (const float*)V, ws.hpart, ws.zpart, D.N, D.d, nch);
+                (const float*)K, (const float*)V, ws.hpart, ws.zpart, D.N, D.d, nch, D.H, D.st);
         else
             summaries_valu_kernel<uint16_t><<<dim3(nch, (unsigned)D.BH), 256, 0, s>>>(
-                (const uint16_t*)K, (const uint16_t*)V, ws.hpart, ws.zpart, D.N, D.d, nch);
+                (const uint16_t*)K, (const uint16_t*)V, ws.hpart, ws.zpart, D.N, D.d, nch, D.H,
+                D.st);
         timing_after(s, K_SUMM_VALU);
         hipError_t e = launch_summaries_reduce(D, ws, s);
         if (e != hipSuccess) return e;
@@ -270,11 +275,12 @@ hipError_t launch_forward_valu(const Dims& D, const void* Q, const void* K, cons
     if (D.dtype == SLA2_F32)
         fused_valu_kernel<float><<<g, 256, 0, s>>>(
             (const float*)Q, (const float*)K, (const float*)V, idx, alpha, ws.htot, ws.ztot, O,
-            D.N, D.d, D.bq, D.Tq, D.Tkv, D.k, D.H);
+            D.N, D.d, D.bq, D.Tq, D.Tkv, D.k, D.H, D.st, D.alpha_qblock, D.out_bf16);
     else
         fused_valu_kernel<uint16_t><<<g, 256, 0, s>>>(
             (const uint16_t*)Q, (const uint16_t*)K, (const uint16_t*)V, idx, alpha, ws.htot,
-            ws.ztot, O, D.N, D.d, D.bq, D.Tq, D.Tkv, D.k, D.H);
+            ws.ztot, O, D.N, D.d, D.bq, D.Tq, D.Tkv, D.k, D.H, D.st, D.alpha_qblock,
+            D.out_bf16);
     timing_after(s, K_FUSED_VALU);
     return hipGetLastError();
 }

@@ -17,12 +17,15 @@ OK, EINVAL, EUNSUPPORTED, EWORKSPACE, EHIP = range(5)
 F32, BF16 = 0, 1
 PHI_ELU1 = 0
 OP_ROUTE, OP_FORWARD, OP_FORWARD_FP8 = 0, 1, 2
+LAYOUT_BHND, LAYOUT_BNHD = 0, 1
+ALPHA_PER_HEAD, ALPHA_PER_QBLOCK = 0, 1
 
 
 class Problem(C.Structure):
     _fields_ = [("B", C.c_int32), ("H", C.c_int32), ("N", C.c_int32), ("d", C.c_int32),
                 ("bq", C.c_int32), ("bkv", C.c_int32), ("topk_frac", C.c_float),
-                ("w_heads", C.c_int32), ("phi", C.c_int32), ("dtype", C.c_int32)]
+                ("w_heads", C.c_int32), ("phi", C.c_int32), ("dtype", C.c_int32),
+                ("layout", C.c_int32), ("alpha_mode", C.c_int32), ("out_dtype", C.c_int32)]
 
 
 class SLA2Error(RuntimeError):
@@ -71,11 +74,17 @@ EXPORTS = ("sla2_num_q_blocks", "sla2_num_kv_blocks", "sla2_topk", "sla2_workspa
            "sla2_kernel_name")
 
 
+def _dtype(x):
+    if isinstance(x, str):
+        return F32 if x == "f32" else BF16
+    return x
+
+
 def problem(B, H, N, d, bq=128, bkv=64, topk_frac=0.03, w_heads=1, dtype=BF16,
-            phi=PHI_ELU1) -> Problem:
-    if isinstance(dtype, str):
-        dtype = F32 if dtype == "f32" else BF16
-    return Problem(B, H, N, d, bq, bkv, float(topk_frac), w_heads, phi, dtype)
+            phi=PHI_ELU1, layout=LAYOUT_BHND, alpha_mode=ALPHA_PER_HEAD,
+            out_dtype=F32) -> Problem:
+    return Problem(B, H, N, d, bq, bkv, float(topk_frac), w_heads, phi, _dtype(dtype),
+                   layout, alpha_mode, _dtype(out_dtype))
 
 
 def status_str(s: int) -> str:
@@ -198,11 +207,13 @@ def route(p: Problem, Q, K, Wq, Wk, want_mask=True, ws=None, stream=None):
 
 
 def forward(p: Problem, Q, K, V, topk_idx, alpha, fp8=False, ws=None, out=None, stream=None):
-    """Allocates O (fp32) and the workspace if not given; runs the forward."""
+    """Allocates O (fp32 or bf16, in the problem's layout) and the workspace if
+    not given; runs the forward."""
     import torch
     dev = Q.device
-    O = out if out is not None else torch.empty((p.B, p.H, p.N, p.d), dtype=torch.float32,
-                                                device=dev)
+    shape = (p.B, p.H, p.N, p.d) if p.layout == LAYOUT_BHND else (p.B, p.N, p.H, p.d)
+    dt = torch.float32 if p.out_dtype == F32 else torch.bfloat16
+    O = out if out is not None else torch.empty(shape, dtype=dt, device=dev)
     op = OP_FORWARD_FP8 if fp8 else OP_FORWARD
     if ws is None:
         ws = workspace(p, op, dev)

@@ -63,6 +63,7 @@ def test_topk_matches_oracle_table(orc):
     (dict(topk_frac=float("nan")), S.EINVAL), (dict(w_heads=3), S.EINVAL),
     (dict(dtype=7), S.EINVAL), (dict(d=96), S.EUNSUPPORTED), (dict(bq=32), S.EUNSUPPORTED),
     (dict(bkv=128), S.EUNSUPPORTED), (dict(N=7681 * 64), S.EUNSUPPORTED),
+    (dict(layout=2), S.EINVAL), (dict(alpha_mode=-1), S.EINVAL), (dict(out_dtype=5), S.EINVAL),
 ])
 def test_check_rejects(kw, code):
     assert S.check(p_ok(**kw), S.OP_ROUTE) == code
@@ -76,6 +77,17 @@ def test_fp8_needs_bf16_and_bq128():
     assert S.check(p_ok(), S.OP_FORWARD_FP8) == S.OK
     assert S.check(p_ok(phi=1), S.OP_FORWARD) == S.EUNSUPPORTED
     assert S.check(p_ok(), 9) == S.EINVAL
+
+
+def test_layouts_alpha_modes_and_output_dtypes_are_accepted():
+    for layout in (S.LAYOUT_BHND, S.LAYOUT_BNHD):
+        for am in (S.ALPHA_PER_HEAD, S.ALPHA_PER_QBLOCK):
+            for od in (S.F32, S.BF16):
+                for op in (S.OP_ROUTE, S.OP_FORWARD, S.OP_FORWARD_FP8):
+                    p = p_ok(layout=layout, alpha_mode=am, out_dtype=od)
+                    assert S.check(p, op) == S.OK
+                    # the workspace does not depend on how Q/K/V/O are laid out
+                    assert S.workspace_bytes(p, op) == S.workspace_bytes(p_ok(), op)
 
 
 def test_workspace_sizes_grow_with_the_problem():

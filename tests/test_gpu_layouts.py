@@ -1,0 +1,76 @@
+"""GPU parity of the problem options: the token-major [B,N,H,d] layout of Q,
+K, V and O, alpha per (head, query block) -- the granularity of the pages'
+algorithm ("SLA2 深度解读" 08) -- and a bf16 output.
+
+Every kernel path is covered: fp32 (vector ALU), bf16 with b_q = 64 (vector
+ALU), bf16 d = 64 (matrix cores), bf16 d = 128 (fused d = 128 kernel) and the
+low-bit sparse branch.  The oracle takes the same inputs transposed to
+[B,H,N,d]; its router must match bit for bit, its output within the path's
+tolerance.  A bf16 output must equal, bit for bit, the round-to-nearest-even
+of the fp32 output of the same call.
+"""
+import numpy as np
+import pytest
+import torch
+
+from sparse_linear_attention_amd import inputs as I
+from sparse_linear_attention_amd import sla2 as S
+from tests.test_gpu_parity import TOL, compare_blocks, check_route, dev, say  # noqa: F401
+
+pytestmark = pytest.mark.gpu
+
+PATHS = [  # name, dtype, N, d, bq, frac, fp8
+    ("f32", "f32", 700, 128, 128, 0.3, False),
+    ("bf16-bq64", "bf16", 513, 128, 64, 0.2, False),
+    ("bf16-d64", "bf16", 1000, 64, 128, 0.3, False),
+    ("bf16-d128", "bf16", 4100, 128, 128, 0.05, False),
+    ("fp8", "bf16", 2000, 128, 128, 0.1, True),
+]
+OPTS = [  # layout, alpha mode
+    (S.LAYOUT_BNHD, S.ALPHA_PER_HEAD),
+    (S.LAYOUT_BHND, S.ALPHA_PER_QBLOCK),
+    (S.LAYOUT_BNHD, S.ALPHA_PER_QBLOCK),
+]
+
+
+def upload(a, dev, layout):
+    if layout == S.LAYOUT_BNHD:
+        a = np.ascontiguousarray(a.transpose(0, 2, 1, 3))
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+    return torch.from_numpy(a).to(dev)
+
+
+@pytest.mark.parametrize("opt", OPTS, ids=["bnhd", "alpha-qblock", "bnhd-alpha-qblock"])
+@pytest.mark.parametrize("path", PATHS, ids=[c[0] for c in PATHS])
+def test_layout_alpha_and_bf16_output(orc, dev, path, opt):
+    name, dtype, N, d, bq, frac, fp8 = path
+    layout, amode = opt
+    H = 3
+    gen = "centroids" if dtype == "f32" else "smooth"
+    x = I.make_inputs(I.Workload(name, 1, H, N, d, bq, 64, frac, dtype, gen, seed=11))
+    w = x.wl
+    say(f"case {name}: layout {layout} alpha mode {amode} N={N} d={d} bq={bq}")
+    Tq = w.Tq
+    alpha = (np.random.default_rng(7).uniform(0.2, 0.95, (H, Tq)).astype(np.float32)
+             if amode == S.ALPHA_PER_QBLOCK else x.alpha)
+    q, k, v = (upload(a, dev, layout) for a in (x.q, x.k, x.v))
+    wq, wk = (torch.from_numpy(a).to(dev) for a in (x.wq, x.wk))
+    al = torch.from_numpy(alpha).to(dev)
+    outs = {}
+    for od in (S.F32, S.BF16):
+        p = S.problem(1, H, N, d, bq, 64, frac, 1, dtype, layout=layout, alpha_mode=amode,
+                      out_dtype=od)
+        idx, mask = S.route(p, q, k, wq, wk)
+        outs[od] = S.forward(p, q, k, v, idx, al, fp8=fp8)
+        torch.cuda.synchronize()
+    oidx = check_route(orc, x, idx, mask)
+    # bf16 output: the fp32 result rounded once, to nearest even
+    assert torch.equal(outs[S.BF16], outs[S.F32].to(torch.bfloat16))
+    O = outs[S.F32]
+    if layout == S.LAYOUT_BNHD:
+        O = O.permute(0, 2, 1, 3).contiguous()
+    op = orc.problem(1, H, N, d, bq, 64, frac, 1, dtype, alpha_mode=amode)
+    tol = TOL["fp8"] if fp8 else TOL[dtype]
+    compare_blocks(orc, x, oidx, O, orc.all_blocks(op), tol,
+                   variant="fp8" if fp8 else "exact", op=op, alpha=alpha)

@@ -83,7 +83,7 @@ FP8_ACC_EPS = 2.0 ** -14
 FP8_BULK = (3e-4, 5e-3)
 
 
-def compare_blocks(orc, x, oidx, O, blocks, tol, variant="exact"):
+def compare_blocks(orc, x, oidx, O, blocks, tol, variant="exact", op=None, alpha=None):
     """Element-wise comparison on whole query blocks.  For the low-bit
     variant a row may also move by the oracle's per-row bound: a P value
     whose 256 P~ lies closer to an e4m3 rounding midpoint than the logit
@@ -92,12 +92,13 @@ def compare_blocks(orc, x, oidx, O, blocks, tol, variant="exact"):
     bound is the largest effect of such flips on the row (0 for rows without
     such a decision).  On top of that the bulk of the rows must agree to
     FP8_BULK, which no flip-free difference comes near."""
-    op = orc.problem_of(x)
+    op = orc.problem_of(x) if op is None else op
+    alpha = x.alpha if alpha is None else alpha
     if variant == "fp8":
-        ref, bound = orc.forward(op, x.q, x.k, x.v, oidx, x.alpha, blocks, variant=variant,
+        ref, bound = orc.forward(op, x.q, x.k, x.v, oidx, alpha, blocks, variant=variant,
                                  acc_eps=FP8_ACC_EPS)
     else:
-        ref, bound = orc.forward(op, x.q, x.k, x.v, oidx, x.alpha, blocks), None
+        ref, bound = orc.forward(op, x.q, x.k, x.v, oidx, alpha, blocks), None
     w = x.wl
     Oc = O.cpu().numpy().reshape(w.B * w.H, w.N, w.d)
     errs, bnds = [], []

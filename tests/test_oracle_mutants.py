@@ -38,7 +38,8 @@ MUTANTS = {
                                    "double wgt = amb[a].step / 256.0 * exp(m - amb[a].m) / l * 0.25;"),
     "flip_bound_window_narrow": ("double win = abuf[u - t0] + mA +", "double win = abuf[u - t0] +"),
     "denominator_without_phi_q": ("den += pq[c] * Zi[c];", "den += Zi[c];"),
-    "alpha_of_wrong_head": ("double a = (double)F->alpha[h];", "double a = (double)F->alpha[0];"),
+    "alpha_of_wrong_head": ("F->alpha[h]);", "F->alpha[0]);"),
+    "alpha_block_ignored": ("F->alpha[(size_t)h * Tq + i]", "F->alpha[(size_t)h * Tq]"),
     "numerator_transposed_H": ("num += pq[c] * Hi[(size_t)c * d + e];", "num += pq[c] * Hi[(size_t)e * d + c];"),
 }
 
@@ -54,6 +55,7 @@ PINS = [
     (pins.test_no_blocks_alpha0_is_linear_attention, ("f32", 700, 64)),
     (pins.test_linear_branch_over_unselected_blocks, ()),
     (pins.test_combine_is_alpha_mix_of_the_two_branches, ()),
+    (pins.test_combine_alpha_per_query_block, ()),
     (pins.test_lowbit_identity_quantiser_equals_exact, ("bf16",)),
     (pins.test_lowbit_quantised_inputs, ()),
     (pins.test_lowbit_error_is_small, ()),

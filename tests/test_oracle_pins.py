@@ -377,6 +377,25 @@ def test_combine_is_alpha_mix_of_the_two_branches(orc):
     assert np.abs(o - (a * os_ + (1 - a) * ol)).max() < 1e-13
 
 
+def test_combine_alpha_per_query_block(orc):
+    """alpha [H][T_q] (the algorithm's granularity): query block i of head h is
+    the alpha[h][i] mix of the two branches, with both branches taken from the
+    per-head mode at alpha = 1 and alpha = 0."""
+    x = small(N=700, frac=0.3)
+    p = orc.problem_of(x)
+    idx, _, _, _ = orc.route(p, x.q, x.k, x.wq, x.wk)
+    os_ = orc.forward_full(p, x.q, x.k, x.v, idx, np.ones(2, np.float32))
+    ol = orc.forward_full(p, x.q, x.k, x.v, idx, np.zeros(2, np.float32))
+    Tq = orc.num_blocks(p.N, p.bq)
+    al = np.random.default_rng(5).uniform(0.0, 1.0, (2, Tq)).astype(np.float32)
+    pb = orc.problem(p.B, p.H, p.N, p.d, p.bq, p.bkv, p.topk_frac, p.w_heads, x.wl.dtype,
+                     alpha_mode=1)
+    o = orc.forward_full(pb, x.q, x.k, x.v, idx, al)
+    # alpha per token row: row t of head h uses alpha[h][t // bq]
+    a = np.repeat(al.astype(np.float64), p.bq, axis=1)[:, : p.N][None, :, :, None]
+    assert np.abs(o - (a * os_ + (1 - a) * ol)).max() < 1e-13
+
+
 # --------------------------------------------------------------------------
 # low-bit variant
 # --------------------------------------------------------------------------
