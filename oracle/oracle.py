@@ -31,7 +31,8 @@ def build(force: bool = True) -> str:
 class Problem(C.Structure):
     _fields_ = [("B", C.c_int32), ("H", C.c_int32), ("N", C.c_int32), ("d", C.c_int32),
                 ("bq", C.c_int32), ("bkv", C.c_int32), ("topk_frac", C.c_float),
-                ("w_heads", C.c_int32), ("dtype", C.c_int32), ("alpha_mode", C.c_int32)]
+                ("w_heads", C.c_int32), ("dtype", C.c_int32), ("alpha_mode", C.c_int32),
+                ("lowbit_v", C.c_int32)]
 
 
 _lib = None
@@ -52,6 +53,7 @@ def lib():
         L.orc_forward_fp8.argtypes = [P, vp, vp, vp, ip, vp, ip, C.c_int, C.c_int, dp, dp,
                                       C.c_double, C.c_int]
         L.orc_quant_fp8.argtypes = [P, vp, vp, C.c_long, vp, vp, vp, vp, vp]
+        L.orc_quant_v_fp8.argtypes = [P, vp, C.c_long, vp, vp]
         L.orc_e4m3_encode.argtypes = [C.c_float]
         L.orc_e4m3_encode.restype = C.c_uint8
         L.orc_e4m3_decode.argtypes = [C.c_uint8]
@@ -66,10 +68,12 @@ def _ptr(a):
     return None if a is None else a.ctypes.data
 
 
-def problem(B, H, N, d, bq, bkv, frac, w_heads=1, dtype="f32", alpha_mode=0) -> Problem:
-    """alpha_mode 0: alpha [H]; 1: alpha [H][T_q] (one per query block)."""
+def problem(B, H, N, d, bq, bkv, frac, w_heads=1, dtype="f32", alpha_mode=0,
+            lowbit_v=0) -> Problem:
+    """alpha_mode 0: alpha [H]; 1: alpha [H][T_q] (one per query block).
+    lowbit_v 1: the low-bit variant quantises V too (per channel)."""
     return Problem(B, H, N, d, bq, bkv, float(frac), w_heads, 0 if dtype == "f32" else 1,
-                   alpha_mode)
+                   alpha_mode, lowbit_v)
 
 
 def problem_of(x) -> Problem:
@@ -175,6 +179,14 @@ def quant_fp8(p: Problem, q, k, bh):
     L.orc_quant_fp8(C.byref(p), _ptr(q), _ptr(k), bh, _ptr(qh), _ptr(kh), _ptr(sq),
                     _ptr(sk), _ptr(mu))
     return qh, kh, sq, sk, mu
+
+
+def quant_v_fp8(p: Problem, v, bh):
+    """Per-channel quantised V of one head: (vhat [N,d] u8, sv [d])."""
+    vh = np.zeros((p.N, p.d), np.uint8)
+    sv = np.zeros(p.d, np.float32)
+    lib().orc_quant_v_fp8(C.byref(p), _ptr(_qkv(p, v)), bh, _ptr(vh), _ptr(sv))
+    return vh, sv
 
 
 def e4m3_encode(x: float) -> int:

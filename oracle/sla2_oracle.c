@@ -37,7 +37,10 @@
  *    scales (Q: b_q tokens, K: b_kv tokens); K smoothed by its mean over the N
  *    valid tokens (sparse-branch QK^T only); P quantised as e4m3(256 P~)/256
  *    with P~ = exp(l - running max) and the row sum taken over the quantised
- *    values; V stays bf16; tiles visited in ascending KV-block order.
+ *    values; tiles visited in ascending KV-block order; V stays bf16, or
+ *    (lowbit_v) is quantised as well: s_V(c) = max over the N valid tokens
+ *    of |V(.,c)| / 448 per head and channel (1 if 0), Vhat = e4m3(V / s_V),
+ *    and P V uses Vhat s_V -- the pages quantise P and V for P V.
  */
 #include <math.h>
 #include <pthread.h>
@@ -53,6 +56,7 @@ typedef struct {
     int32_t w_heads;
     int32_t dtype; /* 0: Q,K,V are float32; 1: Q,K,V are bf16 bit patterns */
     int32_t alpha_mode; /* 0: alpha [H]; 1: alpha [H][T_q], one per query block */
+    int32_t lowbit_v;   /* low-bit variant: 1 = V also quantised (per channel) */
 } orc_problem;
 
 /* ------------------------------------------------------------------ */
@@ -356,6 +360,8 @@ typedef struct {
     float* sq;   /* [Tq] */
     float* sk;   /* [Tkv] */
     float* mu;   /* [d] */
+    uint8_t* vh; /* [N][d] e4m3 codes of V / s_V (lowbit_v only) */
+    float* sv;   /* [d] per-channel V scales (lowbit_v only) */
 } quant_t;
 
 static float elemf(const orc_problem* p, const void* X, long bh, long t, long c) {
@@ -405,10 +411,36 @@ static void quant_head(const orc_problem* p, const void* Q, const void* K, long 
     }
 }
 
+/* Per-channel V scales and codes of head bh (the fully low-bit variant:
+   [SLA2-zh] 07 quantises P and V before P V).  The per-channel maximum is
+   exact in fp32; the code is decided in fp32, as the kernel decides it. */
+static void quant_v_head(const orc_problem* p, const void* V, long bh, quant_t* o) {
+    int d = p->d, N = p->N;
+    for (int c = 0; c < d; ++c) {
+        float amax = 0.0f;
+        for (int t = 0; t < N; ++t) {
+            float v = fabsf(elemf(p, V, bh, t, c));
+            if (v > amax) amax = v;
+        }
+        o->sv[c] = amax > 0.0f ? amax / 448.0f : 1.0f;
+    }
+    for (int t = 0; t < N; ++t)
+        for (int c = 0; c < d; ++c)
+            o->vh[(size_t)t * d + c] = orc_e4m3_encode(elemf(p, V, bh, t, c) / o->sv[c]);
+}
+
+/* Quantised V of head bh: vhat [N][d] codes, sv [d] scales. */
+void orc_quant_v_fp8(const orc_problem* p, const void* V, long bh, uint8_t* vhat, float* sv) {
+    quant_t o = {0};
+    o.vh = vhat;
+    o.sv = sv;
+    quant_v_head(p, V, bh, &o);
+}
+
 /* Quantised inputs of head bh (step a4 of the low-bit variant). */
 void orc_quant_fp8(const orc_problem* p, const void* Q, const void* K, long bh,
                    uint8_t* qhat, uint8_t* khat, float* sq, float* sk, float* mu) {
-    quant_t o = {qhat, khat, sq, sk, mu};
+    quant_t o = {qhat, khat, sq, sk, mu, NULL, NULL};
     quant_head(p, Q, K, bh, &o);
 }
 
@@ -448,6 +480,15 @@ typedef struct {
     double m;    /* running max (natural log units) when it was quantised */
     double step; /* distance to the neighbouring code value (256-scaled) */
 } ambig_t;
+
+/* V(u, e) as the low-bit P V sees it: the decoded code times the channel
+   scale when V is quantised (and the quantiser is on), else V itself. */
+static double v_lowbit(const fwd_ctx* F, long u, int e) {
+    const orc_problem* p = F->p;
+    if (p->lowbit_v && F->quantize)
+        return (double)orc_e4m3_decode(F->qt->vh[(size_t)u * p->d + e]) * (double)F->qt->sv[e];
+    return elem(p, F->V, F->bh, u, e);
+}
 
 /* Sparse branch, exact: O_s[t] = softmax(l) V over the selected tokens
    ([SLA2-zh] 04 and 08), as a two-pass max-subtracted softmax. */
@@ -575,7 +616,7 @@ static void sparse_lowbit(const fwd_ctx* F, int i, const int32_t* sel, int k, in
                 ph = pt;
             }
             l += ph;
-            for (int e = 0; e < d; ++e) os[e] += ph * elem(p, F->V, F->bh, u, e);
+            for (int e = 0; e < d; ++e) os[e] += ph * v_lowbit(F, u, e);
         }
         m = mn;
     }
@@ -589,7 +630,7 @@ static void sparse_lowbit(const fwd_ctx* F, int i, const int32_t* sel, int k, in
             double wgt = amb[a].step / 256.0 * exp(amb[a].m - m) / l;
             double dv = 0.0;
             for (int e = 0; e < d; ++e) {
-                double x = fabs(elem(p, F->V, F->bh, amb[a].u, e) - os[e]);
+                double x = fabs(v_lowbit(F, amb[a].u, e) - os[e]);
                 if (x > dv) dv = x;
             }
             b += 2.0 * wgt * dv;
@@ -698,6 +739,11 @@ static int forward_common(const orc_problem* p, const void* Q, const void* K, co
             qt.sk = (float*)malloc(sizeof(float) * Tkv);
             qt.mu = (float*)malloc(sizeof(float) * d);
             quant_head(p, Q, K, bh, &qt);
+            if (p->lowbit_v) {
+                qt.vh = (uint8_t*)malloc((size_t)p->N * d);
+                qt.sv = (float*)malloc(sizeof(float) * d);
+                quant_v_head(p, V, bh, &qt);
+            }
         }
         fwd_ctx F = {p, Q, K, V, idx, alpha, blocks, out, bh, items, h, z,
                      variant, quantize, &qt, bound, acc_eps};
@@ -710,6 +756,8 @@ static int forward_common(const orc_problem* p, const void* Q, const void* K, co
             free(qt.sq);
             free(qt.sk);
             free(qt.mu);
+            free(qt.vh);
+            free(qt.sv);
         }
     }
     free(items);

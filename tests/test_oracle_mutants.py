@@ -40,6 +40,9 @@ MUTANTS = {
     "denominator_without_phi_q": ("den += pq[c] * Zi[c];", "den += Zi[c];"),
     "alpha_of_wrong_head": ("F->alpha[h]);", "F->alpha[0]);"),
     "alpha_block_ignored": ("F->alpha[(size_t)h * Tq + i]", "F->alpha[(size_t)h * Tq]"),
+    "v_scale_wrong_channel": ("(double)F->qt->sv[e]", "(double)F->qt->sv[0]"),
+    "v_codes_unused": ("if (p->lowbit_v && F->quantize)", "if (p->lowbit_v && !F->quantize)"),
+    "v_scale_not_max": ("            if (v > amax) amax = v;", "            amax = v;"),
     "numerator_transposed_H": ("num += pq[c] * Hi[(size_t)c * d + e];", "num += pq[c] * Hi[(size_t)e * d + c];"),
 }
 
@@ -61,6 +64,10 @@ PINS = [
     (pins.test_lowbit_error_is_small, ()),
     (pins.test_lowbit_single_tile_closed_form, ()),
     (pins.test_lowbit_branch_and_flip_bound_brute_force, ()),
+    (pins.test_lowbit_v_codes_and_scales_vs_torch, ()),
+    (pins.test_lowbit_v_identity_quantiser_equals_exact, ()),
+    (pins.test_lowbit_v_single_tile_closed_form, ()),
+    (pins.test_lowbit_v_constant_v, ()),
 ]
 
 

@@ -557,6 +557,78 @@ def test_lowbit_single_tile_closed_form(orc):
 
 
 # --------------------------------------------------------------------------
+# fully low-bit variant: V quantised per channel as well
+# --------------------------------------------------------------------------
+def _lowbit_v_problem(orc, x):
+    w = x.wl
+    return orc.problem(w.B, w.H, w.N, w.d, w.bq, w.bkv, w.topk_frac, 1, w.dtype, lowbit_v=1)
+
+
+def test_lowbit_v_codes_and_scales_vs_torch(orc):
+    """s_V(c) = max over the valid tokens of |V(., c)| / 448 (fp32), and the
+    codes are torch's float8_e4m3fn cast (round to nearest even) of
+    V / s_V saturated to +-448."""
+    x = small(dtype="bf16", N=700, d=64, frac=0.3)
+    p = _lowbit_v_problem(orc, x)
+    for bh in range(2):
+        vh, sv = orc.quant_v_fp8(p, x.v, bh)
+        v = I.bf16_bits_to_f32(x.v[0, bh])
+        ref_s = (np.abs(v).max(0) / np.float32(448.0)).astype(np.float32)
+        assert np.array_equal(sv, np.where(ref_s > 0, ref_s, np.float32(1.0)))
+        r = np.clip(v / sv[None, :], -448.0, 448.0).astype(np.float32)
+        codes = torch.from_numpy(r).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+        assert np.array_equal(vh, codes)
+        dec = torch.from_numpy(vh).view(torch.float8_e4m3fn).float().numpy()
+        assert (np.abs(dec).max(0) == 448.0).all()
+
+
+def test_lowbit_v_identity_quantiser_equals_exact(orc):
+    x = small(dtype="bf16", N=700, d=64, frac=0.3)
+    p = _lowbit_v_problem(orc, x)
+    idx, _, _, _ = orc.route(p, x.q, x.k, x.wq, x.wk)
+    o = orc.forward_full(p, x.q, x.k, x.v, idx, x.alpha)
+    o8 = orc.forward_full(p, x.q, x.k, x.v, idx, x.alpha, variant="fp8", quantize=False)
+    assert np.abs(o - o8).max() < 1e-12
+
+
+def test_lowbit_v_single_tile_closed_form(orc):
+    """One selected tile, alpha = 1: O_s = sum P^ Vhat s_V / sum P^ with P^ and
+    Vhat from torch's float8 cast."""
+    wl = I.Workload("t", 1, 1, 300, 32, 64, 64, 0.2, "bf16", "smooth", seed=2, alpha=(1.0,))
+    x = I.make_inputs(wl)
+    p = _lowbit_v_problem(orc, x)
+    idx, _, _, _ = orc.route(p, x.q, x.k, x.wq, x.wk)
+    assert idx.shape[-1] == 1
+    out = orc.forward(p, x.q, x.k, x.v, idx, x.alpha, orc.all_blocks(p), variant="fp8")
+    val = _e4m3_values()
+    qh, kh, sq, sk, _ = orc.quant_fp8(p, x.q, x.k, 0)
+    v = I.bf16_bits_to_f32(x.v[0, 0])
+    sv = (np.abs(v).max(0) / np.float32(448.0)).astype(np.float32)
+    r = np.clip(v / sv[None, :], -448.0, 448.0).astype(np.float32)
+    Vq = torch.from_numpy(r).to(torch.float8_e4m3fn).double().numpy() * sv.astype(np.float64)
+    for t in range(wl.N):
+        i = t // 64
+        j = int(idx[0, 0, i, 0])
+        u = np.arange(j * 64, min(wl.N, j * 64 + 64))
+        lg = (val[kh[u]] @ val[qh[t]]) * float(sq[i]) * float(sk[j]) / math.sqrt(32)
+        f = torch.from_numpy((256.0 * np.exp(lg - lg.max())).astype(np.float32))
+        ph = f.to(torch.float8_e4m3fn).double().numpy() / 256.0
+        assert np.abs(out[i, t % 64] - ph @ Vq[u] / ph.sum()).max() < 1e-12
+
+
+def test_lowbit_v_constant_v(orc):
+    """V = c everywhere: every code is +-448 and O_s = c up to the fp32
+    rounding of s_V = |c| / 448 (row normalisation survives quantisation)."""
+    x = small(dtype="bf16", N=500, d=64, frac=0.3, alpha=(1.0, 1.0))
+    c = np.float32(-1.375)
+    x.v[...] = I.round_to_bf16_bits(np.full(x.v.shape, c, np.float32))
+    p = _lowbit_v_problem(orc, x)
+    idx, _, _, _ = orc.route(p, x.q, x.k, x.wq, x.wk)
+    o = orc.forward_full(p, x.q, x.k, x.v, idx, x.alpha, variant="fp8")
+    assert np.abs(o - float(c)).max() <= abs(float(c)) * 2.0 ** -22
+
+
+# --------------------------------------------------------------------------
 # workload generator sanity (shapes and statistics stated for the workloads)
 # --------------------------------------------------------------------------
 def test_tiny_workload_statistics():
