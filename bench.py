@@ -317,31 +317,34 @@ def main():
     }
 
     if not args.no_fp8:
-        ws8 = S.workspace(p, S.OP_FORWARD_FP8)
+        # the low-bit sparse branch on the same inputs: Q, K and P in e4m3
+        # ("fp8"), and with V quantised per channel as well ("fp8_v")
+        for key, lb in (("fp8", S.LOWBIT_QK), ("fp8_v", S.LOWBIT_QKV)):
+            p8 = S.problem(w.B, w.H, w.N, w.d, w.bq, w.bkv, w.topk_frac, 1, w.dtype, lowbit=lb)
+            ws8 = S.workspace(p8, S.OP_FORWARD_FP8)
 
-        def step8():
-            S.sla2_route(p, q, k, wq, wk, idx, None, ws_r, stream)
-            S.sla2_forward_fp8(p, q, k, v, idx, al, O, ws8, stream)
+            def step8():
+                S.sla2_route(p8, q, k, wq, wk, idx, None, ws_r, stream)
+                S.sla2_forward_fp8(p8, q, k, v, idx, al, O, ws8, stream)
 
-        for _ in range(args.warmup):
-            step8()
-        torch.cuda.synchronize()
-        S.timing_start(64 * args.steps + 64)
-        ev0.record(stream)
-        for _ in range(args.steps):
-            step8()
-        ev1.record(stream)
-        torch.cuda.synchronize()
-        k8 = S.timing_stop()
-        ms8 = ev0.elapsed_time(ev1) / args.steps
-        st8 = {n_: ms_ / c_ for n_, (ms_, c_) in k8.items()}
-        f8_ms = st8.get("fused_fp8")
-        # the low-bit kernel's work: Q K^T on the fp8 cores, P V and phi(Q) H
-        # on the fp16 ones; priced against the fp16 peak (the larger share)
-        out["fp8"] = {"ms_per_step": ms8, "tops": dense / (ms8 * 1e-3) / 1e12,
-                      "stages_ms": st8,
-                      "fused_fp8_tflops": (fl_sparse + fl_apply) / (f8_ms * 1e-3) / 1e12
-                      if f8_ms else None}
+            for _ in range(args.warmup):
+                step8()
+            torch.cuda.synchronize()
+            S.timing_start(64 * args.steps + 64)
+            ev0.record(stream)
+            for _ in range(args.steps):
+                step8()
+            ev1.record(stream)
+            torch.cuda.synchronize()
+            k8 = S.timing_stop()
+            ms8 = ev0.elapsed_time(ev1) / args.steps
+            st8 = {n_: ms_ / c_ for n_, (ms_, c_) in k8.items()}
+            f8_ms = st8.get("fused_fp8")
+            out[key] = {"ms_per_step": ms8, "tops": dense / (ms8 * 1e-3) / 1e12,
+                        "stages_ms": st8,
+                        "fused_fp8_tflops": (fl_sparse + fl_apply) / (f8_ms * 1e-3) / 1e12
+                        if f8_ms else None}
+            del ws8
 
     if not args.no_cpu_baseline:
         log("bench: timing the CPU oracle on a sample")

@@ -30,7 +30,7 @@
  *    any error nothing is launched and no output is written.
  *  - Returned codes: SLA2_OK; SLA2_EINVAL (null or misaligned pointer,
  *    B/H/N <= 0, topk_frac outside [0,1] or NaN, w_heads not in {1,H}, an
- *    unknown layout, alpha mode or output dtype);
+ *    unknown layout, alpha mode, output dtype or low-bit mode);
  *    SLA2_EUNSUPPORTED (a valid but unbuilt combination: d not in {64,128},
  *    bq not in {64,128}, bkv != 64, phi other than elu+1, fp8 with fp32
  *    inputs or with bq or d other than 128, more than 65535 heads or a number of blocks outside the limits
@@ -78,6 +78,10 @@ typedef enum { SLA2_LAYOUT_BHND = 0, SLA2_LAYOUT_BNHD = 1 } sla2_layout;
  * (alpha [H]) or one per head and query block (alpha [H][T_q]) */
 typedef enum { SLA2_ALPHA_PER_HEAD = 0, SLA2_ALPHA_PER_QBLOCK = 1 } sla2_alpha_mode;
 
+/* what sla2_forward_fp8 quantises ("SLA2 深度解读" 07: low-bit Q K^T and
+ * P V): Q, K and P (V stays bf16), or V as well, per channel */
+typedef enum { SLA2_LOWBIT_QK = 0, SLA2_LOWBIT_QKV = 1 } sla2_lowbit;
+
 /* operations, for sla2_workspace_bytes */
 typedef enum { SLA2_OP_ROUTE = 0, SLA2_OP_FORWARD = 1, SLA2_OP_FORWARD_FP8 = 2 } sla2_op;
 
@@ -91,6 +95,7 @@ typedef struct {
     int32_t layout;      /* sla2_layout of Q, K, V and O                        */
     int32_t alpha_mode;  /* sla2_alpha_mode                                     */
     int32_t out_dtype;   /* sla2_dtype of O (SLA2_F32 or SLA2_BF16)             */
+    int32_t lowbit;      /* sla2_lowbit (sla2_forward_fp8 only)                 */
 } sla2_problem;
 
 /* T_q = ceil(N / bq) and T_kv = ceil(N / bkv).  The last block of each kind
@@ -170,6 +175,11 @@ sla2_status sla2_forward(const sla2_problem* p, const void* Q, const void* K,
  *   P~ = exp(logit - running max) quantised as e4m3(256 P~) / 256 before
  *   P V (V unquantised, fp16) and the row sum taken over the quantised
  *   values.  Router and linear branch are those of sla2_forward.
+ *   With lowbit == SLA2_LOWBIT_QKV, V is quantised too: s_V(c) = max over the
+ *   N valid tokens of |V(., c)| / 448 per head and channel (1 if 0), Vhat =
+ *   e4m3(V / s_V) (fp32 division, round to nearest even, saturating), and
+ *   P V runs on the e4m3 matrix cores as (256 P^) Vhat, scaled by s_V(c) per
+ *   output channel; the linear branch keeps V in fp16.
  *   The fp8 matrix cores do not sum their products exactly (the error of a
  *   dot product reaches about 2^-15 of the sum of the absolute products), so
  *   a P~ lying that close to an e4m3 rounding midpoint may take either
@@ -192,6 +202,18 @@ sla2_status sla2_forward_fp8(const sla2_problem* p, const void* Q, const void* K
 sla2_status sla2_quantize_fp8(const sla2_problem* p, const void* Q, const void* K,
                               uint8_t* Qhat, uint8_t* Khat, float* sQ, float* sK,
                               float* mu, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * sla2_quantize_v_fp8 -- the per-channel V quantisation of the fully low-bit
+ * sparse branch alone (what sla2_forward_fp8 runs with lowbit ==
+ * SLA2_LOWBIT_QKV), for inspection.  Requires dtype == SLA2_BF16, d == 128
+ * and lowbit == SLA2_LOWBIT_QKV.
+ * Out (device): Vhat [B,H,T_kv*bkv,d] e4m3 codes (head-major, rows past N are
+ * 0), s_V [B,H,d] fp32.
+ * ws : sla2_workspace_bytes(p, SLA2_OP_FORWARD_FP8) bytes.
+ */
+sla2_status sla2_quantize_v_fp8(const sla2_problem* p, const void* V, uint8_t* Vhat,
+                                float* sV, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * Kernel timing (diagnostics, host-side state).  sla2_timing_start(n) makes

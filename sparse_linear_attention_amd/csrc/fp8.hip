@@ -9,6 +9,9 @@
 //   Khat    = e4m3(K' / s_K), Qhat = e4m3(Q / s_Q): OCP e4m3, round to
 //             nearest even, saturated at +-448.
 // Rows past N are written as code 0.  d = 128.
+// Fully low-bit variant (P V on the e4m3 matrix cores as well): s_V(c) =
+// max over the N valid tokens of |V(., c)| / 448 per head and channel (1 if
+// 0), Vhat = e4m3(V / s_V) (fp32 division, nearest even, saturated).
 #include "sla2_internal.h"
 
 namespace sla2 {
@@ -133,10 +136,126 @@ __global__ __launch_bounds__(256) void quant_kernel(
     }
 }
 
+// Per-channel max |V| over chunks of 1024 tokens (fp32 max: exact and
+// order independent).  grid (chunks, BH).
+__global__ __launch_bounds__(256) void vmax_kernel(const uint16_t* __restrict__ V,
+                                                   float* __restrict__ part, int N, int nch,
+                                                   int H, Strides st) {
+    __shared__ float red[16][128];
+    const long bh = blockIdx.y;
+    const int chunk = blockIdx.x;
+    const int g = threadIdx.x & 15, r = threadIdx.x >> 4;
+    const int t0 = chunk * kTokPerChunk, t1 = min(N, t0 + kTokPerChunk);
+    const uint16_t* Vh = V + head_base(st, bh, H);
+    float m8[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) m8[e] = 0.0f;
+    for (int t = t0 + r; t < t1; t += 16) {
+        const uint4 v = *reinterpret_cast<const uint4*>(Vh + (size_t)t * st.t + g * 8);
+        const unsigned w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            m8[2 * e] = fmaxf(m8[2 * e], fabsf(bf16_lo(w[e])));
+            m8[2 * e + 1] = fmaxf(m8[2 * e + 1], fabsf(bf16_hi(w[e])));
+        }
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) red[r][g * 8 + e] = m8[e];
+    __syncthreads();
+    if (threadIdx.x < 128) {
+        float a = 0.0f;
+        for (int rr = 0; rr < 16; ++rr) a = fmaxf(a, red[rr][threadIdx.x]);
+        part[((size_t)bh * nch + chunk) * 128 + threadIdx.x] = a;
+    }
+}
+
+// s_V = (max over the chunk maxima) / 448, 1 if the maximum is 0.
+// grid (BH), 128 threads.
+__global__ void vscale_kernel(const float* __restrict__ part, float* __restrict__ sv, int nch) {
+    const long bh = blockIdx.x;
+    const int c = threadIdx.x;
+    float a = 0.0f;
+    for (int k = 0; k < nch; ++k) a = fmaxf(a, part[((size_t)bh * nch + k) * 128 + c]);
+    sv[bh * 128 + c] = a > 0.0f ? a / 448.0f : 1.0f;
+}
+
+// Key u of a 64-key block -> its position in the k operand of the e4m3 P V
+// product: the lane holding query column q and k half h carries the codes of
+// its S^T accumulators s[mt][i] (key 32 mt + 8 (i / 4) + 4 h + i % 4) at
+// positions 32 h + 16 mt + i.
+__device__ inline int pv8_pos(int u) {
+    return 32 * ((u >> 2) & 1) + 16 * (u >> 5) + 4 * ((u >> 3) & 3) + (u & 3);
+}
+
+// Codes of V / s_V for KV block j (grid (Tkv, BH), 256 threads: token u =
+// t % 64, channels 32 (t / 64) .. +31).  TILE: the block transposed, [128
+// channels][64 positions] with key u at pv8_pos(u); otherwise rows [64][128].
+// Rows past N are code 0.
+template <bool TILE>
+__global__ __launch_bounds__(256) void vquant_kernel(const uint16_t* __restrict__ V,
+                                                     const float* __restrict__ sv,
+                                                     uint8_t* __restrict__ out, int N, int Tkv,
+                                                     int H, Strides st) {
+    __shared__ __attribute__((aligned(16))) uint8_t tile[128 * 64];
+    const int j = blockIdx.x;
+    const long bh = blockIdx.y;
+    const int u = threadIdx.x & 63, cg = threadIdx.x >> 6;
+    const int tok = j * 64 + u;
+    const bool ok = tok < N;
+    const uint16_t* vrow = V + head_base(st, bh, H) + (size_t)(ok ? tok : 0) * st.t + 32 * cg;
+    const float* s = sv + bh * 128 + 32 * cg;
+    unsigned words[8];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        uint4 v = make_uint4(0, 0, 0, 0);
+        if (ok) v = *reinterpret_cast<const uint4*>(vrow + 8 * q);
+        const unsigned w[4] = {v.x, v.y, v.z, v.w};
+        unsigned pk[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            pk[e] = e4m3_pair(bf16_lo(w[e]) / s[8 * q + 2 * e], bf16_hi(w[e]) / s[8 * q + 2 * e + 1]);
+        words[2 * q] = pk[0] | (pk[1] << 16);
+        words[2 * q + 1] = pk[2] | (pk[3] << 16);
+    }
+    if (TILE) {
+        const int pos = pv8_pos(u);
+#pragma unroll
+        for (int b = 0; b < 32; ++b)
+            tile[(32 * cg + b) * 64 + pos] = (uint8_t)(words[b >> 2] >> (8 * (b & 3)));
+        __syncthreads();
+        uint8_t* dst = out + ((size_t)bh * Tkv + j) * 8192;
+        *reinterpret_cast<uint4*>(dst + threadIdx.x * 32) =
+            *reinterpret_cast<const uint4*>(tile + threadIdx.x * 32);
+        *reinterpret_cast<uint4*>(dst + threadIdx.x * 32 + 16) =
+            *reinterpret_cast<const uint4*>(tile + threadIdx.x * 32 + 16);
+    } else {
+        uint8_t* dst = out + (((size_t)bh * Tkv + j) * 64 + u) * 128 + 32 * cg;
+        *reinterpret_cast<uint4*>(dst) = make_uint4(words[0], words[1], words[2], words[3]);
+        *reinterpret_cast<uint4*>(dst + 16) = make_uint4(words[4], words[5], words[6], words[7]);
+    }
+}
+
 }  // namespace
 
-hipError_t launch_quantize_fp8(const Dims& D, const void* Q, const void* K, const FwdWS& ws,
-                               hipStream_t s) {
+static hipError_t launch_vscale(const Dims& D, const void* V, const FwdWS& ws, hipStream_t s) {
+    const int nch = (D.N + kTokPerChunk - 1) / kTokPerChunk;
+    vmax_kernel<<<dim3(nch, (unsigned)D.BH), 256, 0, s>>>((const uint16_t*)V, ws.vmax, D.N, nch,
+                                                          D.H, D.st);
+    vscale_kernel<<<dim3((unsigned)D.BH), 128, 0, s>>>(ws.vmax, ws.sv, nch);
+    return hipGetLastError();
+}
+
+hipError_t launch_quantize_v_rows(const Dims& D, const void* V, uint8_t* vhat_rows,
+                                  const FwdWS& ws, hipStream_t s) {
+    hipError_t e = launch_vscale(D, V, ws, s);
+    if (e != hipSuccess) return e;
+    vquant_kernel<false><<<dim3(D.Tkv, (unsigned)D.BH), 256, 0, s>>>(
+        (const uint16_t*)V, ws.sv, vhat_rows, D.N, D.Tkv, D.H, D.st);
+    return hipGetLastError();
+}
+
+hipError_t launch_quantize_fp8(const Dims& D, const void* Q, const void* K, const void* V,
+                               const FwdWS& ws, hipStream_t s) {
     const int nch = (D.N + kTokPerChunk - 1) / kTokPerChunk;
     timing_before(s, K_QUANT_MEAN);
     ksum_kernel<<<dim3(nch, (unsigned)D.BH), 256, 0, s>>>((const uint16_t*)K, ws.ksum, D.N, nch,
@@ -148,6 +267,14 @@ hipError_t launch_quantize_fp8(const Dims& D, const void* Q, const void* K, cons
         (const uint16_t*)Q, (const uint16_t*)K, ws.mu, ws.qhat, ws.khat, ws.sq, ws.sk, D.N, D.Tq,
         D.Tkv, D.H, D.st);
     timing_after(s, K_QUANT);
+    if (D.lowbit_v && V) {
+        timing_before(s, K_QUANT_V);
+        hipError_t e = launch_vscale(D, V, ws, s);
+        if (e != hipSuccess) return e;
+        vquant_kernel<true><<<dim3(D.Tkv, (unsigned)D.BH), 256, 0, s>>>(
+            (const uint16_t*)V, ws.sv, ws.vhat, D.N, D.Tkv, D.H, D.st);
+        timing_after(s, K_QUANT_V);
+    }
     return hipGetLastError();
 }
 

@@ -47,17 +47,19 @@ constexpr int kLdsBytes = 80 * 1024;
 constexpr int kKRaw = 16384;  // K tile, bf16
 constexpr int kKHat = 8192;   // Khat tile, e4m3
 constexpr int kVT = 16384;    // V^T tile, fp16
+constexpr int kV8 = 8192;     // Vhat^T tile, e4m3 (fully low-bit P V)
 constexpr float kRescaleThr = 8.0f;
 
 __shared__ __attribute__((aligned(1024))) char s_lds[kLdsBytes];
 
-template <bool LOWBIT>
+template <bool LOWBIT, bool LOWV>
 struct Plan {
     static constexpr int kStage = LOWBIT ? kKHat : kKRaw;
     static constexpr int kStages = 3;
     static constexpr int vOff = kStages * kStage;
-    static constexpr int nK = LOWBIT ? 2 : 4;  // loads per lane, K tile
-    static_assert(vOff + 2 * kVT <= kLdsBytes, "LDS budget");
+    static constexpr int v8Off = vOff + 2 * kVT;  // Vhat^T stages (LOWV)
+    static constexpr int nK = LOWBIT ? 2 : 4;     // loads per lane, K tile
+    static_assert(vOff + 2 * kVT + (LOWV ? 2 * kV8 : 0) <= kLdsBytes, "LDS budget");
     static_assert(32768 + 512 <= kLdsBytes, "epilogue LDS");
 };
 
@@ -67,10 +69,18 @@ template <> struct QOp<true> { i32x8 f[2]; };    // 2 k-steps of 64 channels
 
 // Tile loads.  A tile is moved in 1 KB pieces, piece u = 4i + w going to
 // byte u * 1024 of its LDS stage; the lane's 16 bytes of piece u sit at the
-// same per-lane byte offset (plus 4 KB per i) in every tile, so each load is
-// a uniform base plus one per-lane offset.
-__device__ inline void load_lds16(const char* src, uint32_t off, char* dst) {
-    __builtin_amdgcn_global_load_lds(src + off, SLA2_LDS(dst), 16, 0, 0);
+// same per-lane byte offset (plus a fixed step per i) in every tile.  The
+// loads are buffer loads on a per-head resource: the tile's offset is a
+// scalar and each lane keeps a single 32-bit offset (the host limits every
+// per-head span to 2^31 bytes).
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+__device__ inline rsrc_t head_rsrc(const void* base) {
+    // raw buffer (stride 0), no range limit, 32-bit data format
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, -1, 0x00020000);
+}
+__device__ inline void load_lds16(rsrc_t r, uint32_t voff, uint32_t soff, char* dst) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, SLA2_LDS(dst), 16, voff, soff, 0, 0);
 }
 
 // per-lane offsets: K rows are 256 B apart in LDS (16-byte chunk c of row r
@@ -88,36 +98,49 @@ __device__ inline uint32_t t_lane_off(int w, int lane) {
 
 // K (or Khat) tile j into one K stage
 template <bool LOWBIT>
-__device__ inline void issue_k(char* kst, const char* k_h, const char* khat_h, int j, int N,
-                               int w, int lane, uint32_t koff, uint32_t toff, uint32_t rp) {
+__device__ inline void issue_k(char* kst, rsrc_t rk, int j, int N, int w, int lane,
+                               uint32_t koff, uint32_t toff, uint32_t rp) {
     if (LOWBIT) {  // Khat rows past N are stored (as zeros)
-        const char* src = khat_h + (size_t)j * 8192;
 #pragma unroll
-        for (int i = 0; i < 2; ++i) load_lds16(src + 4096 * i, toff, kst + (4 * i + w) * 1024);
+        for (int i = 0; i < 2; ++i)
+            load_lds16(rk, toff, (uint32_t)j * 8192 + 4096 * i, kst + (4 * i + w) * 1024);
     } else if (j * 64 + 64 <= N) {
-        const char* src = k_h + (size_t)j * 64 * rp;
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-            load_lds16(src + (size_t)16 * rp * i, koff, kst + (4 * i + w) * 1024);
+            load_lds16(rk, koff, (uint32_t)j * 64 * rp + 16 * rp * i, kst + (4 * i + w) * 1024);
     } else {  // ragged last block: padding rows read row N-1 (their logits are masked)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int row = 16 * i + 4 * w + (lane >> 4);
             const int tok = min(j * 64 + row, N - 1);
             const uint32_t off = (uint32_t)tok * rp + ((uint32_t)((lane & 15) ^ (row & 15)) << 4);
-            load_lds16(k_h, off, kst + (4 * i + w) * 1024);
+            load_lds16(rk, off, 0, kst + (4 * i + w) * 1024);
         }
     }
 }
 
 // V^T tile j into one V stage
-__device__ inline void issue_v(char* vst, const char* vt_h, int j, int w, uint32_t toff) {
-    const char* src = vt_h + (size_t)j * 16384;
+__device__ inline void issue_v(char* vst, rsrc_t rv, int j, int w, uint32_t toff) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) load_lds16(src + 4096 * i, toff, vst + (4 * i + w) * 1024);
+    for (int i = 0; i < 4; ++i)
+        load_lds16(rv, toff, (uint32_t)j * 16384 + 4096 * i, vst + (4 * i + w) * 1024);
 }
 
-template <bool LIN, bool LOWBIT>
+// Vhat^T tile j (8 KB: [128 channels][64 B]) into one stage; LDS row r holds
+// 16-byte chunk q at chunk q ^ ((r >> 2) & 3) (conflict-free reads of 32 B
+// per lane); two 1 KB pieces per wave.
+__device__ inline uint32_t v8_lane_off(int lane) {
+    return (uint32_t)((lane >> 2) * 64 + (((lane & 3) ^ ((lane >> 4) & 3)) << 4));
+}
+__device__ inline void issue_v8(char* v8st, rsrc_t rv8, int j, int w, uint32_t v8off) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int u = 4 * i + w;
+        load_lds16(rv8, v8off, (uint32_t)j * kV8 + u * 1024, v8st + u * 1024);
+    }
+}
+
+template <bool LIN, bool LOWBIT, bool LOWV>
 __global__ __launch_bounds__(256, 2) void fused128_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ vt, const uint16_t* __restrict__ pkt,
@@ -125,9 +148,13 @@ __global__ __launch_bounds__(256, 2) void fused128_kernel(
     const float* __restrict__ alpha, const float* __restrict__ htot,
     const float* __restrict__ ztot, const uint8_t* __restrict__ qhat,
     const uint8_t* __restrict__ khat, const float* __restrict__ sq,
-    const float* __restrict__ sk, void* __restrict__ O, int N, int Tq, int Tkv, int k,
+    const float* __restrict__ sk, const uint8_t* __restrict__ vhat,
+    const float* __restrict__ sv, void* __restrict__ O, int N, int Tq, int Tkv, int k,
     int H, Strides st, int alpha_qblock, int out_bf16) {
-    using P = Plan<LOWBIT>;
+    static_assert(LOWBIT || !LOWV, "quantised V only with the low-bit Q K^T");
+    // V^T in fp16 feeds P V, and G (the linear branch) with LOWV
+    constexpr bool kV16 = !LOWV || LIN;
+    using P = Plan<LOWBIT, LOWV>;
     const int t = threadIdx.x, lane = t & 63, l32 = lane & 31, hl = lane >> 5;
     const int w = __builtin_amdgcn_readfirstlane(t >> 6);
     long bh;
@@ -186,41 +213,45 @@ __global__ __launch_bounds__(256, 2) void fused128_kernel(
     float m_ref = -INFINITY, l_part = 0.0f;
 
     const int32_t* sel = idx + ((size_t)bh * Tq + qb) * k;
-    const char* k_h = reinterpret_cast<const char*>(K + head_base(st, bh, H));
     const uint32_t rp = (uint32_t)st.t * 2;  // bytes between consecutive K rows
-    const char* khat_h =
-        LOWBIT ? reinterpret_cast<const char*>(khat + (size_t)bh * Tkv * 64 * 128) : nullptr;
-    const char* vt_h = reinterpret_cast<const char*>(vt + (size_t)bh * Tkv * 128 * 64);
+    const rsrc_t rk = LOWBIT ? head_rsrc(khat + (size_t)bh * Tkv * 64 * 128)
+                             : head_rsrc(K + head_base(st, bh, H));
+    const rsrc_t rv = head_rsrc(vt + (size_t)bh * Tkv * 128 * 64);
     const uint32_t koff = k_lane_off(w, lane, rp), toff = t_lane_off(w, lane);
     // this wave's rows (phi channels 32w .. 32w+31) of the phi(K)^T tiles, and
     // the matching z_j entries
-    const char* pk_h = reinterpret_cast<const char*>(pkt + (size_t)bh * Tkv * 128 * 64);
+    const rsrc_t rpk = head_rsrc(pkt + (size_t)bh * Tkv * 128 * 64);
     const uint32_t pkoff = (uint32_t)((32 * w + l32) * 128 + 16 * hl);
-    const char* zb_h = reinterpret_cast<const char*>(zb + (size_t)bh * Tkv * 128);
+    const rsrc_t rz = head_rsrc(zb + (size_t)bh * Tkv * 128);
     const uint32_t zoff = (uint32_t)(32 * w + l32) * 4;
     const float* sk_h = LOWBIT ? sk + (size_t)bh * Tkv : nullptr;
     char* const kbase = s_lds;
     char* const vbase = s_lds + P::vOff;
+    char* const v8base = s_lds + P::v8Off;
+    const rsrc_t rv8 = head_rsrc(LOWV ? vhat + (size_t)bh * Tkv * kV8 : vhat);
+    const uint32_t v8off = v8_lane_off(lane);
     constexpr int DK = P::kStages - 1;  // K prefetch distance
 
     // phi(K_j)^T as the B operand of 4 k-steps of 16 keys, and z_j
     f16x8 pk[4];
     float zj = 0.0f;
     auto load_pk = [&](int j) {
-        const char* src = pk_h + (size_t)j * 16384;
 #pragma unroll
         for (int kq = 0; kq < 4; ++kq)
-            pk[kq] = *reinterpret_cast<const f16x8*>(src + 32 * kq + pkoff);
-        const float z = *reinterpret_cast<const float*>(zb_h + (size_t)j * 512 + zoff);
+            pk[kq] = __builtin_bit_cast(
+                f16x8, __builtin_amdgcn_raw_buffer_load_b128(rpk, pkoff + 32 * kq, (uint32_t)j * 16384, 0));
+        const float z = __builtin_bit_cast(
+            float, __builtin_amdgcn_raw_buffer_load_b32(rz, zoff, (uint32_t)j * 512, 0));
         zj = hl == 0 ? z : 0.0f;
     };
 
     // ---- prologue: K_0, V_0, K_1 [, phi(K_0)^T, z_0]
     if (k > 0) {
-        issue_k<LOWBIT>(kbase, k_h, khat_h, sel[0], N, w, lane, koff, toff, rp);
-        issue_v(vbase, vt_h, sel[0], w, toff);
+        issue_k<LOWBIT>(kbase, rk, sel[0], N, w, lane, koff, toff, rp);
+        if (kV16) issue_v(vbase, rv, sel[0], w, toff);
+        if (LOWV) issue_v8(v8base, rv8, sel[0], w, v8off);
         if (k > 1)
-            issue_k<LOWBIT>(kbase + P::kStage, k_h, khat_h, sel[1], N, w, lane, koff, toff, rp);
+            issue_k<LOWBIT>(kbase + P::kStage, rk, sel[1], N, w, lane, koff, toff, rp);
         asm volatile("" ::: "memory");
         if (LIN) load_pk(sel[0]);
         asm volatile("" ::: "memory");
@@ -235,15 +266,18 @@ __global__ __launch_bounds__(256, 2) void fused128_kernel(
         else if (LIN) wait_vmcnt<5>();
         else wait_vmcnt<0>();
         wg_barrier();  // ... and for every wave; all waves are done with tile r-1
-        if (r + 1 < k) issue_v(vbase + ((r + 1) & 1) * kVT, vt_h, sel[r + 1], w, toff);
+        if (r + 1 < k) {
+            if (kV16) issue_v(vbase + ((r + 1) & 1) * kVT, rv, sel[r + 1], w, toff);
+            if (LOWV) issue_v8(v8base + ((r + 1) & 1) * kV8, rv8, sel[r + 1], w, v8off);
+        }
         if (r + DK < k) {
             const int s2 = kslot + DK >= P::kStages ? kslot + DK - P::kStages : kslot + DK;
-            issue_k<LOWBIT>(kbase + s2 * P::kStage, k_h, khat_h, sel[r + DK], N, w, lane, koff,
-                            toff, rp);
+            issue_k<LOWBIT>(kbase + s2 * P::kStage, rk, sel[r + DK], N, w, lane, koff, toff, rp);
         }
         const int j = sel[r];
         const char* kst = kbase + kslot * P::kStage;
         const char* vst = vbase + (r & 1) * kVT;
+        const char* v8st = v8base + (r & 1) * kV8;
         kslot = kslot + 1 == P::kStages ? 0 : kslot + 1;
         const float c_tile = LOWBIT ? c_base * sk_h[j] : c_base;
 
@@ -259,6 +293,16 @@ __global__ __launch_bounds__(256, 2) void fused128_kernel(
                     vst + erow * 128 + (((2 * kq + hl) ^ ((erow >> 1) & 7)) << 4));
                 o[mt] = mfma_f16(a, pfk, o[mt]);
                 if (LIN) g[mt] = mfma_f16(a, pk[kq], g[mt]);
+            }
+        };
+        // G^T += V^T phi(K) alone (when P V runs on the e4m3 operands)
+        auto g_step = [&](int kq) {
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt) {
+                const int erow = 32 * mt + l32;
+                const f16x8 a = *reinterpret_cast<const f16x8*>(
+                    vst + erow * 128 + (((2 * kq + hl) ^ ((erow >> 1) & 7)) << 4));
+                g[mt] = mfma_f16(a, pk[kq], g[mt]);
             }
         };
         // new running reference after a block of logits whose maximum (over
@@ -325,35 +369,76 @@ __global__ __launch_bounds__(256, 2) void fused128_kernel(
 #pragma unroll
         for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[1][i]);
         const float mref = update_ref(mx);
-        // P^T as the B operand of k-step kq (16 keys) takes rows 8(kq&1)..
-        // 8(kq&1)+7 of m-tile kq>>1
+        if (LOWV) {
+            // codes of 256 P~ as the k operand of the e4m3 P V product: byte
+            // 16 mt + i of this lane is the code of s[mt][i]; the row sum is
+            // taken over the decoded values
+            const float bias = 8.0f - mref;
+            i32x8 pc;
 #pragma unroll
-        for (int kq = 0; kq < 4; ++kq) {
-            f16x8 pf;
-            if (LOWBIT) {  // 256 P~ rounded onto the e4m3 grid, carried exactly in fp16
-                const float bias = 8.0f - mref;
+            for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-                for (int e = 0; e < 8; e += 2) {
-                    const float p0 = __builtin_amdgcn_exp2f(fmaf(s[kq >> 1][8 * (kq & 1) + e], c_tile, bias));
-                    const float p1 = __builtin_amdgcn_exp2f(fmaf(s[kq >> 1][8 * (kq & 1) + e + 1], c_tile, bias));
-                    const int code = __builtin_amdgcn_cvt_pk_fp8_f32(fminf(p0, 448.0f),
-                                                                     fminf(p1, 448.0f), 0, false);
-                    const auto back = __builtin_amdgcn_cvt_pk_f32_fp8(code, false);
-                    pf[e] = (_Float16)back[0];
-                    pf[e + 1] = (_Float16)back[1];
+                for (int q = 0; q < 4; ++q) {
+                    float p4[4];
+#pragma unroll
+                    for (int c = 0; c < 4; ++c)
+                        p4[c] = fminf(__builtin_amdgcn_exp2f(fmaf(s[mt][4 * q + c], c_tile, bias)),
+                                      448.0f);
+                    int wv = __builtin_amdgcn_cvt_pk_fp8_f32(p4[0], p4[1], 0, false);
+                    wv = __builtin_amdgcn_cvt_pk_fp8_f32(p4[2], p4[3], wv, true);
+                    pc[4 * mt + q] = wv;
+                    const auto b0 = __builtin_amdgcn_cvt_pk_f32_fp8(wv, false);
+                    const auto b1 = __builtin_amdgcn_cvt_pk_f32_fp8(wv, true);
+                    l_part += (b0[0] + b0[1]) + (b1[0] + b1[1]);
                 }
-            } else {
+            // O^T += Vhat^T (256 P^)^T on the e4m3 matrix cores (one k-step of
+            // 64 keys per d-tile); the channel scales s_V apply at the end
 #pragma unroll
-                for (int e = 0; e < 8; ++e)
-                    pf[e] = (_Float16)__builtin_amdgcn_exp2f(
-                        fmaf(s[kq >> 1][8 * (kq & 1) + e], c_tile, -mref));
+            for (int mt = 0; mt < 4; ++mt) {
+                const int vrow = 32 * mt + l32, sw = (vrow >> 2) & 3;
+                const uint4 lo = *reinterpret_cast<const uint4*>(v8st + vrow * 64 + (((2 * hl) ^ sw) << 4));
+                const uint4 hi =
+                    *reinterpret_cast<const uint4*>(v8st + vrow * 64 + (((2 * hl + 1) ^ sw) << 4));
+                i32x8 a;
+                a[0] = lo.x; a[1] = lo.y; a[2] = lo.z; a[3] = lo.w;
+                a[4] = hi.x; a[5] = hi.y; a[6] = hi.z; a[7] = hi.w;
+                o[mt] = mfma_fp8(a, pc, o[mt]);
             }
+            if (LIN) {
 #pragma unroll
-            for (int e = 0; e < 8; e += 2) {
-                const f16x2 pr = {pf[e], pf[e + 1]};
-                l_part = __builtin_amdgcn_fdot2(pr, ones, l_part, false);
+                for (int kq = 0; kq < 4; ++kq) g_step(kq);
             }
-            pv_step(kq, pf);
+        } else {
+            // P^T as the B operand of k-step kq (16 keys) takes rows 8(kq&1)..
+            // 8(kq&1)+7 of m-tile kq>>1
+    #pragma unroll
+            for (int kq = 0; kq < 4; ++kq) {
+                f16x8 pf;
+                if (LOWBIT) {  // 256 P~ rounded onto the e4m3 grid, carried exactly in fp16
+                    const float bias = 8.0f - mref;
+    #pragma unroll
+                    for (int e = 0; e < 8; e += 2) {
+                        const float p0 = __builtin_amdgcn_exp2f(fmaf(s[kq >> 1][8 * (kq & 1) + e], c_tile, bias));
+                        const float p1 = __builtin_amdgcn_exp2f(fmaf(s[kq >> 1][8 * (kq & 1) + e + 1], c_tile, bias));
+                        const int code = __builtin_amdgcn_cvt_pk_fp8_f32(fminf(p0, 448.0f),
+                                                                         fminf(p1, 448.0f), 0, false);
+                        const auto back = __builtin_amdgcn_cvt_pk_f32_fp8(code, false);
+                        pf[e] = (_Float16)back[0];
+                        pf[e + 1] = (_Float16)back[1];
+                    }
+                } else {
+    #pragma unroll
+                    for (int e = 0; e < 8; ++e)
+                        pf[e] = (_Float16)__builtin_amdgcn_exp2f(
+                            fmaf(s[kq >> 1][8 * (kq & 1) + e], c_tile, -mref));
+                }
+    #pragma unroll
+                for (int e = 0; e < 8; e += 2) {
+                    const f16x2 pr = {pf[e], pf[e + 1]};
+                    l_part = __builtin_amdgcn_fdot2(pr, ones, l_part, false);
+                }
+                pv_step(kq, pf);
+            }
         }
         if (LIN) {
             zacc += zj;
@@ -438,10 +523,20 @@ __global__ __launch_bounds__(256, 2) void fused128_kernel(
         for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
             for (int i4 = 0; i4 < 4; ++i4) {
+                // O^T row e = 32 mt + 8 i4 + 4 hl + c; with LOWV scaled by s_V(e)
+                float vs[4] = {1.0f, 1.0f, 1.0f, 1.0f};
+                if (LOWV) {
+                    const float4 s4 = *reinterpret_cast<const float4*>(
+                        sv + bh * 128 + 32 * mt + 8 * i4 + 4 * hl);
+                    vs[0] = s4.x;
+                    vs[1] = s4.y;
+                    vs[2] = s4.z;
+                    vs[3] = s4.w;
+                }
                 float v[4];
 #pragma unroll
                 for (int c = 0; c < 4; ++c)
-                    v[c] = a_h * (o[mt][4 * i4 + c] * inv_l) +
+                    v[c] = a_h * (o[mt][4 * i4 + c] * vs[c] * inv_l) +
                            (1.0f - a_h) * (ol[mt][4 * i4 + c] * inv_den);
                 store_out4(O, orow + 32 * mt + 8 * i4 + 4 * hl, v[0], v[1], v[2], v[3], out_bf16);
             }
@@ -462,11 +557,14 @@ hipError_t launch_fused128(const Dims& D, const void* Q, const void* K, const in
     const uint8_t* kh = lowbit ? ws.khat : nullptr;
     const float* sq = lowbit ? ws.sq : nullptr;
     const float* sk = lowbit ? ws.sk : nullptr;
-    auto kern = lowbit ? (lin ? fused128_kernel<true, true> : fused128_kernel<false, true>)
-                       : (lin ? fused128_kernel<true, false> : fused128_kernel<false, false>);
+    const bool lowv = lowbit && D.lowbit_v;
+    auto kern = !lowbit ? (lin ? fused128_kernel<true, false, false> : fused128_kernel<false, false, false>)
+                : !lowv ? (lin ? fused128_kernel<true, true, false> : fused128_kernel<false, true, false>)
+                        : (lin ? fused128_kernel<true, true, true> : fused128_kernel<false, true, true>);
     timing_before(s, lowbit ? K_FUSED_FP8 : K_FUSED_MFMA);
     kern<<<g, 256, 0, s>>>(q, kk, ws.vt, ws.pkt, ws.zb, idx, alpha, ws.htot, ws.ztot, qh, kh, sq,
-                           sk, O, D.N, D.Tq, D.Tkv, D.k, D.H, D.st, D.alpha_qblock, D.out_bf16);
+                           sk, lowv ? ws.vhat : nullptr, lowv ? ws.sv : nullptr, O, D.N, D.Tq,
+                           D.Tkv, D.k, D.H, D.st, D.alpha_qblock, D.out_bf16);
     timing_after(s, lowbit ? K_FUSED_FP8 : K_FUSED_MFMA);
     return hipGetLastError();
 }

@@ -36,6 +36,7 @@ static sla2_status make_dims(const sla2_problem* p, int op, Dims* D) {
     if (p->alpha_mode != SLA2_ALPHA_PER_HEAD && p->alpha_mode != SLA2_ALPHA_PER_QBLOCK)
         return SLA2_EINVAL;
     if (p->out_dtype != SLA2_F32 && p->out_dtype != SLA2_BF16) return SLA2_EINVAL;
+    if (p->lowbit != SLA2_LOWBIT_QK && p->lowbit != SLA2_LOWBIT_QKV) return SLA2_EINVAL;
     if (op < SLA2_OP_ROUTE || op > SLA2_OP_FORWARD_FP8) return SLA2_EINVAL;
     if (p->d != 64 && p->d != 128) return SLA2_EUNSUPPORTED;
     if (p->bq != 64 && p->bq != 128) return SLA2_EUNSUPPORTED;
@@ -70,6 +71,9 @@ static sla2_status make_dims(const sla2_problem* p, int op, Dims* D) {
     }
     D->alpha_qblock = p->alpha_mode == SLA2_ALPHA_PER_QBLOCK;
     D->out_bf16 = p->out_dtype == SLA2_BF16;
+    D->lowbit_v = p->lowbit == SLA2_LOWBIT_QKV;
+    // the fused kernels address a head's rows with 32-bit byte offsets
+    if ((double)p->N * D->st.t * 4.0 >= 2147483648.0) return SLA2_EUNSUPPORTED;
     return SLA2_OK;
 }
 
@@ -116,6 +120,11 @@ size_t layout_forward(const Dims& D, int op, char* base, FwdWS* ws) {
         w.sk = carve<float>(base, off, 4 * bh * D.Tkv);
         w.mu = carve<float>(base, off, 4 * bh * d);
         w.ksum = carve<double>(base, off, 8 * bh * ((D.N + 1023) / 1024) * d);
+        if (D.lowbit_v) {
+            w.vhat = carve<uint8_t>(base, off, bh * (size_t)D.Tkv * d * 64);
+            w.vmax = carve<float>(base, off, 4 * bh * ((D.N + 1023) / 1024) * d);
+            w.sv = carve<float>(base, off, 4 * bh * d);
+        }
     }
     if (ws) *ws = w;
     return align256(off);
@@ -144,7 +153,7 @@ struct Timing {
 const char* kKindNames[K_NUM_KINDS] = {
     "pool_project", "score",       "topk_select", "summaries_valu",
     "summaries_reduce", "fused_valu", "summaries_mfma", "fused_mfma",
-    "quant_mean",   "quant_fp8",   "fused_fp8",
+    "quant_mean",   "quant_fp8",   "fused_fp8",  "quant_v_fp8",
 };
 }  // namespace
 
@@ -274,7 +283,7 @@ SLA2_API sla2_status sla2_forward_fp8(const sla2_problem* p, const void* Q, cons
                                   ws_bytes, &D, &w);
     if (st != SLA2_OK) return st;
     hipStream_t s = (hipStream_t)stream;
-    hipError_t e = launch_quantize_fp8(D, Q, K, w, s);
+    hipError_t e = launch_quantize_fp8(D, Q, K, V, w, s);
     if (e == hipSuccess) e = launch_summaries_mfma(D, K, V, w, s);
     if (e == hipSuccess) e = launch_fused128(D, Q, K, topk_idx, alpha, O, w, true, s);
     return e == hipSuccess ? SLA2_OK : SLA2_EHIP;
@@ -297,7 +306,22 @@ SLA2_API sla2_status sla2_quantize_fp8(const sla2_problem* p, const void* Q, con
     w.sq = sQ;
     w.sk = sK;
     w.mu = mu;
-    hipError_t e = launch_quantize_fp8(D, Q, K, w, (hipStream_t)stream);
+    hipError_t e = launch_quantize_fp8(D, Q, K, nullptr, w, (hipStream_t)stream);
+    return e == hipSuccess ? SLA2_OK : SLA2_EHIP;
+}
+
+SLA2_API sla2_status sla2_quantize_v_fp8(const sla2_problem* p, const void* V, uint8_t* Vhat,
+                                         float* sV, void* ws, size_t ws_bytes, void* stream) {
+    Dims D;
+    sla2_status st = make_dims(p, SLA2_OP_FORWARD_FP8, &D);
+    if (st != SLA2_OK) return st;
+    if (!D.lowbit_v) return SLA2_EUNSUPPORTED;
+    if (!ok_ptr(V) || !ok_ptr(Vhat) || !ok_ptr(sV)) return SLA2_EINVAL;
+    if ((st = check_ws(D, SLA2_OP_FORWARD_FP8, ws, ws_bytes)) != SLA2_OK) return st;
+    FwdWS w;
+    layout_forward(D, SLA2_OP_FORWARD_FP8, (char*)ws, &w);
+    w.sv = sV;
+    hipError_t e = launch_quantize_v_rows(D, V, Vhat, w, (hipStream_t)stream);
     return e == hipSuccess ? SLA2_OK : SLA2_EHIP;
 }
 

@@ -24,6 +24,7 @@ enum KernelKind {
     K_QUANT_MEAN,
     K_QUANT,
     K_FUSED_FP8,
+    K_QUANT_V,
     K_NUM_KINDS
 };
 
@@ -47,6 +48,7 @@ struct Dims {
     Strides st;          // layout of Q, K, V and O
     int alpha_qblock;    // alpha is [H][Tq] (else [H])
     int out_bf16;        // O is bf16 (else fp32)
+    int lowbit_v;        // the low-bit forward quantises V too
 };
 
 // Four consecutive outputs (element offset off, a multiple of 4) as fp32, or
@@ -107,6 +109,11 @@ struct FwdWS {
     float* sk;       // [BH][Tkv]
     float* mu;       // [BH][d]
     double* ksum;    // [BH][ceil(N/1024)][d] partial column sums of K
+    // fully low-bit (V quantised per channel)
+    uint8_t* vhat;   // [BH][Tkv][d][64] e4m3 codes of V / s_V, keys in the order
+                     // of the e4m3 P V product's k operand (see fused128.hip)
+    float* vmax;     // [BH][ceil(N/1024)][d] partial max |V|
+    float* sv;       // [BH][d]
 };
 
 // Lays out the workspace of `op` starting at `base` (may be null to size
@@ -143,8 +150,11 @@ hipError_t launch_fused_mfma(const Dims& D, const void* Q, const void* K,
                              const FwdWS& ws, hipStream_t s);
 
 // low bit
-hipError_t launch_quantize_fp8(const Dims& D, const void* Q, const void* K, const FwdWS& ws,
-                               hipStream_t s);
+hipError_t launch_quantize_fp8(const Dims& D, const void* Q, const void* K, const void* V,
+                               const FwdWS& ws, hipStream_t s);
+// V codes in rows [BH][Tkv*64][d] (inspection; s_V into ws.sv)
+hipError_t launch_quantize_v_rows(const Dims& D, const void* V, uint8_t* vhat_rows,
+                                  const FwdWS& ws, hipStream_t s);
 // d = 128, b_q = 128 fused kernel (bf16, or the low-bit Q K^T with lowbit)
 hipError_t launch_fused128(const Dims& D, const void* Q, const void* K, const int32_t* idx,
                            const float* alpha, void* O, const FwdWS& ws, bool lowbit,

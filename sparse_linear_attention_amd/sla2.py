@@ -19,13 +19,15 @@ PHI_ELU1 = 0
 OP_ROUTE, OP_FORWARD, OP_FORWARD_FP8 = 0, 1, 2
 LAYOUT_BHND, LAYOUT_BNHD = 0, 1
 ALPHA_PER_HEAD, ALPHA_PER_QBLOCK = 0, 1
+LOWBIT_QK, LOWBIT_QKV = 0, 1
 
 
 class Problem(C.Structure):
     _fields_ = [("B", C.c_int32), ("H", C.c_int32), ("N", C.c_int32), ("d", C.c_int32),
                 ("bq", C.c_int32), ("bkv", C.c_int32), ("topk_frac", C.c_float),
                 ("w_heads", C.c_int32), ("phi", C.c_int32), ("dtype", C.c_int32),
-                ("layout", C.c_int32), ("alpha_mode", C.c_int32), ("out_dtype", C.c_int32)]
+                ("layout", C.c_int32), ("alpha_mode", C.c_int32), ("out_dtype", C.c_int32),
+                ("lowbit", C.c_int32)]
 
 
 class SLA2Error(RuntimeError):
@@ -60,6 +62,7 @@ def lib():
         L.sla2_forward.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, C.c_size_t, vp]
         L.sla2_forward_fp8.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, C.c_size_t, vp]
         L.sla2_quantize_fp8.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, C.c_size_t, vp]
+        L.sla2_quantize_v_fp8.argtypes = [P, vp, vp, vp, vp, C.c_size_t, vp]
         L.sla2_timing_start.argtypes = [C.c_int32]
         L.sla2_timing_stop.argtypes = [vp, vp, C.c_int32]
         L.sla2_kernel_name.argtypes = [C.c_int32]
@@ -70,8 +73,8 @@ def lib():
 
 EXPORTS = ("sla2_num_q_blocks", "sla2_num_kv_blocks", "sla2_topk", "sla2_workspace_bytes",
            "sla2_check", "sla2_status_str", "sla2_route", "sla2_forward", "sla2_forward_fp8",
-           "sla2_quantize_fp8", "sla2_timing_start", "sla2_timing_stop", "sla2_kernel_kinds",
-           "sla2_kernel_name")
+           "sla2_quantize_fp8", "sla2_quantize_v_fp8", "sla2_timing_start", "sla2_timing_stop",
+           "sla2_kernel_kinds", "sla2_kernel_name")
 
 
 def _dtype(x):
@@ -82,9 +85,9 @@ def _dtype(x):
 
 def problem(B, H, N, d, bq=128, bkv=64, topk_frac=0.03, w_heads=1, dtype=BF16,
             phi=PHI_ELU1, layout=LAYOUT_BHND, alpha_mode=ALPHA_PER_HEAD,
-            out_dtype=F32) -> Problem:
+            out_dtype=F32, lowbit=LOWBIT_QK) -> Problem:
     return Problem(B, H, N, d, bq, bkv, float(topk_frac), w_heads, phi, _dtype(dtype),
-                   layout, alpha_mode, _dtype(out_dtype))
+                   layout, alpha_mode, _dtype(out_dtype), lowbit)
 
 
 def status_str(s: int) -> str:
@@ -159,6 +162,12 @@ def sla2_quantize_fp8(p, Q, K, Qhat, Khat, sQ, sK, mu, ws=None, stream=None):
     _raise(lib().sla2_quantize_fp8(C.byref(p), _ptr(Q), _ptr(K), _ptr(Qhat), _ptr(Khat),
                                    _ptr(sQ), _ptr(sK), _ptr(mu), wp, wb, _stream(stream)),
            "sla2_quantize_fp8")
+
+
+def sla2_quantize_v_fp8(p, V, Vhat, sV, ws=None, stream=None):
+    wp, wb = _ws(ws)
+    _raise(lib().sla2_quantize_v_fp8(C.byref(p), _ptr(V), _ptr(Vhat), _ptr(sV), wp, wb,
+                                     _stream(stream)), "sla2_quantize_v_fp8")
 
 
 def kernel_names():

@@ -64,6 +64,7 @@ def test_topk_matches_oracle_table(orc):
     (dict(dtype=7), S.EINVAL), (dict(d=96), S.EUNSUPPORTED), (dict(bq=32), S.EUNSUPPORTED),
     (dict(bkv=128), S.EUNSUPPORTED), (dict(N=7681 * 64), S.EUNSUPPORTED),
     (dict(layout=2), S.EINVAL), (dict(alpha_mode=-1), S.EINVAL), (dict(out_dtype=5), S.EINVAL),
+    (dict(lowbit=2), S.EINVAL),
 ])
 def test_check_rejects(kw, code):
     assert S.check(p_ok(**kw), S.OP_ROUTE) == code
@@ -88,6 +89,10 @@ def test_layouts_alpha_modes_and_output_dtypes_are_accepted():
                     assert S.check(p, op) == S.OK
                     # the workspace does not depend on how Q/K/V/O are laid out
                     assert S.workspace_bytes(p, op) == S.workspace_bytes(p_ok(), op)
+    # quantising V as well needs its codes and scales in the fp8 workspace only
+    pv = p_ok(lowbit=S.LOWBIT_QKV)
+    assert S.workspace_bytes(pv, S.OP_FORWARD_FP8) > S.workspace_bytes(p_ok(), S.OP_FORWARD_FP8)
+    assert S.workspace_bytes(pv, S.OP_FORWARD) == S.workspace_bytes(p_ok(), S.OP_FORWARD)
 
 
 def test_workspace_sizes_grow_with_the_problem():

@@ -19,12 +19,13 @@ from tests.test_gpu_parity import TOL, compare_blocks, check_route, dev, say  # 
 
 pytestmark = pytest.mark.gpu
 
-PATHS = [  # name, dtype, N, d, bq, frac, fp8
-    ("f32", "f32", 700, 128, 128, 0.3, False),
-    ("bf16-bq64", "bf16", 513, 128, 64, 0.2, False),
-    ("bf16-d64", "bf16", 1000, 64, 128, 0.3, False),
-    ("bf16-d128", "bf16", 4100, 128, 128, 0.05, False),
-    ("fp8", "bf16", 2000, 128, 128, 0.1, True),
+PATHS = [  # name, dtype, N, d, bq, frac, fp8, lowbit
+    ("f32", "f32", 700, 128, 128, 0.3, False, S.LOWBIT_QK),
+    ("bf16-bq64", "bf16", 513, 128, 64, 0.2, False, S.LOWBIT_QK),
+    ("bf16-d64", "bf16", 1000, 64, 128, 0.3, False, S.LOWBIT_QK),
+    ("bf16-d128", "bf16", 4100, 128, 128, 0.05, False, S.LOWBIT_QK),
+    ("fp8", "bf16", 2000, 128, 128, 0.1, True, S.LOWBIT_QK),
+    ("fp8-v", "bf16", 2000, 128, 128, 0.1, True, S.LOWBIT_QKV),
 ]
 OPTS = [  # layout, alpha mode
     (S.LAYOUT_BNHD, S.ALPHA_PER_HEAD),
@@ -44,7 +45,7 @@ def upload(a, dev, layout):
 @pytest.mark.parametrize("opt", OPTS, ids=["bnhd", "alpha-qblock", "bnhd-alpha-qblock"])
 @pytest.mark.parametrize("path", PATHS, ids=[c[0] for c in PATHS])
 def test_layout_alpha_and_bf16_output(orc, dev, path, opt):
-    name, dtype, N, d, bq, frac, fp8 = path
+    name, dtype, N, d, bq, frac, fp8, lowbit = path
     layout, amode = opt
     H = 3
     gen = "centroids" if dtype == "f32" else "smooth"
@@ -60,7 +61,7 @@ def test_layout_alpha_and_bf16_output(orc, dev, path, opt):
     outs = {}
     for od in (S.F32, S.BF16):
         p = S.problem(1, H, N, d, bq, 64, frac, 1, dtype, layout=layout, alpha_mode=amode,
-                      out_dtype=od)
+                      out_dtype=od, lowbit=lowbit)
         idx, mask = S.route(p, q, k, wq, wk)
         outs[od] = S.forward(p, q, k, v, idx, al, fp8=fp8)
         torch.cuda.synchronize()
@@ -70,7 +71,8 @@ def test_layout_alpha_and_bf16_output(orc, dev, path, opt):
     O = outs[S.F32]
     if layout == S.LAYOUT_BNHD:
         O = O.permute(0, 2, 1, 3).contiguous()
-    op = orc.problem(1, H, N, d, bq, 64, frac, 1, dtype, alpha_mode=amode)
+    op = orc.problem(1, H, N, d, bq, 64, frac, 1, dtype, alpha_mode=amode,
+                     lowbit_v=int(lowbit == S.LOWBIT_QKV))
     tol = TOL["fp8"] if fp8 else TOL[dtype]
     compare_blocks(orc, x, oidx, O, orc.all_blocks(op), tol,
                    variant="fp8" if fp8 else "exact", op=op, alpha=alpha)

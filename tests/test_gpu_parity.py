@@ -41,13 +41,20 @@ def to_dev(x, dev):
     return t(x.q), t(x.k), t(x.v), t(x.wq), t(x.wk), t(x.alpha)
 
 
-def problem_of(x):
+def problem_of(x, lowbit=S.LOWBIT_QK):
     w = x.wl
-    return S.problem(w.B, w.H, w.N, w.d, w.bq, w.bkv, w.topk_frac, x.wq.shape[0], w.dtype)
+    return S.problem(w.B, w.H, w.N, w.d, w.bq, w.bkv, w.topk_frac, x.wq.shape[0], w.dtype,
+                     lowbit=lowbit)
 
 
-def run_gpu(x, dev, fp8=False, want_mask=True):
-    p = problem_of(x)
+def oracle_problem(orc, x, lowbit=S.LOWBIT_QK):
+    w = x.wl
+    return orc.problem(w.B, w.H, w.N, w.d, w.bq, w.bkv, w.topk_frac, x.wq.shape[0], w.dtype,
+                       lowbit_v=int(lowbit == S.LOWBIT_QKV))
+
+
+def run_gpu(x, dev, fp8=False, want_mask=True, lowbit=S.LOWBIT_QK):
+    p = problem_of(x, lowbit)
     q, k, v, wq, wk, al = to_dev(x, dev)
     idx, mask = S.route(p, q, k, wq, wk, want_mask=want_mask)
     o = S.forward(p, q, k, v, idx, al, fp8=fp8)
@@ -315,20 +322,48 @@ FP8_SMALL = [
 ]
 
 
+LOWBITS = [S.LOWBIT_QK, S.LOWBIT_QKV]
+
+
+@pytest.mark.parametrize("lowbit", LOWBITS, ids=["qk", "qkv"])
 @pytest.mark.parametrize("w", FP8_SMALL, ids=[w.name for w in FP8_SMALL])
-def test_fp8_forward_parity(orc, dev, w):
-    say(f"case {w.name}: N={w.N} frac={w.topk_frac}")
+def test_fp8_forward_parity(orc, dev, w, lowbit):
+    say(f"case {w.name}: N={w.N} frac={w.topk_frac} lowbit {lowbit}")
     x = I.make_inputs(w)
-    p, idx, mask, O = run_gpu(x, dev, fp8=True)
+    p, idx, mask, O = run_gpu(x, dev, fp8=True, lowbit=lowbit)
     oidx = check_route(orc, x, idx, mask)
-    compare_blocks(orc, x, oidx, O, orc.all_blocks(orc.problem_of(x)), TOL["fp8"],
-                   variant="fp8")
+    op = oracle_problem(orc, x, lowbit)
+    compare_blocks(orc, x, oidx, O, orc.all_blocks(op), TOL["fp8"], variant="fp8", op=op)
 
 
-def test_fp8_wan14b_sampled(orc, dev):
+@pytest.mark.parametrize("N,H", [(700, 2), (4100, 3), (75600, 1)])
+def test_quantized_v_matches_oracle(orc, dev, N, H):
+    """Per-channel V scales and codes of the fully low-bit branch, bit-exact."""
+    w = wl(f"v{N}", "bf16", N, 128, 128, 0.03, H=H)
+    if N == 75600:
+        w = w.with_(grid=(21, 45, 80))
+    x = I.make_inputs(w)
+    p = problem_of(x, S.LOWBIT_QKV)
+    _, _, v, _, _, _ = to_dev(x, dev)
+    BH = w.B * w.H
+    vh = torch.empty((BH, w.Tkv * 64, w.d), dtype=torch.uint8, device=dev)
+    sv = torch.empty((BH, w.d), dtype=torch.float32, device=dev)
+    S.sla2_quantize_v_fp8(p, v, vh, sv, S.workspace(p, S.OP_FORWARD_FP8))
+    torch.cuda.synchronize()
+    vh, sv = vh.cpu().numpy(), sv.cpu().numpy()
+    op = oracle_problem(orc, x, S.LOWBIT_QKV)
+    for bh in range(BH):
+        ovh, osv = orc.quant_v_fp8(op, x.v, bh)
+        assert np.array_equal(sv[bh], osv)
+        assert np.array_equal(vh[bh, :N], ovh), int((vh[bh, :N] != ovh).sum())
+        assert not vh[bh, N:].any()
+
+
+@pytest.mark.parametrize("lowbit", LOWBITS, ids=["qk", "qkv"])
+def test_fp8_wan14b_sampled(orc, dev, lowbit):
     w = I.WAN14B
     x = I.make_inputs(w)
-    p, idx, mask, O = run_gpu(x, dev, fp8=True, want_mask=False)
+    p, idx, mask, O = run_gpu(x, dev, fp8=True, want_mask=False, lowbit=lowbit)
     assert torch.isfinite(O).all()
     heads = [5, 31]
     op = orc.problem_of(x)
@@ -337,4 +372,5 @@ def test_fp8_wan14b_sampled(orc, dev):
     assert np.array_equal(gi[heads], oidx.reshape(w.B * w.H, w.Tq, -1)[heads])
     rng = np.random.default_rng(3)
     blocks = [(h, int(i)) for h in heads for i in {0, w.Tq - 1, *rng.choice(w.Tq, 4).tolist()}]
-    compare_blocks(orc, x, oidx, O, blocks, TOL["fp8"], variant="fp8")
+    compare_blocks(orc, x, oidx, O, blocks, TOL["fp8"], variant="fp8",
+                   op=oracle_problem(orc, x, lowbit))
