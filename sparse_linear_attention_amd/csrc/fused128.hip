@@ -36,6 +36,8 @@
 // group of 16 stored at positions with bits 2 and 3 swapped, which makes the
 // k order of P^T (taken straight from the S^T accumulators) line up with it;
 // phi(K)^T is stored the same way.
+#include <type_traits>
+
 #include "cdna4.h"
 #include "sla2_internal.h"
 
@@ -240,9 +242,9 @@ __global__ __launch_bounds__(256, 2) void fused128_kernel(
         for (int kq = 0; kq < 4; ++kq)
             pk[kq] = __builtin_bit_cast(
                 f16x8, __builtin_amdgcn_raw_buffer_load_b128(rpk, pkoff + 32 * kq, (uint32_t)j * 16384, 0));
-        const float z = __builtin_bit_cast(
+        // consumed one tile later: nothing here may wait for the load
+        zj = __builtin_bit_cast(
             float, __builtin_amdgcn_raw_buffer_load_b32(rz, zoff, (uint32_t)j * 512, 0));
-        zj = hl == 0 ? z : 0.0f;
     };
 
     // ---- prologue: K_0, V_0, K_1 [, phi(K_0)^T, z_0]
@@ -257,20 +259,27 @@ __global__ __launch_bounds__(256, 2) void fused128_kernel(
         asm volatile("" ::: "memory");
     }
 
+    // One tile step.  MORE1 / MORE2: tiles r+1 / r+2 exist.  The last two
+    // steps are peeled off the loop, so that inside it every load is
+    // unconditional and the compiler's own waits for the phi(K)^T registers
+    // count the tile loads issued after them exactly (with a conditional load
+    // it has to assume the path without it, and waits for the next tile too).
     int kslot = 0;
-    for (int r = 0; r < k; ++r) {
+    auto step = [&](int r, auto more1_c, auto more2_c) {
+        constexpr bool MORE1 = decltype(more1_c)::value;
+        constexpr bool MORE2 = decltype(more2_c)::value;
         // tile r's K and V^T have landed for this wave (loads issued after
         // V_r: at most one K tile and the phi(K_r)^T slice, may still be in
         // flight; the compiler waits for the latter before its use) ...
-        if (r + 1 < k) wait_vmcnt<P::nK + (LIN ? 5 : 0)>();
+        if (MORE1) wait_vmcnt<P::nK + (LIN ? 5 : 0)>();
         else if (LIN) wait_vmcnt<5>();
         else wait_vmcnt<0>();
         wg_barrier();  // ... and for every wave; all waves are done with tile r-1
-        if (r + 1 < k) {
+        if (MORE1) {
             if (kV16) issue_v(vbase + ((r + 1) & 1) * kVT, rv, sel[r + 1], w, toff);
             if (LOWV) issue_v8(v8base + ((r + 1) & 1) * kV8, rv8, sel[r + 1], w, v8off);
         }
-        if (r + DK < k) {
+        if (MORE2) {
             const int s2 = kslot + DK >= P::kStages ? kslot + DK - P::kStages : kslot + DK;
             issue_k<LOWBIT>(kbase + s2 * P::kStage, rk, sel[r + DK], N, w, lane, koff, toff, rp);
         }
@@ -441,14 +450,18 @@ __global__ __launch_bounds__(256, 2) void fused128_kernel(
             }
         }
         if (LIN) {
-            zacc += zj;
+            zacc += hl == 0 ? zj : 0.0f;  // one lane half holds the channel's z_j
             // the waits above count these loads as issued last in the
             // iteration: keep the compiler from moving them
             asm volatile("" ::: "memory");
-            if (r + 1 < k) load_pk(sel[r + 1]);
+            if (MORE1) load_pk(sel[r + 1]);
             asm volatile("" ::: "memory");
         }
-    }
+    };
+    int r = 0;
+    for (; r + 2 < k; ++r) step(r, std::true_type{}, std::true_type{});
+    if (r + 1 < k) step(r++, std::true_type{}, std::false_type{});
+    if (r < k) step(r, std::false_type{}, std::false_type{});
 
     // ---- epilogue
     const float l_all = l_part + __shfl_xor(l_part, 32);
