@@ -86,7 +86,7 @@ def linear_summary_flop(BH, N, d) -> float:
 
 # --------------------------------------------------------------------------
 COPY_BYTES = 1 << 30
-FUSED_KERNEL_RX = r"fused128_kernel<true, false>"
+FUSED_KERNEL_RX = r"fused128_kernel<true, false, false>"
 
 
 def copy_calibration():
