@@ -32,7 +32,7 @@ class Problem(C.Structure):
     _fields_ = [("B", C.c_int32), ("H", C.c_int32), ("N", C.c_int32), ("d", C.c_int32),
                 ("bq", C.c_int32), ("bkv", C.c_int32), ("topk_frac", C.c_float),
                 ("w_heads", C.c_int32), ("dtype", C.c_int32), ("alpha_mode", C.c_int32),
-                ("lowbit_v", C.c_int32)]
+                ("lowbit_v", C.c_int32), ("int8_qk", C.c_int32)]
 
 
 _lib = None
@@ -58,6 +58,8 @@ def lib():
         L.orc_e4m3_encode.restype = C.c_uint8
         L.orc_e4m3_decode.argtypes = [C.c_uint8]
         L.orc_e4m3_decode.restype = C.c_float
+        L.orc_i8_encode.argtypes = [C.c_float]
+        L.orc_i8_encode.restype = C.c_int8
         L.orc_bf16_encode.argtypes = [C.c_float]
         L.orc_bf16_encode.restype = C.c_uint16
         _lib = L
@@ -69,11 +71,12 @@ def _ptr(a):
 
 
 def problem(B, H, N, d, bq, bkv, frac, w_heads=1, dtype="f32", alpha_mode=0,
-            lowbit_v=0) -> Problem:
+            lowbit_v=0, int8_qk=0) -> Problem:
     """alpha_mode 0: alpha [H]; 1: alpha [H][T_q] (one per query block).
-    lowbit_v 1: the low-bit variant quantises V too (per channel)."""
+    lowbit_v 1: the low-bit variant quantises V too (per channel).
+    int8_qk 1: the low-bit variant takes int8 Q/K codes instead of e4m3."""
     return Problem(B, H, N, d, bq, bkv, float(frac), w_heads, 0 if dtype == "f32" else 1,
-                   alpha_mode, lowbit_v)
+                   alpha_mode, lowbit_v, int8_qk)
 
 
 def problem_of(x) -> Problem:
@@ -191,6 +194,10 @@ def quant_v_fp8(p: Problem, v, bh):
 
 def e4m3_encode(x: float) -> int:
     return int(lib().orc_e4m3_encode(float(x)))
+
+
+def i8_encode(x: float) -> int:
+    return int(lib().orc_i8_encode(float(x)))
 
 
 def e4m3_decode(c: int) -> float:

@@ -40,7 +40,11 @@
  *    values; tiles visited in ascending KV-block order; V stays bf16, or
  *    (lowbit_v) is quantised as well: s_V(c) = max over the N valid tokens
  *    of |V(.,c)| / 448 per head and channel (1 if 0), Vhat = e4m3(V / s_V),
- *    and P V uses Vhat s_V -- the pages quantise P and V for P V.
+ *    and P V uses Vhat s_V -- the pages quantise P and V for P V;
+ *  - the pages allow INT8 or FP8 for Q K^T: with int8_qk the Q and smoothed K
+ *    codes are int8, s = absmax / 127 per block (1 if 0), code =
+ *    round-half-even(x / s) clamped to +-127, and the dot products of the
+ *    codes are exact integers.
  */
 #include <math.h>
 #include <pthread.h>
@@ -57,6 +61,7 @@ typedef struct {
     int32_t dtype; /* 0: Q,K,V are float32; 1: Q,K,V are bf16 bit patterns */
     int32_t alpha_mode; /* 0: alpha [H]; 1: alpha [H][T_q], one per query block */
     int32_t lowbit_v;   /* low-bit variant: 1 = V also quantised (per channel) */
+    int32_t int8_qk;    /* low-bit variant: 1 = Q, K as int8 codes (else e4m3) */
 } orc_problem;
 
 /* ------------------------------------------------------------------ */
@@ -134,6 +139,18 @@ uint8_t orc_e4m3_encode(float x) {
     }
     int m = (int)llround((vf * 2.0 - 1.0) * 8.0);
     return sign | (uint8_t)((E << 3) | m);
+}
+
+/* Round-half-to-even onto the integers, saturating at +-127: the int8 codes
+ * of the int8 Q K^T variant, decided on the exact fp32 quotient. */
+int8_t orc_i8_encode(float x) {
+    double a = (double)x;
+    double r = floor(a);
+    double frac = a - r;
+    if (frac > 0.5 || (frac == 0.5 && ((long long)r & 1) != 0)) r += 1.0;
+    if (r > 127.0) r = 127.0;
+    if (r < -127.0) r = -127.0;
+    return (int8_t)r;
 }
 
 /* fp32 -> bf16 bits, round to nearest even (finite inputs) */
@@ -355,7 +372,7 @@ static void summary_block(void* vctx, long j) {
 /* low-bit inputs of one head (fp32 decisions, as the kernel takes them) */
 /* ------------------------------------------------------------------ */
 typedef struct {
-    uint8_t* qh; /* [N][d] e4m3 codes */
+    uint8_t* qh; /* [N][d] e4m3 codes (int8 codes with int8_qk) */
     uint8_t* kh; /* [N][d] */
     float* sq;   /* [Tq] */
     float* sk;   /* [Tkv] */
@@ -372,6 +389,7 @@ static void quant_head(const orc_problem* p, const void* Q, const void* K, long 
                        quant_t* o) {
     int d = p->d, N = p->N;
     int Tq = ceil_div(N, p->bq), Tkv = ceil_div(N, p->bkv);
+    const float qmax = p->int8_qk ? 127.0f : 448.0f; /* largest code magnitude */
     /* K channel mean over the N valid tokens (column-mean smoothing,
        [SLA2-zh] 07): summed in fp64, rounded once to fp32 */
     for (int c = 0; c < d; ++c) {
@@ -387,12 +405,13 @@ static void quant_head(const orc_problem* p, const void* Q, const void* K, long 
                 float ks = elemf(p, K, bh, t, c) - o->mu[c];
                 if (fabsf(ks) > amax) amax = fabsf(ks);
             }
-        float s = amax > 0.0f ? amax / 448.0f : 1.0f;
+        float s = amax > 0.0f ? amax / qmax : 1.0f;
         o->sk[j] = s;
         for (int t = t0; t < t0 + n; ++t)
             for (int c = 0; c < d; ++c) {
                 float ks = elemf(p, K, bh, t, c) - o->mu[c];
-                o->kh[(size_t)t * d + c] = orc_e4m3_encode(ks / s);
+                o->kh[(size_t)t * d + c] = p->int8_qk ? (uint8_t)orc_i8_encode(ks / s)
+                                                      : orc_e4m3_encode(ks / s);
             }
     }
     for (int i = 0; i < Tq; ++i) {
@@ -403,11 +422,14 @@ static void quant_head(const orc_problem* p, const void* Q, const void* K, long 
                 float x = elemf(p, Q, bh, t, c);
                 if (fabsf(x) > amax) amax = fabsf(x);
             }
-        float s = amax > 0.0f ? amax / 448.0f : 1.0f;
+        float s = amax > 0.0f ? amax / qmax : 1.0f;
         o->sq[i] = s;
         for (int t = t0; t < t0 + n; ++t)
-            for (int c = 0; c < d; ++c)
-                o->qh[(size_t)t * d + c] = orc_e4m3_encode(elemf(p, Q, bh, t, c) / s);
+            for (int c = 0; c < d; ++c) {
+                float x = elemf(p, Q, bh, t, c) / s;
+                o->qh[(size_t)t * d + c] = p->int8_qk ? (uint8_t)orc_i8_encode(x)
+                                                      : orc_e4m3_encode(x);
+            }
     }
 }
 
@@ -571,7 +593,10 @@ static void sparse_lowbit(const fwd_ctx* F, int i, const int32_t* sel, int k, in
             double s = 0.0, sa = 0.0;
             for (int c = 0; c < d; ++c) {
                 double a, b;
-                if (F->quantize) {
+                if (F->quantize && p->int8_qk) {
+                    a = (double)(int8_t)Qt->qh[(size_t)t * d + c];
+                    b = (double)(int8_t)Qt->kh[(size_t)u * d + c];
+                } else if (F->quantize) {
                     a = orc_e4m3_decode(Qt->qh[(size_t)t * d + c]);
                     b = orc_e4m3_decode(Qt->kh[(size_t)u * d + c]);
                 } else { /* identity quantiser: x / s exactly */

@@ -43,6 +43,12 @@ MUTANTS = {
     "v_scale_wrong_channel": ("(double)F->qt->sv[e]", "(double)F->qt->sv[0]"),
     "v_codes_unused": ("if (p->lowbit_v && F->quantize)", "if (p->lowbit_v && !F->quantize)"),
     "v_scale_not_max": ("            if (v > amax) amax = v;", "            amax = v;"),
+    "i8_scale_uses_e4m3_max": ("p->int8_qk ? 127.0f : 448.0f", "p->int8_qk ? 448.0f : 448.0f"),
+    "i8_ties_away_from_zero": ("(frac == 0.5 && ((long long)r & 1) != 0)", "(frac == 0.5 && r >= 0.0)"),
+    "i8_no_clamp": ("    if (r > 127.0) r = 127.0;\n", ""),
+    "i8_codes_unsigned": ("a = (double)(int8_t)Qt->qh[(size_t)t * d + c];", "a = (double)Qt->qh[(size_t)t * d + c];"),
+    "i8_k_not_smoothed": ("o->kh[(size_t)t * d + c] = p->int8_qk ? (uint8_t)orc_i8_encode(ks / s)",
+                          "o->kh[(size_t)t * d + c] = p->int8_qk ? (uint8_t)orc_i8_encode((ks + o->mu[c]) / s)"),
     "numerator_transposed_H": ("num += pq[c] * Hi[(size_t)c * d + e];", "num += pq[c] * Hi[(size_t)e * d + c];"),
 }
 
@@ -68,6 +74,10 @@ PINS = [
     (pins.test_lowbit_v_identity_quantiser_equals_exact, ()),
     (pins.test_lowbit_v_single_tile_closed_form, ()),
     (pins.test_lowbit_v_constant_v, ()),
+    (pins.test_i8_encode_vs_torch_round, ()),
+    (pins.test_lowbit_i8_quantised_inputs, ()),
+    (pins.test_lowbit_i8_identity_quantiser_equals_exact, ()),
+    (pins.test_lowbit_i8_single_tile_closed_form, (0,)),
 ]
 
 

@@ -629,6 +629,108 @@ def test_lowbit_v_constant_v(orc):
 
 
 # --------------------------------------------------------------------------
+# int8 Q K^T variant: int8 codes for Q and smoothed K
+# --------------------------------------------------------------------------
+def _i8_problem(orc, x, lowbit_v=0):
+    w = x.wl
+    return orc.problem(w.B, w.H, w.N, w.d, w.bq, w.bkv, w.topk_frac, 1, w.dtype,
+                       lowbit_v=lowbit_v, int8_qk=1)
+
+
+def test_i8_encode_vs_torch_round(orc):
+    """Codes are torch.round (half to even) of the fp32 input, clamped to
+    +-127: ties, near-ties, saturation and signed zero."""
+    rng = np.random.default_rng(5)
+    ties = np.arange(-130, 131, dtype=np.float32) + np.float32(0.5)
+    near = np.concatenate([np.nextafter(ties, np.float32(np.inf)),
+                           np.nextafter(ties, np.float32(-np.inf))])
+    vals = np.concatenate([ties, near, rng.normal(0, 60, 4000).astype(np.float32),
+                           np.float32([0.0, -0.0, 126.5, 127.49998, 127.5, 1e9, -1e9])])
+    ref = torch.clamp(torch.round(torch.from_numpy(vals)), -127, 127).numpy().astype(np.int64)
+    mine = np.array([orc.i8_encode(v) for v in vals], np.int64)
+    assert np.array_equal(mine, ref)
+
+
+def test_lowbit_i8_quantised_inputs(orc):
+    """Per-block s = absmax / 127 (fp32), codes round(x / s) in fp32: every
+    block reaches +-127 and reconstructs within s / 2."""
+    x = small(dtype="bf16", N=700, d=64, frac=0.3)
+    p = _i8_problem(orc, x)
+    N = x.wl.N
+    qh, kh, sq, sk, mu = orc.quant_fp8(p, x.q, x.k, 1)
+    qi, ki = qh.view(np.int8).astype(np.int64), kh.view(np.int8).astype(np.int64)
+    q = I.bf16_bits_to_f32(x.q[0, 1])
+    k = I.bf16_bits_to_f32(x.k[0, 1])
+    for i in range(x.wl.Tq):
+        r = slice(i * 128, min(N, (i + 1) * 128))
+        s = np.float32(np.abs(q[r]).max() / np.float32(127.0))
+        assert sq[i] == s
+        ref = torch.round(torch.from_numpy(q[r] / s)).numpy().astype(np.int64)
+        assert np.array_equal(qi[r], ref) and np.abs(qi[r]).max() == 127
+        assert (np.abs(qi[r] * float(s) - q[r]) <= float(s) * 0.5 * (1 + 1e-6)).all()
+    for j in range(x.wl.Tkv):
+        r = slice(j * 64, min(N, (j + 1) * 64))
+        ks = (k[r] - mu[None, :]).astype(np.float32)
+        s = np.float32(np.abs(ks).max() / np.float32(127.0))
+        assert sk[j] == s
+        ref = torch.round(torch.from_numpy(ks / s)).numpy().astype(np.int64)
+        assert np.array_equal(ki[r], ref) and np.abs(ki[r]).max() == 127
+
+
+def test_lowbit_i8_identity_quantiser_equals_exact(orc):
+    x = small(dtype="bf16", N=700, d=64, frac=0.3)
+    p = _i8_problem(orc, x)
+    idx, _, _, _ = orc.route(p, x.q, x.k, x.wq, x.wk)
+    o = orc.forward_full(p, x.q, x.k, x.v, idx, x.alpha)
+    o8 = orc.forward_full(p, x.q, x.k, x.v, idx, x.alpha, variant="fp8", quantize=False)
+    assert np.abs(o - o8).max() < 1e-12
+
+
+@pytest.mark.parametrize("lowbit_v", [0, 1])
+def test_lowbit_i8_single_tile_closed_form(orc, lowbit_v):
+    """One selected tile, alpha = 1: logits are exact integer dot products of
+    the int8 codes times s_Q s_K / sqrt d; P^ from torch's float8 cast; V
+    bf16 or per-channel e4m3 codes times s_V."""
+    wl = I.Workload("t", 1, 1, 300, 32, 64, 64, 0.2, "bf16", "smooth", seed=2, alpha=(1.0,))
+    x = I.make_inputs(wl)
+    p = _i8_problem(orc, x, lowbit_v)
+    idx, _, _, _ = orc.route(p, x.q, x.k, x.wq, x.wk)
+    assert idx.shape[-1] == 1
+    out = orc.forward(p, x.q, x.k, x.v, idx, x.alpha, orc.all_blocks(p), variant="fp8")
+    qh, kh, sq, sk, _ = orc.quant_fp8(p, x.q, x.k, 0)
+    qi, ki = qh.view(np.int8).astype(np.int64), kh.view(np.int8).astype(np.int64)
+    v = I.bf16_bits_to_f32(x.v[0, 0])
+    if lowbit_v:
+        sv = (np.abs(v).max(0) / np.float32(448.0)).astype(np.float32)
+        r = np.clip(v / sv[None, :], -448.0, 448.0).astype(np.float32)
+        V = torch.from_numpy(r).to(torch.float8_e4m3fn).double().numpy() * sv.astype(np.float64)
+    else:
+        V = v.astype(np.float64)
+    for t in range(wl.N):
+        i = t // 64
+        j = int(idx[0, 0, i, 0])
+        u = np.arange(j * 64, min(wl.N, j * 64 + 64))
+        lg = (ki[u] @ qi[t]).astype(np.float64) * float(sq[i]) * float(sk[j]) / math.sqrt(32)
+        f = torch.from_numpy((256.0 * np.exp(lg - lg.max())).astype(np.float32))
+        ph = f.to(torch.float8_e4m3fn).double().numpy() / 256.0
+        assert np.abs(out[i, t % 64] - ph @ V[u] / ph.sum()).max() < 1e-12
+
+
+def test_lowbit_i8_error_is_small(orc):
+    """Reported, not a parity gate: int8 Q K^T keeps the output near the exact
+    one, closer than e4m3 (7 significant bits against 4)."""
+    x = small(dtype="bf16", N=1024, d=128, frac=0.25)
+    p = _i8_problem(orc, x)
+    pe = orc.problem_of(x)
+    idx, _, _, _ = orc.route(p, x.q, x.k, x.wq, x.wk)
+    o = orc.forward_full(p, x.q, x.k, x.v, idx, x.alpha)
+    oi = orc.forward_full(p, x.q, x.k, x.v, idx, x.alpha, variant="fp8")
+    oe = orc.forward_full(pe, x.q, x.k, x.v, idx, x.alpha, variant="fp8")
+    ei, ee = np.abs(o - oi).max(), np.abs(o - oe).max()
+    assert ei < 0.1 and ei < ee
+
+
+# --------------------------------------------------------------------------
 # workload generator sanity (shapes and statistics stated for the workloads)
 # --------------------------------------------------------------------------
 def test_tiny_workload_statistics():
