@@ -12,8 +12,8 @@ FlashAttention2's dense work).  Prints ONE JSON line.
 
 Options: --steps K --warmup W; --gpus N (only 1: the path runs on one GPU);
 --no-cpu-baseline skips the oracle timing; --workload wan13b for the smaller
-shape; --no-fp8 skips the extra timing of sla2_forward_fp8 (the low-bit
-sparse branch on the same inputs); --copy-calibration runs only a plain 1 GiB
+shape; --no-fp8 skips the extra timings of sla2_forward_fp8 (the low-bit
+sparse branch on the same inputs: e4m3 or int8 Q/K, V bf16 or e4m3); --copy-calibration runs only a plain 1 GiB
 device copy (used to scale rocprofv3 FETCH_SIZE / WRITE_SIZE);
 --counters-summary FETCH WRITE COPY_FETCH COPY_WRITE turns four rocprofv3
 --pmc output folders (the bench, then the copy) into the per-launch HBM
@@ -318,8 +318,10 @@ def main():
 
     if not args.no_fp8:
         # the low-bit sparse branch on the same inputs: Q, K and P in e4m3
-        # ("fp8"), and with V quantised per channel as well ("fp8_v")
-        for key, lb in (("fp8", S.LOWBIT_QK), ("fp8_v", S.LOWBIT_QKV)):
+        # ("fp8"), with V quantised per channel as well ("fp8_v"), and the
+        # same two with int8 Q/K codes ("i8", "i8_v")
+        for key, lb in (("fp8", S.LOWBIT_QK), ("fp8_v", S.LOWBIT_QKV),
+                        ("i8", S.LOWBIT_I8QK), ("i8_v", S.LOWBIT_I8QKV)):
             p8 = S.problem(w.B, w.H, w.N, w.d, w.bq, w.bkv, w.topk_frac, 1, w.dtype, lowbit=lb)
             ws8 = S.workspace(p8, S.OP_FORWARD_FP8)
 
@@ -339,10 +341,10 @@ def main():
             k8 = S.timing_stop()
             ms8 = ev0.elapsed_time(ev1) / args.steps
             st8 = {n_: ms_ / c_ for n_, (ms_, c_) in k8.items()}
-            f8_ms = st8.get("fused_fp8")
+            f8_ms = st8.get("fused_i8" if lb & S.LOWBIT_I8QK else "fused_fp8")
             out[key] = {"ms_per_step": ms8, "tops": dense / (ms8 * 1e-3) / 1e12,
                         "stages_ms": st8,
-                        "fused_fp8_tflops": (fl_sparse + fl_apply) / (f8_ms * 1e-3) / 1e12
+                        "fused_lowbit_tflops": (fl_sparse + fl_apply) / (f8_ms * 1e-3) / 1e12
                         if f8_ms else None}
             del ws8
 

@@ -79,8 +79,14 @@ typedef enum { SLA2_LAYOUT_BHND = 0, SLA2_LAYOUT_BNHD = 1 } sla2_layout;
 typedef enum { SLA2_ALPHA_PER_HEAD = 0, SLA2_ALPHA_PER_QBLOCK = 1 } sla2_alpha_mode;
 
 /* what sla2_forward_fp8 quantises ("SLA2 深度解读" 07: low-bit Q K^T and
- * P V): Q, K and P (V stays bf16), or V as well, per channel */
-typedef enum { SLA2_LOWBIT_QK = 0, SLA2_LOWBIT_QKV = 1 } sla2_lowbit;
+ * P V, INT8 or FP8 for Q K^T): a bit mask.  Q, K and P always; bit 0: V as
+ * well, per channel; bit 1: Q and K as int8 codes instead of e4m3 */
+typedef enum {
+    SLA2_LOWBIT_QK = 0,    /* e4m3 Q, K; V bf16           */
+    SLA2_LOWBIT_QKV = 1,   /* e4m3 Q, K; e4m3 V           */
+    SLA2_LOWBIT_I8QK = 2,  /* int8 Q, K; V bf16           */
+    SLA2_LOWBIT_I8QKV = 3  /* int8 Q, K; e4m3 V           */
+} sla2_lowbit;
 
 /* operations, for sla2_workspace_bytes */
 typedef enum { SLA2_OP_ROUTE = 0, SLA2_OP_FORWARD = 1, SLA2_OP_FORWARD_FP8 = 2 } sla2_op;
@@ -175,7 +181,12 @@ sla2_status sla2_forward(const sla2_problem* p, const void* Q, const void* K,
  *   P~ = exp(logit - running max) quantised as e4m3(256 P~) / 256 before
  *   P V (V unquantised, fp16) and the row sum taken over the quantised
  *   values.  Router and linear branch are those of sla2_forward.
- *   With lowbit == SLA2_LOWBIT_QKV, V is quantised too: s_V(c) = max over the
+ *   With bit 1 of lowbit set (SLA2_LOWBIT_I8QK, SLA2_LOWBIT_I8QKV) Q and K'
+ *   take int8 codes instead: s = block max / 127, code = round-half-even(x /
+ *   s) clamped to +-127 (fp32 division), and the logits are the exact int32
+ *   dot products of the codes (int8 matrix cores) times s_Q s_K / sqrt(d).
+ *   With bit 0 of lowbit set (SLA2_LOWBIT_QKV, SLA2_LOWBIT_I8QKV), V is
+ *   quantised too: s_V(c) = max over the
  *   N valid tokens of |V(., c)| / 448 per head and channel (1 if 0), Vhat =
  *   e4m3(V / s_V) (fp32 division, round to nearest even, saturating), and
  *   P V runs on the e4m3 matrix cores as (256 P^) Vhat, scaled by s_V(c) per
@@ -194,7 +205,8 @@ sla2_status sla2_forward_fp8(const sla2_problem* p, const void* Q, const void* K
 /*
  * sla2_quantize_fp8 -- the low-bit inputs alone (the quantisation step that
  * sla2_forward_fp8 runs first), for inspection.  Requires dtype == SLA2_BF16.
- * Out (device): Qhat [B,H,T_q*bq,d] and Khat [B,H,T_kv*bkv,d] e4m3 codes
+ * Out (device): Qhat [B,H,T_q*bq,d] and Khat [B,H,T_kv*bkv,d] e4m3 codes, or
+ * int8 codes (two's complement) with bit 1 of lowbit set
  * (always head-major, whatever the layout of Q and K)
  * (rows past N are 0), s_Q [B,H,T_q], s_K [B,H,T_kv], mu [B,H,d] fp32.
  * ws : sla2_workspace_bytes(p, SLA2_OP_FORWARD_FP8) bytes.
@@ -207,7 +219,7 @@ sla2_status sla2_quantize_fp8(const sla2_problem* p, const void* Q, const void* 
  * sla2_quantize_v_fp8 -- the per-channel V quantisation of the fully low-bit
  * sparse branch alone (what sla2_forward_fp8 runs with lowbit ==
  * SLA2_LOWBIT_QKV), for inspection.  Requires dtype == SLA2_BF16, d == 128
- * and lowbit == SLA2_LOWBIT_QKV.
+ * and bit 0 of lowbit (SLA2_LOWBIT_QKV or SLA2_LOWBIT_I8QKV).
  * Out (device): Vhat [B,H,T_kv*bkv,d] e4m3 codes (head-major, rows past N are
  * 0), s_V [B,H,d] fp32.
  * ws : sla2_workspace_bytes(p, SLA2_OP_FORWARD_FP8) bytes.

@@ -4,7 +4,8 @@
 // lane l holds row l%32 and k = 8*(l/32)+[0..7]; B (16 x 32) lane l holds
 // column l%32 and the same k; C (32 x 32) lane l holds column l%32 and rows
 // 8*(r/4) + 4*(l/32) + r%4, r = 0..15.  The scaled e4m3 form (32x32x64) takes
-// 32 consecutive k per lane: k = 32*(l/32)+[0..31].
+// 32 consecutive k per lane: k = 32*(l/32)+[0..31]; the int8 form
+// (v_mfma_i32_32x32x32_i8) 16: k = 16*(l/32)+[0..15], with exact int32 sums.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -18,6 +19,8 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x16 __attribute__((ext_vector_type(16)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
 __device__ inline f32x16 mfma_bf16(bf16x8 a, bf16x8 b, f32x16 c) {
@@ -29,6 +32,11 @@ __device__ inline f32x16 mfma_f16(f16x8 a, f16x8 b, f32x16 c) {
 // e4m3 x e4m3 -> fp32 (32x32x64); E8M0 scale 127 = 1.0
 __device__ inline f32x16 mfma_fp8(i32x8 a, i32x8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+}
+
+// int8 x int8 -> int32 (32x32x32), exact
+__device__ inline i32x16 mfma_i8(i32x4 a, i32x4 b, i32x16 c) {
+    return __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, c, 0, 0, 0);
 }
 
 __device__ inline f32x16 zero16() {

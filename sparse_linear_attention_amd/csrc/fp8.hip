@@ -8,6 +8,8 @@
 //             block i / 448 (1 when the maximum is 0);
 //   Khat    = e4m3(K' / s_K), Qhat = e4m3(Q / s_Q): OCP e4m3, round to
 //             nearest even, saturated at +-448.
+// With int8 Q/K codes (the pages allow INT8 or FP8 for Q K^T) the scales are
+// max / 127 and the codes round-half-even(x / s) clamped to +-127.
 // Rows past N are written as code 0.  d = 128.
 // Fully low-bit variant (P V on the e4m3 matrix cores as well): s_V(c) =
 // max over the N valid tokens of |V(., c)| / 448 per head and channel (1 if
@@ -70,9 +72,23 @@ __device__ inline unsigned e4m3_pair(float a, float b) {
     return (unsigned)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false) & 0xffffu;
 }
 
+// two int8 codes: nearest integer, ties to even (v_rndne), clamped to +-127
+__device__ inline unsigned i8_pair(float a, float b) {
+    const int ia = (int)fminf(fmaxf(__builtin_rintf(a), -127.0f), 127.0f);
+    const int ib = (int)fminf(fmaxf(__builtin_rintf(b), -127.0f), 127.0f);
+    return ((unsigned)ia & 0xffu) | (((unsigned)ib & 0xffu) << 8);
+}
+
+template <bool I8>
+__device__ inline unsigned code_pair(float a, float b) {
+    if constexpr (I8) return i8_pair(a, b);
+    else return e4m3_pair(a, b);
+}
+
 // One work-group per (head, block): blocks [0, Tq) are query blocks of 128
 // tokens, the rest KV blocks of 64.  Each thread handles rows r, r+R, ... of
-// one 8-channel group.
+// one 8-channel group.  I8: int8 codes (else e4m3).
+template <bool I8>
 __global__ __launch_bounds__(256) void quant_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const float* __restrict__ mu, uint8_t* __restrict__ qhat, uint8_t* __restrict__ khat,
@@ -108,7 +124,7 @@ __global__ __launch_bounds__(256) void quant_kernel(
     if (threadIdx.x == 0) {
         float a = 0.0f;
         for (int i = 0; i < 256; ++i) a = fmaxf(a, red[i]);
-        const float s = a > 0.0f ? a / 448.0f : 1.0f;
+        const float s = a > 0.0f ? a / (I8 ? 127.0f : 448.0f) : 1.0f;
         s_scale = s;
         if (isq) sq[bh * Tq + j] = s;
         else sk[bh * Tkv + j] = s;
@@ -127,8 +143,8 @@ __global__ __launch_bounds__(256) void quant_kernel(
             unsigned pk[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e)
-                pk[e] = e4m3_pair((bf16_lo(w[e]) - m8[2 * e]) / s,
-                                  (bf16_hi(w[e]) - m8[2 * e + 1]) / s);
+                pk[e] = code_pair<I8>((bf16_lo(w[e]) - m8[2 * e]) / s,
+                                      (bf16_hi(w[e]) - m8[2 * e + 1]) / s);
             codes.x = pk[0] | (pk[1] << 16);
             codes.y = pk[2] | (pk[3] << 16);
         }
@@ -262,11 +278,13 @@ hipError_t launch_quantize_fp8(const Dims& D, const void* Q, const void* K, cons
                                                           D.H, D.st);
     kmean_kernel<<<dim3((unsigned)D.BH), 128, 0, s>>>(ws.ksum, ws.mu, D.N, nch);
     timing_after(s, K_QUANT_MEAN);
-    timing_before(s, K_QUANT);
-    quant_kernel<<<dim3(D.Tq + D.Tkv, (unsigned)D.BH), 256, 0, s>>>(
+    const KernelKind kq = D.int8_qk ? K_QUANT_I8 : K_QUANT;
+    timing_before(s, kq);
+    (D.int8_qk ? quant_kernel<true> : quant_kernel<false>)<<<dim3(D.Tq + D.Tkv, (unsigned)D.BH),
+                                                             256, 0, s>>>(
         (const uint16_t*)Q, (const uint16_t*)K, ws.mu, ws.qhat, ws.khat, ws.sq, ws.sk, D.N, D.Tq,
         D.Tkv, D.H, D.st);
-    timing_after(s, K_QUANT);
+    timing_after(s, kq);
     if (D.lowbit_v && V) {
         timing_before(s, K_QUANT_V);
         hipError_t e = launch_vscale(D, V, ws, s);

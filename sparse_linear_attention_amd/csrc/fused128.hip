@@ -1,5 +1,6 @@
 // Fused sparse + linear + combine kernel for d = 128, b_q = 128, b_kv = 64
-// (bf16 inputs; with LOWBIT the Q K^T products run on the e4m3 matrix cores).
+// (bf16 inputs; in the low-bit forms the Q K^T products run on the e4m3 or
+// the int8 matrix cores).
 //
 // One work-group of 4 waves per (head, query block); wave w owns queries
 // 32w .. 32w+31 of the block and all 64 keys of every selected KV tile, so
@@ -10,8 +11,8 @@
 //
 // Per selected KV block j, in ascending order ("SLA2 深度解读" 04, 07, 08:
 // only mask-hit blocks run Q K^T and P V, online softmax over them):
-//   S^T = K_j Q^T                       bf16 MFMA (LOWBIT: Khat Qhat^T, e4m3,
-//                                       times s_Q s_K)
+//   S^T = K_j Q^T                       bf16 MFMA (low bit: Khat Qhat^T on
+//                                       e4m3 or int8 codes, times s_Q s_K)
 //   online softmax on S^T               one query per lane column
 //   O^T += V_j^T P^T                    fp16 MFMA (LOWBIT: P on the e4m3 grid)
 //   G^T += V_j^T phi(K_j)               fp16 MFMA; phi(K_j)^T comes from the
@@ -142,7 +143,8 @@ __device__ inline void issue_v8(char* v8st, rsrc_t rv8, int j, int w, uint32_t v
     }
 }
 
-template <bool LIN, bool LOWBIT, bool LOWV>
+// QK: 0 = bf16 Q K^T, 1 = e4m3 codes, 2 = int8 codes
+template <bool LIN, int QK, bool LOWV>
 __global__ __launch_bounds__(256, 2) void fused128_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ vt, const uint16_t* __restrict__ pkt,
@@ -153,6 +155,7 @@ __global__ __launch_bounds__(256, 2) void fused128_kernel(
     const float* __restrict__ sk, const uint8_t* __restrict__ vhat,
     const float* __restrict__ sv, void* __restrict__ O, int N, int Tq, int Tkv, int k,
     int H, Strides st, int alpha_qblock, int out_bf16) {
+    constexpr bool LOWBIT = QK != 0;
     static_assert(LOWBIT || !LOWV, "quantised V only with the low-bit Q K^T");
     // V^T in fp16 feeds P V, and G (the linear branch) with LOWV
     constexpr bool kV16 = !LOWV || LIN;
@@ -339,7 +342,35 @@ __global__ __launch_bounds__(256, 2) void fused128_kernel(
         // running maximum is updated once per tile (with LOWBIT the
         // quantisation grid of P follows it)
         f32x16 s[2] = {zero16(), zero16()};
-        if (LOWBIT) {
+        if (QK == 2) {
+            // int8 codes: the 32 bytes of a lane's 64-channel step go to two
+            // int8 MFMAs (16 each; A and B split alike, so each sums a
+            // matching half of the channels); the int32 sums are exact and
+            // converted once per tile
+            i32x16 si[2];
+#pragma unroll
+            for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) si[mt][i] = 0;
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+                for (int mt = 0; mt < 2; ++mt) {
+                    const int kr = 32 * mt + l32, sw = (kr >> 1) & 7, c0 = 4 * ks + 2 * hl;
+                    const uint4 lo = *reinterpret_cast<const uint4*>(kst + kr * 128 + ((c0 ^ sw) << 4));
+                    const uint4 hi =
+                        *reinterpret_cast<const uint4*>(kst + kr * 128 + (((c0 + 1) ^ sw) << 4));
+                    const i32x8 q8 = reinterpret_cast<const i32x8*>(Qo.f)[ks];
+                    const i32x4 qlo = {q8[0], q8[1], q8[2], q8[3]};
+                    const i32x4 qhi = {q8[4], q8[5], q8[6], q8[7]};
+                    si[mt] = mfma_i8(i32x4{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w}, qlo, si[mt]);
+                    si[mt] = mfma_i8(i32x4{(int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w}, qhi, si[mt]);
+                }
+#pragma unroll
+            for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) s[mt][i] = (float)si[mt][i];
+        } else if (LOWBIT) {
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
@@ -571,14 +602,18 @@ hipError_t launch_fused128(const Dims& D, const void* Q, const void* K, const in
     const float* sq = lowbit ? ws.sq : nullptr;
     const float* sk = lowbit ? ws.sk : nullptr;
     const bool lowv = lowbit && D.lowbit_v;
-    auto kern = !lowbit ? (lin ? fused128_kernel<true, false, false> : fused128_kernel<false, false, false>)
-                : !lowv ? (lin ? fused128_kernel<true, true, false> : fused128_kernel<false, true, false>)
-                        : (lin ? fused128_kernel<true, true, true> : fused128_kernel<false, true, true>);
-    timing_before(s, lowbit ? K_FUSED_FP8 : K_FUSED_MFMA);
+    const bool i8 = lowbit && D.int8_qk;
+    auto kern = !lowbit ? (lin ? fused128_kernel<true, 0, false> : fused128_kernel<false, 0, false>)
+                : i8 ? (!lowv ? (lin ? fused128_kernel<true, 2, false> : fused128_kernel<false, 2, false>)
+                              : (lin ? fused128_kernel<true, 2, true> : fused128_kernel<false, 2, true>))
+                : !lowv ? (lin ? fused128_kernel<true, 1, false> : fused128_kernel<false, 1, false>)
+                        : (lin ? fused128_kernel<true, 1, true> : fused128_kernel<false, 1, true>);
+    const KernelKind kind = !lowbit ? K_FUSED_MFMA : i8 ? K_FUSED_I8 : K_FUSED_FP8;
+    timing_before(s, kind);
     kern<<<g, 256, 0, s>>>(q, kk, ws.vt, ws.pkt, ws.zb, idx, alpha, ws.htot, ws.ztot, qh, kh, sq,
                            sk, lowv ? ws.vhat : nullptr, lowv ? ws.sv : nullptr, O, D.N, D.Tq,
                            D.Tkv, D.k, D.H, D.st, D.alpha_qblock, D.out_bf16);
-    timing_after(s, lowbit ? K_FUSED_FP8 : K_FUSED_MFMA);
+    timing_after(s, kind);
     return hipGetLastError();
 }
 

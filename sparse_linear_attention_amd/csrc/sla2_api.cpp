@@ -36,7 +36,7 @@ static sla2_status make_dims(const sla2_problem* p, int op, Dims* D) {
     if (p->alpha_mode != SLA2_ALPHA_PER_HEAD && p->alpha_mode != SLA2_ALPHA_PER_QBLOCK)
         return SLA2_EINVAL;
     if (p->out_dtype != SLA2_F32 && p->out_dtype != SLA2_BF16) return SLA2_EINVAL;
-    if (p->lowbit != SLA2_LOWBIT_QK && p->lowbit != SLA2_LOWBIT_QKV) return SLA2_EINVAL;
+    if (p->lowbit < SLA2_LOWBIT_QK || p->lowbit > SLA2_LOWBIT_I8QKV) return SLA2_EINVAL;
     if (op < SLA2_OP_ROUTE || op > SLA2_OP_FORWARD_FP8) return SLA2_EINVAL;
     if (p->d != 64 && p->d != 128) return SLA2_EUNSUPPORTED;
     if (p->bq != 64 && p->bq != 128) return SLA2_EUNSUPPORTED;
@@ -71,7 +71,8 @@ static sla2_status make_dims(const sla2_problem* p, int op, Dims* D) {
     }
     D->alpha_qblock = p->alpha_mode == SLA2_ALPHA_PER_QBLOCK;
     D->out_bf16 = p->out_dtype == SLA2_BF16;
-    D->lowbit_v = p->lowbit == SLA2_LOWBIT_QKV;
+    D->lowbit_v = (p->lowbit & SLA2_LOWBIT_QKV) != 0;
+    D->int8_qk = (p->lowbit & SLA2_LOWBIT_I8QK) != 0;
     // the fused kernels address a head's rows with 32-bit byte offsets
     if ((double)p->N * D->st.t * 4.0 >= 2147483648.0) return SLA2_EUNSUPPORTED;
     return SLA2_OK;
@@ -154,6 +155,7 @@ const char* kKindNames[K_NUM_KINDS] = {
     "pool_project", "score",       "topk_select", "summaries_valu",
     "summaries_reduce", "fused_valu", "summaries_mfma", "fused_mfma",
     "quant_mean",   "quant_fp8",   "fused_fp8",  "quant_v_fp8",
+    "quant_i8",     "fused_i8",
 };
 }  // namespace
 

@@ -25,6 +25,8 @@ enum KernelKind {
     K_QUANT,
     K_FUSED_FP8,
     K_QUANT_V,
+    K_QUANT_I8,
+    K_FUSED_I8,
     K_NUM_KINDS
 };
 
@@ -49,6 +51,7 @@ struct Dims {
     int alpha_qblock;    // alpha is [H][Tq] (else [H])
     int out_bf16;        // O is bf16 (else fp32)
     int lowbit_v;        // the low-bit forward quantises V too
+    int int8_qk;         // the low-bit forward takes int8 Q/K codes (else e4m3)
 };
 
 // Four consecutive outputs (element offset off, a multiple of 4) as fp32, or

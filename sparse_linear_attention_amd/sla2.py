@@ -19,7 +19,7 @@ PHI_ELU1 = 0
 OP_ROUTE, OP_FORWARD, OP_FORWARD_FP8 = 0, 1, 2
 LAYOUT_BHND, LAYOUT_BNHD = 0, 1
 ALPHA_PER_HEAD, ALPHA_PER_QBLOCK = 0, 1
-LOWBIT_QK, LOWBIT_QKV = 0, 1
+LOWBIT_QK, LOWBIT_QKV, LOWBIT_I8QK, LOWBIT_I8QKV = 0, 1, 2, 3
 
 
 class Problem(C.Structure):

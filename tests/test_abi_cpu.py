@@ -64,7 +64,8 @@ def test_topk_matches_oracle_table(orc):
     (dict(dtype=7), S.EINVAL), (dict(d=96), S.EUNSUPPORTED), (dict(bq=32), S.EUNSUPPORTED),
     (dict(bkv=128), S.EUNSUPPORTED), (dict(N=7681 * 64), S.EUNSUPPORTED),
     (dict(layout=2), S.EINVAL), (dict(alpha_mode=-1), S.EINVAL), (dict(out_dtype=5), S.EINVAL),
-    (dict(lowbit=2), S.EINVAL),
+    (dict(lowbit=4), S.EINVAL),
+    (dict(lowbit=-1), S.EINVAL),
 ])
 def test_check_rejects(kw, code):
     assert S.check(p_ok(**kw), S.OP_ROUTE) == code
@@ -93,6 +94,11 @@ def test_layouts_alpha_modes_and_output_dtypes_are_accepted():
     pv = p_ok(lowbit=S.LOWBIT_QKV)
     assert S.workspace_bytes(pv, S.OP_FORWARD_FP8) > S.workspace_bytes(p_ok(), S.OP_FORWARD_FP8)
     assert S.workspace_bytes(pv, S.OP_FORWARD) == S.workspace_bytes(p_ok(), S.OP_FORWARD)
+    # int8 Q/K codes take the same room as e4m3 ones
+    for lb, same in ((S.LOWBIT_I8QK, p_ok()), (S.LOWBIT_I8QKV, pv)):
+        assert S.check(p_ok(lowbit=lb), S.OP_FORWARD_FP8) == S.OK
+        assert S.workspace_bytes(p_ok(lowbit=lb), S.OP_FORWARD_FP8) == S.workspace_bytes(
+            same, S.OP_FORWARD_FP8)
 
 
 def test_workspace_sizes_grow_with_the_problem():

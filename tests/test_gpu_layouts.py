@@ -26,6 +26,7 @@ PATHS = [  # name, dtype, N, d, bq, frac, fp8, lowbit
     ("bf16-d128", "bf16", 4100, 128, 128, 0.05, False, S.LOWBIT_QK),
     ("fp8", "bf16", 2000, 128, 128, 0.1, True, S.LOWBIT_QK),
     ("fp8-v", "bf16", 2000, 128, 128, 0.1, True, S.LOWBIT_QKV),
+    ("i8-v", "bf16", 2000, 128, 128, 0.1, True, S.LOWBIT_I8QKV),
 ]
 OPTS = [  # layout, alpha mode
     (S.LAYOUT_BNHD, S.ALPHA_PER_HEAD),
@@ -72,7 +73,7 @@ def test_layout_alpha_and_bf16_output(orc, dev, path, opt):
     if layout == S.LAYOUT_BNHD:
         O = O.permute(0, 2, 1, 3).contiguous()
     op = orc.problem(1, H, N, d, bq, 64, frac, 1, dtype, alpha_mode=amode,
-                     lowbit_v=int(lowbit == S.LOWBIT_QKV))
+                     lowbit_v=lowbit & 1, int8_qk=(lowbit >> 1) & 1)
     tol = TOL["fp8"] if fp8 else TOL[dtype]
     compare_blocks(orc, x, oidx, O, orc.all_blocks(op), tol,
                    variant="fp8" if fp8 else "exact", op=op, alpha=alpha)

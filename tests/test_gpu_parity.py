@@ -50,7 +50,7 @@ def problem_of(x, lowbit=S.LOWBIT_QK):
 def oracle_problem(orc, x, lowbit=S.LOWBIT_QK):
     w = x.wl
     return orc.problem(w.B, w.H, w.N, w.d, w.bq, w.bkv, w.topk_frac, x.wq.shape[0], w.dtype,
-                       lowbit_v=int(lowbit == S.LOWBIT_QKV))
+                       lowbit_v=lowbit & 1, int8_qk=(lowbit >> 1) & 1)
 
 
 def run_gpu(x, dev, fp8=False, want_mask=True, lowbit=S.LOWBIT_QK):
@@ -279,8 +279,8 @@ def test_sparsity_sweep(orc, dev, frac):
 # --------------------------------------------------------------------------
 # low-bit sparse branch
 # --------------------------------------------------------------------------
-def quantize_gpu(x, dev):
-    p = problem_of(x)
+def quantize_gpu(x, dev, lowbit=S.LOWBIT_QK):
+    p = problem_of(x, lowbit)
     q, k, _, _, _, _ = to_dev(x, dev)
     w = x.wl
     BH = w.B * w.H
@@ -294,15 +294,17 @@ def quantize_gpu(x, dev):
     return [t.cpu().numpy() for t in (qh, kh, sq, sk, mu)]
 
 
+@pytest.mark.parametrize("lowbit", [S.LOWBIT_QK, S.LOWBIT_I8QK], ids=["e4m3", "int8"])
 @pytest.mark.parametrize("N,H", [(700, 2), (4100, 3), (75600, 1)])
-def test_quantized_inputs_match_oracle(orc, dev, N, H):
+def test_quantized_inputs_match_oracle(orc, dev, N, H, lowbit):
     """Q/K codes, per-block scales and the K channel mean are bit-exact."""
     w = wl(f"q{N}", "bf16", N, 128, 128, 0.03, H=H)
     if N == 75600:
         w = w.with_(grid=(21, 45, 80))
     x = I.make_inputs(w)
-    qh, kh, sq, sk, mu = quantize_gpu(x, dev)
-    op = orc.problem_of(x)
+    say(f"case quantize N={N} H={H} lowbit {lowbit}")
+    qh, kh, sq, sk, mu = quantize_gpu(x, dev, lowbit)
+    op = oracle_problem(orc, x, lowbit)
     for bh in range(w.B * w.H):
         oqh, okh, osq, osk, omu = orc.quant_fp8(op, x.q, x.k, bh)
         assert np.array_equal(mu[bh], omu)
@@ -322,10 +324,11 @@ FP8_SMALL = [
 ]
 
 
-LOWBITS = [S.LOWBIT_QK, S.LOWBIT_QKV]
+LOWBITS = [S.LOWBIT_QK, S.LOWBIT_QKV, S.LOWBIT_I8QK, S.LOWBIT_I8QKV]
+LOWBIT_IDS = ["qk", "qkv", "i8qk", "i8qkv"]
 
 
-@pytest.mark.parametrize("lowbit", LOWBITS, ids=["qk", "qkv"])
+@pytest.mark.parametrize("lowbit", LOWBITS, ids=LOWBIT_IDS)
 @pytest.mark.parametrize("w", FP8_SMALL, ids=[w.name for w in FP8_SMALL])
 def test_fp8_forward_parity(orc, dev, w, lowbit):
     say(f"case {w.name}: N={w.N} frac={w.topk_frac} lowbit {lowbit}")
@@ -359,7 +362,7 @@ def test_quantized_v_matches_oracle(orc, dev, N, H):
         assert not vh[bh, N:].any()
 
 
-@pytest.mark.parametrize("lowbit", LOWBITS, ids=["qk", "qkv"])
+@pytest.mark.parametrize("lowbit", LOWBITS, ids=LOWBIT_IDS)
 def test_fp8_wan14b_sampled(orc, dev, lowbit):
     w = I.WAN14B
     x = I.make_inputs(w)
