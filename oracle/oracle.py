@@ -32,7 +32,8 @@ class Problem(C.Structure):
     _fields_ = [("B", C.c_int32), ("H", C.c_int32), ("N", C.c_int32), ("d", C.c_int32),
                 ("bq", C.c_int32), ("bkv", C.c_int32), ("topk_frac", C.c_float),
                 ("w_heads", C.c_int32), ("dtype", C.c_int32), ("alpha_mode", C.c_int32),
-                ("lowbit_v", C.c_int32), ("int8_qk", C.c_int32)]
+                ("lowbit_v", C.c_int32), ("int8_qk", C.c_int32), ("phi", C.c_int32),
+                ("mode", C.c_int32), ("low_frac", C.c_float)]
 
 
 _lib = None
@@ -47,6 +48,9 @@ def lib():
         P = C.POINTER(Problem)
         vp, ip, dp = C.c_void_p, C.c_void_p, C.c_void_p
         L.orc_topk.argtypes = [P]
+        L.orc_topk_low.argtypes = [P]
+        L.orc_route_v1.argtypes = [P, vp, vp, ip, C.c_int, ip, ip, vp, dp, dp, C.c_int]
+        L.orc_forward_v1.argtypes = [P, vp, vp, vp, ip, ip, vp, ip, C.c_int, dp, C.c_int]
         L.orc_num_blocks.argtypes = [C.c_int, C.c_int]
         L.orc_route.argtypes = [P, vp, vp, vp, vp, ip, C.c_int, ip, vp, dp, dp, C.c_int]
         L.orc_forward.argtypes = [P, vp, vp, vp, ip, vp, ip, C.c_int, dp, C.c_int]
@@ -71,12 +75,14 @@ def _ptr(a):
 
 
 def problem(B, H, N, d, bq, bkv, frac, w_heads=1, dtype="f32", alpha_mode=0,
-            lowbit_v=0, int8_qk=0) -> Problem:
+            lowbit_v=0, int8_qk=0, phi=0, mode=0, low_frac=0.0) -> Problem:
     """alpha_mode 0: alpha [H]; 1: alpha [H][T_q] (one per query block).
     lowbit_v 1: the low-bit variant quantises V too (per channel).
-    int8_qk 1: the low-bit variant takes int8 Q/K codes instead of e4m3."""
+    int8_qk 1: the low-bit variant takes int8 Q/K codes instead of e4m3.
+    phi 0: elu + 1; 1: softmax over the d channels of a row.
+    mode 1: SLA (v1) with low_frac of the blocks negligible per row."""
     return Problem(B, H, N, d, bq, bkv, float(frac), w_heads, 0 if dtype == "f32" else 1,
-                   alpha_mode, lowbit_v, int8_qk)
+                   alpha_mode, lowbit_v, int8_qk, phi, mode, float(low_frac))
 
 
 def problem_of(x) -> Problem:
@@ -95,6 +101,11 @@ def _qkv(p: Problem, a):
 
 def topk(p: Problem) -> int:
     return lib().orc_topk(C.byref(p))
+
+
+def topk_low(p: Problem) -> int:
+    """v1: number of negligible blocks per row (0 in SLA2 mode)."""
+    return lib().orc_topk_low(C.byref(p))
 
 
 def num_blocks(n: int, b: int) -> int:
@@ -121,6 +132,50 @@ def route(p: Problem, q, k, wq, wk, heads=None, nthreads=0, want_scores=False):
     L.orc_route(C.byref(p), _ptr(q), _ptr(k), _ptr(wq), _ptr(wk), _ptr(heads), len(heads),
                 _ptr(idx), _ptr(mask), _ptr(gap), _ptr(sc), nthreads)
     return idx, mask, gap, sc
+
+
+def route_v1(p: Problem, q, k, heads=None, nthreads=0, want_scores=False):
+    """SLA (v1) router (p.mode == 1): returns (crit [B,H,Tq,k_h], negl
+    [B,H,Tq,k_l], both int32 ascending; mask [B,H,Tq,Tkv] uint8 with 1 / 0xFF
+    / 0 for critical / negligible / marginal; gap_rel; scores or None)."""
+    L = lib()
+    B, H, N = p.B, p.H, p.N
+    Tq, Tkv = num_blocks(N, p.bq), num_blocks(N, p.bkv)
+    kh, kl = topk(p), topk_low(p)
+    heads = np.arange(B * H, dtype=np.int32) if heads is None else np.asarray(heads, np.int32)
+    q, k = _qkv(p, q), _qkv(p, k)
+    crit = np.full((B, H, Tq, kh), -1, np.int32)
+    negl = np.full((B, H, Tq, kl), -1, np.int32)
+    mask = np.zeros((B, H, Tq, Tkv), np.uint8)
+    gap = np.full((B, H, Tq), np.nan)
+    sc = np.full((B, H, Tq, Tkv), np.nan) if want_scores else None
+    rc = L.orc_route_v1(C.byref(p), _ptr(q), _ptr(k), _ptr(heads), len(heads), _ptr(crit),
+                        _ptr(negl), _ptr(mask), _ptr(gap), _ptr(sc), nthreads)
+    if rc < 0:
+        raise ValueError("oracle: route_v1 needs mode 1")
+    return crit, negl, mask, gap, sc
+
+
+def forward_v1(p: Problem, q, k, v, crit, negl, wp, blocks, nthreads=0):
+    """SLA (v1) forward for the query blocks ``blocks``: [n_blocks, bq, d]."""
+    L = lib()
+    blocks = np.ascontiguousarray(np.asarray(blocks, np.int32).reshape(-1, 2))
+    out = np.zeros((blocks.shape[0], p.bq, p.d))
+    q, k, v = _qkv(p, q), _qkv(p, k), _qkv(p, v)
+    crit, negl = _arr(crit, np.int32), _arr(negl, np.int32)
+    wp = _arr(wp, np.float32)
+    rc = L.orc_forward_v1(C.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(crit), _ptr(negl),
+                          _ptr(wp), _ptr(blocks), blocks.shape[0], _ptr(out), nthreads)
+    if rc != 0:
+        raise ValueError(f"oracle: forward_v1 failed ({rc})")
+    return out
+
+
+def forward_v1_full(p: Problem, q, k, v, crit, negl, wp, nthreads=0):
+    out = forward_v1(p, q, k, v, crit, negl, wp, all_blocks(p), nthreads)
+    Tq = num_blocks(p.N, p.bq)
+    o = out.reshape(p.B, p.H, Tq * p.bq, p.d)[:, :, : p.N]
+    return np.ascontiguousarray(o)
 
 
 def forward(p: Problem, q, k, v, idx, alpha, blocks, nthreads=0, variant="exact",

@@ -16,9 +16,14 @@
  *            05 (pool, proj_q / proj_k, P_c, hard Top-k, b_q=128, b_kv=64),
  *            07 (low-bit Q/K and P, K column-mean smoothing, online softmax
  *            over mask-hit blocks only), 08 (what runs for hit / missed blocks).
- *  [SLA-zh]  "SLA: Beyond Sparsity ..." notes (papernotes.org), key design 3
- *            (H_i, Z_i, O_i^l = phi(Q_i) H_i / phi(Q_i) Z_i) and key design 4
- *            (per-block h_j = phi(K_j)^T V_j and z_j, H_i += h_j).
+ *  [SLA-zh]  "SLA: Beyond Sparsity ..." notes (papernotes.org), key design 2
+ *            (P_c = softmax(pool(Q) pool(K)^T / sqrt d); per row the top k_h %
+ *            of blocks critical, the bottom k_l % negligible, the rest
+ *            marginal), key design 3 (H_i, Z_i over the marginal blocks,
+ *            O_i^l = phi(Q_i) H_i / phi(Q_i) Z_i, O = O^s + Proj(O^l)), key
+ *            design 4 (per-block h_j = phi(K_j)^T V_j and z_j, H_i += h_j),
+ *            and the training-strategy section (phi = softmax, k_h = 5 %,
+ *            k_l = 10 %).
  *  [SLA2-en] gist.science explainer, section 2A (O = alpha O_s + (1-alpha) O_l,
  *            both branches row-normalised).
  *
@@ -29,7 +34,17 @@
  *  - k = clamp(ceil(frac * T_kv - 1e-6), 0, T_kv); ties broken by lower index;
  *  - tokens beyond N in a ragged last block are excluded everywhere (means
  *    divide by the valid count, no logit, no phi term);
- *  - phi = elu + 1 elementwise on raw Q and K;
+ *  - phi = elu + 1 elementwise on raw Q and K, or (phi = 1) softmax over the
+ *    d channels of each raw Q or K row;
+ *  - SLA (v1) mode (mode = 1): the router pools without projections (the
+ *    softmax and 1/sqrt d of P_c keep the row order of the plain product);
+ *    one total order per row, score descending then index ascending: the
+ *    first k_h blocks are critical, the last k_l negligible, k_h as k above
+ *    and k_l = clamp(ceil(low_frac * T_kv - 1e-6), 0, T_kv - k_h); the
+ *    sparse branch runs over the critical blocks, the linear branch over the
+ *    marginal ones (neither critical nor negligible), O = O_s + O_l W_p with
+ *    W_p [w_heads][d][d] (Proj = x W_p, no bias, like the router's
+ *    projections); alpha is not used;
  *  - empty selected set -> O_s = 0; empty unselected set -> O_l = 0;
  *  - alpha is per head, or per head and query block (the algorithm's
  *    granularity; alpha_mode 1);
@@ -62,6 +77,9 @@ typedef struct {
     int32_t alpha_mode; /* 0: alpha [H]; 1: alpha [H][T_q], one per query block */
     int32_t lowbit_v;   /* low-bit variant: 1 = V also quantised (per channel) */
     int32_t int8_qk;    /* low-bit variant: 1 = Q, K as int8 codes (else e4m3) */
+    int32_t phi;        /* 0: elu + 1; 1: softmax over the d channels of a row */
+    int32_t mode;       /* 0: SLA2; 1: SLA (v1), ternary blocks and Proj combine */
+    float low_frac;     /* v1: fraction of negligible blocks per row */
 } orc_problem;
 
 /* ------------------------------------------------------------------ */
@@ -77,6 +95,17 @@ int orc_topk(const orc_problem* p) {
     double k = ceil((double)p->topk_frac * (double)tkv - 1e-6);
     if (k < 0) k = 0;
     if (k > tkv) k = tkv;
+    return (int)k;
+}
+
+/* v1: k_l = clamp(ceil(low_frac * T_kv - 1e-6), 0, T_kv - k_h); 0 in SLA2 mode */
+int orc_topk_low(const orc_problem* p) {
+    if (p->mode != 1) return 0;
+    int tkv = ceil_div(p->N, p->bkv);
+    double k = ceil((double)p->low_frac * (double)tkv - 1e-6);
+    int kh = orc_topk(p);
+    if (k < 0) k = 0;
+    if (k > tkv - kh) k = tkv - kh;
     return (int)k;
 }
 
@@ -96,6 +125,26 @@ static double elem(const orc_problem* p, const void* X, long bh, long t, long c)
 
 /* phi = elu + 1: x + 1 for x > 0, exp(x) otherwise */
 static double phi(double x) { return x > 0.0 ? x + 1.0 : exp(x); }
+
+/* phi of row t of X (head bh): elu + 1 per element, or the softmax of the
+   row over its d channels */
+static void phi_row(const orc_problem* p, const void* X, long bh, long t, double* out) {
+    int d = p->d;
+    if (p->phi == 0) {
+        for (int c = 0; c < d; ++c) out[c] = phi(elem(p, X, bh, t, c));
+        return;
+    }
+    double m = -INFINITY, s = 0.0;
+    for (int c = 0; c < d; ++c) {
+        out[c] = elem(p, X, bh, t, c);
+        if (out[c] > m) m = out[c];
+    }
+    for (int c = 0; c < d; ++c) {
+        out[c] = exp(out[c] - m);
+        s += out[c];
+    }
+    for (int c = 0; c < d; ++c) out[c] /= s;
+}
 
 /* ------------------------------------------------------------------ */
 /* OCP fp8 E4M3 (bias 7, no infinities, S.1111.111 = NaN, max 448)      */
@@ -230,6 +279,7 @@ typedef struct {
     uint8_t* mask;
     double* gap_rel;
     double* scores; /* optional [B*H][Tq][Tkv] */
+    int32_t* nidx;  /* v1: negligible blocks [B*H][Tq][k_l] (optional) */
 } route_ctx;
 
 /* mean of the valid rows of block `blk` (size bs) of head bh, in fp64 */
@@ -259,8 +309,10 @@ static void route_head(void* vctx, long item) {
     int d = p->d;
     int Tq = ceil_div(p->N, p->bq), Tkv = ceil_div(p->N, p->bkv);
     int k = orc_topk(p);
-    const float* Wq = C->Wq + (p->w_heads == 1 ? 0 : (size_t)h * d * d);
-    const float* Wk = C->Wk + (p->w_heads == 1 ? 0 : (size_t)h * d * d);
+    int kl = orc_topk_low(p);
+    const int v1 = p->mode == 1; /* no projections in the v1 router */
+    const float* Wq = v1 ? NULL : C->Wq + (p->w_heads == 1 ? 0 : (size_t)h * d * d);
+    const float* Wk = v1 ? NULL : C->Wk + (p->w_heads == 1 ? 0 : (size_t)h * d * d);
 
     double* bar = (double*)malloc(sizeof(double) * d);
     double* qt = (double*)malloc(sizeof(double) * (size_t)Tq * d);
@@ -270,11 +322,13 @@ static void route_head(void* vctx, long item) {
     /* step 2 (pool) and step 3 (project) */
     for (int i = 0; i < Tq; ++i) {
         pool_block(p, C->Q, bh, i, p->bq, bar);
-        project(d, bar, Wq, qt + (size_t)i * d);
+        if (v1) memcpy(qt + (size_t)i * d, bar, sizeof(double) * d);
+        else project(d, bar, Wq, qt + (size_t)i * d);
     }
     for (int j = 0; j < Tkv; ++j) {
         pool_block(p, C->K, bh, j, p->bkv, bar);
-        project(d, bar, Wk, kt + (size_t)j * d);
+        if (v1) memcpy(kt + (size_t)j * d, bar, sizeof(double) * d);
+        else project(d, bar, Wk, kt + (size_t)j * d);
     }
     for (int i = 0; i < Tq; ++i) {
         /* step 4: compressed score row P_c[i, :] */
@@ -293,6 +347,18 @@ static void route_head(void* vctx, long item) {
         if (mrow) memset(mrow, 0, Tkv);
         for (int r = 0; r < k; ++r)
             if (mrow) mrow[row[r].j] = 1;
+        /* v1: the last k_l blocks of the order are negligible (mask -1) */
+        for (int r = Tkv - kl; r < Tkv; ++r)
+            if (mrow) mrow[row[r].j] = 0xFF;
+        if (C->nidx && kl > 0) {
+            int32_t* nrow = C->nidx + ((size_t)bh * Tq + i) * kl;
+            uint8_t* tmp = (uint8_t*)calloc(Tkv, 1);
+            for (int r = Tkv - kl; r < Tkv; ++r) tmp[row[r].j] = 1;
+            int w = 0;
+            for (int j = 0; j < Tkv; ++j)
+                if (tmp[j]) nrow[w++] = j;
+            free(tmp);
+        }
         /* emit selected indices ascending */
         if (C->idx) {
             int32_t* irow = C->idx + ((size_t)bh * Tq + i) * k;
@@ -311,6 +377,11 @@ static void route_head(void* vctx, long item) {
                 double gap = row[k - 1].s - row[k].s;
                 g = smax > 0.0 ? gap / smax : 0.0;
             }
+            if (kl > 0 && kl + k < Tkv) { /* v1: also the negligible cut */
+                double gap = row[Tkv - kl - 1].s - row[Tkv - kl].s;
+                double gl = smax > 0.0 ? gap / smax : 0.0;
+                if (gl < g) g = gl;
+            }
             C->gap_rel[(size_t)bh * Tq + i] = g;
         }
     }
@@ -326,9 +397,22 @@ static void route_head(void* vctx, long item) {
 int orc_route(const orc_problem* p, const void* Q, const void* K, const float* Wq,
               const float* Wk, const int32_t* heads, int n_heads, int32_t* idx,
               uint8_t* mask, double* gap_rel, double* scores, int nthreads) {
-    route_ctx C = {p, Q, K, Wq, Wk, heads, idx, mask, gap_rel, scores};
+    route_ctx C = {p, Q, K, Wq, Wk, heads, idx, mask, gap_rel, scores, NULL};
     run_pool(route_head, &C, n_heads, nthreads);
     return orc_topk(p);
+}
+
+/* SLA (v1) router (p->mode == 1): idx [B*H][Tq][k_h] critical and nidx
+ * [B*H][Tq][k_l] negligible blocks, both ascending; mask 1 / 0xFF (-1) / 0
+ * for critical / negligible / marginal.  gap_rel: the smaller relative margin
+ * of the two cuts.  Returns k_l, or -1 if p is not in v1 mode. */
+int orc_route_v1(const orc_problem* p, const void* Q, const void* K, const int32_t* heads,
+                 int n_heads, int32_t* idx, int32_t* nidx, uint8_t* mask, double* gap_rel,
+                 double* scores, int nthreads) {
+    if (p->mode != 1) return -1;
+    route_ctx C = {p, Q, K, NULL, NULL, heads, idx, mask, gap_rel, scores, nidx};
+    run_pool(route_head, &C, n_heads, nthreads);
+    return orc_topk_low(p);
 }
 
 /* ------------------------------------------------------------------ */
@@ -357,7 +441,7 @@ static void summary_block(void* vctx, long j) {
     int t0 = (int)j * p->bkv;
     int n = p->N - t0 < p->bkv ? p->N - t0 : p->bkv;
     for (int u = t0; u < t0 + n; ++u) {
-        for (int c = 0; c < d; ++c) pk[c] = phi(elem(p, S->K, S->bh, u, c));
+        phi_row(p, S->K, S->bh, u, pk);
         for (int e = 0; e < d; ++e) vv[e] = elem(p, S->V, S->bh, u, e);
         for (int c = 0; c < d; ++c) {
             z[c] += pk[c];
@@ -484,6 +568,8 @@ typedef struct {
     const quant_t* qt;     /* this head's quantised inputs (low bit) */
     double* bound;         /* low bit, optional: [n_blocks][bq] near-midpoint bound */
     double acc_eps;        /* relative accumulation error assumed for the bound */
+    const int32_t* nidx;   /* v1: negligible blocks [B*H][Tq][k_l] */
+    const float* Wp;       /* v1: Proj weights [w_heads][d][d] */
 } fwd_ctx;
 
 /* Ambiguous P-quantisation decisions.  A second implementation computes the
@@ -673,16 +759,24 @@ static void forward_block(void* vctx, long it) {
     int d = p->d, Tq = ceil_div(p->N, p->bq), Tkv = ceil_div(p->N, p->bkv);
     int k = orc_topk(p);
     int h = (int)(F->bh % p->H);
-    /* step 8 weight: per head, or per head and query block */
-    double a = (double)(p->alpha_mode ? F->alpha[(size_t)h * Tq + i] : F->alpha[h]);
+    const int v1 = p->mode == 1;
+    int kl = orc_topk_low(p);
+    /* step 8 weight: per head, or per head and query block (SLA2 only) */
+    double a = v1 ? 1.0
+                  : (double)(p->alpha_mode ? F->alpha[(size_t)h * Tq + i] : F->alpha[h]);
     const int32_t* sel = F->idx + ((size_t)F->bh * Tq + i) * k;
     double* out = F->out + (size_t)pos * p->bq * d;
     memset(out, 0, sizeof(double) * (size_t)p->bq * d);
 
-    /* unselected set, H_i and Z_i ([SLA-zh] key design 3) */
+    /* linear set, H_i and Z_i ([SLA-zh] key design 3): the unselected
+       blocks; in v1 mode the marginal ones (neither critical nor negligible) */
     uint8_t* hit = (uint8_t*)calloc(Tkv, 1);
     for (int r = 0; r < k; ++r) hit[sel[r]] = 1;
-    int n_unsel = Tkv - k;
+    if (v1)
+        for (int r = 0; r < kl; ++r) hit[F->nidx[((size_t)F->bh * Tq + i) * kl + r]] = 1;
+    int n_unsel = Tkv - k - (v1 ? kl : 0);
+    const float* Wp = v1 ? F->Wp + (p->w_heads == 1 ? 0 : (size_t)h * d * d) : NULL;
+    double* ol = (double*)malloc(sizeof(double) * d);
     double* Hi = (double*)calloc((size_t)d * d, sizeof(double));
     double* Zi = (double*)calloc(d, sizeof(double));
     if (n_unsel > 0) {
@@ -706,20 +800,30 @@ static void forward_block(void* vctx, long it) {
         else sparse_lowbit(F, i, sel, k, t, os, lbuf, bnd);
         if (bnd) *bnd *= a; /* the combine scales O_s by alpha */
         /* step 7: linear branch O_l = phi(q) H_i / (phi(q) . Z_i) */
-        for (int c = 0; c < d; ++c) pq[c] = phi(elem(p, F->Q, F->bh, t, c));
+        phi_row(p, F->Q, F->bh, t, pq);
         if (n_unsel > 0) {
             double den = 0.0;
             for (int c = 0; c < d; ++c) den += pq[c] * Zi[c];
             for (int e = 0; e < d; ++e) {
                 double num = 0.0;
                 for (int c = 0; c < d; ++c) num += pq[c] * Hi[(size_t)c * d + e];
-                /* step 8: combine */
-                o[e] = a * os[e] + (1.0 - a) * (num / den);
+                ol[e] = num / den;
             }
         } else {
-            for (int e = 0; e < d; ++e) o[e] = a * os[e];
+            for (int e = 0; e < d; ++e) ol[e] = 0.0;
+        }
+        /* step 8: combine; v1: O = O_s + O_l W_p ([SLA-zh] key design 3) */
+        for (int e = 0; e < d; ++e) {
+            if (v1) {
+                double pr = 0.0;
+                for (int c = 0; c < d; ++c) pr += ol[c] * (double)Wp[(size_t)c * d + e];
+                o[e] = os[e] + pr;
+            } else {
+                o[e] = a * os[e] + (1.0 - a) * ol[e];
+            }
         }
     }
+    free(ol);
     free(hit);
     free(Hi);
     free(Zi);
@@ -731,9 +835,10 @@ static void forward_block(void* vctx, long it) {
 static int forward_common(const orc_problem* p, const void* Q, const void* K, const void* V,
                           const int32_t* idx, const float* alpha, const int32_t* blocks,
                           int n_blocks, double* out, int nthreads, int variant,
-                          int quantize, double* bound, double acc_eps) {
+                          int quantize, double* bound, double acc_eps, const int32_t* nidx,
+                          const float* Wp) {
     int d = p->d, Tq = ceil_div(p->N, p->bq), Tkv = ceil_div(p->N, p->bkv);
-    int k = orc_topk(p);
+    int k = orc_topk(p) + orc_topk_low(p); /* blocks outside the linear branch */
     long nbh = (long)p->B * p->H;
     /* process heads one at a time: the per-block summaries of a head are
        large (T_kv * d * d doubles) */
@@ -771,7 +876,7 @@ static int forward_common(const orc_problem* p, const void* Q, const void* K, co
             }
         }
         fwd_ctx F = {p, Q, K, V, idx, alpha, blocks, out, bh, items, h, z,
-                     variant, quantize, &qt, bound, acc_eps};
+                     variant, quantize, &qt, bound, acc_eps, nidx, Wp};
         run_pool(forward_block, &F, n_it, nthreads);
         free(h);
         free(z);
@@ -796,8 +901,21 @@ static int forward_common(const orc_problem* p, const void* Q, const void* K, co
 int orc_forward(const orc_problem* p, const void* Q, const void* K, const void* V,
                 const int32_t* idx, const float* alpha, const int32_t* blocks,
                 int n_blocks, double* out, int nthreads) {
+    if (p->mode != 0) return -2;
     return forward_common(p, Q, K, V, idx, alpha, blocks, n_blocks, out, nthreads, 0, 1, NULL,
-                          0.0);
+                          0.0, NULL, NULL);
+}
+
+/* SLA (v1) forward (p->mode == 1): sparse branch over the critical blocks
+ * idx [B*H][Tq][k_h], linear branch over the marginal blocks (neither in idx
+ * nor in nidx [B*H][Tq][k_l]), O = O_s + O_l Wp.  Same block list and output
+ * as orc_forward.  Returns 0, -1 on a bad block, -2 if p is not in v1 mode. */
+int orc_forward_v1(const orc_problem* p, const void* Q, const void* K, const void* V,
+                   const int32_t* idx, const int32_t* nidx, const float* Wp,
+                   const int32_t* blocks, int n_blocks, double* out, int nthreads) {
+    if (p->mode != 1) return -2;
+    return forward_common(p, Q, K, V, idx, NULL, blocks, n_blocks, out, nthreads, 0, 1, NULL,
+                          0.0, nidx, Wp);
 }
 
 /* Forward with the low-bit sparse branch (quantize=1: e4m3; 0: identity).
@@ -810,7 +928,7 @@ int orc_forward_fp8(const orc_problem* p, const void* Q, const void* K, const vo
                     int n_blocks, int quantize, double* out, double* bound, double acc_eps,
                     int nthreads) {
     if (bound) memset(bound, 0, sizeof(double) * (size_t)n_blocks * p->bq);
-    if (p->bkv > 512) return -2;
+    if (p->bkv > 512 || p->mode != 0) return -2;
     return forward_common(p, Q, K, V, idx, alpha, blocks, n_blocks, out, nthreads, 1,
-                          quantize, bound, acc_eps);
+                          quantize, bound, acc_eps, NULL, NULL);
 }

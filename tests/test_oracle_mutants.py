@@ -17,7 +17,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 SRC = os.path.join(ROOT, "oracle", "sla2_oracle.c")
 
 MUTANTS = {
-    "combine_weight": ("(1.0 - a) * (num / den)", "a * (num / den)"),
+    "combine_weight": ("(1.0 - a) * ol[e]", "a * ol[e]"),
     "linear_over_selected": ("if (hit[j]) continue;", "if (!hit[j]) continue;"),
     "phi_without_plus_one": ("x > 0.0 ? x + 1.0 : exp(x)", "x > 0.0 ? x : exp(x)"),
     "no_softmax_scale": ("double inv = 1.0 / sqrt((double)d);\n    for (int e = 0; e < d; ++e) os[e] = 0.0;\n    if (k == 0) return;\n    long nu",
@@ -49,6 +49,13 @@ MUTANTS = {
     "i8_codes_unsigned": ("a = (double)(int8_t)Qt->qh[(size_t)t * d + c];", "a = (double)Qt->qh[(size_t)t * d + c];"),
     "i8_k_not_smoothed": ("o->kh[(size_t)t * d + c] = p->int8_qk ? (uint8_t)orc_i8_encode(ks / s)",
                           "o->kh[(size_t)t * d + c] = p->int8_qk ? (uint8_t)orc_i8_encode((ks + o->mu[c]) / s)"),
+    "v1_negligible_kept_in_linear": ("    if (v1)\n        for (int r = 0; r < kl; ++r) hit[", "    if (0)\n        for (int r = 0; r < kl; ++r) hit["),
+    "v1_proj_transposed": ("(double)Wp[(size_t)c * d + e]", "(double)Wp[(size_t)e * d + c]"),
+    "v1_negligible_cut_off_by_one": ("for (int r = Tkv - kl; r < Tkv; ++r)\n            if (mrow)", "for (int r = Tkv - kl - 1; r < Tkv - 1; ++r)\n            if (mrow)"),
+    "v1_low_not_clamped": ("    if (k > tkv - kh) k = tkv - kh;\n", ""),
+    "v1_sparse_halved": ("o[e] = os[e] + pr;", "o[e] = 0.5 * os[e] + pr;"),
+    "phi_softmax_not_normalised": ("    for (int c = 0; c < d; ++c) out[c] /= s;\n", ""),
+    "phi_softmax_no_exp": ("        out[c] = exp(out[c] - m);\n", "        out[c] = out[c] - m + 30.0;\n"),
     "numerator_transposed_H": ("num += pq[c] * Hi[(size_t)c * d + e];", "num += pq[c] * Hi[(size_t)e * d + c];"),
 }
 
@@ -78,6 +85,11 @@ PINS = [
     (pins.test_lowbit_i8_quantised_inputs, ()),
     (pins.test_lowbit_i8_identity_quantiser_equals_exact, ()),
     (pins.test_lowbit_i8_single_tile_closed_form, (0,)),
+    (pins.test_phi_softmax_linear_attention, ("f32",)),
+    (pins.test_v1_negligible_count_table, ()),
+    (pins.test_v1_router_brute_force, ()),
+    (pins.test_v1_is_sparse_plus_projected_linear, (1,)),
+    (pins.test_v1_all_marginal_or_none, ()),
 ]
 
 

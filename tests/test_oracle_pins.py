@@ -731,6 +731,168 @@ def test_lowbit_i8_error_is_small(orc):
 
 
 # --------------------------------------------------------------------------
+# softmax feature map, and SLA (v1) compatibility mode
+# --------------------------------------------------------------------------
+def phi_softmax(x):
+    """phi = softmax over the channels of each row (torch, float64)."""
+    return torch.softmax(torch.from_numpy(np.asarray(x, np.float64)), dim=-1).numpy()
+
+
+def linear_quadratic_sm(q, k, v, keep):
+    """Linear attention with softmax features in its quadratic form."""
+    a = (phi_softmax(q) @ phi_softmax(k).T) * keep
+    return (a @ v) / a.sum(axis=1, keepdims=True)
+
+
+def masked_attention(q, k, v, keep):
+    """softmax(q k^T / sqrt d) v over the tokens with keep true (brute force)."""
+    lg = (q @ k.T) / math.sqrt(q.shape[1])
+    lg = np.where(keep, lg, -np.inf)
+    lg = lg - lg.max(axis=1, keepdims=True)
+    w = np.exp(lg)
+    return (w @ v) / w.sum(axis=1, keepdims=True)
+
+
+def _v1_problem(orc, x, low, phi=1, frac=None):
+    w = x.wl
+    return orc.problem(w.B, w.H, w.N, w.d, w.bq, w.bkv, w.topk_frac if frac is None else frac,
+                       1, w.dtype, phi=phi, mode=1, low_frac=low)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_phi_softmax_linear_attention(orc, dtype):
+    """k = 0, alpha = 0, phi = softmax: the output is linear attention with
+    softmax features over all tokens (SLA notes, key design 3; the training
+    section picks softmax for phi)."""
+    x = small(dtype=dtype, N=700, d=64, frac=0.0, alpha=(0.0, 0.0))
+    w = x.wl
+    p = orc.problem(w.B, w.H, w.N, w.d, w.bq, w.bkv, 0.0, 1, dtype, phi=1)
+    idx = np.zeros((1, 2, w.Tq, 0), np.int32)
+    o = orc.forward_full(p, x.q, x.k, x.v, idx, x.alpha)
+    keep = np.ones((w.N, w.N), bool)
+    for h in range(2):
+        ref = linear_quadratic_sm(as_f64(x.q[0, h], dtype), as_f64(x.k[0, h], dtype),
+                                  as_f64(x.v[0, h], dtype), keep)
+        assert np.abs(o[0, h] - ref).max() < 1e-12
+
+
+def test_v1_negligible_count_table(orc):
+    """k_l = clamp(ceil(low * T_kv - 1e-6), 0, T_kv - k_h): 10 % of the 1.3B
+    and 14B shapes' KV blocks, clamping, and the SLA2 mode's 0."""
+    def kl(N, frac, low, mode=1):
+        return orc.topk_low(orc.problem(1, 1, N, 128, 128, 64, frac, mode=mode, low_frac=low))
+    assert kl(32760, 0.05, 0.10) == 52 and kl(75600, 0.05, 0.10) == 119
+    assert kl(64 * 10, 0.1, 0.1) == 1 and kl(64 * 10, 0.0, 0.0) == 0
+    assert kl(64 * 10, 0.7, 0.5) == 3  # clamped to T_kv - k_h
+    assert kl(64 * 10, 1.0, 0.5) == 0
+    assert kl(32760, 0.05, 0.10, mode=0) == 0
+
+
+def test_v1_router_brute_force(orc):
+    """Critical = the first k_h, negligible = the last k_l blocks of the order
+    (pooled score descending, index ascending), no projections."""
+    x = small(dtype="bf16", N=1500, d=64, frac=0.1, H=2)
+    w = x.wl
+    p = _v1_problem(orc, x, 0.2)
+    kh, kl = orc.topk(p), orc.topk_low(p)
+    crit, negl, mask, gap, sc = orc.route_v1(p, x.q, x.k, want_scores=True)
+    assert kh == 3 and kl == 5
+    for h in range(2):
+        q, k = as_f64(x.q[0, h], "bf16"), as_f64(x.k[0, h], "bf16")
+        qb = np.stack([q[i * 128:(i + 1) * 128].mean(0) for i in range(w.Tq)])
+        kb = np.stack([k[j * 64:(j + 1) * 64].mean(0) for j in range(w.Tkv)])
+        S = qb @ kb.T
+        assert np.allclose(sc[0, h], S, rtol=1e-12, atol=1e-12)
+        for i in range(w.Tq):
+            order = np.lexsort((np.arange(w.Tkv), -S[i]))
+            assert np.array_equal(crit[0, h, i], np.sort(order[:kh]))
+            assert np.array_equal(negl[0, h, i], np.sort(order[w.Tkv - kl:]))
+            want = np.zeros(w.Tkv, np.uint8)
+            want[order[:kh]] = 1
+            want[order[w.Tkv - kl:]] = 0xFF
+            assert np.array_equal(mask[0, h, i], want)
+
+
+def test_v1_router_negligible_ties_go_to_higher_index(orc):
+    """Duplicated KV blocks: at the negligible cut the pair member with the
+    higher index is the one dropped (it comes later in the order)."""
+    wl = I.TINY.with_(k_noise=0.0)
+    x = I.make_inputs(wl)
+    assert np.array_equal(x.k[0, 0, 0:64], x.k[0, 0, 64:128])
+    p = orc.problem(1, wl.H, wl.N, wl.d, wl.bq, wl.bkv, 0.0, 1, wl.dtype, mode=1,
+                    low_frac=5 / 16)
+    crit, negl, mask, gap, _ = orc.route_v1(p, x.q, x.k)
+    assert orc.topk_low(p) == 5
+    for row in mask.reshape(-1, 16):
+        split = [m for m in range(8) if row[2 * m] != row[2 * m + 1]]
+        assert len(split) == 1
+        m = split[0]
+        assert row[2 * m] == 0 and row[2 * m + 1] == 0xFF
+    assert (gap == 0).all()
+
+
+@pytest.mark.parametrize("phi", [0, 1])
+def test_v1_is_sparse_plus_projected_linear(orc, phi):
+    """O = softmax attention over the critical tokens + (linear attention over
+    the marginal tokens) W_p, both by brute force; W_p is not symmetric, so a
+    transposed projection fails.  Negligible tokens appear in neither."""
+    x = small(dtype="f32", N=1000, d=64, frac=0.15, H=2)
+    w = x.wl
+    p = _v1_problem(orc, x, 0.25, phi=phi)
+    crit, negl, mask, _, _ = orc.route_v1(p, x.q, x.k)
+    wp = np.random.default_rng(4).normal(0, 0.2, (1, 64, 64)).astype(np.float32)
+    o = orc.forward_v1_full(p, x.q, x.k, x.v, crit, negl, wp)
+    feat = phi_softmax if phi else (lambda a: phi_torch(np.asarray(a, np.float64)))
+    for h in range(2):
+        q, k, v = (np.asarray(a[0, h], np.float64) for a in (x.q, x.k, x.v))
+        m = mask[0, h]
+        crit_t = token_mask(m == 1, w.N, w.bq, w.bkv)
+        marg_t = token_mask(m == 0, w.N, w.bq, w.bkv)
+        os_ = masked_attention(q, k, v, crit_t)
+        a = (feat(q) @ feat(k).T) * marg_t
+        ol = (a @ v) / a.sum(axis=1, keepdims=True)
+        ref = os_ + ol @ wp[0].astype(np.float64)
+        assert np.abs(o[0, h] - ref).max() < 1e-11
+
+
+def test_v1_without_negligible_relates_to_sla2(orc):
+    """k_l = 0 and W_p = I: the v1 output is O_s + O_l, twice the SLA2
+    combine at alpha = 1/2 on the same selection."""
+    x = small(dtype="bf16", N=900, d=64, frac=0.2, alpha=(0.5, 0.5))
+    p1 = _v1_problem(orc, x, 0.0)
+    crit, negl, _, _, _ = orc.route_v1(p1, x.q, x.k)
+    o1 = orc.forward_v1_full(p1, x.q, x.k, x.v, crit, negl, np.eye(64, dtype=np.float32)[None])
+    w = x.wl
+    p2 = orc.problem(w.B, w.H, w.N, w.d, w.bq, w.bkv, w.topk_frac, 1, "bf16", phi=1)
+    o2 = orc.forward_full(p2, x.q, x.k, x.v, crit, x.alpha)
+    assert np.abs(o1 - 2.0 * o2).max() < 1e-12
+
+
+def test_v1_all_marginal_or_none(orc):
+    """k_h = k_l = 0: pure projected linear attention; k_h + k_l = T_kv: no
+    marginal block, O = O_s."""
+    x = small(dtype="f32", N=640, d=64, frac=0.0)
+    w = x.wl
+    wp = np.random.default_rng(2).normal(0, 0.2, (1, 64, 64)).astype(np.float32)
+    p = _v1_problem(orc, x, 0.0, frac=0.0)
+    crit, negl, _, _, _ = orc.route_v1(p, x.q, x.k)
+    o = orc.forward_v1_full(p, x.q, x.k, x.v, crit, negl, wp)
+    keep = np.ones((w.N, w.N), bool)
+    for h in range(2):
+        q, k, v = (np.asarray(a[0, h], np.float64) for a in (x.q, x.k, x.v))
+        ref = linear_quadratic_sm(q, k, v, keep) @ wp[0].astype(np.float64)
+        assert np.abs(o[0, h] - ref).max() < 1e-12
+    p = _v1_problem(orc, x, 1.0, frac=0.3)
+    crit, negl, mask, _, _ = orc.route_v1(p, x.q, x.k)
+    assert not (mask == 0).any()
+    o = orc.forward_v1_full(p, x.q, x.k, x.v, crit, negl, wp)
+    for h in range(2):
+        q, k, v = (np.asarray(a[0, h], np.float64) for a in (x.q, x.k, x.v))
+        ref = masked_attention(q, k, v, token_mask(mask[0, h] == 1, w.N, w.bq, w.bkv))
+        assert np.abs(o[0, h] - ref).max() < 1e-12
+
+
+# --------------------------------------------------------------------------
 # workload generator sanity (shapes and statistics stated for the workloads)
 # --------------------------------------------------------------------------
 def test_tiny_workload_statistics():
