@@ -13,7 +13,9 @@ FlashAttention2's dense work).  Prints ONE JSON line.
 Options: --steps K --warmup W; --gpus N (only 1: the path runs on one GPU);
 --no-cpu-baseline skips the oracle timing; --workload wan13b for the smaller
 shape; --no-fp8 skips the extra timings of sla2_forward_fp8 (the low-bit
-sparse branch on the same inputs: e4m3 or int8 Q/K, V bf16 or e4m3); --copy-calibration runs only a plain 1 GiB
+sparse branch on the same inputs: e4m3 or int8 Q/K, V bf16 or e4m3);
+--no-sla1 skips the extra timing of the SLA (v1) mode (sla1_route +
+sla1_forward, k_h 5 %, k_l 10 %, softmax phi) on the same inputs; --copy-calibration runs only a plain 1 GiB
 device copy (used to scale rocprofv3 FETCH_SIZE / WRITE_SIZE);
 --counters-summary FETCH WRITE COPY_FETCH COPY_WRITE turns four rocprofv3
 --pmc output folders (the bench, then the copy) into the per-launch HBM
@@ -86,7 +88,7 @@ def linear_summary_flop(BH, N, d) -> float:
 
 # --------------------------------------------------------------------------
 COPY_BYTES = 1 << 30
-FUSED_KERNEL_RX = r"fused128_kernel<true, false, false>"
+FUSED_KERNEL_RX = r"fused128_kernel<true, 0, false, false, false>"
 
 
 def copy_calibration():
@@ -192,6 +194,7 @@ def main():
     ap.add_argument("--workload", default="wan14b", choices=["wan14b", "wan13b"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-fp8", action="store_true")
+    ap.add_argument("--no-sla1", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--counters-summary", nargs=4, metavar="DIR")
     args = ap.parse_args()
@@ -347,6 +350,37 @@ def main():
                         "fused_lowbit_tflops": (fl_sparse + fl_apply) / (f8_ms * 1e-3) / 1e12
                         if f8_ms else None}
             del ws8
+
+    if not args.no_sla1:
+        # the SLA (v1) mode on the same inputs: k_h = 5 %, k_l = 10 %, softmax
+        # phi, O = O_s + O_l W_p (SLA notes, training section)
+        low = 0.10
+        p1 = S.problem(w.B, w.H, w.N, w.d, w.bq, w.bkv, 0.05, 1, w.dtype, phi=S.PHI_SOFTMAX)
+        kh1, kl1 = S.topk(p1), S.num_negligible(p1, low)
+        crit1 = torch.empty((w.B, w.H, Tq, kh1), dtype=torch.int32, device=dev)
+        negl1 = torch.empty((w.B, w.H, Tq, kl1), dtype=torch.int32, device=dev)
+        wp1 = torch.from_numpy(np.random.default_rng(0).normal(
+            0, w.d ** -0.5, (1, w.d, w.d)).astype(np.float32)).to(dev)
+        ws1 = S.workspace(p1, S.OP_SLA1_FORWARD)
+
+        def step1():
+            S.sla1_route(p1, q, k, low, crit1, negl1, None, ws_r, stream)
+            S.sla1_forward(p1, q, k, v, crit1, negl1, low, wp1, O, ws1, stream)
+
+        for _ in range(args.warmup):
+            step1()
+        torch.cuda.synchronize()
+        S.timing_start(64 * args.steps + 64)
+        ev0.record(stream)
+        for _ in range(args.steps):
+            step1()
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        st1 = {n_: ms_ / c_ for n_, (ms_, c_) in S.timing_stop().items()}
+        ms1 = ev0.elapsed_time(ev1) / args.steps
+        out["sla1"] = {"k_h": kh1, "k_l": kl1, "phi": "softmax", "ms_per_step": ms1,
+                       "tops": dense / (ms1 * 1e-3) / 1e12, "stages_ms": st1}
+        del ws1
 
     if not args.no_cpu_baseline:
         log("bench: timing the CPU oracle on a sample")

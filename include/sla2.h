@@ -15,7 +15,11 @@
  *   combine  O = alpha O_s + (1 - alpha) O_l ["SLA2 深度解读" 04; gist.science
  *            explainer, section 2A];
  *   low bit  Q, K quantised to fp8 e4m3 with per-block scales, K smoothed by
- *            its channel mean, P quantised before P V ["SLA2 深度解读" 07].
+ *            its channel mean, P quantised before P V ["SLA2 深度解读" 07];
+ *   SLA v1   the predecessor's ternary routing (critical / marginal /
+ *            negligible blocks), linear branch over the marginal blocks, O =
+ *            O_s + Proj(O_l), softmax feature map ["SLA: Beyond Sparsity ..."
+ *            notes, key designs 2 and 3, training section] -- sla1_* below.
  *
  * Conventions (all entry points):
  *  - Q, K, V, O, topk_idx, block_mask, alpha, Wq, Wk and ws are DEVICE
@@ -32,7 +36,7 @@
  *    B/H/N <= 0, topk_frac outside [0,1] or NaN, w_heads not in {1,H}, an
  *    unknown layout, alpha mode, output dtype or low-bit mode);
  *    SLA2_EUNSUPPORTED (a valid but unbuilt combination: d not in {64,128},
- *    bq not in {64,128}, bkv != 64, phi other than elu+1, fp8 with fp32
+ *    bq not in {64,128}, bkv != 64, phi softmax outside its path, fp8 with fp32
  *    inputs or with bq or d other than 128, more than 65535 heads or a number of blocks outside the limits
  *    below); SLA2_EWORKSPACE (ws_bytes smaller than sla2_workspace_bytes);
  *    SLA2_EHIP (a HIP launch error, reported right after the launch;
@@ -67,8 +71,11 @@ typedef enum {
 
 typedef enum { SLA2_F32 = 0, SLA2_BF16 = 1 } sla2_dtype;
 
-/* feature map of the linear branch: elu(x) + 1, elementwise on raw Q and K */
-typedef enum { SLA2_PHI_ELU1 = 0 } sla2_phi;
+/* feature map of the linear branch: elu(x) + 1, elementwise on raw Q and K,
+ * or the softmax of each raw Q or K row over its d channels (the SLA notes'
+ * training section picks softmax; SLA2_PHI_SOFTMAX needs bf16, d = 128 and
+ * bq = 128, and is not taken by sla2_forward_fp8) */
+typedef enum { SLA2_PHI_ELU1 = 0, SLA2_PHI_SOFTMAX = 1 } sla2_phi;
 
 /* memory layout of Q, K, V and O */
 typedef enum { SLA2_LAYOUT_BHND = 0, SLA2_LAYOUT_BNHD = 1 } sla2_layout;
@@ -89,7 +96,12 @@ typedef enum {
 } sla2_lowbit;
 
 /* operations, for sla2_workspace_bytes */
-typedef enum { SLA2_OP_ROUTE = 0, SLA2_OP_FORWARD = 1, SLA2_OP_FORWARD_FP8 = 2 } sla2_op;
+typedef enum {
+    SLA2_OP_ROUTE = 0,         /* sla2_route, sla1_route     */
+    SLA2_OP_FORWARD = 1,       /* sla2_forward               */
+    SLA2_OP_FORWARD_FP8 = 2,   /* sla2_forward_fp8           */
+    SLA2_OP_SLA1_FORWARD = 3   /* sla1_forward               */
+} sla2_op;
 
 typedef struct {
     int32_t B, H, N, d;  /* batch, heads, tokens, head dim (64 or 128)       */
@@ -239,6 +251,64 @@ sla2_status sla2_timing_start(int32_t max_launches);
 sla2_status sla2_timing_stop(float* total_ms, int32_t* launches, int32_t n_kinds);
 int32_t sla2_kernel_kinds(void);
 const char* sla2_kernel_name(int32_t kind);
+
+/*
+ * SLA (v1) compatibility ("SLA: Beyond Sparsity ..." notes: key design 2,
+ * the three-way block classification; key design 3, the linear branch over
+ * the marginal blocks and O = O_s + Proj(O_l); training section: phi =
+ * softmax, k_h = 5 %, k_l = 10 %).  Same problem struct: topk_frac is k_h %,
+ * low_frac (an argument) is k_l %, problem.phi picks the feature map;
+ * w_heads applies to W_p; alpha_mode and lowbit are not used.
+ *
+ * sla1_num_negligible -- k_l = clamp(ceil(low_frac * T_kv - 1e-6), 0,
+ * T_kv - k_h), k_h = sla2_topk(p).  -1 if the problem is invalid or low_frac
+ * is outside [0,1].
+ */
+int32_t sla1_num_negligible(const sla2_problem* p, float low_frac);
+
+/*
+ * sla1_route -- ternary router.  Pools as sla2_route but without
+ * projections (P_c = softmax(Qbar Kbar^T / sqrt(d)) keeps the row order of
+ * the plain product Qbar . Kbar, computed in fp64).  One total order per row:
+ * score descending, then block index ascending; its first k_h blocks are
+ * critical, its last k_l negligible (so ties at the negligible cut drop the
+ * higher index), the rest marginal.
+ * In : Q, K (dtype, problem.layout).
+ * Out: crit_idx [B,H,T_q,k_h] and negl_idx [B,H,T_q,k_l] int32, rows
+ *      ascending (either may be NULL when its count is 0); block_mask
+ *      [B,H,T_q,T_kv] int8 stored as uint8: 1 critical, 0 marginal, 0xFF (-1)
+ *      negligible, or NULL.
+ * ws : sla2_workspace_bytes(p, SLA2_OP_ROUTE) bytes.
+ * Errors as sla2_route; low_frac outside [0,1] or NaN is SLA2_EINVAL.
+ */
+sla2_status sla1_route(const sla2_problem* p, const void* Q, const void* K, float low_frac,
+                       int32_t* crit_idx, int32_t* negl_idx, uint8_t* block_mask, void* ws,
+                       size_t ws_bytes, void* stream);
+
+/*
+ * sla1_forward -- SLA (v1) forward.  Requires dtype == SLA2_BF16, d == 128
+ * and bq == 128 (SLA2_EUNSUPPORTED otherwise; the notes run v1 with b_q =
+ * 64, this build's matrix-core kernel tiles 128 queries).
+ *   O_s: the sparse branch of sla2_forward over the critical blocks.
+ *   O_l: phi(Q_t) H_i / (phi(Q_t) . Z_i) with H_i, Z_i summed over the
+ *        marginal blocks (neither critical nor negligible), evaluated as the
+ *        totals minus the critical and the negligible blocks; O_l = 0 when no
+ *        block is marginal.
+ *   O  = O_s + O_l W_p[h'] (Proj(x) = x W_p, W_p row-major [d][d], no bias;
+ *        h' = 0 if w_heads == 1, else h).  O_l enters the projection on the
+ *        fp16 matrix cores as the sum of two fp16 terms (high part + rest),
+ *        W_p rounded to fp16.
+ * In : Q, K, V (dtype, problem.layout); crit_idx / negl_idx from sla1_route
+ *      (ascending rows; NULL allowed when the count is 0); Wp [w_heads,d,d]
+ *      fp32.
+ * Out: O in problem.layout, fp32 or bf16 (problem.out_dtype).
+ * ws : sla2_workspace_bytes(p, SLA2_OP_SLA1_FORWARD) bytes.
+ * Precision as sla2_forward's bf16 path; phi = softmax is evaluated in fp32
+ * (max-subtracted) and carried in fp16.
+ */
+sla2_status sla1_forward(const sla2_problem* p, const void* Q, const void* K, const void* V,
+                         const int32_t* crit_idx, const int32_t* negl_idx, float low_frac,
+                         const float* Wp, void* O, void* ws, size_t ws_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -26,6 +26,14 @@
 // Epilogue: O_l^T = H_i^T phi(Q)^T / (phi(Q) . Z_i), O = alpha O_s +
 // (1 - alpha) O_l ("SLA2 深度解读" 04).
 //
+// PHISM: phi is the softmax of each row over its 128 channels (the block
+// summaries pass applies the same map to K).  V1 (SLA v1, "SLA: Beyond
+// Sparsity ..." notes, key designs 2 and 3): the selected blocks are the
+// critical ones, the negligible blocks are subtracted from H and Z as well
+// (a second loop over their V^T and phi(K)^T tiles, G products only), and
+// O = O_s + O_l W_p, the projection on the fp16 matrix cores with O_l split
+// into a high fp16 part and the fp16 rest.
+//
 // K (or Khat) and V^T tiles arrive by direct-to-LDS loads, K two tiles
 // ahead (three stages), V^T one tile ahead (two stages); the phi(K)^T slice
 // and z_j of the next tile are loaded into registers once the current tile's
@@ -144,7 +152,7 @@ __device__ inline void issue_v8(char* v8st, rsrc_t rv8, int j, int w, uint32_t v
 }
 
 // QK: 0 = bf16 Q K^T, 1 = e4m3 codes, 2 = int8 codes
-template <bool LIN, int QK, bool LOWV>
+template <bool LIN, int QK, bool LOWV, bool PHISM, bool V1>
 __global__ __launch_bounds__(256, 2) void fused128_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ vt, const uint16_t* __restrict__ pkt,
@@ -154,8 +162,10 @@ __global__ __launch_bounds__(256, 2) void fused128_kernel(
     const uint8_t* __restrict__ khat, const float* __restrict__ sq,
     const float* __restrict__ sk, const uint8_t* __restrict__ vhat,
     const float* __restrict__ sv, void* __restrict__ O, int N, int Tq, int Tkv, int k,
-    int H, Strides st, int alpha_qblock, int out_bf16) {
+    int H, Strides st, int alpha_qblock, int out_bf16, const int32_t* __restrict__ negl, int kl,
+    const uint16_t* __restrict__ wpf, int w_heads) {
     constexpr bool LOWBIT = QK != 0;
+    static_assert(!(PHISM || V1) || (QK == 0 && !LOWV), "softmax phi and v1: bf16 path only");
     static_assert(LOWBIT || !LOWV, "quantised V only with the low-bit Q K^T");
     // V^T in fp16 feeds P V, and G (the linear branch) with LOWV
     constexpr bool kV16 = !LOWV || LIN;
@@ -494,6 +504,38 @@ __global__ __launch_bounds__(256, 2) void fused128_kernel(
     if (r + 1 < k) step(r++, std::true_type{}, std::false_type{});
     if (r < k) step(r, std::false_type{}, std::false_type{});
 
+    // V1: subtract the negligible blocks from G and z as well (their V^T
+    // tiles through the two V stages, phi(K)^T and z_j one tile ahead)
+    if constexpr (V1 && LIN) {
+        if (kl > 0) {
+            const int32_t* nsel = negl + ((size_t)bh * Tq + qb) * kl;
+            wg_barrier();  // every wave is done with the tile stages
+            issue_v(vbase, rv, nsel[0], w, toff);
+            asm volatile("" ::: "memory");
+            load_pk(nsel[0]);
+            asm volatile("" ::: "memory");
+            for (int rn = 0; rn < kl; ++rn) {
+                wait_vmcnt<5>();  // V_rn landed (issued after it: phi(K_rn)^T, z_rn)
+                wg_barrier();     // ... for every wave; all are done with tile rn-1
+                if (rn + 1 < kl) issue_v(vbase + ((rn + 1) & 1) * kVT, rv, nsel[rn + 1], w, toff);
+                const char* vst = vbase + (rn & 1) * kVT;
+#pragma unroll
+                for (int kq = 0; kq < 4; ++kq)
+#pragma unroll
+                    for (int mt = 0; mt < 4; ++mt) {
+                        const int erow = 32 * mt + l32;
+                        const f16x8 a = *reinterpret_cast<const f16x8*>(
+                            vst + erow * 128 + (((2 * kq + hl) ^ ((erow >> 1) & 7)) << 4));
+                        g[mt] = mfma_f16(a, pk[kq], g[mt]);
+                    }
+                zacc += hl == 0 ? zj : 0.0f;
+                asm volatile("" ::: "memory");
+                if (rn + 1 < kl) load_pk(nsel[rn + 1]);
+                asm volatile("" ::: "memory");
+            }
+        }
+    }
+
     // ---- epilogue
     const float l_all = l_part + __shfl_xor(l_part, 32);
     const float inv_l = (k > 0 && l_all > 0.0f) ? 1.0f / l_all : 0.0f;
@@ -535,6 +577,23 @@ __global__ __launch_bounds__(256, 2) void fused128_kernel(
         }
         f16x8 pq[8];
         float den = 0.0f;
+        // softmax phi: max and 1 / sum exp over the query's 128 channels (64
+        // in this lane, 64 in its partner lane ^ 32)
+        float qmax = 0.0f, qinv = 1.0f;
+        if (PHISM) {
+            qmax = -INFINITY;
+#pragma unroll
+            for (int ks = 0; ks < 8; ++ks)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) qmax = fmaxf(qmax, (float)qraw[ks][e]);
+            qmax = fmaxf(qmax, __shfl_xor(qmax, 32));
+            float qs = 0.0f;
+#pragma unroll
+            for (int ks = 0; ks < 8; ++ks)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) qs += __expf((float)qraw[ks][e] - qmax);
+            qinv = 1.0f / (qs + __shfl_xor(qs, 32));
+        }
 #pragma unroll
         for (int ks = 0; ks < 8; ++ks) {
             const float4 z0 = *reinterpret_cast<const float4*>(sZ + 16 * ks + 8 * hl);
@@ -542,7 +601,8 @@ __global__ __launch_bounds__(256, 2) void fused128_kernel(
             const float zz[8] = {z0.x, z0.y, z0.z, z0.w, z1.x, z1.y, z1.z, z1.w};
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                const float p = phi_fast((float)qraw[ks][e]);
+                const float p = PHISM ? __expf((float)qraw[ks][e] - qmax) * qinv
+                                      : phi_fast((float)qraw[ks][e]);
                 pq[ks][e] = (_Float16)p;
                 den = fmaf(p, zz[e], den);
             }
@@ -559,6 +619,50 @@ __global__ __launch_bounds__(256, 2) void fused128_kernel(
                 ol[mt] = mfma_f16(a, pq[ks], ol[mt]);
             }
         }
+    }
+    if constexpr (V1) {
+        // O = O_s + O_l W_p: out^T (128 channels x 32 queries) = W_p^T O_l^T,
+        // B = O_l^T from the accumulators (k-step 2 mt + h takes entries
+        // 8h .. 8h+7 of m-tile mt; the fragments of W_p^T follow the same
+        // k order), O_l as fp16 high part + fp16 rest
+        f16x8 bhi[8], blo[8];
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float x = LIN ? ol[mt][8 * h + e] * inv_den : 0.0f;
+                    const _Float16 hi = (_Float16)x;
+                    bhi[2 * mt + h][e] = hi;
+                    blo[2 * mt + h][e] = (_Float16)(x - (float)hi);
+                }
+        const uint16_t* wf = wpf + (w_heads == 1 ? 0 : (size_t)(bh % H) * 128 * 128);
+        const size_t orow = head_base(st, bh, H) + (size_t)(valid_q ? tq : 0) * st.t;
+#pragma unroll
+        for (int mo = 0; mo < 4; ++mo) {
+            f32x16 pr = zero16();
+            if (LIN) {
+#pragma unroll
+                for (int ks = 0; ks < 8; ++ks) {
+                    const f16x8 a = *reinterpret_cast<const f16x8*>(
+                        wf + ((size_t)(mo * 8 + ks) * 64 + lane) * 8);
+                    pr = mfma_f16(a, bhi[ks], pr);
+                    pr = mfma_f16(a, blo[ks], pr);
+                }
+            }
+            if (valid_q) {
+#pragma unroll
+                for (int i4 = 0; i4 < 4; ++i4) {
+                    float v[4];
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) v[c] = o[mo][4 * i4 + c] * inv_l + pr[4 * i4 + c];
+                    store_out4(O, orow + 32 * mo + 8 * i4 + 4 * hl, v[0], v[1], v[2], v[3],
+                               out_bf16);
+                }
+            }
+        }
+        return;
     }
     if (valid_q) {
         const float a_h = alpha_of(alpha, bh, H, qb, Tq, alpha_qblock);
@@ -587,14 +691,34 @@ __global__ __launch_bounds__(256, 2) void fused128_kernel(
     }
 }
 
+__global__ __launch_bounds__(256) void wp_frag_kernel(const float* __restrict__ Wp,
+                                                     uint16_t* __restrict__ wpf) {
+    // fragment (m-tile mo, k-step ks, lane, e) = W_p[dd][m]: m = 32 mo +
+    // lane % 32, dd = 32 (ks / 2) + 16 (ks % 2) + 8 (e / 4) + 4 (lane / 32) + e % 4
+    const float* W = Wp + (size_t)blockIdx.x * 128 * 128;
+    uint16_t* out = wpf + (size_t)blockIdx.x * 128 * 128;
+    for (int x = threadIdx.x; x < 128 * 128; x += 256) {
+        const int e = x & 7, ln = (x >> 3) & 63, ks = (x >> 9) & 7, mo = x >> 12;
+        const int m = 32 * mo + (ln & 31);
+        const int dd = 32 * (ks >> 1) + 16 * (ks & 1) + 8 * (e >> 2) + 4 * (ln >> 5) + (e & 3);
+        const _Float16 h = (_Float16)W[(size_t)dd * 128 + m];
+        out[x] = __builtin_bit_cast(uint16_t, h);
+    }
+}
+
 }  // namespace
+
+hipError_t launch_wp_frag(const Dims& D, const float* Wp, const FwdWS& ws, hipStream_t s) {
+    wp_frag_kernel<<<dim3((unsigned)D.w_heads), 256, 0, s>>>(Wp, ws.wpf);
+    return hipGetLastError();
+}
 
 hipError_t launch_fused128(const Dims& D, const void* Q, const void* K, const int32_t* idx,
                            const float* alpha, void* O, const FwdWS& ws, bool lowbit,
-                           hipStream_t s) {
+                           hipStream_t s, const int32_t* negl) {
     // one work-group per (head, query block), Tq padded to a multiple of 8
     const dim3 g((unsigned)(((D.Tq + 7) / 8) * 8 * D.BH), 1);
-    const bool lin = D.k < D.Tkv;
+    const bool lin = D.k + (D.v1 ? D.kl : 0) < D.Tkv;
     const uint16_t* q = (const uint16_t*)Q;
     const uint16_t* kk = (const uint16_t*)K;
     const uint8_t* qh = lowbit ? ws.qhat : nullptr;
@@ -603,16 +727,31 @@ hipError_t launch_fused128(const Dims& D, const void* Q, const void* K, const in
     const float* sk = lowbit ? ws.sk : nullptr;
     const bool lowv = lowbit && D.lowbit_v;
     const bool i8 = lowbit && D.int8_qk;
-    auto kern = !lowbit ? (lin ? fused128_kernel<true, 0, false> : fused128_kernel<false, 0, false>)
-                : i8 ? (!lowv ? (lin ? fused128_kernel<true, 2, false> : fused128_kernel<false, 2, false>)
-                              : (lin ? fused128_kernel<true, 2, true> : fused128_kernel<false, 2, true>))
-                : !lowv ? (lin ? fused128_kernel<true, 1, false> : fused128_kernel<false, 1, false>)
-                        : (lin ? fused128_kernel<true, 1, true> : fused128_kernel<false, 1, true>);
-    const KernelKind kind = !lowbit ? K_FUSED_MFMA : i8 ? K_FUSED_I8 : K_FUSED_FP8;
+#define F128(L, Q, V) fused128_kernel<L, Q, V, false, false>
+    auto kern = !lowbit ? (lin ? F128(true, 0, false) : F128(false, 0, false))
+                : i8 ? (!lowv ? (lin ? F128(true, 2, false) : F128(false, 2, false))
+                              : (lin ? F128(true, 2, true) : F128(false, 2, true)))
+                : !lowv ? (lin ? F128(true, 1, false) : F128(false, 1, false))
+                        : (lin ? F128(true, 1, true) : F128(false, 1, true));
+#undef F128
+    if (!lowbit && (D.phi_sm || D.v1)) {
+        const bool sm = D.phi_sm, v1 = D.v1;
+        kern = lin ? (sm ? (v1 ? fused128_kernel<true, 0, false, true, true>
+                               : fused128_kernel<true, 0, false, true, false>)
+                         : (v1 ? fused128_kernel<true, 0, false, false, true>
+                               : fused128_kernel<true, 0, false, false, false>))
+                   : (sm ? (v1 ? fused128_kernel<false, 0, false, true, true>
+                               : fused128_kernel<false, 0, false, true, false>)
+                         : (v1 ? fused128_kernel<false, 0, false, false, true>
+                               : fused128_kernel<false, 0, false, false, false>));
+    }
+    const KernelKind kind = D.v1 ? K_FUSED_SLA1
+                            : !lowbit ? K_FUSED_MFMA : i8 ? K_FUSED_I8 : K_FUSED_FP8;
     timing_before(s, kind);
     kern<<<g, 256, 0, s>>>(q, kk, ws.vt, ws.pkt, ws.zb, idx, alpha, ws.htot, ws.ztot, qh, kh, sq,
                            sk, lowv ? ws.vhat : nullptr, lowv ? ws.sv : nullptr, O, D.N, D.Tq,
-                           D.Tkv, D.k, D.H, D.st, D.alpha_qblock, D.out_bf16);
+                           D.Tkv, D.k, D.H, D.st, D.alpha_qblock, D.out_bf16, negl,
+                           D.v1 ? D.kl : 0, D.v1 ? ws.wpf : nullptr, D.w_heads);
     timing_after(s, kind);
     return hipGetLastError();
 }

@@ -7,6 +7,8 @@
 //    with bits 2 and 3 swapped), and the per-block z_j = colsum phi(K_j); it
 //    accumulates h = sum_j phi(K_j)^T V_j and z = sum_j z_j on the matrix
 //    cores into per-chunk partials (reduced in a fixed order afterwards).
+//    phi is elu + 1, or (phi_sm) the softmax of each K row over its D
+//    channels in fp32 (the SLA notes' feature map), max-subtracted.
 //    Linear-branch block summaries: SLA notes, key design 4 (h_j =
 //    phi(K_j)^T V_j, z_j).
 // 2) fused_mfma (d = 64): per (head, query block of 128) a work-group of 4
@@ -50,11 +52,12 @@ template <int D>
 __global__ __launch_bounds__(256) void summaries_mfma_kernel(
     const uint16_t* __restrict__ K, const uint16_t* __restrict__ V, uint16_t* __restrict__ vt,
     uint16_t* __restrict__ pkt, float* __restrict__ zb, float* __restrict__ hpart,
-    float* __restrict__ zpart, int N, int Tkv, int nch, int H, Strides st) {
+    float* __restrict__ zpart, int N, int Tkv, int nch, int H, Strides st, int phi_sm) {
     constexpr int NT = D / 32;
     constexpr int TPW = NT * NT / 4;  // h^T tiles per wave
     __shared__ __attribute__((aligned(16))) char sV[D * kTPitch];
     __shared__ __attribute__((aligned(16))) char sP[D * kTPitch];
+    __shared__ float sRed[2][4][64];  // softmax phi: per-wave row max / sum
     // wave index as a scalar: conditions on it must be wave-uniform branches
     // (matrix instructions ignore EXEC, so they may never sit under a lane mask)
     const int t = threadIdx.x, lane = t & 63, l32 = lane & 31, hl = lane >> 5;
@@ -78,25 +81,59 @@ __global__ __launch_bounds__(256) void summaries_mfma_kernel(
         __syncthreads();
         // load 64 tokens x D channels; lane -> token, wave + pass -> channel group
         constexpr int CG = D / 8;
+        constexpr int NP = CG / 4;
+        const int u = lane;
+        const int tok = j * 64 + u;
+        const bool ok = tok < N;
+        uint4 kvs[NP], vvs[NP];
 #pragma unroll
-        for (int pass = 0; pass < CG / 4; ++pass) {
+        for (int pass = 0; pass < NP; ++pass) {
             const int cg = w + 4 * pass;
-            const int u = lane;
-            const int tok = j * 64 + u;
-            uint4 kv = make_uint4(0, 0, 0, 0), vv = make_uint4(0, 0, 0, 0);
-            const bool ok = tok < N;
+            kvs[pass] = make_uint4(0, 0, 0, 0);
+            vvs[pass] = make_uint4(0, 0, 0, 0);
             if (ok) {
-                kv = *reinterpret_cast<const uint4*>(Kh + (size_t)tok * st.t + cg * 8);
-                vv = *reinterpret_cast<const uint4*>(Vh + (size_t)tok * st.t + cg * 8);
+                kvs[pass] = *reinterpret_cast<const uint4*>(Kh + (size_t)tok * st.t + cg * 8);
+                vvs[pass] = *reinterpret_cast<const uint4*>(Vh + (size_t)tok * st.t + cg * 8);
             }
-            const unsigned kw[4] = {kv.x, kv.y, kv.z, kv.w};
-            const unsigned vw[4] = {vv.x, vv.y, vv.z, vv.w};
+        }
+        // softmax phi: row max and 1 / sum exp over the D channels of token u
+        // (this wave holds NP groups of 8; the four waves are combined in LDS)
+        float rmax = 0.0f, rinv = 1.0f;
+        if (phi_sm) {
+            float m = -INFINITY;
+#pragma unroll
+            for (int pass = 0; pass < NP; ++pass) {
+                const unsigned kw[4] = {kvs[pass].x, kvs[pass].y, kvs[pass].z, kvs[pass].w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) m = fmaxf(m, fmaxf(bf16_lo(kw[e]), bf16_hi(kw[e])));
+            }
+            sRed[0][w][u] = m;
+            __syncthreads();
+            rmax = fmaxf(fmaxf(sRed[0][0][u], sRed[0][1][u]), fmaxf(sRed[0][2][u], sRed[0][3][u]));
+            float sum = 0.0f;
+#pragma unroll
+            for (int pass = 0; pass < NP; ++pass) {
+                const unsigned kw[4] = {kvs[pass].x, kvs[pass].y, kvs[pass].z, kvs[pass].w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    sum += __expf(bf16_lo(kw[e]) - rmax) + __expf(bf16_hi(kw[e]) - rmax);
+            }
+            sRed[1][w][u] = sum;
+            __syncthreads();
+            rinv = 1.0f / ((sRed[1][0][u] + sRed[1][1][u]) + (sRed[1][2][u] + sRed[1][3][u]));
+        }
+#pragma unroll
+        for (int pass = 0; pass < NP; ++pass) {
+            const int cg = w + 4 * pass;
+            const unsigned kw[4] = {kvs[pass].x, kvs[pass].y, kvs[pass].z, kvs[pass].w};
+            const unsigned vw[4] = {vvs[pass].x, vvs[pass].y, vvs[pass].z, vvs[pass].w};
             const int pos = perm_pos(u);
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 const float kf = (e & 1) ? bf16_hi(kw[e >> 1]) : bf16_lo(kw[e >> 1]);
                 const float vf = (e & 1) ? bf16_hi(vw[e >> 1]) : bf16_lo(vw[e >> 1]);
-                const _Float16 ph = ok ? (_Float16)phi_fast(kf) : (_Float16)0.0f;
+                const float pf = phi_sm ? __expf(kf - rmax) * rinv : phi_fast(kf);
+                const _Float16 ph = ok ? (_Float16)pf : (_Float16)0.0f;
                 const _Float16 vh = ok ? (_Float16)vf : (_Float16)0.0f;
                 const int c = cg * 8 + e;
                 *reinterpret_cast<_Float16*>(sP + c * kTPitch + pos * 2) = ph;
@@ -421,11 +458,11 @@ hipError_t launch_summaries_mfma(const Dims& D, const void* K, const void* V,
     if (D.d == 128)
         summaries_mfma_kernel<128><<<g, 256, 0, s>>>((const uint16_t*)K, (const uint16_t*)V,
                                                      ws.vt, ws.pkt, ws.zb, ws.hpart, ws.zpart,
-                                                     D.N, D.Tkv, nch, D.H, D.st);
+                                                     D.N, D.Tkv, nch, D.H, D.st, D.phi_sm);
     else
         summaries_mfma_kernel<64><<<g, 256, 0, s>>>((const uint16_t*)K, (const uint16_t*)V,
                                                     ws.vt, ws.pkt, ws.zb, ws.hpart, ws.zpart,
-                                                    D.N, D.Tkv, nch, D.H, D.st);
+                                                    D.N, D.Tkv, nch, D.H, D.st, D.phi_sm);
     timing_after(s, K_SUMM_MFMA);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

@@ -1,6 +1,8 @@
 // Router kernels: block mean-pool + projection, compressed score, hard top-k
 // ("SLA2 深度解读" section 05: Qbar = pool(Q), Kbar = pool(K),
-// P_c = proj_q(Qbar) proj_k(Kbar)^T, M_c = Top-k(k%, P_c)).
+// P_c = proj_q(Qbar) proj_k(Kbar)^T, M_c = Top-k(k%, P_c)).  The SLA (v1)
+// router ("SLA: Beyond Sparsity ..." notes, key design 2) pools without
+// projections and also marks the bottom k_l % of each row negligible.
 //
 // All arithmetic is fp64.  Block sums of <= 128 bf16 values are exact in
 // fp64, so the pooled means do not depend on summation order; the scores
@@ -30,7 +32,8 @@ __device__ inline void load8(const uint16_t* __restrict__ p, float* o) {
 }
 
 // One work-group per (head, block); blocks [0, Tq) are query blocks, the
-// rest KV blocks.  Output: proj(mean of the valid rows) in fp64.
+// rest KV blocks.  Output: proj(mean of the valid rows) in fp64, or the mean
+// itself when Wq and Wk are null (SLA v1).
 template <typename T>
 __global__ __launch_bounds__(256) void pool_project_kernel(
     const T* __restrict__ Q, const T* __restrict__ K, const float* __restrict__ Wq,
@@ -73,11 +76,15 @@ __global__ __launch_bounds__(256) void pool_project_kernel(
     if (threadIdx.x < d) {
         const int e = threadIdx.x;
         const int h = (int)(bh % H);
-        const float* W = (isq ? Wq : Wk) + (w_heads == 1 ? 0 : (size_t)h * d * d);
-        double y = 0.0;
-        for (int c = 0; c < d; ++c) y = fma(xbar[c], (double)W[(size_t)c * d + e], y);
         double* out = isq ? qt + ((size_t)bh * Tq + j) * d : kt + ((size_t)bh * Tkv + j) * d;
-        out[e] = y;
+        if (!Wq) {
+            out[e] = xbar[e];
+        } else {
+            const float* W = (isq ? Wq : Wk) + (w_heads == 1 ? 0 : (size_t)h * d * d);
+            double y = 0.0;
+            for (int c = 0; c < d; ++c) y = fma(xbar[c], (double)W[(size_t)c * d + e], y);
+            out[e] = y;
+        }
     }
 }
 
@@ -143,9 +150,12 @@ __device__ inline unsigned long long score_key(double v) {
 // One work-group per score row: radix-select the k-th largest key, then keep
 // every larger key and the lowest-index keys equal to it; indices are emitted
 // ascending.  Deterministic (counts only, no order-dependent arithmetic).
+// low: the k LAST blocks of the order (score descending, index ascending)
+// instead, i.e. the smallest scores with ties to the higher index; the mask
+// then gets 0xFF at those blocks and is left alone elsewhere.
 __global__ __launch_bounds__(256) void topk_kernel(const double* __restrict__ S, int Tq,
                                                    int Tkv, int k, int32_t* __restrict__ idx,
-                                                   uint8_t* __restrict__ mask) {
+                                                   uint8_t* __restrict__ mask, int low) {
     extern __shared__ unsigned long long keys[];  // [Tkv]
     __shared__ unsigned hist[256];
     __shared__ unsigned long long s_prefix;
@@ -158,14 +168,20 @@ __global__ __launch_bounds__(256) void topk_kernel(const double* __restrict__ S,
     uint8_t* mrow = mask ? mask + row * Tkv : nullptr;
     int32_t* irow = idx + row * k;
 
+    const uint8_t mark = low ? 0xFF : 1;
     if (k == Tkv) {  // everything selected
         for (int j = t; j < Tkv; j += 256) {
-            if (mrow) mrow[j] = 1;
+            if (mrow) mrow[j] = mark;
             irow[j] = j;
         }
         return;
     }
-    for (int j = t; j < Tkv; j += 256) keys[j] = score_key(srow[j]);
+    // low: keys inverted and stored at position Tkv-1-j, so that the scan
+    // below (positions ascending) meets equal keys from the higher index down
+    for (int j = t; j < Tkv; j += 256) {
+        if (low) keys[Tkv - 1 - j] = ~score_key(srow[j]);
+        else keys[j] = score_key(srow[j]);
+    }
 
     unsigned long long prefix = 0, pmask = 0;
     int kr = k;
@@ -246,8 +262,13 @@ __global__ __launch_bounds__(256) void topk_kernel(const double* __restrict__ S,
             sel_total += s_cnt[w];
         }
         if (j < Tkv) {
-            if (mrow) mrow[j] = sel ? 1 : 0;
-            if (sel) irow[sel_before + sel_rank] = j;
+            if (!low) {
+                if (mrow) mrow[j] = sel ? 1 : 0;
+                if (sel) irow[sel_before + sel_rank] = j;
+            } else if (sel) {  // position j is block Tkv-1-j; emit ascending
+                if (mrow) mrow[Tkv - 1 - j] = 0xFF;
+                irow[k - 1 - (sel_before + sel_rank)] = Tkv - 1 - j;
+            }
         }
         eq_base += eq_total;
         out_base += sel_total;
@@ -295,7 +316,49 @@ hipError_t launch_route(const Dims& D, const void* Q, const void* K, const float
     dim3 g3(D.Tq, (unsigned)D.BH);
     timing_before(s, K_TOPK);
     topk_kernel<<<g3, 256, sizeof(unsigned long long) * D.Tkv, s>>>(ws.S, D.Tq, D.Tkv, D.k,
-                                                                    idx, mask);
+                                                                    idx, mask, 0);
+    timing_after(s, K_TOPK);
+    return hipGetLastError();
+}
+
+hipError_t launch_route_v1(const Dims& D, const void* Q, const void* K, int kl, int32_t* crit,
+                           int32_t* negl, uint8_t* mask, const RouteWS& ws, hipStream_t s) {
+    if (D.k == 0 && kl == 0) {  // every block marginal
+        if (mask) {
+            const size_t n = (size_t)D.BH * D.Tq * D.Tkv;
+            const size_t nb = (n + 255) / 256;
+            timing_before(s, K_TOPK);
+            zero_mask_kernel<<<dim3((unsigned)(nb < 65535 ? nb : 65535)), 256, 0, s>>>(mask, n);
+            timing_after(s, K_TOPK);
+        }
+        return hipGetLastError();
+    }
+    dim3 g1(D.Tq + D.Tkv, (unsigned)D.BH);
+    timing_before(s, K_POOL_PROJECT);
+    if (D.dtype == SLA2_F32)
+        pool_project_kernel<float><<<g1, 256, 0, s>>>(
+            (const float*)Q, (const float*)K, nullptr, nullptr, ws.qt, ws.kt, D.N, D.d, D.bq,
+            D.bkv, D.Tq, D.Tkv, D.H, D.w_heads, D.st);
+    else
+        pool_project_kernel<uint16_t><<<g1, 256, 0, s>>>(
+            (const uint16_t*)Q, (const uint16_t*)K, nullptr, nullptr, ws.qt, ws.kt, D.N, D.d,
+            D.bq, D.bkv, D.Tq, D.Tkv, D.H, D.w_heads, D.st);
+    timing_after(s, K_POOL_PROJECT);
+    dim3 g2((D.Tkv + 63) / 64, (D.Tq + 63) / 64, (unsigned)D.BH);
+    timing_before(s, K_SCORE);
+    score_kernel<<<g2, 256, 0, s>>>(ws.qt, ws.kt, ws.S, D.Tq, D.Tkv, D.d);
+    timing_after(s, K_SCORE);
+    dim3 g3(D.Tq, (unsigned)D.BH);
+    const size_t sh = sizeof(unsigned long long) * D.Tkv;
+    timing_before(s, K_TOPK);
+    if (D.k > 0) {
+        topk_kernel<<<g3, 256, sh, s>>>(ws.S, D.Tq, D.Tkv, D.k, crit, mask, 0);
+    } else if (mask) {
+        const size_t n = (size_t)D.BH * D.Tq * D.Tkv;
+        const size_t nb = (n + 255) / 256;
+        zero_mask_kernel<<<dim3((unsigned)(nb < 65535 ? nb : 65535)), 256, 0, s>>>(mask, n);
+    }
+    if (kl > 0) topk_kernel<<<g3, 256, sh, s>>>(ws.S, D.Tq, D.Tkv, kl, negl, mask, 1);
     timing_after(s, K_TOPK);
     return hipGetLastError();
 }

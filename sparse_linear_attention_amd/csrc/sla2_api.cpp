@@ -37,12 +37,16 @@ static sla2_status make_dims(const sla2_problem* p, int op, Dims* D) {
         return SLA2_EINVAL;
     if (p->out_dtype != SLA2_F32 && p->out_dtype != SLA2_BF16) return SLA2_EINVAL;
     if (p->lowbit < SLA2_LOWBIT_QK || p->lowbit > SLA2_LOWBIT_I8QKV) return SLA2_EINVAL;
-    if (op < SLA2_OP_ROUTE || op > SLA2_OP_FORWARD_FP8) return SLA2_EINVAL;
+    if (op < SLA2_OP_ROUTE || op > SLA2_OP_SLA1_FORWARD) return SLA2_EINVAL;
     if (p->d != 64 && p->d != 128) return SLA2_EUNSUPPORTED;
     if (p->bq != 64 && p->bq != 128) return SLA2_EUNSUPPORTED;
     if (p->bkv != 64) return SLA2_EUNSUPPORTED;
-    if (p->phi != SLA2_PHI_ELU1) return SLA2_EUNSUPPORTED;
-    if (op == SLA2_OP_FORWARD_FP8 && (p->dtype != SLA2_BF16 || p->bq != 128 || p->d != 128))
+    if (p->phi != SLA2_PHI_ELU1 && p->phi != SLA2_PHI_SOFTMAX) return SLA2_EUNSUPPORTED;
+    const bool fast = p->dtype == SLA2_BF16 && p->bq == 128 && p->d == 128;
+    if ((op == SLA2_OP_FORWARD_FP8 || op == SLA2_OP_SLA1_FORWARD) && !fast)
+        return SLA2_EUNSUPPORTED;
+    // softmax phi: the bf16 d = 128, bq = 128 kernels only (routing ignores phi)
+    if (p->phi == SLA2_PHI_SOFTMAX && (op == SLA2_OP_FORWARD_FP8 || (op != SLA2_OP_ROUTE && !fast)))
         return SLA2_EUNSUPPORTED;
     long bh = (long)p->B * p->H;
     if (bh > 65535) return SLA2_EUNSUPPORTED;
@@ -73,6 +77,9 @@ static sla2_status make_dims(const sla2_problem* p, int op, Dims* D) {
     D->out_bf16 = p->out_dtype == SLA2_BF16;
     D->lowbit_v = (p->lowbit & SLA2_LOWBIT_QKV) != 0;
     D->int8_qk = (p->lowbit & SLA2_LOWBIT_I8QK) != 0;
+    D->phi_sm = p->phi == SLA2_PHI_SOFTMAX;
+    D->v1 = op == SLA2_OP_SLA1_FORWARD;
+    D->kl = 0;
     // the fused kernels address a head's rows with 32-bit byte offsets
     if ((double)p->N * D->st.t * 4.0 >= 2147483648.0) return SLA2_EUNSUPPORTED;
     return SLA2_OK;
@@ -127,6 +134,8 @@ size_t layout_forward(const Dims& D, int op, char* base, FwdWS* ws) {
             w.sv = carve<float>(base, off, 4 * bh * d);
         }
     }
+    if (op == SLA2_OP_SLA1_FORWARD)
+        w.wpf = carve<uint16_t>(base, off, 2 * (size_t)D.w_heads * d * d);
     if (ws) *ws = w;
     return align256(off);
 }
@@ -155,7 +164,7 @@ const char* kKindNames[K_NUM_KINDS] = {
     "pool_project", "score",       "topk_select", "summaries_valu",
     "summaries_reduce", "fused_valu", "summaries_mfma", "fused_mfma",
     "quant_mean",   "quant_fp8",   "fused_fp8",  "quant_v_fp8",
-    "quant_i8",     "fused_i8",
+    "quant_i8",     "fused_i8",    "fused_sla1",
 };
 }  // namespace
 
@@ -324,6 +333,66 @@ SLA2_API sla2_status sla2_quantize_v_fp8(const sla2_problem* p, const void* V, u
     layout_forward(D, SLA2_OP_FORWARD_FP8, (char*)ws, &w);
     w.sv = sV;
     hipError_t e = launch_quantize_v_rows(D, V, Vhat, w, (hipStream_t)stream);
+    return e == hipSuccess ? SLA2_OK : SLA2_EHIP;
+}
+
+// ---------------------------------------------------------------------------
+// SLA (v1) compatibility
+// ---------------------------------------------------------------------------
+// k_l = clamp(ceil(low_frac * T_kv - 1e-6), 0, T_kv - k_h); -1 if low_frac is bad
+static int low_of(const Dims& D, float low_frac) {
+    if (!(low_frac >= 0.0f && low_frac <= 1.0f)) return -1;
+    double k = ceil((double)low_frac * (double)D.Tkv - 1e-6);
+    if (k < 0) k = 0;
+    if (k > D.Tkv - D.k) k = D.Tkv - D.k;
+    return (int)k;
+}
+
+SLA2_API int32_t sla1_num_negligible(const sla2_problem* p, float low_frac) {
+    Dims D;
+    if (make_dims(p, SLA2_OP_ROUTE, &D) != SLA2_OK) return -1;
+    return low_of(D, low_frac);
+}
+
+SLA2_API sla2_status sla1_route(const sla2_problem* p, const void* Q, const void* K,
+                                float low_frac, int32_t* crit_idx, int32_t* negl_idx,
+                                uint8_t* block_mask, void* ws, size_t ws_bytes, void* stream) {
+    Dims D;
+    sla2_status st = make_dims(p, SLA2_OP_ROUTE, &D);
+    if (st != SLA2_OK) return st;
+    const int kl = low_of(D, low_frac);
+    if (kl < 0) return SLA2_EINVAL;
+    if (!ok_ptr(Q) || !ok_ptr(K)) return SLA2_EINVAL;
+    if (D.k > 0 && !ok_ptr(crit_idx)) return SLA2_EINVAL;
+    if (kl > 0 && !ok_ptr(negl_idx)) return SLA2_EINVAL;
+    if (block_mask && !aligned(block_mask, 16)) return SLA2_EINVAL;
+    if ((st = check_ws(D, SLA2_OP_ROUTE, ws, ws_bytes)) != SLA2_OK) return st;
+    RouteWS w;
+    layout_route(D, (char*)ws, &w);
+    hipError_t e = launch_route_v1(D, Q, K, kl, crit_idx, negl_idx, block_mask, w,
+                                   (hipStream_t)stream);
+    return e == hipSuccess ? SLA2_OK : SLA2_EHIP;
+}
+
+SLA2_API sla2_status sla1_forward(const sla2_problem* p, const void* Q, const void* K,
+                                  const void* V, const int32_t* crit_idx,
+                                  const int32_t* negl_idx, float low_frac, const float* Wp,
+                                  void* O, void* ws, size_t ws_bytes, void* stream) {
+    Dims D;
+    sla2_status st = make_dims(p, SLA2_OP_SLA1_FORWARD, &D);
+    if (st != SLA2_OK) return st;
+    D.kl = low_of(D, low_frac);
+    if (D.kl < 0) return SLA2_EINVAL;
+    if (!ok_ptr(Q) || !ok_ptr(K) || !ok_ptr(V) || !ok_ptr(Wp) || !ok_ptr(O)) return SLA2_EINVAL;
+    if (D.k > 0 && !ok_ptr(crit_idx)) return SLA2_EINVAL;
+    if (D.kl > 0 && !ok_ptr(negl_idx)) return SLA2_EINVAL;
+    if ((st = check_ws(D, SLA2_OP_SLA1_FORWARD, ws, ws_bytes)) != SLA2_OK) return st;
+    FwdWS w;
+    layout_forward(D, SLA2_OP_SLA1_FORWARD, (char*)ws, &w);
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t e = launch_summaries_mfma(D, K, V, w, s);
+    if (e == hipSuccess) e = launch_wp_frag(D, Wp, w, s);
+    if (e == hipSuccess) e = launch_fused128(D, Q, K, crit_idx, nullptr, O, w, false, s, negl_idx);
     return e == hipSuccess ? SLA2_OK : SLA2_EHIP;
 }
 

@@ -27,6 +27,7 @@ enum KernelKind {
     K_QUANT_V,
     K_QUANT_I8,
     K_FUSED_I8,
+    K_FUSED_SLA1,
     K_NUM_KINDS
 };
 
@@ -52,6 +53,9 @@ struct Dims {
     int out_bf16;        // O is bf16 (else fp32)
     int lowbit_v;        // the low-bit forward quantises V too
     int int8_qk;         // the low-bit forward takes int8 Q/K codes (else e4m3)
+    int phi_sm;          // phi = softmax over the channels of a row (else elu + 1)
+    int v1;              // SLA (v1) forward: ternary blocks, O = O_s + O_l W_p
+    int kl;              // v1: negligible blocks per query block
 };
 
 // Four consecutive outputs (element offset off, a multiple of 4) as fp32, or
@@ -117,6 +121,8 @@ struct FwdWS {
                      // of the e4m3 P V product's k operand (see fused128.hip)
     float* vmax;     // [BH][ceil(N/1024)][d] partial max |V|
     float* sv;       // [BH][d]
+    // SLA (v1): W_p as fp16 A-operand fragments of the projection product
+    uint16_t* wpf;   // [w_heads][4 m-tiles][8 k-steps][64 lanes][8]
 };
 
 // Lays out the workspace of `op` starting at `base` (may be null to size
@@ -136,6 +142,10 @@ void timing_after(hipStream_t s, int kind);
 hipError_t launch_route(const Dims& D, const void* Q, const void* K, const float* Wq,
                         const float* Wk, int32_t* idx, uint8_t* mask, const RouteWS& ws,
                         hipStream_t s);
+
+// SLA (v1) router: critical (top k) and negligible (bottom kl) blocks
+hipError_t launch_route_v1(const Dims& D, const void* Q, const void* K, int kl, int32_t* crit,
+                           int32_t* negl, uint8_t* mask, const RouteWS& ws, hipStream_t s);
 
 // fp32 path: VALU block summaries + VALU fused kernel
 hipError_t launch_forward_valu(const Dims& D, const void* Q, const void* K, const void* V,
@@ -159,7 +169,10 @@ hipError_t launch_quantize_fp8(const Dims& D, const void* Q, const void* K, cons
 hipError_t launch_quantize_v_rows(const Dims& D, const void* V, uint8_t* vhat_rows,
                                   const FwdWS& ws, hipStream_t s);
 // d = 128, b_q = 128 fused kernel (bf16, or the low-bit Q K^T with lowbit)
+// (D.v1: the SLA (v1) forward, negl = the negligible blocks, ws.wpf filled)
 hipError_t launch_fused128(const Dims& D, const void* Q, const void* K, const int32_t* idx,
                            const float* alpha, void* O, const FwdWS& ws, bool lowbit,
-                           hipStream_t s);
+                           hipStream_t s, const int32_t* negl = nullptr);
+// W_p [w_heads][d][d] fp32 -> ws.wpf (d = 128)
+hipError_t launch_wp_frag(const Dims& D, const float* Wp, const FwdWS& ws, hipStream_t s);
 }  // namespace sla2

@@ -15,8 +15,8 @@ LIB_PATH = os.path.join(PKG, "libsla2.so")
 
 OK, EINVAL, EUNSUPPORTED, EWORKSPACE, EHIP = range(5)
 F32, BF16 = 0, 1
-PHI_ELU1 = 0
-OP_ROUTE, OP_FORWARD, OP_FORWARD_FP8 = 0, 1, 2
+PHI_ELU1, PHI_SOFTMAX = 0, 1
+OP_ROUTE, OP_FORWARD, OP_FORWARD_FP8, OP_SLA1_FORWARD = 0, 1, 2, 3
 LAYOUT_BHND, LAYOUT_BNHD = 0, 1
 ALPHA_PER_HEAD, ALPHA_PER_QBLOCK = 0, 1
 LOWBIT_QK, LOWBIT_QKV, LOWBIT_I8QK, LOWBIT_I8QKV = 0, 1, 2, 3
@@ -67,6 +67,9 @@ def lib():
         L.sla2_timing_stop.argtypes = [vp, vp, C.c_int32]
         L.sla2_kernel_name.argtypes = [C.c_int32]
         L.sla2_kernel_name.restype = C.c_char_p
+        L.sla1_num_negligible.argtypes = [P, C.c_float]
+        L.sla1_route.argtypes = [P, vp, vp, C.c_float, vp, vp, vp, vp, C.c_size_t, vp]
+        L.sla1_forward.argtypes = [P, vp, vp, vp, vp, vp, C.c_float, vp, vp, vp, C.c_size_t, vp]
         _lib = L
     return _lib
 
@@ -74,7 +77,8 @@ def lib():
 EXPORTS = ("sla2_num_q_blocks", "sla2_num_kv_blocks", "sla2_topk", "sla2_workspace_bytes",
            "sla2_check", "sla2_status_str", "sla2_route", "sla2_forward", "sla2_forward_fp8",
            "sla2_quantize_fp8", "sla2_quantize_v_fp8", "sla2_timing_start", "sla2_timing_stop",
-           "sla2_kernel_kinds", "sla2_kernel_name")
+           "sla2_kernel_kinds", "sla2_kernel_name", "sla1_num_negligible", "sla1_route",
+           "sla1_forward")
 
 
 def _dtype(x):
@@ -170,6 +174,24 @@ def sla2_quantize_v_fp8(p, V, Vhat, sV, ws=None, stream=None):
                                      _stream(stream)), "sla2_quantize_v_fp8")
 
 
+def num_negligible(p: Problem, low_frac: float) -> int:
+    return int(lib().sla1_num_negligible(C.byref(p), float(low_frac)))
+
+
+def sla1_route(p, Q, K, low_frac, crit_idx, negl_idx, block_mask=None, ws=None, stream=None):
+    wp, wb = _ws(ws)
+    _raise(lib().sla1_route(C.byref(p), _ptr(Q), _ptr(K), float(low_frac), _ptr(crit_idx),
+                            _ptr(negl_idx), _ptr(block_mask), wp, wb, _stream(stream)),
+           "sla1_route")
+
+
+def sla1_forward(p, Q, K, V, crit_idx, negl_idx, low_frac, Wp, O, ws=None, stream=None):
+    wp, wb = _ws(ws)
+    _raise(lib().sla1_forward(C.byref(p), _ptr(Q), _ptr(K), _ptr(V), _ptr(crit_idx),
+                              _ptr(negl_idx), float(low_frac), _ptr(Wp), _ptr(O), wp, wb,
+                              _stream(stream)), "sla1_forward")
+
+
 def kernel_names():
     L = lib()
     return [L.sla2_kernel_name(i).decode() for i in range(L.sla2_kernel_kinds())]
@@ -213,6 +235,35 @@ def route(p: Problem, Q, K, Wq, Wk, want_mask=True, ws=None, stream=None):
         ws = workspace(p, OP_ROUTE, dev)
     sla2_route(p, Q, K, Wq, Wk, idx if k > 0 else None, mask, ws, stream)
     return idx, mask
+
+
+def route_v1(p: Problem, Q, K, low_frac, want_mask=True, ws=None, stream=None):
+    """Allocates outputs, runs sla1_route; returns (crit_idx, negl_idx, mask)."""
+    import torch
+    dev = Q.device
+    Tq, Tkv, kh, kl = num_q_blocks(p), num_kv_blocks(p), topk(p), num_negligible(p, low_frac)
+    crit = torch.empty((p.B, p.H, Tq, max(kh, 0)), dtype=torch.int32, device=dev)
+    negl = torch.empty((p.B, p.H, Tq, max(kl, 0)), dtype=torch.int32, device=dev)
+    mask = torch.empty((p.B, p.H, Tq, Tkv), dtype=torch.uint8, device=dev) if want_mask else None
+    if ws is None:
+        ws = workspace(p, OP_ROUTE, dev)
+    sla1_route(p, Q, K, low_frac, crit if kh > 0 else None, negl if kl > 0 else None, mask, ws,
+               stream)
+    return crit, negl, mask
+
+
+def forward_v1(p: Problem, Q, K, V, crit, negl, low_frac, Wp, ws=None, out=None, stream=None):
+    """Allocates O and the workspace if not given; runs sla1_forward."""
+    import torch
+    dev = Q.device
+    shape = (p.B, p.H, p.N, p.d) if p.layout == LAYOUT_BHND else (p.B, p.N, p.H, p.d)
+    dt = torch.float32 if p.out_dtype == F32 else torch.bfloat16
+    O = out if out is not None else torch.empty(shape, dtype=dt, device=dev)
+    if ws is None:
+        ws = workspace(p, OP_SLA1_FORWARD, dev)
+    sla1_forward(p, Q, K, V, crit if topk(p) > 0 else None,
+                 negl if num_negligible(p, low_frac) > 0 else None, low_frac, Wp, O, ws, stream)
+    return O
 
 
 def forward(p: Problem, Q, K, V, topk_idx, alpha, fp8=False, ws=None, out=None, stream=None):

@@ -20,7 +20,7 @@ HEADER = os.path.join(ROOT, "include", "sla2.h")
 def declared_functions():
     src = open(HEADER).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(sla2_[a-z0-9_]+)\s*\(", src)))
+    return sorted(set(re.findall(r"\b(sla[12]_[a-z0-9_]+)\s*\(", src)))
 
 
 def test_library_exports_every_declared_symbol():
@@ -77,7 +77,33 @@ def test_fp8_needs_bf16_and_bq128():
     assert S.check(p_ok(dtype=S.F32), S.OP_FORWARD_FP8) == S.EUNSUPPORTED
     assert S.check(p_ok(bq=64), S.OP_FORWARD_FP8) == S.EUNSUPPORTED
     assert S.check(p_ok(), S.OP_FORWARD_FP8) == S.OK
-    assert S.check(p_ok(phi=1), S.OP_FORWARD) == S.EUNSUPPORTED
+    # softmax phi: the bf16, d = 128, bq = 128 kernels only (routing ignores phi)
+    assert S.check(p_ok(phi=S.PHI_SOFTMAX), S.OP_FORWARD) == S.OK
+    assert S.check(p_ok(phi=S.PHI_SOFTMAX), S.OP_ROUTE) == S.OK
+    assert S.check(p_ok(phi=S.PHI_SOFTMAX, dtype=S.F32), S.OP_FORWARD) == S.EUNSUPPORTED
+    assert S.check(p_ok(phi=S.PHI_SOFTMAX, d=64), S.OP_FORWARD) == S.EUNSUPPORTED
+    assert S.check(p_ok(phi=S.PHI_SOFTMAX), S.OP_FORWARD_FP8) == S.EUNSUPPORTED
+    assert S.check(p_ok(phi=2), S.OP_FORWARD) == S.EUNSUPPORTED
+
+
+def test_sla1_counts_and_checks(orc):
+    """k_l as the oracle counts it; v1 forward needs the bf16 d = 128 bq = 128
+    path; its workspace adds the W_p fragments (32 KB per projection)."""
+    for N, kh, low in ((32760, 0.05, 0.10), (75600, 0.05, 0.10), (640, 0.7, 0.5), (640, 1.0, 0.3),
+                       (640, 0.0, 0.0), (1000, 0.2, 0.33)):
+        p = p_ok(N=N, topk_frac=kh)
+        want = orc.topk_low(orc.problem(1, 2, N, 128, 128, 64, kh, mode=1, low_frac=low))
+        assert S.num_negligible(p, low) == want
+    assert S.num_negligible(p_ok(), -0.1) == -1 and S.num_negligible(p_ok(), float("nan")) == -1
+    assert S.num_negligible(p_ok(B=0), 0.1) == -1
+    assert S.check(p_ok(), S.OP_SLA1_FORWARD) == S.OK
+    for kw in (dict(dtype=S.F32), dict(bq=64), dict(d=64)):
+        assert S.check(p_ok(**kw), S.OP_SLA1_FORWARD) == S.EUNSUPPORTED
+    assert S.check(p_ok(), 4) == S.EINVAL
+    for wh in (1, 2):
+        extra = S.workspace_bytes(p_ok(w_heads=wh), S.OP_SLA1_FORWARD) - S.workspace_bytes(
+            p_ok(w_heads=wh), S.OP_FORWARD)
+        assert extra == wh * 128 * 128 * 2
     assert S.check(p_ok(), 9) == S.EINVAL
 
 
@@ -138,6 +164,20 @@ def test_entry_points_validate_before_launching():
     f8 = S.workspace_bytes(p, S.OP_FORWARD_FP8)
     assert L.sla2_forward_fp8(C.byref(pf), good, good, good, good, good, good, good, f8, None) == S.EUNSUPPORTED
     assert L.sla2_quantize_fp8(C.byref(p), good, good, None, good, good, good, good, good, f8, None) == S.EINVAL
+    # v1 entry points
+    assert L.sla1_route(C.byref(p), good, good, C.c_float(0.1), good, None, None, good, ws_need,
+                        None) == S.EINVAL  # k_l > 0 needs negl_idx
+    assert L.sla1_route(C.byref(p), good, good, C.c_float(1.5), good, good, None, good, ws_need,
+                        None) == S.EINVAL
+    assert L.sla1_route(C.byref(p), good, good, C.c_float(0.1), good, good, None, good,
+                        ws_need - 256, None) == S.EWORKSPACE
+    v1w = S.workspace_bytes(p, S.OP_SLA1_FORWARD)
+    assert L.sla1_forward(C.byref(p), good, good, good, good, good, C.c_float(0.1), None, good,
+                          good, v1w, None) == S.EINVAL  # no W_p
+    assert L.sla1_forward(C.byref(p), good, good, good, good, good, C.c_float(0.1), good, good,
+                          good, fw, None) == S.EWORKSPACE
+    assert L.sla1_forward(C.byref(pf), good, good, good, good, good, C.c_float(0.1), good, good,
+                          good, v1w, None) == S.EUNSUPPORTED
     # idx may be null only when k == 0
     p0 = p_ok(topk_frac=0.0)
     assert L.sla2_route(C.byref(p), good, good, good, good, None, None, good, ws_need, None) == S.EINVAL
