@@ -140,6 +140,66 @@ __global__ __launch_bounds__(256) void score_kernel(const double* __restrict__ q
     }
 }
 
+// y = x W for the pooled rows of one (head, side): grid (row tiles of 64,
+// 2 d / 64, BH) with y = side * (d / 64) + column tile (side 0: queries
+// with Wq, 1: keys with Wk); 4x4 outputs per thread, fp64, each output
+// accumulated over c = 0 .. d-1 in order (the same rounding as a plain loop).
+__global__ __launch_bounds__(256) void proj_kernel(const double* __restrict__ xq,
+                                                   const double* __restrict__ xk,
+                                                   const float* __restrict__ Wq,
+                                                   const float* __restrict__ Wk,
+                                                   double* __restrict__ qt, double* __restrict__ kt,
+                                                   int Tq, int Tkv, int d, int H, int w_heads) {
+    __shared__ double As[16][65];
+    __shared__ double Bs[16][65];
+    const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
+    const long bh = blockIdx.z;
+    const int ct = d >> 6;
+    const int side = (int)blockIdx.y / ct;
+    const int rows = side ? Tkv : Tq;
+    const int i0 = blockIdx.x * 64, e0 = ((int)blockIdx.y % ct) * 64;
+    if (i0 >= rows) return;
+    const double* X = side ? xk + (size_t)bh * Tkv * d : xq + (size_t)bh * Tq * d;
+    const float* W = (side ? Wk : Wq) + (w_heads == 1 ? 0 : (size_t)(bh % H) * d * d);
+    double* Y = side ? kt + (size_t)bh * Tkv * d : qt + (size_t)bh * Tq * d;
+    double acc[4][4];
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int b = 0; b < 4; ++b) acc[a][b] = 0.0;
+    for (int k0 = 0; k0 < d; k0 += 16) {
+        for (int x = threadIdx.x; x < 1024; x += 256) {
+            const int row = x >> 4, kk = x & 15;
+            const int gi = i0 + row;
+            As[kk][row] = gi < rows ? X[(size_t)gi * d + k0 + kk] : 0.0;
+            const int col = x & 63, kr = x >> 6;
+            Bs[kr][col] = (double)W[(size_t)(k0 + kr) * d + e0 + col];
+        }
+        __syncthreads();
+#pragma unroll
+        for (int kk = 0; kk < 16; ++kk) {
+            double a[4], b[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                a[q] = As[kk][ty + 16 * q];
+                b[q] = Bs[kk][tx + 16 * q];
+            }
+#pragma unroll
+            for (int p = 0; p < 4; ++p)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) acc[p][q] = fma(a[p], b[q], acc[p][q]);
+        }
+        __syncthreads();
+    }
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        const int i = i0 + ty + 16 * p;
+        if (i >= rows) continue;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) Y[(size_t)i * d + e0 + tx + 16 * q] = acc[p][q];
+    }
+}
+
 // Order-preserving map of an fp64 score to an unsigned key (-0 -> +0 first).
 __device__ inline unsigned long long score_key(double v) {
     if (v == 0.0) v = 0.0;
@@ -296,16 +356,20 @@ hipError_t launch_route(const Dims& D, const void* Q, const void* K, const float
         }
         return hipGetLastError();
     }
+    // pool (means into ws.xq / ws.xk), then project them with a tiled product
     dim3 g1(D.Tq + D.Tkv, (unsigned)D.BH);
     timing_before(s, K_POOL_PROJECT);
     if (D.dtype == SLA2_F32)
         pool_project_kernel<float><<<g1, 256, 0, s>>>(
-            (const float*)Q, (const float*)K, Wq, Wk, ws.qt, ws.kt, D.N, D.d, D.bq, D.bkv, D.Tq,
-            D.Tkv, D.H, D.w_heads, D.st);
+            (const float*)Q, (const float*)K, nullptr, nullptr, ws.xq, ws.xk, D.N, D.d, D.bq,
+            D.bkv, D.Tq, D.Tkv, D.H, D.w_heads, D.st);
     else
         pool_project_kernel<uint16_t><<<g1, 256, 0, s>>>(
-            (const uint16_t*)Q, (const uint16_t*)K, Wq, Wk, ws.qt, ws.kt, D.N, D.d, D.bq, D.bkv,
-            D.Tq, D.Tkv, D.H, D.w_heads, D.st);
+            (const uint16_t*)Q, (const uint16_t*)K, nullptr, nullptr, ws.xq, ws.xk, D.N, D.d,
+            D.bq, D.bkv, D.Tq, D.Tkv, D.H, D.w_heads, D.st);
+    dim3 gp((max(D.Tq, D.Tkv) + 63) / 64, 2 * (D.d / 64), (unsigned)D.BH);
+    proj_kernel<<<gp, 256, 0, s>>>(ws.xq, ws.xk, Wq, Wk, ws.qt, ws.kt, D.Tq, D.Tkv, D.d, D.H,
+                                   D.w_heads);
     timing_after(s, K_POOL_PROJECT);
 
     dim3 g2((D.Tkv + 63) / 64, (D.Tq + 63) / 64, (unsigned)D.BH);

@@ -102,6 +102,8 @@ size_t layout_route(const Dims& D, char* base, RouteWS* ws) {
     w.qt = carve<double>(base, off, sizeof(double) * D.BH * D.Tq * D.d);
     w.kt = carve<double>(base, off, sizeof(double) * D.BH * D.Tkv * D.d);
     w.S = carve<double>(base, off, sizeof(double) * D.BH * D.Tq * D.Tkv);
+    w.xq = carve<double>(base, off, sizeof(double) * D.BH * D.Tq * D.d);
+    w.xk = carve<double>(base, off, sizeof(double) * D.BH * D.Tkv * D.d);
     if (ws) *ws = w;
     return align256(off);
 }

@@ -97,6 +97,8 @@ struct RouteWS {
     double* qt;  // [BH][Tq][d]   projected pooled queries
     double* kt;  // [BH][Tkv][d]  projected pooled keys
     double* S;   // [BH][Tq][Tkv] compressed scores
+    double* xq;  // [BH][Tq][d]   pooled queries (before the projection)
+    double* xk;  // [BH][Tkv][d]  pooled keys
 };
 
 struct FwdWS {
