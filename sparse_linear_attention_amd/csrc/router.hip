@@ -220,6 +220,7 @@ __global__ __launch_bounds__(256) void topk_kernel(const double* __restrict__ S,
     __shared__ unsigned hist[256];
     __shared__ unsigned long long s_prefix;
     __shared__ int s_kr;
+    __shared__ int s_done;
     __shared__ int s_cnt[4];
     const int t = threadIdx.x, lane = t & 63;
     const int wid = __builtin_amdgcn_readfirstlane(t >> 6);
@@ -276,6 +277,9 @@ __global__ __launch_bounds__(256) void topk_kernel(const double* __restrict__ S,
                         if (run + c[q] >= (unsigned)kr) {
                             digit = 255 - 4 * lane - q;
                             s_kr = kr - (int)run;
+                            // the bucket holds exactly the keys still wanted:
+                            // the prefix so far decides the selection
+                            s_done = c[q] == (unsigned)(kr - (int)run);
                         } else {
                             run += c[q];
                         }
@@ -288,13 +292,17 @@ __global__ __launch_bounds__(256) void topk_kernel(const double* __restrict__ S,
         prefix = s_prefix;
         kr = s_kr;
         pmask |= 255ull << shift;
+        if (s_done) break;
     }
 
+    // keys compared on the decided prefix (all 64 bits unless a bucket held
+    // exactly the remaining keys, in which case every key equal to the prefix
+    // there is selected)
     const unsigned long long thr = prefix;
     int eq_base = 0, out_base = 0;
     for (int j0 = 0; j0 < Tkv; j0 += 256) {
         const int j = j0 + t;
-        const unsigned long long key = j < Tkv ? keys[j] : 0ull;
+        const unsigned long long key = j < Tkv ? (keys[j] & pmask) : 0ull;
         const bool gt = j < Tkv && key > thr;
         const bool eq = j < Tkv && key == thr;
         const unsigned long long below = (1ull << lane) - 1ull;

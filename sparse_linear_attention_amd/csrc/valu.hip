@@ -84,6 +84,8 @@ __global__ __launch_bounds__(256) void summaries_reduce_kernel(
     const int dd = d * d;
     if (x < dd) {
         float s = 0.0f;
+        // loads issued ahead, additions in chunk order
+#pragma unroll 8
         for (int c = 0; c < nch; ++c) s += hpart[((size_t)bh * nch + c) * dd + x];
         htot[(size_t)bh * dd + x] = s;
     }
