@@ -49,6 +49,9 @@ def lib():
         vp, ip, dp = C.c_void_p, C.c_void_p, C.c_void_p
         L.orc_topk.argtypes = [P]
         L.orc_topk_low.argtypes = [P]
+        L.orc_route_grad.argtypes = [P, vp, vp, vp, vp, dp, dp, dp]
+        L.orc_soft_topk_rows.argtypes = [dp, C.c_long, C.c_int, C.c_int, C.c_double, dp, dp]
+        L.orc_soft_topk_grad_rows.argtypes = [vp, vp, C.c_long, C.c_int, C.c_double, dp]
         L.orc_route_v1.argtypes = [P, vp, vp, ip, C.c_int, ip, ip, vp, dp, dp, C.c_int]
         L.orc_forward_v1.argtypes = [P, vp, vp, vp, ip, ip, vp, ip, C.c_int, dp, C.c_int]
         L.orc_num_blocks.argtypes = [C.c_int, C.c_int]
@@ -132,6 +135,39 @@ def route(p: Problem, q, k, wq, wk, heads=None, nthreads=0, want_scores=False):
     L.orc_route(C.byref(p), _ptr(q), _ptr(k), _ptr(wq), _ptr(wk), _ptr(heads), len(heads),
                 _ptr(idx), _ptr(mask), _ptr(gap), _ptr(sc), nthreads)
     return idx, mask, gap, sc
+
+
+def route_grad(p: Problem, q, k, wq, wk, dS):
+    """dL/dWq, dL/dWk [w_heads, d, d] (fp64) from dL/dS [B, H, Tq, Tkv]."""
+    q, k = _qkv(p, q), _qkv(p, k)
+    wq, wk = _arr(wq, np.float32), _arr(wk, np.float32)
+    dS = _arr(dS, np.float64)
+    gq = np.zeros((p.w_heads, p.d, p.d))
+    gk = np.zeros((p.w_heads, p.d, p.d))
+    lib().orc_route_grad(C.byref(p), _ptr(q), _ptr(k), _ptr(wq), _ptr(wk), _ptr(dS), _ptr(gq),
+                         _ptr(gk))
+    return gq, gk
+
+
+def soft_topk(scores, k: int, tau: float = 0.1):
+    """SoftTop-k of score rows [..., Tkv] (fp64): (M, lambda)."""
+    S = np.ascontiguousarray(scores, np.float64)
+    Tkv = S.shape[-1]
+    rows = S.size // Tkv
+    M = np.zeros_like(S)
+    lam = np.zeros(S.shape[:-1])
+    lib().orc_soft_topk_rows(_ptr(S), rows, Tkv, int(k), float(tau), _ptr(M), _ptr(lam))
+    return M, lam
+
+
+def soft_topk_grad(M, dM, tau: float = 0.1):
+    """dL/dS through SoftTop-k from the fp32 mask M and fp32 dL/dM: fp64."""
+    M = np.ascontiguousarray(M, np.float32)
+    dM = np.ascontiguousarray(dM, np.float32)
+    Tkv = M.shape[-1]
+    dS = np.zeros(M.shape)
+    lib().orc_soft_topk_grad_rows(_ptr(M), _ptr(dM), M.size // Tkv, Tkv, float(tau), _ptr(dS))
+    return dS
 
 
 def route_v1(p: Problem, q, k, heads=None, nthreads=0, want_scores=False):

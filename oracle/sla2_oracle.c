@@ -26,6 +26,9 @@
  *            k_l = 10 %).
  *  [SLA2-en] gist.science explainer, section 2A (O = alpha O_s + (1-alpha) O_l,
  *            both branches row-normalised).
+ *  [SLA2-zh] 06 also gives the training-time router: SoftTop-k(P_c)_ij =
+ *            sigma((P_c)_ij / tau + lambda_i), tau = 0.1, lambda_i found by
+ *            bisection so that each row's soft selections sum to the budget.
  *
  * Readings where the pages are silent or ambiguous:
  *  - router score is the plain product proj_q(Qbar) . proj_k(Kbar), no 1/sqrt(d)
@@ -56,6 +59,12 @@
  *    (lowbit_v) is quantised as well: s_V(c) = max over the N valid tokens
  *    of |V(.,c)| / 448 per head and channel (1 if 0), Vhat = e4m3(V / s_V),
  *    and P V uses Vhat s_V -- the pages quantise P and V for P V;
+ *  - SoftTop-k: the budget is the hard router's k; lambda_i by bisection on
+ *    f(lambda) = sum_j sigma(S_ij / tau + lambda) - k over the bracket
+ *    [-max_j S_ij / tau - 50, -min_j S_ij / tau + 50], a fixed 100 halvings,
+ *    lambda = the final midpoint; k = 0 gives M = 0 (lambda = -inf) and
+ *    k = T_kv gives M = 1 (lambda = +inf); its gradient is the implicit one
+ *    (lambda moves so that the row sum stays k), evaluated from the mask M;
  *  - the pages allow INT8 or FP8 for Q K^T: with int8_qk the Q and smoothed K
  *    codes are int8, s = absmax / 127 per block (1 if 0), code =
  *    round-half-even(x / s) clamped to +-127, and the dot products of the
@@ -413,6 +422,123 @@ int orc_route_v1(const orc_problem* p, const void* Q, const void* K, const int32
     route_ctx C = {p, Q, K, NULL, NULL, heads, idx, mask, gap_rel, scores, nidx};
     run_pool(route_head, &C, n_heads, nthreads);
     return orc_topk_low(p);
+}
+
+/* Gradient of the router scores S = proj_q(Qbar) proj_k(Kbar)^T with
+ * respect to the projections ([SLA2-zh] 05, 06: Stage 1 trains proj_q and
+ * proj_k): qt = Qbar Wq, kt = Kbar Wk, dqt = dS kt, dkt = dS^T qt,
+ * dWq = Qbar^T dqt, dWk = Kbar^T dkt, summed over the heads that share a
+ * projection.  dS [B*H][Tq][Tkv]; dWq, dWk [w_heads][d][d], overwritten. */
+void orc_route_grad(const orc_problem* p, const void* Q, const void* K, const float* Wq,
+                    const float* Wk, const double* dS, double* dWq, double* dWk) {
+    int d = p->d, Tq = ceil_div(p->N, p->bq), Tkv = ceil_div(p->N, p->bkv);
+    long nbh = (long)p->B * p->H;
+    memset(dWq, 0, sizeof(double) * (size_t)p->w_heads * d * d);
+    memset(dWk, 0, sizeof(double) * (size_t)p->w_heads * d * d);
+    double* qb = (double*)malloc(sizeof(double) * (size_t)Tq * d);
+    double* kb = (double*)malloc(sizeof(double) * (size_t)Tkv * d);
+    double* qt = (double*)malloc(sizeof(double) * (size_t)Tq * d);
+    double* kt = (double*)malloc(sizeof(double) * (size_t)Tkv * d);
+    double* dq = (double*)malloc(sizeof(double) * (size_t)Tq * d);
+    double* dk = (double*)malloc(sizeof(double) * (size_t)Tkv * d);
+    for (long bh = 0; bh < nbh; ++bh) {
+        int hw = p->w_heads == 1 ? 0 : (int)(bh % p->H);
+        const float* wq = Wq + (size_t)hw * d * d;
+        const float* wk = Wk + (size_t)hw * d * d;
+        for (int i = 0; i < Tq; ++i) {
+            pool_block(p, Q, bh, i, p->bq, qb + (size_t)i * d);
+            project(d, qb + (size_t)i * d, wq, qt + (size_t)i * d);
+        }
+        for (int j = 0; j < Tkv; ++j) {
+            pool_block(p, K, bh, j, p->bkv, kb + (size_t)j * d);
+            project(d, kb + (size_t)j * d, wk, kt + (size_t)j * d);
+        }
+        const double* g = dS + (size_t)bh * Tq * Tkv;
+        memset(dq, 0, sizeof(double) * (size_t)Tq * d);
+        memset(dk, 0, sizeof(double) * (size_t)Tkv * d);
+        for (int i = 0; i < Tq; ++i)
+            for (int j = 0; j < Tkv; ++j) {
+                double gij = g[(size_t)i * Tkv + j];
+                for (int e = 0; e < d; ++e) {
+                    dq[(size_t)i * d + e] += gij * kt[(size_t)j * d + e];
+                    dk[(size_t)j * d + e] += gij * qt[(size_t)i * d + e];
+                }
+            }
+        double* gq = dWq + (size_t)hw * d * d;
+        double* gk = dWk + (size_t)hw * d * d;
+        for (int c = 0; c < d; ++c)
+            for (int e = 0; e < d; ++e) {
+                double a = 0.0, b = 0.0;
+                for (int i = 0; i < Tq; ++i) a += qb[(size_t)i * d + c] * dq[(size_t)i * d + e];
+                for (int j = 0; j < Tkv; ++j) b += kb[(size_t)j * d + c] * dk[(size_t)j * d + e];
+                gq[(size_t)c * d + e] += a;
+                gk[(size_t)c * d + e] += b;
+            }
+    }
+    free(qb);
+    free(kb);
+    free(qt);
+    free(kt);
+    free(dq);
+    free(dk);
+}
+
+/* ------------------------------------------------------------------ */
+/* SoftTop-k ([SLA2-zh] 06, Stage 1)                                   */
+/* ------------------------------------------------------------------ */
+static double sigmoid(double x) { return 1.0 / (1.0 + exp(-x)); }
+
+/* rows of scores S [rows][Tkv] -> M = sigma(S / tau + lambda_row) with
+ * sum_j M = k per row; lambda [rows] (+-inf at k = T_kv / 0). */
+void orc_soft_topk_rows(const double* S, long rows, int Tkv, int k, double tau, double* M,
+                        double* lambda) {
+    for (long r = 0; r < rows; ++r) {
+        const double* x = S + (size_t)r * Tkv;
+        double* m = M + (size_t)r * Tkv;
+        if (k <= 0 || k >= Tkv) {
+            for (int j = 0; j < Tkv; ++j) m[j] = k <= 0 ? 0.0 : 1.0;
+            lambda[r] = k <= 0 ? -INFINITY : INFINITY;
+            continue;
+        }
+        double smax = -INFINITY, smin = INFINITY;
+        for (int j = 0; j < Tkv; ++j) {
+            if (x[j] / tau > smax) smax = x[j] / tau;
+            if (x[j] / tau < smin) smin = x[j] / tau;
+        }
+        double lo = -smax - 50.0, hi = -smin + 50.0;
+        for (int it = 0; it < 100; ++it) {
+            double mid = 0.5 * (lo + hi), f = -(double)k;
+            for (int j = 0; j < Tkv; ++j) f += sigmoid(x[j] / tau + mid);
+            if (f > 0.0) hi = mid;
+            else lo = mid;
+        }
+        double lam = 0.5 * (lo + hi);
+        lambda[r] = lam;
+        for (int j = 0; j < Tkv; ++j) m[j] = sigmoid(x[j] / tau + lam);
+    }
+}
+
+/* Gradient through SoftTop-k: with s_j = M_j (1 - M_j) and lambda implicit
+ * (sum_j M_j = k), dS_l = s_l / tau * (dM_l - sum_j dM_j s_j / sum_j s_j);
+ * the second term is 0 when sum_j s_j = 0.  M and dM fp32 (as the mask is
+ * stored), arithmetic fp64. */
+void orc_soft_topk_grad_rows(const float* M, const float* dM, long rows, int Tkv, double tau,
+                             double* dS) {
+    for (long r = 0; r < rows; ++r) {
+        const float* m = M + (size_t)r * Tkv;
+        const float* g = dM + (size_t)r * Tkv;
+        double a = 0.0, b = 0.0;
+        for (int j = 0; j < Tkv; ++j) {
+            double sj = (double)m[j] * (1.0 - (double)m[j]);
+            a += (double)g[j] * sj;
+            b += sj;
+        }
+        double c = b > 0.0 ? a / b : 0.0;
+        for (int j = 0; j < Tkv; ++j) {
+            double sj = (double)m[j] * (1.0 - (double)m[j]);
+            dS[(size_t)r * Tkv + j] = sj / tau * ((double)g[j] - c);
+        }
+    }
 }
 
 /* ------------------------------------------------------------------ */

@@ -56,6 +56,11 @@ MUTANTS = {
     "v1_sparse_halved": ("o[e] = os[e] + pr;", "o[e] = 0.5 * os[e] + pr;"),
     "phi_softmax_not_normalised": ("    for (int c = 0; c < d; ++c) out[c] /= s;\n", ""),
     "phi_softmax_no_exp": ("        out[c] = exp(out[c] - m);\n", "        out[c] = out[c] - m + 30.0;\n"),
+    "soft_topk_tau_multiplies": ("f += sigmoid(x[j] / tau + mid);", "f += sigmoid(x[j] * tau + mid);"),
+    "soft_topk_bisection_flipped": ("if (f > 0.0) hi = mid;", "if (f < 0.0) hi = mid;"),
+    "soft_topk_grad_no_lambda_term": ("sj / tau * ((double)g[j] - c)", "sj / tau * ((double)g[j])"),
+    "route_grad_dk_from_kt": ("dk[(size_t)j * d + e] += gij * qt[(size_t)i * d + e];", "dk[(size_t)j * d + e] += gij * kt[(size_t)j * d + e];"),
+    "route_grad_dq_transposed": ("a += qb[(size_t)i * d + c] * dq[(size_t)i * d + e];", "a += qb[(size_t)i * d + e] * dq[(size_t)i * d + c];"),
     "numerator_transposed_H": ("num += pq[c] * Hi[(size_t)c * d + e];", "num += pq[c] * Hi[(size_t)e * d + c];"),
 }
 
@@ -90,6 +95,9 @@ PINS = [
     (pins.test_v1_router_brute_force, ()),
     (pins.test_v1_is_sparse_plus_projected_linear, (1,)),
     (pins.test_v1_all_marginal_or_none, ()),
+    (pins.test_soft_topk_keeps_the_budget, (5,)),
+    (pins.test_soft_topk_gradient_vs_finite_differences, ()),
+    (pins.test_route_grad_vs_finite_differences, ()),
 ]
 
 

@@ -893,6 +893,107 @@ def test_v1_all_marginal_or_none(orc):
 
 
 # --------------------------------------------------------------------------
+# SoftTop-k and the router gradient (Stage 1 of the training, SLA2 深度解读 06)
+# --------------------------------------------------------------------------
+def _rows(n=6, tkv=40, seed=0, scale=1.0):
+    return np.random.default_rng(seed).normal(0, scale, (n, tkv))
+
+
+@pytest.mark.parametrize("k", [1, 5, 20, 39])
+def test_soft_topk_keeps_the_budget(orc, k):
+    S = _rows()
+    M, lam = orc.soft_topk(S, k, 0.1)
+    assert np.abs(M.sum(1) - k).max() < 1e-9
+    assert ((M >= 0) & (M <= 1)).all()
+    # the mask orders blocks as the scores do
+    for r in range(S.shape[0]):
+        o = np.argsort(S[r])
+        assert (np.diff(M[r][o]) >= 0).all()
+
+
+def test_soft_topk_two_blocks_closed_form(orc):
+    """T_kv = 2, k = 1: by symmetry lambda = -(a + b) / (2 tau) and
+    M = (sigma((a - b) / (2 tau)), sigma((b - a) / (2 tau)))."""
+    S = np.array([[0.3, -0.1], [2.0, 1.5], [-0.7, -0.7]])
+    M, lam = orc.soft_topk(S, 1, 0.1)
+    sig = lambda x: 1.0 / (1.0 + np.exp(-x))
+    assert np.abs(lam + S.sum(1) / 0.2).max() < 1e-9
+    assert np.abs(M[:, 0] - sig((S[:, 0] - S[:, 1]) / 0.2)).max() < 1e-12
+
+
+def test_soft_topk_shift_invariance_and_edges(orc):
+    S = _rows(seed=1)
+    M0, l0 = orc.soft_topk(S, 7, 0.1)
+    M1, l1 = orc.soft_topk(S + 3.25, 7, 0.1)
+    assert np.abs(M0 - M1).max() < 1e-9 and np.abs(l1 - (l0 - 32.5)).max() < 1e-7
+    Mz, lz = orc.soft_topk(S, 0, 0.1)
+    Mf, lf = orc.soft_topk(S, 40, 0.1)
+    assert (Mz == 0).all() and np.isneginf(lz).all() and (Mf == 1).all() and np.isposinf(lf).all()
+
+
+def test_soft_topk_small_tau_is_hard_topk(orc):
+    """Well separated scores and a small temperature: the soft mask is the
+    hard top-k mask (ties none)."""
+    S = _rows(seed=2, scale=3.0)
+    M, _ = orc.soft_topk(S, 6, 1e-3)
+    for r in range(S.shape[0]):
+        s = np.sort(S[r])[::-1]
+        assert s[5] - s[6] > 5e-2  # the seed separates the cut
+        hard = np.zeros(S.shape[1])
+        hard[np.argsort(-S[r])[:6]] = 1.0
+        assert np.abs(M[r] - hard).max() < 1e-6
+
+
+def test_soft_topk_gradient_vs_finite_differences(orc):
+    """The implicit-lambda gradient against central differences of the
+    bisection solution itself."""
+    S = _rows(n=3, tkv=12, seed=3, scale=0.3)
+    tau, k = 0.1, 4
+    M, _ = orc.soft_topk(S, k, tau)
+    dM = np.random.default_rng(4).normal(0, 1, S.shape).astype(np.float32)
+    M32 = M.astype(np.float32)
+    g = orc.soft_topk_grad(M32, dM, tau)
+    h = 1e-6
+    num = np.zeros_like(S)
+    for r in range(S.shape[0]):
+        for j in range(S.shape[1]):
+            Sp, Sm = S.copy(), S.copy()
+            Sp[r, j] += h
+            Sm[r, j] -= h
+            num[r, j] = ((orc.soft_topk(Sp, k, tau)[0] - orc.soft_topk(Sm, k, tau)[0])[r]
+                         * dM[r].astype(np.float64)).sum() / (2 * h)
+    # M enters the analytic form through its fp32 rounding
+    assert np.abs(g - num).max() < 2e-5 * max(1.0, np.abs(num).max())
+
+
+def test_route_grad_vs_finite_differences(orc):
+    """S is linear in each projection, so central differences in one entry of
+    Wq or Wk are exact up to rounding."""
+    x = small(dtype="f32", N=640, d=32, H=2, frac=0.2)
+    w = x.wl
+    rng = np.random.default_rng(6)
+    wq = rng.normal(0, 0.2, (1, 32, 32)).astype(np.float32)
+    wk = rng.normal(0, 0.2, (1, 32, 32)).astype(np.float32)
+    p = orc.problem(1, 2, w.N, 32, w.bq, w.bkv, 0.2, 1, "f32")
+    _, _, _, S0 = orc.route(p, x.q, x.k, wq, wk, want_scores=True)
+    dS = rng.normal(0, 1, S0.shape)
+    gq, gk = orc.route_grad(p, x.q, x.k, wq, wk, dS)
+    for which, grad in (("q", gq), ("k", gk)):
+        for (c, e) in [(0, 0), (3, 17), (31, 5), (12, 12)]:
+            h = 0.25  # exact: S is affine in each entry
+            wp_, wm_ = (wq.copy(), wq.copy()) if which == "q" else (wk.copy(), wk.copy())
+            wp_[0, c, e] += h
+            wm_[0, c, e] -= h
+            args_p = (wp_, wk) if which == "q" else (wq, wp_)
+            args_m = (wm_, wk) if which == "q" else (wq, wm_)
+            Sp = orc.route(p, x.q, x.k, *args_p, want_scores=True)[3]
+            Sm = orc.route(p, x.q, x.k, *args_m, want_scores=True)[3]
+            step = float(wp_[0, c, e]) - float(wm_[0, c, e])  # the fp32 step taken
+            num = ((Sp - Sm) * dS).sum() / step
+            assert abs(grad[0, c, e] - num) < 1e-9 * max(1.0, abs(num))
+
+
+# --------------------------------------------------------------------------
 # workload generator sanity (shapes and statistics stated for the workloads)
 # --------------------------------------------------------------------------
 def test_tiny_workload_statistics():
