@@ -100,7 +100,8 @@ typedef enum {
     SLA2_OP_ROUTE = 0,         /* sla2_route, sla1_route     */
     SLA2_OP_FORWARD = 1,       /* sla2_forward               */
     SLA2_OP_FORWARD_FP8 = 2,   /* sla2_forward_fp8           */
-    SLA2_OP_SLA1_FORWARD = 3   /* sla1_forward               */
+    SLA2_OP_SLA1_FORWARD = 3,  /* sla1_forward               */
+    SLA2_OP_ROUTE_GRAD = 4     /* sla2_route_grad            */
 } sla2_op;
 
 typedef struct {
@@ -251,6 +252,50 @@ sla2_status sla2_timing_start(int32_t max_launches);
 sla2_status sla2_timing_stop(float* total_ms, int32_t* launches, int32_t n_kinds);
 int32_t sla2_kernel_kinds(void);
 const char* sla2_kernel_name(int32_t kind);
+
+/*
+ * Training-time router ("SLA2 深度解读" 06, Stage 1: proj_q, proj_k and alpha
+ * are fitted against full attention with a differentiable SoftTop-k in place
+ * of the hard top-k; inference keeps the hard top-k).
+ *
+ * sla2_soft_topk -- M_ij = sigma(S_ij / tau + lambda_i) for the router scores
+ *   S of sla2_route (same pooling, projections and fp64 arithmetic), with
+ *   lambda_i found by bisection so that sum_j M_ij = k (k = sla2_topk(p)):
+ *   f(lambda) = sum_j sigma(S_ij / tau + lambda) - k over the bracket
+ *   [-max_j S_ij / tau - 50, -min_j S_ij / tau + 50], 100 halvings, lambda =
+ *   the final midpoint.  k = 0 gives M = 0 (lambda = -inf), k = T_kv M = 1
+ *   (lambda = +inf).  The pages use tau = 0.1.
+ * Out: M [B,H,T_q,T_kv] fp32; lambda [B,H,T_q] fp64, or NULL.
+ * ws : sla2_workspace_bytes(p, SLA2_OP_ROUTE) bytes.  tau <= 0 or not finite:
+ *      SLA2_EINVAL.
+ */
+sla2_status sla2_soft_topk(const sla2_problem* p, const void* Q, const void* K,
+                           const float* Wq, const float* Wk, float tau, float* M,
+                           double* lambda, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * sla2_soft_topk_grad -- dL/dS from dL/dM through SoftTop-k, lambda moving
+ *   with S so that every row keeps its sum k: with s = M (1 - M),
+ *   dS_ij = s_ij / tau * (dM_ij - sum_l dM_il s_il / sum_l s_il) (the second
+ *   term 0 when sum_l s_il = 0).  fp64 arithmetic from the fp32 M and dM.
+ * In : M (from sla2_soft_topk), dM [B,H,T_q,T_kv] fp32.  Out: dS, same shape.
+ *      No workspace.
+ */
+sla2_status sla2_soft_topk_grad(const sla2_problem* p, const float* M, const float* dM,
+                                float tau, float* dS, void* stream);
+
+/*
+ * sla2_route_grad -- dL/dWq and dL/dWk from dL/dS for the router scores
+ *   S = (Qbar Wq[h']) (Kbar Wk[h'])^T: dqt = dS kt, dkt = dS^T qt,
+ *   dWq = Qbar^T dqt, dWk = Kbar^T dkt per head, summed in head order over
+ *   the heads that share a projection (w_heads == 1: all).  fp64 inside.
+ * In : Q, K, Wq, Wk as sla2_route; dS [B,H,T_q,T_kv] fp32.
+ * Out: dWq, dWk [w_heads,d,d] fp32 (overwritten).
+ * ws : sla2_workspace_bytes(p, SLA2_OP_ROUTE_GRAD) bytes.
+ */
+sla2_status sla2_route_grad(const sla2_problem* p, const void* Q, const void* K,
+                            const float* Wq, const float* Wk, const float* dS, float* dWq,
+                            float* dWk, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * SLA (v1) compatibility ("SLA: Beyond Sparsity ..." notes: key design 2,

@@ -16,7 +16,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libsla2.so")
-SOURCES = ["sla2_api.cpp", "router.hip", "valu.hip", "mfma.hip", "fused128.hip", "fp8.hip"]
+SOURCES = ["sla2_api.cpp", "router.hip", "valu.hip", "mfma.hip", "fused128.hip", "fp8.hip",
+           "train.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 FLAGS = [

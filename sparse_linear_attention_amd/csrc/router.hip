@@ -351,19 +351,8 @@ __global__ void zero_mask_kernel(uint8_t* __restrict__ mask, size_t n) {
 
 }  // namespace
 
-hipError_t launch_route(const Dims& D, const void* Q, const void* K, const float* Wq,
-                        const float* Wk, int32_t* idx, uint8_t* mask, const RouteWS& ws,
-                        hipStream_t s) {
-    if (D.k == 0) {  // nothing is selected: only the mask (if wanted) is written
-        if (mask) {
-            const size_t n = (size_t)D.BH * D.Tq * D.Tkv;
-            timing_before(s, K_TOPK);
-            const size_t nb = (n + 255) / 256;
-            zero_mask_kernel<<<dim3((unsigned)(nb < 65535 ? nb : 65535)), 256, 0, s>>>(mask, n);
-            timing_after(s, K_TOPK);
-        }
-        return hipGetLastError();
-    }
+hipError_t launch_pool_project(const Dims& D, const void* Q, const void* K, const float* Wq,
+                               const float* Wk, const RouteWS& ws, hipStream_t s) {
     // pool (means into ws.xq / ws.xk), then project them with a tiled product
     dim3 g1(D.Tq + D.Tkv, (unsigned)D.BH);
     timing_before(s, K_POOL_PROJECT);
@@ -379,11 +368,35 @@ hipError_t launch_route(const Dims& D, const void* Q, const void* K, const float
     proj_kernel<<<gp, 256, 0, s>>>(ws.xq, ws.xk, Wq, Wk, ws.qt, ws.kt, D.Tq, D.Tkv, D.d, D.H,
                                    D.w_heads);
     timing_after(s, K_POOL_PROJECT);
+    return hipGetLastError();
+}
 
+hipError_t launch_scores(const Dims& D, const void* Q, const void* K, const float* Wq,
+                         const float* Wk, const RouteWS& ws, hipStream_t s) {
+    hipError_t e = launch_pool_project(D, Q, K, Wq, Wk, ws, s);
+    if (e != hipSuccess) return e;
     dim3 g2((D.Tkv + 63) / 64, (D.Tq + 63) / 64, (unsigned)D.BH);
     timing_before(s, K_SCORE);
     score_kernel<<<g2, 256, 0, s>>>(ws.qt, ws.kt, ws.S, D.Tq, D.Tkv, D.d);
     timing_after(s, K_SCORE);
+    return hipGetLastError();
+}
+
+hipError_t launch_route(const Dims& D, const void* Q, const void* K, const float* Wq,
+                        const float* Wk, int32_t* idx, uint8_t* mask, const RouteWS& ws,
+                        hipStream_t s) {
+    if (D.k == 0) {  // nothing is selected: only the mask (if wanted) is written
+        if (mask) {
+            const size_t n = (size_t)D.BH * D.Tq * D.Tkv;
+            timing_before(s, K_TOPK);
+            const size_t nb = (n + 255) / 256;
+            zero_mask_kernel<<<dim3((unsigned)(nb < 65535 ? nb : 65535)), 256, 0, s>>>(mask, n);
+            timing_after(s, K_TOPK);
+        }
+        return hipGetLastError();
+    }
+    hipError_t e = launch_scores(D, Q, K, Wq, Wk, ws, s);
+    if (e != hipSuccess) return e;
 
     dim3 g3(D.Tq, (unsigned)D.BH);
     timing_before(s, K_TOPK);

@@ -37,7 +37,7 @@ static sla2_status make_dims(const sla2_problem* p, int op, Dims* D) {
         return SLA2_EINVAL;
     if (p->out_dtype != SLA2_F32 && p->out_dtype != SLA2_BF16) return SLA2_EINVAL;
     if (p->lowbit < SLA2_LOWBIT_QK || p->lowbit > SLA2_LOWBIT_I8QKV) return SLA2_EINVAL;
-    if (op < SLA2_OP_ROUTE || op > SLA2_OP_SLA1_FORWARD) return SLA2_EINVAL;
+    if (op < SLA2_OP_ROUTE || op > SLA2_OP_ROUTE_GRAD) return SLA2_EINVAL;
     if (p->d != 64 && p->d != 128) return SLA2_EUNSUPPORTED;
     if (p->bq != 64 && p->bq != 128) return SLA2_EUNSUPPORTED;
     if (p->bkv != 64) return SLA2_EUNSUPPORTED;
@@ -46,7 +46,8 @@ static sla2_status make_dims(const sla2_problem* p, int op, Dims* D) {
     if ((op == SLA2_OP_FORWARD_FP8 || op == SLA2_OP_SLA1_FORWARD) && !fast)
         return SLA2_EUNSUPPORTED;
     // softmax phi: the bf16 d = 128, bq = 128 kernels only (routing ignores phi)
-    if (p->phi == SLA2_PHI_SOFTMAX && (op == SLA2_OP_FORWARD_FP8 || (op != SLA2_OP_ROUTE && !fast)))
+    const bool routing = op == SLA2_OP_ROUTE || op == SLA2_OP_ROUTE_GRAD;
+    if (p->phi == SLA2_PHI_SOFTMAX && (op == SLA2_OP_FORWARD_FP8 || (!routing && !fast)))
         return SLA2_EUNSUPPORTED;
     long bh = (long)p->B * p->H;
     if (bh > 65535) return SLA2_EUNSUPPORTED;
@@ -108,6 +109,17 @@ size_t layout_route(const Dims& D, char* base, RouteWS* ws) {
     return align256(off);
 }
 
+size_t layout_route_grad(const Dims& D, char* base, RouteWS* ws, GradWS* gw) {
+    size_t off = layout_route(D, base, ws);
+    GradWS g;
+    g.dq = carve<double>(base, off, sizeof(double) * D.BH * D.Tq * D.d);
+    g.dk = carve<double>(base, off, sizeof(double) * D.BH * D.Tkv * D.d);
+    g.pq = carve<double>(base, off, sizeof(double) * D.BH * D.d * D.d);
+    g.pk = carve<double>(base, off, sizeof(double) * D.BH * D.d * D.d);
+    if (gw) *gw = g;
+    return align256(off);
+}
+
 size_t layout_forward(const Dims& D, int op, char* base, FwdWS* ws) {
     size_t off = 0;
     FwdWS w;
@@ -144,6 +156,7 @@ size_t layout_forward(const Dims& D, int op, char* base, FwdWS* ws) {
 
 static size_t ws_bytes_of(const Dims& D, int op) {
     if (op == SLA2_OP_ROUTE) return layout_route(D, nullptr, nullptr);
+    if (op == SLA2_OP_ROUTE_GRAD) return layout_route_grad(D, nullptr, nullptr, nullptr);
     return layout_forward(D, op, nullptr, nullptr);
 }
 
@@ -395,6 +408,55 @@ SLA2_API sla2_status sla1_forward(const sla2_problem* p, const void* Q, const vo
     hipError_t e = launch_summaries_mfma(D, K, V, w, s);
     if (e == hipSuccess) e = launch_wp_frag(D, Wp, w, s);
     if (e == hipSuccess) e = launch_fused128(D, Q, K, crit_idx, nullptr, O, w, false, s, negl_idx);
+    return e == hipSuccess ? SLA2_OK : SLA2_EHIP;
+}
+
+// ---------------------------------------------------------------------------
+// training-time router (Stage 1)
+// ---------------------------------------------------------------------------
+SLA2_API sla2_status sla2_soft_topk(const sla2_problem* p, const void* Q, const void* K,
+                                    const float* Wq, const float* Wk, float tau, float* M,
+                                    double* lambda, void* ws, size_t ws_bytes, void* stream) {
+    Dims D;
+    sla2_status st = make_dims(p, SLA2_OP_ROUTE, &D);
+    if (st != SLA2_OK) return st;
+    if (!(tau > 0.0f) || !isfinite(tau)) return SLA2_EINVAL;
+    if (!ok_ptr(Q) || !ok_ptr(K) || !ok_ptr(Wq) || !ok_ptr(Wk) || !ok_ptr(M)) return SLA2_EINVAL;
+    if (lambda && !aligned(lambda, 16)) return SLA2_EINVAL;
+    if ((st = check_ws(D, SLA2_OP_ROUTE, ws, ws_bytes)) != SLA2_OK) return st;
+    RouteWS w;
+    layout_route(D, (char*)ws, &w);
+    hipError_t e = launch_soft_topk(D, Q, K, Wq, Wk, (double)tau, M, lambda, w,
+                                    (hipStream_t)stream);
+    return e == hipSuccess ? SLA2_OK : SLA2_EHIP;
+}
+
+SLA2_API sla2_status sla2_soft_topk_grad(const sla2_problem* p, const float* M, const float* dM,
+                                         float tau, float* dS, void* stream) {
+    Dims D;
+    sla2_status st = make_dims(p, SLA2_OP_ROUTE, &D);
+    if (st != SLA2_OK) return st;
+    if (!(tau > 0.0f) || !isfinite(tau)) return SLA2_EINVAL;
+    if (!ok_ptr(M) || !ok_ptr(dM) || !ok_ptr(dS)) return SLA2_EINVAL;
+    hipError_t e = launch_soft_topk_grad(D, M, dM, (double)tau, dS, (hipStream_t)stream);
+    return e == hipSuccess ? SLA2_OK : SLA2_EHIP;
+}
+
+SLA2_API sla2_status sla2_route_grad(const sla2_problem* p, const void* Q, const void* K,
+                                     const float* Wq, const float* Wk, const float* dS,
+                                     float* dWq, float* dWk, void* ws, size_t ws_bytes,
+                                     void* stream) {
+    Dims D;
+    sla2_status st = make_dims(p, SLA2_OP_ROUTE_GRAD, &D);
+    if (st != SLA2_OK) return st;
+    if (!ok_ptr(Q) || !ok_ptr(K) || !ok_ptr(Wq) || !ok_ptr(Wk) || !ok_ptr(dS) || !ok_ptr(dWq) ||
+        !ok_ptr(dWk))
+        return SLA2_EINVAL;
+    if ((st = check_ws(D, SLA2_OP_ROUTE_GRAD, ws, ws_bytes)) != SLA2_OK) return st;
+    RouteWS w;
+    GradWS g;
+    layout_route_grad(D, (char*)ws, &w, &g);
+    hipError_t e = launch_route_grad(D, Q, K, Wq, Wk, dS, dWq, dWk, w, g, (hipStream_t)stream);
     return e == hipSuccess ? SLA2_OK : SLA2_EHIP;
 }
 

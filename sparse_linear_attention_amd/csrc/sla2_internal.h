@@ -127,9 +127,18 @@ struct FwdWS {
     uint16_t* wpf;   // [w_heads][4 m-tiles][8 k-steps][64 lanes][8]
 };
 
+// router gradient (SLA2_OP_ROUTE_GRAD: the route layout, then these)
+struct GradWS {
+    double* dq;  // [BH][Tq][d]   dL/dqt
+    double* dk;  // [BH][Tkv][d]  dL/dkt
+    double* pq;  // [BH][d][d]    per-head dL/dWq
+    double* pk;  // [BH][d][d]    per-head dL/dWk
+};
+
 // Lays out the workspace of `op` starting at `base` (may be null to size
 // only); returns the bytes needed.
 size_t layout_route(const Dims& D, char* base, RouteWS* ws);
+size_t layout_route_grad(const Dims& D, char* base, RouteWS* ws, GradWS* gw);
 size_t layout_forward(const Dims& D, int op, char* base, FwdWS* ws);
 
 // ---------------------------------------------------------------------------
@@ -144,6 +153,23 @@ void timing_after(hipStream_t s, int kind);
 hipError_t launch_route(const Dims& D, const void* Q, const void* K, const float* Wq,
                         const float* Wk, int32_t* idx, uint8_t* mask, const RouteWS& ws,
                         hipStream_t s);
+
+// router stages: pooled rows and their projections (ws.xq/xk, ws.qt/kt);
+// then the scores (ws.S)
+hipError_t launch_pool_project(const Dims& D, const void* Q, const void* K, const float* Wq,
+                               const float* Wk, const RouteWS& ws, hipStream_t s);
+hipError_t launch_scores(const Dims& D, const void* Q, const void* K, const float* Wq,
+                         const float* Wk, const RouteWS& ws, hipStream_t s);
+
+// training-time router: SoftTop-k, its gradient, the projections' gradient
+hipError_t launch_soft_topk(const Dims& D, const void* Q, const void* K, const float* Wq,
+                            const float* Wk, double tau, float* M, double* lambda,
+                            const RouteWS& ws, hipStream_t s);
+hipError_t launch_soft_topk_grad(const Dims& D, const float* M, const float* dM, double tau,
+                                 float* dS, hipStream_t s);
+hipError_t launch_route_grad(const Dims& D, const void* Q, const void* K, const float* Wq,
+                             const float* Wk, const float* dS, float* dWq, float* dWk,
+                             const RouteWS& ws, const GradWS& gw, hipStream_t s);
 
 // SLA (v1) router: critical (top k) and negligible (bottom kl) blocks
 hipError_t launch_route_v1(const Dims& D, const void* Q, const void* K, int kl, int32_t* crit,

@@ -16,7 +16,7 @@ LIB_PATH = os.path.join(PKG, "libsla2.so")
 OK, EINVAL, EUNSUPPORTED, EWORKSPACE, EHIP = range(5)
 F32, BF16 = 0, 1
 PHI_ELU1, PHI_SOFTMAX = 0, 1
-OP_ROUTE, OP_FORWARD, OP_FORWARD_FP8, OP_SLA1_FORWARD = 0, 1, 2, 3
+OP_ROUTE, OP_FORWARD, OP_FORWARD_FP8, OP_SLA1_FORWARD, OP_ROUTE_GRAD = 0, 1, 2, 3, 4
 LAYOUT_BHND, LAYOUT_BNHD = 0, 1
 ALPHA_PER_HEAD, ALPHA_PER_QBLOCK = 0, 1
 LOWBIT_QK, LOWBIT_QKV, LOWBIT_I8QK, LOWBIT_I8QKV = 0, 1, 2, 3
@@ -68,6 +68,9 @@ def lib():
         L.sla2_kernel_name.argtypes = [C.c_int32]
         L.sla2_kernel_name.restype = C.c_char_p
         L.sla1_num_negligible.argtypes = [P, C.c_float]
+        L.sla2_soft_topk.argtypes = [P, vp, vp, vp, vp, C.c_float, vp, vp, vp, C.c_size_t, vp]
+        L.sla2_soft_topk_grad.argtypes = [P, vp, vp, C.c_float, vp, vp]
+        L.sla2_route_grad.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, C.c_size_t, vp]
         L.sla1_route.argtypes = [P, vp, vp, C.c_float, vp, vp, vp, vp, C.c_size_t, vp]
         L.sla1_forward.argtypes = [P, vp, vp, vp, vp, vp, C.c_float, vp, vp, vp, C.c_size_t, vp]
         _lib = L
@@ -78,7 +81,7 @@ EXPORTS = ("sla2_num_q_blocks", "sla2_num_kv_blocks", "sla2_topk", "sla2_workspa
            "sla2_check", "sla2_status_str", "sla2_route", "sla2_forward", "sla2_forward_fp8",
            "sla2_quantize_fp8", "sla2_quantize_v_fp8", "sla2_timing_start", "sla2_timing_stop",
            "sla2_kernel_kinds", "sla2_kernel_name", "sla1_num_negligible", "sla1_route",
-           "sla1_forward")
+           "sla1_forward", "sla2_soft_topk", "sla2_soft_topk_grad", "sla2_route_grad")
 
 
 def _dtype(x):
@@ -190,6 +193,55 @@ def sla1_forward(p, Q, K, V, crit_idx, negl_idx, low_frac, Wp, O, ws=None, strea
     _raise(lib().sla1_forward(C.byref(p), _ptr(Q), _ptr(K), _ptr(V), _ptr(crit_idx),
                               _ptr(negl_idx), float(low_frac), _ptr(Wp), _ptr(O), wp, wb,
                               _stream(stream)), "sla1_forward")
+
+
+def sla2_soft_topk(p, Q, K, Wq, Wk, tau, M, lam=None, ws=None, stream=None):
+    wp, wb = _ws(ws)
+    _raise(lib().sla2_soft_topk(C.byref(p), _ptr(Q), _ptr(K), _ptr(Wq), _ptr(Wk), float(tau),
+                                _ptr(M), _ptr(lam), wp, wb, _stream(stream)), "sla2_soft_topk")
+
+
+def sla2_soft_topk_grad(p, M, dM, tau, dS, stream=None):
+    _raise(lib().sla2_soft_topk_grad(C.byref(p), _ptr(M), _ptr(dM), float(tau), _ptr(dS),
+                                     _stream(stream)), "sla2_soft_topk_grad")
+
+
+def sla2_route_grad(p, Q, K, Wq, Wk, dS, dWq, dWk, ws=None, stream=None):
+    wp, wb = _ws(ws)
+    _raise(lib().sla2_route_grad(C.byref(p), _ptr(Q), _ptr(K), _ptr(Wq), _ptr(Wk), _ptr(dS),
+                                 _ptr(dWq), _ptr(dWk), wp, wb, _stream(stream)),
+           "sla2_route_grad")
+
+
+def soft_topk(p: Problem, Q, K, Wq, Wk, tau=0.1, ws=None, stream=None):
+    """Allocates outputs, runs sla2_soft_topk; returns (M fp32, lambda fp64)."""
+    import torch
+    dev = Q.device
+    M = torch.empty((p.B, p.H, num_q_blocks(p), num_kv_blocks(p)), dtype=torch.float32,
+                    device=dev)
+    lam = torch.empty((p.B, p.H, num_q_blocks(p)), dtype=torch.float64, device=dev)
+    if ws is None:
+        ws = workspace(p, OP_ROUTE, dev)
+    sla2_soft_topk(p, Q, K, Wq, Wk, tau, M, lam, ws, stream)
+    return M, lam
+
+
+def soft_topk_grad(p: Problem, M, dM, tau=0.1, stream=None):
+    import torch
+    dS = torch.empty_like(M)
+    sla2_soft_topk_grad(p, M, dM, tau, dS, stream)
+    return dS
+
+
+def route_grad(p: Problem, Q, K, Wq, Wk, dS, ws=None, stream=None):
+    """Allocates dWq, dWk and the workspace; runs sla2_route_grad."""
+    import torch
+    dWq = torch.empty_like(Wq)
+    dWk = torch.empty_like(Wk)
+    if ws is None:
+        ws = workspace(p, OP_ROUTE_GRAD, Q.device)
+    sla2_route_grad(p, Q, K, Wq, Wk, dS, dWq, dWk, ws, stream)
+    return dWq, dWk
 
 
 def kernel_names():

@@ -99,7 +99,8 @@ def test_sla1_counts_and_checks(orc):
     assert S.check(p_ok(), S.OP_SLA1_FORWARD) == S.OK
     for kw in (dict(dtype=S.F32), dict(bq=64), dict(d=64)):
         assert S.check(p_ok(**kw), S.OP_SLA1_FORWARD) == S.EUNSUPPORTED
-    assert S.check(p_ok(), 4) == S.EINVAL
+    assert S.check(p_ok(), S.OP_ROUTE_GRAD) == S.OK
+    assert S.check(p_ok(), 5) == S.EINVAL
     for wh in (1, 2):
         extra = S.workspace_bytes(p_ok(w_heads=wh), S.OP_SLA1_FORWARD) - S.workspace_bytes(
             p_ok(w_heads=wh), S.OP_FORWARD)
@@ -178,6 +179,22 @@ def test_entry_points_validate_before_launching():
                           good, fw, None) == S.EWORKSPACE
     assert L.sla1_forward(C.byref(pf), good, good, good, good, good, C.c_float(0.1), good, good,
                           good, v1w, None) == S.EUNSUPPORTED
+    # training-time router
+    assert L.sla2_soft_topk(C.byref(p), good, good, good, good, C.c_float(0.0), good, None, good,
+                            ws_need, None) == S.EINVAL  # tau must be > 0
+    assert L.sla2_soft_topk(C.byref(p), good, good, good, good, C.c_float(0.1), None, None, good,
+                            ws_need, None) == S.EINVAL  # no M
+    assert L.sla2_soft_topk(C.byref(p), good, good, good, good, C.c_float(0.1), good, None, good,
+                            ws_need - 256, None) == S.EWORKSPACE
+    assert L.sla2_soft_topk_grad(C.byref(p), good, None, C.c_float(0.1), good, None) == S.EINVAL
+    assert L.sla2_soft_topk_grad(C.byref(p), good, good, C.c_float(float("nan")), good,
+                                 None) == S.EINVAL
+    rg = S.workspace_bytes(p, S.OP_ROUTE_GRAD)
+    assert rg > ws_need
+    assert L.sla2_route_grad(C.byref(p), good, good, good, good, good, good, None, good, rg,
+                             None) == S.EINVAL
+    assert L.sla2_route_grad(C.byref(p), good, good, good, good, good, good, good, good,
+                             rg - 256, None) == S.EWORKSPACE
     # idx may be null only when k == 0
     p0 = p_ok(topk_frac=0.0)
     assert L.sla2_route(C.byref(p), good, good, good, good, None, None, good, ws_need, None) == S.EINVAL
