@@ -50,6 +50,7 @@ def lib():
         L.orc_topk.argtypes = [P]
         L.orc_topk_low.argtypes = [P]
         L.orc_route_grad.argtypes = [P, vp, vp, vp, vp, dp, dp, dp]
+        L.orc_backward.argtypes = [P, vp, vp, vp, ip, vp, dp, dp, dp, dp, dp, C.c_int]
         L.orc_soft_topk_rows.argtypes = [dp, C.c_long, C.c_int, C.c_int, C.c_double, dp, dp]
         L.orc_soft_topk_grad_rows.argtypes = [vp, vp, C.c_long, C.c_int, C.c_double, dp]
         L.orc_route_v1.argtypes = [P, vp, vp, ip, C.c_int, ip, ip, vp, dp, dp, C.c_int]
@@ -135,6 +136,24 @@ def route(p: Problem, q, k, wq, wk, heads=None, nthreads=0, want_scores=False):
     L.orc_route(C.byref(p), _ptr(q), _ptr(k), _ptr(wq), _ptr(wk), _ptr(heads), len(heads),
                 _ptr(idx), _ptr(mask), _ptr(gap), _ptr(sc), nthreads)
     return idx, mask, gap, sc
+
+
+def backward(p: Problem, q, k, v, idx, alpha, dO, nthreads=0):
+    """Gradients of sum(dO * O) for the SLA2 forward with idx fixed:
+    (dQ, dK, dV [B,H,N,d] fp64, dalpha [H] or [H,Tq])."""
+    q, k, v = _qkv(p, q), _qkv(p, k), _qkv(p, v)
+    idx = _arr(idx, np.int32)
+    alpha = _arr(alpha, np.float32)
+    dO = _arr(dO, np.float64)
+    shape = (p.B, p.H, p.N, p.d)
+    dQ, dK, dV = np.zeros(shape), np.zeros(shape), np.zeros(shape)
+    Tq = num_blocks(p.N, p.bq)
+    da = np.zeros((p.H, Tq) if p.alpha_mode else (p.H,))
+    rc = lib().orc_backward(C.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(idx), _ptr(alpha),
+                            _ptr(dO), _ptr(dQ), _ptr(dK), _ptr(dV), _ptr(da), nthreads)
+    if rc != 0:
+        raise ValueError(f"oracle: backward failed ({rc})")
+    return dQ, dK, dV, da
 
 
 def route_grad(p: Problem, q, k, wq, wk, dS):

@@ -59,6 +59,12 @@
  *    (lowbit_v) is quantised as well: s_V(c) = max over the N valid tokens
  *    of |V(.,c)| / 448 per head and channel (1 if 0), Vhat = e4m3(V / s_V),
  *    and P V uses Vhat s_V -- the pages quantise P and V for P V;
+ *  - backward (SLA2 mode, exact sparse branch, the hard selection held
+ *    fixed): the chain rule through O = alpha O_s + (1 - alpha) O_l --
+ *    softmax attention over the selected tokens for O_s, and for O_l the
+ *    linear branch's H_i, Z_i summed over the unselected blocks, so that
+ *    block j's summary h_j, z_j receives the gradients of every query block
+ *    that does not select it; alpha's gradient is summed over its rows;
  *  - SoftTop-k: the budget is the hard router's k; lambda_i by bisection on
  *    f(lambda) = sum_j sigma(S_ij / tau + lambda) - k over the bracket
  *    [-max_j S_ij / tau - 50, -min_j S_ij / tau + 50], a fixed 100 halvings,
@@ -576,6 +582,224 @@ static void summary_block(void* vctx, long j) {
     }
     free(pk);
     free(vv);
+}
+
+/* ------------------------------------------------------------------ */
+/* Backward of the SLA2 forward (hard selection fixed)                  */
+/* ------------------------------------------------------------------ */
+/* dx from dphi for row t of X: elu + 1 has phi' = 1 (x > 0) or exp(x);
+   softmax has dx = phi (dphi - phi . dphi) */
+static void phi_row_backward(const orc_problem* p, const void* X, long bh, long t,
+                             const double* ph, const double* dph, double* dx) {
+    int d = p->d;
+    if (p->phi == 0) {
+        for (int c = 0; c < d; ++c) {
+            double x = elem(p, X, bh, t, c);
+            dx[c] = dph[c] * (x > 0.0 ? 1.0 : exp(x));
+        }
+        return;
+    }
+    double dot = 0.0;
+    for (int c = 0; c < d; ++c) dot += ph[c] * dph[c];
+    for (int c = 0; c < d; ++c) dx[c] = ph[c] * (dph[c] - dot);
+}
+
+typedef struct {
+    const orc_problem* p;
+    const void *Q, *K, *V;
+    const int32_t* idx;
+    const float* alpha;
+    const double* dO;          /* [B*H][N][d] */
+    double *dQ, *dK, *dV;      /* [B*H][N][d], accumulated (zeroed by the caller) */
+    double* dalpha_part;       /* [B*H][Tq] per-(head, query block) partials */
+} bwd_ctx;
+
+static void backward_head(void* vctx, long bh) {
+    bwd_ctx* C = (bwd_ctx*)vctx;
+    const orc_problem* p = C->p;
+    int d = p->d, N = p->N, Tq = ceil_div(N, p->bq), Tkv = ceil_div(N, p->bkv);
+    int k = orc_topk(p), h = (int)(bh % p->H);
+    double inv = 1.0 / sqrt((double)d);
+    size_t dd = (size_t)d * d;
+    double* hj = (double*)malloc(sizeof(double) * Tkv * dd);
+    double* zj = (double*)malloc(sizeof(double) * Tkv * d);
+    summ_ctx S = {p, C->K, C->V, bh, hj, zj};
+    for (int j = 0; j < Tkv; ++j) summary_block(&S, j);
+    double* dH = (double*)calloc((size_t)Tq * dd, sizeof(double));
+    double* dZ = (double*)calloc((size_t)Tq * d, sizeof(double));
+    uint8_t* hit = (uint8_t*)malloc((size_t)Tq * Tkv);
+    double* Hi = (double*)malloc(sizeof(double) * dd);
+    double* Zi = (double*)malloc(sizeof(double) * d);
+    double* pq = (double*)malloc(sizeof(double) * d);
+    double* os = (double*)malloc(sizeof(double) * d);
+    double* olin = (double*)malloc(sizeof(double) * d);
+    double* g = (double*)malloc(sizeof(double) * d);
+    double* dq = (double*)malloc(sizeof(double) * d);
+    double* dph = (double*)malloc(sizeof(double) * d);
+    double* dx = (double*)malloc(sizeof(double) * d);
+    double* dn = (double*)malloc(sizeof(double) * d);
+    double* lw = (double*)malloc(sizeof(double) * ((size_t)k * p->bkv + 1));
+    int n_unsel = Tkv - k;
+    for (int i = 0; i < Tq; ++i) {
+        const int32_t* sel = C->idx + ((size_t)bh * Tq + i) * k;
+        uint8_t* hrow = hit + (size_t)i * Tkv;
+        memset(hrow, 0, Tkv);
+        for (int r = 0; r < k; ++r) hrow[sel[r]] = 1;
+        memset(Hi, 0, sizeof(double) * dd);
+        memset(Zi, 0, sizeof(double) * d);
+        for (int j = 0; j < Tkv; ++j) {
+            if (hrow[j]) continue;
+            for (size_t x = 0; x < dd; ++x) Hi[x] += hj[(size_t)j * dd + x];
+            for (int c = 0; c < d; ++c) Zi[c] += zj[(size_t)j * d + c];
+        }
+        double a = (double)(p->alpha_mode ? C->alpha[(size_t)h * Tq + i] : C->alpha[h]);
+        int t0 = i * p->bq, nq = N - t0 < p->bq ? N - t0 : p->bq;
+        for (int t = t0; t < t0 + nq; ++t) {
+            const double* gt = C->dO + ((size_t)bh * N + t) * d;
+            for (int e = 0; e < d; ++e) g[e] = gt[e];
+            for (int e = 0; e < d; ++e) dq[e] = 0.0;
+            /* forward of the row: sparse branch (two-pass softmax) */
+            long nu = 0;
+            double m = -INFINITY, l = 0.0;
+            for (int r = 0; r < k; ++r) {
+                int u0 = sel[r] * p->bkv, n = N - u0 < p->bkv ? N - u0 : p->bkv;
+                for (int u = u0; u < u0 + n; ++u) {
+                    double sc = 0.0;
+                    for (int c = 0; c < d; ++c)
+                        sc += elem(p, C->Q, bh, t, c) * elem(p, C->K, bh, u, c);
+                    lw[nu++] = sc * inv;
+                    if (sc * inv > m) m = sc * inv;
+                }
+            }
+            for (long x = 0; x < nu; ++x) {
+                lw[x] = exp(lw[x] - m);
+                l += lw[x];
+            }
+            for (int e = 0; e < d; ++e) os[e] = 0.0;
+            nu = 0;
+            for (int r = 0; r < k; ++r) {
+                int u0 = sel[r] * p->bkv, n = N - u0 < p->bkv ? N - u0 : p->bkv;
+                for (int u = u0; u < u0 + n; ++u, ++nu) {
+                    lw[nu] /= l; /* p_tu */
+                    for (int e = 0; e < d; ++e) os[e] += lw[nu] * elem(p, C->V, bh, u, e);
+                }
+            }
+            /* linear branch */
+            phi_row(p, C->Q, bh, t, pq);
+            double den = 0.0;
+            for (int c = 0; c < d; ++c) den += Zi[c] * pq[c];
+            for (int e = 0; e < d; ++e) {
+                double num = 0.0;
+                if (n_unsel > 0)
+                    for (int c = 0; c < d; ++c) num += Hi[(size_t)c * d + e] * pq[c];
+                olin[e] = n_unsel > 0 ? num / den : 0.0;
+            }
+            /* alpha: dO . (O_s - O_l) */
+            double da = 0.0;
+            for (int e = 0; e < d; ++e) da += g[e] * (os[e] - olin[e]);
+            C->dalpha_part[(size_t)bh * Tq + i] += da;
+            /* sparse branch: dO_s = a dO, D = dO_s . O_s, dl = p (dO_s . v - D) */
+            double D = 0.0;
+            for (int e = 0; e < d; ++e) D += a * g[e] * os[e];
+            nu = 0;
+            for (int r = 0; r < k; ++r) {
+                int u0 = sel[r] * p->bkv, n = N - u0 < p->bkv ? N - u0 : p->bkv;
+                for (int u = u0; u < u0 + n; ++u, ++nu) {
+                    double dp = 0.0;
+                    for (int e = 0; e < d; ++e) dp += a * g[e] * elem(p, C->V, bh, u, e);
+                    double dl = lw[nu] * (dp - D);
+                    double* dku = C->dK + ((size_t)bh * N + u) * d;
+                    double* dvu = C->dV + ((size_t)bh * N + u) * d;
+                    for (int c = 0; c < d; ++c) {
+                        dq[c] += dl * elem(p, C->K, bh, u, c) * inv;
+                        dku[c] += dl * elem(p, C->Q, bh, t, c) * inv;
+                    }
+                    for (int e = 0; e < d; ++e) dvu[e] += lw[nu] * a * g[e];
+                }
+            }
+            /* linear branch: dn = (1-a) dO / den, ds = -((1-a) dO . O_l) / den */
+            if (n_unsel > 0) {
+                double dsv = 0.0;
+                for (int e = 0; e < d; ++e) {
+                    dn[e] = (1.0 - a) * g[e] / den;
+                    dsv -= (1.0 - a) * g[e] * olin[e] / den;
+                }
+                for (int c = 0; c < d; ++c) {
+                    double v = Zi[c] * dsv;
+                    for (int e = 0; e < d; ++e) v += Hi[(size_t)c * d + e] * dn[e];
+                    dph[c] = v;
+                    for (int e = 0; e < d; ++e) dH[(size_t)i * dd + (size_t)c * d + e] += pq[c] * dn[e];
+                    dZ[(size_t)i * d + c] += pq[c] * dsv;
+                }
+                phi_row_backward(p, C->Q, bh, t, pq, dph, dx);
+                for (int c = 0; c < d; ++c) dq[c] += dx[c];
+            }
+            double* dqt = C->dQ + ((size_t)bh * N + t) * d;
+            for (int c = 0; c < d; ++c) dqt[c] += dq[c];
+        }
+    }
+    /* block summaries: dh_j, dz_j gather every query block not selecting j */
+    double* dhj = (double*)malloc(sizeof(double) * dd);
+    double* dzj = (double*)malloc(sizeof(double) * d);
+    double* pk = (double*)malloc(sizeof(double) * d);
+    for (int j = 0; j < Tkv; ++j) {
+        memset(dhj, 0, sizeof(double) * dd);
+        memset(dzj, 0, sizeof(double) * d);
+        for (int i = 0; i < Tq; ++i) {
+            if (hit[(size_t)i * Tkv + j]) continue;
+            for (size_t x = 0; x < dd; ++x) dhj[x] += dH[(size_t)i * dd + x];
+            for (int c = 0; c < d; ++c) dzj[c] += dZ[(size_t)i * d + c];
+        }
+        int u0 = j * p->bkv, n = N - u0 < p->bkv ? N - u0 : p->bkv;
+        for (int u = u0; u < u0 + n; ++u) {
+            phi_row(p, C->K, bh, u, pk);
+            double* dvu = C->dV + ((size_t)bh * N + u) * d;
+            for (int e = 0; e < d; ++e) {
+                double v = 0.0;
+                for (int c = 0; c < d; ++c) v += pk[c] * dhj[(size_t)c * d + e];
+                dvu[e] += v;
+            }
+            for (int c = 0; c < d; ++c) {
+                double v = dzj[c];
+                for (int e = 0; e < d; ++e) v += dhj[(size_t)c * d + e] * elem(p, C->V, bh, u, e);
+                dph[c] = v;
+            }
+            phi_row_backward(p, C->K, bh, u, pk, dph, dx);
+            double* dku = C->dK + ((size_t)bh * N + u) * d;
+            for (int c = 0; c < d; ++c) dku[c] += dx[c];
+        }
+    }
+    free(hj); free(zj); free(dH); free(dZ); free(hit); free(Hi); free(Zi); free(pq); free(os);
+    free(olin); free(g); free(dq); free(dph); free(dx); free(dn); free(lw); free(dhj);
+    free(dzj); free(pk);
+}
+
+/* Gradients of L = sum dO . O for the SLA2 forward with the selection idx
+ * held fixed (exact sparse branch).  dO [B*H][N][d] fp64; dQ, dK, dV
+ * [B*H][N][d] fp64 (overwritten); dalpha [H] or [H][Tq] (alpha_mode),
+ * overwritten.  Returns 0, -2 if p is not in SLA2 mode. */
+int orc_backward(const orc_problem* p, const void* Q, const void* K, const void* V,
+                 const int32_t* idx, const float* alpha, const double* dO, double* dQ,
+                 double* dK, double* dV, double* dalpha, int nthreads) {
+    if (p->mode != 0) return -2;
+    int d = p->d, N = p->N, Tq = ceil_div(N, p->bq);
+    long nbh = (long)p->B * p->H;
+    size_t n = (size_t)nbh * N * d;
+    memset(dQ, 0, sizeof(double) * n);
+    memset(dK, 0, sizeof(double) * n);
+    memset(dV, 0, sizeof(double) * n);
+    double* part = (double*)calloc((size_t)nbh * Tq, sizeof(double));
+    bwd_ctx C = {p, Q, K, V, idx, alpha, dO, dQ, dK, dV, part};
+    run_pool(backward_head, &C, nbh, nthreads);
+    int na = p->alpha_mode ? p->H * Tq : p->H;
+    for (int x = 0; x < na; ++x) dalpha[x] = 0.0;
+    for (long bh = 0; bh < nbh; ++bh) {
+        int h = (int)(bh % p->H);
+        for (int i = 0; i < Tq; ++i)
+            dalpha[p->alpha_mode ? (size_t)h * Tq + i : (size_t)h] += part[(size_t)bh * Tq + i];
+    }
+    free(part);
+    return 0;
 }
 
 /* ------------------------------------------------------------------ */

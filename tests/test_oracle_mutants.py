@@ -61,6 +61,12 @@ MUTANTS = {
     "soft_topk_grad_no_lambda_term": ("sj / tau * ((double)g[j] - c)", "sj / tau * ((double)g[j])"),
     "route_grad_dk_from_kt": ("dk[(size_t)j * d + e] += gij * qt[(size_t)i * d + e];", "dk[(size_t)j * d + e] += gij * kt[(size_t)j * d + e];"),
     "route_grad_dq_transposed": ("a += qb[(size_t)i * d + c] * dq[(size_t)i * d + e];", "a += qb[(size_t)i * d + e] * dq[(size_t)i * d + c];"),
+    "bwd_no_D_term": ("double dl = lw[nu] * (dp - D);", "double dl = lw[nu] * dp;"),
+    "bwd_dh_over_selected": ("            if (hit[(size_t)i * Tkv + j]) continue;", "            if (!hit[(size_t)i * Tkv + j]) continue;"),
+    "bwd_no_ds": ("                    dsv -= (1.0 - a) * g[e] * olin[e] / den;\n", ""),
+    "bwd_elu_prime_one": ("dx[c] = dph[c] * (x > 0.0 ? 1.0 : exp(x));", "dx[c] = dph[c];"),
+    "bwd_alpha_sign": ("da += g[e] * (os[e] - olin[e]);", "da += g[e] * (olin[e] - os[e]);"),
+    "bwd_dv_without_alpha": ("dvu[e] += lw[nu] * a * g[e];", "dvu[e] += lw[nu] * g[e];"),
     "numerator_transposed_H": ("num += pq[c] * Hi[(size_t)c * d + e];", "num += pq[c] * Hi[(size_t)e * d + c];"),
 }
 
@@ -98,6 +104,8 @@ PINS = [
     (pins.test_soft_topk_keeps_the_budget, (5,)),
     (pins.test_soft_topk_gradient_vs_finite_differences, ()),
     (pins.test_route_grad_vs_finite_differences, ()),
+    (pins.test_backward_vs_torch_autograd, (0, 0, 0.4)),
+    (pins.test_backward_vs_finite_differences, ()),
 ]
 
 

@@ -893,6 +893,92 @@ def test_v1_all_marginal_or_none(orc):
 
 
 # --------------------------------------------------------------------------
+# backward of the SLA2 forward (hard selection fixed)
+# --------------------------------------------------------------------------
+def _torch_sla2(q, k, v, a_rows, crit_t, phi):
+    """Independent dense formulation in torch float64: per row t, O_t =
+    a_t softmax over the selected tokens + (1 - a_t) linear attention over
+    the unselected ones (phi features)."""
+    d = q.shape[1]
+    lg = (q @ k.T) / math.sqrt(d)
+    lg = torch.where(crit_t, lg, torch.full_like(lg, -float("inf")))
+    has = crit_t.any(1, keepdim=True)
+    P = torch.softmax(torch.where(has, lg, torch.zeros_like(lg)), dim=1) * has
+    os_ = P @ v
+    fq, fk = phi(q), phi(k)
+    A = (fq @ fk.T) * (~crit_t)
+    den = A.sum(1, keepdim=True)
+    ol = torch.where(den > 0, (A @ v) / torch.where(den > 0, den, torch.ones_like(den)),
+                     torch.zeros_like(os_))
+    return a_rows[:, None] * os_ + (1 - a_rows[:, None]) * ol
+
+
+@pytest.mark.parametrize("phi,alpha_mode,frac", [(0, 0, 0.4), (1, 0, 0.4), (0, 1, 0.4),
+                                                 (0, 0, 0.0), (1, 0, 1.0)])
+def test_backward_vs_torch_autograd(orc, phi, alpha_mode, frac):
+    """The oracle's chain rule against autograd of an independent dense
+    formulation (masks expanded to tokens, float64)."""
+    x = small(dtype="f32", N=300, d=16, bq=64, frac=frac, H=2, seed=3, alpha=(0.6, 0.3))
+    w = x.wl
+    p = orc.problem(w.B, w.H, w.N, w.d, w.bq, w.bkv, frac, 1, "f32", alpha_mode=alpha_mode,
+                    phi=phi)
+    idx, mask, _, _ = orc.route(p, x.q, x.k, x.wq, x.wk)
+    rng = np.random.default_rng(8)
+    alpha = (rng.uniform(0.2, 0.9, (2, w.Tq)).astype(np.float32) if alpha_mode else x.alpha)
+    dO = rng.normal(0, 1, (1, 2, w.N, w.d))
+    dQ, dK, dV, da = orc.backward(p, x.q, x.k, x.v, idx, alpha, dO)
+    feat = ((lambda t: torch.softmax(t, dim=1)) if phi else
+            (lambda t: torch.nn.functional.elu(t) + 1.0))
+    for h in range(2):
+        q, k, v = (torch.tensor(np.asarray(a[0, h], np.float64), requires_grad=True)
+                   for a in (x.q, x.k, x.v))
+        av = torch.tensor(np.asarray(alpha[h], np.float64), requires_grad=True)
+        a_rows = (av.repeat_interleave(w.bq)[:w.N] if alpha_mode else av.expand(w.N))
+        crit_t = torch.from_numpy(token_mask(mask[0, h] == 1, w.N, w.bq, w.bkv))
+        o = _torch_sla2(q, k, v, a_rows, crit_t, feat)
+        (o * torch.from_numpy(dO[0, h])).sum().backward()
+        for got, ref in ((dQ[0, h], q.grad), (dK[0, h], k.grad), (dV[0, h], v.grad),
+                         (da[h], av.grad)):
+            ref = ref.numpy()
+            assert np.abs(got - ref).max() <= 1e-10 * max(1.0, np.abs(ref).max())
+
+
+def test_backward_vs_finite_differences(orc):
+    """Central differences of the forward oracle itself, for sampled entries
+    of Q, K, V and alpha (the selection fixed), each step taken in fp32."""
+    x = small(dtype="f32", N=200, d=8, bq=64, frac=0.4, H=1, seed=6, alpha=(0.55,))
+    w = x.wl
+    p = orc.problem(w.B, w.H, w.N, w.d, w.bq, w.bkv, 0.4, 1, "f32")
+    idx, _, _, _ = orc.route(p, x.q, x.k, x.wq, x.wk)
+    dO = np.random.default_rng(1).normal(0, 1, (1, 1, w.N, w.d))
+    dQ, dK, dV, da = orc.backward(p, x.q, x.k, x.v, idx, x.alpha, dO)
+
+    def loss(q, k, v, al):
+        return (orc.forward_full(p, q, k, v, idx, al) * dO).sum()
+
+    rng = np.random.default_rng(2)
+    h = 1e-3
+    for name, arr, grad in (("q", x.q, dQ), ("k", x.k, dK), ("v", x.v, dV)):
+        for _ in range(6):
+            t, c = int(rng.integers(w.N)), int(rng.integers(w.d))
+            ap, am = arr.copy(), arr.copy()
+            ap[0, 0, t, c] += h
+            am[0, 0, t, c] -= h
+            step = float(ap[0, 0, t, c]) - float(am[0, 0, t, c])
+            args_p = [x.q, x.k, x.v]
+            args_m = [x.q, x.k, x.v]
+            pos = "qkv".index(name)
+            args_p[pos], args_m[pos] = ap, am
+            num = (loss(*args_p, x.alpha) - loss(*args_m, x.alpha)) / step
+            assert abs(grad[0, 0, t, c] - num) <= 1e-5 * max(1.0, abs(num)), (name, t, c)
+    ap, am = x.alpha.copy(), x.alpha.copy()
+    ap[0] += 0.01
+    am[0] -= 0.01
+    num = (loss(x.q, x.k, x.v, ap) - loss(x.q, x.k, x.v, am)) / (float(ap[0]) - float(am[0]))
+    assert abs(da[0] - num) <= 1e-7 * max(1.0, abs(num))
+
+
+# --------------------------------------------------------------------------
 # SoftTop-k and the router gradient (Stage 1 of the training, SLA2 深度解读 06)
 # --------------------------------------------------------------------------
 def _rows(n=6, tkv=40, seed=0, scale=1.0):
