@@ -101,7 +101,8 @@ typedef enum {
     SLA2_OP_FORWARD = 1,       /* sla2_forward               */
     SLA2_OP_FORWARD_FP8 = 2,   /* sla2_forward_fp8           */
     SLA2_OP_SLA1_FORWARD = 3,  /* sla1_forward               */
-    SLA2_OP_ROUTE_GRAD = 4     /* sla2_route_grad            */
+    SLA2_OP_ROUTE_GRAD = 4,    /* sla2_route_grad            */
+    SLA2_OP_BACKWARD = 5       /* sla2_backward              */
 } sla2_op;
 
 typedef struct {
@@ -252,6 +253,28 @@ sla2_status sla2_timing_start(int32_t max_launches);
 sla2_status sla2_timing_stop(float* total_ms, int32_t* launches, int32_t n_kinds);
 int32_t sla2_kernel_kinds(void);
 const char* sla2_kernel_name(int32_t kind);
+
+/*
+ * sla2_backward -- gradients of L = sum dO . O for sla2_forward with the
+ *   selection topk_idx held fixed (the hard top-k has no gradient; "SLA2
+ *   深度解读" 06 fine-tunes the model and alpha with it in Stage 2):
+ *   sparse branch as FlashAttention's backward restricted to the selected
+ *   tokens (p = exp(l - LSE), dl = p (alpha dO . v - alpha dO . O_s));
+ *   linear branch through O_l = n / s with n = phi(q) H_i, s = phi(q) . Z_i,
+ *   so that each block summary h_j, z_j collects the gradients of every
+ *   query block that does not select it (evaluated as the head's total
+ *   minus the selecting query blocks); dalpha = sum of dO . (O_s - O_l) over
+ *   the rows alpha applies to.  phi must be elu + 1 (SLA2_EUNSUPPORTED
+ *   otherwise).  Vector-ALU fp32 arithmetic for every dtype, d and bq.
+ * In : Q, K, V, topk_idx, alpha as sla2_forward; dO fp32 in problem.layout.
+ * Out: dQ, dK, dV fp32 in problem.layout; dalpha [H] or [H][T_q] fp32
+ *      (problem.alpha_mode).  All overwritten.
+ * ws : sla2_workspace_bytes(p, SLA2_OP_BACKWARD) bytes.
+ */
+sla2_status sla2_backward(const sla2_problem* p, const void* Q, const void* K, const void* V,
+                          const int32_t* topk_idx, const float* alpha, const float* dO,
+                          float* dQ, float* dK, float* dV, float* dalpha, void* ws,
+                          size_t ws_bytes, void* stream);
 
 /*
  * Training-time router ("SLA2 深度解读" 06, Stage 1: proj_q, proj_k and alpha

@@ -37,7 +37,7 @@ static sla2_status make_dims(const sla2_problem* p, int op, Dims* D) {
         return SLA2_EINVAL;
     if (p->out_dtype != SLA2_F32 && p->out_dtype != SLA2_BF16) return SLA2_EINVAL;
     if (p->lowbit < SLA2_LOWBIT_QK || p->lowbit > SLA2_LOWBIT_I8QKV) return SLA2_EINVAL;
-    if (op < SLA2_OP_ROUTE || op > SLA2_OP_ROUTE_GRAD) return SLA2_EINVAL;
+    if (op < SLA2_OP_ROUTE || op > SLA2_OP_BACKWARD) return SLA2_EINVAL;
     if (p->d != 64 && p->d != 128) return SLA2_EUNSUPPORTED;
     if (p->bq != 64 && p->bq != 128) return SLA2_EUNSUPPORTED;
     if (p->bkv != 64) return SLA2_EUNSUPPORTED;
@@ -47,6 +47,8 @@ static sla2_status make_dims(const sla2_problem* p, int op, Dims* D) {
         return SLA2_EUNSUPPORTED;
     // softmax phi: the bf16 d = 128, bq = 128 kernels only (routing ignores phi)
     const bool routing = op == SLA2_OP_ROUTE || op == SLA2_OP_ROUTE_GRAD;
+    // the backward takes elu + 1 only
+    if (op == SLA2_OP_BACKWARD && p->phi != SLA2_PHI_ELU1) return SLA2_EUNSUPPORTED;
     if (p->phi == SLA2_PHI_SOFTMAX && (op == SLA2_OP_FORWARD_FP8 || (!routing && !fast)))
         return SLA2_EUNSUPPORTED;
     long bh = (long)p->B * p->H;
@@ -109,6 +111,32 @@ size_t layout_route(const Dims& D, char* base, RouteWS* ws) {
     return align256(off);
 }
 
+size_t layout_backward(const Dims& D, char* base, FwdWS* ws, BwdWS* bw) {
+    size_t off = 0;
+    FwdWS w;
+    memset(&w, 0, sizeof(w));
+    const size_t bh = (size_t)D.BH, d = D.d, n = (size_t)D.N;
+    const int nch = summ_chunks(D);
+    w.hpart = carve<float>(base, off, 4 * bh * nch * d * d);
+    w.zpart = carve<float>(base, off, 4 * bh * nch * d);
+    w.htot = carve<float>(base, off, 4 * bh * d * d);
+    w.ztot = carve<float>(base, off, 4 * bh * d);
+    BwdWS b;
+    b.lse = carve<float>(base, off, 4 * bh * n);
+    b.D = carve<float>(base, off, 4 * bh * n);
+    b.ds = carve<float>(base, off, 4 * bh * n);
+    b.dn = carve<float>(base, off, 4 * bh * n * d);
+    b.da = carve<float>(base, off, 4 * bh * n);
+    b.dHt = carve<float>(base, off, 4 * bh * d * d);
+    b.dZt = carve<float>(base, off, 4 * bh * d);
+    b.off = carve<int32_t>(base, off, 4 * bh * (D.Tkv + 1));
+    b.cnt = carve<int32_t>(base, off, 4 * bh * D.Tkv);
+    b.list = carve<int32_t>(base, off, 4 * bh * (size_t)D.Tq * (D.k > 0 ? D.k : 1));
+    if (ws) *ws = w;
+    if (bw) *bw = b;
+    return align256(off);
+}
+
 size_t layout_route_grad(const Dims& D, char* base, RouteWS* ws, GradWS* gw) {
     size_t off = layout_route(D, base, ws);
     GradWS g;
@@ -157,6 +185,7 @@ size_t layout_forward(const Dims& D, int op, char* base, FwdWS* ws) {
 static size_t ws_bytes_of(const Dims& D, int op) {
     if (op == SLA2_OP_ROUTE) return layout_route(D, nullptr, nullptr);
     if (op == SLA2_OP_ROUTE_GRAD) return layout_route_grad(D, nullptr, nullptr, nullptr);
+    if (op == SLA2_OP_BACKWARD) return layout_backward(D, nullptr, nullptr, nullptr);
     return layout_forward(D, op, nullptr, nullptr);
 }
 
@@ -179,7 +208,8 @@ const char* kKindNames[K_NUM_KINDS] = {
     "pool_project", "score",       "topk_select", "summaries_valu",
     "summaries_reduce", "fused_valu", "summaries_mfma", "fused_mfma",
     "quant_mean",   "quant_fp8",   "fused_fp8",  "quant_v_fp8",
-    "quant_i8",     "fused_i8",    "fused_sla1",
+    "quant_i8",     "fused_i8",    "fused_sla1",  "bwd_rows",
+    "bwd_dh",       "bwd_keys",
 };
 }  // namespace
 
@@ -457,6 +487,26 @@ SLA2_API sla2_status sla2_route_grad(const sla2_problem* p, const void* Q, const
     GradWS g;
     layout_route_grad(D, (char*)ws, &w, &g);
     hipError_t e = launch_route_grad(D, Q, K, Wq, Wk, dS, dWq, dWk, w, g, (hipStream_t)stream);
+    return e == hipSuccess ? SLA2_OK : SLA2_EHIP;
+}
+
+SLA2_API sla2_status sla2_backward(const sla2_problem* p, const void* Q, const void* K,
+                                   const void* V, const int32_t* topk_idx, const float* alpha,
+                                   const float* dO, float* dQ, float* dK, float* dV,
+                                   float* dalpha, void* ws, size_t ws_bytes, void* stream) {
+    Dims D;
+    sla2_status st = make_dims(p, SLA2_OP_BACKWARD, &D);
+    if (st != SLA2_OK) return st;
+    if (!ok_ptr(Q) || !ok_ptr(K) || !ok_ptr(V) || !ok_ptr(alpha) || !ok_ptr(dO) ||
+        !ok_ptr(dQ) || !ok_ptr(dK) || !ok_ptr(dV) || !ok_ptr(dalpha))
+        return SLA2_EINVAL;
+    if (D.k > 0 && !ok_ptr(topk_idx)) return SLA2_EINVAL;
+    if ((st = check_ws(D, SLA2_OP_BACKWARD, ws, ws_bytes)) != SLA2_OK) return st;
+    FwdWS w;
+    BwdWS b;
+    layout_backward(D, (char*)ws, &w, &b);
+    hipError_t e = launch_backward(D, Q, K, V, dO, topk_idx, alpha, dQ, dK, dV, dalpha, w, b,
+                                   (hipStream_t)stream);
     return e == hipSuccess ? SLA2_OK : SLA2_EHIP;
 }
 

@@ -28,6 +28,9 @@ enum KernelKind {
     K_QUANT_I8,
     K_FUSED_I8,
     K_FUSED_SLA1,
+    K_BWD_ROWS,
+    K_BWD_DH,
+    K_BWD_KEYS,
     K_NUM_KINDS
 };
 
@@ -127,6 +130,21 @@ struct FwdWS {
     uint16_t* wpf;   // [w_heads][4 m-tiles][8 k-steps][64 lanes][8]
 };
 
+// backward (SLA2_OP_BACKWARD: the forward's summary buffers, then these)
+struct BwdWS {
+    float* lse;     // [BH][N]  log-sum-exp of each row's selected logits
+    float* D;       // [BH][N]  alpha dO . O_s
+    float* ds;      // [BH][N]  dL/d(denominator of O_l)
+    float* dn;      // [BH][N][d] dL/d(numerator of O_l)
+    float* da;      // [BH][N]  dO . (O_s - O_l)
+    float* dHt;     // [BH][d][d] sum_t phi(q_t)^T dn_t
+    float* dZt;     // [BH][d]    sum_t phi(q_t) ds_t
+    int32_t* off;   // [BH][Tkv + 1] query blocks selecting each KV block:
+    int32_t* cnt;   // [BH][Tkv]     offsets, counts,
+    int32_t* list;  // [BH][Tq * k]  and the lists (ascending)
+};
+size_t layout_backward(const Dims& D, char* base, FwdWS* ws, BwdWS* bw);
+
 // router gradient (SLA2_OP_ROUTE_GRAD: the route layout, then these)
 struct GradWS {
     double* dq;  // [BH][Tq][d]   dL/dqt
@@ -179,6 +197,16 @@ hipError_t launch_route_v1(const Dims& D, const void* Q, const void* K, int kl, 
 hipError_t launch_forward_valu(const Dims& D, const void* Q, const void* K, const void* V,
                                const int32_t* idx, const float* alpha, void* O,
                                const FwdWS& ws, hipStream_t s);
+
+// fp32 block summaries (h_tot, z_tot via the chunk partials)
+hipError_t launch_summaries_valu(const Dims& D, const void* K, const void* V, const FwdWS& ws,
+                                 hipStream_t s);
+
+// backward of the SLA2 forward (selection fixed)
+hipError_t launch_backward(const Dims& D, const void* Q, const void* K, const void* V,
+                           const float* dO, const int32_t* idx, const float* alpha, float* dQ,
+                           float* dK, float* dV, float* dalpha, const FwdWS& ws,
+                           const BwdWS& bw, hipStream_t s);
 
 // deterministic reduction of the per-chunk summary partials
 hipError_t launch_summaries_reduce(const Dims& D, const FwdWS& ws, hipStream_t s);

@@ -255,21 +255,28 @@ hipError_t launch_summaries_reduce(const Dims& D, const FwdWS& ws, hipStream_t s
     return hipGetLastError();
 }
 
+hipError_t launch_summaries_valu(const Dims& D, const void* K, const void* V, const FwdWS& ws,
+                                 hipStream_t s) {
+    const int nch = summ_chunks(D);
+    timing_before(s, K_SUMM_VALU);
+    if (D.dtype == SLA2_F32)
+        summaries_valu_kernel<float><<<dim3(nch, (unsigned)D.BH), 256, 0, s>>>(
+            (const float*)K, (const float*)V, ws.hpart, ws.zpart, D.N, D.d, nch, D.H, D.st);
+    else
+        summaries_valu_kernel<uint16_t><<<dim3(nch, (unsigned)D.BH), 256, 0, s>>>(
+            (const uint16_t*)K, (const uint16_t*)V, ws.hpart, ws.zpart, D.N, D.d, nch, D.H,
+            D.st);
+    timing_after(s, K_SUMM_VALU);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    return launch_summaries_reduce(D, ws, s);
+}
+
 hipError_t launch_forward_valu(const Dims& D, const void* Q, const void* K, const void* V,
                                const int32_t* idx, const float* alpha, void* O,
                                const FwdWS& ws, hipStream_t s) {
-    const int nch = summ_chunks(D);
     if (D.k < D.Tkv) {
-        timing_before(s, K_SUMM_VALU);
-        if (D.dtype == SLA2_F32)
-            summaries_valu_kernel<float><<<dim3(nch, (unsigned)D.BH), 256, 0, s>>>(
-                (const float*)K, (const float*)V, ws.hpart, ws.zpart, D.N, D.d, nch, D.H, D.st);
-        else
-            summaries_valu_kernel<uint16_t><<<dim3(nch, (unsigned)D.BH), 256, 0, s>>>(
-                (const uint16_t*)K, (const uint16_t*)V, ws.hpart, ws.zpart, D.N, D.d, nch, D.H,
-                D.st);
-        timing_after(s, K_SUMM_VALU);
-        hipError_t e = launch_summaries_reduce(D, ws, s);
+        hipError_t e = launch_summaries_valu(D, K, V, ws, s);
         if (e != hipSuccess) return e;
     }
     dim3 g(D.Tq * (D.bq / 32), (unsigned)D.BH);

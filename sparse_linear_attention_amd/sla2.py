@@ -16,7 +16,7 @@ LIB_PATH = os.path.join(PKG, "libsla2.so")
 OK, EINVAL, EUNSUPPORTED, EWORKSPACE, EHIP = range(5)
 F32, BF16 = 0, 1
 PHI_ELU1, PHI_SOFTMAX = 0, 1
-OP_ROUTE, OP_FORWARD, OP_FORWARD_FP8, OP_SLA1_FORWARD, OP_ROUTE_GRAD = 0, 1, 2, 3, 4
+OP_ROUTE, OP_FORWARD, OP_FORWARD_FP8, OP_SLA1_FORWARD, OP_ROUTE_GRAD, OP_BACKWARD = range(6)
 LAYOUT_BHND, LAYOUT_BNHD = 0, 1
 ALPHA_PER_HEAD, ALPHA_PER_QBLOCK = 0, 1
 LOWBIT_QK, LOWBIT_QKV, LOWBIT_I8QK, LOWBIT_I8QKV = 0, 1, 2, 3
@@ -71,6 +71,7 @@ def lib():
         L.sla2_soft_topk.argtypes = [P, vp, vp, vp, vp, C.c_float, vp, vp, vp, C.c_size_t, vp]
         L.sla2_soft_topk_grad.argtypes = [P, vp, vp, C.c_float, vp, vp]
         L.sla2_route_grad.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, C.c_size_t, vp]
+        L.sla2_backward.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, C.c_size_t, vp]
         L.sla1_route.argtypes = [P, vp, vp, C.c_float, vp, vp, vp, vp, C.c_size_t, vp]
         L.sla1_forward.argtypes = [P, vp, vp, vp, vp, vp, C.c_float, vp, vp, vp, C.c_size_t, vp]
         _lib = L
@@ -81,7 +82,8 @@ EXPORTS = ("sla2_num_q_blocks", "sla2_num_kv_blocks", "sla2_topk", "sla2_workspa
            "sla2_check", "sla2_status_str", "sla2_route", "sla2_forward", "sla2_forward_fp8",
            "sla2_quantize_fp8", "sla2_quantize_v_fp8", "sla2_timing_start", "sla2_timing_stop",
            "sla2_kernel_kinds", "sla2_kernel_name", "sla1_num_negligible", "sla1_route",
-           "sla1_forward", "sla2_soft_topk", "sla2_soft_topk_grad", "sla2_route_grad")
+           "sla1_forward", "sla2_soft_topk", "sla2_soft_topk_grad", "sla2_route_grad",
+           "sla2_backward")
 
 
 def _dtype(x):
@@ -193,6 +195,27 @@ def sla1_forward(p, Q, K, V, crit_idx, negl_idx, low_frac, Wp, O, ws=None, strea
     _raise(lib().sla1_forward(C.byref(p), _ptr(Q), _ptr(K), _ptr(V), _ptr(crit_idx),
                               _ptr(negl_idx), float(low_frac), _ptr(Wp), _ptr(O), wp, wb,
                               _stream(stream)), "sla1_forward")
+
+
+def sla2_backward(p, Q, K, V, topk_idx, alpha, dO, dQ, dK, dV, dalpha, ws=None, stream=None):
+    wp, wb = _ws(ws)
+    _raise(lib().sla2_backward(C.byref(p), _ptr(Q), _ptr(K), _ptr(V), _ptr(topk_idx),
+                               _ptr(alpha), _ptr(dO), _ptr(dQ), _ptr(dK), _ptr(dV),
+                               _ptr(dalpha), wp, wb, _stream(stream)), "sla2_backward")
+
+
+def backward(p: Problem, Q, K, V, topk_idx, alpha, dO, ws=None, stream=None):
+    """Allocates dQ, dK, dV (fp32, the problem's layout), dalpha and the
+    workspace; runs sla2_backward."""
+    import torch
+    f = lambda t: torch.empty(t.shape, dtype=torch.float32, device=t.device)
+    dQ, dK, dV = f(Q), f(K), f(V)
+    dal = torch.empty_like(alpha, dtype=torch.float32)
+    if ws is None:
+        ws = workspace(p, OP_BACKWARD, Q.device)
+    sla2_backward(p, Q, K, V, topk_idx if topk(p) > 0 else None, alpha, dO, dQ, dK, dV, dal,
+                  ws, stream)
+    return dQ, dK, dV, dal
 
 
 def sla2_soft_topk(p, Q, K, Wq, Wk, tau, M, lam=None, ws=None, stream=None):

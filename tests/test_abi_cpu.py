@@ -100,7 +100,9 @@ def test_sla1_counts_and_checks(orc):
     for kw in (dict(dtype=S.F32), dict(bq=64), dict(d=64)):
         assert S.check(p_ok(**kw), S.OP_SLA1_FORWARD) == S.EUNSUPPORTED
     assert S.check(p_ok(), S.OP_ROUTE_GRAD) == S.OK
-    assert S.check(p_ok(), 5) == S.EINVAL
+    assert S.check(p_ok(), S.OP_BACKWARD) == S.OK
+    assert S.check(p_ok(dtype=S.F32, d=64, bq=64), S.OP_BACKWARD) == S.OK
+    assert S.check(p_ok(), 6) == S.EINVAL
     for wh in (1, 2):
         extra = S.workspace_bytes(p_ok(w_heads=wh), S.OP_SLA1_FORWARD) - S.workspace_bytes(
             p_ok(w_heads=wh), S.OP_FORWARD)
@@ -179,6 +181,16 @@ def test_entry_points_validate_before_launching():
                           good, fw, None) == S.EWORKSPACE
     assert L.sla1_forward(C.byref(pf), good, good, good, good, good, C.c_float(0.1), good, good,
                           good, v1w, None) == S.EUNSUPPORTED
+    # backward
+    bw = S.workspace_bytes(p, S.OP_BACKWARD)
+    assert bw > 0
+    assert L.sla2_backward(C.byref(p), good, good, good, good, good, None, good, good, good,
+                           good, good, bw, None) == S.EINVAL  # no dO
+    assert L.sla2_backward(C.byref(p), good, good, good, good, good, good, good, good, good,
+                           good, good, bw - 256, None) == S.EWORKSPACE
+    psm = p_ok(phi=S.PHI_SOFTMAX)
+    assert L.sla2_backward(C.byref(psm), good, good, good, good, good, good, good, good, good,
+                           good, good, bw, None) == S.EUNSUPPORTED
     # training-time router
     assert L.sla2_soft_topk(C.byref(p), good, good, good, good, C.c_float(0.0), good, None, good,
                             ws_need, None) == S.EINVAL  # tau must be > 0

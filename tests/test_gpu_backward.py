@@ -1,0 +1,89 @@
+"""GPU parity of sla2_backward against the CPU oracle's backward, through the
+C ABI.
+
+Both sides differentiate the same forward (same inputs, same selection); the
+GPU works in fp32 and the oracle in fp64, so the bar is relative to each
+tensor's scale: max-abs error <= 2e-4 x max |oracle| for dQ, dK, dV and
+dalpha (fp32 sums over up to a few thousand terms).
+"""
+import numpy as np
+import pytest
+import torch
+
+from sparse_linear_attention_amd import inputs as I
+from sparse_linear_attention_amd import sla2 as S
+from tests.test_gpu_parity import dev, say, to_dev  # noqa: F401
+
+pytestmark = pytest.mark.gpu
+
+REL = 2e-4
+
+CASES = [  # name, dtype, N, H, d, bq, frac, alpha_mode, layout
+    ("f32-d64-bq64", "f32", 700, 2, 64, 64, 0.25, S.ALPHA_PER_HEAD, S.LAYOUT_BHND),
+    ("bf16-d128", "bf16", 1500, 2, 128, 128, 0.1, S.ALPHA_PER_HEAD, S.LAYOUT_BHND),
+    ("bf16-ragged-qblock-alpha", "bf16", 1000, 3, 128, 128, 0.2, S.ALPHA_PER_QBLOCK,
+     S.LAYOUT_BHND),
+    ("bf16-bnhd", "bf16", 900, 2, 128, 64, 0.3, S.ALPHA_PER_HEAD, S.LAYOUT_BNHD),
+    ("k0", "bf16", 640, 2, 128, 128, 0.0, S.ALPHA_PER_HEAD, S.LAYOUT_BHND),
+    ("all-selected", "f32", 500, 2, 64, 64, 1.0, S.ALPHA_PER_HEAD, S.LAYOUT_BHND),
+    ("one-token", "bf16", 1, 2, 128, 128, 1.0, S.ALPHA_PER_HEAD, S.LAYOUT_BHND),
+]
+
+
+def _check(name, got, ref):
+    ref = np.asarray(ref, np.float64)
+    g = np.asarray(got, np.float64)
+    scale = max(np.abs(ref).max(), 1e-30)
+    err = np.abs(g - ref).max()
+    say(f"  {name}: max-abs {err:.2e} (scale {scale:.2e})")
+    assert np.isfinite(g).all()
+    assert err <= REL * scale, (name, err, scale)
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_backward_parity(orc, dev, case):
+    name, dtype, N, H, d, bq, frac, amode, layout = case
+    say(f"case backward {name}: N={N} H={H} d={d} bq={bq} frac={frac}")
+    gen = "centroids" if dtype == "f32" else "smooth"
+    w = I.Workload(name, 1, H, N, d, bq, 64, frac, dtype, gen, seed=13)
+    x = I.make_inputs(w)
+    rng = np.random.default_rng(3)
+    alpha = (rng.uniform(0.2, 0.9, (H, w.Tq)).astype(np.float32) if amode else x.alpha)
+    dO = rng.normal(0, 1, (1, H, N, d)).astype(np.float32)
+    q, k, v, wq, wk, _ = to_dev(x, dev)
+    p = S.problem(1, H, N, d, bq, 64, frac, 1, dtype, layout=layout, alpha_mode=amode)
+    idx, _ = S.route(S.problem(1, H, N, d, bq, 64, frac, 1, dtype), q, k, wq, wk,
+                     want_mask=False)
+    t = ((lambda a: a.permute(0, 2, 1, 3).contiguous()) if layout == S.LAYOUT_BNHD
+         else (lambda a: a))
+    dOd = t(torch.from_numpy(dO).to(dev))
+    dQ, dK, dV, da = S.backward(p, t(q), t(k), t(v), idx, torch.from_numpy(alpha).to(dev), dOd)
+    torch.cuda.synchronize()
+    back = (lambda a: a.permute(0, 2, 1, 3).contiguous()) if layout == S.LAYOUT_BNHD else t
+    op = orc.problem(1, H, N, d, bq, 64, frac, 1, dtype, alpha_mode=amode)
+    oidx = idx.cpu().numpy()
+    rQ, rK, rV, ra = orc.backward(op, x.q, x.k, x.v, oidx, alpha, dO.astype(np.float64))
+    _check("dQ", back(dQ).cpu().numpy(), rQ)
+    _check("dK", back(dK).cpu().numpy(), rK)
+    _check("dV", back(dV).cpu().numpy(), rV)
+    _check("dalpha", da.cpu().numpy(), ra)
+
+
+def test_backward_wan13b_one_head(orc, dev):
+    """One head of the 1.3B shape (N = 32760, k = 16 of 512): every gradient
+    entry against the oracle."""
+    w = I.WAN13B.with_(H=1)
+    x = I.make_inputs(w)
+    q, k, v, wq, wk, al = to_dev(x, dev)
+    p = S.problem(1, 1, w.N, w.d, w.bq, w.bkv, w.topk_frac, 1, w.dtype)
+    idx, _ = S.route(p, q, k, wq, wk, want_mask=False)
+    dO = np.random.default_rng(4).normal(0, 1, (1, 1, w.N, w.d)).astype(np.float32)
+    dQ, dK, dV, da = S.backward(p, q, k, v, idx, al, torch.from_numpy(dO).to(dev))
+    torch.cuda.synchronize()
+    op = orc.problem(1, 1, w.N, w.d, w.bq, w.bkv, w.topk_frac, 1, w.dtype)
+    rQ, rK, rV, ra = orc.backward(op, x.q, x.k, x.v, idx.cpu().numpy(), x.alpha,
+                                  dO.astype(np.float64))
+    _check("dQ", dQ.cpu().numpy(), rQ)
+    _check("dK", dK.cpu().numpy(), rK)
+    _check("dV", dV.cpu().numpy(), rV)
+    _check("dalpha", da.cpu().numpy(), ra)
