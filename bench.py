@@ -15,7 +15,9 @@ Options: --steps K --warmup W; --gpus N (only 1: the path runs on one GPU);
 shape; --no-fp8 skips the extra timings of sla2_forward_fp8 (the low-bit
 sparse branch on the same inputs: e4m3 or int8 Q/K, V bf16 or e4m3);
 --no-sla1 skips the extra timing of the SLA (v1) mode (sla1_route +
-sla1_forward, k_h 5 %, k_l 10 %, softmax phi) on the same inputs; --copy-calibration runs only a plain 1 GiB
+sla1_forward, k_h 5 %, k_l 10 %, softmax phi) on the same inputs;
+--no-train skips the timing of the training-side calls on the same inputs
+(sla2_backward; sla2_soft_topk + sla2_soft_topk_grad + sla2_route_grad); --copy-calibration runs only a plain 1 GiB
 device copy (used to scale rocprofv3 FETCH_SIZE / WRITE_SIZE);
 --counters-summary FETCH WRITE COPY_FETCH COPY_WRITE turns four rocprofv3
 --pmc output folders (the bench, then the copy) into the per-launch HBM
@@ -195,6 +197,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-fp8", action="store_true")
     ap.add_argument("--no-sla1", action="store_true")
+    ap.add_argument("--no-train", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--counters-summary", nargs=4, metavar="DIR")
     args = ap.parse_args()
@@ -381,6 +384,43 @@ def main():
         out["sla1"] = {"k_h": kh1, "k_l": kl1, "phi": "softmax", "ms_per_step": ms1,
                        "tops": dense / (ms1 * 1e-3) / 1e12, "stages_ms": st1}
         del ws1
+
+    if not args.no_train:
+        # training side on the same inputs: the backward with the selection
+        # of the timed steps, and the Stage-1 router calls
+        reps = max(1, min(args.steps, 3))
+        dO = torch.randn((w.B, w.H, w.N, w.d), dtype=torch.float32, device=dev)
+        f32 = lambda: torch.empty((w.B, w.H, w.N, w.d), dtype=torch.float32, device=dev)
+        dQ, dK, dV = f32(), f32(), f32()
+        dal = torch.empty_like(al)
+        wsb = S.workspace(p, S.OP_BACKWARD)
+        M = torch.empty((w.B, w.H, Tq, Tkv), dtype=torch.float32, device=dev)
+        dM = torch.randn_like(M)
+        dSg = torch.empty_like(M)
+        dWq, dWk = torch.empty_like(wq), torch.empty_like(wk)
+        wsg = S.workspace(p, S.OP_ROUTE_GRAD)
+        legs = {
+            "backward": lambda: S.sla2_backward(p, q, k, v, idx, al, dO, dQ, dK, dV, dal, wsb,
+                                                stream),
+            "router_stage1": lambda: (
+                S.sla2_soft_topk(p, q, k, wq, wk, 0.1, M, None, ws_r, stream),
+                S.sla2_soft_topk_grad(p, M, dM, 0.1, dSg, stream),
+                S.sla2_route_grad(p, q, k, wq, wk, dSg, dWq, dWk, wsg, stream)),
+        }
+        out["train"] = {}
+        for name_, fn in legs.items():
+            fn()
+            torch.cuda.synchronize()
+            S.timing_start(64 * reps + 64)
+            ev0.record(stream)
+            for _ in range(reps):
+                fn()
+            ev1.record(stream)
+            torch.cuda.synchronize()
+            stt = {n_: ms_ / c_ for n_, (ms_, c_) in S.timing_stop().items()}
+            out["train"][name_] = {"ms": ev0.elapsed_time(ev1) / reps, "reps": reps,
+                                   "stages_ms": stt}
+        del wsb, wsg
 
     if not args.no_cpu_baseline:
         log("bench: timing the CPU oracle on a sample")
