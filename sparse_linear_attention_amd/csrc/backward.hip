@@ -39,8 +39,9 @@ __device__ inline float row8(float v) {
     return v;
 }
 
-// Query rows: 32 rows per work-group, 8 threads per row (d / 8 channels
-// each).  grid (Tq * bq / 32, BH), 256 threads.
+// Query rows: 32 rows per work-group, 8 threads per row; thread `sub` of a
+// row owns channels sub, sub + 8, ... (d / 8 of them), so that the 8 threads
+// read 8 different LDS banks.  grid (Tq * bq / 32, BH), 256 threads.
 template <typename T>
 __global__ __launch_bounds__(256) void bwd_rows_kernel(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
@@ -57,8 +58,7 @@ __global__ __launch_bounds__(256) void bwd_rows_kernel(
     const int per_blk = bq >> 5;
     const int qb = blockIdx.x / per_blk;
     const int row = threadIdx.x >> 3, sub = threadIdx.x & 7;
-    const int CS = d >> 3;
-    const int c0 = sub * CS;
+    const int CS = d >> 3;  // channels sub, sub + 8, ... (conflict-free LDS reads)
     const long bh = blockIdx.y;
     const int tq = qb * bq + (blockIdx.x % per_blk) * 32 + row;
     const bool valid_q = tq < N;
@@ -73,8 +73,8 @@ __global__ __launch_bounds__(256) void bwd_rows_kernel(
 #pragma unroll
     for (int c = 0; c < 16; ++c) {
         const bool ok = c < CS && valid_q;
-        q[c] = ok ? ldx(Qh + (size_t)tq * st.t + c0 + c) : 0.0f;
-        g[c] = ok ? dOh[(size_t)tq * st.t + c0 + c] : 0.0f;
+        q[c] = ok ? ldx(Qh + (size_t)tq * st.t + sub + 8 * c) : 0.0f;
+        g[c] = ok ? dOh[(size_t)tq * st.t + sub + 8 * c] : 0.0f;
         pq[c] = phi_e(q[c]);
         acc[c] = 0.0f;
         corr[c] = 0.0f;
@@ -110,8 +110,8 @@ __global__ __launch_bounds__(256) void bwd_rows_kernel(
 #pragma unroll
                 for (int c = 0; c < 16; ++c)
                     if (c < CS) {
-                        sp = fmaf(q[c], Kt[u * d + c0 + c], sp);
-                        ap = fmaf(pq[c], Pk[u * d + c0 + c], ap);
+                        sp = fmaf(q[c], Kt[u * d + sub + 8 * c], sp);
+                        ap = fmaf(pq[c], Pk[u * d + sub + 8 * c], ap);
                     }
                 sp = row8(sp);
                 ap = row8(ap);
@@ -122,7 +122,7 @@ __global__ __launch_bounds__(256) void bwd_rows_kernel(
                     zc += ap;
 #pragma unroll
                     for (int c = 0; c < 16; ++c)
-                        if (c < CS) corr[c] = fmaf(ap, Vt[u * d + c0 + c], corr[c]);
+                        if (c < CS) corr[c] = fmaf(ap, Vt[u * d + sub + 8 * c], corr[c]);
                 }
             }
             const float mn = fmaxf(m, tmax);
@@ -135,7 +135,7 @@ __global__ __launch_bounds__(256) void bwd_rows_kernel(
                 l += p;
 #pragma unroll
                 for (int c = 0; c < 16; ++c)
-                    if (c < CS) acc[c] = fmaf(p, Vt[u * d + c0 + c], acc[c]);
+                    if (c < CS) acc[c] = fmaf(p, Vt[u * d + sub + 8 * c], acc[c]);
             }
             m = mn;
             __syncthreads();
@@ -159,11 +159,11 @@ __global__ __launch_bounds__(256) void bwd_rows_kernel(
         // O_l = (phi(q) h_tot - corr) / (phi(q) . z_tot - zc); phi(q) rows in LDS
 #pragma unroll
         for (int c = 0; c < 16; ++c)
-            if (c < CS) Rw[row * d + c0 + c] = pq[c];
+            if (c < CS) Rw[row * d + sub + 8 * c] = pq[c];
         float dz = 0.0f;
 #pragma unroll
         for (int c = 0; c < 16; ++c)
-            if (c < CS) dz = fmaf(pq[c], zT[c0 + c], dz);
+            if (c < CS) dz = fmaf(pq[c], zT[sub + 8 * c], dz);
         den = row8(dz) - zc;
         float num[16];
 #pragma unroll
@@ -176,7 +176,7 @@ __global__ __launch_bounds__(256) void bwd_rows_kernel(
                 const float pv = Rw[row * d + cb + cc];
 #pragma unroll
                 for (int c = 0; c < 16; ++c)
-                    if (c < CS) num[c] = fmaf(pv, Vt[cc * d + c0 + c], num[c]);
+                    if (c < CS) num[c] = fmaf(pv, Vt[cc * d + sub + 8 * c], num[c]);
             }
         }
 #pragma unroll
@@ -194,24 +194,24 @@ __global__ __launch_bounds__(256) void bwd_rows_kernel(
         __syncthreads();
 #pragma unroll
         for (int c = 0; c < 16; ++c)
-            if (c < CS) Rw[row * d + c0 + c] = dn[c];
-        for (int eb = 0; eb < d; eb += 32) {
+            if (c < CS) Rw[row * d + sub + 8 * c] = dn[c];
+        for (int eb = 0; eb < d; eb += 16) {
             __syncthreads();
-            for (int x = threadIdx.x; x < 32 * d; x += 256) {
-                const int cr = x / 32, ec = x % 32;  // Vt[cr][ec] = h_tot[cr][eb + ec]
-                Vt[cr * 32 + ec] = hT[(size_t)cr * d + eb + ec];
+            for (int x = threadIdx.x; x < 16 * d; x += 256) {
+                const int cr = x / 16, ec = x % 16;  // Vt[cr][ec] = h_tot[cr][eb + ec]
+                Vt[cr * 17 + ec] = hT[(size_t)cr * d + eb + ec];
             }
             __syncthreads();
-            for (int ec = 0; ec < 32; ++ec) {
+            for (int ec = 0; ec < 16; ++ec) {
                 const float w = Rw[row * d + eb + ec];
 #pragma unroll
                 for (int c = 0; c < 16; ++c)
-                    if (c < CS) dph[c] = fmaf(Vt[(c0 + c) * 32 + ec], w, dph[c]);
+                    if (c < CS) dph[c] = fmaf(Vt[(sub + 8 * c) * 17 + ec], w, dph[c]);
             }
         }
 #pragma unroll
         for (int c = 0; c < 16; ++c)
-            if (c < CS) dph[c] = fmaf(zT[c0 + c], ds, dph[c]);
+            if (c < CS) dph[c] = fmaf(zT[sub + 8 * c], ds, dph[c]);
         __syncthreads();
     }
     // D = a g . O_s; dalpha row value g . (O_s - O_l)
@@ -240,7 +240,7 @@ __global__ __launch_bounds__(256) void bwd_rows_kernel(
 #pragma unroll
                 for (int c = 0; c < 16; ++c)
                     if (c < CS) {
-                        const float kv = Kt[u * d + c0 + c], vv = Vt[u * d + c0 + c];
+                        const float kv = Kt[u * d + sub + 8 * c], vv = Vt[u * d + sub + 8 * c];
                         sp = fmaf(q[c], kv, sp);
                         dp = fmaf(a * g[c], vv, dp);
                         vd = fmaf(vv, dn[c], vd);
@@ -254,21 +254,21 @@ __global__ __launch_bounds__(256) void bwd_rows_kernel(
 #pragma unroll
                 for (int c = 0; c < 16; ++c)
                     if (c < CS) {
-                        dq[c] = fmaf(dl, Kt[u * d + c0 + c], dq[c]);
-                        if (lin) dph[c] = fmaf(-cc, Pk[u * d + c0 + c], dph[c]);
+                        dq[c] = fmaf(dl, Kt[u * d + sub + 8 * c], dq[c]);
+                        if (lin) dph[c] = fmaf(-cc, Pk[u * d + sub + 8 * c], dph[c]);
                     }
             }
             __syncthreads();
         }
     }
     if (valid_q) {
-        const size_t o = head_base(st, bh, H) + (size_t)tq * st.t + c0;
+        const size_t o = head_base(st, bh, H) + (size_t)tq * st.t + sub;
         const size_t rr = (size_t)bh * N + tq;
 #pragma unroll
         for (int c = 0; c < 16; ++c)
             if (c < CS) {
-                dQ[o + c] = dq[c] + (lin ? dph[c] * dphi_e(q[c]) : 0.0f);
-                dn_out[rr * d + c0 + c] = dn[c];
+                dQ[o + 8 * c] = dq[c] + (lin ? dph[c] * dphi_e(q[c]) : 0.0f);
+                dn_out[rr * d + sub + 8 * c] = dn[c];
             }
         if (sub == 0) {
             lse[rr] = L;
@@ -402,8 +402,7 @@ __global__ __launch_bounds__(256) void bwd_keys_kernel(
     const int j = blockIdx.x >> 1, half = blockIdx.x & 1;
     const long bh = blockIdx.y;
     const int key = threadIdx.x >> 3, sub = threadIdx.x & 7;
-    const int CS = d >> 3;
-    const int c0 = sub * CS;
+    const int CS = d >> 3;  // channels sub, sub + 8, ... (conflict-free LDS reads)
     const int u = j * 64 + half * 32 + key;
     const bool valid_k = u < N;
     const T* Qh = Q + head_base(st, bh, H);
@@ -417,8 +416,8 @@ __global__ __launch_bounds__(256) void bwd_keys_kernel(
 #pragma unroll
     for (int c = 0; c < 16; ++c) {
         const bool ok = c < CS && valid_k;
-        kv[c] = ok ? ldx(Kh + (size_t)u * st.t + c0 + c) : 0.0f;
-        vv[c] = ok ? ldx(Vh + (size_t)u * st.t + c0 + c) : 0.0f;
+        kv[c] = ok ? ldx(Kh + (size_t)u * st.t + sub + 8 * c) : 0.0f;
+        vv[c] = ok ? ldx(Vh + (size_t)u * st.t + sub + 8 * c) : 0.0f;
         pk[c] = phi_e(kv[c]);
         dk[c] = 0.0f;
         dv[c] = 0.0f;
@@ -457,10 +456,10 @@ __global__ __launch_bounds__(256) void bwd_keys_kernel(
 #pragma unroll
                 for (int c = 0; c < 16; ++c)
                     if (c < CS) {
-                        sp = fmaf(kv[c], sQ[rr * d + c0 + c], sp);
-                        dp = fmaf(vv[c], sG[rr * d + c0 + c], dp);
-                        ap = fmaf(pk[c], sP[rr * d + c0 + c], ap);
-                        vd = fmaf(vv[c], sN[rr * d + c0 + c], vd);
+                        sp = fmaf(kv[c], sQ[rr * d + sub + 8 * c], sp);
+                        dp = fmaf(vv[c], sG[rr * d + sub + 8 * c], dp);
+                        ap = fmaf(pk[c], sP[rr * d + sub + 8 * c], ap);
+                        vd = fmaf(vv[c], sN[rr * d + sub + 8 * c], vd);
                     }
                 sp = row8(sp);
                 dp = row8(dp);
@@ -472,11 +471,11 @@ __global__ __launch_bounds__(256) void bwd_keys_kernel(
 #pragma unroll
                 for (int c = 0; c < 16; ++c)
                     if (c < CS) {
-                        dk[c] = fmaf(dl, sQ[rr * d + c0 + c], dk[c]);
-                        dv[c] = fmaf(p, sG[rr * d + c0 + c], dv[c]);
+                        dk[c] = fmaf(dl, sQ[rr * d + sub + 8 * c], dk[c]);
+                        dv[c] = fmaf(p, sG[rr * d + sub + 8 * c], dv[c]);
                         if (lin) {
-                            dv[c] = fmaf(-ap, sN[rr * d + c0 + c], dv[c]);
-                            dph[c] = fmaf(-cc, sP[rr * d + c0 + c], dph[c]);
+                            dv[c] = fmaf(-ap, sN[rr * d + sub + 8 * c], dv[c]);
+                            dph[c] = fmaf(-cc, sP[rr * d + sub + 8 * c], dph[c]);
                         }
                     }
             }
@@ -493,8 +492,8 @@ __global__ __launch_bounds__(256) void bwd_keys_kernel(
 #pragma unroll
                 for (int c = 0; c < 16; ++c)
                     if (c < CS) {
-                        sP[(key & 15) * d + c0 + c] = pk[c];
-                        sN[(key & 15) * d + c0 + c] = vv[c];
+                        sP[(key & 15) * d + sub + 8 * c] = pk[c];
+                        sN[(key & 15) * d + sub + 8 * c] = vv[c];
                     }
             }
             __syncthreads();
@@ -506,23 +505,23 @@ __global__ __launch_bounds__(256) void bwd_keys_kernel(
                     for (int c = 0; c < 16; ++c)
                         if (c < CS) {
                             // dv[e] += phi(k)[cc] dH[cc][e];  dphi[c] += dH[c][cc] v[cc]
-                            dv[c] = fmaf(pc, H0[(size_t)cc * d + c0 + c], dv[c]);
-                            dph[c] = fmaf(H0[(size_t)(c0 + c) * d + cc], vc, dph[c]);
+                            dv[c] = fmaf(pc, H0[(size_t)cc * d + sub + 8 * c], dv[c]);
+                            dph[c] = fmaf(H0[(size_t)(sub + 8 * c) * d + cc], vc, dph[c]);
                         }
                 }
             }
         }
 #pragma unroll
         for (int c = 0; c < 16; ++c)
-            if (c < CS) dph[c] += Z0[c0 + c];
+            if (c < CS) dph[c] += Z0[sub + 8 * c];
     }
     if (valid_k) {
-        const size_t ob = head_base(st, bh, H) + (size_t)u * st.t + c0;
+        const size_t ob = head_base(st, bh, H) + (size_t)u * st.t + sub;
 #pragma unroll
         for (int c = 0; c < 16; ++c)
             if (c < CS) {
-                dK[ob + c] = dk[c] + (lin ? dph[c] * dphi_e(kv[c]) : 0.0f);
-                dV[ob + c] = dv[c];
+                dK[ob + 8 * c] = dk[c] + (lin ? dph[c] * dphi_e(kv[c]) : 0.0f);
+                dV[ob + 8 * c] = dv[c];
             }
     }
 }
