@@ -1,8 +1,9 @@
 """Benchmark of the SLA2 forward pass on one MI355X.
 
 A step is one pass of the whole hot path over one batch: the router
-(sla2_route: pool + projection + score + top-k) and the forward
-(sla2_forward: block summaries, sparse branch, linear branch, combine) on the
+(pool + projection + score + top-k) and the forward (block summaries, sparse
+branch, linear branch, combine), issued as one sla2_attention call (which
+overlaps the block summaries with the router), on the
 Wan2.1-14B-720P attention shape (B=1, H=40, N=75600, d=128, bf16, b_q=128,
 b_kv=64, top-k 3 % = 36 of 1182 KV blocks), with inputs resident in HBM.
 
@@ -240,9 +241,15 @@ def main():
     O = torch.empty((w.B, w.H, w.N, w.d), dtype=torch.float32, device=dev)
     ws_r = S.workspace(p, S.OP_ROUTE)
     ws_f = S.workspace(p, S.OP_FORWARD)
+    ws_a = S.workspace(p, S.OP_ATTENTION)
     stream = torch.cuda.current_stream()
 
+    # one step = sla2_attention: the router and the forward in one call (the
+    # block summaries overlap the router on a helper stream)
     def step():
+        S.sla2_attention(p, q, k, v, wq, wk, al, idx, O, ws_a, stream)
+
+    def step_sequential():
         S.sla2_route(p, q, k, wq, wk, idx, None, ws_r, stream)
         S.sla2_forward(p, q, k, v, idx, al, O, ws_f, stream)
 
@@ -268,6 +275,15 @@ def main():
     kernels = S.timing_stop()
     ms_step = ev0.elapsed_time(ev1) / args.steps
     log(f"bench: {ms_step:.3f} ms/step (wall {1e3 * t_wall / args.steps:.3f})")
+    # the same work as separate sla2_route + sla2_forward calls, for reference
+    for _ in range(args.warmup):
+        step_sequential()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step_sequential()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms_seq = ev0.elapsed_time(ev1) / args.steps
 
     BH = w.B * w.H
     dense = dense_equivalent_flop(w.B, w.H, w.N, w.d)
@@ -313,6 +329,7 @@ def main():
         "roofline": roofline,
         "stages_ms": stages,
         "route_ms": route_ms,
+        "sequential_ms_per_step": ms_seq,
         "forward_ms": fwd_ms,
         "forward_only_tops": dense / (fwd_ms * 1e-3) / 1e12 if fwd_ms else None,
         "sparse_flop_per_step": fl_sparse,

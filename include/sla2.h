@@ -102,7 +102,8 @@ typedef enum {
     SLA2_OP_FORWARD_FP8 = 2,   /* sla2_forward_fp8           */
     SLA2_OP_SLA1_FORWARD = 3,  /* sla1_forward               */
     SLA2_OP_ROUTE_GRAD = 4,    /* sla2_route_grad            */
-    SLA2_OP_BACKWARD = 5       /* sla2_backward              */
+    SLA2_OP_BACKWARD = 5,      /* sla2_backward              */
+    SLA2_OP_ATTENTION = 6      /* sla2_attention             */
 } sla2_op;
 
 typedef struct {
@@ -180,6 +181,23 @@ sla2_status sla2_route(const sla2_problem* p, const void* Q, const void* K,
 sla2_status sla2_forward(const sla2_problem* p, const void* Q, const void* K,
                          const void* V, const int32_t* topk_idx, const float* alpha,
                          void* O, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * sla2_attention -- sla2_route followed by sla2_forward in one call (same
+ *   kernels, bit-identical O and topk_idx).  On the bf16 bq = 128 path the
+ *   block summaries (which read only K and V) run on a helper stream,
+ *   concurrently with the router (Q and K), joined before the fused kernel
+ *   with events; other paths run in sequence.  The helper stream and its two
+ *   events are created once per device on first use (default priority) and
+ *   kept until the process ends; calls on one device from several host
+ *   threads at once are not supported.
+ * In : Q, K, V, Wq, Wk, alpha as sla2_route / sla2_forward.
+ * Out: topk_idx [B,H,T_q,k] (NULL allowed when k = 0); O as sla2_forward.
+ * ws : sla2_workspace_bytes(p, SLA2_OP_ATTENTION) bytes.
+ */
+sla2_status sla2_attention(const sla2_problem* p, const void* Q, const void* K, const void* V,
+                           const float* Wq, const float* Wk, const float* alpha,
+                           int32_t* topk_idx, void* O, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * sla2_forward_fp8 -- as sla2_forward, with the low-bit sparse branch

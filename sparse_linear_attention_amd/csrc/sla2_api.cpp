@@ -3,6 +3,7 @@
 #include <math.h>
 #include <string.h>
 
+#include <mutex>
 #include <vector>
 
 #include "sla2_internal.h"
@@ -37,7 +38,7 @@ static sla2_status make_dims(const sla2_problem* p, int op, Dims* D) {
         return SLA2_EINVAL;
     if (p->out_dtype != SLA2_F32 && p->out_dtype != SLA2_BF16) return SLA2_EINVAL;
     if (p->lowbit < SLA2_LOWBIT_QK || p->lowbit > SLA2_LOWBIT_I8QKV) return SLA2_EINVAL;
-    if (op < SLA2_OP_ROUTE || op > SLA2_OP_BACKWARD) return SLA2_EINVAL;
+    if (op < SLA2_OP_ROUTE || op > SLA2_OP_ATTENTION) return SLA2_EINVAL;
     if (p->d != 64 && p->d != 128) return SLA2_EUNSUPPORTED;
     if (p->bq != 64 && p->bq != 128) return SLA2_EUNSUPPORTED;
     if (p->bkv != 64) return SLA2_EUNSUPPORTED;
@@ -186,6 +187,9 @@ static size_t ws_bytes_of(const Dims& D, int op) {
     if (op == SLA2_OP_ROUTE) return layout_route(D, nullptr, nullptr);
     if (op == SLA2_OP_ROUTE_GRAD) return layout_route_grad(D, nullptr, nullptr, nullptr);
     if (op == SLA2_OP_BACKWARD) return layout_backward(D, nullptr, nullptr, nullptr);
+    if (op == SLA2_OP_ATTENTION)  // route region, then the forward's
+        return layout_route(D, nullptr, nullptr) +
+               layout_forward(D, SLA2_OP_FORWARD, nullptr, nullptr);
     return layout_forward(D, op, nullptr, nullptr);
 }
 
@@ -326,6 +330,72 @@ SLA2_API sla2_status sla2_forward(const sla2_problem* p, const void* Q, const vo
         e = launch_summaries_mfma(D, K, V, w, s);
         if (e == hipSuccess) e = launch_fused_mfma(D, Q, K, topk_idx, alpha, O, w, s);
     }
+    return e == hipSuccess ? SLA2_OK : SLA2_EHIP;
+}
+
+// ---------------------------------------------------------------------------
+// route + forward in one call, the block summaries on a helper stream
+// ---------------------------------------------------------------------------
+namespace {
+struct Side {
+    hipStream_t s = nullptr;
+    hipEvent_t fork = nullptr, join = nullptr;
+};
+constexpr int kMaxDevices = 64;
+Side g_side[kMaxDevices];
+std::mutex g_side_mu;
+
+hipError_t side_stream(Side** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lk(g_side_mu);
+    Side& sd = g_side[dev];
+    if (!sd.s) {
+        // default priority (no priority argument), independent of the null stream
+        if ((e = hipStreamCreateWithFlags(&sd.s, hipStreamNonBlocking)) != hipSuccess) return e;
+        if ((e = hipEventCreateWithFlags(&sd.fork, hipEventDisableTiming)) != hipSuccess) return e;
+        if ((e = hipEventCreateWithFlags(&sd.join, hipEventDisableTiming)) != hipSuccess) return e;
+    }
+    *out = &sd;
+    return hipSuccess;
+}
+}  // namespace
+
+SLA2_API sla2_status sla2_attention(const sla2_problem* p, const void* Q, const void* K,
+                                    const void* V, const float* Wq, const float* Wk,
+                                    const float* alpha, int32_t* topk_idx, void* O, void* ws,
+                                    size_t ws_bytes, void* stream) {
+    Dims D;
+    sla2_status st = make_dims(p, SLA2_OP_ATTENTION, &D);
+    if (st != SLA2_OK) return st;
+    if (!ok_ptr(Q) || !ok_ptr(K) || !ok_ptr(V) || !ok_ptr(Wq) || !ok_ptr(Wk) || !ok_ptr(alpha) ||
+        !ok_ptr(O))
+        return SLA2_EINVAL;
+    if (D.k > 0 && !ok_ptr(topk_idx)) return SLA2_EINVAL;
+    if ((st = check_ws(D, SLA2_OP_ATTENTION, ws, ws_bytes)) != SLA2_OK) return st;
+    RouteWS rw;
+    FwdWS fw;
+    const size_t roff = layout_route(D, (char*)ws, &rw);
+    layout_forward(D, SLA2_OP_FORWARD, (char*)ws + roff, &fw);
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t e;
+    if (D.dtype == SLA2_F32 || D.bq != 128) {  // vector-ALU path: in sequence
+        e = launch_route(D, Q, K, Wq, Wk, topk_idx, nullptr, rw, s);
+        if (e == hipSuccess) e = launch_forward_valu(D, Q, K, V, topk_idx, alpha, O, fw, s);
+        return e == hipSuccess ? SLA2_OK : SLA2_EHIP;
+    }
+    Side* sd = nullptr;
+    if ((e = side_stream(&sd)) != hipSuccess) return SLA2_EHIP;
+    // summaries (K, V) on the helper stream, the router (Q, K) on the caller's
+    if ((e = hipEventRecord(sd->fork, s)) != hipSuccess) return SLA2_EHIP;
+    if ((e = hipStreamWaitEvent(sd->s, sd->fork, 0)) != hipSuccess) return SLA2_EHIP;
+    e = launch_summaries_mfma(D, K, V, fw, sd->s);
+    if (e == hipSuccess) e = hipEventRecord(sd->join, sd->s);
+    if (e == hipSuccess) e = launch_route(D, Q, K, Wq, Wk, topk_idx, nullptr, rw, s);
+    if (e == hipSuccess) e = hipStreamWaitEvent(s, sd->join, 0);
+    if (e == hipSuccess) e = launch_fused_mfma(D, Q, K, topk_idx, alpha, O, fw, s);
     return e == hipSuccess ? SLA2_OK : SLA2_EHIP;
 }
 

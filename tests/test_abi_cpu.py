@@ -102,7 +102,10 @@ def test_sla1_counts_and_checks(orc):
     assert S.check(p_ok(), S.OP_ROUTE_GRAD) == S.OK
     assert S.check(p_ok(), S.OP_BACKWARD) == S.OK
     assert S.check(p_ok(dtype=S.F32, d=64, bq=64), S.OP_BACKWARD) == S.OK
-    assert S.check(p_ok(), 6) == S.EINVAL
+    assert S.check(p_ok(), S.OP_ATTENTION) == S.OK
+    assert S.workspace_bytes(p_ok(), S.OP_ATTENTION) == (
+        S.workspace_bytes(p_ok(), S.OP_ROUTE) + S.workspace_bytes(p_ok(), S.OP_FORWARD))
+    assert S.check(p_ok(), 7) == S.EINVAL
     for wh in (1, 2):
         extra = S.workspace_bytes(p_ok(w_heads=wh), S.OP_SLA1_FORWARD) - S.workspace_bytes(
             p_ok(w_heads=wh), S.OP_FORWARD)

@@ -77,3 +77,24 @@ def test_layout_alpha_and_bf16_output(orc, dev, path, opt):
     tol = TOL["fp8"] if fp8 else TOL[dtype]
     compare_blocks(orc, x, oidx, O, orc.all_blocks(op), tol,
                    variant="fp8" if fp8 else "exact", op=op, alpha=alpha)
+
+
+@pytest.mark.parametrize("path", PATHS[:4], ids=[c[0] for c in PATHS[:4]])
+def test_attention_call_equals_route_then_forward(orc, dev, path):
+    """sla2_attention (router and block summaries overlapped on the bf16 bq =
+    128 path) gives the same selection and the same output bits as
+    sla2_route followed by sla2_forward."""
+    name, dtype, N, d, bq, frac, fp8, lowbit = path
+    gen = "centroids" if dtype == "f32" else "smooth"
+    x = I.make_inputs(I.Workload(name, 1, 3, N, d, bq, 64, frac, dtype, gen, seed=17))
+    say(f"case attention call {name}: N={N} d={d} bq={bq}")
+    q, k, v = (upload(a, dev, S.LAYOUT_BHND) for a in (x.q, x.k, x.v))
+    wq, wk, al = (torch.from_numpy(a).to(dev) for a in (x.wq, x.wk, x.alpha))
+    p = S.problem(1, 3, N, d, bq, 64, frac, 1, dtype)
+    idx0, _ = S.route(p, q, k, wq, wk, want_mask=False)
+    O0 = S.forward(p, q, k, v, idx0, al)
+    for _ in range(2):  # the helper stream and its events are reused
+        idx1, O1 = S.attention(p, q, k, v, wq, wk, al)
+        torch.cuda.synchronize()
+        assert torch.equal(idx0, idx1)
+        assert torch.equal(O0, O1)
