@@ -31,11 +31,19 @@ __device__ inline float ldx(const uint16_t* p) { return __uint_as_float((unsigne
 __device__ inline float phi_e(float x) { return x > 0.0f ? x + 1.0f : expf(x); }
 __device__ inline float dphi_e(float x) { return x > 0.0f ? 1.0f : expf(x); }
 
-// sum over the 8 consecutive lanes that share a row
+// sum over the 8 consecutive lanes that share a row, with DPP lane moves
+// (VALU speed): quad_perm [1,0,3,2] (xor 1), quad_perm [2,3,0,1] (xor 2),
+// then the half-row mirror (lane i <-> 7 - i) adds the other quad's sum; every
+// lane of the 8 ends with the same value
+template <int CTRL>
+__device__ inline float dpp_mov(float v) {
+    return __builtin_bit_cast(
+        float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
 __device__ inline float row8(float v) {
-    v += __shfl_xor(v, 1);
-    v += __shfl_xor(v, 2);
-    v += __shfl_xor(v, 4);
+    v += dpp_mov<0xB1>(v);
+    v += dpp_mov<0x4E>(v);
+    v += dpp_mov<0x141>(v);
     return v;
 }
 
