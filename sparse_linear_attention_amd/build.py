@@ -17,7 +17,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libsla2.so")
 SOURCES = ["sla2_api.cpp", "router.hip", "valu.hip", "mfma.hip", "fused128.hip", "fp8.hip",
-           "train.hip", "backward.hip"]
+           "train.hip", "backward.hip", "backward_mfma.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 FLAGS = [

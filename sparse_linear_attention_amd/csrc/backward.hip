@@ -555,13 +555,31 @@ __global__ void dalpha_kernel(const float* __restrict__ da_row, float* __restric
 
 }  // namespace
 
+hipError_t launch_invert(const Dims& D, const int32_t* idx, const BwdWS& bw, hipStream_t s) {
+    invert_kernel<<<dim3((unsigned)D.BH), 256, 0, s>>>(idx, D.Tq, D.Tkv, D.k, bw.off, bw.cnt,
+                                                       bw.list);
+    return hipGetLastError();
+}
+
+hipError_t launch_dalpha(const Dims& D, const BwdWS& bw, float* dalpha, hipStream_t s) {
+    const int na = D.alpha_qblock ? D.H * D.Tq : D.H;
+    dalpha_kernel<<<dim3((unsigned)na), 64, 0, s>>>(bw.da, dalpha, D.B, D.H, D.N, D.bq, D.Tq,
+                                                    D.alpha_qblock);
+    return hipGetLastError();
+}
+
 hipError_t launch_backward(const Dims& D, const void* Q, const void* K, const void* V,
                            const float* dO, const int32_t* idx, const float* alpha, float* dQ,
                            float* dK, float* dV, float* dalpha, const FwdWS& ws,
                            const BwdWS& bw, hipStream_t s) {
+    hipError_t e = hipSuccess;
+    if (bwd_mfma_path(D)) {
+        e = launch_backward_mfma(D, Q, K, V, dO, idx, alpha, dQ, dK, dV, ws, bw, s);
+        if (e != hipSuccess) return e;
+        return launch_dalpha(D, bw, dalpha, s);
+    }
     const int nch = summ_chunks(D);
     const bool f32 = D.dtype == SLA2_F32;
-    hipError_t e = hipSuccess;
     if (D.k < D.Tkv) {
         e = launch_summaries_valu(D, K, V, ws, s);
         if (e != hipSuccess) return e;
@@ -597,9 +615,10 @@ hipError_t launch_backward(const Dims& D, const void* Q, const void* K, const vo
         e = launch_summaries_reduce(D, r, s);
         if (e != hipSuccess) return e;
     }
-    if (D.k > 0)
-        invert_kernel<<<dim3((unsigned)D.BH), 256, 0, s>>>(idx, D.Tq, D.Tkv, D.k, bw.off, bw.cnt,
-                                                           bw.list);
+    if (D.k > 0) {
+        e = launch_invert(D, idx, bw, s);
+        if (e != hipSuccess) return e;
+    }
     dim3 gk(D.Tkv * 2, (unsigned)D.BH);
     timing_before(s, K_BWD_KEYS);
     if (f32)
@@ -613,10 +632,9 @@ hipError_t launch_backward(const Dims& D, const void* Q, const void* K, const vo
             bw.ds, bw.dn, bw.dHt, bw.dZt, bw.off, bw.list, dK, dV, D.N, D.d, D.bq, D.Tq, D.Tkv,
             D.k, D.H, D.st, D.alpha_qblock);
     timing_after(s, K_BWD_KEYS);
-    const int na = D.alpha_qblock ? D.H * D.Tq : D.H;
-    dalpha_kernel<<<dim3((unsigned)na), 64, 0, s>>>(bw.da, dalpha, D.B, D.H, D.N, D.bq, D.Tq,
-                                                    D.alpha_qblock);
-    return hipGetLastError();
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    return launch_dalpha(D, bw, dalpha, s);
 }
 
 }  // namespace sla2

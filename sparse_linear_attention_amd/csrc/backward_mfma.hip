@@ -1,0 +1,860 @@
+// Backward of the SLA2 forward on the matrix cores: bf16 Q, K, V with
+// d = b_q = 128, b_kv = 64, phi = elu + 1; fp32 dO and gradients; the hard
+// selection is held fixed.  L = sum dO . O, O = alpha O_s + (1 - alpha) O_l
+// ("SLA2 深度解读" 04; SLA notes, key designs 3 and 4: the sparse part
+// backpropagates as in FlashAttention, the linear part by the chain rule with
+// per-block dH, dZ collected by additions).
+//
+// Sparse part, per row t of query block i (g = dO_t, selected tokens u):
+//   P_tu = exp(l_tu - LSE_t), D_t = alpha g . O_s,t,
+//   dl_tu = P_tu (alpha g . v_u - D_t) / sqrt(d);
+//   dq_t = sum_u dl_tu k_u, dk_u = sum_t dl_tu q_t, dv_u = sum_t P_tu alpha g_t.
+// Linear part, per query block i, with H_i = h_tot - sum over the selected
+// blocks of h_j (Z_i likewise), s_t = phi(q_t) . Z_i, O_l,t = phi(q_t) H_i / s_t,
+// e = (1 - alpha) g, dn_t = e / s_t, ds_t = -(e . O_l,t) / s_t:
+//   dphi(q_t) = H_i dn_t + Z_i ds_t;  dH_i = sum_t phi(q_t)^T dn_t,
+//   dZ_i = sum_t phi(q_t) ds_t;  every block summary receives the dH_i of
+//   the query blocks that do not select it, dh_j = dH_tot - sum over the
+//   selecting i of dH_i (dz_j likewise), and passes it to its tokens:
+//   dphi(k_u) = dh_j v_u + dz_j, dv_u += phi(k_u) dh_j.
+//
+// Kernels, in launch order: per-block summaries h_j, z_j and their totals;
+// the linear rows pass (dQ's phi part, dH_i, dZ_i, g . O_l); dH_tot; the
+// selection inverted per KV block; the linear keys pass (dK's phi part and
+// dV's linear part); the sparse rows pass (recomputes LSE and O_s, then dQ);
+// the sparse keys pass (dK, dV over the query blocks that select each KV
+// block).  The two linear passes are fp32 vector-ALU products on LDS tiles.
+// The sparse passes run every product on the bf16 matrix cores (32x32x16):
+// Q, K, V enter exactly; every fp32 operand (P, dl, alpha dO) is split into
+// a bf16 high part and the bf16 rounding of the rest, and the products keep
+// the hi*hi, hi*lo and lo*hi terms (16 significant bits per operand).
+#include "cdna4.h"
+#include "sla2_internal.h"
+
+namespace sla2 {
+namespace {
+using namespace cdna4;
+
+constexpr int kD = 128;
+constexpr int kLd = 129;  // row stride of fp32 LDS matrices: rows and columns hit distinct banks
+constexpr float kLog2e = 1.4426950408889634f;
+
+__device__ inline float bfv(uint16_t b) { return __uint_as_float((unsigned)b << 16); }
+__device__ inline float phi1(float x) { return x > 0.0f ? x + 1.0f : expf(x); }
+// phi'(x) from y = phi(x): 1 where x > 0 (there y > 1), else e^x = y
+__device__ inline float dphi_of(float y) { return fminf(y, 1.0f); }
+
+// sum over the 16 lanes that share t >> 4 (fixed butterfly order)
+__device__ inline float sum16(float v) {
+    v += __shfl_xor(v, 1);
+    v += __shfl_xor(v, 2);
+    v += __shfl_xor(v, 4);
+    v += __shfl_xor(v, 8);
+    return v;
+}
+
+// c[p][q] += sum over kk < K of A(m_p, kk) B(kk, n_q), m_p = ty + 16 p,
+// n_q = tx + 16 q; A(m, kk) = A[m am + kk ak], B(kk, n) = B[kk bk + n bn] in LDS
+template <int MP>
+__device__ inline void tile_gemm(float (&c)[MP][8], const float* A, int am, int ak,
+                                 const float* B, int bk, int bn, int K, int ty, int tx) {
+#pragma unroll 2
+    for (int kk = 0; kk < K; ++kk) {
+        float a[MP], b[8];
+#pragma unroll
+        for (int p = 0; p < MP; ++p) a[p] = A[(ty + 16 * p) * am + kk * ak];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) b[q] = B[kk * bk + (tx + 16 * q) * bn];
+#pragma unroll
+        for (int p = 0; p < MP; ++p)
+#pragma unroll
+            for (int q = 0; q < 8; ++q) c[p][q] = fmaf(a[p], b[q], c[p][q]);
+    }
+}
+
+// acc (16 floats per thread: entries 4 (t + 256 m) .. +3 of a d x d matrix)
+// into an LDS matrix with row stride kLd
+__device__ inline void put_dd(float* dst, const float4 (&acc)[16], int t) {
+#pragma unroll
+    for (int m = 0; m < 16; ++m) {
+        const int x = 4 * (t + 256 * m), r = x >> 7, c = x & 127;
+        dst[r * kLd + c] = acc[m].x;
+        dst[r * kLd + c + 1] = acc[m].y;
+        dst[r * kLd + c + 2] = acc[m].z;
+        dst[r * kLd + c + 3] = acc[m].w;
+    }
+}
+__device__ inline void sub4(float4& a, const float4 b) {
+    a.x -= b.x;
+    a.y -= b.y;
+    a.z -= b.z;
+    a.w -= b.w;
+}
+
+// ---------------------------------------------------------------------------
+// Linear rows pass: one work-group per (head, query block), 256 threads.
+// Writes dQ (the phi chain; the first writer of dQ), dH_i, dZ_i and g . O_l
+// per row into gol.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void bwd_lin_rows_kernel(
+    const uint16_t* __restrict__ Q, const float* __restrict__ dO,
+    const int32_t* __restrict__ idx, const float* __restrict__ alpha,
+    const float* __restrict__ htot, const float* __restrict__ ztot,
+    const float* __restrict__ hblk, const float* __restrict__ zblk, float* __restrict__ dQ,
+    float* __restrict__ dHq, float* __restrict__ dZq, float* __restrict__ gol, int N, int Tq,
+    int Tkv, int k, int H, Strides st, int alpha_qblock) {
+    __shared__ float sH[kD * kLd];  // H_i [c][e]
+    __shared__ float sA[64 * kLd];  // phi(q) of 64 rows [m][c]
+    __shared__ float sB[64 * kLd];  // dn of the same rows [m][e]
+    __shared__ float sZ[kD], sS[64], sDs[64];
+    const int t = threadIdx.x, ty = t >> 4, tx = t & 15;
+    long bh;
+    int qb;
+    if (!head_major_map(blockIdx.x, Tq, &bh, &qb)) return;
+    const long hb = head_base(st, bh, H);
+    const int32_t* sel = idx + ((size_t)bh * Tq + qb) * k;
+    {
+        const float4* ht = reinterpret_cast<const float4*>(htot + (size_t)bh * kD * kD);
+        float4 acc[16];
+#pragma unroll
+        for (int m = 0; m < 16; ++m) acc[m] = ht[t + 256 * m];
+        for (int r = 0; r < k; ++r) {
+            const float4* hj =
+                reinterpret_cast<const float4*>(hblk + ((size_t)bh * Tkv + sel[r]) * kD * kD);
+#pragma unroll
+            for (int m = 0; m < 16; ++m) sub4(acc[m], hj[t + 256 * m]);
+        }
+        put_dd(sH, acc, t);
+        if (t < kD) {
+            float z = ztot[(size_t)bh * kD + t];
+            for (int r = 0; r < k; ++r) z -= zblk[((size_t)bh * Tkv + sel[r]) * kD + t];
+            sZ[t] = z;
+        }
+    }
+    const float a = alpha_of(alpha, bh, H, qb, Tq, alpha_qblock);
+    const float om = 1.0f - a;
+    float dh[8][8], dzp[8];
+#pragma unroll
+    for (int p = 0; p < 8; ++p) {
+        dzp[p] = 0.0f;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) dh[p][q] = 0.0f;
+    }
+    for (int half = 0; half < 2; ++half) {
+        const int m0 = qb * 128 + 64 * half;
+        __syncthreads();  // sH, sZ written; the previous half's reads of sA, sB done
+        for (int x = t; x < 64 * kD; x += 256) {
+            const int m = x >> 7, c = x & 127, tq = m0 + m;
+            sA[m * kLd + c] = tq < N ? phi1(bfv(Q[hb + (size_t)tq * st.t + c])) : 0.0f;
+        }
+        __syncthreads();
+        if (t < 64) {
+            float s = 0.0f;
+            for (int c = 0; c < kD; ++c) s = fmaf(sA[t * kLd + c], sZ[c], s);
+            sS[t] = s;
+        }
+        float n[4][8];
+#pragma unroll
+        for (int p = 0; p < 4; ++p)
+#pragma unroll
+            for (int q = 0; q < 8; ++q) n[p][q] = 0.0f;
+        tile_gemm<4>(n, sA, kLd, 1, sH, kLd, 1, kD, ty, tx);  // phi(q) H_i
+        __syncthreads();                                     // sS
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+            const int m = ty + 16 * p, tq = m0 + m;
+            const bool ok = tq < N;
+            const float inv = ok ? 1.0f / sS[m] : 0.0f;
+            const float* grow = dO + hb + (size_t)(ok ? tq : 0) * st.t;
+            float d1 = 0.0f, d2 = 0.0f;
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                const int e = tx + 16 * q;
+                const float g = ok ? grow[e] : 0.0f;
+                const float ol = n[p][q] * inv, ee = om * g;
+                d1 = fmaf(ee, ol, d1);
+                d2 = fmaf(g, ol, d2);
+                sB[m * kLd + e] = ee * inv;
+            }
+            d1 = sum16(d1);
+            d2 = sum16(d2);
+            if (tx == 0) {
+                sDs[m] = -d1 * inv;
+                if (ok) gol[(size_t)bh * N + tq] = d2;
+            }
+        }
+        __syncthreads();
+        // dphi(q) = dn H_i^T + ds Z_i^T; dQ = dphi phi'(q)
+        float dp[4][8];
+#pragma unroll
+        for (int p = 0; p < 4; ++p)
+#pragma unroll
+            for (int q = 0; q < 8; ++q) dp[p][q] = 0.0f;
+        tile_gemm<4>(dp, sB, kLd, 1, sH, 1, kLd, kD, ty, tx);
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+            const int m = ty + 16 * p, tq = m0 + m;
+            if (tq >= N) continue;
+            float* qo = dQ + hb + (size_t)tq * st.t;
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                const int c = tx + 16 * q;
+                qo[c] = fmaf(sZ[c], sDs[m], dp[p][q]) * dphi_of(sA[m * kLd + c]);
+            }
+        }
+        // dH_i += phi(Q)^T dn, dZ_i += phi(Q)^T ds over these 64 rows
+        tile_gemm<8>(dh, sA, 1, kLd, sB, kLd, 1, 64, ty, tx);
+#pragma unroll
+        for (int p = 0; p < 8; ++p) {
+            const int c = ty + 16 * p;
+#pragma unroll
+            for (int mm = 0; mm < 4; ++mm) {
+                const int m = tx + 16 * mm;
+                dzp[p] = fmaf(sA[m * kLd + c], sDs[m], dzp[p]);
+            }
+        }
+    }
+    float* dHo = dHq + ((size_t)bh * Tq + qb) * kD * kD;
+#pragma unroll
+    for (int p = 0; p < 8; ++p)
+#pragma unroll
+        for (int q = 0; q < 8; ++q) dHo[(ty + 16 * p) * kD + tx + 16 * q] = dh[p][q];
+#pragma unroll
+    for (int p = 0; p < 8; ++p) {
+        const float z = sum16(dzp[p]);
+        if (tx == 0) dZq[((size_t)bh * Tq + qb) * kD + ty + 16 * p] = z;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Linear keys pass: one work-group per (head, KV block j), 256 threads.
+// dh_j = dH_tot - sum over the query blocks selecting j of dH_i (ascending),
+// dz_j likewise; writes dK = (dh_j v_u + dz_j) phi'(k_u) and dV = phi(k_u)
+// dh_j (the first writers of dK and dV).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void bwd_lin_keys_kernel(
+    const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
+    const float* __restrict__ dHt, const float* __restrict__ dZt,
+    const float* __restrict__ dHq, const float* __restrict__ dZq,
+    const int32_t* __restrict__ off, const int32_t* __restrict__ list, float* __restrict__ dK,
+    float* __restrict__ dV, int N, int Tq, int Tkv, int k, int H, Strides st) {
+    __shared__ float sH[kD * kLd];  // dh_j [c][e]
+    __shared__ float sA[64 * kLd];  // V_j [u][e]
+    __shared__ float sB[64 * kLd];  // phi(K_j) [u][c]
+    __shared__ float sZ[kD];
+    const int t = threadIdx.x, ty = t >> 4, tx = t & 15;
+    long bh;
+    int j;
+    if (!head_major_map(blockIdx.x, Tkv, &bh, &j)) return;
+    const long hb = head_base(st, bh, H);
+    const int n0 = k > 0 ? off[(size_t)bh * (Tkv + 1) + j] : 0;
+    const int n1 = k > 0 ? off[(size_t)bh * (Tkv + 1) + j + 1] : 0;
+    const int32_t* L = list + (size_t)bh * Tq * k;
+    {
+        const float4* ht = reinterpret_cast<const float4*>(dHt + (size_t)bh * kD * kD);
+        float4 acc[16];
+#pragma unroll
+        for (int m = 0; m < 16; ++m) acc[m] = ht[t + 256 * m];
+        for (int n = n0; n < n1; ++n) {
+            const float4* hi =
+                reinterpret_cast<const float4*>(dHq + ((size_t)bh * Tq + L[n]) * kD * kD);
+#pragma unroll
+            for (int m = 0; m < 16; ++m) sub4(acc[m], hi[t + 256 * m]);
+        }
+        put_dd(sH, acc, t);
+        if (t < kD) {
+            float z = dZt[(size_t)bh * kD + t];
+            for (int n = n0; n < n1; ++n) z -= dZq[((size_t)bh * Tq + L[n]) * kD + t];
+            sZ[t] = z;
+        }
+    }
+    for (int x = t; x < 64 * kD; x += 256) {
+        const int u = x >> 7, c = x & 127, tok = j * 64 + u;
+        const bool ok = tok < N;
+        sA[u * kLd + c] = ok ? bfv(V[hb + (size_t)tok * st.t + c]) : 0.0f;
+        sB[u * kLd + c] = ok ? phi1(bfv(K[hb + (size_t)tok * st.t + c])) : 0.0f;
+    }
+    __syncthreads();
+    float x4[4][8], y4[4][8];
+#pragma unroll
+    for (int p = 0; p < 4; ++p)
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            x4[p][q] = 0.0f;
+            y4[p][q] = 0.0f;
+        }
+    tile_gemm<4>(x4, sA, kLd, 1, sH, 1, kLd, kD, ty, tx);  // sum_e v[u][e] dh[c][e]
+    tile_gemm<4>(y4, sB, kLd, 1, sH, kLd, 1, kD, ty, tx);  // sum_c phi(k)[u][c] dh[c][e]
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        const int u = ty + 16 * p, tok = j * 64 + u;
+        if (tok >= N) continue;
+        float* ko = dK + hb + (size_t)tok * st.t;
+        float* vo = dV + hb + (size_t)tok * st.t;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            const int c = tx + 16 * q;
+            ko[c] = (x4[p][q] + sZ[c]) * dphi_of(sB[u * kLd + c]);
+            vo[c] = y4[p][q];
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Matrix-core helpers for the sparse passes.
+//
+// Tiles of 64 rows x 128 bf16 channels sit in LDS as [64][256 B] with the
+// 16-byte chunk c of row r at chunk c ^ (r & 15).  frag() reads the A or B
+// operand of a 32x32x16 product along the channels (lane: row, 8 channels);
+// tfrag() reads the operand along the rows (lane: one channel, 8 rows) with
+// two transposed LDS reads.  Its k order (element e = row rowbase + 8 (e/4)
+// + 4 (lane/32) + e%4) is the order in which a 32x32 accumulator holds its
+// rows, so an accumulator's 8 registers 8 h .. 8 h + 7 are the matching
+// operand of rows 16 h .. 16 h + 15 of its tile without any data movement.
+// ---------------------------------------------------------------------------
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+__device__ inline rsrc_t head_rsrc(const void* base) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, -1, 0x00020000);
+}
+__device__ inline void load_lds16(rsrc_t r, uint32_t voff, uint32_t soff, char* dst) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, SLA2_LDS(dst), 16, voff, soff, 0, 0);
+}
+__device__ inline int swz(int r, int c) { return r * 256 + ((c ^ (r & 15)) << 4); }
+__device__ inline bf16x8 frag(const char* tile, int r, int c) {
+    return *reinterpret_cast<const bf16x8*>(tile + swz(r, c));
+}
+__device__ inline bf16x8 tfrag(const char* tile, int rowbase, int chbase, int lane) {
+    const int r = lane & 15, hl = lane >> 5;
+    const int ch = chbase + 16 * ((lane >> 4) & 1) + 4 * (r & 3);
+    const int row = rowbase + 4 * hl + (r >> 2);
+    const int cb = (ch & 7) * 2;
+    const s16x4 lo = lds_read_tr16(tile + swz(row, ch >> 3) + cb);
+    const s16x4 hi = lds_read_tr16(tile + swz(row + 8, ch >> 3) + cb);
+    typedef short s16x8 __attribute__((ext_vector_type(8)));
+    const s16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    return __builtin_bit_cast(bf16x8, v);
+}
+// x = hi + lo with hi = bf16(x), lo = bf16(x - hi)
+__device__ inline void split8(const float* x, bf16x8& hi, bf16x8& lo) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const __bf16 h = (__bf16)x[e];
+        hi[e] = h;
+        lo[e] = (__bf16)(x[e] - (float)h);
+    }
+}
+
+// Rows j*64 .. j*64+63 of a head's [N][128] bf16 matrix (rows rp bytes apart)
+// into a tile by direct-to-LDS loads: piece u = 4 i + w (1 KB) holds rows
+// 4 u .. 4 u + 3; the lane's 16 bytes are chunk (lane & 15) ^ (row & 15) of
+// row 4 u + lane / 16.  Rows past N repeat row N - 1 (their logits are
+// masked).
+__device__ inline uint32_t tile_lane_off(int w, int lane, uint32_t rp) {
+    const int row = 4 * w + (lane >> 4);
+    return (uint32_t)row * rp + ((uint32_t)((lane & 15) ^ (row & 15)) << 4);
+}
+__device__ inline void issue_tile(char* dst, rsrc_t r, int j, int N, int w, int lane,
+                                  uint32_t loff, uint32_t rp) {
+    if (j * 64 + 64 <= N) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            load_lds16(r, loff, (uint32_t)j * 64 * rp + 16 * rp * i, dst + (4 * i + w) * 1024);
+    } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int row = 16 * i + 4 * w + (lane >> 4);
+            const int tok = min(j * 64 + row, N - 1);
+            const uint32_t o = (uint32_t)tok * rp + ((uint32_t)((lane & 15) ^ (row & 15)) << 4);
+            load_lds16(r, o, 0, dst + (4 * i + w) * 1024);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Sparse rows pass: one work-group of 4 waves per (head, query block); wave
+// w owns queries 32 w .. 32 w + 31 (one per lane column).  Two passes over
+// the selected KV tiles (K and V tiles double-buffered in LDS):
+//   1. S^T = K Q^T, online softmax, O_s^T += V^T P^T  ->  LSE, D = alpha g . O_s
+//   2. S^T again, P = exp(S - LSE), dP^T = V (alpha G)^T, dl = P (dP - D) /
+//      sqrt(d), dQ^T += K^T dl^T.
+// LSE is kept in the log2 domain (l2se).  dQ is added to the linear part
+// when `lin` (else written); da = g . O_s - (lin ? da : 0).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void bwd_rows_mfma_kernel(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+    const uint16_t* __restrict__ V, const float* __restrict__ dO,
+    const int32_t* __restrict__ idx, const float* __restrict__ alpha, float* __restrict__ dQ,
+    float* __restrict__ l2se, float* __restrict__ Dv, float* __restrict__ da, int N, int Tq,
+    int k, int H, Strides st, int alpha_qblock, int lin) {
+    __shared__ __attribute__((aligned(1024))) char lds[2 * 32768];  // 2 x (K tile, V tile)
+    const int t = threadIdx.x, lane = t & 63, l32 = lane & 31, hl = lane >> 5;
+    const int w = __builtin_amdgcn_readfirstlane(t >> 6);
+    long bh;
+    int qb;
+    if (!head_major_map(blockIdx.x, Tq, &bh, &qb)) return;
+    const int tq = qb * 128 + 32 * w + l32;
+    const bool valid_q = tq < N;
+    const long hb = head_base(st, bh, H);
+    const float c2 = kLog2e / sqrtf(128.0f);
+    const float isd = 1.0f / sqrtf(128.0f);
+
+    bf16x8 qf[8];  // Q^T operand: query tq, channels 16 ks + 8 hl ..
+    {
+        const uint16_t* qrow = Q + hb + (size_t)(valid_q ? tq : 0) * st.t;
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) {
+            uint4 v = make_uint4(0, 0, 0, 0);
+            if (valid_q) v = *reinterpret_cast<const uint4*>(qrow + 16 * ks + 8 * hl);
+            qf[ks] = __builtin_bit_cast(bf16x8, v);
+        }
+    }
+    const int32_t* sel = idx + ((size_t)bh * Tq + qb) * k;
+    const uint32_t rp = (uint32_t)st.t * 2;
+    const rsrc_t rk = head_rsrc(K + hb), rv = head_rsrc(V + hb);
+    const uint32_t loff = tile_lane_off(w, lane, rp);
+    auto issue = [&](int r) {
+        char* dst = lds + (r & 1) * 32768;
+        issue_tile(dst, rk, sel[r], N, w, lane, loff, rp);
+        issue_tile(dst + 16384, rv, sel[r], N, w, lane, loff, rp);
+    };
+    auto scores = [&](const char* kt, int j, f32x16 (&s)[2]) {
+        s[0] = zero16();
+        s[1] = zero16();
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks)
+#pragma unroll
+            for (int mt = 0; mt < 2; ++mt)
+                s[mt] = mfma_bf16(frag(kt, 32 * mt + l32, 2 * ks + hl), qf[ks], s[mt]);
+        if (j * 64 + 64 > N) {
+#pragma unroll
+            for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+                for (int i = 0; i < 16; ++i)
+                    if (j * 64 + 32 * mt + 8 * (i >> 2) + 4 * hl + (i & 3) >= N)
+                        s[mt][i] = -INFINITY;
+        }
+    };
+
+    // ---- pass 1: LSE and O_s
+    f32x16 o[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) o[i] = zero16();
+    float m2 = -INFINITY, lsum = 0.0f;
+    if (k > 0) issue(0);
+    for (int r = 0; r < k; ++r) {
+        wait_vmcnt<0>();  // tile r has landed (this wave's pieces) ...
+        wg_barrier();     // ... for every wave; all waves are done with tile r - 1
+        if (r + 1 < k) issue(r + 1);
+        const char* kt = lds + (r & 1) * 32768;
+        const char* vt = kt + 16384;
+        f32x16 s[2];
+        scores(kt, sel[r], s);
+        float mx = s[0][0];
+#pragma unroll
+        for (int i = 1; i < 16; ++i) mx = fmaxf(mx, s[0][i]);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[1][i]);
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx),
+                                                         false, false);
+        mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+        const float xm = mx * c2;
+        if (xm > m2) {
+            const float f = exp2f(m2 - xm);
+            lsum *= f;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) o[i][e] *= f;
+            m2 = xm;
+        }
+#pragma unroll
+        for (int kq = 0; kq < 4; ++kq) {
+            float pv[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                pv[e] = exp2f(fmaf(s[kq >> 1][8 * (kq & 1) + e], c2, -m2));
+                lsum += pv[e];
+            }
+            bf16x8 ph, pl;
+            split8(pv, ph, pl);
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt) {
+                const bf16x8 av = tfrag(vt, 16 * kq, 32 * mt, lane);
+                o[mt] = mfma_bf16(av, ph, o[mt]);
+                o[mt] = mfma_bf16(av, pl, o[mt]);
+            }
+        }
+    }
+    const float l_all = lsum + __shfl_xor(lsum, 32);
+    const float L2 = k > 0 ? m2 + log2f(l_all) : 0.0f;
+    const float inv_l = k > 0 ? 1.0f / l_all : 0.0f;
+    const float* grow = dO + hb + (size_t)(valid_q ? tq : 0) * st.t;
+    float go = 0.0f;  // g . O_s over this lane's channels 32 mt + 8 i4 + 4 hl + 0..3
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4) {
+            float4 g = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+            if (valid_q) g = *reinterpret_cast<const float4*>(grow + 32 * mt + 8 * i4 + 4 * hl);
+            go = fmaf(g.x, o[mt][4 * i4], go);
+            go = fmaf(g.y, o[mt][4 * i4 + 1], go);
+            go = fmaf(g.z, o[mt][4 * i4 + 2], go);
+            go = fmaf(g.w, o[mt][4 * i4 + 3], go);
+        }
+    go = (go + __shfl_xor(go, 32)) * inv_l;
+    const float a = alpha_of(alpha, bh, H, qb, Tq, alpha_qblock);
+    const float Dq = a * go;
+
+    // ---- pass 2: dQ
+    bf16x8 gh[8], gl[8];  // (alpha G)^T operand: query tq, channels 16 ks + 8 hl ..
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+        float gv[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) gv[e] = 0.0f;
+        if (valid_q) {
+            const float4 g0 = *reinterpret_cast<const float4*>(grow + 16 * ks + 8 * hl);
+            const float4 g1 = *reinterpret_cast<const float4*>(grow + 16 * ks + 8 * hl + 4);
+            gv[0] = a * g0.x;
+            gv[1] = a * g0.y;
+            gv[2] = a * g0.z;
+            gv[3] = a * g0.w;
+            gv[4] = a * g1.x;
+            gv[5] = a * g1.y;
+            gv[6] = a * g1.z;
+            gv[7] = a * g1.w;
+        }
+        split8(gv, gh[ks], gl[ks]);
+    }
+    f32x16 dq[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dq[i] = zero16();
+    wg_barrier();  // every wave is done with the last tile of pass 1
+    if (k > 0) issue(0);
+    for (int r = 0; r < k; ++r) {
+        wait_vmcnt<0>();
+        wg_barrier();
+        if (r + 1 < k) issue(r + 1);
+        const char* kt = lds + (r & 1) * 32768;
+        const char* vt = kt + 16384;
+        f32x16 s[2];
+        scores(kt, sel[r], s);
+        f32x16 dp[2] = {zero16(), zero16()};
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks)
+#pragma unroll
+            for (int mt = 0; mt < 2; ++mt) {
+                const bf16x8 av = frag(vt, 32 * mt + l32, 2 * ks + hl);
+                dp[mt] = mfma_bf16(av, gh[ks], dp[mt]);
+                dp[mt] = mfma_bf16(av, gl[ks], dp[mt]);
+            }
+#pragma unroll
+        for (int kq = 0; kq < 4; ++kq) {
+            float dl[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int i = 8 * (kq & 1) + e;
+                const float p = exp2f(fmaf(s[kq >> 1][i], c2, -L2));
+                dl[e] = p * (dp[kq >> 1][i] - Dq) * isd;
+            }
+            bf16x8 dh, dlo;
+            split8(dl, dh, dlo);
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt) {
+                const bf16x8 ak = tfrag(kt, 16 * kq, 32 * mt, lane);
+                dq[mt] = mfma_bf16(ak, dh, dq[mt]);
+                dq[mt] = mfma_bf16(ak, dlo, dq[mt]);
+            }
+        }
+    }
+    if (valid_q) {
+        float* qo = dQ + hb + (size_t)tq * st.t;
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+            for (int i4 = 0; i4 < 4; ++i4) {
+                float4* p4 = reinterpret_cast<float4*>(qo + 32 * mt + 8 * i4 + 4 * hl);
+                float4 v = make_float4(dq[mt][4 * i4], dq[mt][4 * i4 + 1], dq[mt][4 * i4 + 2],
+                                       dq[mt][4 * i4 + 3]);
+                if (lin) {
+                    const float4 old = *p4;
+                    v.x += old.x;
+                    v.y += old.y;
+                    v.z += old.z;
+                    v.w += old.w;
+                }
+                *p4 = v;
+            }
+        if (hl == 0) {
+            const size_t rr = (size_t)bh * N + tq;
+            l2se[rr] = L2;
+            Dv[rr] = Dq;
+            da[rr] = lin ? go - da[rr] : go;
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Sparse keys pass: one work-group of 4 waves per (head, KV block j); wave
+// w owns keys 32 (w & 1) .. +31 of the block (one per lane column) and rows
+// 32 (w >> 1) .. +31 of every 64-row stage of the query blocks that select
+// j.  Per stage (Q, alpha dO split into bf16 high and low parts, LSE and D of
+// 64 rows, staged through registers one stage ahead):
+//   S = Q K^T, P = exp(S - LSE), dP = (alpha G) V^T, dl = P (dP - D) / sqrt d,
+//   dV^T += (alpha G)^T P, dK^T += Q^T dl.
+// The two row halves are summed at the end (fixed order); dK and dV are
+// added to the linear parts when `lin` (else written).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void bwd_keys_mfma_kernel(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+    const uint16_t* __restrict__ V, const float* __restrict__ dO,
+    const float* __restrict__ alpha, const float* __restrict__ l2se,
+    const float* __restrict__ Dv, const int32_t* __restrict__ off,
+    const int32_t* __restrict__ list, float* __restrict__ dK, float* __restrict__ dV, int N,
+    int Tq, int Tkv, int k, int H, Strides st, int alpha_qblock, int lin) {
+    __shared__ __attribute__((aligned(1024))) char lds[3 * 16384 + 512];
+    char* const sQ = lds;
+    char* const sGh = lds + 16384;
+    char* const sGl = lds + 32768;
+    float* const sL = reinterpret_cast<float*>(lds + 49152);
+    float* const sD = sL + 64;
+    const int t = threadIdx.x, lane = t & 63, l32 = lane & 31, hl = lane >> 5;
+    const int w = __builtin_amdgcn_readfirstlane(t >> 6);
+    const int kh = w & 1, qh = w >> 1;
+    long bh;
+    int j;
+    if (!head_major_map(blockIdx.x, Tkv, &bh, &j)) return;
+    const int n0 = k > 0 ? off[(size_t)bh * (Tkv + 1) + j] : 0;
+    const int n1 = k > 0 ? off[(size_t)bh * (Tkv + 1) + j + 1] : 0;
+    const int nst = 2 * (n1 - n0);
+    if (nst == 0 && lin) return;  // nothing to add
+    const long hb = head_base(st, bh, H);
+    const int u = j * 64 + 32 * kh + l32;
+    const bool valid_k = u < N;
+    const float c2 = kLog2e / sqrtf(128.0f);
+    const float isd = 1.0f / sqrtf(128.0f);
+
+    bf16x8 kf[8], vf[8];  // K^T and V^T operands: key u, channels 16 ks + 8 hl ..
+    {
+        const uint16_t* krow = K + hb + (size_t)(valid_k ? u : 0) * st.t;
+        const uint16_t* vrow = V + hb + (size_t)(valid_k ? u : 0) * st.t;
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) {
+            uint4 a = make_uint4(0, 0, 0, 0), b = make_uint4(0, 0, 0, 0);
+            if (valid_k) {
+                a = *reinterpret_cast<const uint4*>(krow + 16 * ks + 8 * hl);
+                b = *reinterpret_cast<const uint4*>(vrow + 16 * ks + 8 * hl);
+            }
+            kf[ks] = __builtin_bit_cast(bf16x8, a);
+            vf[ks] = __builtin_bit_cast(bf16x8, b);
+        }
+    }
+    const int32_t* Ls = list + (size_t)bh * Tq * k;
+    uint4 qv[4];
+    float4 gv[8];
+    float lv = INFINITY, dvv = 0.0f, a_st = 0.0f;
+    auto fetch = [&](int s) {
+        const int i = Ls[n0 + (s >> 1)];
+        const int row0 = i * 128 + 64 * (s & 1);
+        a_st = alpha_of(alpha, bh, H, i, Tq, alpha_qblock);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int x = t + 256 * e, tok = row0 + (x >> 4);
+            qv[e] = make_uint4(0, 0, 0, 0);
+            if (tok < N)
+                qv[e] = *reinterpret_cast<const uint4*>(Q + hb + (size_t)tok * st.t + 8 * (x & 15));
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int x = t + 256 * e, tok = row0 + (x >> 5);
+            gv[e] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+            if (tok < N)
+                gv[e] = *reinterpret_cast<const float4*>(dO + hb + (size_t)tok * st.t + 4 * (x & 31));
+        }
+        if (t < 64) {
+            const int tok = row0 + t;
+            lv = tok < N ? l2se[(size_t)bh * N + tok] : INFINITY;
+            dvv = tok < N ? Dv[(size_t)bh * N + tok] : 0.0f;
+        }
+    };
+    typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+    auto put = [&]() {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int x = t + 256 * e;
+            *reinterpret_cast<uint4*>(sQ + swz(x >> 4, x & 15)) = qv[e];
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int x = t + 256 * e, row = x >> 5, c4 = x & 31;
+            const float g[4] = {a_st * gv[e].x, a_st * gv[e].y, a_st * gv[e].z, a_st * gv[e].w};
+            bf16x4 h, l;
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                h[c] = (__bf16)g[c];
+                l[c] = (__bf16)(g[c] - (float)h[c]);
+            }
+            const int o = swz(row, c4 >> 1) + (c4 & 1) * 8;
+            *reinterpret_cast<bf16x4*>(sGh + o) = h;
+            *reinterpret_cast<bf16x4*>(sGl + o) = l;
+        }
+        if (t < 64) {
+            sL[t] = lv;
+            sD[t] = dvv;
+        }
+    };
+
+    f32x16 dk[4], dv[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        dk[i] = zero16();
+        dv[i] = zero16();
+    }
+    const int rb = 32 * qh;
+    if (nst > 0) fetch(0);
+    for (int s = 0; s < nst; ++s) {
+        __syncthreads();  // every wave is done with stage s - 1
+        put();
+        __syncthreads();
+        if (s + 1 < nst) fetch(s + 1);
+        f32x16 sc = zero16(), dp = zero16();
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) {
+            sc = mfma_bf16(frag(sQ, rb + l32, 2 * ks + hl), kf[ks], sc);
+            dp = mfma_bf16(frag(sGh, rb + l32, 2 * ks + hl), vf[ks], dp);
+            dp = mfma_bf16(frag(sGl, rb + l32, 2 * ks + hl), vf[ks], dp);
+        }
+        float p[16], dl[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int qr = rb + 8 * (i >> 2) + 4 * hl + (i & 3);
+            p[i] = exp2f(fmaf(sc[i], c2, -sL[qr]));
+            dl[i] = p[i] * (dp[i] - sD[qr]) * isd;
+        }
+#pragma unroll
+        for (int kq = 0; kq < 2; ++kq) {
+            bf16x8 ph, pl, dh, dlo;
+            split8(p + 8 * kq, ph, pl);
+            split8(dl + 8 * kq, dh, dlo);
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt) {
+                const bf16x8 gth = tfrag(sGh, rb + 16 * kq, 32 * mt, lane);
+                const bf16x8 gtl = tfrag(sGl, rb + 16 * kq, 32 * mt, lane);
+                const bf16x8 qt = tfrag(sQ, rb + 16 * kq, 32 * mt, lane);
+                dv[mt] = mfma_bf16(gth, ph, dv[mt]);
+                dk[mt] = mfma_bf16(qt, dh, dk[mt]);
+                dv[mt] = mfma_bf16(gth, pl, dv[mt]);
+                dk[mt] = mfma_bf16(qt, dlo, dk[mt]);
+                dv[mt] = mfma_bf16(gtl, ph, dv[mt]);
+            }
+        }
+    }
+    // rows 32..63 of every stage (waves qh = 1) onto rows 0..31 (qh = 0)
+    float* red = reinterpret_cast<float*>(lds);  // [kh][mt][16][64 lanes]: 32 KB
+#pragma unroll
+    for (int arr = 0; arr < 2; ++arr) {
+        __syncthreads();
+        if (qh == 1) {
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+                for (int i = 0; i < 16; ++i)
+                    red[((kh * 4 + mt) * 16 + i) * 64 + lane] = arr ? dv[mt][i] : dk[mt][i];
+        }
+        __syncthreads();
+        if (qh == 0) {
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const float x = red[((kh * 4 + mt) * 16 + i) * 64 + lane];
+                    if (arr) dv[mt][i] += x;
+                    else dk[mt][i] += x;
+                }
+        }
+    }
+    if (qh == 0 && valid_k) {
+        float* ko = dK + hb + (size_t)u * st.t;
+        float* vo = dV + hb + (size_t)u * st.t;
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+            for (int i4 = 0; i4 < 4; ++i4) {
+                const int ch = 32 * mt + 8 * i4 + 4 * hl;
+                float4 a = make_float4(dk[mt][4 * i4], dk[mt][4 * i4 + 1], dk[mt][4 * i4 + 2],
+                                       dk[mt][4 * i4 + 3]);
+                float4 b = make_float4(dv[mt][4 * i4], dv[mt][4 * i4 + 1], dv[mt][4 * i4 + 2],
+                                       dv[mt][4 * i4 + 3]);
+                if (lin) {
+                    const float4 ao = *reinterpret_cast<const float4*>(ko + ch);
+                    const float4 bo = *reinterpret_cast<const float4*>(vo + ch);
+                    a.x += ao.x;
+                    a.y += ao.y;
+                    a.z += ao.z;
+                    a.w += ao.w;
+                    b.x += bo.x;
+                    b.y += bo.y;
+                    b.z += bo.z;
+                    b.w += bo.w;
+                }
+                *reinterpret_cast<float4*>(ko + ch) = a;
+                *reinterpret_cast<float4*>(vo + ch) = b;
+            }
+    }
+}
+
+inline dim3 head_major_grid(long BH, int T) { return dim3((unsigned)(BH * 8 * ((T + 7) / 8))); }
+
+}  // namespace
+
+hipError_t launch_backward_mfma(const Dims& D, const void* Q, const void* K, const void* V,
+                                const float* dO, const int32_t* idx, const float* alpha,
+                                float* dQ, float* dK, float* dV, const FwdWS& ws,
+                                const BwdWS& bw, hipStream_t s) {
+    const bool lin = D.k < D.Tkv;
+    const uint16_t* q = static_cast<const uint16_t*>(Q);
+    const uint16_t* kk = static_cast<const uint16_t*>(K);
+    const uint16_t* v = static_cast<const uint16_t*>(V);
+    hipError_t e = hipSuccess;
+    if (lin) {
+        if ((e = launch_summaries_blocks(D, K, V, bw.hblk, bw.zblk, s)) != hipSuccess) return e;
+        if ((e = launch_partials_reduce(D, bw.hblk, bw.zblk, ws.htot, ws.ztot, D.Tkv, s)) !=
+            hipSuccess)
+            return e;
+        timing_before(s, K_BWD_LIN_ROWS);
+        bwd_lin_rows_kernel<<<head_major_grid(D.BH, D.Tq), 256, 0, s>>>(
+            q, dO, idx, alpha, ws.htot, ws.ztot, bw.hblk, bw.zblk, dQ, bw.dHq, bw.dZq, bw.da, D.N,
+            D.Tq, D.Tkv, D.k, D.H, D.st, D.alpha_qblock);
+        timing_after(s, K_BWD_LIN_ROWS);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        if ((e = launch_partials_reduce(D, bw.dHq, bw.dZq, bw.dHt, bw.dZt, D.Tq, s)) != hipSuccess)
+            return e;
+    }
+    if (D.k > 0 && (e = launch_invert(D, idx, bw, s)) != hipSuccess) return e;
+    if (lin) {
+        timing_before(s, K_BWD_LIN_KEYS);
+        bwd_lin_keys_kernel<<<head_major_grid(D.BH, D.Tkv), 256, 0, s>>>(
+            kk, v, bw.dHt, bw.dZt, bw.dHq, bw.dZq, bw.off, bw.list, dK, dV, D.N, D.Tq, D.Tkv, D.k,
+            D.H, D.st);
+        timing_after(s, K_BWD_LIN_KEYS);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    timing_before(s, K_BWD_ROWS_MFMA);
+    bwd_rows_mfma_kernel<<<head_major_grid(D.BH, D.Tq), 256, 0, s>>>(
+        q, kk, v, dO, idx, alpha, dQ, bw.lse, bw.D, bw.da, D.N, D.Tq, D.k, D.H, D.st,
+        D.alpha_qblock, lin ? 1 : 0);
+    timing_after(s, K_BWD_ROWS_MFMA);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if (D.k > 0) {
+        timing_before(s, K_BWD_KEYS_MFMA);
+        bwd_keys_mfma_kernel<<<head_major_grid(D.BH, D.Tkv), 256, 0, s>>>(
+            q, kk, v, dO, alpha, bw.lse, bw.D, bw.off, bw.list, dK, dV, D.N, D.Tq, D.Tkv, D.k,
+            D.H, D.st, D.alpha_qblock, lin ? 1 : 0);
+        timing_after(s, K_BWD_KEYS_MFMA);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+}  // namespace sla2

@@ -116,17 +116,26 @@ size_t layout_backward(const Dims& D, char* base, FwdWS* ws, BwdWS* bw) {
     size_t off = 0;
     FwdWS w;
     memset(&w, 0, sizeof(w));
+    BwdWS b;
+    memset(&b, 0, sizeof(b));
     const size_t bh = (size_t)D.BH, d = D.d, n = (size_t)D.N;
-    const int nch = summ_chunks(D);
-    w.hpart = carve<float>(base, off, 4 * bh * nch * d * d);
-    w.zpart = carve<float>(base, off, 4 * bh * nch * d);
+    const bool mf = bwd_mfma_path(D);
     w.htot = carve<float>(base, off, 4 * bh * d * d);
     w.ztot = carve<float>(base, off, 4 * bh * d);
-    BwdWS b;
+    if (mf) {
+        b.hblk = carve<float>(base, off, 4 * bh * D.Tkv * d * d);
+        b.zblk = carve<float>(base, off, 4 * bh * D.Tkv * d);
+        b.dHq = carve<float>(base, off, 4 * bh * D.Tq * d * d);
+        b.dZq = carve<float>(base, off, 4 * bh * D.Tq * d);
+    } else {
+        const int nch = summ_chunks(D);
+        w.hpart = carve<float>(base, off, 4 * bh * nch * d * d);
+        w.zpart = carve<float>(base, off, 4 * bh * nch * d);
+        b.ds = carve<float>(base, off, 4 * bh * n);
+        b.dn = carve<float>(base, off, 4 * bh * n * d);
+    }
     b.lse = carve<float>(base, off, 4 * bh * n);
     b.D = carve<float>(base, off, 4 * bh * n);
-    b.ds = carve<float>(base, off, 4 * bh * n);
-    b.dn = carve<float>(base, off, 4 * bh * n * d);
     b.da = carve<float>(base, off, 4 * bh * n);
     b.dHt = carve<float>(base, off, 4 * bh * d * d);
     b.dZt = carve<float>(base, off, 4 * bh * d);
@@ -213,7 +222,8 @@ const char* kKindNames[K_NUM_KINDS] = {
     "summaries_reduce", "fused_valu", "summaries_mfma", "fused_mfma",
     "quant_mean",   "quant_fp8",   "fused_fp8",  "quant_v_fp8",
     "quant_i8",     "fused_i8",    "fused_sla1",  "bwd_rows",
-    "bwd_dh",       "bwd_keys",
+    "bwd_dh",       "bwd_keys",    "bwd_lin_rows", "bwd_lin_keys",
+    "bwd_rows_mfma", "bwd_keys_mfma",
 };
 }  // namespace
 

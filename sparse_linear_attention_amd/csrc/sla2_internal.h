@@ -31,6 +31,10 @@ enum KernelKind {
     K_BWD_ROWS,
     K_BWD_DH,
     K_BWD_KEYS,
+    K_BWD_LIN_ROWS,
+    K_BWD_LIN_KEYS,
+    K_BWD_ROWS_MFMA,
+    K_BWD_KEYS_MFMA,
     K_NUM_KINDS
 };
 
@@ -142,7 +146,18 @@ struct BwdWS {
     int32_t* off;   // [BH][Tkv + 1] query blocks selecting each KV block:
     int32_t* cnt;   // [BH][Tkv]     offsets, counts,
     int32_t* list;  // [BH][Tq * k]  and the lists (ascending)
+    // matrix-core path only (bwd_mfma_path): per-block summaries and the
+    // per-query-block gradients of H_i, Z_i
+    float* hblk;    // [BH][Tkv][d][d] h_j
+    float* zblk;    // [BH][Tkv][d]    z_j
+    float* dHq;     // [BH][Tq][d][d]  dL/dH_i
+    float* dZq;     // [BH][Tq][d]     dL/dZ_i
 };
+// the backward runs on the matrix cores for bf16 inputs with d = b_q = 128
+// (b_kv = 64) and phi = elu + 1; other problems take the vector-ALU kernels
+inline bool bwd_mfma_path(const Dims& D) {
+    return D.dtype == SLA2_BF16 && D.d == 128 && D.bq == 128 && D.bkv == 64 && !D.phi_sm;
+}
 size_t layout_backward(const Dims& D, char* base, FwdWS* ws, BwdWS* bw);
 
 // router gradient (SLA2_OP_ROUTE_GRAD: the route layout, then these)
@@ -210,6 +225,21 @@ hipError_t launch_backward(const Dims& D, const void* Q, const void* K, const vo
 
 // deterministic reduction of the per-chunk summary partials
 hipError_t launch_summaries_reduce(const Dims& D, const FwdWS& ws, hipStream_t s);
+// tot[bh] = sum over c < nch of part[bh][c] (d x d), ztot likewise (d), in order
+hipError_t launch_partials_reduce(const Dims& D, const float* part, const float* zpart,
+                                  float* tot, float* ztot, int nch, hipStream_t s);
+// per-KV-block summaries h_j, z_j (fp32) into hblk [BH][Tkv][d][d], zblk [BH][Tkv][d]
+hipError_t launch_summaries_blocks(const Dims& D, const void* K, const void* V, float* hblk,
+                                   float* zblk, hipStream_t s);
+// matrix-core backward (bwd_mfma_path)
+hipError_t launch_backward_mfma(const Dims& D, const void* Q, const void* K, const void* V,
+                                const float* dO, const int32_t* idx, const float* alpha,
+                                float* dQ, float* dK, float* dV, const FwdWS& ws,
+                                const BwdWS& bw, hipStream_t s);
+// the selection inverted per KV block (bw.off, bw.cnt, bw.list)
+hipError_t launch_invert(const Dims& D, const int32_t* idx, const BwdWS& bw, hipStream_t s);
+// dalpha from the per-row values bw.da
+hipError_t launch_dalpha(const Dims& D, const BwdWS& bw, float* dalpha, hipStream_t s);
 
 // bf16 path: MFMA block summaries + MFMA fused kernel (bq = 128)
 hipError_t launch_summaries_mfma(const Dims& D, const void* K, const void* V,

@@ -18,19 +18,20 @@ __device__ inline float ld1(const uint16_t* p) { return __uint_as_float((unsigne
 __device__ inline float phi_f(float x) { return x > 0.0f ? x + 1.0f : expf(x); }
 
 // Per-chunk partial h[c][e] = sum_u phi(K_u)[c] V_u[e] and z[c] = sum_u phi(K_u)[c]
-// over the valid tokens of the chunk.  grid (chunks, BH), 256 threads.
+// over the valid tokens of the chunk (bpc KV blocks).  grid (chunks, BH), 256
+// threads.
 template <typename T>
 __global__ __launch_bounds__(256) void summaries_valu_kernel(
     const T* __restrict__ K, const T* __restrict__ V, float* __restrict__ hpart,
-    float* __restrict__ zpart, int N, int d, int nch, int H, Strides st) {
+    float* __restrict__ zpart, int N, int d, int nch, int H, Strides st, int bpc) {
     __shared__ float pk[32 * 128];
     __shared__ float vv[32 * 128];
     const int chunk = blockIdx.x;
     const long bh = blockIdx.y;
     const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
     const int SB = d >> 4;  // 8 or 4
-    const int t_begin = chunk * kSummBlocksPerChunk * 64;
-    const int t_end = min(N, t_begin + kSummBlocksPerChunk * 64);
+    const int t_begin = chunk * bpc * 64;
+    const int t_end = min(N, t_begin + bpc * 64);
     const T* Kh = K + head_base(st, bh, H);
     const T* Vh = V + head_base(st, bh, H);
     float acc[8][8];
@@ -246,30 +247,45 @@ __global__ __launch_bounds__(256) void fused_valu_kernel(
 
 }  // namespace
 
-hipError_t launch_summaries_reduce(const Dims& D, const FwdWS& ws, hipStream_t s) {
-    const int nch = summ_chunks(D);
+hipError_t launch_partials_reduce(const Dims& D, const float* part, const float* zpart,
+                                  float* tot, float* ztot, int nch, hipStream_t s) {
     timing_before(s, K_SUMM_REDUCE);
     summaries_reduce_kernel<<<dim3((D.d * D.d + 255) / 256, (unsigned)D.BH), 256, 0, s>>>(
-        ws.hpart, ws.zpart, ws.htot, ws.ztot, D.d, nch);
+        part, zpart, tot, ztot, D.d, nch);
     timing_after(s, K_SUMM_REDUCE);
+    return hipGetLastError();
+}
+
+hipError_t launch_summaries_reduce(const Dims& D, const FwdWS& ws, hipStream_t s) {
+    return launch_partials_reduce(D, ws.hpart, ws.zpart, ws.htot, ws.ztot, summ_chunks(D), s);
+}
+
+// per-chunk partials over chunks of bpc KV blocks
+static hipError_t summaries_chunks(const Dims& D, const void* K, const void* V, float* hpart,
+                                   float* zpart, int bpc, hipStream_t s) {
+    const int nch = (D.Tkv + bpc - 1) / bpc;
+    timing_before(s, K_SUMM_VALU);
+    if (D.dtype == SLA2_F32)
+        summaries_valu_kernel<float><<<dim3(nch, (unsigned)D.BH), 256, 0, s>>>(
+            (const float*)K, (const float*)V, hpart, zpart, D.N, D.d, nch, D.H, D.st, bpc);
+    else
+        summaries_valu_kernel<uint16_t><<<dim3(nch, (unsigned)D.BH), 256, 0, s>>>(
+            (const uint16_t*)K, (const uint16_t*)V, hpart, zpart, D.N, D.d, nch, D.H, D.st,
+            bpc);
+    timing_after(s, K_SUMM_VALU);
     return hipGetLastError();
 }
 
 hipError_t launch_summaries_valu(const Dims& D, const void* K, const void* V, const FwdWS& ws,
                                  hipStream_t s) {
-    const int nch = summ_chunks(D);
-    timing_before(s, K_SUMM_VALU);
-    if (D.dtype == SLA2_F32)
-        summaries_valu_kernel<float><<<dim3(nch, (unsigned)D.BH), 256, 0, s>>>(
-            (const float*)K, (const float*)V, ws.hpart, ws.zpart, D.N, D.d, nch, D.H, D.st);
-    else
-        summaries_valu_kernel<uint16_t><<<dim3(nch, (unsigned)D.BH), 256, 0, s>>>(
-            (const uint16_t*)K, (const uint16_t*)V, ws.hpart, ws.zpart, D.N, D.d, nch, D.H,
-            D.st);
-    timing_after(s, K_SUMM_VALU);
-    hipError_t e = hipGetLastError();
+    hipError_t e = summaries_chunks(D, K, V, ws.hpart, ws.zpart, kSummBlocksPerChunk, s);
     if (e != hipSuccess) return e;
     return launch_summaries_reduce(D, ws, s);
+}
+
+hipError_t launch_summaries_blocks(const Dims& D, const void* K, const void* V, float* hblk,
+                                   float* zblk, hipStream_t s) {
+    return summaries_chunks(D, K, V, hblk, zblk, 1, s);
 }
 
 hipError_t launch_forward_valu(const Dims& D, const void* Q, const void* K, const void* V,
