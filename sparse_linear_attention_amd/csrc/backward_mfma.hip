@@ -28,6 +28,8 @@
 // Q, K, V enter exactly; every fp32 operand (P, dl, alpha dO) is split into
 // a bf16 high part and the bf16 rounding of the rest, and the products keep
 // the hi*hi, hi*lo and lo*hi terms (16 significant bits per operand).
+#include <type_traits>
+
 #include "cdna4.h"
 #include "sla2_internal.h"
 
@@ -304,13 +306,14 @@ __global__ __launch_bounds__(256) void bwd_lin_keys_kernel(
 // Matrix-core helpers for the sparse passes.
 //
 // Tiles of 64 rows x 128 bf16 channels sit in LDS as [64][256 B] with the
-// 16-byte chunk c of row r at chunk c ^ (r & 15).  frag() reads the A or B
-// operand of a 32x32x16 product along the channels (lane: row, 8 channels);
-// tfrag() reads the operand along the rows (lane: one channel, 8 rows) with
-// two transposed LDS reads.  Its k order (element e = row rowbase + 8 (e/4)
-// + 4 (lane/32) + e%4) is the order in which a 32x32 accumulator holds its
-// rows, so an accumulator's 8 registers 8 h .. 8 h + 7 are the matching
-// operand of rows 16 h .. 16 h + 15 of its tile without any data movement.
+// 16-byte chunk c of row r at chunk c ^ (r & 15).  A "row operand" of a
+// 32x32x16 product (lane: one row, 8 channels) is one 16-byte read; a
+// "column operand" (lane: one channel, 8 rows) is two transposed 8-byte
+// reads (ds_read_b64_tr_b16).  The column operand's k order (element e = row
+// 8 (e/4) + 4 (lane/32) + e%4 of its 16) is the order in which a 32x32
+// accumulator holds its rows, so registers 8 h .. 8 h + 7 of an accumulator
+// are the matching operand of rows 16 h .. 16 h + 15 with no data movement.
+// The per-lane parts of both addresses are computed once (LaneOffs).
 // ---------------------------------------------------------------------------
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 
@@ -320,43 +323,107 @@ __device__ inline rsrc_t head_rsrc(const void* base) {
 __device__ inline void load_lds16(rsrc_t r, uint32_t voff, uint32_t soff, char* dst) {
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, SLA2_LDS(dst), 16, voff, soff, 0, 0);
 }
-__device__ inline int swz(int r, int c) { return r * 256 + ((c ^ (r & 15)) << 4); }
-__device__ inline bf16x8 frag(const char* tile, int r, int c) {
-    return *reinterpret_cast<const bf16x8*>(tile + swz(r, c));
+__device__ inline void load_lds4(rsrc_t r, uint32_t voff, uint32_t soff, char* dst) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, SLA2_LDS(dst), 4, voff, soff, 0, 0);
 }
-__device__ inline bf16x8 tfrag(const char* tile, int rowbase, int chbase, int lane) {
-    const int r = lane & 15, hl = lane >> 5;
-    const int ch = chbase + 16 * ((lane >> 4) & 1) + 4 * (r & 3);
-    const int row = rowbase + 4 * hl + (r >> 2);
-    const int cb = (ch & 7) * 2;
-    const s16x4 lo = lds_read_tr16(tile + swz(row, ch >> 3) + cb);
-    const s16x4 hi = lds_read_tr16(tile + swz(row + 8, ch >> 3) + cb);
-    typedef short s16x8 __attribute__((ext_vector_type(8)));
-    const s16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-    return __builtin_bit_cast(bf16x8, v);
-}
-// x = hi + lo with hi = bf16(x), lo = bf16(x - hi)
-__device__ inline void split8(const float* x, bf16x8& hi, bf16x8& lo) {
+
+struct LaneOffs {
+    int ro[8];     // row operand, row (base + l32), chunk 2 ks + hl
+    int co[4][2];  // column operand of m-tile mt (channels 32 mt ..), rows +0 / +8
+};
+// row base rb (a multiple of 32) folded in
+__device__ inline void lane_offsets(int lane, int rb, LaneOffs& o) {
+    const int l32 = lane & 31, hl = lane >> 5, r = lane & 15, g1 = (lane >> 4) & 1;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        const __bf16 h = (__bf16)x[e];
-        hi[e] = h;
-        lo[e] = (__bf16)(x[e] - (float)h);
+    for (int ks = 0; ks < 8; ++ks)
+        o.ro[ks] = (rb + l32) * 256 + (((2 * ks + hl) ^ (l32 & 15)) << 4);
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int row = 4 * hl + (r >> 2) + 8 * h;  // within a 16-row group
+            const int chunk = 4 * mt + 2 * g1 + ((r & 3) >> 1);
+            o.co[mt][h] = (rb + row) * 256 + ((chunk ^ row) << 4) + (r & 1) * 8;
+        }
+}
+__device__ inline bf16x8 row_op(const char* tile, const LaneOffs& o, int ks) {
+    return *reinterpret_cast<const bf16x8*>(tile + o.ro[ks]);
+}
+// Column operands of the four m-tiles (channels 32 mt ..) of rows 16 g ..
+// 16 g + 15, for tiles whose LDS address is base (a per-stage VGPR offset,
+// plus the per-lane offsets: a[2 mt + h] = base + co[mt][h]) plus the
+// constant OFF (tile offset + 4096 g).  The eight transposed reads sit in one
+// asm block that waits for them before it ends, so their results are
+// complete when the block returns; the compiler does not see them as reads
+// of the tiles that direct-to-LDS loads fill (it would otherwise wait for
+// every tile load in flight, including the prefetched ones), and the
+// kernels' own vmcnt waits and barriers order them after those loads.
+template <int OFF>
+__device__ inline void col_ops4(const uint32_t (&a)[8], bf16x8 (&out)[4]) {
+    s16x4 r0, r1, r2, r3, r4, r5, r6, r7;
+    asm volatile(
+        "ds_read_b64_tr_b16 %0, %8 offset:%16\n\t"
+        "ds_read_b64_tr_b16 %1, %9 offset:%16\n\t"
+        "ds_read_b64_tr_b16 %2, %10 offset:%16\n\t"
+        "ds_read_b64_tr_b16 %3, %11 offset:%16\n\t"
+        "ds_read_b64_tr_b16 %4, %12 offset:%16\n\t"
+        "ds_read_b64_tr_b16 %5, %13 offset:%16\n\t"
+        "ds_read_b64_tr_b16 %6, %14 offset:%16\n\t"
+        "ds_read_b64_tr_b16 %7, %15 offset:%16\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(r0), "=&v"(r1), "=&v"(r2), "=&v"(r3), "=&v"(r4), "=&v"(r5), "=&v"(r6), "=&v"(r7)
+        : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]),
+          "v"(a[7]), "i"(OFF));
+    typedef short s16x8 __attribute__((ext_vector_type(8)));
+    const s16x4 rr[8] = {r0, r1, r2, r3, r4, r5, r6, r7};
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+        const s16x4 x = rr[2 * mt], y = rr[2 * mt + 1];
+        const s16x8 v = {x[0], x[1], x[2], x[3], y[0], y[1], y[2], y[3]};
+        out[mt] = __builtin_bit_cast(bf16x8, v);
+    }
+}
+__device__ inline uint32_t lds_addr(const void* p) {
+    return (uint32_t)(uintptr_t)SLA2_LDS(p);
+}
+// per-stage column-operand addresses
+__device__ inline void col_addrs(const char* stage, const LaneOffs& o, uint32_t (&a)[8]) {
+    const uint32_t b = lds_addr(stage);
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+        a[2 * mt] = b + (uint32_t)o.co[mt][0];
+        a[2 * mt + 1] = b + (uint32_t)o.co[mt][1];
+    }
+}
+// x = hi + lo with hi = bf16(x), lo = bf16(x - hi), two values per conversion
+__device__ inline void split8(const float* x, bf16x8& hi, bf16x8& lo) {
+    typedef float f32x2 __attribute__((ext_vector_type(2)));
+    typedef __bf16 b16x2 __attribute__((ext_vector_type(2)));
+#pragma unroll
+    for (int e = 0; e < 8; e += 2) {
+        const f32x2 v = {x[e], x[e + 1]};
+        const b16x2 h = __builtin_convertvector(v, b16x2);
+        const f32x2 hf = __builtin_convertvector(h, f32x2);
+        const f32x2 r = {v[0] - hf[0], v[1] - hf[1]};
+        const b16x2 l = __builtin_convertvector(r, b16x2);
+        hi[e] = h[0];
+        hi[e + 1] = h[1];
+        lo[e] = l[0];
+        lo[e + 1] = l[1];
     }
 }
 
-// Rows j*64 .. j*64+63 of a head's [N][128] bf16 matrix (rows rp bytes apart)
-// into a tile by direct-to-LDS loads: piece u = 4 i + w (1 KB) holds rows
-// 4 u .. 4 u + 3; the lane's 16 bytes are chunk (lane & 15) ^ (row & 15) of
-// row 4 u + lane / 16.  Rows past N repeat row N - 1 (their logits are
-// masked).
+// Rows j*64 .. j*64+63 of a head's [rows][128] bf16 matrix (rows rp bytes
+// apart) into a tile by direct-to-LDS loads: piece u = 4 i + w (1 KB) holds
+// rows 4 u .. 4 u + 3; the lane's 16 bytes are chunk (lane & 15) ^ (row & 15)
+// of row 4 u + lane / 16.  Rows at or past n repeat row n - 1.
 __device__ inline uint32_t tile_lane_off(int w, int lane, uint32_t rp) {
     const int row = 4 * w + (lane >> 4);
     return (uint32_t)row * rp + ((uint32_t)((lane & 15) ^ (row & 15)) << 4);
 }
-__device__ inline void issue_tile(char* dst, rsrc_t r, int j, int N, int w, int lane,
+__device__ inline void issue_tile(char* dst, rsrc_t r, int j, int n, int w, int lane,
                                   uint32_t loff, uint32_t rp) {
-    if (j * 64 + 64 <= N) {
+    if (j * 64 + 64 <= n) {
 #pragma unroll
         for (int i = 0; i < 4; ++i)
             load_lds16(r, loff, (uint32_t)j * 64 * rp + 16 * rp * i, dst + (4 * i + w) * 1024);
@@ -364,7 +431,7 @@ __device__ inline void issue_tile(char* dst, rsrc_t r, int j, int N, int w, int 
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int row = 16 * i + 4 * w + (lane >> 4);
-            const int tok = min(j * 64 + row, N - 1);
+            const int tok = min(j * 64 + row, n - 1);
             const uint32_t o = (uint32_t)tok * rp + ((uint32_t)((lane & 15) ^ (row & 15)) << 4);
             load_lds16(r, o, 0, dst + (4 * i + w) * 1024);
         }
@@ -374,20 +441,27 @@ __device__ inline void issue_tile(char* dst, rsrc_t r, int j, int N, int w, int 
 // ---------------------------------------------------------------------------
 // Sparse rows pass: one work-group of 4 waves per (head, query block); wave
 // w owns queries 32 w .. 32 w + 31 (one per lane column).  Two passes over
-// the selected KV tiles (K and V tiles double-buffered in LDS):
+// the selected KV tiles, run as one sequence of 2 k steps whose K and V
+// tiles arrive by direct-to-LDS loads two steps ahead (three buffers):
 //   1. S^T = K Q^T, online softmax, O_s^T += V^T P^T  ->  LSE, D = alpha g . O_s
 //   2. S^T again, P = exp(S - LSE), dP^T = V (alpha G)^T, dl = P (dP - D) /
 //      sqrt(d), dQ^T += K^T dl^T.
-// LSE is kept in the log2 domain (l2se).  dQ is added to the linear part
-// when `lin` (else written); da = g . O_s - (lin ? da : 0).
+// dQ is added to the linear part when `lin` (else written); da = g . O_s -
+// (lin ? da : 0).  For the keys pass it leaves, over the query blocks' whole
+// 128 rows (rows past N: LSE = +inf, D = 0, alpha dO = 0), the log2-domain
+// LSE, D and alpha dO split into bf16 high and low parts.
 // ---------------------------------------------------------------------------
+constexpr int kRStage = 32768;  // K tile, V tile
+constexpr int kRLoads = 8;      // direct loads per wave and step
+
 __global__ __launch_bounds__(256) void bwd_rows_mfma_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, const float* __restrict__ dO,
     const int32_t* __restrict__ idx, const float* __restrict__ alpha, float* __restrict__ dQ,
-    float* __restrict__ l2se, float* __restrict__ Dv, float* __restrict__ da, int N, int Tq,
-    int k, int H, Strides st, int alpha_qblock, int lin) {
-    __shared__ __attribute__((aligned(1024))) char lds[2 * 32768];  // 2 x (K tile, V tile)
+    float* __restrict__ l2se, float* __restrict__ Dv, float* __restrict__ da,
+    uint16_t* __restrict__ Gh, uint16_t* __restrict__ Gl, int N, int Tq, int k, int H,
+    Strides st, int alpha_qblock, int lin) {
+    __shared__ __attribute__((aligned(1024))) char lds[3 * kRStage];
     const int t = threadIdx.x, lane = t & 63, l32 = lane & 31, hl = lane >> 5;
     const int w = __builtin_amdgcn_readfirstlane(t >> 6);
     long bh;
@@ -398,6 +472,8 @@ __global__ __launch_bounds__(256) void bwd_rows_mfma_kernel(
     const long hb = head_base(st, bh, H);
     const float c2 = kLog2e / sqrtf(128.0f);
     const float isd = 1.0f / sqrtf(128.0f);
+    LaneOffs lo;
+    lane_offsets(lane, 0, lo);
 
     bf16x8 qf[8];  // Q^T operand: query tq, channels 16 ks + 8 hl ..
     {
@@ -413,10 +489,20 @@ __global__ __launch_bounds__(256) void bwd_rows_mfma_kernel(
     const uint32_t rp = (uint32_t)st.t * 2;
     const rsrc_t rk = head_rsrc(K + hb), rv = head_rsrc(V + hb);
     const uint32_t loff = tile_lane_off(w, lane, rp);
+    const int nsteps = 2 * k;
+    // step r: tile sel[r] (pass 1) or sel[r - k] (pass 2) into buffer r % 3
     auto issue = [&](int r) {
-        char* dst = lds + (r & 1) * 32768;
-        issue_tile(dst, rk, sel[r], N, w, lane, loff, rp);
-        issue_tile(dst + 16384, rv, sel[r], N, w, lane, loff, rp);
+        char* dst = lds + (r % 3) * kRStage;
+        const int j = sel[r < k ? r : r - k];
+        issue_tile(dst, rk, j, N, w, lane, loff, rp);
+        issue_tile(dst + 16384, rv, j, N, w, lane, loff, rp);
+    };
+    // wait for step r's tiles (this wave's loads, then every wave's)
+    auto arrive = [&](int r) {
+        if (r + 1 < nsteps) wait_vmcnt<kRLoads>();
+        else wait_vmcnt<0>();
+        wg_barrier();  // all waves are also done with step r - 1
+        if (r + 2 < nsteps) issue(r + 2);
     };
     auto scores = [&](const char* kt, int j, f32x16 (&s)[2]) {
         s[0] = zero16();
@@ -425,8 +511,9 @@ __global__ __launch_bounds__(256) void bwd_rows_mfma_kernel(
         for (int ks = 0; ks < 8; ++ks)
 #pragma unroll
             for (int mt = 0; mt < 2; ++mt)
-                s[mt] = mfma_bf16(frag(kt, 32 * mt + l32, 2 * ks + hl), qf[ks], s[mt]);
-        if (j * 64 + 64 > N) {
+                s[mt] = mfma_bf16(row_op(kt + 8192 * mt, lo, ks), qf[ks], s[mt]);
+        if (j * 64 + 64 > N) {  // the ragged last block only
+            asm volatile("" ::: "memory");
 #pragma unroll
             for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
@@ -435,19 +522,19 @@ __global__ __launch_bounds__(256) void bwd_rows_mfma_kernel(
                         s[mt][i] = -INFINITY;
         }
     };
+    if (nsteps > 0) issue(0);
+    if (nsteps > 1) issue(1);
 
     // ---- pass 1: LSE and O_s
     f32x16 o[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) o[i] = zero16();
     float m2 = -INFINITY, lsum = 0.0f;
-    if (k > 0) issue(0);
     for (int r = 0; r < k; ++r) {
-        wait_vmcnt<0>();  // tile r has landed (this wave's pieces) ...
-        wg_barrier();     // ... for every wave; all waves are done with tile r - 1
-        if (r + 1 < k) issue(r + 1);
-        const char* kt = lds + (r & 1) * 32768;
-        const char* vt = kt + 16384;
+        arrive(r);
+        const char* kt = lds + (r % 3) * kRStage;
+        uint32_t ca[8];
+        col_addrs(kt, lo, ca);
         f32x16 s[2];
         scores(kt, sel[r], s);
         float mx = s[0][0];
@@ -460,7 +547,7 @@ __global__ __launch_bounds__(256) void bwd_rows_mfma_kernel(
         mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
         const float xm = mx * c2;
         if (xm > m2) {
-            const float f = exp2f(m2 - xm);
+            const float f = __builtin_amdgcn_exp2f(m2 - xm);
             lsum *= f;
 #pragma unroll
             for (int i = 0; i < 4; ++i)
@@ -468,23 +555,28 @@ __global__ __launch_bounds__(256) void bwd_rows_mfma_kernel(
                 for (int e = 0; e < 16; ++e) o[i][e] *= f;
             m2 = xm;
         }
-#pragma unroll
-        for (int kq = 0; kq < 4; ++kq) {
-            float pv[8];
+        // O_s^T += V^T P^T, k-step kq = keys 16 kq .. 16 kq + 15
+        auto pv = [&](auto kq_c) {
+            constexpr int kq = decltype(kq_c)::value;
+            float pv8[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                pv[e] = exp2f(fmaf(s[kq >> 1][8 * (kq & 1) + e], c2, -m2));
-                lsum += pv[e];
+                pv8[e] = __builtin_amdgcn_exp2f(fmaf(s[kq >> 1][8 * (kq & 1) + e], c2, -m2));
+                lsum += pv8[e];
             }
-            bf16x8 ph, pl;
-            split8(pv, ph, pl);
+            bf16x8 ph, pl, av[4];
+            split8(pv8, ph, pl);
+            col_ops4<16384 + 4096 * kq>(ca, av);
 #pragma unroll
             for (int mt = 0; mt < 4; ++mt) {
-                const bf16x8 av = tfrag(vt, 16 * kq, 32 * mt, lane);
-                o[mt] = mfma_bf16(av, ph, o[mt]);
-                o[mt] = mfma_bf16(av, pl, o[mt]);
+                o[mt] = mfma_bf16(av[mt], ph, o[mt]);
+                o[mt] = mfma_bf16(av[mt], pl, o[mt]);
             }
-        }
+        };
+        pv(std::integral_constant<int, 0>{});
+        pv(std::integral_constant<int, 1>{});
+        pv(std::integral_constant<int, 2>{});
+        pv(std::integral_constant<int, 3>{});
     }
     const float l_all = lsum + __shfl_xor(lsum, 32);
     const float L2 = k > 0 ? m2 + log2f(l_all) : 0.0f;
@@ -508,6 +600,7 @@ __global__ __launch_bounds__(256) void bwd_rows_mfma_kernel(
 
     // ---- pass 2: dQ
     bf16x8 gh[8], gl[8];  // (alpha G)^T operand: query tq, channels 16 ks + 8 hl ..
+    const size_t prow = (size_t)bh * Tq * 128 + (size_t)qb * 128 + 32 * w + l32;  // padded row
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) {
         float gv[8];
@@ -526,47 +619,56 @@ __global__ __launch_bounds__(256) void bwd_rows_mfma_kernel(
             gv[7] = a * g1.w;
         }
         split8(gv, gh[ks], gl[ks]);
+        *reinterpret_cast<bf16x8*>(Gh + prow * 128 + 16 * ks + 8 * hl) = gh[ks];
+        *reinterpret_cast<bf16x8*>(Gl + prow * 128 + 16 * ks + 8 * hl) = gl[ks];
+    }
+    if (hl == 0) {
+        l2se[prow] = valid_q ? L2 : INFINITY;
+        Dv[prow] = valid_q ? Dq : 0.0f;
     }
     f32x16 dq[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) dq[i] = zero16();
-    wg_barrier();  // every wave is done with the last tile of pass 1
-    if (k > 0) issue(0);
-    for (int r = 0; r < k; ++r) {
-        wait_vmcnt<0>();
-        wg_barrier();
-        if (r + 1 < k) issue(r + 1);
-        const char* kt = lds + (r & 1) * 32768;
+    for (int r = k; r < nsteps; ++r) {
+        arrive(r);
+        const char* kt = lds + (r % 3) * kRStage;
         const char* vt = kt + 16384;
+        uint32_t ca[8];
+        col_addrs(kt, lo, ca);
         f32x16 s[2];
-        scores(kt, sel[r], s);
+        scores(kt, sel[r - k], s);
         f32x16 dp[2] = {zero16(), zero16()};
 #pragma unroll
         for (int ks = 0; ks < 8; ++ks)
 #pragma unroll
             for (int mt = 0; mt < 2; ++mt) {
-                const bf16x8 av = frag(vt, 32 * mt + l32, 2 * ks + hl);
+                const bf16x8 av = row_op(vt + 8192 * mt, lo, ks);
                 dp[mt] = mfma_bf16(av, gh[ks], dp[mt]);
                 dp[mt] = mfma_bf16(av, gl[ks], dp[mt]);
             }
-#pragma unroll
-        for (int kq = 0; kq < 4; ++kq) {
+        // dQ^T += K^T dl^T, k-step kq
+        auto kd = [&](auto kq_c) {
+            constexpr int kq = decltype(kq_c)::value;
             float dl[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 const int i = 8 * (kq & 1) + e;
-                const float p = exp2f(fmaf(s[kq >> 1][i], c2, -L2));
+                const float p = __builtin_amdgcn_exp2f(fmaf(s[kq >> 1][i], c2, -L2));
                 dl[e] = p * (dp[kq >> 1][i] - Dq) * isd;
             }
-            bf16x8 dh, dlo;
+            bf16x8 dh, dlo, ak[4];
             split8(dl, dh, dlo);
+            col_ops4<4096 * kq>(ca, ak);
 #pragma unroll
             for (int mt = 0; mt < 4; ++mt) {
-                const bf16x8 ak = tfrag(kt, 16 * kq, 32 * mt, lane);
-                dq[mt] = mfma_bf16(ak, dh, dq[mt]);
-                dq[mt] = mfma_bf16(ak, dlo, dq[mt]);
+                dq[mt] = mfma_bf16(ak[mt], dh, dq[mt]);
+                dq[mt] = mfma_bf16(ak[mt], dlo, dq[mt]);
             }
-        }
+        };
+        kd(std::integral_constant<int, 0>{});
+        kd(std::integral_constant<int, 1>{});
+        kd(std::integral_constant<int, 2>{});
+        kd(std::integral_constant<int, 3>{});
     }
     if (valid_q) {
         float* qo = dQ + hb + (size_t)tq * st.t;
@@ -588,8 +690,6 @@ __global__ __launch_bounds__(256) void bwd_rows_mfma_kernel(
             }
         if (hl == 0) {
             const size_t rr = (size_t)bh * N + tq;
-            l2se[rr] = L2;
-            Dv[rr] = Dq;
             da[rr] = lin ? go - da[rr] : go;
         }
     }
@@ -599,26 +699,24 @@ __global__ __launch_bounds__(256) void bwd_rows_mfma_kernel(
 // Sparse keys pass: one work-group of 4 waves per (head, KV block j); wave
 // w owns keys 32 (w & 1) .. +31 of the block (one per lane column) and rows
 // 32 (w >> 1) .. +31 of every 64-row stage of the query blocks that select
-// j.  Per stage (Q, alpha dO split into bf16 high and low parts, LSE and D of
-// 64 rows, staged through registers one stage ahead):
-//   S = Q K^T, P = exp(S - LSE), dP = (alpha G) V^T, dl = P (dP - D) / sqrt d,
-//   dV^T += (alpha G)^T P, dK^T += Q^T dl.
+// j.  A stage holds Q, the high and low parts of alpha dO, LSE and D of 64
+// rows; stages arrive by direct-to-LDS loads two ahead (three buffers).  Per
+// stage:  S = Q K^T, P = exp(S - LSE), dP = (alpha G) V^T,
+//         dl = P (dP - D) / sqrt d,  dV^T += (alpha G)^T P,  dK^T += Q^T dl.
 // The two row halves are summed at the end (fixed order); dK and dV are
 // added to the linear parts when `lin` (else written).
 // ---------------------------------------------------------------------------
+constexpr int kKStage = 3 * 16384 + 512;
+constexpr int kKLoads = 14;  // direct loads per wave and stage
+
 __global__ __launch_bounds__(256) void bwd_keys_mfma_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
-    const uint16_t* __restrict__ V, const float* __restrict__ dO,
-    const float* __restrict__ alpha, const float* __restrict__ l2se,
+    const uint16_t* __restrict__ V, const uint16_t* __restrict__ Gh,
+    const uint16_t* __restrict__ Gl, const float* __restrict__ l2se,
     const float* __restrict__ Dv, const int32_t* __restrict__ off,
     const int32_t* __restrict__ list, float* __restrict__ dK, float* __restrict__ dV, int N,
-    int Tq, int Tkv, int k, int H, Strides st, int alpha_qblock, int lin) {
-    __shared__ __attribute__((aligned(1024))) char lds[3 * 16384 + 512];
-    char* const sQ = lds;
-    char* const sGh = lds + 16384;
-    char* const sGl = lds + 32768;
-    float* const sL = reinterpret_cast<float*>(lds + 49152);
-    float* const sD = sL + 64;
+    int Tq, int Tkv, int k, int H, Strides st, int lin) {
+    __shared__ __attribute__((aligned(1024))) char lds[3 * kKStage];
     const int t = threadIdx.x, lane = t & 63, l32 = lane & 31, hl = lane >> 5;
     const int w = __builtin_amdgcn_readfirstlane(t >> 6);
     const int kh = w & 1, qh = w >> 1;
@@ -634,6 +732,9 @@ __global__ __launch_bounds__(256) void bwd_keys_mfma_kernel(
     const bool valid_k = u < N;
     const float c2 = kLog2e / sqrtf(128.0f);
     const float isd = 1.0f / sqrtf(128.0f);
+    const int rb = 32 * qh;
+    LaneOffs lo;
+    lane_offsets(lane, rb, lo);
 
     bf16x8 kf[8], vf[8];  // K^T and V^T operands: key u, channels 16 ks + 8 hl ..
     {
@@ -651,57 +752,25 @@ __global__ __launch_bounds__(256) void bwd_keys_mfma_kernel(
         }
     }
     const int32_t* Ls = list + (size_t)bh * Tq * k;
-    uint4 qv[4];
-    float4 gv[8];
-    float lv = INFINITY, dvv = 0.0f, a_st = 0.0f;
-    auto fetch = [&](int s) {
-        const int i = Ls[n0 + (s >> 1)];
-        const int row0 = i * 128 + 64 * (s & 1);
-        a_st = alpha_of(alpha, bh, H, i, Tq, alpha_qblock);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int x = t + 256 * e, tok = row0 + (x >> 4);
-            qv[e] = make_uint4(0, 0, 0, 0);
-            if (tok < N)
-                qv[e] = *reinterpret_cast<const uint4*>(Q + hb + (size_t)tok * st.t + 8 * (x & 15));
-        }
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const int x = t + 256 * e, tok = row0 + (x >> 5);
-            gv[e] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-            if (tok < N)
-                gv[e] = *reinterpret_cast<const float4*>(dO + hb + (size_t)tok * st.t + 4 * (x & 31));
-        }
-        if (t < 64) {
-            const int tok = row0 + t;
-            lv = tok < N ? l2se[(size_t)bh * N + tok] : INFINITY;
-            dvv = tok < N ? Dv[(size_t)bh * N + tok] : 0.0f;
-        }
-    };
-    typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-    auto put = [&]() {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int x = t + 256 * e;
-            *reinterpret_cast<uint4*>(sQ + swz(x >> 4, x & 15)) = qv[e];
-        }
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const int x = t + 256 * e, row = x >> 5, c4 = x & 31;
-            const float g[4] = {a_st * gv[e].x, a_st * gv[e].y, a_st * gv[e].z, a_st * gv[e].w};
-            bf16x4 h, l;
-#pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                h[c] = (__bf16)g[c];
-                l[c] = (__bf16)(g[c] - (float)h[c]);
-            }
-            const int o = swz(row, c4 >> 1) + (c4 & 1) * 8;
-            *reinterpret_cast<bf16x4*>(sGh + o) = h;
-            *reinterpret_cast<bf16x4*>(sGl + o) = l;
-        }
-        if (t < 64) {
-            sL[t] = lv;
-            sD[t] = dvv;
+    const int Np = Tq * 128;
+    const uint32_t rpq = (uint32_t)st.t * 2;
+    const rsrc_t rq = head_rsrc(Q + hb);
+    const rsrc_t rgh = head_rsrc(Gh + (size_t)bh * Np * 128);
+    const rsrc_t rgl = head_rsrc(Gl + (size_t)bh * Np * 128);
+    const rsrc_t rl = head_rsrc(l2se + (size_t)bh * Np);
+    const rsrc_t rd = head_rsrc(Dv + (size_t)bh * Np);
+    const uint32_t loffq = tile_lane_off(w, lane, rpq), loffg = tile_lane_off(w, lane, 256);
+    // stage s: rows 64 (s & 1) .. of query block list[n0 + s / 2] (64-row tile tb)
+    auto issue = [&](int s) {
+        char* dst = lds + (s % 3) * kKStage;
+        const int tb = 2 * Ls[n0 + (s >> 1)] + (s & 1);
+        issue_tile(dst, rq, tb, N, w, lane, loffq, rpq);
+        issue_tile(dst + 16384, rgh, tb, Np, w, lane, loffg, 256);
+        issue_tile(dst + 32768, rgl, tb, Np, w, lane, loffg, 256);
+        if (lane < 16) {  // LSE and D: 16 rows per wave
+            load_lds4(rl, (uint32_t)(16 * w + lane) * 4, (uint32_t)tb * 256, dst + 49152 + 64 * w);
+            load_lds4(rd, (uint32_t)(16 * w + lane) * 4, (uint32_t)tb * 256,
+                      dst + 49152 + 256 + 64 * w);
         }
     };
 
@@ -711,44 +780,57 @@ __global__ __launch_bounds__(256) void bwd_keys_mfma_kernel(
         dk[i] = zero16();
         dv[i] = zero16();
     }
-    const int rb = 32 * qh;
-    if (nst > 0) fetch(0);
+    if (nst > 0) issue(0);
+    if (nst > 1) issue(1);
     for (int s = 0; s < nst; ++s) {
-        __syncthreads();  // every wave is done with stage s - 1
-        put();
-        __syncthreads();
-        if (s + 1 < nst) fetch(s + 1);
+        if (s + 1 < nst) wait_vmcnt<kKLoads>();  // stage s has landed for this wave ...
+        else wait_vmcnt<0>();
+        wg_barrier();  // ... and for every wave; all waves are done with stage s - 1
+        if (s + 2 < nst) issue(s + 2);
+        const char* sQ = lds + (s % 3) * kKStage;
+        const char* sGh = sQ + 16384;
+        const char* sGl = sQ + 32768;
+        const float* sL = reinterpret_cast<const float*>(sQ + 49152);
+        const float* sD = sL + 64;
         f32x16 sc = zero16(), dp = zero16();
 #pragma unroll
         for (int ks = 0; ks < 8; ++ks) {
-            sc = mfma_bf16(frag(sQ, rb + l32, 2 * ks + hl), kf[ks], sc);
-            dp = mfma_bf16(frag(sGh, rb + l32, 2 * ks + hl), vf[ks], dp);
-            dp = mfma_bf16(frag(sGl, rb + l32, 2 * ks + hl), vf[ks], dp);
+            sc = mfma_bf16(row_op(sQ, lo, ks), kf[ks], sc);
+            dp = mfma_bf16(row_op(sGh, lo, ks), vf[ks], dp);
+            dp = mfma_bf16(row_op(sGl, lo, ks), vf[ks], dp);
         }
         float p[16], dl[16];
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
             const int qr = rb + 8 * (i >> 2) + 4 * hl + (i & 3);
-            p[i] = exp2f(fmaf(sc[i], c2, -sL[qr]));
+            p[i] = __builtin_amdgcn_exp2f(fmaf(sc[i], c2, -sL[qr]));
             dl[i] = p[i] * (dp[i] - sD[qr]) * isd;
         }
-#pragma unroll
-        for (int kq = 0; kq < 2; ++kq) {
-            bf16x8 ph, pl, dh, dlo;
+        uint32_t ca[8];
+        col_addrs(sQ, lo, ca);
+        auto kv = [&](auto kq_c) {
+            constexpr int kq = decltype(kq_c)::value;
+            bf16x8 ph, pl, dh, dlo, gth[4], gtl[4], qt[4];
             split8(p + 8 * kq, ph, pl);
             split8(dl + 8 * kq, dh, dlo);
+            col_ops4<16384 + 4096 * kq>(ca, gth);
 #pragma unroll
             for (int mt = 0; mt < 4; ++mt) {
-                const bf16x8 gth = tfrag(sGh, rb + 16 * kq, 32 * mt, lane);
-                const bf16x8 gtl = tfrag(sGl, rb + 16 * kq, 32 * mt, lane);
-                const bf16x8 qt = tfrag(sQ, rb + 16 * kq, 32 * mt, lane);
-                dv[mt] = mfma_bf16(gth, ph, dv[mt]);
-                dk[mt] = mfma_bf16(qt, dh, dk[mt]);
-                dv[mt] = mfma_bf16(gth, pl, dv[mt]);
-                dk[mt] = mfma_bf16(qt, dlo, dk[mt]);
-                dv[mt] = mfma_bf16(gtl, ph, dv[mt]);
+                dv[mt] = mfma_bf16(gth[mt], ph, dv[mt]);
+                dv[mt] = mfma_bf16(gth[mt], pl, dv[mt]);
             }
-        }
+            col_ops4<4096 * kq>(ca, qt);
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt) {
+                dk[mt] = mfma_bf16(qt[mt], dh, dk[mt]);
+                dk[mt] = mfma_bf16(qt[mt], dlo, dk[mt]);
+            }
+            col_ops4<32768 + 4096 * kq>(ca, gtl);
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt) dv[mt] = mfma_bf16(gtl[mt], ph, dv[mt]);
+        };
+        kv(std::integral_constant<int, 0>{});
+        kv(std::integral_constant<int, 1>{});
     }
     // rows 32..63 of every stage (waves qh = 1) onto rows 0..31 (qh = 0)
     float* red = reinterpret_cast<float*>(lds);  // [kh][mt][16][64 lanes]: 32 KB
@@ -842,15 +924,15 @@ hipError_t launch_backward_mfma(const Dims& D, const void* Q, const void* K, con
     }
     timing_before(s, K_BWD_ROWS_MFMA);
     bwd_rows_mfma_kernel<<<head_major_grid(D.BH, D.Tq), 256, 0, s>>>(
-        q, kk, v, dO, idx, alpha, dQ, bw.lse, bw.D, bw.da, D.N, D.Tq, D.k, D.H, D.st,
-        D.alpha_qblock, lin ? 1 : 0);
+        q, kk, v, dO, idx, alpha, dQ, bw.lse, bw.D, bw.da, bw.gh, bw.gl, D.N, D.Tq, D.k, D.H,
+        D.st, D.alpha_qblock, lin ? 1 : 0);
     timing_after(s, K_BWD_ROWS_MFMA);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if (D.k > 0) {
         timing_before(s, K_BWD_KEYS_MFMA);
         bwd_keys_mfma_kernel<<<head_major_grid(D.BH, D.Tkv), 256, 0, s>>>(
-            q, kk, v, dO, alpha, bw.lse, bw.D, bw.off, bw.list, dK, dV, D.N, D.Tq, D.Tkv, D.k,
-            D.H, D.st, D.alpha_qblock, lin ? 1 : 0);
+            q, kk, v, bw.gh, bw.gl, bw.lse, bw.D, bw.off, bw.list, dK, dV, D.N, D.Tq, D.Tkv, D.k,
+            D.H, D.st, lin ? 1 : 0);
         timing_after(s, K_BWD_KEYS_MFMA);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }

@@ -127,15 +127,20 @@ size_t layout_backward(const Dims& D, char* base, FwdWS* ws, BwdWS* bw) {
         b.zblk = carve<float>(base, off, 4 * bh * D.Tkv * d);
         b.dHq = carve<float>(base, off, 4 * bh * D.Tq * d * d);
         b.dZq = carve<float>(base, off, 4 * bh * D.Tq * d);
+        const size_t np = (size_t)D.Tq * 128;
+        b.gh = carve<uint16_t>(base, off, 2 * bh * np * d);
+        b.gl = carve<uint16_t>(base, off, 2 * bh * np * d);
+        b.lse = carve<float>(base, off, 4 * bh * np);
+        b.D = carve<float>(base, off, 4 * bh * np);
     } else {
         const int nch = summ_chunks(D);
         w.hpart = carve<float>(base, off, 4 * bh * nch * d * d);
         w.zpart = carve<float>(base, off, 4 * bh * nch * d);
         b.ds = carve<float>(base, off, 4 * bh * n);
         b.dn = carve<float>(base, off, 4 * bh * n * d);
+        b.lse = carve<float>(base, off, 4 * bh * n);
+        b.D = carve<float>(base, off, 4 * bh * n);
     }
-    b.lse = carve<float>(base, off, 4 * bh * n);
-    b.D = carve<float>(base, off, 4 * bh * n);
     b.da = carve<float>(base, off, 4 * bh * n);
     b.dHt = carve<float>(base, off, 4 * bh * d * d);
     b.dZt = carve<float>(base, off, 4 * bh * d);

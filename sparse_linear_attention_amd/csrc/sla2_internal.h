@@ -137,7 +137,8 @@ struct FwdWS {
 // backward (SLA2_OP_BACKWARD: the forward's summary buffers, then these)
 struct BwdWS {
     float* lse;     // [BH][N]  log-sum-exp of each row's selected logits
-    float* D;       // [BH][N]  alpha dO . O_s
+                    //          (matrix-core path: [BH][Tq * 128], log2 domain)
+    float* D;       // [BH][N]  alpha dO . O_s (matrix-core path: [BH][Tq * 128])
     float* ds;      // [BH][N]  dL/d(denominator of O_l)
     float* dn;      // [BH][N][d] dL/d(numerator of O_l)
     float* da;      // [BH][N]  dO . (O_s - O_l)
@@ -152,6 +153,8 @@ struct BwdWS {
     float* zblk;    // [BH][Tkv][d]    z_j
     float* dHq;     // [BH][Tq][d][d]  dL/dH_i
     float* dZq;     // [BH][Tq][d]     dL/dZ_i
+    uint16_t* gh;   // [BH][Tq * 128][d] bf16 high part of alpha dO (rows past N: 0)
+    uint16_t* gl;   // [BH][Tq * 128][d] bf16 rest of alpha dO
 };
 // the backward runs on the matrix cores for bf16 inputs with d = b_q = 128
 // (b_kv = 64) and phi = elu + 1; other problems take the vector-ALU kernels
