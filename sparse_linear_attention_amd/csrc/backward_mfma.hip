@@ -55,24 +55,45 @@ __device__ inline float sum16(float v) {
     return v;
 }
 
-// c[p][q] += sum over kk < K of A(m_p, kk) B(kk, n_q), m_p = ty + 16 p,
-// n_q = tx + 16 q; A(m, kk) = A[m am + kk ak], B(kk, n) = B[kk bk + n bn] in LDS
-template <int MP>
-__device__ inline void tile_gemm(float (&c)[MP][8], const float* A, int am, int ak,
-                                 const float* B, int bk, int bn, int K, int ty, int tx) {
-#pragma unroll 2
-    for (int kk = 0; kk < K; ++kk) {
-        float a[MP], b[8];
+// NT side-by-side 32x32 tiles (columns n0 + 32 i) of C += A B over kk < K
+// on the fp32 matrix cores (32x32x2, exact fp32 products): lane l supplies
+// A(m0 + l%32, kk + l/32) and B(kk + l/32, n0 + 32 i + l%32), with A(m, kk)
+// = A[m am + kk ak] and B(kk, n) = B[kk bk + n bn] in LDS.  Tile i's
+// register r holds C(m0 + 8 (r/4) + 4 (l/32) + r%4, n0 + 32 i + l%32).
+template <int NT>
+__device__ inline void mfma_f32_row(f32x16 (&c)[NT], const float* A, int am, int ak,
+                                    const float* B, int bk, int bn, int m0, int n0, int K,
+                                    int lane) {
+    const int l32 = lane & 31, h = lane >> 5;
+    const float* pa = A + (m0 + l32) * am + h * ak;
+    const float* pb = B + h * bk + (n0 + l32) * bn;
+#pragma unroll 4
+    for (int kk = 0; kk < K; kk += 2) {
+        const float av = pa[kk * ak];
 #pragma unroll
-        for (int p = 0; p < MP; ++p) a[p] = A[(ty + 16 * p) * am + kk * ak];
-#pragma unroll
-        for (int q = 0; q < 8; ++q) b[q] = B[kk * bk + (tx + 16 * q) * bn];
-#pragma unroll
-        for (int p = 0; p < MP; ++p)
-#pragma unroll
-            for (int q = 0; q < 8; ++q) c[p][q] = fmaf(a[p], b[q], c[p][q]);
+        for (int i = 0; i < NT; ++i)
+            c[i] = __builtin_amdgcn_mfma_f32_32x32x2f32(av, pb[kk * bk + 32 * i * bn], c[i], 0,
+                                                        0, 0);
     }
 }
+// Work-groups run round-robin over the 8 XCDs (dispatch index g on XCD g % 8).
+// For the per-KV-block passes, whose work grows with the number of query
+// blocks selecting the block (the first and last blocks of a sequence are
+// selected far more often), the blocks of a head are dealt to the XCDs
+// interleaved (XCD x takes positions x, x + 8, ... of one head at a time),
+// and position p is block p / 2 for even p and T - 1 - p / 2 for odd p, so
+// both heavy ends come early and each head ends with light blocks.
+__device__ inline bool head_interleaved_map(int g, int T, long* bh, int* j) {
+    const int R = (T + 7) >> 3;
+    const int x = g & 7, s = g >> 3;
+    *bh = s / R;
+    const int p = (s % R) * 8 + x;
+    *j = (p & 1) ? T - 1 - (p >> 1) : (p >> 1);
+    return p < T;
+}
+
+// row of register r of a 32x32 accumulator tile, relative to the tile
+__device__ inline int acc_row(int r, int lane) { return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3); }
 
 // acc (16 floats per thread: entries 4 (t + 256 m) .. +3 of a d x d matrix)
 // into an LDS matrix with row stride kLd
@@ -135,13 +156,14 @@ __global__ __launch_bounds__(256) void bwd_lin_rows_kernel(
     }
     const float a = alpha_of(alpha, bh, H, qb, Tq, alpha_qblock);
     const float om = 1.0f - a;
-    float dh[8][8], dzp[8];
+    const int lane = t & 63, w = t >> 6, l32 = lane & 31;
+    const int mt = w & 1, n0 = 64 * (w >> 1);  // this wave's 64-row x 128 products: tiles (mt, n0 + 32 i)
+    f32x16 dh[4];  // dH_i rows 32 w .., columns 32 i ..
 #pragma unroll
-    for (int p = 0; p < 8; ++p) {
-        dzp[p] = 0.0f;
+    for (int i = 0; i < 4; ++i) dh[i] = zero16();
+    float dzp[8];
 #pragma unroll
-        for (int q = 0; q < 8; ++q) dh[p][q] = 0.0f;
-    }
+    for (int p = 0; p < 8; ++p) dzp[p] = 0.0f;
     for (int half = 0; half < 2; ++half) {
         const int m0 = qb * 128 + 64 * half;
         __syncthreads();  // sH, sZ written; the previous half's reads of sA, sB done
@@ -151,17 +173,20 @@ __global__ __launch_bounds__(256) void bwd_lin_rows_kernel(
         }
         __syncthreads();
         if (t < 64) {
-            float s = 0.0f;
-            for (int c = 0; c < kD; ++c) s = fmaf(sA[t * kLd + c], sZ[c], s);
-            sS[t] = s;
+            float sv = 0.0f;
+            for (int c = 0; c < kD; ++c) sv = fmaf(sA[t * kLd + c], sZ[c], sv);
+            sS[t] = sv;
         }
-        float n[4][8];
+        {  // numerator phi(q) H_i into sB
+            f32x16 n[2] = {zero16(), zero16()};
+            mfma_f32_row<2>(n, sA, kLd, 1, sH, kLd, 1, 32 * mt, n0, kD, lane);
 #pragma unroll
-        for (int p = 0; p < 4; ++p)
+            for (int i = 0; i < 2; ++i)
 #pragma unroll
-            for (int q = 0; q < 8; ++q) n[p][q] = 0.0f;
-        tile_gemm<4>(n, sA, kLd, 1, sH, kLd, 1, kD, ty, tx);  // phi(q) H_i
-        __syncthreads();                                     // sS
+                for (int r = 0; r < 16; ++r)
+                    sB[(32 * mt + acc_row(r, lane)) * kLd + n0 + 32 * i + l32] = n[i][r];
+        }
+        __syncthreads();  // sS and the numerators
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
             const int m = ty + 16 * p, tq = m0 + m;
@@ -173,10 +198,10 @@ __global__ __launch_bounds__(256) void bwd_lin_rows_kernel(
             for (int q = 0; q < 8; ++q) {
                 const int e = tx + 16 * q;
                 const float g = ok ? grow[e] : 0.0f;
-                const float ol = n[p][q] * inv, ee = om * g;
+                const float ol = sB[m * kLd + e] * inv, ee = om * g;
                 d1 = fmaf(ee, ol, d1);
                 d2 = fmaf(g, ol, d2);
-                sB[m * kLd + e] = ee * inv;
+                sB[m * kLd + e] = ee * inv;  // dn replaces the numerator
             }
             d1 = sum16(d1);
             d2 = sum16(d2);
@@ -186,26 +211,23 @@ __global__ __launch_bounds__(256) void bwd_lin_rows_kernel(
             }
         }
         __syncthreads();
-        // dphi(q) = dn H_i^T + ds Z_i^T; dQ = dphi phi'(q)
-        float dp[4][8];
+        {  // dphi(q) = dn H_i^T + ds Z_i^T; dQ = dphi phi'(q)
+            f32x16 dp[2] = {zero16(), zero16()};
+            mfma_f32_row<2>(dp, sB, kLd, 1, sH, 1, kLd, 32 * mt, n0, kD, lane);
 #pragma unroll
-        for (int p = 0; p < 4; ++p)
+            for (int r = 0; r < 16; ++r) {
+                const int m = 32 * mt + acc_row(r, lane), tq = m0 + m;
+                if (tq >= N) continue;
+                float* qo = dQ + hb + (size_t)tq * st.t;
 #pragma unroll
-            for (int q = 0; q < 8; ++q) dp[p][q] = 0.0f;
-        tile_gemm<4>(dp, sB, kLd, 1, sH, 1, kLd, kD, ty, tx);
-#pragma unroll
-        for (int p = 0; p < 4; ++p) {
-            const int m = ty + 16 * p, tq = m0 + m;
-            if (tq >= N) continue;
-            float* qo = dQ + hb + (size_t)tq * st.t;
-#pragma unroll
-            for (int q = 0; q < 8; ++q) {
-                const int c = tx + 16 * q;
-                qo[c] = fmaf(sZ[c], sDs[m], dp[p][q]) * dphi_of(sA[m * kLd + c]);
+                for (int i = 0; i < 2; ++i) {
+                    const int c = n0 + 32 * i + l32;
+                    qo[c] = fmaf(sZ[c], sDs[m], dp[i][r]) * dphi_of(sA[m * kLd + c]);
+                }
             }
         }
         // dH_i += phi(Q)^T dn, dZ_i += phi(Q)^T ds over these 64 rows
-        tile_gemm<8>(dh, sA, 1, kLd, sB, kLd, 1, 64, ty, tx);
+        mfma_f32_row<4>(dh, sA, 1, kLd, sB, kLd, 1, 32 * w, 0, 64, lane);
 #pragma unroll
         for (int p = 0; p < 8; ++p) {
             const int c = ty + 16 * p;
@@ -218,9 +240,10 @@ __global__ __launch_bounds__(256) void bwd_lin_rows_kernel(
     }
     float* dHo = dHq + ((size_t)bh * Tq + qb) * kD * kD;
 #pragma unroll
-    for (int p = 0; p < 8; ++p)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int q = 0; q < 8; ++q) dHo[(ty + 16 * p) * kD + tx + 16 * q] = dh[p][q];
+        for (int r = 0; r < 16; ++r)
+            dHo[(32 * w + acc_row(r, lane)) * kD + 32 * i + l32] = dh[i][r];
 #pragma unroll
     for (int p = 0; p < 8; ++p) {
         const float z = sum16(dzp[p]);
@@ -247,7 +270,7 @@ __global__ __launch_bounds__(256) void bwd_lin_keys_kernel(
     const int t = threadIdx.x, ty = t >> 4, tx = t & 15;
     long bh;
     int j;
-    if (!head_major_map(blockIdx.x, Tkv, &bh, &j)) return;
+    if (!head_interleaved_map(blockIdx.x, Tkv, &bh, &j)) return;
     const long hb = head_base(st, bh, H);
     const int n0 = k > 0 ? off[(size_t)bh * (Tkv + 1) + j] : 0;
     const int n1 = k > 0 ? off[(size_t)bh * (Tkv + 1) + j + 1] : 0;
@@ -277,28 +300,91 @@ __global__ __launch_bounds__(256) void bwd_lin_keys_kernel(
         sB[u * kLd + c] = ok ? phi1(bfv(K[hb + (size_t)tok * st.t + c])) : 0.0f;
     }
     __syncthreads();
-    float x4[4][8], y4[4][8];
+    const int lane = t & 63, w = t >> 6, l32 = lane & 31;
+    const int mt = w & 1, c0 = 64 * (w >> 1);
+    f32x16 x[2] = {zero16(), zero16()}, y[2] = {zero16(), zero16()};
+    mfma_f32_row<2>(x, sA, kLd, 1, sH, 1, kLd, 32 * mt, c0, kD, lane);  // sum_e v[u][e] dh[c][e]
+    mfma_f32_row<2>(y, sB, kLd, 1, sH, kLd, 1, 32 * mt, c0, kD, lane);  // sum_c phi(k)[u][c] dh[c][e]
 #pragma unroll
-    for (int p = 0; p < 4; ++p)
-#pragma unroll
-        for (int q = 0; q < 8; ++q) {
-            x4[p][q] = 0.0f;
-            y4[p][q] = 0.0f;
-        }
-    tile_gemm<4>(x4, sA, kLd, 1, sH, 1, kLd, kD, ty, tx);  // sum_e v[u][e] dh[c][e]
-    tile_gemm<4>(y4, sB, kLd, 1, sH, kLd, 1, kD, ty, tx);  // sum_c phi(k)[u][c] dh[c][e]
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-        const int u = ty + 16 * p, tok = j * 64 + u;
+    for (int r = 0; r < 16; ++r) {
+        const int u = 32 * mt + acc_row(r, lane), tok = j * 64 + u;
         if (tok >= N) continue;
         float* ko = dK + hb + (size_t)tok * st.t;
         float* vo = dV + hb + (size_t)tok * st.t;
 #pragma unroll
-        for (int q = 0; q < 8; ++q) {
-            const int c = tx + 16 * q;
-            ko[c] = (x4[p][q] + sZ[c]) * dphi_of(sB[u * kLd + c]);
-            vo[c] = y4[p][q];
+        for (int i = 0; i < 2; ++i) {
+            const int c = c0 + 32 * i + l32;
+            ko[c] = (x[i][r] + sZ[c]) * dphi_of(sB[u * kLd + c]);
+            vo[c] = y[i][r];
         }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Per-KV-block summaries on the fp32 matrix cores: h_j = phi(K_j)^T V_j
+// ([c][e], over the block's tokens below N) and z_j = colsum phi(K_j).  One
+// work-group per (head, block), 256 threads.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void blk_summ_kernel(const uint16_t* __restrict__ K,
+                                                       const uint16_t* __restrict__ V,
+                                                       float* __restrict__ hblk,
+                                                       float* __restrict__ zblk, int N, int Tkv,
+                                                       int H, Strides st) {
+    __shared__ float sP[64 * kLd];  // phi(K_j) [u][c]
+    __shared__ float sV[64 * kLd];  // V_j [u][e]
+    const int t = threadIdx.x, lane = t & 63, w = t >> 6, l32 = lane & 31;
+    long bh;
+    int j;
+    if (!head_major_map(blockIdx.x, Tkv, &bh, &j)) return;
+    const long hb = head_base(st, bh, H);
+    for (int x = t; x < 64 * kD; x += 256) {
+        const int u = x >> 7, c = x & 127, tok = j * 64 + u;
+        const bool ok = tok < N;
+        sP[u * kLd + c] = ok ? phi1(bfv(K[hb + (size_t)tok * st.t + c])) : 0.0f;
+        sV[u * kLd + c] = ok ? bfv(V[hb + (size_t)tok * st.t + c]) : 0.0f;
+    }
+    __syncthreads();
+    f32x16 h[4] = {zero16(), zero16(), zero16(), zero16()};
+    mfma_f32_row<4>(h, sP, 1, kLd, sV, kLd, 1, 32 * w, 0, 64, lane);
+    float* ho = hblk + ((size_t)bh * Tkv + j) * kD * kD;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) ho[(32 * w + acc_row(r, lane)) * kD + 32 * i + l32] = h[i][r];
+    if (t < kD) {
+        float z = 0.0f;
+        for (int u = 0; u < 64; ++u) z += sP[u * kLd + t];
+        zblk[((size_t)bh * Tkv + j) * kD + t] = z;
+    }
+}
+
+// tot[bh][e] = sum over c < nch of part[bh][c][e] for the d*d entries of the
+// matrices and the d entries of the vectors (entries past d*d index zpart);
+// 8 interleaved slices of c per entry, added in a fixed order.  grid
+// ((d*d + d) / 32, BH), 256 threads.
+__global__ __launch_bounds__(256) void sum_parts_kernel(const float* __restrict__ part,
+                                                        const float* __restrict__ zpart,
+                                                        float* __restrict__ tot,
+                                                        float* __restrict__ ztot, int nch) {
+    __shared__ float red[8][33];
+    const int t = threadIdx.x, sl = t >> 5;
+    const long bh = blockIdx.y;
+    const int e = blockIdx.x * 32 + (t & 31);
+    const bool mat = e < kD * kD;
+    const float* src = mat ? part + (size_t)bh * nch * kD * kD + e
+                           : zpart + (size_t)bh * nch * kD + (e - kD * kD);
+    const size_t stride = mat ? (size_t)kD * kD : (size_t)kD;
+    float acc = 0.0f;
+#pragma unroll 4
+    for (int c = sl; c < nch; c += 8) acc += src[(size_t)c * stride];
+    red[sl][t & 31] = acc;
+    __syncthreads();
+    if (sl == 0) {
+        const int i = t & 31;
+        const float v = ((red[0][i] + red[1][i]) + (red[2][i] + red[3][i])) +
+                        ((red[4][i] + red[5][i]) + (red[6][i] + red[7][i]));
+        if (mat) tot[(size_t)bh * kD * kD + e] = v;
+        else ztot[(size_t)bh * kD + e - kD * kD] = v;
     }
 }
 
@@ -722,7 +808,7 @@ __global__ __launch_bounds__(256) void bwd_keys_mfma_kernel(
     const int kh = w & 1, qh = w >> 1;
     long bh;
     int j;
-    if (!head_major_map(blockIdx.x, Tkv, &bh, &j)) return;
+    if (!head_interleaved_map(blockIdx.x, Tkv, &bh, &j)) return;
     const int n0 = k > 0 ? off[(size_t)bh * (Tkv + 1) + j] : 0;
     const int n1 = k > 0 ? off[(size_t)bh * (Tkv + 1) + j + 1] : 0;
     const int nst = 2 * (n1 - n0);
@@ -888,6 +974,15 @@ __global__ __launch_bounds__(256) void bwd_keys_mfma_kernel(
 
 inline dim3 head_major_grid(long BH, int T) { return dim3((unsigned)(BH * 8 * ((T + 7) / 8))); }
 
+hipError_t sum_parts(const Dims& D, const float* part, const float* zpart, float* tot,
+                     float* ztot, int nch, hipStream_t s) {
+    timing_before(s, K_SUMM_REDUCE);
+    sum_parts_kernel<<<dim3((kD * kD + kD) / 32, (unsigned)D.BH), 256, 0, s>>>(part, zpart, tot,
+                                                                              ztot, nch);
+    timing_after(s, K_SUMM_REDUCE);
+    return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_backward_mfma(const Dims& D, const void* Q, const void* K, const void* V,
@@ -900,9 +995,12 @@ hipError_t launch_backward_mfma(const Dims& D, const void* Q, const void* K, con
     const uint16_t* v = static_cast<const uint16_t*>(V);
     hipError_t e = hipSuccess;
     if (lin) {
-        if ((e = launch_summaries_blocks(D, K, V, bw.hblk, bw.zblk, s)) != hipSuccess) return e;
-        if ((e = launch_partials_reduce(D, bw.hblk, bw.zblk, ws.htot, ws.ztot, D.Tkv, s)) !=
-            hipSuccess)
+        timing_before(s, K_SUMM_VALU);
+        blk_summ_kernel<<<head_major_grid(D.BH, D.Tkv), 256, 0, s>>>(kk, v, bw.hblk, bw.zblk, D.N,
+                                                                     D.Tkv, D.H, D.st);
+        timing_after(s, K_SUMM_VALU);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        if ((e = sum_parts(D, bw.hblk, bw.zblk, ws.htot, ws.ztot, D.Tkv, s)) != hipSuccess)
             return e;
         timing_before(s, K_BWD_LIN_ROWS);
         bwd_lin_rows_kernel<<<head_major_grid(D.BH, D.Tq), 256, 0, s>>>(
@@ -910,8 +1008,7 @@ hipError_t launch_backward_mfma(const Dims& D, const void* Q, const void* K, con
             D.Tq, D.Tkv, D.k, D.H, D.st, D.alpha_qblock);
         timing_after(s, K_BWD_LIN_ROWS);
         if ((e = hipGetLastError()) != hipSuccess) return e;
-        if ((e = launch_partials_reduce(D, bw.dHq, bw.dZq, bw.dHt, bw.dZt, D.Tq, s)) != hipSuccess)
-            return e;
+        if ((e = sum_parts(D, bw.dHq, bw.dZq, bw.dHt, bw.dZt, D.Tq, s)) != hipSuccess) return e;
     }
     if (D.k > 0 && (e = launch_invert(D, idx, bw, s)) != hipSuccess) return e;
     if (lin) {
