@@ -41,7 +41,6 @@ constexpr int kD = 128;
 constexpr int kLd = 129;  // row stride of fp32 LDS matrices: rows and columns hit distinct banks
 constexpr float kLog2e = 1.4426950408889634f;
 
-__device__ inline float bfv(uint16_t b) { return __uint_as_float((unsigned)b << 16); }
 __device__ inline float phi1(float x) { return x > 0.0f ? x + 1.0f : expf(x); }
 // phi'(x) from y = phi(x): 1 where x > 0 (there y > 1), else e^x = y
 __device__ inline float dphi_of(float y) { return fminf(y, 1.0f); }
@@ -107,6 +106,30 @@ __device__ inline void put_dd(float* dst, const float4 (&acc)[16], int t) {
         dst[r * kLd + c + 3] = acc[m].w;
     }
 }
+// rows r0 .. r0 + 63 of a head's [rows][128] bf16 matrix (rows st_t elements
+// apart) as fp32 into an LDS matrix with row stride kLd, through phi when
+// PHI; rows at or past N are 0.  16-byte loads, 4 per thread.
+template <bool PHI>
+__device__ inline void fill64(float* dst, const uint16_t* src, int st_t, int r0, int N, int t) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int x = t + 256 * i, u = x >> 4, c8 = (x & 15) * 8, tok = r0 + u;
+        const bool ok = tok < N;
+        uint4 v = make_uint4(0, 0, 0, 0);
+        if (ok) v = *reinterpret_cast<const uint4*>(src + (size_t)tok * st_t + c8);
+        const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            float lo = __uint_as_float(wv[q] << 16), hi = __uint_as_float(wv[q] & 0xffff0000u);
+            if (PHI) {
+                lo = ok ? phi1(lo) : 0.0f;
+                hi = ok ? phi1(hi) : 0.0f;
+            }
+            dst[u * kLd + c8 + 2 * q] = lo;
+            dst[u * kLd + c8 + 2 * q + 1] = hi;
+        }
+    }
+}
 __device__ inline void sub4(float4& a, const float4 b) {
     a.x -= b.x;
     a.y -= b.y;
@@ -167,10 +190,7 @@ __global__ __launch_bounds__(256) void bwd_lin_rows_kernel(
     for (int half = 0; half < 2; ++half) {
         const int m0 = qb * 128 + 64 * half;
         __syncthreads();  // sH, sZ written; the previous half's reads of sA, sB done
-        for (int x = t; x < 64 * kD; x += 256) {
-            const int m = x >> 7, c = x & 127, tq = m0 + m;
-            sA[m * kLd + c] = tq < N ? phi1(bfv(Q[hb + (size_t)tq * st.t + c])) : 0.0f;
-        }
+        fill64<true>(sA, Q + hb, st.t, m0, N, t);
         __syncthreads();
         if (t < 64) {
             float sv = 0.0f;
@@ -293,12 +313,8 @@ __global__ __launch_bounds__(256) void bwd_lin_keys_kernel(
             sZ[t] = z;
         }
     }
-    for (int x = t; x < 64 * kD; x += 256) {
-        const int u = x >> 7, c = x & 127, tok = j * 64 + u;
-        const bool ok = tok < N;
-        sA[u * kLd + c] = ok ? bfv(V[hb + (size_t)tok * st.t + c]) : 0.0f;
-        sB[u * kLd + c] = ok ? phi1(bfv(K[hb + (size_t)tok * st.t + c])) : 0.0f;
-    }
+    fill64<false>(sA, V + hb, st.t, j * 64, N, t);
+    fill64<true>(sB, K + hb, st.t, j * 64, N, t);
     __syncthreads();
     const int lane = t & 63, w = t >> 6, l32 = lane & 31;
     const int mt = w & 1, c0 = 64 * (w >> 1);
@@ -337,12 +353,8 @@ __global__ __launch_bounds__(256) void blk_summ_kernel(const uint16_t* __restric
     int j;
     if (!head_major_map(blockIdx.x, Tkv, &bh, &j)) return;
     const long hb = head_base(st, bh, H);
-    for (int x = t; x < 64 * kD; x += 256) {
-        const int u = x >> 7, c = x & 127, tok = j * 64 + u;
-        const bool ok = tok < N;
-        sP[u * kLd + c] = ok ? phi1(bfv(K[hb + (size_t)tok * st.t + c])) : 0.0f;
-        sV[u * kLd + c] = ok ? bfv(V[hb + (size_t)tok * st.t + c]) : 0.0f;
-    }
+    fill64<true>(sP, K + hb, st.t, j * 64, N, t);
+    fill64<false>(sV, V + hb, st.t, j * 64, N, t);
     __syncthreads();
     f32x16 h[4] = {zero16(), zero16(), zero16(), zero16()};
     mfma_f32_row<4>(h, sP, 1, kLd, sV, kLd, 1, 32 * w, 0, 64, lane);
