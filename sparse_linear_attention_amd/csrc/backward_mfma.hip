@@ -988,10 +988,10 @@ inline dim3 head_major_grid(long BH, int T) { return dim3((unsigned)(BH * 8 * ((
 
 hipError_t sum_parts(const Dims& D, const float* part, const float* zpart, float* tot,
                      float* ztot, int nch, hipStream_t s) {
-    timing_before(s, K_SUMM_REDUCE);
+    timing_before(s, K_BWD_SUM_PARTS);
     sum_parts_kernel<<<dim3((kD * kD + kD) / 32, (unsigned)D.BH), 256, 0, s>>>(part, zpart, tot,
                                                                               ztot, nch);
-    timing_after(s, K_SUMM_REDUCE);
+    timing_after(s, K_BWD_SUM_PARTS);
     return hipGetLastError();
 }
 
@@ -1007,10 +1007,10 @@ hipError_t launch_backward_mfma(const Dims& D, const void* Q, const void* K, con
     const uint16_t* v = static_cast<const uint16_t*>(V);
     hipError_t e = hipSuccess;
     if (lin) {
-        timing_before(s, K_SUMM_VALU);
+        timing_before(s, K_BWD_BLK_SUMM);
         blk_summ_kernel<<<head_major_grid(D.BH, D.Tkv), 256, 0, s>>>(kk, v, bw.hblk, bw.zblk, D.N,
                                                                      D.Tkv, D.H, D.st);
-        timing_after(s, K_SUMM_VALU);
+        timing_after(s, K_BWD_BLK_SUMM);
         if ((e = hipGetLastError()) != hipSuccess) return e;
         if ((e = sum_parts(D, bw.hblk, bw.zblk, ws.htot, ws.ztot, D.Tkv, s)) != hipSuccess)
             return e;

@@ -35,6 +35,8 @@ enum KernelKind {
     K_BWD_LIN_KEYS,
     K_BWD_ROWS_MFMA,
     K_BWD_KEYS_MFMA,
+    K_BWD_BLK_SUMM,
+    K_BWD_SUM_PARTS,
     K_NUM_KINDS
 };
 
