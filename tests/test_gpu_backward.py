@@ -84,6 +84,33 @@ def test_backward_parity(orc, dev, case):
     _check("dalpha", da.cpu().numpy(), ra)
 
 
+@pytest.mark.parametrize("dtype,bq", [("bf16", 128), ("f32", 64)], ids=["matrix-core", "valu"])
+def test_backward_two_batches(orc, dev, dtype, bq):
+    """B = 2 with per-query-block alpha: the batch stride and the head of each
+    (batch, head) pair on both paths."""
+    B, H, N, d = 2, 2, 700, 128 if dtype == "bf16" else 64
+    say(f"case backward B=2 {dtype}: N={N} H={H} d={d} bq={bq}")
+    gen = "centroids" if dtype == "f32" else "smooth"
+    w = I.Workload("b2", B, H, N, d, bq, 64, 0.2, dtype, gen, seed=21)
+    x = I.make_inputs(w)
+    rng = np.random.default_rng(6)
+    alpha = rng.uniform(0.2, 0.9, (H, w.Tq)).astype(np.float32)
+    dO = rng.normal(0, 1, (B, H, N, d)).astype(np.float32)
+    q, k, v, wq, wk, _ = to_dev(x, dev)
+    p = S.problem(B, H, N, d, bq, 64, 0.2, 1, dtype, alpha_mode=S.ALPHA_PER_QBLOCK)
+    idx, _ = S.route(S.problem(B, H, N, d, bq, 64, 0.2, 1, dtype), q, k, wq, wk, want_mask=False)
+    dQ, dK, dV, da = S.backward(p, q, k, v, idx, torch.from_numpy(alpha).to(dev),
+                                torch.from_numpy(dO).to(dev))
+    torch.cuda.synchronize()
+    op = orc.problem(B, H, N, d, bq, 64, 0.2, 1, dtype, alpha_mode=S.ALPHA_PER_QBLOCK)
+    rQ, rK, rV, ra = orc.backward(op, x.q, x.k, x.v, idx.cpu().numpy(), alpha,
+                                  dO.astype(np.float64))
+    _check("dQ", dQ.cpu().numpy(), rQ)
+    _check("dK", dK.cpu().numpy(), rK)
+    _check("dV", dV.cpu().numpy(), rV)
+    _check("dalpha", da.cpu().numpy(), ra)
+
+
 def test_backward_wan13b_one_head(orc, dev):
     """One head of the 1.3B shape (N = 32760, k = 16 of 512): every gradient
     entry against the oracle."""
