@@ -98,3 +98,40 @@ def test_attention_call_equals_route_then_forward(orc, dev, path):
         torch.cuda.synchronize()
         assert torch.equal(idx0, idx1)
         assert torch.equal(O0, O1)
+
+
+ATTN_CASES = [  # B, H, layout, alpha mode, w_heads, out dtype, frac
+    (2, 8, S.LAYOUT_BHND, S.ALPHA_PER_HEAD, 8, S.F32, 0.1),
+    (1, 12, S.LAYOUT_BNHD, S.ALPHA_PER_QBLOCK, 1, S.BF16, 0.2),
+    (2, 9, S.LAYOUT_BNHD, S.ALPHA_PER_QBLOCK, 9, S.F32, 0.0),
+]
+
+
+@pytest.mark.parametrize("case", ATTN_CASES, ids=["b2-h8-whead", "h12-bnhd-bf16out", "b2-h9-k0"])
+def test_attention_batches_and_options(dev, case):
+    """sla2_attention with two batch entries, per-head projections, the
+    token-major layout, bf16 output and k = 0: the selection and the output
+    bits equal sla2_route followed by sla2_forward."""
+    B, H, lay, amode, wh, odt, frac = case
+    N, d = 1300, 128
+    say(f"case attention call: B={B} H={H} layout={lay} alpha={amode} w_heads={wh}")
+    x = I.make_inputs(I.Workload("attn", B, H, N, d, 128, 64, frac, "bf16", "smooth", seed=23))
+    rng = np.random.default_rng(9)
+    q, k, v = (upload(a, dev, lay) for a in (x.q, x.k, x.v))
+    wq = torch.from_numpy(rng.normal(0, d ** -0.5, (wh, d, d)).astype(np.float32)).to(dev)
+    wk = torch.from_numpy(rng.normal(0, d ** -0.5, (wh, d, d)).astype(np.float32)).to(dev)
+    p = S.problem(B, H, N, d, 128, 64, frac, wh, "bf16", layout=lay, alpha_mode=amode,
+                  out_dtype=odt)
+    shape = (H, S.num_q_blocks(p)) if amode == S.ALPHA_PER_QBLOCK else (H,)
+    al = torch.from_numpy(rng.uniform(0.2, 0.9, shape).astype(np.float32)).to(dev)
+    if frac > 0:
+        idx0, _ = S.route(p, q, k, wq, wk, want_mask=False)
+    else:
+        idx0 = None
+    O0 = S.forward(p, q, k, v, idx0, al)
+    for _ in range(2):
+        idx1, O1 = S.attention(p, q, k, v, wq, wk, al)
+        torch.cuda.synchronize()
+        if frac > 0:
+            assert torch.equal(idx0, idx1)
+        assert torch.equal(O0, O1)
