@@ -94,18 +94,6 @@ __device__ inline bool head_interleaved_map(int g, int T, long* bh, int* j) {
 // row of register r of a 32x32 accumulator tile, relative to the tile
 __device__ inline int acc_row(int r, int lane) { return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3); }
 
-// acc (16 floats per thread: entries 4 (t + 256 m) .. +3 of a d x d matrix)
-// into an LDS matrix with row stride kLd
-__device__ inline void put_dd(float* dst, const float4 (&acc)[16], int t) {
-#pragma unroll
-    for (int m = 0; m < 16; ++m) {
-        const int x = 4 * (t + 256 * m), r = x >> 7, c = x & 127;
-        dst[r * kLd + c] = acc[m].x;
-        dst[r * kLd + c + 1] = acc[m].y;
-        dst[r * kLd + c + 2] = acc[m].z;
-        dst[r * kLd + c + 3] = acc[m].w;
-    }
-}
 // rows r0 .. r0 + 63 of a head's [rows][128] bf16 matrix (rows st_t elements
 // apart) as fp32 into an LDS matrix with row stride kLd, through phi when
 // PHI; rows at or past N are 0.  16-byte loads, 4 per thread.
@@ -130,11 +118,42 @@ __device__ inline void fill64(float* dst, const uint16_t* src, int st_t, int r0,
         }
     }
 }
-__device__ inline void sub4(float4& a, const float4 b) {
-    a.x -= b.x;
-    a.y -= b.y;
-    a.z -= b.z;
-    a.w -= b.w;
+// base - sum of bf16 d x d matrices, per thread: floats 8 (t + 256 m) .. +7
+// (m < 8) of the flattened matrix
+__device__ inline void load_base8(float (&acc)[8][8], const float* base, int t) {
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+        const float4 a = *reinterpret_cast<const float4*>(base + 8 * (t + 256 * m));
+        const float4 b = *reinterpret_cast<const float4*>(base + 8 * (t + 256 * m) + 4);
+        acc[m][0] = a.x;
+        acc[m][1] = a.y;
+        acc[m][2] = a.z;
+        acc[m][3] = a.w;
+        acc[m][4] = b.x;
+        acc[m][5] = b.y;
+        acc[m][6] = b.z;
+        acc[m][7] = b.w;
+    }
+}
+__device__ inline void sub_bf16_8(float (&acc)[8][8], const uint16_t* src, int t) {
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+        const uint4 u = *reinterpret_cast<const uint4*>(src + 8 * (t + 256 * m));
+        const uint32_t wv[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            acc[m][2 * q] -= __uint_as_float(wv[q] << 16);
+            acc[m][2 * q + 1] -= __uint_as_float(wv[q] & 0xffff0000u);
+        }
+    }
+}
+__device__ inline void put_dd8(float* dst, const float (&acc)[8][8], int t) {
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+        const int x = 8 * (t + 256 * m), r = x >> 7, c = x & 127;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) dst[r * kLd + c + i] = acc[m][i];
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -146,9 +165,10 @@ __global__ __launch_bounds__(256) void bwd_lin_rows_kernel(
     const uint16_t* __restrict__ Q, const float* __restrict__ dO,
     const int32_t* __restrict__ idx, const float* __restrict__ alpha,
     const float* __restrict__ htot, const float* __restrict__ ztot,
-    const float* __restrict__ hblk, const float* __restrict__ zblk, float* __restrict__ dQ,
-    float* __restrict__ dHq, float* __restrict__ dZq, float* __restrict__ gol, int N, int Tq,
-    int Tkv, int k, int H, Strides st, int alpha_qblock) {
+    const uint16_t* __restrict__ hb16, const float* __restrict__ zblk, float* __restrict__ dQ,
+    float* __restrict__ dHq, uint16_t* __restrict__ dHb16, float* __restrict__ dZq,
+    float* __restrict__ gol, int N, int Tq, int Tkv, int k, int H, Strides st,
+    int alpha_qblock) {
     __shared__ float sH[kD * kLd];  // H_i [c][e]
     __shared__ float sA[64 * kLd];  // phi(q) of 64 rows [m][c]
     __shared__ float sB[64 * kLd];  // dn of the same rows [m][e]
@@ -160,17 +180,11 @@ __global__ __launch_bounds__(256) void bwd_lin_rows_kernel(
     const long hb = head_base(st, bh, H);
     const int32_t* sel = idx + ((size_t)bh * Tq + qb) * k;
     {
-        const float4* ht = reinterpret_cast<const float4*>(htot + (size_t)bh * kD * kD);
-        float4 acc[16];
-#pragma unroll
-        for (int m = 0; m < 16; ++m) acc[m] = ht[t + 256 * m];
-        for (int r = 0; r < k; ++r) {
-            const float4* hj =
-                reinterpret_cast<const float4*>(hblk + ((size_t)bh * Tkv + sel[r]) * kD * kD);
-#pragma unroll
-            for (int m = 0; m < 16; ++m) sub4(acc[m], hj[t + 256 * m]);
-        }
-        put_dd(sH, acc, t);
+        float acc[8][8];
+        load_base8(acc, htot + (size_t)bh * kD * kD, t);
+        for (int r = 0; r < k; ++r)
+            sub_bf16_8(acc, hb16 + ((size_t)bh * Tkv + sel[r]) * kD * kD, t);
+        put_dd8(sH, acc, t);
         if (t < kD) {
             float z = ztot[(size_t)bh * kD + t];
             for (int r = 0; r < k; ++r) z -= zblk[((size_t)bh * Tkv + sel[r]) * kD + t];
@@ -180,7 +194,8 @@ __global__ __launch_bounds__(256) void bwd_lin_rows_kernel(
     const float a = alpha_of(alpha, bh, H, qb, Tq, alpha_qblock);
     const float om = 1.0f - a;
     const int lane = t & 63, w = t >> 6, l32 = lane & 31;
-    const int mt = w & 1, n0 = 64 * (w >> 1);  // this wave's 64-row x 128 products: tiles (mt, n0 + 32 i)
+    // this wave's tiles of the 64-row x 128 products: (rows 32 mt, columns n0 + 32 i)
+    const int mt = w & 1, n0 = 64 * (w >> 1);
     f32x16 dh[4];  // dH_i rows 32 w .., columns 32 i ..
 #pragma unroll
     for (int i = 0; i < 4; ++i) dh[i] = zero16();
@@ -259,11 +274,15 @@ __global__ __launch_bounds__(256) void bwd_lin_rows_kernel(
         }
     }
     float* dHo = dHq + ((size_t)bh * Tq + qb) * kD * kD;
+    uint16_t* dHo16 = dHb16 + ((size_t)bh * Tq + qb) * kD * kD;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-            dHo[(32 * w + acc_row(r, lane)) * kD + 32 * i + l32] = dh[i][r];
+        for (int r = 0; r < 16; ++r) {
+            const int o = (32 * w + acc_row(r, lane)) * kD + 32 * i + l32;
+            dHo[o] = dh[i][r];
+            dHo16[o] = __builtin_bit_cast(uint16_t, (__bf16)dh[i][r]);
+        }
 #pragma unroll
     for (int p = 0; p < 8; ++p) {
         const float z = sum16(dzp[p]);
@@ -280,7 +299,7 @@ __global__ __launch_bounds__(256) void bwd_lin_rows_kernel(
 __global__ __launch_bounds__(256) void bwd_lin_keys_kernel(
     const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const float* __restrict__ dHt, const float* __restrict__ dZt,
-    const float* __restrict__ dHq, const float* __restrict__ dZq,
+    const uint16_t* __restrict__ dHb16, const float* __restrict__ dZq,
     const int32_t* __restrict__ off, const int32_t* __restrict__ list, float* __restrict__ dK,
     float* __restrict__ dV, int N, int Tq, int Tkv, int k, int H, Strides st) {
     __shared__ float sH[kD * kLd];  // dh_j [c][e]
@@ -296,17 +315,11 @@ __global__ __launch_bounds__(256) void bwd_lin_keys_kernel(
     const int n1 = k > 0 ? off[(size_t)bh * (Tkv + 1) + j + 1] : 0;
     const int32_t* L = list + (size_t)bh * Tq * k;
     {
-        const float4* ht = reinterpret_cast<const float4*>(dHt + (size_t)bh * kD * kD);
-        float4 acc[16];
-#pragma unroll
-        for (int m = 0; m < 16; ++m) acc[m] = ht[t + 256 * m];
-        for (int n = n0; n < n1; ++n) {
-            const float4* hi =
-                reinterpret_cast<const float4*>(dHq + ((size_t)bh * Tq + L[n]) * kD * kD);
-#pragma unroll
-            for (int m = 0; m < 16; ++m) sub4(acc[m], hi[t + 256 * m]);
-        }
-        put_dd(sH, acc, t);
+        float acc[8][8];
+        load_base8(acc, dHt + (size_t)bh * kD * kD, t);
+        for (int n = n0; n < n1; ++n)
+            sub_bf16_8(acc, dHb16 + ((size_t)bh * Tq + L[n]) * kD * kD, t);
+        put_dd8(sH, acc, t);
         if (t < kD) {
             float z = dZt[(size_t)bh * kD + t];
             for (int n = n0; n < n1; ++n) z -= dZq[((size_t)bh * Tq + L[n]) * kD + t];
@@ -319,8 +332,9 @@ __global__ __launch_bounds__(256) void bwd_lin_keys_kernel(
     const int lane = t & 63, w = t >> 6, l32 = lane & 31;
     const int mt = w & 1, c0 = 64 * (w >> 1);
     f32x16 x[2] = {zero16(), zero16()}, y[2] = {zero16(), zero16()};
-    mfma_f32_row<2>(x, sA, kLd, 1, sH, 1, kLd, 32 * mt, c0, kD, lane);  // sum_e v[u][e] dh[c][e]
-    mfma_f32_row<2>(y, sB, kLd, 1, sH, kLd, 1, 32 * mt, c0, kD, lane);  // sum_c phi(k)[u][c] dh[c][e]
+    // x = sum_e v[u][e] dh[c][e], y = sum_c phi(k)[u][c] dh[c][e]
+    mfma_f32_row<2>(x, sA, kLd, 1, sH, 1, kLd, 32 * mt, c0, kD, lane);
+    mfma_f32_row<2>(y, sB, kLd, 1, sH, kLd, 1, 32 * mt, c0, kD, lane);
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
         const int u = 32 * mt + acc_row(r, lane), tok = j * 64 + u;
@@ -344,6 +358,7 @@ __global__ __launch_bounds__(256) void bwd_lin_keys_kernel(
 __global__ __launch_bounds__(256) void blk_summ_kernel(const uint16_t* __restrict__ K,
                                                        const uint16_t* __restrict__ V,
                                                        float* __restrict__ hblk,
+                                                       uint16_t* __restrict__ hb16,
                                                        float* __restrict__ zblk, int N, int Tkv,
                                                        int H, Strides st) {
     __shared__ float sP[64 * kLd];  // phi(K_j) [u][c]
@@ -359,10 +374,15 @@ __global__ __launch_bounds__(256) void blk_summ_kernel(const uint16_t* __restric
     f32x16 h[4] = {zero16(), zero16(), zero16(), zero16()};
     mfma_f32_row<4>(h, sP, 1, kLd, sV, kLd, 1, 32 * w, 0, 64, lane);
     float* ho = hblk + ((size_t)bh * Tkv + j) * kD * kD;
+    uint16_t* ho16 = hb16 + ((size_t)bh * Tkv + j) * kD * kD;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) ho[(32 * w + acc_row(r, lane)) * kD + 32 * i + l32] = h[i][r];
+        for (int r = 0; r < 16; ++r) {
+            const int o = (32 * w + acc_row(r, lane)) * kD + 32 * i + l32;
+            ho[o] = h[i][r];
+            ho16[o] = __builtin_bit_cast(uint16_t, (__bf16)h[i][r]);
+        }
     if (t < kD) {
         float z = 0.0f;
         for (int u = 0; u < 64; ++u) z += sP[u * kLd + t];
@@ -1008,16 +1028,16 @@ hipError_t launch_backward_mfma(const Dims& D, const void* Q, const void* K, con
     hipError_t e = hipSuccess;
     if (lin) {
         timing_before(s, K_BWD_BLK_SUMM);
-        blk_summ_kernel<<<head_major_grid(D.BH, D.Tkv), 256, 0, s>>>(kk, v, bw.hblk, bw.zblk, D.N,
-                                                                     D.Tkv, D.H, D.st);
+        blk_summ_kernel<<<head_major_grid(D.BH, D.Tkv), 256, 0, s>>>(
+            kk, v, bw.hblk, bw.hb16, bw.zblk, D.N, D.Tkv, D.H, D.st);
         timing_after(s, K_BWD_BLK_SUMM);
         if ((e = hipGetLastError()) != hipSuccess) return e;
         if ((e = sum_parts(D, bw.hblk, bw.zblk, ws.htot, ws.ztot, D.Tkv, s)) != hipSuccess)
             return e;
         timing_before(s, K_BWD_LIN_ROWS);
         bwd_lin_rows_kernel<<<head_major_grid(D.BH, D.Tq), 256, 0, s>>>(
-            q, dO, idx, alpha, ws.htot, ws.ztot, bw.hblk, bw.zblk, dQ, bw.dHq, bw.dZq, bw.da, D.N,
-            D.Tq, D.Tkv, D.k, D.H, D.st, D.alpha_qblock);
+            q, dO, idx, alpha, ws.htot, ws.ztot, bw.hb16, bw.zblk, dQ, bw.dHq, bw.dHb16, bw.dZq,
+            bw.da, D.N, D.Tq, D.Tkv, D.k, D.H, D.st, D.alpha_qblock);
         timing_after(s, K_BWD_LIN_ROWS);
         if ((e = hipGetLastError()) != hipSuccess) return e;
         if ((e = sum_parts(D, bw.dHq, bw.dZq, bw.dHt, bw.dZt, D.Tq, s)) != hipSuccess) return e;
@@ -1026,8 +1046,8 @@ hipError_t launch_backward_mfma(const Dims& D, const void* Q, const void* K, con
     if (lin) {
         timing_before(s, K_BWD_LIN_KEYS);
         bwd_lin_keys_kernel<<<head_major_grid(D.BH, D.Tkv), 256, 0, s>>>(
-            kk, v, bw.dHt, bw.dZt, bw.dHq, bw.dZq, bw.off, bw.list, dK, dV, D.N, D.Tq, D.Tkv, D.k,
-            D.H, D.st);
+            kk, v, bw.dHt, bw.dZt, bw.dHb16, bw.dZq, bw.off, bw.list, dK, dV, D.N, D.Tq, D.Tkv,
+            D.k, D.H, D.st);
         timing_after(s, K_BWD_LIN_KEYS);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }

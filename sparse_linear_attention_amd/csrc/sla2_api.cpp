@@ -127,6 +127,8 @@ size_t layout_backward(const Dims& D, char* base, FwdWS* ws, BwdWS* bw) {
         b.zblk = carve<float>(base, off, 4 * bh * D.Tkv * d);
         b.dHq = carve<float>(base, off, 4 * bh * D.Tq * d * d);
         b.dZq = carve<float>(base, off, 4 * bh * D.Tq * d);
+        b.hb16 = carve<uint16_t>(base, off, 2 * bh * D.Tkv * d * d);
+        b.dHb16 = carve<uint16_t>(base, off, 2 * bh * D.Tq * d * d);
         const size_t np = (size_t)D.Tq * 128;
         b.gh = carve<uint16_t>(base, off, 2 * bh * np * d);
         b.gl = carve<uint16_t>(base, off, 2 * bh * np * d);

@@ -155,6 +155,8 @@ struct BwdWS {
     float* zblk;    // [BH][Tkv][d]    z_j
     float* dHq;     // [BH][Tq][d][d]  dL/dH_i
     float* dZq;     // [BH][Tq][d]     dL/dZ_i
+    uint16_t* hb16; // [BH][Tkv][d][d] h_j rounded to bf16 (for the per-pair gathers)
+    uint16_t* dHb16;// [BH][Tq][d][d]  dH_i rounded to bf16
     uint16_t* gh;   // [BH][Tq * 128][d] bf16 high part of alpha dO (rows past N: 0)
     uint16_t* gl;   // [BH][Tq * 128][d] bf16 rest of alpha dO
 };
