@@ -535,22 +535,25 @@ __global__ __launch_bounds__(256) void bwd_keys_kernel(
 }
 
 // dalpha: per head (or per head and query block), the row values summed over
-// batch and rows in order.  grid (H or H * Tq), 64 threads.
-__global__ void dalpha_kernel(const float* __restrict__ da_row, float* __restrict__ dalpha,
-                              int B, int H, int N, int bq, int Tq, int per_qblock) {
+// batch and rows in a fixed order: 256 threads take interleaved rows (fp64
+// partial sums), combined by a fixed tree.  grid (H or H * Tq).
+__global__ __launch_bounds__(256) void dalpha_kernel(const float* __restrict__ da_row,
+                                                     float* __restrict__ dalpha, int B, int H,
+                                                     int N, int bq, int Tq, int per_qblock) {
+    __shared__ double red[4];
     const int x = blockIdx.x;
     const int h = per_qblock ? x / Tq : x;
     const int qb = per_qblock ? x % Tq : 0;
     const int t0 = per_qblock ? qb * bq : 0, t1 = per_qblock ? min(N, t0 + bq) : N;
-    double s = 0.0;
+    double part = 0.0;
     for (int b = 0; b < B; ++b) {
         const float* r = da_row + ((size_t)b * H + h) * N;
-        double part = 0.0;
-        for (int t = t0 + (int)threadIdx.x; t < t1; t += 64) part += (double)r[t];
-        for (int off = 32; off >= 1; off >>= 1) part += __shfl_xor(part, off);
-        s += part;
+        for (int t = t0 + (int)threadIdx.x; t < t1; t += 256) part += (double)r[t];
     }
-    if (threadIdx.x == 0) dalpha[x] = (float)s;
+    for (int off = 32; off >= 1; off >>= 1) part += __shfl_xor(part, off);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = part;
+    __syncthreads();
+    if (threadIdx.x == 0) dalpha[x] = (float)((red[0] + red[1]) + (red[2] + red[3]));
 }
 
 }  // namespace
@@ -563,8 +566,8 @@ hipError_t launch_invert(const Dims& D, const int32_t* idx, const BwdWS& bw, hip
 
 hipError_t launch_dalpha(const Dims& D, const BwdWS& bw, float* dalpha, hipStream_t s) {
     const int na = D.alpha_qblock ? D.H * D.Tq : D.H;
-    dalpha_kernel<<<dim3((unsigned)na), 64, 0, s>>>(bw.da, dalpha, D.B, D.H, D.N, D.bq, D.Tq,
-                                                    D.alpha_qblock);
+    dalpha_kernel<<<dim3((unsigned)na), 256, 0, s>>>(bw.da, dalpha, D.B, D.H, D.N, D.bq, D.Tq,
+                                                     D.alpha_qblock);
     return hipGetLastError();
 }
 
