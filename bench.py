@@ -13,8 +13,8 @@ FlashAttention2's dense work).  Prints ONE JSON line.
 
 Options: --steps K --warmup W; --gpus N (only 1: the path runs on one GPU);
 --no-cpu-baseline skips the oracle timing; --workload wan13b for the smaller
-shape; --no-fp8 skips the extra timings of sla2_forward_fp8 (the low-bit
-sparse branch on the same inputs: e4m3 or int8 Q/K, V bf16 or e4m3);
+shape; --no-fp8 skips the extra timings of sla2_attention_fp8 (route + the
+low-bit sparse branch on the same inputs: e4m3 or int8 Q/K, V bf16 or e4m3);
 --no-sla1 skips the extra timing of the SLA (v1) mode (sla1_route +
 sla1_forward, k_h 5 %, k_l 10 %, softmax phi) on the same inputs;
 --no-train skips the timing of the training-side calls on the same inputs
@@ -346,11 +346,10 @@ def main():
         for key, lb in (("fp8", S.LOWBIT_QK), ("fp8_v", S.LOWBIT_QKV),
                         ("i8", S.LOWBIT_I8QK), ("i8_v", S.LOWBIT_I8QKV)):
             p8 = S.problem(w.B, w.H, w.N, w.d, w.bq, w.bkv, w.topk_frac, 1, w.dtype, lowbit=lb)
-            ws8 = S.workspace(p8, S.OP_FORWARD_FP8)
+            ws8 = S.workspace(p8, S.OP_ATTENTION_FP8)
 
-            def step8():
-                S.sla2_route(p8, q, k, wq, wk, idx, None, ws_r, stream)
-                S.sla2_forward_fp8(p8, q, k, v, idx, al, O, ws8, stream)
+            def step8():  # route + low-bit forward in one call, as the bf16 step
+                S.sla2_attention_fp8(p8, q, k, v, wq, wk, al, idx, O, ws8, stream)
 
             for _ in range(args.warmup):
                 step8()

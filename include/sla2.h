@@ -103,7 +103,8 @@ typedef enum {
     SLA2_OP_SLA1_FORWARD = 3,  /* sla1_forward               */
     SLA2_OP_ROUTE_GRAD = 4,    /* sla2_route_grad            */
     SLA2_OP_BACKWARD = 5,      /* sla2_backward              */
-    SLA2_OP_ATTENTION = 6      /* sla2_attention             */
+    SLA2_OP_ATTENTION = 6,     /* sla2_attention             */
+    SLA2_OP_ATTENTION_FP8 = 7  /* sla2_attention_fp8         */
 } sla2_op;
 
 typedef struct {
@@ -233,6 +234,23 @@ sla2_status sla2_attention(const sla2_problem* p, const void* Q, const void* K, 
 sla2_status sla2_forward_fp8(const sla2_problem* p, const void* Q, const void* K,
                              const void* V, const int32_t* topk_idx, const float* alpha,
                              void* O, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * sla2_attention_fp8 -- sla2_route followed by sla2_forward_fp8 in one call
+ *   (same kernels, bit-identical O and topk_idx; same requirements as
+ *   sla2_forward_fp8).  The low-bit quantisation and the block summaries
+ *   (which read K, V, and Q only for its codes) run on the helper stream of
+ *   sla2_attention, concurrently with the router, joined before the fused
+ *   kernel with events; the helper stream is shared with sla2_attention (the
+ *   same conditions apply).
+ * In : Q, K, V, Wq, Wk, alpha as sla2_route / sla2_forward_fp8.
+ * Out: topk_idx [B,H,T_q,k] (NULL allowed when k = 0); O as sla2_forward_fp8.
+ * ws : sla2_workspace_bytes(p, SLA2_OP_ATTENTION_FP8) bytes.
+ */
+sla2_status sla2_attention_fp8(const sla2_problem* p, const void* Q, const void* K,
+                               const void* V, const float* Wq, const float* Wk,
+                               const float* alpha, int32_t* topk_idx, void* O, void* ws,
+                               size_t ws_bytes, void* stream);
 
 /*
  * sla2_quantize_fp8 -- the low-bit inputs alone (the quantisation step that

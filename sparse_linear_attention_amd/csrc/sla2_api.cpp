@@ -38,19 +38,19 @@ static sla2_status make_dims(const sla2_problem* p, int op, Dims* D) {
         return SLA2_EINVAL;
     if (p->out_dtype != SLA2_F32 && p->out_dtype != SLA2_BF16) return SLA2_EINVAL;
     if (p->lowbit < SLA2_LOWBIT_QK || p->lowbit > SLA2_LOWBIT_I8QKV) return SLA2_EINVAL;
-    if (op < SLA2_OP_ROUTE || op > SLA2_OP_ATTENTION) return SLA2_EINVAL;
+    if (op < SLA2_OP_ROUTE || op > SLA2_OP_ATTENTION_FP8) return SLA2_EINVAL;
     if (p->d != 64 && p->d != 128) return SLA2_EUNSUPPORTED;
     if (p->bq != 64 && p->bq != 128) return SLA2_EUNSUPPORTED;
     if (p->bkv != 64) return SLA2_EUNSUPPORTED;
     if (p->phi != SLA2_PHI_ELU1 && p->phi != SLA2_PHI_SOFTMAX) return SLA2_EUNSUPPORTED;
     const bool fast = p->dtype == SLA2_BF16 && p->bq == 128 && p->d == 128;
-    if ((op == SLA2_OP_FORWARD_FP8 || op == SLA2_OP_SLA1_FORWARD) && !fast)
-        return SLA2_EUNSUPPORTED;
+    const bool lowbit_op = op == SLA2_OP_FORWARD_FP8 || op == SLA2_OP_ATTENTION_FP8;
+    if ((lowbit_op || op == SLA2_OP_SLA1_FORWARD) && !fast) return SLA2_EUNSUPPORTED;
     // softmax phi: the bf16 d = 128, bq = 128 kernels only (routing ignores phi)
     const bool routing = op == SLA2_OP_ROUTE || op == SLA2_OP_ROUTE_GRAD;
     // the backward takes elu + 1 only
     if (op == SLA2_OP_BACKWARD && p->phi != SLA2_PHI_ELU1) return SLA2_EUNSUPPORTED;
-    if (p->phi == SLA2_PHI_SOFTMAX && (op == SLA2_OP_FORWARD_FP8 || (!routing && !fast)))
+    if (p->phi == SLA2_PHI_SOFTMAX && (lowbit_op || (!routing && !fast)))
         return SLA2_EUNSUPPORTED;
     long bh = (long)p->B * p->H;
     if (bh > 65535) return SLA2_EUNSUPPORTED;
@@ -206,6 +206,9 @@ static size_t ws_bytes_of(const Dims& D, int op) {
     if (op == SLA2_OP_ATTENTION)  // route region, then the forward's
         return layout_route(D, nullptr, nullptr) +
                layout_forward(D, SLA2_OP_FORWARD, nullptr, nullptr);
+    if (op == SLA2_OP_ATTENTION_FP8)
+        return layout_route(D, nullptr, nullptr) +
+               layout_forward(D, SLA2_OP_FORWARD_FP8, nullptr, nullptr);
     return layout_forward(D, op, nullptr, nullptr);
 }
 
@@ -413,6 +416,39 @@ SLA2_API sla2_status sla2_attention(const sla2_problem* p, const void* Q, const 
     if (e == hipSuccess) e = launch_route(D, Q, K, Wq, Wk, topk_idx, nullptr, rw, s);
     if (e == hipSuccess) e = hipStreamWaitEvent(s, sd->join, 0);
     if (e == hipSuccess) e = launch_fused_mfma(D, Q, K, topk_idx, alpha, O, fw, s);
+    return e == hipSuccess ? SLA2_OK : SLA2_EHIP;
+}
+
+SLA2_API sla2_status sla2_attention_fp8(const sla2_problem* p, const void* Q, const void* K,
+                                        const void* V, const float* Wq, const float* Wk,
+                                        const float* alpha, int32_t* topk_idx, void* O,
+                                        void* ws, size_t ws_bytes, void* stream) {
+    Dims D;
+    sla2_status st = make_dims(p, SLA2_OP_ATTENTION_FP8, &D);
+    if (st != SLA2_OK) return st;
+    if (!ok_ptr(Q) || !ok_ptr(K) || !ok_ptr(V) || !ok_ptr(Wq) || !ok_ptr(Wk) || !ok_ptr(alpha) ||
+        !ok_ptr(O))
+        return SLA2_EINVAL;
+    if (D.k > 0 && !ok_ptr(topk_idx)) return SLA2_EINVAL;
+    if ((st = check_ws(D, SLA2_OP_ATTENTION_FP8, ws, ws_bytes)) != SLA2_OK) return st;
+    RouteWS rw;
+    FwdWS fw;
+    const size_t roff = layout_route(D, (char*)ws, &rw);
+    layout_forward(D, SLA2_OP_FORWARD_FP8, (char*)ws + roff, &fw);
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t e;
+    Side* sd = nullptr;
+    if ((e = side_stream(&sd)) != hipSuccess) return SLA2_EHIP;
+    // quantisation and block summaries on the helper stream, the router on
+    // the caller's
+    if ((e = hipEventRecord(sd->fork, s)) != hipSuccess) return SLA2_EHIP;
+    if ((e = hipStreamWaitEvent(sd->s, sd->fork, 0)) != hipSuccess) return SLA2_EHIP;
+    e = launch_quantize_fp8(D, Q, K, V, fw, sd->s);
+    if (e == hipSuccess) e = launch_summaries_mfma(D, K, V, fw, sd->s);
+    if (e == hipSuccess) e = hipEventRecord(sd->join, sd->s);
+    if (e == hipSuccess) e = launch_route(D, Q, K, Wq, Wk, topk_idx, nullptr, rw, s);
+    if (e == hipSuccess) e = hipStreamWaitEvent(s, sd->join, 0);
+    if (e == hipSuccess) e = launch_fused128(D, Q, K, topk_idx, alpha, O, fw, true, s);
     return e == hipSuccess ? SLA2_OK : SLA2_EHIP;
 }
 

@@ -17,7 +17,7 @@ OK, EINVAL, EUNSUPPORTED, EWORKSPACE, EHIP = range(5)
 F32, BF16 = 0, 1
 PHI_ELU1, PHI_SOFTMAX = 0, 1
 (OP_ROUTE, OP_FORWARD, OP_FORWARD_FP8, OP_SLA1_FORWARD, OP_ROUTE_GRAD, OP_BACKWARD,
- OP_ATTENTION) = range(7)
+ OP_ATTENTION, OP_ATTENTION_FP8) = range(8)
 LAYOUT_BHND, LAYOUT_BNHD = 0, 1
 ALPHA_PER_HEAD, ALPHA_PER_QBLOCK = 0, 1
 LOWBIT_QK, LOWBIT_QKV, LOWBIT_I8QK, LOWBIT_I8QKV = 0, 1, 2, 3
@@ -73,6 +73,7 @@ def lib():
         L.sla2_soft_topk_grad.argtypes = [P, vp, vp, C.c_float, vp, vp]
         L.sla2_route_grad.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, C.c_size_t, vp]
         L.sla2_attention.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, C.c_size_t, vp]
+        L.sla2_attention_fp8.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, C.c_size_t, vp]
         L.sla2_backward.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, C.c_size_t, vp]
         L.sla1_route.argtypes = [P, vp, vp, C.c_float, vp, vp, vp, vp, C.c_size_t, vp]
         L.sla1_forward.argtypes = [P, vp, vp, vp, vp, vp, C.c_float, vp, vp, vp, C.c_size_t, vp]
@@ -85,7 +86,7 @@ EXPORTS = ("sla2_num_q_blocks", "sla2_num_kv_blocks", "sla2_topk", "sla2_workspa
            "sla2_quantize_fp8", "sla2_quantize_v_fp8", "sla2_timing_start", "sla2_timing_stop",
            "sla2_kernel_kinds", "sla2_kernel_name", "sla1_num_negligible", "sla1_route",
            "sla1_forward", "sla2_soft_topk", "sla2_soft_topk_grad", "sla2_route_grad",
-           "sla2_backward", "sla2_attention")
+           "sla2_backward", "sla2_attention", "sla2_attention_fp8")
 
 
 def _dtype(x):
@@ -206,9 +207,17 @@ def sla2_attention(p, Q, K, V, Wq, Wk, alpha, topk_idx, O, ws=None, stream=None)
            "sla2_attention")
 
 
-def attention(p: Problem, Q, K, V, Wq, Wk, alpha, ws=None, stream=None):
+def sla2_attention_fp8(p, Q, K, V, Wq, Wk, alpha, topk_idx, O, ws=None, stream=None):
+    wp, wb = _ws(ws)
+    _raise(lib().sla2_attention_fp8(C.byref(p), _ptr(Q), _ptr(K), _ptr(V), _ptr(Wq), _ptr(Wk),
+                                    _ptr(alpha), _ptr(topk_idx), _ptr(O), wp, wb,
+                                    _stream(stream)), "sla2_attention_fp8")
+
+
+def attention(p: Problem, Q, K, V, Wq, Wk, alpha, ws=None, stream=None, fp8=False):
     """Allocates idx, O and the workspace; runs sla2_attention (route +
-    forward); returns (idx, O)."""
+    forward), or sla2_attention_fp8 (route + low-bit forward) with fp8;
+    returns (idx, O)."""
     import torch
     dev = Q.device
     idx = torch.empty((p.B, p.H, num_q_blocks(p), max(topk(p), 0)), dtype=torch.int32,
@@ -217,8 +226,9 @@ def attention(p: Problem, Q, K, V, Wq, Wk, alpha, ws=None, stream=None):
     O = torch.empty(shape, dtype=torch.float32 if p.out_dtype == F32 else torch.bfloat16,
                     device=dev)
     if ws is None:
-        ws = workspace(p, OP_ATTENTION, dev)
-    sla2_attention(p, Q, K, V, Wq, Wk, alpha, idx if topk(p) > 0 else None, O, ws, stream)
+        ws = workspace(p, OP_ATTENTION_FP8 if fp8 else OP_ATTENTION, dev)
+    fn = sla2_attention_fp8 if fp8 else sla2_attention
+    fn(p, Q, K, V, Wq, Wk, alpha, idx if topk(p) > 0 else None, O, ws, stream)
     return idx, O
 
 

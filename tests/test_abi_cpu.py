@@ -105,7 +105,12 @@ def test_sla1_counts_and_checks(orc):
     assert S.check(p_ok(), S.OP_ATTENTION) == S.OK
     assert S.workspace_bytes(p_ok(), S.OP_ATTENTION) == (
         S.workspace_bytes(p_ok(), S.OP_ROUTE) + S.workspace_bytes(p_ok(), S.OP_FORWARD))
-    assert S.check(p_ok(), 7) == S.EINVAL
+    assert S.check(p_ok(), S.OP_ATTENTION_FP8) == S.OK
+    assert S.workspace_bytes(p_ok(), S.OP_ATTENTION_FP8) == (
+        S.workspace_bytes(p_ok(), S.OP_ROUTE) + S.workspace_bytes(p_ok(), S.OP_FORWARD_FP8))
+    for kw in (dict(dtype=S.F32), dict(bq=64), dict(d=64), dict(phi=S.PHI_SOFTMAX)):
+        assert S.check(p_ok(**kw), S.OP_ATTENTION_FP8) == S.EUNSUPPORTED
+    assert S.check(p_ok(), 8) == S.EINVAL
     for wh in (1, 2):
         extra = S.workspace_bytes(p_ok(w_heads=wh), S.OP_SLA1_FORWARD) - S.workspace_bytes(
             p_ok(w_heads=wh), S.OP_FORWARD)

@@ -135,3 +135,29 @@ def test_attention_batches_and_options(dev, case):
         if frac > 0:
             assert torch.equal(idx0, idx1)
         assert torch.equal(O0, O1)
+
+
+@pytest.mark.parametrize("lowbit", [S.LOWBIT_QK, S.LOWBIT_QKV, S.LOWBIT_I8QK, S.LOWBIT_I8QKV],
+                         ids=["fp8", "fp8-v", "i8", "i8-v"])
+def test_attention_fp8_equals_route_then_forward_fp8(dev, lowbit):
+    """sla2_attention_fp8 (quantisation and block summaries on the helper
+    stream beside the router) gives the same selection and the same output
+    bits as sla2_route followed by sla2_forward_fp8; two batch entries,
+    token-major layout, per-query-block alpha."""
+    B, H, N, d = 2, 3, 2000, 128
+    say(f"case attention fp8 lowbit={lowbit}: B={B} H={H} N={N}")
+    x = I.make_inputs(I.Workload("a8", B, H, N, d, 128, 64, 0.1, "bf16", "smooth", seed=29))
+    lay = S.LAYOUT_BNHD
+    q, k, v = (upload(a, dev, lay) for a in (x.q, x.k, x.v))
+    wq, wk = (torch.from_numpy(a).to(dev) for a in (x.wq, x.wk))
+    p = S.problem(B, H, N, d, 128, 64, 0.1, 1, "bf16", layout=lay,
+                  alpha_mode=S.ALPHA_PER_QBLOCK, lowbit=lowbit)
+    rng = np.random.default_rng(31)
+    al = torch.from_numpy(rng.uniform(0.2, 0.9, (H, S.num_q_blocks(p))).astype(np.float32)).to(dev)
+    idx0, _ = S.route(p, q, k, wq, wk, want_mask=False)
+    O0 = S.forward(p, q, k, v, idx0, al, fp8=True)
+    for _ in range(2):
+        idx1, O1 = S.attention(p, q, k, v, wq, wk, al, fp8=True)
+        torch.cuda.synchronize()
+        assert torch.equal(idx0, idx1)
+        assert torch.equal(O0, O1)
