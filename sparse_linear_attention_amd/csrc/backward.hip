@@ -1,7 +1,8 @@
-// Backward of the SLA2 forward with the hard selection held fixed (vector
-// ALU, fp32 arithmetic; any dtype, d in {64, 128}, b_q in {64, 128}, phi =
-// elu + 1).  L = sum dO . O with O = alpha O_s + (1 - alpha) O_l
-// ("SLA2 深度解读" 04; the SLA notes' key designs 3 and 4 for O_l).
+// Backward of the SLA2 forward with the hard selection held fixed, vector-ALU
+// form (fp32 arithmetic; phi = elu + 1) for the problems the matrix-core
+// backward (backward_mfma.hip: bf16 with d = b_q = 128) does not take: fp32
+// inputs, d = 64 or b_q = 64.  L = sum dO . O with O = alpha O_s + (1 -
+// alpha) O_l ("SLA2 深度解读" 04; the SLA notes' key designs 3 and 4 for O_l).
 //
 // Per query row t of block i, with g = dO_t, gs = alpha g, e = (1 - alpha) g:
 //   sparse  D = gs . O_s; for every selected token u: p = exp(l_tu - LSE_t),
