@@ -129,3 +129,27 @@ def test_backward_wan13b_one_head(orc, dev):
     _check("dK", dK.cpu().numpy(), rK)
     _check("dV", dV.cpu().numpy(), rV)
     _check("dalpha", da.cpu().numpy(), ra)
+
+
+@pytest.mark.parametrize("dtype,bq,frac", [("bf16", 128, 0.2), ("bf16", 128, 1.0), ("f32", 64, 0.25)],
+                         ids=["matrix-core", "matrix-core-all-selected", "valu"])
+def test_backward_ignores_workspace_contents(dev, dtype, bq, frac):
+    """A workspace filled with NaN bit patterns gives the same gradients, bit
+    for bit, as a zeroed one: no pass reads workspace memory it has not
+    written in the same call."""
+    N, H, d = 1100, 2, 128 if dtype == "bf16" else 64
+    gen = "centroids" if dtype == "f32" else "smooth"
+    w = I.Workload("ws", 1, H, N, d, bq, 64, frac, dtype, gen, seed=41)
+    x = I.make_inputs(w)
+    q, k, v, wq, wk, al = to_dev(x, dev)
+    p = S.problem(1, H, N, d, bq, 64, frac, 1, dtype)
+    idx, _ = S.route(p, q, k, wq, wk, want_mask=False)
+    dO = torch.from_numpy(np.random.default_rng(8).normal(0, 1, (1, H, N, d)).astype(np.float32)).to(dev)
+    outs = []
+    for fill in (0x00, 0xFF):
+        ws = S.workspace(p, S.OP_BACKWARD, dev)
+        ws.fill_(fill)
+        outs.append(S.backward(p, q, k, v, idx, al, dO, ws=ws))
+        torch.cuda.synchronize()
+    for a, b in zip(*outs):
+        assert torch.equal(a, b)

@@ -161,3 +161,22 @@ def test_attention_fp8_equals_route_then_forward_fp8(dev, lowbit):
         torch.cuda.synchronize()
         assert torch.equal(idx0, idx1)
         assert torch.equal(O0, O1)
+
+
+@pytest.mark.parametrize("fp8", [False, True], ids=["bf16", "fp8"])
+def test_attention_ignores_workspace_contents(dev, fp8):
+    """A workspace filled with NaN bit patterns gives the same selection and
+    output bits as a zeroed one."""
+    B, H, N, d = 1, 2, 1500, 128
+    x = I.make_inputs(I.Workload("ws", B, H, N, d, 128, 64, 0.15, "bf16", "smooth", seed=43))
+    q, k, v = (upload(a, dev, S.LAYOUT_BHND) for a in (x.q, x.k, x.v))
+    wq, wk, al = (torch.from_numpy(a).to(dev) for a in (x.wq, x.wk, x.alpha))
+    p = S.problem(B, H, N, d, 128, 64, 0.15, 1, "bf16")
+    outs = []
+    for fill in (0x00, 0xFF):
+        ws = S.workspace(p, S.OP_ATTENTION_FP8 if fp8 else S.OP_ATTENTION, dev)
+        ws.fill_(fill)
+        outs.append(S.attention(p, q, k, v, wq, wk, al, ws=ws, fp8=fp8))
+        torch.cuda.synchronize()
+    assert torch.equal(outs[0][0], outs[1][0])
+    assert torch.equal(outs[0][1], outs[1][1])
