@@ -352,11 +352,13 @@ __global__ void zero_mask_kernel(uint8_t* __restrict__ mask, size_t n) {
 }  // namespace
 
 hipError_t launch_pool_project(const Dims& D, const void* Q, const void* K, const float* Wq,
-                               const float* Wk, const RouteWS& ws, hipStream_t s) {
+                               const float* Wk, const RouteWS& ws, hipStream_t s, bool pooled) {
     // pool (means into ws.xq / ws.xk), then project them with a tiled product
     dim3 g1(D.Tq + D.Tkv, (unsigned)D.BH);
     timing_before(s, K_POOL_PROJECT);
-    if (D.dtype == SLA2_F32)
+    if (pooled) {
+        // the means are there already
+    } else if (D.dtype == SLA2_F32)
         pool_project_kernel<float><<<g1, 256, 0, s>>>(
             (const float*)Q, (const float*)K, nullptr, nullptr, ws.xq, ws.xk, D.N, D.d, D.bq,
             D.bkv, D.Tq, D.Tkv, D.H, D.w_heads, D.st);
@@ -372,8 +374,8 @@ hipError_t launch_pool_project(const Dims& D, const void* Q, const void* K, cons
 }
 
 hipError_t launch_scores(const Dims& D, const void* Q, const void* K, const float* Wq,
-                         const float* Wk, const RouteWS& ws, hipStream_t s) {
-    hipError_t e = launch_pool_project(D, Q, K, Wq, Wk, ws, s);
+                         const float* Wk, const RouteWS& ws, hipStream_t s, bool pooled) {
+    hipError_t e = launch_pool_project(D, Q, K, Wq, Wk, ws, s, pooled);
     if (e != hipSuccess) return e;
     dim3 g2((D.Tkv + 63) / 64, (D.Tq + 63) / 64, (unsigned)D.BH);
     timing_before(s, K_SCORE);
@@ -384,7 +386,7 @@ hipError_t launch_scores(const Dims& D, const void* Q, const void* K, const floa
 
 hipError_t launch_route(const Dims& D, const void* Q, const void* K, const float* Wq,
                         const float* Wk, int32_t* idx, uint8_t* mask, const RouteWS& ws,
-                        hipStream_t s) {
+                        hipStream_t s, bool pooled) {
     if (D.k == 0) {  // nothing is selected: only the mask (if wanted) is written
         if (mask) {
             const size_t n = (size_t)D.BH * D.Tq * D.Tkv;
@@ -395,7 +397,7 @@ hipError_t launch_route(const Dims& D, const void* Q, const void* K, const float
         }
         return hipGetLastError();
     }
-    hipError_t e = launch_scores(D, Q, K, Wq, Wk, ws, s);
+    hipError_t e = launch_scores(D, Q, K, Wq, Wk, ws, s, pooled);
     if (e != hipSuccess) return e;
 
     dim3 g3(D.Tq, (unsigned)D.BH);

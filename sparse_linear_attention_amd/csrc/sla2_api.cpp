@@ -3,6 +3,7 @@
 #include <math.h>
 #include <string.h>
 
+#include <algorithm>
 #include <mutex>
 #include <vector>
 
@@ -180,13 +181,17 @@ size_t layout_forward(const Dims& D, int op, char* base, FwdWS* ws) {
     w.zpart = carve<float>(base, off, 4 * bh * nch * d);
     w.htot = carve<float>(base, off, 4 * bh * d * d);
     w.ztot = carve<float>(base, off, 4 * bh * d);
-    if (op == SLA2_OP_FORWARD_FP8) {
+    if (op == SLA2_OP_FORWARD_FP8 || op == SLA2_OP_ATTENTION_FP8) {
         w.qhat = carve<uint8_t>(base, off, bh * (size_t)D.Tq * D.bq * d);
         w.khat = carve<uint8_t>(base, off, bh * (size_t)D.Tkv * 64 * d);
         w.sq = carve<float>(base, off, 4 * bh * D.Tq);
         w.sk = carve<float>(base, off, 4 * bh * D.Tkv);
         w.mu = carve<float>(base, off, 4 * bh * d);
-        w.ksum = carve<double>(base, off, 8 * bh * ((D.N + 1023) / 1024) * d);
+        // the combined call keeps one row of column sums per KV block
+        const size_t krows = op == SLA2_OP_ATTENTION_FP8
+                                 ? (size_t)std::max(D.Tkv, (D.N + 1023) / 1024)
+                                 : (size_t)((D.N + 1023) / 1024);
+        w.ksum = carve<double>(base, off, 8 * bh * krows * d);
         if (D.lowbit_v) {
             w.vhat = carve<uint8_t>(base, off, bh * (size_t)D.Tkv * d * 64);
             w.vmax = carve<float>(base, off, 4 * bh * ((D.N + 1023) / 1024) * d);
@@ -208,7 +213,7 @@ static size_t ws_bytes_of(const Dims& D, int op) {
                layout_forward(D, SLA2_OP_FORWARD, nullptr, nullptr);
     if (op == SLA2_OP_ATTENTION_FP8)
         return layout_route(D, nullptr, nullptr) +
-               layout_forward(D, SLA2_OP_FORWARD_FP8, nullptr, nullptr);
+               layout_forward(D, SLA2_OP_ATTENTION_FP8, nullptr, nullptr);
     return layout_forward(D, op, nullptr, nullptr);
 }
 
@@ -233,7 +238,7 @@ const char* kKindNames[K_NUM_KINDS] = {
     "quant_mean",   "quant_fp8",   "fused_fp8",  "quant_v_fp8",
     "quant_i8",     "fused_i8",    "fused_sla1",  "bwd_rows",
     "bwd_dh",       "bwd_keys",    "bwd_lin_rows", "bwd_lin_keys",
-    "bwd_rows_mfma", "bwd_keys_mfma", "bwd_blk_summ", "bwd_sum_parts",
+    "bwd_rows_mfma", "bwd_keys_mfma", "bwd_blk_summ", "bwd_sum_parts", "pool_quant",
 };
 }  // namespace
 
@@ -359,7 +364,7 @@ SLA2_API sla2_status sla2_forward(const sla2_problem* p, const void* Q, const vo
 namespace {
 struct Side {
     hipStream_t s = nullptr;
-    hipEvent_t fork = nullptr, join = nullptr;
+    hipEvent_t fork = nullptr, join = nullptr, pooled = nullptr;
 };
 constexpr int kMaxDevices = 64;
 Side g_side[kMaxDevices];
@@ -377,6 +382,8 @@ hipError_t side_stream(Side** out) {
         if ((e = hipStreamCreateWithFlags(&sd.s, hipStreamNonBlocking)) != hipSuccess) return e;
         if ((e = hipEventCreateWithFlags(&sd.fork, hipEventDisableTiming)) != hipSuccess) return e;
         if ((e = hipEventCreateWithFlags(&sd.join, hipEventDisableTiming)) != hipSuccess) return e;
+        if ((e = hipEventCreateWithFlags(&sd.pooled, hipEventDisableTiming)) != hipSuccess)
+            return e;
     }
     *out = &sd;
     return hipSuccess;
@@ -434,19 +441,24 @@ SLA2_API sla2_status sla2_attention_fp8(const sla2_problem* p, const void* Q, co
     RouteWS rw;
     FwdWS fw;
     const size_t roff = layout_route(D, (char*)ws, &rw);
-    layout_forward(D, SLA2_OP_FORWARD_FP8, (char*)ws + roff, &fw);
+    layout_forward(D, SLA2_OP_ATTENTION_FP8, (char*)ws + roff, &fw);
     hipStream_t s = (hipStream_t)stream;
     hipError_t e;
     Side* sd = nullptr;
     if ((e = side_stream(&sd)) != hipSuccess) return SLA2_EHIP;
-    // quantisation and block summaries on the helper stream, the router on
-    // the caller's
+    // caller's stream: the router, whose pooling pass also writes the query
+    // codes and the K block sums; helper stream: the block summaries, then
+    // (once the pooling pass is done) the K mean, the key codes and the V
+    // codes.  The same codes as sla2_quantize_fp8 (exact fp64 sums).
     if ((e = hipEventRecord(sd->fork, s)) != hipSuccess) return SLA2_EHIP;
     if ((e = hipStreamWaitEvent(sd->s, sd->fork, 0)) != hipSuccess) return SLA2_EHIP;
-    e = launch_quantize_fp8(D, Q, K, V, fw, sd->s);
-    if (e == hipSuccess) e = launch_summaries_mfma(D, K, V, fw, sd->s);
+    e = launch_summaries_mfma(D, K, V, fw, sd->s);
+    if (e == hipSuccess) e = launch_pool_quant(D, Q, K, rw, fw, s);
+    if (e == hipSuccess) e = hipEventRecord(sd->pooled, s);
+    if (e == hipSuccess) e = hipStreamWaitEvent(sd->s, sd->pooled, 0);
+    if (e == hipSuccess) e = launch_quantize_k(D, K, V, fw, sd->s);
     if (e == hipSuccess) e = hipEventRecord(sd->join, sd->s);
-    if (e == hipSuccess) e = launch_route(D, Q, K, Wq, Wk, topk_idx, nullptr, rw, s);
+    if (e == hipSuccess) e = launch_route(D, Q, K, Wq, Wk, topk_idx, nullptr, rw, s, true);
     if (e == hipSuccess) e = hipStreamWaitEvent(s, sd->join, 0);
     if (e == hipSuccess) e = launch_fused128(D, Q, K, topk_idx, alpha, O, fw, true, s);
     return e == hipSuccess ? SLA2_OK : SLA2_EHIP;

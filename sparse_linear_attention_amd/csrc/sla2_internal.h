@@ -37,6 +37,7 @@ enum KernelKind {
     K_BWD_KEYS_MFMA,
     K_BWD_BLK_SUMM,
     K_BWD_SUM_PARTS,
+    K_POOL_QUANT,
     K_NUM_KINDS
 };
 
@@ -126,7 +127,8 @@ struct FwdWS {
     float* sq;       // [BH][Tq]
     float* sk;       // [BH][Tkv]
     float* mu;       // [BH][d]
-    double* ksum;    // [BH][ceil(N/1024)][d] partial column sums of K
+    double* ksum;    // [BH][ceil(N/1024)][d] partial column sums of K (in the
+                     // combined low-bit call: [BH][Tkv][d], one row per KV block)
     // fully low-bit (V quantised per channel)
     uint8_t* vhat;   // [BH][Tkv][d][64] e4m3 codes of V / s_V, keys in the order
                      // of the e4m3 P V product's k operand (see fused128.hip)
@@ -190,16 +192,20 @@ void timing_after(hipStream_t s, int kind);
 // ---------------------------------------------------------------------------
 // launchers (each returns hipGetLastError() after its launches)
 // ---------------------------------------------------------------------------
+// pooled: ws.xq / ws.xk already hold the pooled means (launch_pool_quant),
+// so the pooling pass is skipped
 hipError_t launch_route(const Dims& D, const void* Q, const void* K, const float* Wq,
                         const float* Wk, int32_t* idx, uint8_t* mask, const RouteWS& ws,
-                        hipStream_t s);
+                        hipStream_t s, bool pooled = false);
 
 // router stages: pooled rows and their projections (ws.xq/xk, ws.qt/kt);
 // then the scores (ws.S)
 hipError_t launch_pool_project(const Dims& D, const void* Q, const void* K, const float* Wq,
-                               const float* Wk, const RouteWS& ws, hipStream_t s);
+                               const float* Wk, const RouteWS& ws, hipStream_t s,
+                               bool pooled = false);
 hipError_t launch_scores(const Dims& D, const void* Q, const void* K, const float* Wq,
-                         const float* Wk, const RouteWS& ws, hipStream_t s);
+                         const float* Wk, const RouteWS& ws, hipStream_t s,
+                         bool pooled = false);
 
 // training-time router: SoftTop-k, its gradient, the projections' gradient
 hipError_t launch_soft_topk(const Dims& D, const void* Q, const void* K, const float* Wq,
@@ -258,6 +264,15 @@ hipError_t launch_fused_mfma(const Dims& D, const void* Q, const void* K,
 // low bit
 hipError_t launch_quantize_fp8(const Dims& D, const void* Q, const void* K, const void* V,
                                const FwdWS& ws, hipStream_t s);
+// The same codes in two parts that share the router's reads:
+// launch_pool_quant pools Q and K for the router (rw.xq, rw.xk), writes the
+// query codes and scales and each KV block's column sums of K (fw.ksum, Tkv
+// rows per head); launch_quantize_k then takes the K mean from those sums,
+// writes the key codes and scales, and the V codes with lowbit_v.
+hipError_t launch_pool_quant(const Dims& D, const void* Q, const void* K, const RouteWS& rw,
+                             const FwdWS& fw, hipStream_t s);
+hipError_t launch_quantize_k(const Dims& D, const void* K, const void* V, const FwdWS& fw,
+                             hipStream_t s);
 // V codes in rows [BH][Tkv*64][d] (inspection; s_V into ws.sv)
 hipError_t launch_quantize_v_rows(const Dims& D, const void* V, uint8_t* vhat_rows,
                                   const FwdWS& ws, hipStream_t s);
