@@ -237,12 +237,14 @@ sla2_status sla2_forward_fp8(const sla2_problem* p, const void* Q, const void* K
 
 /*
  * sla2_attention_fp8 -- sla2_route followed by sla2_forward_fp8 in one call
- *   (same kernels, bit-identical O and topk_idx; same requirements as
- *   sla2_forward_fp8).  The low-bit quantisation and the block summaries
- *   (which read K, V, and Q only for its codes) run on the helper stream of
- *   sla2_attention, concurrently with the router, joined before the fused
- *   kernel with events; the helper stream is shared with sla2_attention (the
- *   same conditions apply).
+ *   (bit-identical O and topk_idx; same requirements as sla2_forward_fp8).
+ *   The router's pooling pass also writes the query codes and the column
+ *   sums of K per KV block, so Q is read once; the block summaries run on
+ *   the helper stream of sla2_attention from the start, then (after the
+ *   pooling pass, through an event) the K mean, the key codes and, with the
+ *   low-bit V, the V codes, concurrently with the rest of the router; both
+ *   streams join before the fused kernel.  The helper stream is shared with
+ *   sla2_attention (the same conditions apply).
  * In : Q, K, V, Wq, Wk, alpha as sla2_route / sla2_forward_fp8.
  * Out: topk_idx [B,H,T_q,k] (NULL allowed when k = 0); O as sla2_forward_fp8.
  * ws : sla2_workspace_bytes(p, SLA2_OP_ATTENTION_FP8) bytes.
