@@ -88,56 +88,66 @@ __global__ __launch_bounds__(256) void pool_project_kernel(
     }
 }
 
-// S[bh][i][j] = qt[bh][i] . kt[bh][j]; 64x64 tile per work-group, 4x4 per thread.
+typedef double f64x4 __attribute__((ext_vector_type(4)));
+
+// S[bh][i][j] = qt[bh][i] . kt[bh][j] on the fp64 matrix cores
+// (v_mfma_f64_16x16x4_f64: A[i][k] in lane i + 16 k, B[k][j] in lane
+// j + 16 k, D[i][j] in lane j + 16 (i % 4), item i / 4).  A 64 x 64 tile
+// per work-group, 32 x 32 (2 x 2 products) per wave, operands straight from
+// L2 (a head's qt and kt are (Tq + Tkv) d 8 B).  For channels k0 .. k0+7
+// lane i + 16 kq loads the pair k0 + 2 kq, k0 + 2 kq + 1 of its row in one
+// 16-byte load; the first product of the step takes the first of each pair,
+// the second the other, so every channel enters each score exactly once.
+// Rows past Tq / Tkv read the last row and are not stored.  d = 64 or 128.
+template <int d>
 __global__ __launch_bounds__(256) void score_kernel(const double* __restrict__ qt,
                                                     const double* __restrict__ kt,
-                                                    double* __restrict__ S, int Tq, int Tkv,
-                                                    int d) {
-    __shared__ double As[16][65];
-    __shared__ double Bs[16][65];
-    const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
-    const int i0 = blockIdx.y * 64, j0 = blockIdx.x * 64;
+                                                    double* __restrict__ S, int Tq, int Tkv) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int r16 = lane & 15, kq = lane >> 4;
     const long bh = blockIdx.z;
+    const int iw = blockIdx.y * 64 + 32 * (w >> 1), jw = blockIdx.x * 64 + 32 * (w & 1);
     const double* A = qt + (size_t)bh * Tq * d;
-    const double* Bm = kt + (size_t)bh * Tkv * d;
-    double acc[4][4];
+    const double* B = kt + (size_t)bh * Tkv * d;
+    const double* ar[2];
+    const double* br[2];
 #pragma unroll
-    for (int a = 0; a < 4; ++a)
+    for (int m = 0; m < 2; ++m) {
+        ar[m] = A + (size_t)min(iw + 16 * m + r16, Tq - 1) * d + 2 * kq;
+        br[m] = B + (size_t)min(jw + 16 * m + r16, Tkv - 1) * d + 2 * kq;
+    }
+    f64x4 acc[2][2];
 #pragma unroll
-        for (int b = 0; b < 4; ++b) acc[a][b] = 0.0;
-    for (int k0 = 0; k0 < d; k0 += 16) {
-        for (int x = threadIdx.x; x < 1024; x += 256) {
-            const int row = x >> 4, kk = x & 15;
-            const int gi = i0 + row, gj = j0 + row;
-            As[kk][row] = gi < Tq ? A[(size_t)gi * d + k0 + kk] : 0.0;
-            Bs[kk][row] = gj < Tkv ? Bm[(size_t)gj * d + k0 + kk] : 0.0;
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) acc[mt][nt] = f64x4{0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+    for (int k0 = 0; k0 < d; k0 += 8) {
+        double2 a[2], b[2];
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+            a[m] = *reinterpret_cast<const double2*>(ar[m] + k0);
+            b[m] = *reinterpret_cast<const double2*>(br[m] + k0);
         }
-        __syncthreads();
 #pragma unroll
-        for (int kk = 0; kk < 16; ++kk) {
-            double a[4], b[4];
+        for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                a[q] = As[kk][ty + 16 * q];
-                b[q] = Bs[kk][tx + 16 * q];
+            for (int nt = 0; nt < 2; ++nt) {
+                acc[mt][nt] = __builtin_amdgcn_mfma_f64_16x16x4f64(a[mt].x, b[nt].x, acc[mt][nt],
+                                                                   0, 0, 0);
+                acc[mt][nt] = __builtin_amdgcn_mfma_f64_16x16x4f64(a[mt].y, b[nt].y, acc[mt][nt],
+                                                                   0, 0, 0);
             }
-#pragma unroll
-            for (int p = 0; p < 4; ++p)
-#pragma unroll
-                for (int q = 0; q < 4; ++q) acc[p][q] = fma(a[p], b[q], acc[p][q]);
-        }
-        __syncthreads();
     }
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {
-        const int i = i0 + ty + 16 * p;
-        if (i >= Tq) continue;
+    for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int j = j0 + tx + 16 * q;
-            if (j < Tkv) S[((size_t)bh * Tq + i) * Tkv + j] = acc[p][q];
-        }
-    }
+        for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int i = iw + 16 * mt + kq + 4 * r, j = jw + 16 * nt + r16;
+                if (i < Tq && j < Tkv) S[((size_t)bh * Tq + i) * Tkv + j] = acc[mt][nt][r];
+            }
 }
 
 // y = x W for the pooled rows of one (head, side): grid (row tiles of 64,
@@ -349,6 +359,14 @@ __global__ void zero_mask_kernel(uint8_t* __restrict__ mask, size_t n) {
         mask[i] = 0;
 }
 
+void launch_score_kernel(const Dims& D, const RouteWS& ws, hipStream_t s) {
+    dim3 g2((D.Tkv + 63) / 64, (D.Tq + 63) / 64, (unsigned)D.BH);
+    if (D.d == 128)
+        score_kernel<128><<<g2, 256, 0, s>>>(ws.qt, ws.kt, ws.S, D.Tq, D.Tkv);
+    else
+        score_kernel<64><<<g2, 256, 0, s>>>(ws.qt, ws.kt, ws.S, D.Tq, D.Tkv);
+}
+
 }  // namespace
 
 hipError_t launch_pool_project(const Dims& D, const void* Q, const void* K, const float* Wq,
@@ -377,9 +395,8 @@ hipError_t launch_scores(const Dims& D, const void* Q, const void* K, const floa
                          const float* Wk, const RouteWS& ws, hipStream_t s, bool pooled) {
     hipError_t e = launch_pool_project(D, Q, K, Wq, Wk, ws, s, pooled);
     if (e != hipSuccess) return e;
-    dim3 g2((D.Tkv + 63) / 64, (D.Tq + 63) / 64, (unsigned)D.BH);
     timing_before(s, K_SCORE);
-    score_kernel<<<g2, 256, 0, s>>>(ws.qt, ws.kt, ws.S, D.Tq, D.Tkv, D.d);
+    launch_score_kernel(D, ws, s);
     timing_after(s, K_SCORE);
     return hipGetLastError();
 }
@@ -431,9 +448,8 @@ hipError_t launch_route_v1(const Dims& D, const void* Q, const void* K, int kl, 
             (const uint16_t*)Q, (const uint16_t*)K, nullptr, nullptr, ws.qt, ws.kt, D.N, D.d,
             D.bq, D.bkv, D.Tq, D.Tkv, D.H, D.w_heads, D.st);
     timing_after(s, K_POOL_PROJECT);
-    dim3 g2((D.Tkv + 63) / 64, (D.Tq + 63) / 64, (unsigned)D.BH);
     timing_before(s, K_SCORE);
-    score_kernel<<<g2, 256, 0, s>>>(ws.qt, ws.kt, ws.S, D.Tq, D.Tkv, D.d);
+    launch_score_kernel(D, ws, s);
     timing_after(s, K_SCORE);
     dim3 g3(D.Tq, (unsigned)D.BH);
     const size_t sh = sizeof(unsigned long long) * D.Tkv;
