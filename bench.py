@@ -23,7 +23,11 @@ device copy (used to scale rocprofv3 FETCH_SIZE / WRITE_SIZE);
 --counters-summary FETCH WRITE COPY_FETCH COPY_WRITE turns four rocprofv3
 --pmc output folders (the bench, then the copy) into the per-launch HBM
 traffic of the fused kernel, written to profiles/ and read back by later
-runs while the kernel source is unchanged.
+runs while the kernel source is unchanged; --traffic-table FETCH WRITE
+COPY_FETCH COPY_WRITE prints the same scaled traffic, the mean dispatch
+time and the achieved GB/s for every kernel in those folders;
+--counter-table DIR prints every counter's mean per dispatch and the mean
+dispatch time for every kernel in one rocprofv3 --pmc folder.
 """
 from __future__ import annotations
 
@@ -131,6 +135,68 @@ def _counter_means(folder, counter, name_rx):
     return sum(v) / len(v), len(v), sorted(names)
 
 
+def _per_kernel(folder):
+    """{short kernel name: {"n": dispatches, "ns": mean duration, counter: mean
+    per dispatch}} from a rocprofv3 --pmc csv folder (durations from the
+    dispatch timestamps of the counter run)."""
+    import csv
+    import glob
+    import re
+    files = glob.glob(os.path.join(folder, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no counter_collection.csv under {folder}")
+    disp = {}
+    for f in files:
+        for r in csv.DictReader(open(f)):
+            name = re.sub(r"^(void )?sla2::\(anonymous namespace\)::", "", r["Kernel_Name"])
+            name = re.sub(r"\(.*$", "", name)
+            d = disp.setdefault((name, f, r["Dispatch_Id"]), {})
+            d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+            d["ns"] = float(r["End_Timestamp"]) - float(r["Start_Timestamp"])
+    out = {}
+    for (name, _, _), d in disp.items():
+        e = out.setdefault(name, {"n": 0})
+        e["n"] += 1
+        for k, v in d.items():
+            e[k] = e.get(k, 0.0) + v
+    for e in out.values():
+        for k in list(e):
+            if k != "n":
+                e[k] /= e["n"]
+    return out
+
+
+def traffic_table(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir):
+    cf, _, _ = _counter_means(copy_fetch_dir, "FETCH_SIZE", "copyBuffer")
+    cw, _, _ = _counter_means(copy_write_dir, "WRITE_SIZE", "copyBuffer")
+    f_fac = COPY_BYTES / (cf * 1024.0)
+    w_fac = COPY_BYTES / (cw * 1024.0)
+    fk, wk = _per_kernel(fetch_dir), _per_kernel(write_dir)
+    print(f"scale: FETCH_SIZE x {f_fac:.3f}, WRITE_SIZE x {w_fac:.3f} "
+          f"(1 GiB device copy: {cf:.0f} KiB fetched, {cw:.0f} KiB written per dispatch)")
+    print(f"{'kernel':58s} {'disp':>4s} {'read GB':>9s} {'write GB':>9s} {'ms':>8s} "
+          f"{'GB/s':>8s} {'of 8 TB/s':>9s}")
+    for name in sorted(fk, key=lambda n: -fk[n]["ns"]):
+        if "copyBuffer" in name or name not in wk or "FETCH_SIZE" not in fk[name]:
+            continue
+        rd = fk[name]["FETCH_SIZE"] * 1024.0 * f_fac
+        wr = wk[name].get("WRITE_SIZE", 0.0) * 1024.0 * w_fac
+        ns = fk[name]["ns"]
+        gbs = (rd + wr) / ns
+        print(f"{name[:58]:58s} {fk[name]['n']:4d} {rd / 1e9:9.3f} {wr / 1e9:9.3f} "
+              f"{ns / 1e6:8.3f} {gbs:8.0f} {gbs / 8000:9.1%}")
+
+
+def counter_table(folder):
+    pk = _per_kernel(folder)
+    for name in sorted(pk, key=lambda n: -pk[n]["ns"]):
+        e = pk[name]
+        print(f"{name}: {e['n']} dispatches, {e['ns'] / 1e6:.3f} ms per dispatch")
+        for k in sorted(e):
+            if k not in ("n", "ns"):
+                print(f"    {k:32s} {e[k]:.6g}")
+
+
 def counters_summary(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, workload):
     fk, fn, names = _counter_means(fetch_dir, "FETCH_SIZE", FUSED_KERNEL_RX)
     wk, wn, _ = _counter_means(write_dir, "WRITE_SIZE", FUSED_KERNEL_RX)
@@ -201,10 +267,18 @@ def main():
     ap.add_argument("--no-train", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--counters-summary", nargs=4, metavar="DIR")
+    ap.add_argument("--traffic-table", nargs=4, metavar="DIR")
+    ap.add_argument("--counter-table", metavar="DIR")
     args = ap.parse_args()
 
     if args.counters_summary:
         counters_summary(*args.counters_summary, workload=args.workload)
+        return
+    if args.traffic_table:
+        traffic_table(*args.traffic_table)
+        return
+    if args.counter_table:
+        counter_table(args.counter_table)
         return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
