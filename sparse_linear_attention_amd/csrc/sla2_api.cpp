@@ -378,12 +378,22 @@ hipError_t side_stream(Side** out) {
     std::lock_guard<std::mutex> lk(g_side_mu);
     Side& sd = g_side[dev];
     if (!sd.s) {
-        // default priority (no priority argument), independent of the null stream
-        if ((e = hipStreamCreateWithFlags(&sd.s, hipStreamNonBlocking)) != hipSuccess) return e;
-        if ((e = hipEventCreateWithFlags(&sd.fork, hipEventDisableTiming)) != hipSuccess) return e;
-        if ((e = hipEventCreateWithFlags(&sd.join, hipEventDisableTiming)) != hipSuccess) return e;
-        if ((e = hipEventCreateWithFlags(&sd.pooled, hipEventDisableTiming)) != hipSuccess)
+        // default priority (no priority argument), independent of the null stream.
+        // Kept only once all four handles exist, so that a failure here is
+        // retried by the next call instead of leaving some of them null.
+        Side n;
+        if ((e = hipStreamCreateWithFlags(&n.s, hipStreamNonBlocking)) == hipSuccess &&
+            (e = hipEventCreateWithFlags(&n.fork, hipEventDisableTiming)) == hipSuccess &&
+            (e = hipEventCreateWithFlags(&n.join, hipEventDisableTiming)) == hipSuccess &&
+            (e = hipEventCreateWithFlags(&n.pooled, hipEventDisableTiming)) == hipSuccess) {
+            sd = n;
+        } else {
+            if (n.pooled) (void)hipEventDestroy(n.pooled);
+            if (n.join) (void)hipEventDestroy(n.join);
+            if (n.fork) (void)hipEventDestroy(n.fork);
+            if (n.s) (void)hipStreamDestroy(n.s);
             return e;
+        }
     }
     *out = &sd;
     return hipSuccess;
