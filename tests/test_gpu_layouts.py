@@ -140,10 +140,11 @@ def test_attention_batches_and_options(dev, case):
 @pytest.mark.parametrize("lowbit", [S.LOWBIT_QK, S.LOWBIT_QKV, S.LOWBIT_I8QK, S.LOWBIT_I8QKV],
                          ids=["fp8", "fp8-v", "i8", "i8-v"])
 def test_attention_fp8_equals_route_then_forward_fp8(dev, lowbit):
-    """sla2_attention_fp8 (quantisation and block summaries on the helper
-    stream beside the router) gives the same selection and the same output
-    bits as sla2_route followed by sla2_forward_fp8; two batch entries,
-    token-major layout, per-query-block alpha."""
+    """sla2_attention_fp8 (query codes and K block sums from the router's
+    pooling pass, block summaries and key codes on the helper stream) gives
+    the same selection and the same output bits as sla2_route followed by
+    sla2_forward_fp8; two batch entries, token-major layout, per-query-block
+    alpha."""
     B, H, N, d = 2, 3, 2000, 128
     say(f"case attention fp8 lowbit={lowbit}: B={B} H={H} N={N}")
     x = I.make_inputs(I.Workload("a8", B, H, N, d, 128, 64, 0.1, "bf16", "smooth", seed=29))
@@ -161,6 +162,27 @@ def test_attention_fp8_equals_route_then_forward_fp8(dev, lowbit):
         torch.cuda.synchronize()
         assert torch.equal(idx0, idx1)
         assert torch.equal(O0, O1)
+
+
+@pytest.mark.parametrize("frac", [0.0, 1.0], ids=["k0", "all-selected"])
+@pytest.mark.parametrize("lowbit", [S.LOWBIT_QK, S.LOWBIT_I8QKV], ids=["fp8", "i8-v"])
+def test_attention_fp8_edge_selections(dev, lowbit, frac):
+    """sla2_attention_fp8 with nothing selected (k = 0: only the linear
+    branch) and with every block selected (k = T_kv): the same output bits as
+    sla2_route + sla2_forward_fp8; ragged last blocks (N = 1500)."""
+    B, H, N, d = 1, 2, 1500, 128
+    say(f"case attention fp8 lowbit={lowbit} frac={frac}: N={N}")
+    x = I.make_inputs(I.Workload("a8e", B, H, N, d, 128, 64, frac, "bf16", "smooth", seed=37))
+    q, k, v = (upload(a, dev, S.LAYOUT_BHND) for a in (x.q, x.k, x.v))
+    wq, wk, al = (torch.from_numpy(a).to(dev) for a in (x.wq, x.wk, x.alpha))
+    p = S.problem(B, H, N, d, 128, 64, frac, 1, "bf16", lowbit=lowbit)
+    idx0 = S.route(p, q, k, wq, wk, want_mask=False)[0] if frac > 0 else None
+    O0 = S.forward(p, q, k, v, idx0, al, fp8=True)
+    idx1, O1 = S.attention(p, q, k, v, wq, wk, al, fp8=True)
+    torch.cuda.synchronize()
+    if frac > 0:
+        assert torch.equal(idx0, idx1)
+    assert torch.equal(O0, O1)
 
 
 @pytest.mark.parametrize("fp8", [False, True], ids=["bf16", "fp8"])
