@@ -362,6 +362,24 @@ def test_quantized_v_matches_oracle(orc, dev, N, H):
         assert not vh[bh, N:].any()
 
 
+def test_attention_fp8_wan14b_equals_route_then_forward_fp8(dev):
+    """At the full 14B shape, in the configuration the bench times, the
+    one-call low-bit attention (query codes and K block sums from the
+    router's pooling pass) gives the same selection and output bits as
+    sla2_route followed by sla2_forward_fp8 (whose codes the quantisation
+    tests pin to the oracle)."""
+    x = I.make_inputs(I.WAN14B)
+    p = problem_of(x, S.LOWBIT_QK)
+    q, k, v, wq, wk, al = to_dev(x, dev)
+    say("case attention fp8 at the 14B shape")
+    idx0, _ = S.route(p, q, k, wq, wk, want_mask=False)
+    O0 = S.forward(p, q, k, v, idx0, al, fp8=True)
+    idx1, O1 = S.attention(p, q, k, v, wq, wk, al, fp8=True)
+    torch.cuda.synchronize()
+    assert torch.equal(idx0, idx1)
+    assert torch.equal(O0, O1)
+
+
 @pytest.mark.parametrize("lowbit", LOWBITS, ids=LOWBIT_IDS)
 def test_fp8_wan14b_sampled(orc, dev, lowbit):
     w = I.WAN14B
