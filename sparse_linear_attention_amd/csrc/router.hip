@@ -150,64 +150,72 @@ __global__ __launch_bounds__(256) void score_kernel(const double* __restrict__ q
             }
 }
 
-// y = x W for the pooled rows of one (head, side): grid (row tiles of 64,
-// 2 d / 64, BH) with y = side * (d / 64) + column tile (side 0: queries
-// with Wq, 1: keys with Wk); 4x4 outputs per thread, fp64, each output
-// accumulated over c = 0 .. d-1 in order (the same rounding as a plain loop).
+// y = x W for the pooled rows of one (head, side) on the fp64 matrix cores,
+// with the operand layouts of score_kernel: grid (row tiles of 64, 2 d / 64,
+// BH) with y = side * (d / 64) + column tile (side 0: queries with Wq, 1:
+// keys with Wk); 32 x 32 outputs (2 x 2 products) per wave.  Lane i + 16 kq
+// loads the pair of channels k0 + 2 kq, k0 + 2 kq + 1 of its x row in one
+// 16-byte load and the matching two fp32 entries of its W column; the two
+// products of a step of 8 channels take the first and the second of each
+// pair.  Rows past the side's count read its last row and are not stored.
+template <int d>
 __global__ __launch_bounds__(256) void proj_kernel(const double* __restrict__ xq,
                                                    const double* __restrict__ xk,
                                                    const float* __restrict__ Wq,
                                                    const float* __restrict__ Wk,
                                                    double* __restrict__ qt, double* __restrict__ kt,
-                                                   int Tq, int Tkv, int d, int H, int w_heads) {
-    __shared__ double As[16][65];
-    __shared__ double Bs[16][65];
-    const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
+                                                   int Tq, int Tkv, int H, int w_heads) {
+    constexpr int ct = d / 64;
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int r16 = lane & 15, kq = lane >> 4;
     const long bh = blockIdx.z;
-    const int ct = d >> 6;
     const int side = (int)blockIdx.y / ct;
     const int rows = side ? Tkv : Tq;
-    const int i0 = blockIdx.x * 64, e0 = ((int)blockIdx.y % ct) * 64;
-    if (i0 >= rows) return;
+    const int iw = blockIdx.x * 64 + 32 * (w >> 1);
+    const int ew = ((int)blockIdx.y % ct) * 64 + 32 * (w & 1);
+    if ((int)blockIdx.x * 64 >= rows) return;
     const double* X = side ? xk + (size_t)bh * Tkv * d : xq + (size_t)bh * Tq * d;
     const float* W = (side ? Wk : Wq) + (w_heads == 1 ? 0 : (size_t)(bh % H) * d * d);
     double* Y = side ? kt + (size_t)bh * Tkv * d : qt + (size_t)bh * Tq * d;
-    double acc[4][4];
+    const double* xr[2];
 #pragma unroll
-    for (int a = 0; a < 4; ++a)
+    for (int m = 0; m < 2; ++m) xr[m] = X + (size_t)min(iw + 16 * m + r16, rows - 1) * d + 2 * kq;
+    f64x4 acc[2][2];
 #pragma unroll
-        for (int b = 0; b < 4; ++b) acc[a][b] = 0.0;
-    for (int k0 = 0; k0 < d; k0 += 16) {
-        for (int x = threadIdx.x; x < 1024; x += 256) {
-            const int row = x >> 4, kk = x & 15;
-            const int gi = i0 + row;
-            As[kk][row] = gi < rows ? X[(size_t)gi * d + k0 + kk] : 0.0;
-            const int col = x & 63, kr = x >> 6;
-            Bs[kr][col] = (double)W[(size_t)(k0 + kr) * d + e0 + col];
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) acc[mt][nt] = f64x4{0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+    for (int k0 = 0; k0 < d; k0 += 8) {
+        double2 a[2];
+        double b0[2], b1[2];
+#pragma unroll
+        for (int m = 0; m < 2; ++m) a[m] = *reinterpret_cast<const double2*>(xr[m] + k0);
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) {
+            const float* wc = W + (size_t)(k0 + 2 * kq) * d + ew + 16 * nt + r16;
+            b0[nt] = (double)wc[0];
+            b1[nt] = (double)wc[d];
         }
-        __syncthreads();
 #pragma unroll
-        for (int kk = 0; kk < 16; ++kk) {
-            double a[4], b[4];
+        for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                a[q] = As[kk][ty + 16 * q];
-                b[q] = Bs[kk][tx + 16 * q];
+            for (int nt = 0; nt < 2; ++nt) {
+                acc[mt][nt] =
+                    __builtin_amdgcn_mfma_f64_16x16x4f64(a[mt].x, b0[nt], acc[mt][nt], 0, 0, 0);
+                acc[mt][nt] =
+                    __builtin_amdgcn_mfma_f64_16x16x4f64(a[mt].y, b1[nt], acc[mt][nt], 0, 0, 0);
             }
-#pragma unroll
-            for (int p = 0; p < 4; ++p)
-#pragma unroll
-                for (int q = 0; q < 4; ++q) acc[p][q] = fma(a[p], b[q], acc[p][q]);
-        }
-        __syncthreads();
     }
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {
-        const int i = i0 + ty + 16 * p;
-        if (i >= rows) continue;
+    for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) Y[(size_t)i * d + e0 + tx + 16 * q] = acc[p][q];
-    }
+        for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int i = iw + 16 * mt + kq + 4 * r;
+                if (i < rows) Y[(size_t)i * d + ew + 16 * nt + r16] = acc[mt][nt][r];
+            }
 }
 
 // Order-preserving map of an fp64 score to an unsigned key (-0 -> +0 first).
@@ -385,8 +393,12 @@ hipError_t launch_pool_project(const Dims& D, const void* Q, const void* K, cons
             (const uint16_t*)Q, (const uint16_t*)K, nullptr, nullptr, ws.xq, ws.xk, D.N, D.d,
             D.bq, D.bkv, D.Tq, D.Tkv, D.H, D.w_heads, D.st);
     dim3 gp((max(D.Tq, D.Tkv) + 63) / 64, 2 * (D.d / 64), (unsigned)D.BH);
-    proj_kernel<<<gp, 256, 0, s>>>(ws.xq, ws.xk, Wq, Wk, ws.qt, ws.kt, D.Tq, D.Tkv, D.d, D.H,
-                                   D.w_heads);
+    if (D.d == 128)
+        proj_kernel<128><<<gp, 256, 0, s>>>(ws.xq, ws.xk, Wq, Wk, ws.qt, ws.kt, D.Tq, D.Tkv, D.H,
+                                            D.w_heads);
+    else
+        proj_kernel<64><<<gp, 256, 0, s>>>(ws.xq, ws.xk, Wq, Wk, ws.qt, ws.kt, D.Tq, D.Tkv, D.H,
+                                           D.w_heads);
     timing_after(s, K_POOL_PROJECT);
     return hipGetLastError();
 }
