@@ -350,14 +350,18 @@ def main():
     ms_step = ev0.elapsed_time(ev1) / args.steps
     log(f"bench: {ms_step:.3f} ms/step (wall {1e3 * t_wall / args.steps:.3f})")
     # the same work as separate sla2_route + sla2_forward calls, for reference
+    # (every kernel alone on one stream: the per-kernel times without overlap)
     for _ in range(args.warmup):
         step_sequential()
+    torch.cuda.synchronize()
+    S.timing_start(64 * args.steps + 64)
     ev0.record(stream)
     for _ in range(args.steps):
         step_sequential()
     ev1.record(stream)
     torch.cuda.synchronize()
     ms_seq = ev0.elapsed_time(ev1) / args.steps
+    seq_stages = {name: ms / n for name, (ms, n) in S.timing_stop().items()}
 
     BH = w.B * w.H
     dense = dense_equivalent_flop(w.B, w.H, w.N, w.d)
@@ -404,6 +408,7 @@ def main():
         "stages_ms": stages,
         "route_ms": route_ms,
         "sequential_ms_per_step": ms_seq,
+        "sequential_stages_ms": seq_stages,
         "forward_ms": fwd_ms,
         "forward_only_tops": dense / (fwd_ms * 1e-3) / 1e12 if fwd_ms else None,
         "sparse_flop_per_step": fl_sparse,

@@ -46,6 +46,12 @@ __device__ inline f32x16 zero16() {
     return z;
 }
 
+// max of two floats (not NaN) in one instruction: the median of a, b and
+// +inf.  fmaxf quiets each operand with an extra instruction first; written
+// as a builtin (not inline asm) so that the compiler keeps the wait states
+// between a matrix instruction and the reads of its result.
+__device__ inline float max2f(float a, float b) { return __builtin_amdgcn_fmed3f(a, b, INFINITY); }
+
 __device__ inline float bf16_bits(unsigned short b) { return __uint_as_float((unsigned)b << 16); }
 
 // phi = elu + 1

@@ -15,29 +15,23 @@
 //                                       e4m3 or int8 codes, times s_Q s_K)
 //   online softmax on S^T               one query per lane column
 //   O^T += V_j^T P^T                    fp16 MFMA (LOWBIT: P on the e4m3 grid)
-//   G^T += V_j^T phi(K_j)               fp16 MFMA; phi(K_j)^T comes from the
-//                                       block summaries pass, each wave loads
-//                                       its 32 channels straight into
-//                                       registers
-//   z   += z_j = colsum phi(K_j)        (also from the summaries pass)
-// G starts at -h_tot^T and z at -z_tot, so at the end H_i^T = -G^T and
-// Z_i = -z: the linear branch's sums over the unselected blocks (SLA notes,
-// key designs 3 and 4: H_i, Z_i as the total minus the selected blocks).
-// Epilogue: O_l^T = H_i^T phi(Q)^T / (phi(Q) . Z_i), O = alpha O_s +
-// (1 - alpha) O_l ("SLA2 深度解读" 04).
+// The linear branch's sums over the blocks the query block leaves out,
+// H_i = sum h_j and Z_i = sum z_j (SLA notes, key designs 3 and 4), come
+// ready from the dense product of linear.hip (one fp32 row per query block).
+// Epilogue: H_i^T scaled by a power of two into the fp16 range, O_l^T =
+// H_i^T phi(Q)^T / (phi(Q) . Z_i), O = alpha O_s + (1 - alpha) O_l
+// ("SLA2 深度解读" 04).
 //
 // PHISM: phi is the softmax of each row over its 128 channels (the block
 // summaries pass applies the same map to K).  V1 (SLA v1, "SLA: Beyond
 // Sparsity ..." notes, key designs 2 and 3): the selected blocks are the
-// critical ones, the negligible blocks are subtracted from H and Z as well
-// (a second loop over their V^T and phi(K)^T tiles, G products only), and
-// O = O_s + O_l W_p, the projection on the fp16 matrix cores with O_l split
-// into a high fp16 part and the fp16 rest.
+// critical ones, the linear branch covers the marginal blocks only (the
+// product leaves the negligible ones out as well), and O = O_s + O_l W_p,
+// the projection on the fp16 matrix cores with O_l split into a high fp16
+// part and the fp16 rest.
 //
 // K (or Khat) and V^T tiles arrive by direct-to-LDS loads, K two tiles
-// ahead (three stages), V^T one tile ahead (two stages); the phi(K)^T slice
-// and z_j of the next tile are loaded into registers once the current tile's
-// G^T products have been issued.  LDS layouts:
+// ahead (three stages), V^T one tile ahead (two stages).  LDS layouts:
 //   K    [64 keys][256 B]   16-byte chunk c of row r at chunk c ^ (r & 15)
 //   Khat [64 keys][128 B]   chunk c of row r at chunk c ^ ((r >> 1) & 7)
 //   V^T  [128 ch][128 B]    chunk c of row r at chunk c ^ ((r >> 1) & 7)
@@ -155,20 +149,18 @@ __device__ inline void issue_v8(char* v8st, rsrc_t rv8, int j, int w, uint32_t v
 template <bool LIN, int QK, bool LOWV, bool PHISM, bool V1>
 __global__ __launch_bounds__(256, 2) void fused128_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
-    const uint16_t* __restrict__ vt, const uint16_t* __restrict__ pkt,
-    const float* __restrict__ zb, const int32_t* __restrict__ idx,
-    const float* __restrict__ alpha, const float* __restrict__ htot,
-    const float* __restrict__ ztot, const uint8_t* __restrict__ qhat,
-    const uint8_t* __restrict__ khat, const float* __restrict__ sq,
-    const float* __restrict__ sk, const uint8_t* __restrict__ vhat,
-    const float* __restrict__ sv, void* __restrict__ O, int N, int Tq, int Tkv, int k,
-    int H, Strides st, int alpha_qblock, int out_bf16, const int32_t* __restrict__ negl, int kl,
+    const uint16_t* __restrict__ vt, const int32_t* __restrict__ idx,
+    const float* __restrict__ alpha, const float* __restrict__ HZ,
+    const uint8_t* __restrict__ qhat, const uint8_t* __restrict__ khat,
+    const float* __restrict__ sq, const float* __restrict__ sk,
+    const uint8_t* __restrict__ vhat, const float* __restrict__ sv, void* __restrict__ O,
+    int N, int Tq, int Tkv, int k, int H, Strides st, int alpha_qblock, int out_bf16,
     const uint16_t* __restrict__ wpf, int w_heads) {
     constexpr bool LOWBIT = QK != 0;
     static_assert(!(PHISM || V1) || (QK == 0 && !LOWV), "softmax phi and v1: bf16 path only");
     static_assert(LOWBIT || !LOWV, "quantised V only with the low-bit Q K^T");
-    // V^T in fp16 feeds P V, and G (the linear branch) with LOWV
-    constexpr bool kV16 = !LOWV || LIN;
+    // V^T in fp16 feeds P V (unless P V runs on the e4m3 codes)
+    constexpr bool kV16 = !LOWV;
     using P = Plan<LOWBIT, LOWV>;
     const int t = threadIdx.x, lane = t & 63, l32 = lane & 31, hl = lane >> 5;
     const int w = __builtin_amdgcn_readfirstlane(t >> 6);
@@ -205,26 +197,10 @@ __global__ __launch_bounds__(256, 2) void fused128_kernel(
         }
     }
 
-    // ---- accumulators: O^T (d rows 32mt.., my queries), G^T (d rows 32mt..,
-    // phi channels 32w + l32) starting at -h_tot^T, z starting at -z_tot
-    f32x16 o[4], g[4];
+    // ---- accumulators: O^T (d rows 32mt.., my queries)
+    f32x16 o[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) o[i] = zero16();
-    float zacc = 0.0f;
-    if (LIN) {
-        const float* hrow = htot + (size_t)bh * 128 * 128 + (size_t)(32 * w + l32) * 128;
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-            for (int i4 = 0; i4 < 4; ++i4) {
-                const float4 v = *reinterpret_cast<const float4*>(hrow + 32 * mt + 8 * i4 + 4 * hl);
-                g[mt][4 * i4 + 0] = -v.x;
-                g[mt][4 * i4 + 1] = -v.y;
-                g[mt][4 * i4 + 2] = -v.z;
-                g[mt][4 * i4 + 3] = -v.w;
-            }
-        zacc = hl == 0 ? -ztot[bh * 128 + 32 * w + l32] : 0.0f;
-    }
     float m_ref = -INFINITY, l_part = 0.0f;
 
     const int32_t* sel = idx + ((size_t)bh * Tq + qb) * k;
@@ -233,125 +209,18 @@ __global__ __launch_bounds__(256, 2) void fused128_kernel(
                              : head_rsrc(K + head_base(st, bh, H));
     const rsrc_t rv = head_rsrc(vt + (size_t)bh * Tkv * 128 * 64);
     const uint32_t koff = k_lane_off(w, lane, rp), toff = t_lane_off(w, lane);
-    // this wave's rows (phi channels 32w .. 32w+31) of the phi(K)^T tiles, and
-    // the matching z_j entries
-    const rsrc_t rpk = head_rsrc(pkt + (size_t)bh * Tkv * 128 * 64);
-    const uint32_t pkoff = (uint32_t)((32 * w + l32) * 128 + 16 * hl);
-    const rsrc_t rz = head_rsrc(zb + (size_t)bh * Tkv * 128);
-    const uint32_t zoff = (uint32_t)(32 * w + l32) * 4;
     const float* sk_h = LOWBIT ? sk + (size_t)bh * Tkv : nullptr;
     char* const kbase = s_lds;
     char* const vbase = s_lds + P::vOff;
     char* const v8base = s_lds + P::v8Off;
     const rsrc_t rv8 = head_rsrc(LOWV ? vhat + (size_t)bh * Tkv * kV8 : vhat);
     const uint32_t v8off = v8_lane_off(lane);
-    constexpr int DK = P::kStages - 1;  // K prefetch distance
 
-    // phi(K_j)^T as the B operand of 4 k-steps of 16 keys, and z_j
-    f16x8 pk[4];
-    float zj = 0.0f;
-    auto load_pk = [&](int j) {
-#pragma unroll
-        for (int kq = 0; kq < 4; ++kq)
-            pk[kq] = __builtin_bit_cast(
-                f16x8, __builtin_amdgcn_raw_buffer_load_b128(rpk, pkoff + 32 * kq, (uint32_t)j * 16384, 0));
-        // consumed one tile later: nothing here may wait for the load
-        zj = __builtin_bit_cast(
-            float, __builtin_amdgcn_raw_buffer_load_b32(rz, zoff, (uint32_t)j * 512, 0));
-    };
-
-    // ---- prologue: K_0, V_0, K_1 [, phi(K_0)^T, z_0]
-    if (k > 0) {
-        issue_k<LOWBIT>(kbase, rk, sel[0], N, w, lane, koff, toff, rp);
-        if (kV16) issue_v(vbase, rv, sel[0], w, toff);
-        if (LOWV) issue_v8(v8base, rv8, sel[0], w, v8off);
-        if (k > 1)
-            issue_k<LOWBIT>(kbase + P::kStage, rk, sel[1], N, w, lane, koff, toff, rp);
-        asm volatile("" ::: "memory");
-        if (LIN) load_pk(sel[0]);
-        asm volatile("" ::: "memory");
-    }
-
-    // One tile step.  MORE1 / MORE2: tiles r+1 / r+2 exist.  The last two
-    // steps are peeled off the loop, so that inside it every load is
-    // unconditional and the compiler's own waits for the phi(K)^T registers
-    // count the tile loads issued after them exactly (with a conditional load
-    // it has to assume the path without it, and waits for the next tile too).
-    int kslot = 0;
-    auto step = [&](int r, auto more1_c, auto more2_c) {
-        constexpr bool MORE1 = decltype(more1_c)::value;
-        constexpr bool MORE2 = decltype(more2_c)::value;
-        // tile r's K and V^T have landed for this wave (loads issued after
-        // V_r: at most one K tile and the phi(K_r)^T slice, may still be in
-        // flight; the compiler waits for the latter before its use) ...
-        if (MORE1) wait_vmcnt<P::nK + (LIN ? 5 : 0)>();
-        else if (LIN) wait_vmcnt<5>();
-        else wait_vmcnt<0>();
-        wg_barrier();  // ... and for every wave; all waves are done with tile r-1
-        if (MORE1) {
-            if (kV16) issue_v(vbase + ((r + 1) & 1) * kVT, rv, sel[r + 1], w, toff);
-            if (LOWV) issue_v8(v8base + ((r + 1) & 1) * kV8, rv8, sel[r + 1], w, v8off);
-        }
-        if (MORE2) {
-            const int s2 = kslot + DK >= P::kStages ? kslot + DK - P::kStages : kslot + DK;
-            issue_k<LOWBIT>(kbase + s2 * P::kStage, rk, sel[r + DK], N, w, lane, koff, toff, rp);
-        }
-        const int j = sel[r];
-        const char* kst = kbase + kslot * P::kStage;
-        const char* vst = vbase + (r & 1) * kVT;
-        const char* v8st = v8base + (r & 1) * kV8;
-        kslot = kslot + 1 == P::kStages ? 0 : kslot + 1;
-        const float c_tile = LOWBIT ? c_base * sk_h[j] : c_base;
-
-        const bool ragged = j * 64 + 64 > N;
-        const f16x2 ones = {(_Float16)1.0f, (_Float16)1.0f};
-        // O^T += V^T P^T and G^T += V^T phi(K) for k-step kq (16 keys); the
-        // V^T operand is read once for both products
-        auto pv_step = [&](int kq, const f16x8& pfk) {
-#pragma unroll
-            for (int mt = 0; mt < 4; ++mt) {
-                const int erow = 32 * mt + l32;
-                const f16x8 a = *reinterpret_cast<const f16x8*>(
-                    vst + erow * 128 + (((2 * kq + hl) ^ ((erow >> 1) & 7)) << 4));
-                o[mt] = mfma_f16(a, pfk, o[mt]);
-                if (LIN) g[mt] = mfma_f16(a, pk[kq], g[mt]);
-            }
-        };
-        // G^T += V^T phi(K) alone (when P V runs on the e4m3 operands)
-        auto g_step = [&](int kq) {
-#pragma unroll
-            for (int mt = 0; mt < 4; ++mt) {
-                const int erow = 32 * mt + l32;
-                const f16x8 a = *reinterpret_cast<const f16x8*>(
-                    vst + erow * 128 + (((2 * kq + hl) ^ ((erow >> 1) & 7)) << 4));
-                g[mt] = mfma_f16(a, pk[kq], g[mt]);
-            }
-        };
-        // new running reference after a block of logits whose maximum (over
-        // this wave's column, both lane halves) is mx; rescales O and l
-        auto update_ref = [&](float mx) {
-            const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx),
-                                                             __float_as_uint(mx), false, false);
-            mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
-            const float xmax = mx * c_tile;
-            const bool need = LOWBIT ? (xmax > m_ref) : (xmax > m_ref + kRescaleThr);
-            if (__ballot(need)) {
-                const float nref = need ? xmax : m_ref;
-                const float f = __builtin_amdgcn_exp2f(m_ref - nref);
-                l_part *= f;
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-#pragma unroll
-                    for (int e = 0; e < 16; ++e) o[i][e] *= f;
-                m_ref = nref;
-            }
-            return m_ref == -INFINITY ? 0.0f : m_ref;
-        };
-
-        // S^T = K Q^T over the whole tile (two m-tiles of 32 keys); the
-        // running maximum is updated once per tile (with LOWBIT the
-        // quantisation grid of P follows it)
-        f32x16 s[2] = {zero16(), zero16()};
+    constexpr int nV = (kV16 ? 4 : 0) + (LOWV ? 2 : 0);  // loads per lane, V tile
+    // S^T = K Q^T over the whole tile in K stage kst (two m-tiles of 32 keys)
+    auto compute_s = [&](const char* kst, f32x16 (&s)[2]) {
+        s[0] = zero16();
+        s[1] = zero16();
         if (QK == 2) {
             // int8 codes: the 32 bytes of a lane's 64-channel step go to two
             // int8 MFMAs (16 each; A and B split alike, so each sums a
@@ -405,23 +274,117 @@ __global__ __launch_bounds__(256, 2) void fused128_kernel(
                     s[mt] = mfma_bf16(a, reinterpret_cast<const bf16x8*>(Qo.f)[ks], s[mt]);
                 }
         }
-        if (ragged) {
+    };
+
+    // new running reference after a tile of logits whose maximum (over this
+    // wave's column, both lane halves) is mx, with logit scale ct; rescales
+    // O and l.  Returns the reference the tile's P is taken against.
+    auto update_ref = [&](float mx, float ct) {
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx),
+                                                         false, false);
+        mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+        const float xmax = mx * ct;
+        const bool need = LOWBIT ? (xmax > m_ref) : (xmax > m_ref + kRescaleThr);
+        if (__ballot(need)) {
+            const float nref = need ? xmax : m_ref;
+            const float f = __builtin_amdgcn_exp2f(m_ref - nref);
+            l_part *= f;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) o[i][e] *= f;
+            m_ref = nref;
+        }
+        return m_ref == -INFINITY ? 0.0f : m_ref;
+    };
+    // a tile's S is complete: mask the keys past N, then the running
+    // reference.  Only KV block T_kv - 1 is ragged, and the selection is
+    // ascending (a documented precondition), so only the last selected tile
+    // can be (may_ragged).
+    auto finish_s = [&](f32x16 (&s)[2], int jx, float ct, auto may_ragged_c) {
+        constexpr bool MAY_RAGGED = decltype(may_ragged_c)::value;
+        if (MAY_RAGGED && jx * 64 + 64 > N) {
 #pragma unroll
             for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
                 for (int i = 0; i < 16; ++i)
-                    if (j * 64 + 32 * mt + 8 * (i >> 2) + 4 * hl + (i & 3) >= N)
+                    if (jx * 64 + 32 * mt + 8 * (i >> 2) + 4 * hl + (i & 3) >= N)
                         s[mt][i] = -INFINITY;
         }
-        float mx = s[0][0];
+        // pairwise maxima in a tree (no NaN reaches here)
+        float m[16];
 #pragma unroll
-        for (int i = 1; i < 16; ++i) mx = fmaxf(mx, s[0][i]);
+        for (int i = 0; i < 16; ++i) m[i] = max2f(s[0][i], s[1][i]);
 #pragma unroll
-        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[1][i]);
-        const float mref = update_ref(mx);
+        for (int w2 = 8; w2 >= 1; w2 >>= 1)
+#pragma unroll
+            for (int i = 0; i < w2; ++i) m[i] = max2f(m[i], m[i + w2]);
+        return update_ref(m[0], ct);
+    };
+    auto ctile = [&](int jx) { return LOWBIT ? c_base * sk_h[jx] : c_base; };
+
+    // ---- prologue: K_0, K_1, V_0, K_2 (in this order), then S_0 and its
+    // reference
+    f32x16 sc[2];
+    float cur_ref = 0.0f, cur_ct = c_base;
+    if (k > 0) {
+        issue_k<LOWBIT>(kbase, rk, sel[0], N, w, lane, koff, toff, rp);
+        if (k > 1) issue_k<LOWBIT>(kbase + P::kStage, rk, sel[1], N, w, lane, koff, toff, rp);
+        if (kV16) issue_v(vbase, rv, sel[0], w, toff);
+        if (LOWV) issue_v8(v8base, rv8, sel[0], w, v8off);
+        if (k > 2) issue_k<LOWBIT>(kbase + 2 * P::kStage, rk, sel[2], N, w, lane, koff, toff, rp);
+        // K_0 has landed (issued after it: K_1, V_0, K_2)
+        if (k > 2) wait_vmcnt<2 * P::nK + nV>();
+        else if (k > 1) wait_vmcnt<P::nK + nV>();
+        else wait_vmcnt<nV>();
+        wg_barrier();
+        compute_s(kbase, sc);
+        cur_ct = ctile(sel[0]);
+        if (k == 1) cur_ref = finish_s(sc, sel[0], cur_ct, std::true_type{});
+        else cur_ref = finish_s(sc, sel[0], cur_ct, std::false_type{});
+    }
+
+    // One tile step r, with S of tile r in sc and its reference cur_ref.
+    // MORE1 / MORE2 / MORE3: tiles r+1 / r+2 / r+3 exist.  The products of
+    // tile r+1's S do not depend on tile r, so they sit in one branch-free
+    // block with tile r's P (vector ALU) and P V: the matrix cores work
+    // while the exponentials are evaluated.  Tile r+1's maximum and the
+    // rescale follow once its S is complete.  K tile x sits in stage x % 3,
+    // V tile x in stage x % 2.  The last three steps are peeled off the loop,
+    // so that inside it every load is unconditional.
+    auto step = [&](int r, int ks_r, auto more1_c, auto more2_c, auto more3_c) {
+        constexpr bool MORE1 = decltype(more1_c)::value;
+        constexpr bool MORE2 = decltype(more2_c)::value;
+        constexpr bool MORE3 = decltype(more3_c)::value;
+        // K_{r+1} and V_r have landed for this wave (issued after V_r: K_{r+2}) ...
+        if (MORE2) wait_vmcnt<P::nK>();
+        else wait_vmcnt<0>();
+        wg_barrier();  // ... and for every wave; all waves are done with K_r and V_{r-1}
+        if (MORE1) {
+            if (kV16) issue_v(vbase + ((r + 1) & 1) * kVT, rv, sel[r + 1], w, toff);
+            if (LOWV) issue_v8(v8base + ((r + 1) & 1) * kV8, rv8, sel[r + 1], w, v8off);
+        }
+        if (MORE3)
+            issue_k<LOWBIT>(kbase + ks_r * P::kStage, rk, sel[r + 3], N, w, lane, koff, toff, rp);
+        f32x16 sn[2];
+        if (MORE1) compute_s(kbase + (ks_r == 2 ? 0 : ks_r + 1) * P::kStage, sn);
+        const char* vst = vbase + (r & 1) * kVT;
+        const char* v8st = v8base + (r & 1) * kV8;
+        const float c_tile = cur_ct, mref = cur_ref;
+        const f16x2 ones = {(_Float16)1.0f, (_Float16)1.0f};
+        // O^T += V^T P^T for k-step kq (16 keys)
+        auto pv_step = [&](int kq, const f16x8& pfk) {
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt) {
+                const int erow = 32 * mt + l32;
+                const f16x8 a = *reinterpret_cast<const f16x8*>(
+                    vst + erow * 128 + (((2 * kq + hl) ^ ((erow >> 1) & 7)) << 4));
+                o[mt] = mfma_f16(a, pfk, o[mt]);
+            }
+        };
         if (LOWV) {
             // codes of 256 P~ as the k operand of the e4m3 P V product: byte
-            // 16 mt + i of this lane is the code of s[mt][i]; the row sum is
+            // 16 mt + i of this lane is the code of sc[mt][i]; the row sum is
             // taken over the decoded values
             const float bias = 8.0f - mref;
             i32x8 pc;
@@ -432,7 +395,7 @@ __global__ __launch_bounds__(256, 2) void fused128_kernel(
                     float p4[4];
 #pragma unroll
                     for (int c = 0; c < 4; ++c)
-                        p4[c] = fminf(__builtin_amdgcn_exp2f(fmaf(s[mt][4 * q + c], c_tile, bias)),
+                        p4[c] = fminf(__builtin_amdgcn_exp2f(fmaf(sc[mt][4 * q + c], c_tile, bias)),
                                       448.0f);
                     int wv = __builtin_amdgcn_cvt_pk_fp8_f32(p4[0], p4[1], 0, false);
                     wv = __builtin_amdgcn_cvt_pk_fp8_f32(p4[2], p4[3], wv, true);
@@ -454,10 +417,6 @@ __global__ __launch_bounds__(256, 2) void fused128_kernel(
                 a[4] = hi.x; a[5] = hi.y; a[6] = hi.z; a[7] = hi.w;
                 o[mt] = mfma_fp8(a, pc, o[mt]);
             }
-            if (LIN) {
-#pragma unroll
-                for (int kq = 0; kq < 4; ++kq) g_step(kq);
-            }
         } else {
             // P^T as the B operand of k-step kq (16 keys) takes rows 8(kq&1)..
             // 8(kq&1)+7 of m-tile kq>>1
@@ -468,8 +427,8 @@ __global__ __launch_bounds__(256, 2) void fused128_kernel(
                     const float bias = 8.0f - mref;
     #pragma unroll
                     for (int e = 0; e < 8; e += 2) {
-                        const float p0 = __builtin_amdgcn_exp2f(fmaf(s[kq >> 1][8 * (kq & 1) + e], c_tile, bias));
-                        const float p1 = __builtin_amdgcn_exp2f(fmaf(s[kq >> 1][8 * (kq & 1) + e + 1], c_tile, bias));
+                        const float p0 = __builtin_amdgcn_exp2f(fmaf(sc[kq >> 1][8 * (kq & 1) + e], c_tile, bias));
+                        const float p1 = __builtin_amdgcn_exp2f(fmaf(sc[kq >> 1][8 * (kq & 1) + e + 1], c_tile, bias));
                         const int code = __builtin_amdgcn_cvt_pk_fp8_f32(fminf(p0, 448.0f),
                                                                          fminf(p1, 448.0f), 0, false);
                         const auto back = __builtin_amdgcn_cvt_pk_f32_fp8(code, false);
@@ -480,7 +439,7 @@ __global__ __launch_bounds__(256, 2) void fused128_kernel(
     #pragma unroll
                     for (int e = 0; e < 8; ++e)
                         pf[e] = (_Float16)__builtin_amdgcn_exp2f(
-                            fmaf(s[kq >> 1][8 * (kq & 1) + e], c_tile, -mref));
+                            fmaf(sc[kq >> 1][8 * (kq & 1) + e], c_tile, -mref));
                 }
     #pragma unroll
                 for (int e = 0; e < 8; e += 2) {
@@ -490,51 +449,26 @@ __global__ __launch_bounds__(256, 2) void fused128_kernel(
                 pv_step(kq, pf);
             }
         }
-        if (LIN) {
-            zacc += hl == 0 ? zj : 0.0f;  // one lane half holds the channel's z_j
-            // the waits above count these loads as issued last in the
-            // iteration: keep the compiler from moving them
-            asm volatile("" ::: "memory");
-            if (MORE1) load_pk(sel[r + 1]);
-            asm volatile("" ::: "memory");
+        if (MORE1) {
+            const int jn = sel[r + 1];
+            cur_ct = ctile(jn);
+            cur_ref = finish_s(sn, jn, cur_ct, std::integral_constant<bool, !MORE2>{});
+            sc[0] = sn[0];
+            sc[1] = sn[1];
         }
     };
-    int r = 0;
-    for (; r + 2 < k; ++r) step(r, std::true_type{}, std::true_type{});
-    if (r + 1 < k) step(r++, std::true_type{}, std::false_type{});
-    if (r < k) step(r, std::false_type{}, std::false_type{});
-
-    // V1: subtract the negligible blocks from G and z as well (their V^T
-    // tiles through the two V stages, phi(K)^T and z_j one tile ahead)
-    if constexpr (V1 && LIN) {
-        if (kl > 0) {
-            const int32_t* nsel = negl + ((size_t)bh * Tq + qb) * kl;
-            wg_barrier();  // every wave is done with the tile stages
-            issue_v(vbase, rv, nsel[0], w, toff);
-            asm volatile("" ::: "memory");
-            load_pk(nsel[0]);
-            asm volatile("" ::: "memory");
-            for (int rn = 0; rn < kl; ++rn) {
-                wait_vmcnt<5>();  // V_rn landed (issued after it: phi(K_rn)^T, z_rn)
-                wg_barrier();     // ... for every wave; all are done with tile rn-1
-                if (rn + 1 < kl) issue_v(vbase + ((rn + 1) & 1) * kVT, rv, nsel[rn + 1], w, toff);
-                const char* vst = vbase + (rn & 1) * kVT;
-#pragma unroll
-                for (int kq = 0; kq < 4; ++kq)
-#pragma unroll
-                    for (int mt = 0; mt < 4; ++mt) {
-                        const int erow = 32 * mt + l32;
-                        const f16x8 a = *reinterpret_cast<const f16x8*>(
-                            vst + erow * 128 + (((2 * kq + hl) ^ ((erow >> 1) & 7)) << 4));
-                        g[mt] = mfma_f16(a, pk[kq], g[mt]);
-                    }
-                zacc += hl == 0 ? zj : 0.0f;
-                asm volatile("" ::: "memory");
-                if (rn + 1 < kl) load_pk(nsel[rn + 1]);
-                asm volatile("" ::: "memory");
-            }
-        }
+    int r = 0, ks = 0;
+    for (; r + 3 < k; ++r, ks = ks == 2 ? 0 : ks + 1)
+        step(r, ks, std::true_type{}, std::true_type{}, std::true_type{});
+    if (r + 2 < k) {
+        step(r++, ks, std::true_type{}, std::true_type{}, std::false_type{});
+        ks = ks == 2 ? 0 : ks + 1;
     }
+    if (r + 1 < k) {
+        step(r++, ks, std::true_type{}, std::false_type{}, std::false_type{});
+        ks = ks == 2 ? 0 : ks + 1;
+    }
+    if (r < k) step(r, ks, std::false_type{}, std::false_type{}, std::false_type{});
 
     // ---- epilogue
     const float l_all = l_part + __shfl_xor(l_part, 32);
@@ -543,22 +477,55 @@ __global__ __launch_bounds__(256, 2) void fused128_kernel(
 #pragma unroll
     for (int i = 0; i < 4; ++i) ol[i] = zero16();
     float inv_den = 0.0f;
+    float hscale = 1.0f;
     if (LIN) {
         wg_barrier();  // every wave is done with the tile stages
-        // H^T = -G^T as fp16, [128 d rows][256 B], chunk c' of row e at c' ^ (e & 15)
+        // H_i^T (fp32 row of the product: entry e * 128 + c) times hscale, a
+        // power of two that puts its largest magnitude in [2^14, 2^15), as
+        // fp16 in [128 d rows][256 B], chunk c' of row e at c' ^ (e & 15);
+        // Z_i in fp32
         char* sH = s_lds;
         float* sZ = reinterpret_cast<float*>(s_lds + 32768);
-        const int c = 32 * w + l32;
+        float* sM = sZ + 128;
+        const float* hrow = HZ + ((size_t)bh * Tq + qb) * kHzCols;
+        const int he = t >> 1, hc0 = 64 * (t & 1);  // row e, channels hc0 .. hc0 + 63
+        const float* hp = hrow + he * 128 + hc0;
+        // two passes over the thread's 64 entries (the second from the cache):
+        // the largest magnitude, then the scaled fp16 values
+        float hmx = 0.0f;
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
+        for (int i = 0; i < 16; ++i) {
+            const float4 v = *reinterpret_cast<const float4*>(hp + 4 * i);
+            hmx = fmaxf(hmx, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
+        }
+        if (t < 128) sZ[t] = hrow[128 * 128 + t];
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int e = 32 * mt + 8 * (i >> 2) + 4 * hl + (i & 3);
-                *reinterpret_cast<_Float16*>(sH + e * 256 + (((c >> 3) ^ (e & 15)) << 4) +
-                                             ((c & 7) << 1)) = (_Float16)(-g[mt][i]);
-            }
-        const float zs = zacc + __shfl_xor(zacc, 32);
-        if (hl == 0) sZ[c] = -zs;
+        for (int off = 32; off > 0; off >>= 1) hmx = fmaxf(hmx, __shfl_xor(hmx, off));
+        if (lane == 0) sM[w] = hmx;
+        wait_lgkm0();
+        wg_barrier();
+        const float hmax = fmaxf(fmaxf(sM[0], sM[1]), fmaxf(sM[2], sM[3]));
+        if (hmax > 0.0f) {
+            int ex;
+            (void)frexpf(hmax, &ex);  // hmax = f 2^ex, f in [0.5, 1)
+            hscale = ldexpf(1.0f, 15 - ex);
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const float4 a = *reinterpret_cast<const float4*>(hp + 8 * i);
+            const float4 b = *reinterpret_cast<const float4*>(hp + 8 * i + 4);
+            f16x8 hh;
+            hh[0] = (_Float16)(a.x * hscale);
+            hh[1] = (_Float16)(a.y * hscale);
+            hh[2] = (_Float16)(a.z * hscale);
+            hh[3] = (_Float16)(a.w * hscale);
+            hh[4] = (_Float16)(b.x * hscale);
+            hh[5] = (_Float16)(b.y * hscale);
+            hh[6] = (_Float16)(b.z * hscale);
+            hh[7] = (_Float16)(b.w * hscale);
+            const int cc = (hc0 >> 3) + i;
+            *reinterpret_cast<f16x8*>(sH + he * 256 + ((cc ^ (he & 15)) << 4)) = hh;
+        }
         wait_lgkm0();
         wg_barrier();
         // phi(Q)^T operand from the raw bf16 Q (registers on the bf16 path)
@@ -608,7 +575,7 @@ __global__ __launch_bounds__(256, 2) void fused128_kernel(
             }
         }
         den += __shfl_xor(den, 32);
-        inv_den = 1.0f / den;
+        inv_den = 1.0f / (den * hscale);
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) {
             const int erow = 32 * mt + l32;
@@ -715,10 +682,11 @@ hipError_t launch_wp_frag(const Dims& D, const float* Wp, const FwdWS& ws, hipSt
 
 hipError_t launch_fused128(const Dims& D, const void* Q, const void* K, const int32_t* idx,
                            const float* alpha, void* O, const FwdWS& ws, bool lowbit,
-                           hipStream_t s, const int32_t* negl) {
+                           hipStream_t s) {
     // one work-group per (head, query block), Tq padded to a multiple of 8
     const dim3 g((unsigned)(((D.Tq + 7) / 8) * 8 * D.BH), 1);
     const bool lin = D.k + (D.v1 ? D.kl : 0) < D.Tkv;
+    // the dense linear-branch product has filled ws.HZ (linear.hip)
     const uint16_t* q = (const uint16_t*)Q;
     const uint16_t* kk = (const uint16_t*)K;
     const uint8_t* qh = lowbit ? ws.qhat : nullptr;
@@ -748,10 +716,10 @@ hipError_t launch_fused128(const Dims& D, const void* Q, const void* K, const in
     const KernelKind kind = D.v1 ? K_FUSED_SLA1
                             : !lowbit ? K_FUSED_MFMA : i8 ? K_FUSED_I8 : K_FUSED_FP8;
     timing_before(s, kind);
-    kern<<<g, 256, 0, s>>>(q, kk, ws.vt, ws.pkt, ws.zb, idx, alpha, ws.htot, ws.ztot, qh, kh, sq,
-                           sk, lowv ? ws.vhat : nullptr, lowv ? ws.sv : nullptr, O, D.N, D.Tq,
-                           D.Tkv, D.k, D.H, D.st, D.alpha_qblock, D.out_bf16, negl,
-                           D.v1 ? D.kl : 0, D.v1 ? ws.wpf : nullptr, D.w_heads);
+    kern<<<g, 256, 0, s>>>(q, kk, ws.vt, idx, alpha, ws.HZ, qh, kh, sq, sk,
+                           lowv ? ws.vhat : nullptr, lowv ? ws.sv : nullptr, O, D.N, D.Tq, D.Tkv,
+                           D.k, D.H, D.st, D.alpha_qblock, D.out_bf16,
+                           D.v1 ? ws.wpf : nullptr, D.w_heads);
     timing_after(s, kind);
     return hipGetLastError();
 }

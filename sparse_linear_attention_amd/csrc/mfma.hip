@@ -48,11 +48,17 @@ __device__ inline int perm_pos(int u) {
 // ---------------------------------------------------------------------------
 constexpr int kTPitch = 64 * 2 + 16;  // bytes per row of a [d][64] fp16 tile in LDS
 
-template <int D>
+// HZ: instead of phi(K)^T tiles, z_j and chunk partials, write every block's
+// summaries for the linear-branch product (linear.hip): row j of hz holds
+// h_j^T (V channel e major, phi channel c minor: entry e * D + c) and then
+// z_j, in bf16; V^T tiles only if vt is not null.
+template <int D, bool HZ>
 __global__ __launch_bounds__(256) void summaries_mfma_kernel(
     const uint16_t* __restrict__ K, const uint16_t* __restrict__ V, uint16_t* __restrict__ vt,
     uint16_t* __restrict__ pkt, float* __restrict__ zb, float* __restrict__ hpart,
-    float* __restrict__ zpart, int N, int Tkv, int nch, int H, Strides st, int phi_sm) {
+    float* __restrict__ zpart, uint16_t* __restrict__ hz, int N, int Tkv, int nch, int H,
+    Strides st, int phi_sm) {
+    static_assert(!HZ || D == 128, "per-block summaries: d = 128");
     constexpr int NT = D / 32;
     constexpr int TPW = NT * NT / 4;  // h^T tiles per wave
     __shared__ __attribute__((aligned(16))) char sV[D * kTPitch];
@@ -142,21 +148,64 @@ __global__ __launch_bounds__(256) void summaries_mfma_kernel(
         }
         __syncthreads();
         // write the transposed tiles (contiguous D*64 fp16 each) and z_j
-        uint16_t* gv = vt + ((size_t)bh * Tkv + j) * D * 64;
-        for (int x = t; x < D * 8; x += 256) {
-            const int row = x >> 3, c16 = x & 7;
-            *reinterpret_cast<uint4*>(gv + row * 64 + c16 * 8) =
-                *reinterpret_cast<const uint4*>(sV + row * kTPitch + c16 * 16);
-            uint16_t* gp = pkt + ((size_t)bh * Tkv + j) * D * 64;
-            *reinterpret_cast<uint4*>(gp + row * 64 + c16 * 8) =
-                *reinterpret_cast<const uint4*>(sP + row * kTPitch + c16 * 16);
+        if (!HZ || vt) {
+            uint16_t* gv = vt + ((size_t)bh * Tkv + j) * D * 64;
+            for (int x = t; x < D * 8; x += 256) {
+                const int row = x >> 3, c16 = x & 7;
+                *reinterpret_cast<uint4*>(gv + row * 64 + c16 * 8) =
+                    *reinterpret_cast<const uint4*>(sV + row * kTPitch + c16 * 16);
+                if (!HZ) {
+                    uint16_t* gp = pkt + ((size_t)bh * Tkv + j) * D * 64;
+                    *reinterpret_cast<uint4*>(gp + row * 64 + c16 * 8) =
+                        *reinterpret_cast<const uint4*>(sP + row * kTPitch + c16 * 16);
+                }
+            }
         }
+        uint16_t* hzj = HZ ? hz + ((size_t)bh * Tkv + j) * kHzPitch : nullptr;
         if (t < D) {
             float z = 0.0f;
             const _Float16* rowp = reinterpret_cast<const _Float16*>(sP + t * kTPitch);
             for (int p = 0; p < 64; ++p) z += (float)rowp[p];
-            zb[((size_t)bh * Tkv + j) * D + t] = z;
-            zacc += z;
+            if (HZ) {
+                hzj[D * D + t] = __builtin_bit_cast(uint16_t, (__bf16)z);
+            } else {
+                zb[((size_t)bh * Tkv + j) * D + t] = z;
+                zacc += z;
+            }
+        }
+        if constexpr (HZ) {
+            // h_j (phi channels c x V channels e) = phi(K_j)^T V_j; lane holds
+            // column e and four consecutive rows c per group, stored as
+            // entry e * D + c of h_j^T (8 bytes per group)
+            f32x16 hj[TPW];
+#pragma unroll
+            for (int s = 0; s < TPW; ++s) hj[s] = zero16();
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                const f16x8 b = *reinterpret_cast<const f16x8*>(sV + (32 * nt_w + l32) * kTPitch +
+                                                                (16 * ks + 8 * hl) * 2);
+#pragma unroll
+                for (int s = 0; s < TPW; ++s) {
+                    const int mt = mt_w0 + s * MT_STEP;
+                    const f16x8 a = *reinterpret_cast<const f16x8*>(
+                        sP + (32 * mt + l32) * kTPitch + (16 * ks + 8 * hl) * 2);
+                    hj[s] = mfma_f16(a, b, hj[s]);
+                }
+            }
+            const int e = 32 * nt_w + l32;
+#pragma unroll
+            for (int s = 0; s < TPW; ++s) {
+                const int mt = mt_w0 + s * MT_STEP;
+#pragma unroll
+                for (int g4 = 0; g4 < 4; ++g4) {
+                    typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+                    bf16x4_t b4;
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) b4[c] = (__bf16)hj[s][4 * g4 + c];
+                    *reinterpret_cast<bf16x4_t*>(hzj + e * D + 32 * mt + 8 * g4 + 4 * hl) = b4;
+                }
+            }
+            continue;
         }
         // h^T (V channels x phi(K) channels) += V_j^T phi(K_j)
 #pragma unroll
@@ -172,6 +221,7 @@ __global__ __launch_bounds__(256) void summaries_mfma_kernel(
             }
         }
     }
+    if (HZ) return;
     // partial h[c][e]: c = phi(K) channel (C column), e = V channel (C row)
     float* hp = hpart + ((size_t)bh * nch + chunk) * D * D;
 #pragma unroll
@@ -455,17 +505,21 @@ hipError_t launch_summaries_mfma(const Dims& D, const void* K, const void* V,
     const int nch = summ_chunks(D);
     dim3 g(nch, (unsigned)D.BH);
     timing_before(s, K_SUMM_MFMA);
-    if (D.d == 128)
-        summaries_mfma_kernel<128><<<g, 256, 0, s>>>((const uint16_t*)K, (const uint16_t*)V,
-                                                     ws.vt, ws.pkt, ws.zb, ws.hpart, ws.zpart,
-                                                     D.N, D.Tkv, nch, D.H, D.st, D.phi_sm);
+    if (hz_path(D))
+        summaries_mfma_kernel<128, true><<<g, 256, 0, s>>>(
+            (const uint16_t*)K, (const uint16_t*)V, ws.vt, nullptr, nullptr, nullptr, nullptr,
+            ws.hz, D.N, D.Tkv, nch, D.H, D.st, D.phi_sm);
+    else if (D.d == 128)
+        summaries_mfma_kernel<128, false><<<g, 256, 0, s>>>(
+            (const uint16_t*)K, (const uint16_t*)V, ws.vt, ws.pkt, ws.zb, ws.hpart, ws.zpart,
+            nullptr, D.N, D.Tkv, nch, D.H, D.st, D.phi_sm);
     else
-        summaries_mfma_kernel<64><<<g, 256, 0, s>>>((const uint16_t*)K, (const uint16_t*)V,
-                                                    ws.vt, ws.pkt, ws.zb, ws.hpart, ws.zpart,
-                                                    D.N, D.Tkv, nch, D.H, D.st, D.phi_sm);
+        summaries_mfma_kernel<64, false><<<g, 256, 0, s>>>(
+            (const uint16_t*)K, (const uint16_t*)V, ws.vt, ws.pkt, ws.zb, ws.hpart, ws.zpart,
+            nullptr, D.N, D.Tkv, nch, D.H, D.st, D.phi_sm);
     timing_after(s, K_SUMM_MFMA);
     hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    if (e != hipSuccess || hz_path(D)) return e;
     return launch_summaries_reduce(D, ws, s);
 }
 

@@ -172,16 +172,26 @@ size_t layout_forward(const Dims& D, int op, char* base, FwdWS* ws) {
     memset(&w, 0, sizeof(w));
     const size_t bh = (size_t)D.BH, d = D.d;
     const int nch = summ_chunks(D);
-    if (D.dtype == SLA2_BF16) {
-        w.vt = carve<uint16_t>(base, off, 2 * bh * D.Tkv * d * 64);
-        w.pkt = carve<uint16_t>(base, off, 2 * bh * D.Tkv * d * 64);
-        w.zb = carve<float>(base, off, 4 * bh * D.Tkv * d);
+    const bool lowbit_op = op == SLA2_OP_FORWARD_FP8 || op == SLA2_OP_ATTENTION_FP8;
+    if (hz_path(D)) {
+        // V^T for P V (not needed when P V runs on the e4m3 codes of V), the
+        // per-block summaries, U and the linear-branch product
+        if (!(lowbit_op && D.lowbit_v)) w.vt = carve<uint16_t>(base, off, 2 * bh * D.Tkv * d * 64);
+        w.hz = carve<uint16_t>(base, off, 2 * bh * D.Tkv * (size_t)kHzPitch);
+        w.usel = carve<uint8_t>(base, off, bh * (size_t)(tkv_pad(D) / 64) * ubit_rows(D) * 8);
+        w.HZ = carve<float>(base, off, 4 * bh * D.Tq * (size_t)kHzCols);
+    } else {
+        if (D.dtype == SLA2_BF16) {
+            w.vt = carve<uint16_t>(base, off, 2 * bh * D.Tkv * d * 64);
+            w.pkt = carve<uint16_t>(base, off, 2 * bh * D.Tkv * d * 64);
+            w.zb = carve<float>(base, off, 4 * bh * D.Tkv * d);
+        }
+        w.hpart = carve<float>(base, off, 4 * bh * nch * d * d);
+        w.zpart = carve<float>(base, off, 4 * bh * nch * d);
+        w.htot = carve<float>(base, off, 4 * bh * d * d);
+        w.ztot = carve<float>(base, off, 4 * bh * d);
     }
-    w.hpart = carve<float>(base, off, 4 * bh * nch * d * d);
-    w.zpart = carve<float>(base, off, 4 * bh * nch * d);
-    w.htot = carve<float>(base, off, 4 * bh * d * d);
-    w.ztot = carve<float>(base, off, 4 * bh * d);
-    if (op == SLA2_OP_FORWARD_FP8 || op == SLA2_OP_ATTENTION_FP8) {
+    if (lowbit_op) {
         w.qhat = carve<uint8_t>(base, off, bh * (size_t)D.Tq * D.bq * d);
         w.khat = carve<uint8_t>(base, off, bh * (size_t)D.Tkv * 64 * d);
         w.sq = carve<float>(base, off, 4 * bh * D.Tq);
@@ -239,6 +249,7 @@ const char* kKindNames[K_NUM_KINDS] = {
     "quant_i8",     "fused_i8",    "fused_sla1",  "bwd_rows",
     "bwd_dh",       "bwd_keys",    "bwd_lin_rows", "bwd_lin_keys",
     "bwd_rows_mfma", "bwd_keys_mfma", "bwd_blk_summ", "bwd_sum_parts", "pool_quant",
+    "lin_gemm",
 };
 }  // namespace
 
@@ -339,6 +350,16 @@ static sla2_status forward_args(const sla2_problem* p, int op, const void* Q, co
     return SLA2_OK;
 }
 
+// hz_path: U from the selection, then the linear-branch product (skipped when
+// every block is selected: the fused kernel then has no linear branch)
+static hipError_t linear_product(const Dims& D, const int32_t* idx, const int32_t* negl,
+                                 int kl, const FwdWS& w, hipStream_t s) {
+    if (D.k + kl >= D.Tkv) return hipSuccess;
+    hipError_t e = launch_unsel(D, idx, negl, kl, w, s);
+    if (e == hipSuccess) e = launch_lin_gemm(D, w, s);
+    return e;
+}
+
 SLA2_API sla2_status sla2_forward(const sla2_problem* p, const void* Q, const void* K,
                                   const void* V, const int32_t* topk_idx, const float* alpha,
                                   void* O, void* ws, size_t ws_bytes, void* stream) {
@@ -353,6 +374,7 @@ SLA2_API sla2_status sla2_forward(const sla2_problem* p, const void* Q, const vo
         e = launch_forward_valu(D, Q, K, V, topk_idx, alpha, O, w, s);
     } else {
         e = launch_summaries_mfma(D, K, V, w, s);
+        if (e == hipSuccess && hz_path(D)) e = linear_product(D, topk_idx, nullptr, 0, w, s);
         if (e == hipSuccess) e = launch_fused_mfma(D, Q, K, topk_idx, alpha, O, w, s);
     }
     return e == hipSuccess ? SLA2_OK : SLA2_EHIP;
@@ -431,7 +453,9 @@ SLA2_API sla2_status sla2_attention(const sla2_problem* p, const void* Q, const 
     e = launch_summaries_mfma(D, K, V, fw, sd->s);
     if (e == hipSuccess) e = hipEventRecord(sd->join, sd->s);
     if (e == hipSuccess) e = launch_route(D, Q, K, Wq, Wk, topk_idx, nullptr, rw, s);
+    if (e == hipSuccess && hz_path(D) && D.k < D.Tkv) e = launch_unsel(D, topk_idx, nullptr, 0, fw, s);
     if (e == hipSuccess) e = hipStreamWaitEvent(s, sd->join, 0);
+    if (e == hipSuccess && hz_path(D) && D.k < D.Tkv) e = launch_lin_gemm(D, fw, s);
     if (e == hipSuccess) e = launch_fused_mfma(D, Q, K, topk_idx, alpha, O, fw, s);
     return e == hipSuccess ? SLA2_OK : SLA2_EHIP;
 }
@@ -469,7 +493,9 @@ SLA2_API sla2_status sla2_attention_fp8(const sla2_problem* p, const void* Q, co
     if (e == hipSuccess) e = launch_quantize_k(D, K, V, fw, sd->s);
     if (e == hipSuccess) e = hipEventRecord(sd->join, sd->s);
     if (e == hipSuccess) e = launch_route(D, Q, K, Wq, Wk, topk_idx, nullptr, rw, s, true);
+    if (e == hipSuccess && D.k < D.Tkv) e = launch_unsel(D, topk_idx, nullptr, 0, fw, s);
     if (e == hipSuccess) e = hipStreamWaitEvent(s, sd->join, 0);
+    if (e == hipSuccess && D.k < D.Tkv) e = launch_lin_gemm(D, fw, s);
     if (e == hipSuccess) e = launch_fused128(D, Q, K, topk_idx, alpha, O, fw, true, s);
     return e == hipSuccess ? SLA2_OK : SLA2_EHIP;
 }
@@ -486,6 +512,7 @@ SLA2_API sla2_status sla2_forward_fp8(const sla2_problem* p, const void* Q, cons
     hipStream_t s = (hipStream_t)stream;
     hipError_t e = launch_quantize_fp8(D, Q, K, V, w, s);
     if (e == hipSuccess) e = launch_summaries_mfma(D, K, V, w, s);
+    if (e == hipSuccess) e = linear_product(D, topk_idx, nullptr, 0, w, s);
     if (e == hipSuccess) e = launch_fused128(D, Q, K, topk_idx, alpha, O, w, true, s);
     return e == hipSuccess ? SLA2_OK : SLA2_EHIP;
 }
@@ -582,7 +609,8 @@ SLA2_API sla2_status sla1_forward(const sla2_problem* p, const void* Q, const vo
     hipStream_t s = (hipStream_t)stream;
     hipError_t e = launch_summaries_mfma(D, K, V, w, s);
     if (e == hipSuccess) e = launch_wp_frag(D, Wp, w, s);
-    if (e == hipSuccess) e = launch_fused128(D, Q, K, crit_idx, nullptr, O, w, false, s, negl_idx);
+    if (e == hipSuccess) e = linear_product(D, crit_idx, negl_idx, D.kl, w, s);
+    if (e == hipSuccess) e = launch_fused128(D, Q, K, crit_idx, nullptr, O, w, false, s);
     return e == hipSuccess ? SLA2_OK : SLA2_EHIP;
 }
 

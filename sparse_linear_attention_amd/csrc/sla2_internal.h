@@ -38,6 +38,7 @@ enum KernelKind {
     K_BWD_BLK_SUMM,
     K_BWD_SUM_PARTS,
     K_POOL_QUANT,
+    K_LIN_GEMM,
     K_NUM_KINDS
 };
 
@@ -100,6 +101,21 @@ inline int summ_chunks(const Dims& D) {
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
+// The d = 128, b_q = 128 bf16 path evaluates the linear branch as one dense
+// matrix-core product per head: H_i, Z_i = sum over KV blocks j of
+// U[i][j] (h_j, z_j), U the 0/1 indicator of the blocks query block i leaves
+// to the linear branch (linear.hip).  Rows of the block summaries and of the
+// products hold the d*d entries of h^T (V channel major) and then the d of z.
+constexpr int kHzCols = 128 * 128 + 128;  // entries of a row
+constexpr int kHzPitch = 65 * 256;        // bf16 elements per summaries row
+constexpr int kGemmM = 320;               // query blocks per product tile
+inline bool hz_path(const Dims& D) { return D.dtype == SLA2_BF16 && D.d == 128 && D.bq == 128; }
+// KV blocks of U: Tkv rounded up to a multiple of 64 (one k-step of the product)
+inline int tkv_pad(const Dims& D) { return (D.Tkv + 63) & ~63; }
+// rows of U per head and k-step: whole product tiles plus a 64-row tail (the
+// last tile's U loads run past its 320 rows)
+inline int ubit_rows(const Dims& D) { return (D.Tq + kGemmM - 1) / kGemmM * kGemmM + 64; }
+
 // ---------------------------------------------------------------------------
 // workspace layout.  Every region starts 256-byte aligned.
 // ---------------------------------------------------------------------------
@@ -136,6 +152,10 @@ struct FwdWS {
     float* sv;       // [BH][d]
     // SLA (v1): W_p as fp16 A-operand fragments of the projection product
     uint16_t* wpf;   // [w_heads][4 m-tiles][8 k-steps][64 lanes][8]
+    // d = 128, b_q = 128 bf16 path (hz_path): the linear branch as a product
+    uint16_t* hz;    // [BH][Tkv][kHzPitch] bf16: h_j^T (e * 128 + c), then z_j
+    uint8_t* usel;   // [BH][tkv_pad / 64][ubit_rows][8] bits: block j left to the linear branch
+    float* HZ;       // [BH][Tq][kHzCols] fp32: H_i^T (e * 128 + c), then Z_i
 };
 
 // backward (SLA2_OP_BACKWARD: the forward's summary buffers, then these)
@@ -276,11 +296,17 @@ hipError_t launch_quantize_k(const Dims& D, const void* K, const void* V, const 
 // V codes in rows [BH][Tkv*64][d] (inspection; s_V into ws.sv)
 hipError_t launch_quantize_v_rows(const Dims& D, const void* V, uint8_t* vhat_rows,
                                   const FwdWS& ws, hipStream_t s);
-// d = 128, b_q = 128 fused kernel (bf16, or the low-bit Q K^T with lowbit)
-// (D.v1: the SLA (v1) forward, negl = the negligible blocks, ws.wpf filled)
+// d = 128, b_q = 128 fused kernel (bf16, or the low-bit Q K^T with lowbit);
+// reads ws.HZ (launch_lin_gemm) when some block is left to the linear branch
+// (D.v1: the SLA (v1) forward, ws.wpf filled)
 hipError_t launch_fused128(const Dims& D, const void* Q, const void* K, const int32_t* idx,
                            const float* alpha, void* O, const FwdWS& ws, bool lowbit,
-                           hipStream_t s, const int32_t* negl = nullptr);
+                           hipStream_t s);
+// hz_path: U (ws.usel) from the selected blocks idx [BH][Tq][D.k] and, for
+// SLA v1, the negligible ones negl [BH][Tq][kl]; then ws.HZ = U * ws.hz
+hipError_t launch_unsel(const Dims& D, const int32_t* idx, const int32_t* negl, int kl,
+                        const FwdWS& ws, hipStream_t s);
+hipError_t launch_lin_gemm(const Dims& D, const FwdWS& ws, hipStream_t s);
 // W_p [w_heads][d][d] fp32 -> ws.wpf (d = 128)
 hipError_t launch_wp_frag(const Dims& D, const float* Wp, const FwdWS& ws, hipStream_t s);
 }  // namespace sla2
