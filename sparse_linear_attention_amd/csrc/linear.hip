@@ -18,13 +18,14 @@
 // rows of H_i^T and Z_i that the fused kernel's epilogue reads.
 //
 // Product tiles: 320 query blocks x 128 columns per work-group of 4 waves
-// (2 x 2: each wave 5 x 2 tiles of 32 x 32), 64 KV blocks per LDS stage (one
-// barrier per 40 products of a wave), both operands staged by direct-to-LDS
-// loads three stages ahead, four stages; 80 KB of LDS, so that two
-// work-groups share a compute unit and one's barrier gaps are filled by the
-// other's products.  LDS layouts:
-//   U bits   [320 rows][8 B]    bit b of byte g: KV block 8 g + b of the stage
-//   hz tile  [64 rows][256 B]   64-byte unit u of row r at u ^ (r & 3)
+// (2 x 2: each wave 5 x 2 tiles of 32 x 32, 160 rows x 64 columns), 64 KV
+// blocks per stage, two stages.  Every wave stages its own operands by
+// direct-to-LDS loads one stage ahead (the summaries of a column range are
+// loaded by the two waves that use them), so the loop has no barrier; 80 KB
+// of LDS lets two work-groups share a compute unit.  LDS layouts, per wave
+// and stage:
+//   U bits   [160 rows][8 B]    bit b of byte g: KV block 8 g + b of the stage
+//   hz tile  [64 rows][128 B]   32-byte unit u of row r at u ^ (r & 3)
 //   table    [256][16 B]        byte v -> its 8 bits as bf16 0.0 / 1.0
 // The U operand (row = query block, 8 consecutive KV blocks) is one 16-byte
 // read from the table at the row's byte for those blocks (U is mostly ones,
@@ -50,14 +51,14 @@ constexpr int kMaxTkvPad = 7680;
 constexpr int kGN = 128;                 // columns per tile
 constexpr int kGK = 64;                  // KV blocks per stage
 constexpr int kNT = kHzPitch / kGN;      // column tiles (130)
-constexpr int kUB = 3072;                // U bits per stage: 320 rows x 8 bytes, loaded
-                                         // as three 1 KB pieces (the last one partly unused)
-constexpr int kBB = kGK * kGN * 2;       // summaries stage bytes (16 KB)
-constexpr int kSt = kUB + kBB;
-constexpr int kNS = 4;                   // stages
+// per wave and stage: U bits of its 160 rows (8 bytes each), then the
+// summaries of its 64 columns (64 rows x 128 B)
+constexpr int kWU = 160 * 8;
+constexpr int kWB = kGK * 64 * 2;
+constexpr int kWSt = kWU + kWB;
 constexpr int kTbl = 4096;               // byte -> 8 bf16 0/1 values
 static_assert(kGemmM == 320, "tile shape");
-static_assert(kNS * kSt + kTbl <= 80 * 1024, "LDS budget: two work-groups per CU");
+static_assert(4 * 2 * kWSt + kTbl <= 80 * 1024, "LDS budget: two work-groups per CU");
 
 // One work-group per row of U: query block i of head bh (rows past T_q, up to
 // the padded row count, are all zero).  Bit b of byte g of the row is KV
@@ -124,7 +125,7 @@ __device__ inline void read_sub(const uint32_t (&u)[5], uint32_t b0, uint32_t b1
         : "=&v"(x.a[0]), "=&v"(x.a[1]), "=&v"(x.a[2]), "=&v"(x.a[3]), "=&v"(x.a[4]),
           "=&v"(x.b[0]), "=&v"(x.b[1]), "=&v"(x.b[2]), "=&v"(x.b[3])
         : "v"(u[0]), "v"(u[1]), "v"(u[2]), "v"(u[3]), "v"(u[4]), "v"(b0), "v"(b1),
-          "i"(4096 * S), "i"(4096 * S + 1024));
+          "i"(2048 * S), "i"(2048 * S + 512));
 }
 // The same reads without the wait: their results arrive later, and
 // wait_ops(x, .) must run before any use of x (it names the registers, so no
@@ -148,7 +149,7 @@ __device__ inline void read_sub_async(const uint32_t (&u)[5], uint32_t b0, uint3
           "+v"(p.a[1]), "+v"(p.a[2]), "+v"(p.a[3]), "+v"(p.a[4]), "+v"(p.b[0]), "+v"(p.b[1]),
           "+v"(p.b[2]), "+v"(p.b[3])
         : "v"(u[0]), "v"(u[1]), "v"(u[2]), "v"(u[3]), "v"(u[4]), "v"(b0), "v"(b1),
-          "i"(4096 * S), "i"(4096 * S + 1024));
+          "i"(2048 * S), "i"(2048 * S + 512));
 }
 // wait for the reads of x; the operands p of the products issued since pass
 // through as well, which keeps those products above the wait
@@ -160,19 +161,18 @@ __device__ inline void wait_ops(SubOps& x, SubOps& p) {
                    "+v"(p.b[1]), "+v"(p.b[2]), "+v"(p.b[3]));
 }
 
-// wait until at most `ahead` later stages (L loads each) are in flight
-template <int L>
-__device__ inline void wait_stages(int ahead) {
-    if (ahead >= 2) wait_vmcnt<2 * L>();
-    else if (ahead == 1) wait_vmcnt<L>();
-    else wait_vmcnt<0>();
+__device__ inline void load_lds4(rsrc_t r, uint32_t voff, uint32_t soff, char* dst) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, SLA2_LDS(dst), 4, voff, soff, 0, 0);
 }
 
+// Each wave stages its own operands (no barrier in the loop): waves of a
+// work-group and the two work-groups of a compute unit run unsynchronised,
+// so one wave's load and LDS waits are covered by the others' products.
 __global__ __launch_bounds__(256, 2) void lin_gemm_kernel(const uint8_t* __restrict__ U,
                                                          const uint16_t* __restrict__ hz,
                                                          float* __restrict__ HZ, int Tq, int Tkv,
                                                          int Tkvp, int nM, int rows) {
-    __shared__ __attribute__((aligned(1024))) char lds[kNS * kSt + kTbl];
+    __shared__ __attribute__((aligned(1024))) char lds[4 * 2 * kWSt + kTbl];
     const int t = threadIdx.x, lane = t & 63, l32 = lane & 31, hl = lane >> 5;
     const int w = __builtin_amdgcn_readfirstlane(t >> 6);
     const int wm = w >> 1, wn = w & 1;
@@ -181,60 +181,67 @@ __global__ __launch_bounds__(256, 2) void lin_gemm_kernel(const uint8_t* __restr
     g /= nM;
     const int ni = g % kNT;
     const long bh = g / kNT;
-    const int m0 = mi * kGemmM, n0 = ni * kGN;
+    const int m0 = mi * kGemmM + 160 * wm;  // this wave's first row
+    const int n0 = ni * kGN + 64 * wn;      // this wave's first column
     const int nk = Tkvp / kGK;
     const rsrc_t ru = head_rsrc(U + (size_t)bh * nk * rows * 8);
     const rsrc_t rh = head_rsrc(hz + (size_t)bh * Tkv * kHzPitch);
 
     // byte table: entry v holds the 8 bf16 values bit e of v (0 or 1)
-    char* const tbl = lds + kNS * kSt;
-    if (t < 256) {
+    char* const tbl = lds + 4 * 2 * kWSt;
+    {
         uint32_t d[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e)
             d[e] = (((t >> (2 * e)) & 1) ? 0x3F80u : 0u) | (((t >> (2 * e + 1)) & 1) ? 0x3F800000u : 0u);
         *reinterpret_cast<uint4*>(tbl + 16 * t) = make_uint4(d[0], d[1], d[2], d[3]);
     }
-    wait_lgkm0();  // visible to every wave after the first barrier of the loop
+    wait_lgkm0();
+    __syncthreads();  // the table, once; no barrier after this
 
-    // U bits of a stage: rows m0 .. m0 + 319 of k-step kk (2560 contiguous
-    // bytes), loaded as pieces 0..2 of 1 KB by waves 0..2 (the tail of piece
-    // 2 holds the next rows or the padding, unused)
-    const uint32_t uoff = (uint32_t)(m0 * 8 + 16 * lane);
-    // summaries pieces q = w + 4 i (16 of 4 rows x 256 B): this lane fills
-    // position lane & 15 of row 4 q + lane / 16; rows past T_kv repeat row
-    // T_kv - 1, whose U bits are 0
-    int brow[4], bcol[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        brow[i] = 4 * (w + 4 * i) + (lane >> 4);
-        const int u = ((lane & 15) >> 2) ^ (brow[i] & 3);
-        bcol[i] = n0 + 32 * u + 8 * (lane & 3);
-    }
+    // U bits of a stage: this wave's rows m0 .. m0 + 159 of k-step kk, 1280
+    // contiguous bytes (1 KB piece + 256 B); past T_q they are the padding
+    // rows (zero), whose products are not stored
+    const uint32_t uoff = (uint32_t)(m0 * 8 + 16 * lane), uoff2 = (uint32_t)(m0 * 8 + 1024 + 4 * lane);
+    // summaries: 8 pieces of 8 rows x 128 B; lane fills 16-byte position
+    // lane & 7 of row 8 q + lane / 8, holding 32-byte unit ((lane & 7) / 2) ^
+    // (row & 3) of the wave's 64 columns
+    const int brow = lane >> 3;  // + 8 q (row & 3 does not depend on q)
+    const int bcol = n0 + 16 * (((lane & 7) >> 1) ^ (brow & 3)) + 8 * (lane & 1);
+    const uint32_t boff = (uint32_t)(brow * kHzPitch + bcol) * 2;
+    char* const wbase = lds + w * 2 * kWSt;
     auto issue = [&](int stage, int kk) {
-        char* A = lds + stage * kSt;
-        char* B = A + kUB;
-        if (w < 3) load_lds16(ru, uoff + 1024 * w, (uint32_t)kk * rows * 8, A + 1024 * w);
+        char* A = wbase + stage * kWSt;
+        char* B = A + kWU;
+        const uint32_t us = (uint32_t)kk * rows * 8;
+        load_lds16(ru, uoff, us, A);
+        load_lds4(ru, uoff2, us, A + 1024);
         const int j0 = kk * kGK;
+        if (j0 + kGK <= Tkv) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int jr = min(j0 + brow[i], Tkv - 1);
-            load_lds16(rh, (uint32_t)(jr * kHzPitch + bcol[i]) * 2, 0, B + (w + 4 * i) * 1024);
+            for (int q = 0; q < 8; ++q)
+                load_lds16(rh, boff, (uint32_t)(j0 + 8 * q) * kHzPitch * 2, B + 1024 * q);
+        } else {  // rows past T_kv repeat row T_kv - 1, whose U bits are 0
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                const int jr = min(j0 + 8 * q + brow, Tkv - 1);
+                load_lds16(rh, (uint32_t)(jr * kHzPitch + bcol) * 2, 0, B + 1024 * q);
+            }
         }
     };
 
-    // per-lane LDS addresses (stage 0): this lane's U bits (row 160 wm + 32 m
-    // + l32, 8 bytes) and the summaries operand of column tile nt
+    // per-lane LDS addresses (stage 0): this lane's U bits (row 32 m + l32 of
+    // the wave's, 8 bytes) and the summaries operand of column tile nt
     // (transposed reads; sub-step and half rows as immediates)
-    const uint32_t base = lds_addr(lds), tbase = lds_addr(tbl);
-    const uint32_t ubit = base + (uint32_t)((160 * wm + l32) * 8);
+    const uint32_t tbase = lds_addr(tbl);
+    const uint32_t ubit = lds_addr(wbase) + (uint32_t)(l32 * 8);
     const int r16 = lane & 15, G = lane >> 4;
     uint32_t aB[2];
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt)
-        aB[nt] = base + kUB +
-                 (uint32_t)((8 * (G >> 1) + (r16 >> 2)) * 256 + (((2 * wn + nt) ^ (r16 >> 2)) << 6) +
-                            32 * (G & 1) + 8 * (r16 & 3));
+        aB[nt] = lds_addr(wbase) + kWU +
+                 (uint32_t)((8 * (G >> 1) + (r16 >> 2)) * 128 +
+                            (((2 * nt + (G & 1)) ^ (r16 >> 2)) << 5) + 8 * (r16 & 3));
 
     f32x16 acc[5][2];
 #pragma unroll
@@ -254,18 +261,17 @@ __global__ __launch_bounds__(256, 2) void lin_gemm_kernel(const uint8_t* __restr
         }
     };
 
-#pragma unroll
-    for (int q = 0; q < kNS - 1; ++q)
-        if (q < nk) issue(q, q);
+    issue(0, 0);
     for (int kk = 0; kk < nk; ++kk) {
-        // stage kk has landed for this wave (waves 0-2 issue 5 loads per
-        // stage, the others 4) ...
-        const int ahead = min(kNS - 2, nk - 1 - kk);
-        if (w < 3) wait_stages<5>(ahead);
-        else wait_stages<4>(ahead);
-        wg_barrier();  // ... and for every wave; all are done with stage kk - 1
-        if (kk + kNS - 1 < nk) issue((kk + kNS - 1) % kNS, kk + kNS - 1);
-        const uint32_t so = (uint32_t)((kk % kNS) * kSt);
+        // the next stage goes into the buffer this wave finished reading in
+        // the previous iteration; then wait for stage kk (10 loads per stage)
+        if (kk + 1 < nk) {
+            issue((kk + 1) & 1, kk + 1);
+            wait_vmcnt<10>();
+        } else {
+            wait_vmcnt<0>();
+        }
+        const uint32_t so = (uint32_t)((kk & 1) * kWSt);
         const uint32_t b0 = aB[0] + so, b1 = aB[1] + so;
         // the five rows' U bits of this stage; byte 2 s + hl of row m is the
         // U fragment of sub-step s, read from the table
@@ -310,11 +316,11 @@ __global__ __launch_bounds__(256, 2) void lin_gemm_kernel(const uint8_t* __restr
     for (int m = 0; m < 5; ++m)
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt) {
-            const int col = n0 + 64 * wn + 32 * nt + l32;
+            const int col = n0 + 32 * nt + l32;
             if (col >= kHzCols) continue;
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const int qb = m0 + 160 * wm + 32 * m + 8 * (r >> 2) + 4 * hl + (r & 3);
+                const int qb = m0 + 32 * m + 8 * (r >> 2) + 4 * hl + (r & 3);
                 if (qb < Tq) out[(size_t)qb * kHzCols + col] = acc[m][nt][r];
             }
         }
