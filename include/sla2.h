@@ -107,6 +107,17 @@ typedef enum {
     SLA2_OP_ATTENTION_FP8 = 7  /* sla2_attention_fp8         */
 } sla2_op;
 
+/* stage-timing switches (problem.flags): SKIP_LINEAR leaves the linear
+ * branch out (O = alpha O_s: no block summaries h_j / z_j, no U product, no
+ * epilogue product), SKIP_SPARSE the sparse branch (O = (1 - alpha) O_l: no
+ * Q K^T, softmax or P V; the selection still decides which blocks the
+ * linear branch covers).  Both at once give O = 0.  Taken by sla2_forward,
+ * sla2_attention, sla2_forward_fp8 and sla2_attention_fp8 on the bf16,
+ * d = 128, bq = 128 path (SLA2_EUNSUPPORTED elsewhere; the router and
+ * sla2_workspace_bytes ignore them).  With SKIP_LINEAR, alpha = 1 and
+ * k = T_kv the call is dense softmax attention, the bench's baseline. */
+typedef enum { SLA2_FLAG_SKIP_LINEAR = 1, SLA2_FLAG_SKIP_SPARSE = 2 } sla2_flags;
+
 typedef struct {
     int32_t B, H, N, d;  /* batch, heads, tokens, head dim (64 or 128)       */
     int32_t bq, bkv;     /* query / KV block sizes: bq in {64,128}, bkv = 64   */
@@ -118,6 +129,7 @@ typedef struct {
     int32_t alpha_mode;  /* sla2_alpha_mode                                     */
     int32_t out_dtype;   /* sla2_dtype of O (SLA2_F32 or SLA2_BF16)             */
     int32_t lowbit;      /* sla2_lowbit (sla2_forward_fp8 only)                 */
+    uint32_t flags;      /* 0, or sla2_flags bits (stage timing only)           */
 } sla2_problem;
 
 /* T_q = ceil(N / bq) and T_kv = ceil(N / bkv).  The last block of each kind
@@ -188,10 +200,12 @@ sla2_status sla2_forward(const sla2_problem* p, const void* Q, const void* K,
  *   kernels, bit-identical O and topk_idx).  On the bf16 bq = 128 path the
  *   block summaries (which read only K and V) run on a helper stream,
  *   concurrently with the router (Q and K), joined before the fused kernel
- *   with events; other paths run in sequence.  The helper stream and its two
+ *   with events; other paths run in sequence.  The helper stream and its
  *   events are created once per device on first use (default priority) and
- *   kept until the process ends; calls on one device from several host
- *   threads at once are not supported.
+ *   kept until the process ends.  Calls from several host threads (on
+ *   different streams, with different workspaces) are safe: a lock keeps
+ *   each call's enqueue sequence on the shared helper stream whole, and the
+ *   helper-stream work of concurrent calls runs one after the other.
  * In : Q, K, V, Wq, Wk, alpha as sla2_route / sla2_forward.
  * Out: topk_idx [B,H,T_q,k] (NULL allowed when k = 0); O as sla2_forward.
  * ws : sla2_workspace_bytes(p, SLA2_OP_ATTENTION) bytes.
@@ -278,6 +292,19 @@ sla2_status sla2_quantize_fp8(const sla2_problem* p, const void* Q, const void* 
  */
 sla2_status sla2_quantize_v_fp8(const sla2_problem* p, const void* V, uint8_t* Vhat,
                                 float* sV, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * sla2_fp8_dot_tiles -- diagnostic of the fp8 matrix cores the low-bit
+ * logits run on: C[t] = A[t] B[t]^T for t < ntiles, A[t] and B[t] 32 x 128
+ * OCP e4m3 codes (row-major, device), C[t] 32 x 32 fp32 (row-major), on the
+ * same instruction and operand layout as sla2_forward_fp8's Q K^T (two
+ * chained 32x32x64 products, unit scales).  The hardware does not sum the
+ * 128 products exactly; the parity tests measure that error with this call.
+ * Errors: SLA2_EINVAL for a null or misaligned pointer or ntiles outside
+ * [1, 2^20].
+ */
+sla2_status sla2_fp8_dot_tiles(const uint8_t* A, const uint8_t* B, float* C, int32_t ntiles,
+                               void* stream);
 
 /*
  * Kernel timing (diagnostics, host-side state).  sla2_timing_start(n) makes

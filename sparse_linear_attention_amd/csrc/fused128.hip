@@ -673,7 +673,37 @@ __global__ __launch_bounds__(256) void wp_frag_kernel(const float* __restrict__ 
     }
 }
 
+// Diagnostic of the e4m3 matrix-core dot product of the low-bit logits:
+// C[t] = A[t] B[t]^T for tiles of 32 rows x 128 codes, as two chained
+// 32x32x64 scaled products (scales 1.0) with the operand layout of the Q K^T
+// above (lane l: row l % 32, codes 64 ks + 32 (l / 32) .. + 31).  One wave
+// per tile; C row-major [32][32] fp32.
+__global__ __launch_bounds__(64) void fp8_dot_kernel(const uint8_t* __restrict__ A,
+                                                     const uint8_t* __restrict__ B,
+                                                     float* __restrict__ C) {
+    const size_t tile = blockIdx.x;
+    const int l = threadIdx.x, row = l & 31, half = l >> 5;
+    const uint8_t* a = A + (tile * 32 + row) * 128 + 32 * half;
+    const uint8_t* b = B + (tile * 32 + row) * 128 + 32 * half;
+    f32x16 acc = zero16();
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+        const i32x8 av = *reinterpret_cast<const i32x8*>(a + 64 * ks);
+        const i32x8 bv = *reinterpret_cast<const i32x8*>(b + 64 * ks);
+        acc = mfma_fp8(av, bv, acc);
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+        C[tile * 1024 + (size_t)(8 * (r >> 2) + 4 * half + (r & 3)) * 32 + row] = acc[r];
+}
+
 }  // namespace
+
+hipError_t launch_fp8_dot(const uint8_t* A, const uint8_t* B, float* C, int ntiles,
+                          hipStream_t s) {
+    fp8_dot_kernel<<<dim3((unsigned)ntiles), 64, 0, s>>>(A, B, C);
+    return hipGetLastError();
+}
 
 hipError_t launch_wp_frag(const Dims& D, const float* Wp, const FwdWS& ws, hipStream_t s) {
     wp_frag_kernel<<<dim3((unsigned)D.w_heads), 256, 0, s>>>(Wp, ws.wpf);
@@ -685,7 +715,8 @@ hipError_t launch_fused128(const Dims& D, const void* Q, const void* K, const in
                            hipStream_t s) {
     // one work-group per (head, query block), Tq padded to a multiple of 8
     const dim3 g((unsigned)(((D.Tq + 7) / 8) * 8 * D.BH), 1);
-    const bool lin = D.k + (D.v1 ? D.kl : 0) < D.Tkv;
+    const bool lin = D.k + (D.v1 ? D.kl : 0) < D.Tkv && !D.skip_lin;
+    const int kloop = D.skip_sparse ? 0 : D.k;  // selected tiles the sparse branch visits
     // the dense linear-branch product has filled ws.HZ (linear.hip)
     const uint16_t* q = (const uint16_t*)Q;
     const uint16_t* kk = (const uint16_t*)K;
@@ -718,7 +749,7 @@ hipError_t launch_fused128(const Dims& D, const void* Q, const void* K, const in
     timing_before(s, kind);
     kern<<<g, 256, 0, s>>>(q, kk, ws.vt, idx, alpha, ws.HZ, qh, kh, sq, sk,
                            lowv ? ws.vhat : nullptr, lowv ? ws.sv : nullptr, O, D.N, D.Tq, D.Tkv,
-                           D.k, D.H, D.st, D.alpha_qblock, D.out_bf16,
+                           kloop, D.H, D.st, D.alpha_qblock, D.out_bf16,
                            D.v1 ? ws.wpf : nullptr, D.w_heads);
     timing_after(s, kind);
     return hipGetLastError();

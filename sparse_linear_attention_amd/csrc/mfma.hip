@@ -161,6 +161,7 @@ __global__ __launch_bounds__(256) void summaries_mfma_kernel(
                 }
             }
         }
+        if (HZ && !hz) continue;  // no linear branch: V^T only
         uint16_t* hzj = HZ ? hz + ((size_t)bh * Tkv + j) * kHzPitch : nullptr;
         if (t < D) {
             float z = 0.0f;
@@ -505,10 +506,12 @@ hipError_t launch_summaries_mfma(const Dims& D, const void* K, const void* V,
     const int nch = summ_chunks(D);
     dim3 g(nch, (unsigned)D.BH);
     timing_before(s, K_SUMM_MFMA);
-    if (hz_path(D))
+    if (hz_path(D))  // (stage switches: no V^T without the sparse branch, no h_j, z_j
+                     // without the linear one)
         summaries_mfma_kernel<128, true><<<g, 256, 0, s>>>(
-            (const uint16_t*)K, (const uint16_t*)V, ws.vt, nullptr, nullptr, nullptr, nullptr,
-            ws.hz, D.N, D.Tkv, nch, D.H, D.st, D.phi_sm);
+            (const uint16_t*)K, (const uint16_t*)V, D.skip_sparse ? nullptr : ws.vt, nullptr,
+            nullptr, nullptr, nullptr, D.skip_lin ? nullptr : ws.hz, D.N, D.Tkv, nch, D.H, D.st,
+            D.phi_sm);
     else if (D.d == 128)
         summaries_mfma_kernel<128, false><<<g, 256, 0, s>>>(
             (const uint16_t*)K, (const uint16_t*)V, ws.vt, ws.pkt, ws.zb, ws.hpart, ws.zpart,

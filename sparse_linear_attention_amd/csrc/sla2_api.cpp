@@ -39,6 +39,7 @@ static sla2_status make_dims(const sla2_problem* p, int op, Dims* D) {
         return SLA2_EINVAL;
     if (p->out_dtype != SLA2_F32 && p->out_dtype != SLA2_BF16) return SLA2_EINVAL;
     if (p->lowbit < SLA2_LOWBIT_QK || p->lowbit > SLA2_LOWBIT_I8QKV) return SLA2_EINVAL;
+    if (p->flags & ~(uint32_t)(SLA2_FLAG_SKIP_LINEAR | SLA2_FLAG_SKIP_SPARSE)) return SLA2_EINVAL;
     if (op < SLA2_OP_ROUTE || op > SLA2_OP_ATTENTION_FP8) return SLA2_EINVAL;
     if (p->d != 64 && p->d != 128) return SLA2_EUNSUPPORTED;
     if (p->bq != 64 && p->bq != 128) return SLA2_EUNSUPPORTED;
@@ -85,6 +86,14 @@ static sla2_status make_dims(const sla2_problem* p, int op, Dims* D) {
     D->phi_sm = p->phi == SLA2_PHI_SOFTMAX;
     D->v1 = op == SLA2_OP_SLA1_FORWARD;
     D->kl = 0;
+    D->skip_lin = (p->flags & SLA2_FLAG_SKIP_LINEAR) != 0;
+    D->skip_sparse = (p->flags & SLA2_FLAG_SKIP_SPARSE) != 0;
+    // stage switches: forward-type calls on the d = 128, bq = 128 bf16 path only
+    if (p->flags && !routing && op != SLA2_OP_FORWARD && op != SLA2_OP_FORWARD_FP8 &&
+        op != SLA2_OP_ATTENTION && op != SLA2_OP_ATTENTION_FP8)
+        return SLA2_EUNSUPPORTED;
+    if (p->flags && !routing && !fast) return SLA2_EUNSUPPORTED;
+    if (routing) D->skip_lin = D->skip_sparse = 0;
     // the fused kernels address a head's rows with 32-bit byte offsets
     if ((double)p->N * D->st.t * 4.0 >= 2147483648.0) return SLA2_EUNSUPPORTED;
     return SLA2_OK;
@@ -354,7 +363,7 @@ static sla2_status forward_args(const sla2_problem* p, int op, const void* Q, co
 // every block is selected: the fused kernel then has no linear branch)
 static hipError_t linear_product(const Dims& D, const int32_t* idx, const int32_t* negl,
                                  int kl, const FwdWS& w, hipStream_t s) {
-    if (D.k + kl >= D.Tkv) return hipSuccess;
+    if (D.k + kl >= D.Tkv || D.skip_lin) return hipSuccess;
     hipError_t e = launch_unsel(D, idx, negl, kl, w, s);
     if (e == hipSuccess) e = launch_lin_gemm(D, w, s);
     return e;
@@ -392,12 +401,15 @@ constexpr int kMaxDevices = 64;
 Side g_side[kMaxDevices];
 std::mutex g_side_mu;
 
+// The caller holds g_side_mu from here until its last event record or wait
+// is enqueued: the fork / join events are shared by every call on the device,
+// so the sequence record(fork) .. wait(join) of one call must not interleave
+// with another's.
 hipError_t side_stream(Side** out) {
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return e;
     if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
-    std::lock_guard<std::mutex> lk(g_side_mu);
     Side& sd = g_side[dev];
     if (!sd.s) {
         // default priority (no priority argument), independent of the null stream.
@@ -446,6 +458,7 @@ SLA2_API sla2_status sla2_attention(const sla2_problem* p, const void* Q, const 
         return e == hipSuccess ? SLA2_OK : SLA2_EHIP;
     }
     Side* sd = nullptr;
+    std::lock_guard<std::mutex> lk(g_side_mu);  // see side_stream
     if ((e = side_stream(&sd)) != hipSuccess) return SLA2_EHIP;
     // summaries (K, V) on the helper stream, the router (Q, K) on the caller's
     if ((e = hipEventRecord(sd->fork, s)) != hipSuccess) return SLA2_EHIP;
@@ -453,9 +466,10 @@ SLA2_API sla2_status sla2_attention(const sla2_problem* p, const void* Q, const 
     e = launch_summaries_mfma(D, K, V, fw, sd->s);
     if (e == hipSuccess) e = hipEventRecord(sd->join, sd->s);
     if (e == hipSuccess) e = launch_route(D, Q, K, Wq, Wk, topk_idx, nullptr, rw, s);
-    if (e == hipSuccess && hz_path(D) && D.k < D.Tkv) e = launch_unsel(D, topk_idx, nullptr, 0, fw, s);
+    const bool lin = hz_path(D) && D.k < D.Tkv && !D.skip_lin;
+    if (e == hipSuccess && lin) e = launch_unsel(D, topk_idx, nullptr, 0, fw, s);
     if (e == hipSuccess) e = hipStreamWaitEvent(s, sd->join, 0);
-    if (e == hipSuccess && hz_path(D) && D.k < D.Tkv) e = launch_lin_gemm(D, fw, s);
+    if (e == hipSuccess && lin) e = launch_lin_gemm(D, fw, s);
     if (e == hipSuccess) e = launch_fused_mfma(D, Q, K, topk_idx, alpha, O, fw, s);
     return e == hipSuccess ? SLA2_OK : SLA2_EHIP;
 }
@@ -479,6 +493,7 @@ SLA2_API sla2_status sla2_attention_fp8(const sla2_problem* p, const void* Q, co
     hipStream_t s = (hipStream_t)stream;
     hipError_t e;
     Side* sd = nullptr;
+    std::lock_guard<std::mutex> lk(g_side_mu);  // see side_stream
     if ((e = side_stream(&sd)) != hipSuccess) return SLA2_EHIP;
     // caller's stream: the router, whose pooling pass also writes the query
     // codes and the K block sums; helper stream: the block summaries, then
@@ -493,9 +508,10 @@ SLA2_API sla2_status sla2_attention_fp8(const sla2_problem* p, const void* Q, co
     if (e == hipSuccess) e = launch_quantize_k(D, K, V, fw, sd->s);
     if (e == hipSuccess) e = hipEventRecord(sd->join, sd->s);
     if (e == hipSuccess) e = launch_route(D, Q, K, Wq, Wk, topk_idx, nullptr, rw, s, true);
-    if (e == hipSuccess && D.k < D.Tkv) e = launch_unsel(D, topk_idx, nullptr, 0, fw, s);
+    const bool lin = D.k < D.Tkv && !D.skip_lin;
+    if (e == hipSuccess && lin) e = launch_unsel(D, topk_idx, nullptr, 0, fw, s);
     if (e == hipSuccess) e = hipStreamWaitEvent(s, sd->join, 0);
-    if (e == hipSuccess && D.k < D.Tkv) e = launch_lin_gemm(D, fw, s);
+    if (e == hipSuccess && lin) e = launch_lin_gemm(D, fw, s);
     if (e == hipSuccess) e = launch_fused128(D, Q, K, topk_idx, alpha, O, fw, true, s);
     return e == hipSuccess ? SLA2_OK : SLA2_EHIP;
 }
@@ -680,6 +696,14 @@ SLA2_API sla2_status sla2_backward(const sla2_problem* p, const void* Q, const v
     layout_backward(D, (char*)ws, &w, &b);
     hipError_t e = launch_backward(D, Q, K, V, dO, topk_idx, alpha, dQ, dK, dV, dalpha, w, b,
                                    (hipStream_t)stream);
+    return e == hipSuccess ? SLA2_OK : SLA2_EHIP;
+}
+
+SLA2_API sla2_status sla2_fp8_dot_tiles(const uint8_t* A, const uint8_t* B, float* C,
+                                        int32_t ntiles, void* stream) {
+    if (!ok_ptr(A) || !ok_ptr(B) || !ok_ptr(C)) return SLA2_EINVAL;
+    if (ntiles <= 0 || ntiles > (1 << 20)) return SLA2_EINVAL;
+    hipError_t e = launch_fp8_dot(A, B, C, ntiles, (hipStream_t)stream);
     return e == hipSuccess ? SLA2_OK : SLA2_EHIP;
 }
 

@@ -67,6 +67,8 @@ struct Dims {
     int phi_sm;          // phi = softmax over the channels of a row (else elu + 1)
     int v1;              // SLA (v1) forward: ternary blocks, O = O_s + O_l W_p
     int kl;              // v1: negligible blocks per query block
+    int skip_lin;        // SLA2_FLAG_SKIP_LINEAR: no linear branch (O = alpha O_s)
+    int skip_sparse;     // SLA2_FLAG_SKIP_SPARSE: no sparse branch (O = (1 - alpha) O_l)
 };
 
 // Four consecutive outputs (element offset off, a multiple of 4) as fp32, or
@@ -307,6 +309,9 @@ hipError_t launch_fused128(const Dims& D, const void* Q, const void* K, const in
 hipError_t launch_unsel(const Dims& D, const int32_t* idx, const int32_t* negl, int kl,
                         const FwdWS& ws, hipStream_t s);
 hipError_t launch_lin_gemm(const Dims& D, const FwdWS& ws, hipStream_t s);
+// diagnostic: C[t] = A[t] B[t]^T, 32 x 128 e4m3 tiles, fp8 matrix cores
+hipError_t launch_fp8_dot(const uint8_t* A, const uint8_t* B, float* C, int ntiles,
+                          hipStream_t s);
 // W_p [w_heads][d][d] fp32 -> ws.wpf (d = 128)
 hipError_t launch_wp_frag(const Dims& D, const float* Wp, const FwdWS& ws, hipStream_t s);
 }  // namespace sla2

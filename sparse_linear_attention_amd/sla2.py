@@ -21,6 +21,7 @@ PHI_ELU1, PHI_SOFTMAX = 0, 1
 LAYOUT_BHND, LAYOUT_BNHD = 0, 1
 ALPHA_PER_HEAD, ALPHA_PER_QBLOCK = 0, 1
 LOWBIT_QK, LOWBIT_QKV, LOWBIT_I8QK, LOWBIT_I8QKV = 0, 1, 2, 3
+FLAG_SKIP_LINEAR, FLAG_SKIP_SPARSE = 1, 2
 
 
 class Problem(C.Structure):
@@ -28,7 +29,7 @@ class Problem(C.Structure):
                 ("bq", C.c_int32), ("bkv", C.c_int32), ("topk_frac", C.c_float),
                 ("w_heads", C.c_int32), ("phi", C.c_int32), ("dtype", C.c_int32),
                 ("layout", C.c_int32), ("alpha_mode", C.c_int32), ("out_dtype", C.c_int32),
-                ("lowbit", C.c_int32)]
+                ("lowbit", C.c_int32), ("flags", C.c_uint32)]
 
 
 class SLA2Error(RuntimeError):
@@ -77,6 +78,7 @@ def lib():
         L.sla2_backward.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, C.c_size_t, vp]
         L.sla1_route.argtypes = [P, vp, vp, C.c_float, vp, vp, vp, vp, C.c_size_t, vp]
         L.sla1_forward.argtypes = [P, vp, vp, vp, vp, vp, C.c_float, vp, vp, vp, C.c_size_t, vp]
+        L.sla2_fp8_dot_tiles.argtypes = [vp, vp, vp, C.c_int32, vp]
         _lib = L
     return _lib
 
@@ -86,7 +88,7 @@ EXPORTS = ("sla2_num_q_blocks", "sla2_num_kv_blocks", "sla2_topk", "sla2_workspa
            "sla2_quantize_fp8", "sla2_quantize_v_fp8", "sla2_timing_start", "sla2_timing_stop",
            "sla2_kernel_kinds", "sla2_kernel_name", "sla1_num_negligible", "sla1_route",
            "sla1_forward", "sla2_soft_topk", "sla2_soft_topk_grad", "sla2_route_grad",
-           "sla2_backward", "sla2_attention", "sla2_attention_fp8")
+           "sla2_backward", "sla2_attention", "sla2_attention_fp8", "sla2_fp8_dot_tiles")
 
 
 def _dtype(x):
@@ -97,9 +99,9 @@ def _dtype(x):
 
 def problem(B, H, N, d, bq=128, bkv=64, topk_frac=0.03, w_heads=1, dtype=BF16,
             phi=PHI_ELU1, layout=LAYOUT_BHND, alpha_mode=ALPHA_PER_HEAD,
-            out_dtype=F32, lowbit=LOWBIT_QK) -> Problem:
+            out_dtype=F32, lowbit=LOWBIT_QK, flags=0) -> Problem:
     return Problem(B, H, N, d, bq, bkv, float(topk_frac), w_heads, phi, _dtype(dtype),
-                   layout, alpha_mode, _dtype(out_dtype), lowbit)
+                   layout, alpha_mode, _dtype(out_dtype), lowbit, flags)
 
 
 def status_str(s: int) -> str:
@@ -230,6 +232,11 @@ def attention(p: Problem, Q, K, V, Wq, Wk, alpha, ws=None, stream=None, fp8=Fals
     fn = sla2_attention_fp8 if fp8 else sla2_attention
     fn(p, Q, K, V, Wq, Wk, alpha, idx if topk(p) > 0 else None, O, ws, stream)
     return idx, O
+
+
+def sla2_fp8_dot_tiles(A, B, Cout, ntiles, stream=None):
+    _raise(lib().sla2_fp8_dot_tiles(_ptr(A), _ptr(B), _ptr(Cout), int(ntiles), _stream(stream)),
+           "sla2_fp8_dot_tiles")
 
 
 def sla2_backward(p, Q, K, V, topk_idx, alpha, dO, dQ, dK, dV, dalpha, ws=None, stream=None):

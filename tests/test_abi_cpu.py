@@ -130,9 +130,11 @@ def test_layouts_alpha_modes_and_output_dtypes_are_accepted():
                     assert S.check(p, op) == S.OK
                     # the workspace does not depend on how Q/K/V/O are laid out
                     assert S.workspace_bytes(p, op) == S.workspace_bytes(p_ok(), op)
-    # quantising V as well needs its codes and scales in the fp8 workspace only
+    # quantising V as well: its one-byte codes replace the fp16 V^T copy of
+    # P V in the fp8 workspace (d = 128, bq = 128), and the plain forward's
+    # workspace is unchanged
     pv = p_ok(lowbit=S.LOWBIT_QKV)
-    assert S.workspace_bytes(pv, S.OP_FORWARD_FP8) > S.workspace_bytes(p_ok(), S.OP_FORWARD_FP8)
+    assert S.workspace_bytes(pv, S.OP_FORWARD_FP8) < S.workspace_bytes(p_ok(), S.OP_FORWARD_FP8)
     assert S.workspace_bytes(pv, S.OP_FORWARD) == S.workspace_bytes(p_ok(), S.OP_FORWARD)
     # int8 Q/K codes take the same room as e4m3 ones
     for lb, same in ((S.LOWBIT_I8QK, p_ok()), (S.LOWBIT_I8QKV, pv)):
@@ -229,3 +231,21 @@ def test_status_strings():
         assert S.status_str(s) and S.status_str(s) != "unknown status"
     assert S.status_str(42) == "unknown status"
     assert "fused_mfma" in S.kernel_names()
+
+
+def test_flags_rejected_outside_their_path():
+    assert S.check(S.problem(1, 2, 1000, 64, 128, 64, 0.1, flags=1), S.OP_FORWARD) == S.EUNSUPPORTED
+    assert S.check(S.problem(1, 2, 1000, 128, 64, 64, 0.1, flags=2), S.OP_FORWARD) == S.EUNSUPPORTED
+    assert S.check(S.problem(1, 2, 1000, 128, 128, 64, 0.1, flags=4), S.OP_FORWARD) == S.EINVAL
+    assert S.check(S.problem(1, 2, 1000, 128, 128, 64, 0.1, flags=1), S.OP_SLA1_FORWARD) == \
+        S.EUNSUPPORTED
+    assert S.check(S.problem(1, 2, 1000, 128, 128, 64, 0.1, flags=3), S.OP_ROUTE) == S.OK
+
+
+def test_fp8_dot_tiles_rejects_bad_arguments():
+    L = S.lib()
+    good = 1 << 20
+    assert L.sla2_fp8_dot_tiles(None, good, good, 1, None) == S.EINVAL
+    assert L.sla2_fp8_dot_tiles(good, good + 8, good, 1, None) == S.EINVAL
+    assert L.sla2_fp8_dot_tiles(good, good, good, 0, None) == S.EINVAL
+    assert L.sla2_fp8_dot_tiles(good, good, good, (1 << 20) + 1, None) == S.EINVAL

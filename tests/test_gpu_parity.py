@@ -79,13 +79,15 @@ def check_route(orc, x, idx, mask, heads=None):
 
 # Relative accumulation error of the e4m3 matrix-core dot products of the
 # low-bit logits, |computed - exact| <= FP8_ACC_EPS * sum |q^_c k^_c|.  The
-# gfx950 fp8 MFMA does not sum its 64 products exactly: over 2 x 2^19 dot
+# gfx950 fp8 MFMA does not sum its 64 products exactly; over 2^22 dot
 # products of length 128 of absmax-scaled Gaussian codes (independent and
-# correlated rows; tests/probes/fp8_mfma_accuracy.hip) the largest error was
-# 2^-15.35 of sum|ab|, and only 6-10 % of the results were exact; 2^-14 leaves
-# a factor 2.6.  Uniformly random codes over all exponents reach 2^-11.9, a
-# dynamic range that absmax-scaled blocks do not have.
+# correlated rows) the error stays near 2^-15 of sum|ab|, measured and
+# asserted by test_fp8_matrix_core_accumulation_error below through
+# sla2_fp8_dot_tiles (the same instruction and operand layout).
 FP8_ACC_EPS = 2.0 ** -14
+# Rows the low-bit gate lets past 3e-2 (each only through a recorded flip):
+# at most this share of the compared rows (and at least 2).
+FP8_OVER_SHARE = 1e-3
 # Low-bit bulk agreement: 90 % of the rows within 3e-4, 99 % within 5e-3.
 FP8_BULK = (3e-4, 5e-3)
 
@@ -128,6 +130,16 @@ def compare_blocks(orc, x, oidx, O, blocks, tol, variant="exact", op=None, alpha
     say(f"  max-abs error over {len(blocks)} blocks: {worst:.3e} (tol {tol}{extra})")
     bad = np.flatnonzero(err > tol + bnd)
     assert bad.size == 0, (int(bad[0]), float(err[bad[0]]), float(bnd[bad[0]]))
+    if bound is not None:
+        # every row past tol is there through a recorded flip (bnd > 0 by the
+        # check above), and such rows stay rare
+        over = err > tol
+        n_over = int(over.sum())
+        cap = max(2, int(np.ceil(FP8_OVER_SHARE * err.size)))
+        used = float((err - tol)[over].max()) if n_over else 0.0
+        say(f"  rows over {tol}: {n_over} of {err.size} (cap {cap}); largest allowance "
+            f"used {used:.2e}; plain max-abs {worst:.3e}")
+        assert n_over <= cap, (n_over, cap)
     if bound is not None and err.size >= 100:
         # Flips are rare and every other difference is fp32 rounding, so the
         # bulk of the rows must agree far more tightly than tol: a wrong max,
@@ -322,6 +334,49 @@ FP8_SMALL = [
     wl("fp8-one-token", "bf16", 1, 128, 128, 1.0),
     wl("fp8-alpha1", "bf16", 2000, 128, 128, 0.1, alpha=(1.0, 1.0)),
 ]
+
+
+def e4m3_codes(x: np.ndarray) -> np.ndarray:
+    """float -> OCP e4m3 codes (torch's float8_e4m3fn conversion; |x| <= 448)."""
+    return torch.from_numpy(np.ascontiguousarray(x, np.float32)).to(
+        torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def e4m3_values(c: np.ndarray) -> np.ndarray:
+    return torch.from_numpy(c).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+
+
+@pytest.mark.parametrize("kind", ["gaussian", "correlated"])
+def test_fp8_matrix_core_accumulation_error(dev, kind):
+    """The constant FP8_ACC_EPS of the low-bit gate, measured on the GPU: the
+    e4m3 matrix-core dot products of sla2_fp8_dot_tiles (the instruction and
+    operand layout of the low-bit Q K^T) against exact float64 sums, for rows
+    scaled to absmax 448 as the per-block scales do; 2^22 dot products."""
+    rng = np.random.default_rng(7 if kind == "gaussian" else 8)
+    nt = 4096
+    a = rng.standard_normal((nt, 32, 128))
+    if kind == "gaussian":
+        b = rng.standard_normal((nt, 32, 128))
+    else:  # each row of B close to a row of A: large positive dot products
+        b = a[:, rng.permutation(32)] + 0.3 * rng.standard_normal((nt, 32, 128))
+    a = a / np.abs(a).max(axis=2, keepdims=True) * 448.0
+    b = b / np.abs(b).max(axis=2, keepdims=True) * 448.0
+    ca, cb = e4m3_codes(a), e4m3_codes(b)
+    A = torch.from_numpy(ca).to(dev)
+    B = torch.from_numpy(cb).to(dev)
+    Cd = torch.empty((nt, 32, 32), dtype=torch.float32, device=dev)
+    S.sla2_fp8_dot_tiles(A, B, Cd, nt)
+    torch.cuda.synchronize()
+    va, vb = e4m3_values(ca), e4m3_values(cb)
+    exact = np.matmul(va, vb.transpose(0, 2, 1))      # exact in float64
+    absum = np.matmul(np.abs(va), np.abs(vb).transpose(0, 2, 1))
+    got = Cd.cpu().numpy().astype(np.float64)
+    rel = np.abs(got - exact) / np.maximum(absum, 1e-300)
+    worst = float(rel.max())
+    say(f"fp8 dot products ({kind}): largest |computed - exact| / sum|ab| = {worst:.3e} "
+        f"= 2^{np.log2(max(worst, 1e-300)):.2f}; exact results {float((rel == 0).mean()):.1%}; "
+        f"gate constant 2^{np.log2(FP8_ACC_EPS):.0f}")
+    assert worst <= FP8_ACC_EPS
 
 
 LOWBITS = [S.LOWBIT_QK, S.LOWBIT_QKV, S.LOWBIT_I8QK, S.LOWBIT_I8QKV]
