@@ -93,6 +93,28 @@ def linear_summary_flop(BH, N, d) -> float:
     return 2.0 * BH * N * d * d
 
 
+# Sizes of the linear-branch product (csrc/linear.hip): per head U (T_q rows,
+# padded to tiles of 320) times the block summaries (T_kv rows padded to 64,
+# 16640 columns: d*d entries of h_j plus d of z_j, padded to tiles of 128).
+HZ_COLS, HZ_PITCH, GEMM_M = 128 * 128 + 128, 65 * 256, 320
+
+
+def product_work(BH, Tq, Tkv):
+    """(executed MFMA FLOP, HBM bytes: summaries read once + H written in
+    bf16 and Z in fp32) of one linear-branch product launch."""
+    tq_pad = -(-Tq // GEMM_M) * GEMM_M
+    tkv_pad = -(-Tkv // 64) * 64
+    flop = 2.0 * BH * tq_pad * HZ_PITCH * tkv_pad
+    byts = BH * (Tkv * HZ_PITCH * 2 + Tq * (128 * 128 * 2 + 128 * 4))
+    return flop, byts
+
+
+def summaries_bytes(BH, N, d, Tkv):
+    """Block-summaries pass: read K and V, write V^T (fp16) and the bf16
+    per-block summaries rows."""
+    return BH * (2 * N * d * 2 + Tkv * 64 * d * 2 + Tkv * HZ_COLS * 2)
+
+
 # --------------------------------------------------------------------------
 COPY_BYTES = 1 << 30
 FUSED_KERNEL_RX = r"fused128_kernel<true, 0, false, false, false>"
@@ -222,6 +244,18 @@ def counters_summary(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, workl
     print(json.dumps(res, indent=1))
 
 
+def host_info():
+    model = ""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return {"nproc": os.cpu_count(), "cpu_model": model}
+
+
 def cpu_baseline(x, dense_flop, budget_s=12.0):
     """Times the oracle on a bounded sample of the same workload: whole heads
     (router + forward of every query block of the head), one after another,
@@ -247,12 +281,96 @@ def cpu_baseline(x, dense_flop, budget_s=12.0):
         "value": dense_flop / t_job / 1e12,
         "unit": "TOPS",
         "cores": threads,
+        "threads": threads,
+        **host_info(),
         "kind": "oracle",
         "sample": (f"{len(times)} of {BH} heads, each routed and then run through the forward "
                    f"for all {w.Tq} query blocks ({sum(times):.1f} s, {t_head:.2f} s per head); "
                    f"whole-job CPU time extrapolated as {BH} x per-head time = {t_job:.0f} s"),
         "sample_seconds": sum(times),
     }
+
+
+def time_calls(torch, S, fn, stream, steps, warmup):
+    """(ms per call, {kernel: ms per launch}) of `steps` calls after `warmup`."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    S.timing_start(64 * steps + 64)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    st = {n_: ms_ / c_ for n_, (ms_, c_) in S.timing_stop().items()}
+    return e0.elapsed_time(e1) / steps, st
+
+
+def sweep(args, torch, I, S, dev):
+    """Sparsity sweep at the Wan-1.3B shape (10 / 5 / 3 / 1 % of the KV
+    blocks): per fraction the one-call step, and the same call with the
+    linear branch left out (sparse branch alone) and with the sparse branch
+    left out (linear branch alone); then the dense baseline, k = T_kv,
+    alpha = 1 and no linear branch, i.e. plain softmax attention on the same
+    kernels ("SLA2 深度解读" 13 compares with a dense FlashAttention2
+    kernel)."""
+    base = I.WAN13B
+    x = I.make_inputs(base)
+    stream = torch.cuda.current_stream()
+
+    def t(a):
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(a).to(dev)
+
+    q, k, v, wq, wk, al = t(x.q), t(x.k), t(x.v), t(x.wq), t(x.wk), t(x.alpha)
+    dense = dense_equivalent_flop(base.B, base.H, base.N, base.d)
+    O = torch.empty((base.B, base.H, base.N, base.d), dtype=torch.float32, device=dev)
+    route_k = ("pool_project", "score", "topk_select")
+    rows = []
+    for frac in I.SWEEP_FRACS:
+        res = {"topk_frac": frac}
+        for name, flags in (("full", 0), ("sparse_only", S.FLAG_SKIP_LINEAR),
+                            ("linear_only", S.FLAG_SKIP_SPARSE)):
+            p = S.problem(base.B, base.H, base.N, base.d, base.bq, base.bkv, frac, 1,
+                          base.dtype, flags=flags)
+            kk = S.topk(p)
+            idx = torch.empty((base.B, base.H, S.num_q_blocks(p), kk), dtype=torch.int32,
+                              device=dev)
+            ws = S.workspace(p, S.OP_ATTENTION)
+            ms, st = time_calls(torch, S, lambda: S.sla2_attention(
+                p, q, k, v, wq, wk, al, idx, O, ws, stream), stream, args.steps, args.warmup)
+            res["k"] = kk
+            res[name] = {"ms_per_step": ms, "stages_ms": st,
+                         "route_ms": sum(st.get(n_, 0.0) for n_ in route_k)}
+            del ws
+        res["tops"] = dense / (res["full"]["ms_per_step"] * 1e-3) / 1e12
+        res["sparse_branch_ms"] = res["sparse_only"]["stages_ms"].get("fused_mfma")
+        res["linear_branch_ms"] = (res["full"]["stages_ms"].get("lin_gemm", 0.0) +
+                                   res["linear_only"]["stages_ms"].get("fused_mfma", 0.0))
+        log(f"sweep {frac}: {res['full']['ms_per_step']:.3f} ms/step, sparse "
+            f"{res['sparse_branch_ms']:.3f}, linear {res['linear_branch_ms']:.3f}")
+        rows.append(res)
+    # dense baseline: every block selected, alpha = 1, no linear branch
+    p = S.problem(base.B, base.H, base.N, base.d, base.bq, base.bkv, 1.0, 1, base.dtype,
+                  flags=S.FLAG_SKIP_LINEAR)
+    idx = torch.empty((base.B, base.H, S.num_q_blocks(p), S.topk(p)), dtype=torch.int32,
+                      device=dev)
+    ones = torch.ones_like(al)
+    ws = S.workspace(p, S.OP_ATTENTION)
+    ms, st = time_calls(torch, S, lambda: S.sla2_attention(p, q, k, v, wq, wk, ones, idx, O, ws,
+                                                           stream), stream, args.steps,
+                        args.warmup)
+    fused = st.get("fused_mfma")
+    dense_res = {"k": S.topk(p), "ms_per_step": ms, "stages_ms": st, "fused_ms": fused,
+                 "fused_tflops": dense / (fused * 1e-3) / 1e12 if fused else None}
+    for r in rows:
+        r["speedup_vs_dense_kernel"] = fused / r["full"]["ms_per_step"] if fused else None
+    print(json.dumps({"sweep": rows, "dense_baseline": dense_res,
+                      "workload": f"wan13b: B={base.B} H={base.H} N={base.N} d={base.d} "
+                                  f"b_q={base.bq} b_kv={base.bkv}",
+                      "steps": args.steps, "warmup": args.warmup}))
 
 
 def main():
@@ -269,6 +387,9 @@ def main():
     ap.add_argument("--counters-summary", nargs=4, metavar="DIR")
     ap.add_argument("--traffic-table", nargs=4, metavar="DIR")
     ap.add_argument("--counter-table", metavar="DIR")
+    ap.add_argument("--sweep", action="store_true",
+                    help="sparsity sweep at the 1.3B shape with per-branch times and the "
+                         "dense baseline (one JSON line)")
     args = ap.parse_args()
 
     if args.counters_summary:
@@ -299,6 +420,9 @@ def main():
     S.lib()
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
+    if args.sweep:
+        sweep(args, torch, I, S, dev)
+        return
     w = I.WORKLOADS[args.workload]
     log(f"bench: generating {w.name} inputs")
     x = I.make_inputs(w)
@@ -370,7 +494,7 @@ def main():
     stages = {name: ms / n for name, (ms, n) in kernels.items()}
     fused_ms = stages.get("fused_mfma")
     fwd_ms = sum(v for kname, v in stages.items()
-                 if kname in ("summaries_mfma", "summaries_reduce", "fused_mfma"))
+                 if kname in ("summaries_mfma", "summaries_reduce", "fused_mfma", "lin_gemm"))
     route_ms = sum(v for kname, v in stages.items()
                    if kname in ("pool_project", "score", "topk_select"))
 
@@ -385,7 +509,15 @@ def main():
                 "kernel": "fused_mfma", "algorithmic_flop_per_launch": fl_sparse + fl_apply,
                 "avg_launch_ms": fused_ms}
 
-    qk_bytes = 2.0 * BH * w.N * w.d * 2  # one read of Q and K (router), or K and V
+    qk_bytes = 2.0 * BH * w.N * w.d * 2  # one read of Q and K (router)
+    s_bytes = summaries_bytes(BH, w.N, w.d, Tkv)
+    g_flop, g_bytes = product_work(BH, Tq, Tkv)
+
+    def hbm(byts, ms):  # achieved rate of algorithmic bytes, alone (sequential calls)
+        if not ms:
+            return None
+        gbs = byts / (ms * 1e-3) / 1e9
+        return {"bytes": byts, "ms_alone": ms, "gbs": gbs, "frac_of_8tbs": gbs / PEAK_HBM_GBS}
     out = {
         "metric": "dense-equivalent attention TOPS at 97% sparsity (Wan-14B-720P shape), 1 GPU"
         if w.name == "wan14b" else "dense-equivalent attention TOPS (Wan-1.3B-480P shape), 1 GPU",
@@ -413,8 +545,17 @@ def main():
         "forward_only_tops": dense / (fwd_ms * 1e-3) / 1e12 if fwd_ms else None,
         "sparse_flop_per_step": fl_sparse,
         "sparse_fraction_of_dense": fl_sparse / dense,
-        "router_hbm_gbs": qk_bytes / ((stages.get("pool_project", 0) or 1e-9) * 1e-3) / 1e9,
-        "summaries_hbm_gbs": qk_bytes / ((stages.get("summaries_mfma", 0) or 1e-9) * 1e-3) / 1e9,
+        # pooling reads Q and K; the summaries read K, V and write V^T and the
+        # per-block rows of h_j, z_j; the product reads those rows once and
+        # writes H_i, Z_i (fp32): algorithmic bytes over each kernel's time
+        # alone (the sequential calls), as a fraction of 8 TB/s
+        "router_pool_hbm": hbm(qk_bytes, seq_stages.get("pool_project")),
+        "summaries_hbm": hbm(s_bytes, seq_stages.get("summaries_mfma")),
+        "linear_product": dict(
+            hbm(g_bytes, seq_stages.get("lin_gemm")) or {},
+            mfma_flop=g_flop,
+            tflops=(g_flop / (seq_stages["lin_gemm"] * 1e-3) / 1e12
+                    if seq_stages.get("lin_gemm") else None)),
         "kernel_source_sha": kernel_source_sha(),
     }
 

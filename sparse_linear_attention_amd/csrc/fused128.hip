@@ -17,10 +17,10 @@
 //   O^T += V_j^T P^T                    fp16 MFMA (LOWBIT: P on the e4m3 grid)
 // The linear branch's sums over the blocks the query block leaves out,
 // H_i = sum h_j and Z_i = sum z_j (SLA notes, key designs 3 and 4), come
-// ready from the dense product of linear.hip (one fp32 row per query block).
-// Epilogue: H_i^T scaled by a power of two into the fp16 range, O_l^T =
-// H_i^T phi(Q)^T / (phi(Q) . Z_i), O = alpha O_s + (1 - alpha) O_l
-// ("SLA2 深度解读" 04).
+// ready from the dense product of linear.hip (one row per query block: H_i
+// in bf16, Z_i in fp32).  Epilogue: O_l^T = H_i^T phi(Q)^T (bf16 matrix
+// cores, phi(Q) rounded to bf16) / (phi(Q) . Z_i in fp32), O = alpha O_s +
+// (1 - alpha) O_l ("SLA2 深度解读" 04).
 //
 // PHISM: phi is the softmax of each row over its 128 channels (the block
 // summaries pass applies the same map to K).  V1 (SLA v1, "SLA: Beyond
@@ -150,7 +150,7 @@ template <bool LIN, int QK, bool LOWV, bool PHISM, bool V1>
 __global__ __launch_bounds__(256, 2) void fused128_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ vt, const int32_t* __restrict__ idx,
-    const float* __restrict__ alpha, const float* __restrict__ HZ,
+    const float* __restrict__ alpha, const char* __restrict__ HZ,
     const uint8_t* __restrict__ qhat, const uint8_t* __restrict__ khat,
     const float* __restrict__ sq, const float* __restrict__ sk,
     const uint8_t* __restrict__ vhat, const float* __restrict__ sv, void* __restrict__ O,
@@ -477,55 +477,20 @@ __global__ __launch_bounds__(256, 2) void fused128_kernel(
 #pragma unroll
     for (int i = 0; i < 4; ++i) ol[i] = zero16();
     float inv_den = 0.0f;
-    float hscale = 1.0f;
     if (LIN) {
         wg_barrier();  // every wave is done with the tile stages
-        // H_i^T (fp32 row of the product: entry e * 128 + c) times hscale, a
-        // power of two that puts its largest magnitude in [2^14, 2^15), as
-        // fp16 in [128 d rows][256 B], chunk c' of row e at c' ^ (e & 15);
-        // Z_i in fp32
+        // H_i^T (bf16 row of the product: entry e * 128 + c) into LDS as
+        // [128 d rows][256 B], chunk c' of row e at c' ^ (e & 15); Z_i fp32
         char* sH = s_lds;
         float* sZ = reinterpret_cast<float*>(s_lds + 32768);
-        float* sM = sZ + 128;
-        const float* hrow = HZ + ((size_t)bh * Tq + qb) * kHzCols;
-        const int he = t >> 1, hc0 = 64 * (t & 1);  // row e, channels hc0 .. hc0 + 63
-        const float* hp = hrow + he * 128 + hc0;
-        // two passes over the thread's 64 entries (the second from the cache):
-        // the largest magnitude, then the scaled fp16 values
-        float hmx = 0.0f;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const float4 v = *reinterpret_cast<const float4*>(hp + 4 * i);
-            hmx = fmaxf(hmx, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
-        }
-        if (t < 128) sZ[t] = hrow[128 * 128 + t];
-#pragma unroll
-        for (int off = 32; off > 0; off >>= 1) hmx = fmaxf(hmx, __shfl_xor(hmx, off));
-        if (lane == 0) sM[w] = hmx;
-        wait_lgkm0();
-        wg_barrier();
-        const float hmax = fmaxf(fmaxf(sM[0], sM[1]), fmaxf(sM[2], sM[3]));
-        if (hmax > 0.0f) {
-            int ex;
-            (void)frexpf(hmax, &ex);  // hmax = f 2^ex, f in [0.5, 1)
-            hscale = ldexpf(1.0f, 15 - ex);
-        }
+        const char* hrow = HZ + ((size_t)bh * Tq + qb) * kHzRowBytes;
+        const int he = t >> 1, hc = 8 * (t & 1);  // row e, 16-byte chunks hc .. hc + 7
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            const float4 a = *reinterpret_cast<const float4*>(hp + 8 * i);
-            const float4 b = *reinterpret_cast<const float4*>(hp + 8 * i + 4);
-            f16x8 hh;
-            hh[0] = (_Float16)(a.x * hscale);
-            hh[1] = (_Float16)(a.y * hscale);
-            hh[2] = (_Float16)(a.z * hscale);
-            hh[3] = (_Float16)(a.w * hscale);
-            hh[4] = (_Float16)(b.x * hscale);
-            hh[5] = (_Float16)(b.y * hscale);
-            hh[6] = (_Float16)(b.z * hscale);
-            hh[7] = (_Float16)(b.w * hscale);
-            const int cc = (hc0 >> 3) + i;
-            *reinterpret_cast<f16x8*>(sH + he * 256 + ((cc ^ (he & 15)) << 4)) = hh;
+            const uint4 v = *reinterpret_cast<const uint4*>(hrow + he * 256 + (hc + i) * 16);
+            *reinterpret_cast<uint4*>(sH + he * 256 + (((hc + i) ^ (he & 15)) << 4)) = v;
         }
+        if (t < 128) sZ[t] = reinterpret_cast<const float*>(hrow + 2 * 128 * 128)[t];
         wait_lgkm0();
         wg_barrier();
         // phi(Q)^T operand from the raw bf16 Q (registers on the bf16 path)
@@ -542,7 +507,7 @@ __global__ __launch_bounds__(256, 2) void fused128_kernel(
 #pragma unroll
             for (int ks = 0; ks < 8; ++ks) qraw[ks] = reinterpret_cast<const bf16x8*>(Qo.f)[ks];
         }
-        f16x8 pq[8];
+        bf16x8 pq[8];
         float den = 0.0f;
         // softmax phi: max and 1 / sum exp over the query's 128 channels (64
         // in this lane, 64 in its partner lane ^ 32)
@@ -570,20 +535,22 @@ __global__ __launch_bounds__(256, 2) void fused128_kernel(
             for (int e = 0; e < 8; ++e) {
                 const float p = PHISM ? __expf((float)qraw[ks][e] - qmax) * qinv
                                       : phi_fast((float)qraw[ks][e]);
-                pq[ks][e] = (_Float16)p;
-                den = fmaf(p, zz[e], den);
+                pq[ks][e] = (__bf16)p;
+                // the same rounded phi in the denominator: O_l stays a
+                // weighted mean of the value rows
+                den = fmaf((float)pq[ks][e], zz[e], den);
             }
         }
         den += __shfl_xor(den, 32);
-        inv_den = 1.0f / (den * hscale);
+        inv_den = 1.0f / den;
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) {
             const int erow = 32 * mt + l32;
 #pragma unroll
             for (int ks = 0; ks < 8; ++ks) {
-                const f16x8 a = *reinterpret_cast<const f16x8*>(
+                const bf16x8 a = *reinterpret_cast<const bf16x8*>(
                     sH + erow * 256 + (((2 * ks + hl) ^ (erow & 15)) << 4));
-                ol[mt] = mfma_f16(a, pq[ks], ol[mt]);
+                ol[mt] = mfma_bf16(a, pq[ks], ol[mt]);
             }
         }
     }

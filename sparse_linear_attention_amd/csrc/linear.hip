@@ -170,7 +170,7 @@ __device__ inline void load_lds4(rsrc_t r, uint32_t voff, uint32_t soff, char* d
 // so one wave's load and LDS waits are covered by the others' products.
 __global__ __launch_bounds__(256, 2) void lin_gemm_kernel(const uint8_t* __restrict__ U,
                                                          const uint16_t* __restrict__ hz,
-                                                         float* __restrict__ HZ, int Tq, int Tkv,
+                                                         char* __restrict__ HZ, int Tq, int Tkv,
                                                          int Tkvp, int nM, int rows) {
     __shared__ __attribute__((aligned(1024))) char lds[4 * 2 * kWSt + kTbl];
     const int t = threadIdx.x, lane = t & 63, l32 = lane & 31, hl = lane >> 5;
@@ -309,21 +309,54 @@ __global__ __launch_bounds__(256, 2) void lin_gemm_kernel(const uint8_t* __restr
         mma(x1);
     }
 
-    // rows (query blocks) 8 (r / 4) + 4 hl + r % 4 of each 32 x 32 tile,
-    // column l32: 32 consecutive floats per row and half-wave
-    float* out = HZ + (size_t)bh * Tq * kHzCols;
+    // Output.  Accumulator (m, nt, r) is row 32 m + 8 (r / 4) + 4 hl + r % 4
+    // of the wave's 160 and column 32 nt + l32 of its 64.  The H columns
+    // (below d*d) go out in bf16 (nearest even) through the wave's own LDS
+    // region (free now: no other wave reads it), so that the global stores
+    // are whole 128-byte row pieces: rows of m-tiles 0-2, then 3-4.  The Z
+    // columns (one column tile) go out in fp32 directly.
+    char* out = HZ + (size_t)bh * Tq * kHzRowBytes;
+    if (n0 >= 128 * 128) {
 #pragma unroll
-    for (int m = 0; m < 5; ++m)
+        for (int m = 0; m < 5; ++m)
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt) {
-            const int col = n0 + 32 * nt + l32;
-            if (col >= kHzCols) continue;
+            for (int nt = 0; nt < 2; ++nt) {
+                const int col = n0 + 32 * nt + l32;
+                if (col >= kHzCols) continue;
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int qb = m0 + 32 * m + 8 * (r >> 2) + 4 * hl + (r & 3);
-                if (qb < Tq) out[(size_t)qb * kHzCols + col] = acc[m][nt][r];
+                for (int r = 0; r < 16; ++r) {
+                    const int qb = m0 + 32 * m + 8 * (r >> 2) + 4 * hl + (r & 3);
+                    if (qb < Tq)
+                        reinterpret_cast<float*>(out + (size_t)qb * kHzRowBytes + 2 * 128 * 128)
+                            [col - 128 * 128] = acc[m][nt][r];
+                }
             }
+        return;
+    }
+    __bf16* st = reinterpret_cast<__bf16*>(wbase);  // [rows][64] bf16
+    auto flush = [&](int m_lo, int m_hi) {
+#pragma unroll
+        for (int m = m_lo; m < m_hi; ++m)
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int lr = 32 * (m - m_lo) + 8 * (r >> 2) + 4 * hl + (r & 3);
+                    st[lr * 64 + 32 * nt + l32] = (__bf16)acc[m][nt][r];
+                }
+        wait_lgkm0();
+        const int nrow = 32 * (m_hi - m_lo);
+        for (int i = 0; i < nrow / 8; ++i) {
+            const int lr = 8 * i + (lane >> 3);
+            const int qb = m0 + 32 * m_lo + lr;
+            const uint4 v = *reinterpret_cast<const uint4*>(wbase + lr * 128 + (lane & 7) * 16);
+            if (qb < Tq)
+                *reinterpret_cast<uint4*>(out + (size_t)qb * kHzRowBytes + n0 * 2 + (lane & 7) * 16) = v;
         }
+        wait_lgkm0();  // the reads are done before the region is written again
+    };
+    flush(0, 3);
+    flush(3, 5);
 }
 
 }  // namespace

@@ -188,7 +188,7 @@ size_t layout_forward(const Dims& D, int op, char* base, FwdWS* ws) {
         if (!(lowbit_op && D.lowbit_v)) w.vt = carve<uint16_t>(base, off, 2 * bh * D.Tkv * d * 64);
         w.hz = carve<uint16_t>(base, off, 2 * bh * D.Tkv * (size_t)kHzPitch);
         w.usel = carve<uint8_t>(base, off, bh * (size_t)(tkv_pad(D) / 64) * ubit_rows(D) * 8);
-        w.HZ = carve<float>(base, off, 4 * bh * D.Tq * (size_t)kHzCols);
+        w.HZ = carve<char>(base, off, bh * D.Tq * (size_t)kHzRowBytes);
     } else {
         if (D.dtype == SLA2_BF16) {
             w.vt = carve<uint16_t>(base, off, 2 * bh * D.Tkv * d * 64);

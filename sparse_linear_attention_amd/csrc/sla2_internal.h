@@ -109,6 +109,9 @@ inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 // to the linear branch (linear.hip).  Rows of the block summaries and of the
 // products hold the d*d entries of h^T (V channel major) and then the d of z.
 constexpr int kHzCols = 128 * 128 + 128;  // entries of a row
+// bytes of a product row: H_i^T in bf16 (the fp32 exponent range, so no
+// scaling), then Z_i in fp32
+constexpr int kHzRowBytes = 128 * 128 * 2 + 128 * 4;
 constexpr int kHzPitch = 65 * 256;        // bf16 elements per summaries row
 constexpr int kGemmM = 320;               // query blocks per product tile
 inline bool hz_path(const Dims& D) { return D.dtype == SLA2_BF16 && D.d == 128 && D.bq == 128; }
@@ -157,7 +160,7 @@ struct FwdWS {
     // d = 128, b_q = 128 bf16 path (hz_path): the linear branch as a product
     uint16_t* hz;    // [BH][Tkv][kHzPitch] bf16: h_j^T (e * 128 + c), then z_j
     uint8_t* usel;   // [BH][tkv_pad / 64][ubit_rows][8] bits: block j left to the linear branch
-    float* HZ;       // [BH][Tq][kHzCols] fp32: H_i^T (e * 128 + c), then Z_i
+    char* HZ;        // [BH][Tq][kHzRowBytes]: H_i^T (e * 128 + c) bf16, then Z_i fp32
 };
 
 // backward (SLA2_OP_BACKWARD: the forward's summary buffers, then these)
