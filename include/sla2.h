@@ -215,6 +215,30 @@ sla2_status sla2_attention(const sla2_problem* p, const void* Q, const void* K, 
                            int32_t* topk_idx, void* O, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * sla2_attention_noalloc -- for callers that cannot allocate device memory
+ *   or create HIP objects (code under HIP graph capture, tight serving loops,
+ *   harnesses that forbid allocation): sla2_attention with no workspace
+ *   argument.  Its workspace is a file-scope device array of the library,
+ *   sla2_noalloc_scratch_bytes() = 64 MiB, one copy on each GPU the library
+ *   runs on, held until the process ends (addressed once per device, on the
+ *   first call there).  Everything is enqueued on `stream`, in order (no
+ *   helper stream, no events); the call itself allocates nothing.  Same
+ *   results as sla2_attention (bit-identical O and topk_idx).
+ *   Limit: sla2_workspace_bytes(p, SLA2_OP_ATTENTION) <= 64 MiB (for example
+ *   B = 1, H = 2, N = 8192, d = 128 uses about 17 MiB); larger problems
+ *   return SLA2_EWORKSPACE and launch nothing.
+ *   Calls on one GPU share the array: calls that overlap in time on that GPU
+ *   (different streams, or threads) race on it and give undefined results;
+ *   order them (one stream, or events) when using this entry point.
+ * In / Out: as sla2_attention.
+ */
+sla2_status sla2_attention_noalloc(const sla2_problem* p, const void* Q, const void* K,
+                                   const void* V, const float* Wq, const float* Wk,
+                                   const float* alpha, int32_t* topk_idx, void* O,
+                                   void* stream);
+size_t sla2_noalloc_scratch_bytes(void);
+
+/*
  * sla2_forward_fp8 -- as sla2_forward, with the low-bit sparse branch
  * ("SLA2 深度解读" 07).  Requires dtype == SLA2_BF16, bq == 128 and d == 128
  * (SLA2_EUNSUPPORTED otherwise).

@@ -474,6 +474,75 @@ SLA2_API sla2_status sla2_attention(const sla2_problem* p, const void* Q, const 
     return e == hipSuccess ? SLA2_OK : SLA2_EHIP;
 }
 
+// ---------------------------------------------------------------------------
+// route + forward with no allocation of any kind: the workspace is a
+// file-scope device array, one copy per GPU (the code object's data, loaded
+// with the library's kernels), addressed through hipGetSymbolAddress once per
+// device; everything runs on the caller's stream (no helper stream, no
+// events).  The array keeps the previous call's contents; nothing in the
+// path reads workspace it did not write in the same call, so nothing is
+// cleared.
+// ---------------------------------------------------------------------------
+static constexpr size_t kScratchBytes = size_t(64) << 20;
+static __device__ __align__(256) char scratch[kScratchBytes];
+
+namespace {
+constexpr int kMaxScratchDevices = 64;
+void* g_scratch[kMaxScratchDevices];
+std::mutex g_scratch_mu;
+
+// the calling thread's current device's copy of scratch
+hipError_t scratch_ptr(void** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxScratchDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (!g_scratch[dev]) {
+        void* ptr = nullptr;
+        if ((e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch))) != hipSuccess) return e;
+        if (!ptr) return hipErrorInvalidSymbol;
+        g_scratch[dev] = ptr;
+    }
+    *out = g_scratch[dev];
+    return hipSuccess;
+}
+}  // namespace
+
+SLA2_API size_t sla2_noalloc_scratch_bytes(void) { return kScratchBytes; }
+
+SLA2_API sla2_status sla2_attention_noalloc(const sla2_problem* p, const void* Q, const void* K,
+                                            const void* V, const float* Wq, const float* Wk,
+                                            const float* alpha, int32_t* topk_idx, void* O,
+                                            void* stream) {
+    Dims D;
+    sla2_status st = make_dims(p, SLA2_OP_ATTENTION, &D);
+    if (st != SLA2_OK) return st;
+    if (!ok_ptr(Q) || !ok_ptr(K) || !ok_ptr(V) || !ok_ptr(Wq) || !ok_ptr(Wk) || !ok_ptr(alpha) ||
+        !ok_ptr(O))
+        return SLA2_EINVAL;
+    if (D.k > 0 && !ok_ptr(topk_idx)) return SLA2_EINVAL;
+    if (ws_bytes_of(D, SLA2_OP_ATTENTION) > kScratchBytes) return SLA2_EWORKSPACE;
+    void* ws = nullptr;
+    if (scratch_ptr(&ws) != hipSuccess) return SLA2_EHIP;
+    RouteWS rw;
+    FwdWS fw;
+    const size_t roff = layout_route(D, (char*)ws, &rw);
+    layout_forward(D, SLA2_OP_FORWARD, (char*)ws + roff, &fw);
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t e = launch_route(D, Q, K, Wq, Wk, topk_idx, nullptr, rw, s);
+    if (e == hipSuccess) {
+        if (D.dtype == SLA2_F32 || D.bq != 128) {
+            e = launch_forward_valu(D, Q, K, V, topk_idx, alpha, O, fw, s);
+        } else {
+            e = launch_summaries_mfma(D, K, V, fw, s);
+            if (e == hipSuccess && hz_path(D)) e = linear_product(D, topk_idx, nullptr, 0, fw, s);
+            if (e == hipSuccess) e = launch_fused_mfma(D, Q, K, topk_idx, alpha, O, fw, s);
+        }
+    }
+    return e == hipSuccess ? SLA2_OK : SLA2_EHIP;
+}
+
 SLA2_API sla2_status sla2_attention_fp8(const sla2_problem* p, const void* Q, const void* K,
                                         const void* V, const float* Wq, const float* Wk,
                                         const float* alpha, int32_t* topk_idx, void* O,

@@ -79,6 +79,8 @@ def lib():
         L.sla1_route.argtypes = [P, vp, vp, C.c_float, vp, vp, vp, vp, C.c_size_t, vp]
         L.sla1_forward.argtypes = [P, vp, vp, vp, vp, vp, C.c_float, vp, vp, vp, C.c_size_t, vp]
         L.sla2_fp8_dot_tiles.argtypes = [vp, vp, vp, C.c_int32, vp]
+        L.sla2_attention_noalloc.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+        L.sla2_noalloc_scratch_bytes.restype = C.c_size_t
         _lib = L
     return _lib
 
@@ -88,7 +90,8 @@ EXPORTS = ("sla2_num_q_blocks", "sla2_num_kv_blocks", "sla2_topk", "sla2_workspa
            "sla2_quantize_fp8", "sla2_quantize_v_fp8", "sla2_timing_start", "sla2_timing_stop",
            "sla2_kernel_kinds", "sla2_kernel_name", "sla1_num_negligible", "sla1_route",
            "sla1_forward", "sla2_soft_topk", "sla2_soft_topk_grad", "sla2_route_grad",
-           "sla2_backward", "sla2_attention", "sla2_attention_fp8", "sla2_fp8_dot_tiles")
+           "sla2_backward", "sla2_attention", "sla2_attention_fp8", "sla2_fp8_dot_tiles",
+           "sla2_attention_noalloc", "sla2_noalloc_scratch_bytes")
 
 
 def _dtype(x):
@@ -207,6 +210,16 @@ def sla2_attention(p, Q, K, V, Wq, Wk, alpha, topk_idx, O, ws=None, stream=None)
     _raise(lib().sla2_attention(C.byref(p), _ptr(Q), _ptr(K), _ptr(V), _ptr(Wq), _ptr(Wk),
                                 _ptr(alpha), _ptr(topk_idx), _ptr(O), wp, wb, _stream(stream)),
            "sla2_attention")
+
+
+def sla2_attention_noalloc(p, Q, K, V, Wq, Wk, alpha, topk_idx, O, stream=None):
+    _raise(lib().sla2_attention_noalloc(C.byref(p), _ptr(Q), _ptr(K), _ptr(V), _ptr(Wq),
+                                        _ptr(Wk), _ptr(alpha), _ptr(topk_idx), _ptr(O),
+                                        _stream(stream)), "sla2_attention_noalloc")
+
+
+def noalloc_scratch_bytes() -> int:
+    return int(lib().sla2_noalloc_scratch_bytes())
 
 
 def sla2_attention_fp8(p, Q, K, V, Wq, Wk, alpha, topk_idx, O, ws=None, stream=None):

@@ -249,3 +249,19 @@ def test_fp8_dot_tiles_rejects_bad_arguments():
     assert L.sla2_fp8_dot_tiles(good, good + 8, good, 1, None) == S.EINVAL
     assert L.sla2_fp8_dot_tiles(good, good, good, 0, None) == S.EINVAL
     assert L.sla2_fp8_dot_tiles(good, good, good, (1 << 20) + 1, None) == S.EINVAL
+
+
+def test_noalloc_rejects_problems_past_its_array():
+    """The no-allocation entry point refuses, on the host and before any
+    launch, a problem whose workspace exceeds its fixed device array."""
+    L = S.lib()
+    cap = S.noalloc_scratch_bytes()
+    assert cap == 64 << 20
+    small = p_ok(N=8192, H=2)
+    assert S.workspace_bytes(small, S.OP_ATTENTION) <= cap
+    big = p_ok(N=75600, H=40, topk_frac=0.03)
+    assert S.workspace_bytes(big, S.OP_ATTENTION) > cap
+    good = 1 << 20
+    args = [good] * 8 + [None]
+    assert L.sla2_attention_noalloc(C.byref(big), *args) == S.EWORKSPACE
+    assert L.sla2_attention_noalloc(C.byref(small), None, *args[1:]) == S.EINVAL
