@@ -36,9 +36,9 @@
  *    B/H/N <= 0, topk_frac outside [0,1] or NaN, w_heads not in {1,H}, an
  *    unknown layout, alpha mode, output dtype or low-bit mode);
  *    SLA2_EUNSUPPORTED (a valid but unbuilt combination: d not in {64,128},
- *    bq not in {64,128}, bkv != 64, phi softmax outside its path, fp8 with fp32
- *    inputs or with bq or d other than 128, more than 65535 heads or a number of blocks outside the limits
- *    below); SLA2_EWORKSPACE (ws_bytes smaller than sla2_workspace_bytes);
+ *    bq not in {64,128}, bkv != 64, phi softmax with the low-bit forward or
+ *    the backward, fp8 with fp32 inputs or with bq or d other than 128, more
+ *    than 65535 heads or a number of blocks outside the limits below); SLA2_EWORKSPACE (ws_bytes smaller than sla2_workspace_bytes);
  *    SLA2_EHIP (a HIP launch error, reported right after the launch;
  *    asynchronous faults surface at the caller's next synchronisation).
  *  - Device-resident values are not inspected: Q, K, V must be finite, alpha
@@ -72,9 +72,10 @@ typedef enum {
 typedef enum { SLA2_F32 = 0, SLA2_BF16 = 1 } sla2_dtype;
 
 /* feature map of the linear branch: elu(x) + 1, elementwise on raw Q and K,
- * or the softmax of each raw Q or K row over its d channels (the SLA notes'
- * training section picks softmax; SLA2_PHI_SOFTMAX needs bf16, d = 128 and
- * bq = 128, and is not taken by sla2_forward_fp8) */
+ * or the softmax of each raw Q or K row over its d channels, max-subtracted
+ * (the SLA notes' training section picks softmax).  SLA2_PHI_SOFTMAX is taken
+ * by every forward shape (sla2_forward, sla2_attention, sla1_forward), not by
+ * sla2_forward_fp8, sla2_attention_fp8 or sla2_backward. */
 typedef enum { SLA2_PHI_ELU1 = 0, SLA2_PHI_SOFTMAX = 1 } sla2_phi;
 
 /* memory layout of Q, K, V and O */
@@ -175,8 +176,11 @@ sla2_status sla2_route(const sla2_problem* p, const void* Q, const void* K,
  *        blocks ("SLA2 深度解读" 04, 08); O_s = 0 when k = 0.
  *   O_l: phi(Q_t) H_i / (phi(Q_t) . Z_i), H_i = sum over unselected blocks of
  *        h_j = phi(K_j)^T V_j, Z_i = sum of z_j = colsum phi(K_j) (SLA notes,
- *        key design 3 and 4); evaluated as (total - selected); O_l = 0 when
- *        k = T_kv.
+ *        key design 3 and 4); O_l = 0 when k = T_kv.  On the bf16 d = 128,
+ *        bq = 128 path the sums run over the unselected blocks directly (a
+ *        dense product of the 0/1 matrix of unselected blocks with the
+ *        per-block summaries); elsewhere they are the head totals minus the
+ *        selected blocks.
  *   O   = alpha O_s + (1 - alpha) O_l, written for the N valid rows; alpha is
  *        that of the row's head (and query block, with SLA2_ALPHA_PER_QBLOCK).
  * In : Q, K, V in problem.layout; topk_idx [B,H,T_q,k] from sla2_route
@@ -186,10 +190,17 @@ sla2_status sla2_route(const sla2_problem* p, const void* Q, const void* K,
  *      computed in fp32 and rounded to nearest even once).
  * ws : sla2_workspace_bytes(p, SLA2_OP_FORWARD) bytes.
  * Precision: fp32 inputs are computed in fp32 throughout (vector ALU), and
- * so are bf16 inputs with bq = 64.  bf16 inputs with bq = 128: Q K^T
- * on bf16 matrix cores with fp32 accumulation, P rounded to fp16 for P V
- * (V converted to fp16, exact for |V| < 65504 apart from fp16 subnormals),
- * phi(K) and V in fp16 for the block summaries, fp32 everywhere else.
+ * so are bf16 inputs with bq = 64.  bf16 inputs with bq = 128: Q K^T on bf16
+ * matrix cores with fp32 accumulation, P rounded to fp16 for P V (V
+ * converted to fp16, exact for |V| < 65504 apart from fp16 subnormals), each
+ * block summary h_j = phi(K_j)^T V_j on fp16 matrix cores (phi(K_j) and V_j
+ * in fp16, fp32 accumulation).  With d = 128 the summaries h_j, z_j are then
+ * rounded to bf16, summed on bf16 matrix cores with fp32 accumulation, H_i
+ * rounded to bf16 (Z_i kept in fp32), and phi(Q) . H_i taken on bf16 matrix
+ * cores with phi(Q) rounded to bf16 (also in the denominator); with d = 64
+ * H_i is formed in fp32 and enters phi(Q) H_i in fp16 (scaled by a power of
+ * two).  Everything else is fp32.  Bound reached in the tests: 2e-3 max-abs
+ * against an fp64 evaluation of the same definition.
  */
 sla2_status sla2_forward(const sla2_problem* p, const void* Q, const void* K,
                          const void* V, const int32_t* topk_idx, const float* alpha,
@@ -354,7 +365,9 @@ const char* sla2_kernel_name(int32_t kind);
  *   query block that does not select it (evaluated as the head's total
  *   minus the selecting query blocks); dalpha = sum of dO . (O_s - O_l) over
  *   the rows alpha applies to.  phi must be elu + 1 (SLA2_EUNSUPPORTED
- *   otherwise).  Vector-ALU fp32 arithmetic for every dtype, d and bq.
+ *   otherwise).  bf16 inputs with d = bq = 128 run on the matrix cores
+ *   (bf16 / fp16 operands as in sla2_forward's bf16 path, fp32
+ *   accumulation); every other shape in fp32 on the vector ALU.
  * In : Q, K, V, topk_idx, alpha as sla2_forward; dO fp32 in problem.layout.
  * Out: dQ, dK, dV fp32 in problem.layout; dalpha [H] or [H][T_q] fp32
  *      (problem.alpha_mode).  All overwritten.
@@ -443,25 +456,27 @@ sla2_status sla1_route(const sla2_problem* p, const void* Q, const void* K, floa
                        size_t ws_bytes, void* stream);
 
 /*
- * sla1_forward -- SLA (v1) forward.  Requires dtype == SLA2_BF16, d == 128
- * and bq == 128 (SLA2_EUNSUPPORTED otherwise; the notes run v1 with b_q =
- * 64, this build's matrix-core kernel tiles 128 queries).
+ * sla1_forward -- SLA (v1) forward.  Takes the shapes sla2_forward takes:
+ * bf16 with d = bq = 128 on the matrix cores; bq = 64 (the notes' b_q = b_kv
+ * = 64), d = 64 or fp32 inputs on the vector ALU in fp32.
  *   O_s: the sparse branch of sla2_forward over the critical blocks.
  *   O_l: phi(Q_t) H_i / (phi(Q_t) . Z_i) with H_i, Z_i summed over the
- *        marginal blocks (neither critical nor negligible), evaluated as the
- *        totals minus the critical and the negligible blocks; O_l = 0 when no
- *        block is marginal.
+ *        marginal blocks (neither critical nor negligible): directly on the
+ *        matrix-core path, as the totals minus the critical and the
+ *        negligible blocks on the vector ALU; O_l = 0 when no block is
+ *        marginal.
  *   O  = O_s + O_l W_p[h'] (Proj(x) = x W_p, W_p row-major [d][d], no bias;
- *        h' = 0 if w_heads == 1, else h).  O_l enters the projection on the
- *        fp16 matrix cores as the sum of two fp16 terms (high part + rest),
- *        W_p rounded to fp16.
+ *        h' = 0 if w_heads == 1, else h).  On the matrix-core path O_l enters
+ *        the projection on the fp16 matrix cores as the sum of two fp16 terms
+ *        (high part + rest), W_p rounded to fp16; fp32 on the vector ALU.
  * In : Q, K, V (dtype, problem.layout); crit_idx / negl_idx from sla1_route
  *      (ascending rows; NULL allowed when the count is 0); Wp [w_heads,d,d]
  *      fp32.
  * Out: O in problem.layout, fp32 or bf16 (problem.out_dtype).
  * ws : sla2_workspace_bytes(p, SLA2_OP_SLA1_FORWARD) bytes.
- * Precision as sla2_forward's bf16 path; phi = softmax is evaluated in fp32
- * (max-subtracted) and carried in fp16.
+ * Precision as sla2_forward's path for the same shape; phi = softmax is
+ * evaluated in fp32 (max-subtracted), and carried in fp16 on the matrix-core
+ * path.
  */
 sla2_status sla1_forward(const sla2_problem* p, const void* Q, const void* K, const void* V,
                          const int32_t* crit_idx, const int32_t* negl_idx, float low_frac,

@@ -12,10 +12,11 @@
 // when only a few blocks are left out.
 //
 // unsel_kernel writes U as bits from the selected indices (and, for SLA v1,
-// the negligible ones, which leave the linear branch as well).  lin_gemm_kernel multiplies it with the per-block
-// summaries written by the block-summaries pass (bf16 rows of h_j^T, then
-// z_j) on the bf16 matrix cores (32x32x16, fp32 accumulation) into fp32
-// rows of H_i^T and Z_i that the fused kernel's epilogue reads.
+// the negligible ones, which leave the linear branch as well).
+// lin_gemm_kernel multiplies it with the per-block summaries written by the
+// block-summaries pass (bf16 rows of h_j^T, then z_j) on the bf16 matrix
+// cores (32x32x16, fp32 accumulation) into rows of H_i^T (rounded to bf16)
+// and Z_i (fp32) that the fused kernel's epilogue reads.
 //
 // Product tiles: 320 query blocks x 128 columns per work-group of 4 waves
 // (2 x 2: each wave 5 x 2 tiles of 32 x 32, 160 rows x 64 columns), 64 KV

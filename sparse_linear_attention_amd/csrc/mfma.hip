@@ -434,7 +434,35 @@ __global__ __launch_bounds__(256, 2) void fused_mfma_kernel(
         __syncthreads();
         char* sH = smem;                               // [D][kHPitch] fp16, H^T[e][c]
         float* sZ = reinterpret_cast<float*>(smem + D * SM::kHPitch);
+        float* sM = sZ + D;                            // per-wave max |H| entry
+        static_assert(SM::kEpi + 16 <= SM::kBytes, "epilogue LDS");
         const float* hT = htot + (size_t)bh * D * D;   // h[c][e]
+        // H^T = h_tot^T - G^T goes to fp16 scaled by a power of two that puts
+        // its largest entry in [2^13, 2^14): |H| grows with the number of
+        // tokens left out and with the mean of V, past the fp16 range at
+        // long sequences; the scale is undone after the product (exactly)
+        if (w < NT) {
+            const int c = 32 * nt_w + l32;
+            float hmax = 0.0f;
+#pragma unroll
+            for (int mt = 0; mt < NT; ++mt)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int e = 32 * mt + 8 * (i >> 2) + 4 * hl + (i & 3);
+                    hmax = fmaxf(hmax, fabsf(hT[(size_t)c * D + e] - g[mt][i]));
+                }
+#pragma unroll
+            for (int off = 32; off >= 1; off >>= 1) hmax = fmaxf(hmax, __shfl_xor(hmax, off));
+            if (lane == 0) sM[w] = hmax;
+        }
+        __syncthreads();
+        float hmx = sM[0];
+#pragma unroll
+        for (int i = 1; i < NT; ++i) hmx = fmaxf(hmx, sM[i]);
+        int hex = 0;
+        (void)frexpf(hmx, &hex);  // hmx = f 2^hex, f in [0.5, 1)
+        const int sexp = hmx > 0.0f ? min(max(14 - hex, -100), 100) : 0;
+        const float hs = ldexpf(1.0f, sexp), his = ldexpf(1.0f, -sexp);
         if (w < NT) {
             const int c = 32 * nt_w + l32;
 #pragma unroll
@@ -442,7 +470,7 @@ __global__ __launch_bounds__(256, 2) void fused_mfma_kernel(
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
                     const int e = 32 * mt + 8 * (i >> 2) + 4 * hl + (i & 3);
-                    const float hv = hT[(size_t)c * D + e] - g[mt][i];
+                    const float hv = (hT[(size_t)c * D + e] - g[mt][i]) * hs;
                     *reinterpret_cast<_Float16*>(sH + e * SM::kHPitch + c * 2) = (_Float16)hv;
                 }
         }
@@ -470,7 +498,7 @@ __global__ __launch_bounds__(256, 2) void fused_mfma_kernel(
             }
         }
         den += __shfl_xor(den, 32);
-        inv_den = 1.0f / den;
+        inv_den = (1.0f / den) * his;
         // O_l^T = H^T phi(Q)^T
 #pragma unroll
         for (int mt = 0; mt < NT; ++mt)

@@ -47,13 +47,12 @@ static sla2_status make_dims(const sla2_problem* p, int op, Dims* D) {
     if (p->phi != SLA2_PHI_ELU1 && p->phi != SLA2_PHI_SOFTMAX) return SLA2_EUNSUPPORTED;
     const bool fast = p->dtype == SLA2_BF16 && p->bq == 128 && p->d == 128;
     const bool lowbit_op = op == SLA2_OP_FORWARD_FP8 || op == SLA2_OP_ATTENTION_FP8;
-    if ((lowbit_op || op == SLA2_OP_SLA1_FORWARD) && !fast) return SLA2_EUNSUPPORTED;
-    // softmax phi: the bf16 d = 128, bq = 128 kernels only (routing ignores phi)
+    if (lowbit_op && !fast) return SLA2_EUNSUPPORTED;
     const bool routing = op == SLA2_OP_ROUTE || op == SLA2_OP_ROUTE_GRAD;
-    // the backward takes elu + 1 only
+    // the backward takes elu + 1 only; the low-bit kernels too (routing
+    // ignores phi)
     if (op == SLA2_OP_BACKWARD && p->phi != SLA2_PHI_ELU1) return SLA2_EUNSUPPORTED;
-    if (p->phi == SLA2_PHI_SOFTMAX && (lowbit_op || (!routing && !fast)))
-        return SLA2_EUNSUPPORTED;
+    if (p->phi == SLA2_PHI_SOFTMAX && lowbit_op) return SLA2_EUNSUPPORTED;
     long bh = (long)p->B * p->H;
     if (bh > 65535) return SLA2_EUNSUPPORTED;
     D->B = p->B;
@@ -379,7 +378,7 @@ SLA2_API sla2_status sla2_forward(const sla2_problem* p, const void* Q, const vo
     if (st != SLA2_OK) return st;
     hipStream_t s = (hipStream_t)stream;
     hipError_t e;
-    if (D.dtype == SLA2_F32 || D.bq != 128) {
+    if (valu_path(D)) {
         e = launch_forward_valu(D, Q, K, V, topk_idx, alpha, O, w, s);
     } else {
         e = launch_summaries_mfma(D, K, V, w, s);
@@ -452,7 +451,7 @@ SLA2_API sla2_status sla2_attention(const sla2_problem* p, const void* Q, const 
     layout_forward(D, SLA2_OP_FORWARD, (char*)ws + roff, &fw);
     hipStream_t s = (hipStream_t)stream;
     hipError_t e;
-    if (D.dtype == SLA2_F32 || D.bq != 128) {  // vector-ALU path: in sequence
+    if (valu_path(D)) {  // vector-ALU path: in sequence
         e = launch_route(D, Q, K, Wq, Wk, topk_idx, nullptr, rw, s);
         if (e == hipSuccess) e = launch_forward_valu(D, Q, K, V, topk_idx, alpha, O, fw, s);
         return e == hipSuccess ? SLA2_OK : SLA2_EHIP;
@@ -532,7 +531,7 @@ SLA2_API sla2_status sla2_attention_noalloc(const sla2_problem* p, const void* Q
     hipStream_t s = (hipStream_t)stream;
     hipError_t e = launch_route(D, Q, K, Wq, Wk, topk_idx, nullptr, rw, s);
     if (e == hipSuccess) {
-        if (D.dtype == SLA2_F32 || D.bq != 128) {
+        if (valu_path(D)) {
             e = launch_forward_valu(D, Q, K, V, topk_idx, alpha, O, fw, s);
         } else {
             e = launch_summaries_mfma(D, K, V, fw, s);
@@ -692,6 +691,10 @@ SLA2_API sla2_status sla1_forward(const sla2_problem* p, const void* Q, const vo
     FwdWS w;
     layout_forward(D, SLA2_OP_SLA1_FORWARD, (char*)ws, &w);
     hipStream_t s = (hipStream_t)stream;
+    if (!hz_path(D)) {  // fp32, b_q = 64 or d = 64: the vector-ALU kernels
+        hipError_t e = launch_forward_valu(D, Q, K, V, crit_idx, nullptr, O, w, s, negl_idx, Wp);
+        return e == hipSuccess ? SLA2_OK : SLA2_EHIP;
+    }
     hipError_t e = launch_summaries_mfma(D, K, V, w, s);
     if (e == hipSuccess) e = launch_wp_frag(D, Wp, w, s);
     if (e == hipSuccess) e = linear_product(D, crit_idx, negl_idx, D.kl, w, s);

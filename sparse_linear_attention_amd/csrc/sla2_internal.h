@@ -115,6 +115,11 @@ constexpr int kHzRowBytes = 128 * 128 * 2 + 128 * 4;
 constexpr int kHzPitch = 65 * 256;        // bf16 elements per summaries row
 constexpr int kGemmM = 320;               // query blocks per product tile
 inline bool hz_path(const Dims& D) { return D.dtype == SLA2_BF16 && D.d == 128 && D.bq == 128; }
+// forward on the vector-ALU kernels: fp32 inputs, b_q = 64, or d = 64 with
+// the softmax feature map (the d = 64 matrix-core kernel takes elu + 1 only)
+inline bool valu_path(const Dims& D) {
+    return D.dtype == SLA2_F32 || D.bq != 128 || (D.d != 128 && D.phi_sm);
+}
 // KV blocks of U: Tkv rounded up to a multiple of 64 (one k-step of the product)
 inline int tkv_pad(const Dims& D) { return (D.Tkv + 63) & ~63; }
 // rows of U per head and k-step: whole product tiles plus a 64-row tail (the
@@ -246,10 +251,12 @@ hipError_t launch_route_grad(const Dims& D, const void* Q, const void* K, const 
 hipError_t launch_route_v1(const Dims& D, const void* Q, const void* K, int kl, int32_t* crit,
                            int32_t* negl, uint8_t* mask, const RouteWS& ws, hipStream_t s);
 
-// fp32 path: VALU block summaries + VALU fused kernel
+// vector-ALU path (fp32 inputs, b_q = 64, d = 64): block summaries + fused
+// kernel; with D.v1, negl [BH][Tq][D.kl] and Wp [w_heads][d][d] (alpha unused)
 hipError_t launch_forward_valu(const Dims& D, const void* Q, const void* K, const void* V,
                                const int32_t* idx, const float* alpha, void* O,
-                               const FwdWS& ws, hipStream_t s);
+                               const FwdWS& ws, hipStream_t s, const int32_t* negl = nullptr,
+                               const float* Wp = nullptr);
 
 // fp32 block summaries (h_tot, z_tot via the chunk partials)
 hipError_t launch_summaries_valu(const Dims& D, const void* K, const void* V, const FwdWS& ws,

@@ -77,18 +77,21 @@ def test_fp8_needs_bf16_and_bq128():
     assert S.check(p_ok(dtype=S.F32), S.OP_FORWARD_FP8) == S.EUNSUPPORTED
     assert S.check(p_ok(bq=64), S.OP_FORWARD_FP8) == S.EUNSUPPORTED
     assert S.check(p_ok(), S.OP_FORWARD_FP8) == S.OK
-    # softmax phi: the bf16, d = 128, bq = 128 kernels only (routing ignores phi)
+    # softmax phi: every forward shape; not the low-bit kernels nor the
+    # backward (routing ignores phi)
     assert S.check(p_ok(phi=S.PHI_SOFTMAX), S.OP_FORWARD) == S.OK
     assert S.check(p_ok(phi=S.PHI_SOFTMAX), S.OP_ROUTE) == S.OK
-    assert S.check(p_ok(phi=S.PHI_SOFTMAX, dtype=S.F32), S.OP_FORWARD) == S.EUNSUPPORTED
-    assert S.check(p_ok(phi=S.PHI_SOFTMAX, d=64), S.OP_FORWARD) == S.EUNSUPPORTED
+    for kw in (dict(dtype=S.F32), dict(d=64), dict(bq=64)):
+        assert S.check(p_ok(phi=S.PHI_SOFTMAX, **kw), S.OP_FORWARD) == S.OK
+        assert S.check(p_ok(phi=S.PHI_SOFTMAX, **kw), S.OP_ATTENTION) == S.OK
     assert S.check(p_ok(phi=S.PHI_SOFTMAX), S.OP_FORWARD_FP8) == S.EUNSUPPORTED
     assert S.check(p_ok(phi=2), S.OP_FORWARD) == S.EUNSUPPORTED
 
 
 def test_sla1_counts_and_checks(orc):
-    """k_l as the oracle counts it; v1 forward needs the bf16 d = 128 bq = 128
-    path; its workspace adds the W_p fragments (32 KB per projection)."""
+    """k_l as the oracle counts it; the v1 forward takes every shape the SLA2
+    forward takes; its workspace adds the W_p fragments (32 KB per
+    projection)."""
     for N, kh, low in ((32760, 0.05, 0.10), (75600, 0.05, 0.10), (640, 0.7, 0.5), (640, 1.0, 0.3),
                        (640, 0.0, 0.0), (1000, 0.2, 0.33)):
         p = p_ok(N=N, topk_frac=kh)
@@ -97,8 +100,9 @@ def test_sla1_counts_and_checks(orc):
     assert S.num_negligible(p_ok(), -0.1) == -1 and S.num_negligible(p_ok(), float("nan")) == -1
     assert S.num_negligible(p_ok(B=0), 0.1) == -1
     assert S.check(p_ok(), S.OP_SLA1_FORWARD) == S.OK
-    for kw in (dict(dtype=S.F32), dict(bq=64), dict(d=64)):
-        assert S.check(p_ok(**kw), S.OP_SLA1_FORWARD) == S.EUNSUPPORTED
+    for kw in (dict(dtype=S.F32), dict(bq=64), dict(d=64), dict(bq=64, phi=S.PHI_SOFTMAX)):
+        assert S.check(p_ok(**kw), S.OP_SLA1_FORWARD) == S.OK
+    assert S.check(p_ok(bkv=128), S.OP_SLA1_FORWARD) == S.EUNSUPPORTED
     assert S.check(p_ok(), S.OP_ROUTE_GRAD) == S.OK
     assert S.check(p_ok(), S.OP_BACKWARD) == S.OK
     assert S.check(p_ok(dtype=S.F32, d=64, bq=64), S.OP_BACKWARD) == S.OK
@@ -192,7 +196,8 @@ def test_entry_points_validate_before_launching():
                           good, v1w, None) == S.EINVAL  # no W_p
     assert L.sla1_forward(C.byref(p), good, good, good, good, good, C.c_float(0.1), good, good,
                           good, fw, None) == S.EWORKSPACE
-    assert L.sla1_forward(C.byref(pf), good, good, good, good, good, C.c_float(0.1), good, good,
+    pu = p_ok(d=96)
+    assert L.sla1_forward(C.byref(pu), good, good, good, good, good, C.c_float(0.1), good, good,
                           good, v1w, None) == S.EUNSUPPORTED
     # backward
     bw = S.workspace_bytes(p, S.OP_BACKWARD)
