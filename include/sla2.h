@@ -36,9 +36,9 @@
  *    B/H/N <= 0, topk_frac outside [0,1] or NaN, w_heads not in {1,H}, an
  *    unknown layout, alpha mode, output dtype or low-bit mode);
  *    SLA2_EUNSUPPORTED (a valid but unbuilt combination: d not in {64,128},
- *    bq not in {64,128}, bkv != 64, phi softmax with the low-bit forward or
- *    the backward, fp8 with fp32 inputs or with bq or d other than 128, more
- *    than 65535 heads or a number of blocks outside the limits below); SLA2_EWORKSPACE (ws_bytes smaller than sla2_workspace_bytes);
+ *    bq not in {64,128}, bkv != 64, phi softmax with the low-bit forward,
+ *    fp8 with fp32 inputs or with bq or d other than 128, more than 65535
+ *    heads or a number of blocks outside the limits below); SLA2_EWORKSPACE (ws_bytes smaller than sla2_workspace_bytes);
  *    SLA2_EHIP (a HIP launch error, reported right after the launch;
  *    asynchronous faults surface at the caller's next synchronisation).
  *  - Device-resident values are not inspected: Q, K, V must be finite, alpha
@@ -75,7 +75,7 @@ typedef enum { SLA2_F32 = 0, SLA2_BF16 = 1 } sla2_dtype;
  * or the softmax of each raw Q or K row over its d channels, max-subtracted
  * (the SLA notes' training section picks softmax).  SLA2_PHI_SOFTMAX is taken
  * by every forward shape (sla2_forward, sla2_attention, sla1_forward), not by
- * sla2_forward_fp8, sla2_attention_fp8 or sla2_backward. */
+ * sla2_forward_fp8 or sla2_attention_fp8. */
 typedef enum { SLA2_PHI_ELU1 = 0, SLA2_PHI_SOFTMAX = 1 } sla2_phi;
 
 /* memory layout of Q, K, V and O */
@@ -364,10 +364,12 @@ const char* sla2_kernel_name(int32_t kind);
  *   so that each block summary h_j, z_j collects the gradients of every
  *   query block that does not select it (evaluated as the head's total
  *   minus the selecting query blocks); dalpha = sum of dO . (O_s - O_l) over
- *   the rows alpha applies to.  phi must be elu + 1 (SLA2_EUNSUPPORTED
- *   otherwise).  bf16 inputs with d = bq = 128 run on the matrix cores
- *   (bf16 / fp16 operands as in sla2_forward's bf16 path, fp32
- *   accumulation); every other shape in fp32 on the vector ALU.
+ *   the rows alpha applies to.  Through phi (SLA notes, key design 4):
+ *   dx = dphi * phi'(x) for elu + 1; for the row softmax p = phi(x), dx =
+ *   p * (dphi - p . dphi).  bf16 inputs with d = bq = 128 and phi = elu + 1
+ *   run on the matrix cores (bf16 / fp16 operands as in sla2_forward's bf16
+ *   path, fp32 accumulation); every other problem (softmax phi included) in
+ *   fp32 on the vector ALU.
  * In : Q, K, V, topk_idx, alpha as sla2_forward; dO fp32 in problem.layout.
  * Out: dQ, dK, dV fp32 in problem.layout; dalpha [H] or [H][T_q] fp32
  *      (problem.alpha_mode).  All overwritten.

@@ -1,7 +1,7 @@
 // Backward of the SLA2 forward with the hard selection held fixed, vector-ALU
-// form (fp32 arithmetic; phi = elu + 1) for the problems the matrix-core
-// backward (backward_mfma.hip: bf16 with d = b_q = 128) does not take: fp32
-// inputs, d = 64 or b_q = 64.  L = sum dO . O with O = alpha O_s + (1 -
+// form (fp32 arithmetic) for the problems the matrix-core backward
+// (backward_mfma.hip: bf16 with d = b_q = 128, phi = elu + 1) does not take:
+// fp32 inputs, d = 64, b_q = 64, or phi = the softmax of each row.  L = sum dO . O with O = alpha O_s + (1 -
 // alpha) O_l ("SLA2 深度解读" 04; the SLA notes' key designs 3 and 4 for O_l).
 //
 // Per query row t of block i, with g = dO_t, gs = alpha g, e = (1 - alpha) g:
@@ -18,6 +18,9 @@
 //           dphi(k_u) += dH_tot v_u + dZ_tot with dH_tot = sum_t phi(q_t)^T
 //           dn_t, dZ_tot = sum_t phi(q_t) ds_t over the whole head;
 //   dalpha  sum over its rows of g . (O_s - O_l).
+// Through phi (SLA notes, key design 4: the backward runs through the feature
+// map): dx = dphi * phi'(x) for elu + 1; for the row softmax p = phi(x),
+// dx = p * (dphi - p . dphi).
 // Kernels: block summaries (h_tot, z_tot) as the fp32 forward; a query-row
 // pass (dQ and the per-row values the key pass needs); dH_tot, dZ_tot; the
 // selection inverted per KV block; a key pass over the query blocks that
@@ -47,6 +50,53 @@ __device__ inline float row8(float v) {
     v += dpp_mov<0x141>(v);
     return v;
 }
+__device__ inline float row8max(float v) {
+    v = fmaxf(v, dpp_mov<0xB1>(v));
+    v = fmaxf(v, dpp_mov<0x4E>(v));
+    v = fmaxf(v, dpp_mov<0x141>(v));
+    return v;
+}
+
+// phi of one row held by the 8 lanes of a group (CS channels each, any
+// assignment of channels to lanes): elu + 1, or the softmax over the row
+__device__ inline void phi_row(const float* x, float* y, int CS, int sm) {
+    if (!sm) {
+#pragma unroll
+        for (int c = 0; c < 16; ++c) y[c] = phi_e(x[c]);
+        return;
+    }
+    float m = -INFINITY;
+#pragma unroll
+    for (int c = 0; c < 16; ++c)
+        if (c < CS) m = fmaxf(m, x[c]);
+    m = row8max(m);
+    float sum = 0.0f;
+#pragma unroll
+    for (int c = 0; c < 16; ++c) {
+        y[c] = c < CS ? __expf(x[c] - m) : 0.0f;
+        sum += y[c];
+    }
+    const float inv = 1.0f / row8(sum);
+#pragma unroll
+    for (int c = 0; c < 16; ++c) y[c] *= inv;
+}
+
+// dx from dphi through phi at x (y = phi(x)), row held as in phi_row
+__device__ inline void dphi_row(const float* x, const float* y, const float* g, float* dx,
+                                int CS, int sm) {
+    if (!sm) {
+#pragma unroll
+        for (int c = 0; c < 16; ++c) dx[c] = g[c] * dphi_e(x[c]);
+        return;
+    }
+    float pg = 0.0f;
+#pragma unroll
+    for (int c = 0; c < 16; ++c)
+        if (c < CS) pg = fmaf(y[c], g[c], pg);
+    pg = row8(pg);
+#pragma unroll
+    for (int c = 0; c < 16; ++c) dx[c] = y[c] * (g[c] - pg);
+}
 
 // Query rows: 32 rows per work-group, 8 threads per row; thread `sub` of a
 // row owns channels sub, sub + 8, ... (d / 8 of them), so that the 8 threads
@@ -59,7 +109,7 @@ __global__ __launch_bounds__(256) void bwd_rows_kernel(
     const float* __restrict__ ztot, float* __restrict__ dQ, float* __restrict__ lse,
     float* __restrict__ Dv, float* __restrict__ dsv, float* __restrict__ dn_out,
     float* __restrict__ da_row, int N, int d, int bq, int Tq, int Tkv, int k, int H,
-    Strides st, int alpha_qblock) {
+    Strides st, int alpha_qblock, int phi_sm) {
     __shared__ float Kt[32 * 128];
     __shared__ float Pk[32 * 128];
     __shared__ float Vt[32 * 128];
@@ -84,23 +134,30 @@ __global__ __launch_bounds__(256) void bwd_rows_kernel(
         const bool ok = c < CS && valid_q;
         q[c] = ok ? ldx(Qh + (size_t)tq * st.t + sub + 8 * c) : 0.0f;
         g[c] = ok ? dOh[(size_t)tq * st.t + sub + 8 * c] : 0.0f;
-        pq[c] = phi_e(q[c]);
         acc[c] = 0.0f;
         corr[c] = 0.0f;
     }
+    phi_row(q, pq, CS, phi_sm);
     float m = -INFINITY, l = 0.0f, zc = 0.0f;
     const int32_t* sel = idx + ((size_t)bh * Tq + qb) * k;
 
-    // stage 32 tokens (K, phi(K), V) of selected block j starting at u0
+    // stage 32 tokens (K, phi(K), V) of selected block j starting at u0;
+    // token `row` by the 8 threads of that row (phi of a whole row)
     auto stage = [&](int u0, int nu) {
-        for (int x = threadIdx.x; x < 32 * d; x += 256) {
-            const int u = x / d, c = x % d;
-            const bool ok = u < nu;
-            const float kv = ok ? ldx(Kh + (size_t)(u0 + u) * st.t + c) : 0.0f;
-            Kt[u * d + c] = kv;
-            Pk[u * d + c] = ok ? phi_e(kv) : 0.0f;
-            Vt[u * d + c] = ok ? ldx(Vh + (size_t)(u0 + u) * st.t + c) : 0.0f;
-        }
+        const bool ok = row < nu;
+        float kx[16], px[16];
+#pragma unroll
+        for (int c = 0; c < 16; ++c)
+            kx[c] = (ok && c < CS) ? ldx(Kh + (size_t)(u0 + row) * st.t + sub + 8 * c) : 0.0f;
+        phi_row(kx, px, CS, phi_sm);
+#pragma unroll
+        for (int c = 0; c < 16; ++c)
+            if (c < CS) {
+                const int x = row * d + sub + 8 * c;
+                Kt[x] = kx[c];
+                Pk[x] = ok ? px[c] : 0.0f;
+                Vt[x] = ok ? ldx(Vh + (size_t)(u0 + row) * st.t + sub + 8 * c) : 0.0f;
+            }
         __syncthreads();
     };
 
@@ -270,13 +327,15 @@ __global__ __launch_bounds__(256) void bwd_rows_kernel(
             __syncthreads();
         }
     }
+    float dqp[16];
+    dphi_row(q, pq, dph, dqp, CS, phi_sm);
     if (valid_q) {
         const size_t o = head_base(st, bh, H) + (size_t)tq * st.t + sub;
         const size_t rr = (size_t)bh * N + tq;
 #pragma unroll
         for (int c = 0; c < 16; ++c)
             if (c < CS) {
-                dQ[o + 8 * c] = dq[c] + (lin ? dph[c] * dphi_e(q[c]) : 0.0f);
+                dQ[o + 8 * c] = dq[c] + (lin ? dqp[c] : 0.0f);
                 dn_out[rr * d + sub + 8 * c] = dn[c];
             }
         if (sub == 0) {
@@ -297,7 +356,7 @@ __global__ __launch_bounds__(256) void bwd_dh_kernel(const T* __restrict__ Q,
                                                      const float* __restrict__ dsv,
                                                      float* __restrict__ hpart,
                                                      float* __restrict__ zpart, int N, int d,
-                                                     int nch, int H, Strides st) {
+                                                     int nch, int H, Strides st, int phi_sm) {
     __shared__ float pq[32 * 128];
     __shared__ float dv[32 * 128];
     __shared__ float sds[32];
@@ -316,13 +375,23 @@ __global__ __launch_bounds__(256) void bwd_dh_kernel(const T* __restrict__ Q,
 #pragma unroll
         for (int q = 0; q < 8; ++q) acc[p][q] = 0.0f;
     }
+    const int lr = threadIdx.x >> 3, lsub = threadIdx.x & 7, CS = d >> 3;
     for (int u0 = t_begin; u0 < t_end; u0 += 32) {
-        for (int x = threadIdx.x; x < 32 * d; x += 256) {
-            const int u = x / d, c = x % d;
-            const int t = u0 + u;
+        {  // row lr by the 8 threads of that row (phi of a whole row)
+            const int t = u0 + lr;
             const bool ok = t < t_end;
-            pq[u * d + c] = ok ? phi_e(ldx(Qh + (size_t)t * st.t + c)) : 0.0f;
-            dv[u * d + c] = ok ? dn[((size_t)bh * N + t) * d + c] : 0.0f;
+            float qx[16], px[16];
+#pragma unroll
+            for (int c = 0; c < 16; ++c)
+                qx[c] = (ok && c < CS) ? ldx(Qh + (size_t)t * st.t + lsub + 8 * c) : 0.0f;
+            phi_row(qx, px, CS, phi_sm);
+#pragma unroll
+            for (int c = 0; c < 16; ++c)
+                if (c < CS) {
+                    const int ch = lsub + 8 * c;
+                    pq[lr * d + ch] = ok ? px[c] : 0.0f;
+                    dv[lr * d + ch] = ok ? dn[((size_t)bh * N + t) * d + ch] : 0.0f;
+                }
         }
         if (threadIdx.x < 32) {
             const int t = u0 + threadIdx.x;
@@ -401,7 +470,7 @@ __global__ __launch_bounds__(256) void bwd_keys_kernel(
     const float* __restrict__ dn, const float* __restrict__ dHt, const float* __restrict__ dZt,
     const int32_t* __restrict__ off, const int32_t* __restrict__ list, float* __restrict__ dK,
     float* __restrict__ dV, int N, int d, int bq, int Tq, int Tkv, int k, int H, Strides st,
-    int alpha_qblock) {
+    int alpha_qblock, int phi_sm) {
     __shared__ float sQ[16 * 128];
     __shared__ float sP[16 * 128];  // phi(q)
     __shared__ float sG[16 * 128];  // alpha dO
@@ -427,11 +496,11 @@ __global__ __launch_bounds__(256) void bwd_keys_kernel(
         const bool ok = c < CS && valid_k;
         kv[c] = ok ? ldx(Kh + (size_t)u * st.t + sub + 8 * c) : 0.0f;
         vv[c] = ok ? ldx(Vh + (size_t)u * st.t + sub + 8 * c) : 0.0f;
-        pk[c] = phi_e(kv[c]);
         dk[c] = 0.0f;
         dv[c] = 0.0f;
         dph[c] = 0.0f;
     }
+    phi_row(kv, pk, CS, phi_sm);
     const int32_t* o = off + (size_t)bh * (Tkv + 1);
     const int32_t* L = list + (size_t)bh * Tq * k;
     const int n0 = k > 0 ? o[j] : 0, n1 = k > 0 ? o[j + 1] : 0;
@@ -444,11 +513,24 @@ __global__ __launch_bounds__(256) void bwd_keys_kernel(
                 const int rr = x / d, c = x % d;
                 const int t = i * bq + r0 + rr;
                 const bool ok = t < N;
-                const float qv = ok ? ldx(Qh + (size_t)t * st.t + c) : 0.0f;
-                sQ[rr * d + c] = qv;
-                sP[rr * d + c] = phi_e(qv);
                 sG[rr * d + c] = ok ? a * dOh[(size_t)t * st.t + c] : 0.0f;
                 sN[rr * d + c] = ok ? dn[((size_t)bh * N + t) * d + c] : 0.0f;
+            }
+            if (threadIdx.x < 128) {  // 16 rows of q and phi(q), 8 threads a row
+                const int rr = threadIdx.x >> 3;
+                const int t = i * bq + r0 + rr;
+                const bool ok = t < N;
+                float qx[16], px[16];
+#pragma unroll
+                for (int c = 0; c < 16; ++c)
+                    qx[c] = (ok && c < CS) ? ldx(Qh + (size_t)t * st.t + sub + 8 * c) : 0.0f;
+                phi_row(qx, px, CS, phi_sm);
+#pragma unroll
+                for (int c = 0; c < 16; ++c)
+                    if (c < CS) {
+                        sQ[rr * d + sub + 8 * c] = qx[c];
+                        sP[rr * d + sub + 8 * c] = px[c];
+                    }
             }
             if (threadIdx.x < 16) {
                 const int t = i * bq + r0 + threadIdx.x;
@@ -524,12 +606,14 @@ __global__ __launch_bounds__(256) void bwd_keys_kernel(
         for (int c = 0; c < 16; ++c)
             if (c < CS) dph[c] += Z0[sub + 8 * c];
     }
+    float dkp[16];
+    dphi_row(kv, pk, dph, dkp, CS, phi_sm);
     if (valid_k) {
         const size_t ob = head_base(st, bh, H) + (size_t)u * st.t + sub;
 #pragma unroll
         for (int c = 0; c < 16; ++c)
             if (c < CS) {
-                dK[ob + 8 * c] = dk[c] + (lin ? dph[c] * dphi_e(kv[c]) : 0.0f);
+                dK[ob + 8 * c] = dk[c] + (lin ? dkp[c] : 0.0f);
                 dV[ob + 8 * c] = dv[c];
             }
     }
@@ -594,23 +678,24 @@ hipError_t launch_backward(const Dims& D, const void* Q, const void* K, const vo
         bwd_rows_kernel<float><<<gr, 256, 0, s>>>(
             (const float*)Q, (const float*)K, (const float*)V, dO, idx, alpha, ws.htot, ws.ztot,
             dQ, bw.lse, bw.D, bw.ds, bw.dn, bw.da, D.N, D.d, D.bq, D.Tq, D.Tkv, D.k, D.H, D.st,
-            D.alpha_qblock);
+            D.alpha_qblock, D.phi_sm);
     else
         bwd_rows_kernel<uint16_t><<<gr, 256, 0, s>>>(
             (const uint16_t*)Q, (const uint16_t*)K, (const uint16_t*)V, dO, idx, alpha, ws.htot,
             ws.ztot, dQ, bw.lse, bw.D, bw.ds, bw.dn, bw.da, D.N, D.d, D.bq, D.Tq, D.Tkv, D.k, D.H,
-            D.st, D.alpha_qblock);
+            D.st, D.alpha_qblock, D.phi_sm);
     timing_after(s, K_BWD_ROWS);
     if (D.k < D.Tkv) {
         dim3 gh(nch, (unsigned)D.BH);
         timing_before(s, K_BWD_DH);
         if (f32)
             bwd_dh_kernel<float><<<gh, 256, 0, s>>>((const float*)Q, bw.dn, bw.ds, ws.hpart,
-                                                    ws.zpart, D.N, D.d, nch, D.H, D.st);
+                                                    ws.zpart, D.N, D.d, nch, D.H, D.st,
+                                                    D.phi_sm);
         else
             bwd_dh_kernel<uint16_t><<<gh, 256, 0, s>>>((const uint16_t*)Q, bw.dn, bw.ds,
                                                        ws.hpart, ws.zpart, D.N, D.d, nch, D.H,
-                                                       D.st);
+                                                       D.st, D.phi_sm);
         timing_after(s, K_BWD_DH);
         // reduce into dH_tot / dZ_tot (the forward's totals are no longer needed)
         FwdWS r = ws;
@@ -629,12 +714,12 @@ hipError_t launch_backward(const Dims& D, const void* Q, const void* K, const vo
         bwd_keys_kernel<float><<<gk, 256, 0, s>>>(
             (const float*)Q, (const float*)K, (const float*)V, dO, alpha, bw.lse, bw.D, bw.ds,
             bw.dn, bw.dHt, bw.dZt, bw.off, bw.list, dK, dV, D.N, D.d, D.bq, D.Tq, D.Tkv, D.k, D.H,
-            D.st, D.alpha_qblock);
+            D.st, D.alpha_qblock, D.phi_sm);
     else
         bwd_keys_kernel<uint16_t><<<gk, 256, 0, s>>>(
             (const uint16_t*)Q, (const uint16_t*)K, (const uint16_t*)V, dO, alpha, bw.lse, bw.D,
             bw.ds, bw.dn, bw.dHt, bw.dZt, bw.off, bw.list, dK, dV, D.N, D.d, D.bq, D.Tq, D.Tkv,
-            D.k, D.H, D.st, D.alpha_qblock);
+            D.k, D.H, D.st, D.alpha_qblock, D.phi_sm);
     timing_after(s, K_BWD_KEYS);
     e = hipGetLastError();
     if (e != hipSuccess) return e;

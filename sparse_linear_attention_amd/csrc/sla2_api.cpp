@@ -49,9 +49,7 @@ static sla2_status make_dims(const sla2_problem* p, int op, Dims* D) {
     const bool lowbit_op = op == SLA2_OP_FORWARD_FP8 || op == SLA2_OP_ATTENTION_FP8;
     if (lowbit_op && !fast) return SLA2_EUNSUPPORTED;
     const bool routing = op == SLA2_OP_ROUTE || op == SLA2_OP_ROUTE_GRAD;
-    // the backward takes elu + 1 only; the low-bit kernels too (routing
-    // ignores phi)
-    if (op == SLA2_OP_BACKWARD && p->phi != SLA2_PHI_ELU1) return SLA2_EUNSUPPORTED;
+    // the low-bit kernels take elu + 1 only (routing ignores phi)
     if (p->phi == SLA2_PHI_SOFTMAX && lowbit_op) return SLA2_EUNSUPPORTED;
     long bh = (long)p->B * p->H;
     if (bh > 65535) return SLA2_EUNSUPPORTED;

@@ -206,9 +206,13 @@ def test_entry_points_validate_before_launching():
                            good, good, bw, None) == S.EINVAL  # no dO
     assert L.sla2_backward(C.byref(p), good, good, good, good, good, good, good, good, good,
                            good, good, bw - 256, None) == S.EWORKSPACE
+    # softmax phi: the vector-ALU backward at every shape (its own workspace)
     psm = p_ok(phi=S.PHI_SOFTMAX)
+    assert S.check(psm, S.OP_BACKWARD) == S.OK
+    bsm = S.workspace_bytes(psm, S.OP_BACKWARD)
+    assert bsm > 0 and bsm != bw
     assert L.sla2_backward(C.byref(psm), good, good, good, good, good, good, good, good, good,
-                           good, good, bw, None) == S.EUNSUPPORTED
+                           good, good, bsm - 256, None) == S.EWORKSPACE
     # training-time router
     assert L.sla2_soft_topk(C.byref(p), good, good, good, good, C.c_float(0.0), good, None, good,
                             ws_need, None) == S.EINVAL  # tau must be > 0

@@ -153,3 +153,39 @@ def test_backward_ignores_workspace_contents(dev, dtype, bq, frac):
         torch.cuda.synchronize()
     for a, b in zip(*outs):
         assert torch.equal(a, b)
+
+
+SOFTMAX_CASES = [  # name, dtype, N, H, d, bq, frac
+    ("bf16-d128-bq128", "bf16", 1300, 2, 128, 128, 0.15),
+    ("bf16-d128-bq64", "bf16", 900, 2, 128, 64, 0.25),
+    ("f32-d64-bq64", "f32", 700, 2, 64, 64, 0.2),
+    ("bf16-k0", "bf16", 640, 2, 128, 128, 0.0),
+    ("f32-all-selected", "f32", 500, 2, 64, 64, 1.0),
+]
+
+
+@pytest.mark.parametrize("case", SOFTMAX_CASES, ids=[c[0] for c in SOFTMAX_CASES])
+def test_backward_softmax_phi(orc, dev, case):
+    """phi = the softmax of each row (the SLA notes' training choice): the
+    gradients run through the row softmax's Jacobian, dx = p (dphi - p .
+    dphi), on the vector-ALU kernels; against the oracle's backward, whose
+    softmax-phi derivative is pinned to torch autograd on the CPU."""
+    name, dtype, N, H, d, bq, frac = case
+    say(f"case backward softmax phi {name}: N={N} H={H} d={d} bq={bq} frac={frac}")
+    gen = "centroids" if dtype == "f32" else "smooth"
+    w = I.Workload(name, 1, H, N, d, bq, 64, frac, dtype, gen, seed=17)
+    x = I.make_inputs(w)
+    rng = np.random.default_rng(12)
+    dO = rng.normal(0, 1, (1, H, N, d)).astype(np.float32)
+    q, k, v, wq, wk, al = to_dev(x, dev)
+    p = S.problem(1, H, N, d, bq, 64, frac, 1, dtype, phi=S.PHI_SOFTMAX)
+    idx, _ = S.route(p, q, k, wq, wk, want_mask=False)
+    dQ, dK, dV, da = S.backward(p, q, k, v, idx, al, torch.from_numpy(dO).to(dev))
+    torch.cuda.synchronize()
+    op = orc.problem(1, H, N, d, bq, 64, frac, 1, dtype, phi=1)
+    rQ, rK, rV, ra = orc.backward(op, x.q, x.k, x.v, idx.cpu().numpy(), x.alpha,
+                                  dO.astype(np.float64))
+    _check("dQ", dQ.cpu().numpy(), rQ)
+    _check("dK", dK.cpu().numpy(), rK)
+    _check("dV", dV.cpu().numpy(), rV)
+    _check("dalpha", da.cpu().numpy(), ra)
