@@ -27,7 +27,10 @@ runs while the kernel source is unchanged; --traffic-table FETCH WRITE
 COPY_FETCH COPY_WRITE prints the same scaled traffic, the mean dispatch
 time and the achieved GB/s for every kernel in those folders;
 --counter-table DIR prints every counter's mean per dispatch and the mean
-dispatch time for every kernel in one rocprofv3 --pmc folder.
+dispatch time for every kernel in one rocprofv3 --pmc folder; --peaks
+measures the attainable HBM and matrix-core rates of this GPU with plain
+library kernels (the measured peaks the roofline fractions are set against,
+beside the datasheet's).
 """
 from __future__ import annotations
 
@@ -131,6 +134,63 @@ def copy_calibration():
         y.copy_(x)
     torch.cuda.synchronize()
     print(json.dumps({"copy_calibration_bytes": n, "launches": 3}))
+
+
+def measured_peaks():
+    """Attainable rates of this GPU: HBM by a 4 GiB device-to-device copy
+    (read + write counted) and by a read-only sum over 4 GiB; the dense bf16
+    matrix cores by an 8192^3 product (torch.mm on contiguous operands, i.e.
+    the vendor GEMM library); the matrix-core instruction rate itself (bf16
+    32x32x16 and e4m3 32x32x64, no memory traffic) by the library's
+    sla2_mfma_rate_probe.  Mean of 10 (copy, sum), 20 (product) or 5 (probe)
+    launches after one warm-up."""
+    import torch
+
+    def timeit(fn, n):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(n):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n
+
+    res = {}
+    n = 4 << 30
+    x = torch.empty(n, dtype=torch.uint8, device="cuda")
+    y = torch.empty_like(x)
+    x.fill_(1)
+    ms = timeit(lambda: y.copy_(x), 10)
+    res["hbm_copy"] = {"bytes": 2 * n, "ms": ms, "gbs": 2 * n / ms / 1e6,
+                       "frac_of_8tbs": 2 * n / ms / 1e6 / PEAK_HBM_GBS}
+    xf = x.view(torch.float32)
+    ms = timeit(lambda: xf.sum(), 10)
+    res["hbm_read"] = {"bytes": n, "ms": ms, "gbs": n / ms / 1e6,
+                       "frac_of_8tbs": n / ms / 1e6 / PEAK_HBM_GBS}
+    del x, y, xf
+    m = 8192
+    g = torch.Generator(device="cuda").manual_seed(0)
+    a = torch.randn((m, m), generator=g, device="cuda", dtype=torch.bfloat16)
+    b = torch.randn((m, m), generator=g, device="cuda", dtype=torch.bfloat16)
+    ms = timeit(lambda: torch.mm(a, b), 20)
+    flop = 2.0 * m ** 3
+    res["bf16_mm"] = {"m": m, "flop": flop, "ms": ms, "tflops": flop / ms / 1e9,
+                      "frac_of_2500": flop / ms / 1e9 / PEAK_BF16_TFLOPS}
+    del a, b
+    from sparse_linear_attention_amd import sla2 as S
+    groups, iters = 2048, 4000
+    out = torch.empty(groups * 4, dtype=torch.float32, device="cuda")
+    for kind, name, per in ((0, "mfma_bf16_probe", 2.0 * 32 * 32 * 16),
+                            (1, "mfma_fp8_probe", 2.0 * 32 * 32 * 64)):
+        ms = timeit(lambda: S.sla2_mfma_rate_probe(kind, iters, groups, out), 5)
+        flop = groups * 4.0 * iters * 4.0 * per
+        peak = PEAK_BF16_TFLOPS if kind == 0 else PEAK_FP8_TFLOPS
+        res[name] = {"flop": flop, "ms": ms, "tflops": flop / ms / 1e9,
+                     "frac_of_datasheet": flop / ms / 1e9 / peak}
+    res["device"] = torch.cuda.get_device_name(0)
+    print(json.dumps(res))
 
 
 def _counter_means(folder, counter, name_rx):
@@ -387,6 +447,7 @@ def main():
     ap.add_argument("--counters-summary", nargs=4, metavar="DIR")
     ap.add_argument("--traffic-table", nargs=4, metavar="DIR")
     ap.add_argument("--counter-table", metavar="DIR")
+    ap.add_argument("--peaks", action="store_true")
     ap.add_argument("--sweep", action="store_true",
                     help="sparsity sweep at the 1.3B shape with per-branch times and the "
                          "dense baseline (one JSON line)")
@@ -412,6 +473,9 @@ def main():
 
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.peaks:
+        measured_peaks()
         return
 
     from sparse_linear_attention_amd import inputs as I

@@ -342,6 +342,20 @@ sla2_status sla2_fp8_dot_tiles(const uint8_t* A, const uint8_t* B, float* C, int
                                void* stream);
 
 /*
+ * sla2_mfma_rate_probe -- measurement aid: the matrix-core instruction rate
+ * this GPU reaches, with no memory traffic.  groups work-groups of 4 waves;
+ * every wave runs iters rounds of 4 independent products of one form: kind
+ * 0 bf16 32x32x16 (32768 flop each), kind 1 e4m3 32x32x64 with unit scales
+ * (131072 flop each).  Total flop = groups * 4 * iters * 4 * (flop each);
+ * the caller times the call (events on `stream`).  out: device fp32
+ * [groups * 4], one value per wave (meaningless; keeps the work live).
+ * Errors: SLA2_EINVAL for kind not in {0, 1}, iters outside [1, 2^24],
+ * groups outside [1, 2^16], or a null or misaligned out.
+ */
+sla2_status sla2_mfma_rate_probe(int32_t kind, int32_t iters, int32_t groups, float* out,
+                                 void* stream);
+
+/*
  * Kernel timing (diagnostics, host-side state).  sla2_timing_start(n) makes
  * the library bracket each of its next n kernel launches with a pair of
  * hipEvents on the launch stream (the events are created here, not device

@@ -38,6 +38,48 @@ using namespace cdna4;
 __device__ inline float bf16_lo(unsigned w) { return __uint_as_float(w << 16); }
 __device__ inline float bf16_hi(unsigned w) { return __uint_as_float(w & 0xffff0000u); }
 
+// Cross-lane steps of the fp64 column sums (pooled keys).  Half-exchange:
+// the lanes whose partner bit is clear keep x (their value of the lower half
+// of a channel set), the others keep y (upper half); each gets its kept
+// value plus the partner's value of the same half.  Partner lane ^ 32 and
+// ^ 16 by the gfx950 lane swaps (x' = x's lower lanes with y's lower lanes
+// moved up, y' = the rest; the kept sum is x' + y' in every lane), ^ 8 by a
+// rotation of each 16-lane row.
+__device__ inline double f64_of(unsigned lo, unsigned hi) {
+    return __hiloint2double((int)hi, (int)lo);
+}
+__device__ inline double half_xchg32(double x, double y) {
+    const auto l = __builtin_amdgcn_permlane32_swap((unsigned)__double2loint(x),
+                                                    (unsigned)__double2loint(y), false, false);
+    const auto h = __builtin_amdgcn_permlane32_swap((unsigned)__double2hiint(x),
+                                                    (unsigned)__double2hiint(y), false, false);
+    return f64_of(l[0], h[0]) + f64_of(l[1], h[1]);
+}
+__device__ inline double half_xchg16(double x, double y) {
+    const auto l = __builtin_amdgcn_permlane16_swap((unsigned)__double2loint(x),
+                                                    (unsigned)__double2loint(y), false, false);
+    const auto h = __builtin_amdgcn_permlane16_swap((unsigned)__double2hiint(x),
+                                                    (unsigned)__double2hiint(y), false, false);
+    return f64_of(l[0], h[0]) + f64_of(l[1], h[1]);
+}
+template <int CTRL>
+__device__ inline double dpp_f64(double v) {
+    const int lo = __builtin_amdgcn_mov_dpp(__double2loint(v), CTRL, 0xF, 0xF, false);
+    const int hi = __builtin_amdgcn_mov_dpp(__double2hiint(v), CTRL, 0xF, 0xF, false);
+    return __hiloint2double(hi, lo);
+}
+__device__ inline double half_xchg8(double x, double y, bool up) {
+    return (up ? y : x) + dpp_f64<0x128>(up ? x : y);  // row_ror:8 = lane ^ 8 in a row
+}
+// sum over the 8 lanes of each aligned group: lane ^ 1, ^ 2 (quad
+// permutations), then the mirror inside the 8 (lane i <-> 7 - i)
+__device__ inline double sum8_f64(double v) {
+    v += dpp_f64<0xB1>(v);
+    v += dpp_f64<0x4E>(v);
+    v += dpp_f64<0x141>(v);
+    return v;
+}
+
 // token u of a 64-block -> its position in the transposed layouts
 __device__ inline int perm_pos(int u) {
     return (u & ~12) | ((u >> 1) & 4) | ((u << 1) & 8);
@@ -51,13 +93,19 @@ constexpr int kTPitch = 64 * 2 + 16;  // bytes per row of a [d][64] fp16 tile in
 // HZ: instead of phi(K)^T tiles, z_j and chunk partials, write every block's
 // summaries for the linear-branch product (linear.hip): row j of hz holds
 // h_j^T (V channel e major, phi channel c minor: entry e * D + c) and then
-// z_j, in bf16; V^T tiles only if vt is not null.
+// z_j, in bf16; V^T tiles only if vt is not null.  With xk not null the pass
+// also writes the router's pooled keys ("SLA2 深度解读" 03: the mean of each
+// KV block, [BH][Tkv][D] fp64), from the K rows it holds anyway: each wave
+// sums its channels over the 64 tokens (one per lane) in fp64 by a
+// reduce-scatter across the lanes, 8 channels at a time.  The sums of bf16 values are exact in fp64
+// unless a block's values span more than about 2^39 in magnitude, so they
+// equal those of the router's own pooling pass.
 template <int D, bool HZ>
-__global__ __launch_bounds__(256) void summaries_mfma_kernel(
+__global__ __launch_bounds__(256, 4) void summaries_mfma_kernel(
     const uint16_t* __restrict__ K, const uint16_t* __restrict__ V, uint16_t* __restrict__ vt,
     uint16_t* __restrict__ pkt, float* __restrict__ zb, float* __restrict__ hpart,
     float* __restrict__ zpart, uint16_t* __restrict__ hz, int N, int Tkv, int nch, int H,
-    Strides st, int phi_sm) {
+    Strides st, int phi_sm, double* __restrict__ xk) {
     static_assert(!HZ || D == 128, "per-block summaries: d = 128");
     constexpr int NT = D / 32;
     constexpr int TPW = NT * NT / 4;  // h^T tiles per wave
@@ -145,6 +193,35 @@ __global__ __launch_bounds__(256) void summaries_mfma_kernel(
                 *reinterpret_cast<_Float16*>(sP + c * kTPitch + pos * 2) = ph;
                 *reinterpret_cast<_Float16*>(sV + c * kTPitch + pos * 2) = vh;
             }
+        }
+        if constexpr (HZ) {
+          if (xk) {
+            // block mean of K, per group of 8 channels (w + 4 pass): v[i] is
+            // channel 8 (w + 4 pass) + i of this lane's token; halve the set
+            // per step, keeping the lower or upper half by a lane bit and
+            // adding the partner's copy of it, then add across the remaining
+            // lane bits: lane l ends with channel l / 8 of the group summed
+            // over all 64 tokens
+            const int n = min(64, N - j * 64);
+#pragma unroll
+            for (int pass = 0; pass < NP; ++pass) {
+                const unsigned kw[4] = {kvs[pass].x, kvs[pass].y, kvs[pass].z, kvs[pass].w};
+                double v[8];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    v[2 * e] = (double)bf16_lo(kw[e]);
+                    v[2 * e + 1] = (double)bf16_hi(kw[e]);
+                }
+#pragma unroll
+                for (int i = 0; i < 4; ++i) v[i] = half_xchg32(v[i], v[i + 4]);
+#pragma unroll
+                for (int i = 0; i < 2; ++i) v[i] = half_xchg16(v[i], v[i + 2]);
+                v[0] = sum8_f64(half_xchg8(v[0], v[1], (lane & 8) != 0));
+                if ((lane & 7) == 0)
+                    xk[((size_t)bh * Tkv + j) * D + (w + 4 * pass) * 8 + (lane >> 3)] =
+                        v[0] / (double)n;
+            }
+          }
         }
         __syncthreads();
         // write the transposed tiles (contiguous D*64 fp16 each) and z_j
@@ -530,7 +607,8 @@ __global__ __launch_bounds__(256, 2) void fused_mfma_kernel(
 }  // namespace
 
 hipError_t launch_summaries_mfma(const Dims& D, const void* K, const void* V,
-                                 const FwdWS& ws, hipStream_t s) {
+                                 const FwdWS& ws, hipStream_t s, double* xk) {
+    if (!hz_path(D) && D.d != 64) return hipErrorInvalidValue;  // d = 128 takes hz_path
     const int nch = summ_chunks(D);
     dim3 g(nch, (unsigned)D.BH);
     timing_before(s, K_SUMM_MFMA);
@@ -539,15 +617,11 @@ hipError_t launch_summaries_mfma(const Dims& D, const void* K, const void* V,
         summaries_mfma_kernel<128, true><<<g, 256, 0, s>>>(
             (const uint16_t*)K, (const uint16_t*)V, D.skip_sparse ? nullptr : ws.vt, nullptr,
             nullptr, nullptr, nullptr, D.skip_lin ? nullptr : ws.hz, D.N, D.Tkv, nch, D.H, D.st,
-            D.phi_sm);
-    else if (D.d == 128)
-        summaries_mfma_kernel<128, false><<<g, 256, 0, s>>>(
-            (const uint16_t*)K, (const uint16_t*)V, ws.vt, ws.pkt, ws.zb, ws.hpart, ws.zpart,
-            nullptr, D.N, D.Tkv, nch, D.H, D.st, D.phi_sm);
+            D.phi_sm, xk);
     else
         summaries_mfma_kernel<64, false><<<g, 256, 0, s>>>(
             (const uint16_t*)K, (const uint16_t*)V, ws.vt, ws.pkt, ws.zb, ws.hpart, ws.zpart,
-            nullptr, D.N, D.Tkv, nch, D.H, D.st, D.phi_sm);
+            nullptr, D.N, D.Tkv, nch, D.H, D.st, D.phi_sm, nullptr);
     timing_after(s, K_SUMM_MFMA);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || hz_path(D)) return e;

@@ -403,6 +403,23 @@ hipError_t launch_pool_project(const Dims& D, const void* Q, const void* K, cons
     return hipGetLastError();
 }
 
+hipError_t launch_pool_queries(const Dims& D, const void* Q, const RouteWS& ws, hipStream_t s) {
+    if (D.k == 0) return hipSuccess;
+    // work-groups [0, Tq) of the pooling grid: the query blocks
+    dim3 g1(D.Tq, (unsigned)D.BH);
+    timing_before(s, K_POOL_PROJECT);
+    if (D.dtype == SLA2_F32)
+        pool_project_kernel<float><<<g1, 256, 0, s>>>(
+            (const float*)Q, nullptr, nullptr, nullptr, ws.xq, ws.xk, D.N, D.d, D.bq, D.bkv,
+            D.Tq, D.Tkv, D.H, D.w_heads, D.st);
+    else
+        pool_project_kernel<uint16_t><<<g1, 256, 0, s>>>(
+            (const uint16_t*)Q, nullptr, nullptr, nullptr, ws.xq, ws.xk, D.N, D.d, D.bq,
+            D.bkv, D.Tq, D.Tkv, D.H, D.w_heads, D.st);
+    timing_after(s, K_POOL_PROJECT);
+    return hipGetLastError();
+}
+
 hipError_t launch_scores(const Dims& D, const void* Q, const void* K, const float* Wq,
                          const float* Wk, const RouteWS& ws, hipStream_t s, bool pooled) {
     hipError_t e = launch_pool_project(D, Q, K, Wq, Wk, ws, s, pooled);

@@ -457,9 +457,24 @@ SLA2_API sla2_status sla2_attention(const sla2_problem* p, const void* Q, const 
     Side* sd = nullptr;
     std::lock_guard<std::mutex> lk(g_side_mu);  // see side_stream
     if ((e = side_stream(&sd)) != hipSuccess) return SLA2_EHIP;
-    // summaries (K, V) on the helper stream, the router (Q, K) on the caller's
     if ((e = hipEventRecord(sd->fork, s)) != hipSuccess) return SLA2_EHIP;
     if ((e = hipStreamWaitEvent(sd->s, sd->fork, 0)) != hipSuccess) return SLA2_EHIP;
+    if (hz_path(D)) {
+        // K is read once: the block-summaries pass (helper stream) also
+        // writes the router's pooled keys, while the caller's stream pools
+        // the queries; the projections, scores and top-k follow the join
+        e = launch_summaries_mfma(D, K, V, fw, sd->s, D.k > 0 ? rw.xk : nullptr);
+        if (e == hipSuccess) e = hipEventRecord(sd->join, sd->s);
+        if (e == hipSuccess) e = launch_pool_queries(D, Q, rw, s);
+        if (e == hipSuccess) e = hipStreamWaitEvent(s, sd->join, 0);
+        if (e == hipSuccess) e = launch_route(D, Q, K, Wq, Wk, topk_idx, nullptr, rw, s, true);
+        const bool lin = D.k < D.Tkv && !D.skip_lin;
+        if (e == hipSuccess && lin) e = launch_unsel(D, topk_idx, nullptr, 0, fw, s);
+        if (e == hipSuccess && lin) e = launch_lin_gemm(D, fw, s);
+        if (e == hipSuccess) e = launch_fused_mfma(D, Q, K, topk_idx, alpha, O, fw, s);
+        return e == hipSuccess ? SLA2_OK : SLA2_EHIP;
+    }
+    // summaries (K, V) on the helper stream, the router (Q, K) on the caller's
     e = launch_summaries_mfma(D, K, V, fw, sd->s);
     if (e == hipSuccess) e = hipEventRecord(sd->join, sd->s);
     if (e == hipSuccess) e = launch_route(D, Q, K, Wq, Wk, topk_idx, nullptr, rw, s);
@@ -774,6 +789,15 @@ SLA2_API sla2_status sla2_fp8_dot_tiles(const uint8_t* A, const uint8_t* B, floa
     if (!ok_ptr(A) || !ok_ptr(B) || !ok_ptr(C)) return SLA2_EINVAL;
     if (ntiles <= 0 || ntiles > (1 << 20)) return SLA2_EINVAL;
     hipError_t e = launch_fp8_dot(A, B, C, ntiles, (hipStream_t)stream);
+    return e == hipSuccess ? SLA2_OK : SLA2_EHIP;
+}
+
+SLA2_API sla2_status sla2_mfma_rate_probe(int32_t kind, int32_t iters, int32_t groups,
+                                          float* out, void* stream) {
+    if (kind != 0 && kind != 1) return SLA2_EINVAL;
+    if (iters <= 0 || iters > (1 << 24) || groups <= 0 || groups > (1 << 16)) return SLA2_EINVAL;
+    if (!ok_ptr(out)) return SLA2_EINVAL;
+    hipError_t e = launch_mfma_rate(kind, iters, groups, out, (hipStream_t)stream);
     return e == hipSuccess ? SLA2_OK : SLA2_EHIP;
 }
 

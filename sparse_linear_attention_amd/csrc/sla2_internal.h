@@ -228,6 +228,10 @@ hipError_t launch_route(const Dims& D, const void* Q, const void* K, const float
                         const float* Wk, int32_t* idx, uint8_t* mask, const RouteWS& ws,
                         hipStream_t s, bool pooled = false);
 
+// the pooling pass over the query blocks only (ws.xq), for a caller that
+// has the key blocks' means from the block-summaries pass
+hipError_t launch_pool_queries(const Dims& D, const void* Q, const RouteWS& ws, hipStream_t s);
+
 // router stages: pooled rows and their projections (ws.xq/xk, ws.qt/kt);
 // then the scores (ws.S)
 hipError_t launch_pool_project(const Dims& D, const void* Q, const void* K, const float* Wq,
@@ -253,6 +257,10 @@ hipError_t launch_route_v1(const Dims& D, const void* Q, const void* K, int kl, 
 
 // vector-ALU path (fp32 inputs, b_q = 64, d = 64): block summaries + fused
 // kernel; with D.v1, negl [BH][Tq][D.kl] and Wp [w_heads][d][d] (alpha unused)
+// matrix-core rate probe: kind 0 bf16 32x32x16, 1 e4m3 32x32x64; groups
+// work-groups of 4 waves, each wave iters x 4 products; out [groups * 4]
+hipError_t launch_mfma_rate(int kind, int iters, int groups, float* out, hipStream_t s);
+
 hipError_t launch_forward_valu(const Dims& D, const void* Q, const void* K, const void* V,
                                const int32_t* idx, const float* alpha, void* O,
                                const FwdWS& ws, hipStream_t s, const int32_t* negl = nullptr,
@@ -286,9 +294,10 @@ hipError_t launch_invert(const Dims& D, const int32_t* idx, const BwdWS& bw, hip
 // dalpha from the per-row values bw.da
 hipError_t launch_dalpha(const Dims& D, const BwdWS& bw, float* dalpha, hipStream_t s);
 
-// bf16 path: MFMA block summaries + MFMA fused kernel (bq = 128)
+// bf16 path: MFMA block summaries + MFMA fused kernel (bq = 128).  xk (d =
+// 128, b_q = 128 path only): also write the router's pooled keys there
 hipError_t launch_summaries_mfma(const Dims& D, const void* K, const void* V,
-                                 const FwdWS& ws, hipStream_t s);
+                                 const FwdWS& ws, hipStream_t s, double* xk = nullptr);
 hipError_t launch_fused_mfma(const Dims& D, const void* Q, const void* K,
                              const int32_t* idx, const float* alpha, void* O,
                              const FwdWS& ws, hipStream_t s);

@@ -79,6 +79,7 @@ def lib():
         L.sla1_route.argtypes = [P, vp, vp, C.c_float, vp, vp, vp, vp, C.c_size_t, vp]
         L.sla1_forward.argtypes = [P, vp, vp, vp, vp, vp, C.c_float, vp, vp, vp, C.c_size_t, vp]
         L.sla2_fp8_dot_tiles.argtypes = [vp, vp, vp, C.c_int32, vp]
+        L.sla2_mfma_rate_probe.argtypes = [C.c_int32, C.c_int32, C.c_int32, vp, vp]
         L.sla2_attention_noalloc.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp]
         L.sla2_noalloc_scratch_bytes.restype = C.c_size_t
         _lib = L
@@ -91,7 +92,7 @@ EXPORTS = ("sla2_num_q_blocks", "sla2_num_kv_blocks", "sla2_topk", "sla2_workspa
            "sla2_kernel_kinds", "sla2_kernel_name", "sla1_num_negligible", "sla1_route",
            "sla1_forward", "sla2_soft_topk", "sla2_soft_topk_grad", "sla2_route_grad",
            "sla2_backward", "sla2_attention", "sla2_attention_fp8", "sla2_fp8_dot_tiles",
-           "sla2_attention_noalloc", "sla2_noalloc_scratch_bytes")
+           "sla2_mfma_rate_probe", "sla2_attention_noalloc", "sla2_noalloc_scratch_bytes")
 
 
 def _dtype(x):
@@ -245,6 +246,11 @@ def attention(p: Problem, Q, K, V, Wq, Wk, alpha, ws=None, stream=None, fp8=Fals
     fn = sla2_attention_fp8 if fp8 else sla2_attention
     fn(p, Q, K, V, Wq, Wk, alpha, idx if topk(p) > 0 else None, O, ws, stream)
     return idx, O
+
+
+def sla2_mfma_rate_probe(kind, iters, groups, out, stream=None):
+    _raise(lib().sla2_mfma_rate_probe(int(kind), int(iters), int(groups), _ptr(out),
+                                      _stream(stream)), "sla2_mfma_rate_probe")
 
 
 def sla2_fp8_dot_tiles(A, B, Cout, ntiles, stream=None):

@@ -274,3 +274,15 @@ def test_noalloc_rejects_problems_past_its_array():
     args = [good] * 8 + [None]
     assert L.sla2_attention_noalloc(C.byref(big), *args) == S.EWORKSPACE
     assert L.sla2_attention_noalloc(C.byref(small), None, *args[1:]) == S.EINVAL
+
+
+def test_mfma_rate_probe_rejects_bad_arguments():
+    L = S.lib()
+    good = C.c_void_p(4096)
+    assert L.sla2_mfma_rate_probe(2, 10, 1, good, None) == S.EINVAL
+    assert L.sla2_mfma_rate_probe(0, 0, 1, good, None) == S.EINVAL
+    assert L.sla2_mfma_rate_probe(1, (1 << 24) + 1, 1, good, None) == S.EINVAL
+    assert L.sla2_mfma_rate_probe(0, 10, 0, good, None) == S.EINVAL
+    assert L.sla2_mfma_rate_probe(0, 10, (1 << 16) + 1, good, None) == S.EINVAL
+    assert L.sla2_mfma_rate_probe(0, 10, 1, None, None) == S.EINVAL
+    assert L.sla2_mfma_rate_probe(0, 10, 1, C.c_void_p(4096 + 4), None) == S.EINVAL
