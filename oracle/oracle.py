@@ -15,7 +15,9 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "sla2_oracle.c")
-_LIB = os.path.join(_HERE, "libsla2_oracle.so")
+# a sanitizer build of the same source (tests/test_sanitizers.py) is loaded
+# in place of the plain one when SLA2_ORACLE_LIB names it
+_LIB = os.environ.get("SLA2_ORACLE_LIB") or os.path.join(_HERE, "libsla2_oracle.so")
 
 
 def build(force: bool = True) -> str:
