@@ -409,10 +409,10 @@ hipError_t launch_quantize_fp8(const Dims& D, const void* Q, const void* K, cons
 }
 
 hipError_t launch_pool_quant(const Dims& D, const void* Q, const void* K, const RouteWS& rw,
-                             const FwdWS& fw, hipStream_t s) {
+                             const FwdWS& fw, hipStream_t s, bool queries_only) {
     timing_before(s, K_POOL_QUANT);
     (D.int8_qk ? pool_quant_kernel<true> : pool_quant_kernel<false>)<<<
-        dim3(D.Tq + D.Tkv, (unsigned)D.BH), 256, 0, s>>>(
+        dim3(queries_only ? D.Tq : D.Tq + D.Tkv, (unsigned)D.BH), 256, 0, s>>>(
         (const uint16_t*)Q, (const uint16_t*)K, rw.xq, rw.xk, fw.ksum, fw.qhat, fw.sq, D.N, D.Tq,
         D.Tkv, D.H, D.st);
     timing_after(s, K_POOL_QUANT);

@@ -97,7 +97,9 @@ constexpr int kTPitch = 64 * 2 + 16;  // bytes per row of a [d][64] fp16 tile in
 // also writes the router's pooled keys ("SLA2 深度解读" 03: the mean of each
 // KV block, [BH][Tkv][D] fp64), from the K rows it holds anyway: each wave
 // sums its channels over the 64 tokens (one per lane) in fp64 by a
-// reduce-scatter across the lanes, 8 channels at a time.  The sums of bf16 values are exact in fp64
+// reduce-scatter across the lanes, 8 channels at a time; with kblk not null
+// the sums themselves as well ([BH][Tkv][D] fp64: the low-bit path's K mean
+// is taken from them).  The sums of bf16 values are exact in fp64
 // unless a block's values span more than about 2^39 in magnitude, so they
 // equal those of the router's own pooling pass.
 template <int D, bool HZ>
@@ -105,7 +107,7 @@ __global__ __launch_bounds__(256, 4) void summaries_mfma_kernel(
     const uint16_t* __restrict__ K, const uint16_t* __restrict__ V, uint16_t* __restrict__ vt,
     uint16_t* __restrict__ pkt, float* __restrict__ zb, float* __restrict__ hpart,
     float* __restrict__ zpart, uint16_t* __restrict__ hz, int N, int Tkv, int nch, int H,
-    Strides st, int phi_sm, double* __restrict__ xk) {
+    Strides st, int phi_sm, double* __restrict__ xk, double* __restrict__ kblk) {
     static_assert(!HZ || D == 128, "per-block summaries: d = 128");
     constexpr int NT = D / 32;
     constexpr int TPW = NT * NT / 4;  // h^T tiles per wave
@@ -217,9 +219,11 @@ __global__ __launch_bounds__(256, 4) void summaries_mfma_kernel(
 #pragma unroll
                 for (int i = 0; i < 2; ++i) v[i] = half_xchg16(v[i], v[i + 2]);
                 v[0] = sum8_f64(half_xchg8(v[0], v[1], (lane & 8) != 0));
-                if ((lane & 7) == 0)
-                    xk[((size_t)bh * Tkv + j) * D + (w + 4 * pass) * 8 + (lane >> 3)] =
-                        v[0] / (double)n;
+                if ((lane & 7) == 0) {
+                    const size_t o = ((size_t)bh * Tkv + j) * D + (w + 4 * pass) * 8 + (lane >> 3);
+                    xk[o] = v[0] / (double)n;
+                    if (kblk) kblk[o] = v[0];
+                }
             }
           }
         }
@@ -607,7 +611,7 @@ __global__ __launch_bounds__(256, 2) void fused_mfma_kernel(
 }  // namespace
 
 hipError_t launch_summaries_mfma(const Dims& D, const void* K, const void* V,
-                                 const FwdWS& ws, hipStream_t s, double* xk) {
+                                 const FwdWS& ws, hipStream_t s, double* xk, double* kblk) {
     if (!hz_path(D) && D.d != 64) return hipErrorInvalidValue;  // d = 128 takes hz_path
     const int nch = summ_chunks(D);
     dim3 g(nch, (unsigned)D.BH);
@@ -617,11 +621,11 @@ hipError_t launch_summaries_mfma(const Dims& D, const void* K, const void* V,
         summaries_mfma_kernel<128, true><<<g, 256, 0, s>>>(
             (const uint16_t*)K, (const uint16_t*)V, D.skip_sparse ? nullptr : ws.vt, nullptr,
             nullptr, nullptr, nullptr, D.skip_lin ? nullptr : ws.hz, D.N, D.Tkv, nch, D.H, D.st,
-            D.phi_sm, xk);
+            D.phi_sm, xk, kblk);
     else
         summaries_mfma_kernel<64, false><<<g, 256, 0, s>>>(
             (const uint16_t*)K, (const uint16_t*)V, ws.vt, ws.pkt, ws.zb, ws.hpart, ws.zpart,
-            nullptr, D.N, D.Tkv, nch, D.H, D.st, D.phi_sm, nullptr);
+            nullptr, D.N, D.Tkv, nch, D.H, D.st, D.phi_sm, nullptr, nullptr);
     timing_after(s, K_SUMM_MFMA);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || hz_path(D)) return e;

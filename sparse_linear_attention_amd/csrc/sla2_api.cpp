@@ -576,18 +576,21 @@ SLA2_API sla2_status sla2_attention_fp8(const sla2_problem* p, const void* Q, co
     Side* sd = nullptr;
     std::lock_guard<std::mutex> lk(g_side_mu);  // see side_stream
     if ((e = side_stream(&sd)) != hipSuccess) return SLA2_EHIP;
-    // caller's stream: the router, whose pooling pass also writes the query
-    // codes and the K block sums; helper stream: the block summaries, then
-    // (once the pooling pass is done) the K mean, the key codes and the V
-    // codes.  The same codes as sla2_quantize_fp8 (exact fp64 sums).
+    // K is read by the block-summaries pass (helper stream), which also
+    // writes the router's pooled keys and each KV block's column sums; the
+    // caller's stream pools the queries and writes their codes, then (once
+    // the summaries are done) runs the projections, scores and top-k while
+    // the helper stream takes the K mean from the block sums and writes the
+    // key codes (and the V codes).  The same codes as sla2_quantize_fp8
+    // (exact fp64 sums).
     if ((e = hipEventRecord(sd->fork, s)) != hipSuccess) return SLA2_EHIP;
     if ((e = hipStreamWaitEvent(sd->s, sd->fork, 0)) != hipSuccess) return SLA2_EHIP;
-    e = launch_summaries_mfma(D, K, V, fw, sd->s);
-    if (e == hipSuccess) e = launch_pool_quant(D, Q, K, rw, fw, s);
-    if (e == hipSuccess) e = hipEventRecord(sd->pooled, s);
-    if (e == hipSuccess) e = hipStreamWaitEvent(sd->s, sd->pooled, 0);
+    e = launch_summaries_mfma(D, K, V, fw, sd->s, rw.xk, fw.ksum);
+    if (e == hipSuccess) e = hipEventRecord(sd->pooled, sd->s);
     if (e == hipSuccess) e = launch_quantize_k(D, K, V, fw, sd->s);
     if (e == hipSuccess) e = hipEventRecord(sd->join, sd->s);
+    if (e == hipSuccess) e = launch_pool_quant(D, Q, K, rw, fw, s, true);
+    if (e == hipSuccess) e = hipStreamWaitEvent(s, sd->pooled, 0);
     if (e == hipSuccess) e = launch_route(D, Q, K, Wq, Wk, topk_idx, nullptr, rw, s, true);
     const bool lin = D.k < D.Tkv && !D.skip_lin;
     if (e == hipSuccess && lin) e = launch_unsel(D, topk_idx, nullptr, 0, fw, s);

@@ -295,9 +295,11 @@ hipError_t launch_invert(const Dims& D, const int32_t* idx, const BwdWS& bw, hip
 hipError_t launch_dalpha(const Dims& D, const BwdWS& bw, float* dalpha, hipStream_t s);
 
 // bf16 path: MFMA block summaries + MFMA fused kernel (bq = 128).  xk (d =
-// 128, b_q = 128 path only): also write the router's pooled keys there
+// 128, b_q = 128 path only): also write the router's pooled keys there, and
+// with kblk the fp64 column sums of each KV block of K (xk must be given)
 hipError_t launch_summaries_mfma(const Dims& D, const void* K, const void* V,
-                                 const FwdWS& ws, hipStream_t s, double* xk = nullptr);
+                                 const FwdWS& ws, hipStream_t s, double* xk = nullptr,
+                                 double* kblk = nullptr);
 hipError_t launch_fused_mfma(const Dims& D, const void* Q, const void* K,
                              const int32_t* idx, const float* alpha, void* O,
                              const FwdWS& ws, hipStream_t s);
@@ -309,9 +311,11 @@ hipError_t launch_quantize_fp8(const Dims& D, const void* Q, const void* K, cons
 // launch_pool_quant pools Q and K for the router (rw.xq, rw.xk), writes the
 // query codes and scales and each KV block's column sums of K (fw.ksum, Tkv
 // rows per head); launch_quantize_k then takes the K mean from those sums,
-// writes the key codes and scales, and the V codes with lowbit_v.
+// writes the key codes and scales, and the V codes with lowbit_v.  With
+// queries_only, launch_pool_quant takes the query blocks alone (the block
+// summaries pass writes xk and the K block sums).
 hipError_t launch_pool_quant(const Dims& D, const void* Q, const void* K, const RouteWS& rw,
-                             const FwdWS& fw, hipStream_t s);
+                             const FwdWS& fw, hipStream_t s, bool queries_only = false);
 hipError_t launch_quantize_k(const Dims& D, const void* K, const void* V, const FwdWS& fw,
                              hipStream_t s);
 // V codes in rows [BH][Tkv*64][d] (inspection; s_V into ws.sv)
