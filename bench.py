@@ -141,7 +141,8 @@ def measured_peaks():
     (read + write counted) and by a read-only sum over 4 GiB; the dense bf16
     matrix cores by an 8192^3 product (torch.mm on contiguous operands, i.e.
     the vendor GEMM library); the matrix-core instruction rate itself (bf16
-    32x32x16 and e4m3 32x32x64, no memory traffic) by the library's
+    32x32x16 and 16x16x32, fp16 32x32x16, e4m3 32x32x64, no memory traffic)
+    by the library's
     sla2_mfma_rate_probe.  Mean of 10 (copy, sum), 20 (product) or 5 (probe)
     launches after one warm-up."""
     import torch
@@ -183,10 +184,12 @@ def measured_peaks():
     groups, iters = 2048, 4000
     out = torch.empty(groups * 4, dtype=torch.float32, device="cuda")
     for kind, name, per in ((0, "mfma_bf16_probe", 2.0 * 32 * 32 * 16),
-                            (1, "mfma_fp8_probe", 2.0 * 32 * 32 * 64)):
+                            (1, "mfma_fp8_probe", 2.0 * 32 * 32 * 64),
+                            (2, "mfma_bf16_16x16x32_probe", 2.0 * 16 * 16 * 32),
+                            (3, "mfma_fp16_probe", 2.0 * 32 * 32 * 16)):
         ms = timeit(lambda: S.sla2_mfma_rate_probe(kind, iters, groups, out), 5)
         flop = groups * 4.0 * iters * 4.0 * per
-        peak = PEAK_BF16_TFLOPS if kind == 0 else PEAK_FP8_TFLOPS
+        peak = PEAK_FP8_TFLOPS if kind == 1 else PEAK_BF16_TFLOPS
         res[name] = {"flop": flop, "ms": ms, "tflops": flop / ms / 1e9,
                      "frac_of_datasheet": flop / ms / 1e9 / peak}
     res["device"] = torch.cuda.get_device_name(0)

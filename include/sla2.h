@@ -346,10 +346,11 @@ sla2_status sla2_fp8_dot_tiles(const uint8_t* A, const uint8_t* B, float* C, int
  * this GPU reaches, with no memory traffic.  groups work-groups of 4 waves;
  * every wave runs iters rounds of 4 independent products of one form: kind
  * 0 bf16 32x32x16 (32768 flop each), kind 1 e4m3 32x32x64 with unit scales
- * (131072 flop each).  Total flop = groups * 4 * iters * 4 * (flop each);
+ * (131072 flop each), kind 2 bf16 16x16x32 (16384 flop each), kind 3 fp16
+ * 32x32x16 (32768 flop each).  Total flop = groups * 4 * iters * 4 * (flop each);
  * the caller times the call (events on `stream`).  out: device fp32
  * [groups * 4], one value per wave (meaningless; keeps the work live).
- * Errors: SLA2_EINVAL for kind not in {0, 1}, iters outside [1, 2^24],
+ * Errors: SLA2_EINVAL for kind not in {0, 1, 2, 3}, iters outside [1, 2^24],
  * groups outside [1, 2^16], or a null or misaligned out.
  */
 sla2_status sla2_mfma_rate_probe(int32_t kind, int32_t iters, int32_t groups, float* out,

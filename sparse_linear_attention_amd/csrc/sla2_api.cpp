@@ -797,7 +797,7 @@ SLA2_API sla2_status sla2_fp8_dot_tiles(const uint8_t* A, const uint8_t* B, floa
 
 SLA2_API sla2_status sla2_mfma_rate_probe(int32_t kind, int32_t iters, int32_t groups,
                                           float* out, void* stream) {
-    if (kind != 0 && kind != 1) return SLA2_EINVAL;
+    if (kind < 0 || kind > 3) return SLA2_EINVAL;
     if (iters <= 0 || iters > (1 << 24) || groups <= 0 || groups > (1 << 16)) return SLA2_EINVAL;
     if (!ok_ptr(out)) return SLA2_EINVAL;
     hipError_t e = launch_mfma_rate(kind, iters, groups, out, (hipStream_t)stream);

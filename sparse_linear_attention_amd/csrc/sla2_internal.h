@@ -257,7 +257,8 @@ hipError_t launch_route_v1(const Dims& D, const void* Q, const void* K, int kl, 
 
 // vector-ALU path (fp32 inputs, b_q = 64, d = 64): block summaries + fused
 // kernel; with D.v1, negl [BH][Tq][D.kl] and Wp [w_heads][d][d] (alpha unused)
-// matrix-core rate probe: kind 0 bf16 32x32x16, 1 e4m3 32x32x64; groups
+// matrix-core rate probe: kind 0 bf16 32x32x16, 1 e4m3 32x32x64, 2 bf16
+// 16x16x32, 3 fp16 32x32x16; groups
 // work-groups of 4 waves, each wave iters x 4 products; out [groups * 4]
 hipError_t launch_mfma_rate(int kind, int iters, int groups, float* out, hipStream_t s);
 

@@ -115,7 +115,7 @@ int main() {
     EXPECT(sla1_forward(&p, g, g, g, gi, gi, 0.1f, gf, g, g, w1 - 1, nullptr) ==
            SLA2_EWORKSPACE);
     EXPECT(sla2_fp8_dot_tiles(gb, gb, gf, 0, nullptr) == SLA2_EINVAL);
-    EXPECT(sla2_mfma_rate_probe(3, 1, 1, gf, nullptr) == SLA2_EINVAL);
+    EXPECT(sla2_mfma_rate_probe(4, 1, 1, gf, nullptr) == SLA2_EINVAL);
     // past the no-allocation entry point's fixed array
     sla2_problem big = prob(1, 40, 75600, 128, 128, 0.03f, SLA2_BF16);
     EXPECT(sla2_attention_noalloc(&big, g, g, g, gf, gf, gf, gi, g, nullptr) ==

@@ -279,7 +279,8 @@ def test_noalloc_rejects_problems_past_its_array():
 def test_mfma_rate_probe_rejects_bad_arguments():
     L = S.lib()
     good = C.c_void_p(4096)
-    assert L.sla2_mfma_rate_probe(2, 10, 1, good, None) == S.EINVAL
+    assert L.sla2_mfma_rate_probe(4, 10, 1, good, None) == S.EINVAL
+    assert L.sla2_mfma_rate_probe(-1, 10, 1, good, None) == S.EINVAL
     assert L.sla2_mfma_rate_probe(0, 0, 1, good, None) == S.EINVAL
     assert L.sla2_mfma_rate_probe(1, (1 << 24) + 1, 1, good, None) == S.EINVAL
     assert L.sla2_mfma_rate_probe(0, 10, 0, good, None) == S.EINVAL
