@@ -28,6 +28,8 @@
 // (P^T is fed straight from the S^T accumulators); the k order inside an
 // instruction only has to agree between A and B, which holds because both
 // operands are loaded with the same position rule.
+#include <algorithm>
+
 #include "cdna4.h"
 #include "sla2_internal.h"
 
@@ -107,7 +109,7 @@ __global__ __launch_bounds__(256, 4) void summaries_mfma_kernel(
     const uint16_t* __restrict__ K, const uint16_t* __restrict__ V, uint16_t* __restrict__ vt,
     uint16_t* __restrict__ pkt, float* __restrict__ zb, float* __restrict__ hpart,
     float* __restrict__ zpart, uint16_t* __restrict__ hz, int N, int Tkv, int nch, int H,
-    Strides st, int phi_sm, double* __restrict__ xk, double* __restrict__ kblk) {
+    Strides st, int phi_sm, double* __restrict__ xk, double* __restrict__ kblk, int bpc) {
     static_assert(!HZ || D == 128, "per-block summaries: d = 128");
     constexpr int NT = D / 32;
     constexpr int TPW = NT * NT / 4;  // h^T tiles per wave
@@ -120,8 +122,8 @@ __global__ __launch_bounds__(256, 4) void summaries_mfma_kernel(
     const int w = __builtin_amdgcn_readfirstlane(t >> 6);
     const int chunk = blockIdx.x;
     const long bh = blockIdx.y;
-    const int j0 = chunk * kSummBlocksPerChunk;
-    const int j1 = min(Tkv, j0 + kSummBlocksPerChunk);
+    const int j0 = chunk * bpc;
+    const int j1 = min(Tkv, j0 + bpc);
     const uint16_t* Kh = K + head_base(st, bh, H);
     const uint16_t* Vh = V + head_base(st, bh, H);
     const int nt_w = w % NT;       // this wave's n-tile (phi(K) channels)
@@ -616,16 +618,23 @@ hipError_t launch_summaries_mfma(const Dims& D, const void* K, const void* V,
     const int nch = summ_chunks(D);
     dim3 g(nch, (unsigned)D.BH);
     timing_before(s, K_SUMM_MFMA);
-    if (hz_path(D))  // (stage switches: no V^T without the sparse branch, no h_j, z_j
-                     // without the linear one)
-        summaries_mfma_kernel<128, true><<<g, 256, 0, s>>>(
+    if (hz_path(D)) {
+        // (stage switches: no V^T without the sparse branch, no h_j, z_j
+        // without the linear one).  Blocks per work-group: up to 16, fewer
+        // when that leaves under 2048 work-groups (short sequences or few
+        // heads), so that the pass still fills the GPU
+        const long blocks = (long)D.Tkv * D.BH;
+        const int bpc = (int)std::max(1L, std::min((long)kSummBlocksPerChunk, blocks / 2048));
+        dim3 gh((D.Tkv + bpc - 1) / bpc, (unsigned)D.BH);
+        summaries_mfma_kernel<128, true><<<gh, 256, 0, s>>>(
             (const uint16_t*)K, (const uint16_t*)V, D.skip_sparse ? nullptr : ws.vt, nullptr,
             nullptr, nullptr, nullptr, D.skip_lin ? nullptr : ws.hz, D.N, D.Tkv, nch, D.H, D.st,
-            D.phi_sm, xk, kblk);
-    else
+            D.phi_sm, xk, kblk, bpc);
+    } else
         summaries_mfma_kernel<64, false><<<g, 256, 0, s>>>(
             (const uint16_t*)K, (const uint16_t*)V, ws.vt, ws.pkt, ws.zb, ws.hpart, ws.zpart,
-            nullptr, D.N, D.Tkv, nch, D.H, D.st, D.phi_sm, nullptr, nullptr);
+            nullptr, D.N, D.Tkv, nch, D.H, D.st, D.phi_sm, nullptr, nullptr,
+            kSummBlocksPerChunk);
     timing_after(s, K_SUMM_MFMA);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || hz_path(D)) return e;
