@@ -322,6 +322,24 @@ __global__ __launch_bounds__(256, 2) void fused128_kernel(
         return update_ref(m[0], ct);
     };
     auto ctile = [&](int jx) { return LOWBIT ? c_base * sk_h[jx] : c_base; };
+    // the query block's row of the linear-branch product into LDS by
+    // direct loads: H_i^T (bf16, entry e * 128 + c) as [128 e rows][256 B]
+    // with chunk c' of row e at c' ^ (e & 15) (the K tile layout, 8 pieces of
+    // 1 KB per wave), Z_i (fp32) after it.  Issued at the start of the last
+    // tile step, into the K stages (free from then on; 32.5 KB of the 48),
+    // so that the loads run under the last P V (bf16 path).
+    constexpr bool kEarlyH = LIN && !LOWBIT;
+    auto issue_h = [&]() {
+        const rsrc_t rh = head_rsrc(HZ + (size_t)bh * Tq * kHzRowBytes);
+        const uint32_t hoff = k_lane_off(w, lane, 256u);
+        const uint32_t row0 = (uint32_t)qb * kHzRowBytes;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) load_lds16(rh, hoff, row0 + 4096 * i, s_lds + (4 * i + w) * 1024);
+        if (w < 2)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rh, SLA2_LDS(s_lds + 32768 + 256 * w), 4,
+                                                     (uint32_t)lane * 4,
+                                                     row0 + 32768 + 256 * w, 0, 0);
+    };
 
     // ---- prologue: K_0, K_1, V_0, K_2 (in this order), then S_0 and its
     // reference
@@ -366,6 +384,7 @@ __global__ __launch_bounds__(256, 2) void fused128_kernel(
         }
         if (MORE3)
             issue_k<LOWBIT>(kbase + ks_r * P::kStage, rk, sel[r + 3], N, w, lane, koff, toff, rp);
+        if constexpr (kEarlyH && !MORE1) issue_h();
         f32x16 sn[2];
         if (MORE1) compute_s(kbase + (ks_r == 2 ? 0 : ks_r + 1) * P::kStage, sn);
         const char* vst = vbase + (r & 1) * kVT;
@@ -478,21 +497,27 @@ __global__ __launch_bounds__(256, 2) void fused128_kernel(
     for (int i = 0; i < 4; ++i) ol[i] = zero16();
     float inv_den = 0.0f;
     if (LIN) {
-        wg_barrier();  // every wave is done with the tile stages
-        // H_i^T (bf16 row of the product: entry e * 128 + c) into LDS as
+        // H_i^T (bf16 row of the product: entry e * 128 + c) in LDS as
         // [128 d rows][256 B], chunk c' of row e at c' ^ (e & 15); Z_i fp32
         char* sH = s_lds;
         float* sZ = reinterpret_cast<float*>(s_lds + 32768);
-        const char* hrow = HZ + ((size_t)bh * Tq + qb) * kHzRowBytes;
-        const int he = t >> 1, hc = 8 * (t & 1);  // row e, 16-byte chunks hc .. hc + 7
+        if constexpr (kEarlyH) {
+            if (k == 0) issue_h();  // (no tile step issued it)
+            wait_vmcnt<0>();
+            wg_barrier();  // every wave's pieces have landed
+        } else {
+            wg_barrier();  // every wave is done with the tile stages
+            const char* hrow = HZ + ((size_t)bh * Tq + qb) * kHzRowBytes;
+            const int he = t >> 1, hc = 8 * (t & 1);  // row e, 16-byte chunks hc .. hc + 7
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const uint4 v = *reinterpret_cast<const uint4*>(hrow + he * 256 + (hc + i) * 16);
-            *reinterpret_cast<uint4*>(sH + he * 256 + (((hc + i) ^ (he & 15)) << 4)) = v;
+            for (int i = 0; i < 8; ++i) {
+                const uint4 v = *reinterpret_cast<const uint4*>(hrow + he * 256 + (hc + i) * 16);
+                *reinterpret_cast<uint4*>(sH + he * 256 + (((hc + i) ^ (he & 15)) << 4)) = v;
+            }
+            if (t < 128) sZ[t] = reinterpret_cast<const float*>(hrow + 2 * 128 * 128)[t];
+            wait_lgkm0();
+            wg_barrier();
         }
-        if (t < 128) sZ[t] = reinterpret_cast<const float*>(hrow + 2 * 128 * 128)[t];
-        wait_lgkm0();
-        wg_barrier();
         // phi(Q)^T operand from the raw bf16 Q (registers on the bf16 path)
         bf16x8 qraw[8];
         if (LOWBIT) {
