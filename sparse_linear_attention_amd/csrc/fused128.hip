@@ -202,6 +202,10 @@ __global__ __launch_bounds__(256, 2) void fused128_kernel(
 #pragma unroll
     for (int i = 0; i < 4; ++i) o[i] = zero16();
     float m_ref = -INFINITY, l_part = 0.0f;
+    // LOWV: the row sums of 256 P^ come from the e4m3 matrix cores, as the
+    // product of a row of ones (e4m3 1.0 = 0x38) with the P codes: every row
+    // of lacc holds the sum over the tile's 64 keys for the lane's query
+    f32x16 lacc = zero16();
 
     const int32_t* sel = idx + ((size_t)bh * Tq + qb) * k;
     const uint32_t rp = (uint32_t)st.t * 2;  // bytes between consecutive K rows
@@ -289,6 +293,7 @@ __global__ __launch_bounds__(256, 2) void fused128_kernel(
             const float nref = need ? xmax : m_ref;
             const float f = __builtin_amdgcn_exp2f(m_ref - nref);
             l_part *= f;
+            if (LOWV) lacc[0] *= f;
 #pragma unroll
             for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -419,10 +424,13 @@ __global__ __launch_bounds__(256, 2) void fused128_kernel(
                     int wv = __builtin_amdgcn_cvt_pk_fp8_f32(p4[0], p4[1], 0, false);
                     wv = __builtin_amdgcn_cvt_pk_fp8_f32(p4[2], p4[3], wv, true);
                     pc[4 * mt + q] = wv;
-                    const auto b0 = __builtin_amdgcn_cvt_pk_f32_fp8(wv, false);
-                    const auto b1 = __builtin_amdgcn_cvt_pk_f32_fp8(wv, true);
-                    l_part += (b0[0] + b0[1]) + (b1[0] + b1[1]);
                 }
+            {
+                i32x8 ones;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) ones[i] = 0x38383838;
+                lacc = mfma_fp8(ones, pc, lacc);
+            }
             // O^T += Vhat^T (256 P^)^T on the e4m3 matrix cores (one k-step of
             // 64 keys per d-tile); the channel scales s_V apply at the end
 #pragma unroll
@@ -490,7 +498,7 @@ __global__ __launch_bounds__(256, 2) void fused128_kernel(
     if (r < k) step(r, ks, std::false_type{}, std::false_type{}, std::false_type{});
 
     // ---- epilogue
-    const float l_all = l_part + __shfl_xor(l_part, 32);
+    const float l_all = LOWV ? lacc[0] : l_part + __shfl_xor(l_part, 32);
     const float inv_l = (k > 0 && l_all > 0.0f) ? 1.0f / l_all : 0.0f;
     f32x16 ol[4];
 #pragma unroll
