@@ -390,7 +390,7 @@ def sweep(args, torch, I, S, dev):
     q, k, v, wq, wk, al = t(x.q), t(x.k), t(x.v), t(x.wq), t(x.wk), t(x.alpha)
     dense = dense_equivalent_flop(base.B, base.H, base.N, base.d)
     O = torch.empty((base.B, base.H, base.N, base.d), dtype=torch.float32, device=dev)
-    route_k = ("pool_project", "score", "topk_select")
+    route_k = ("pool_project", "score", "topk_select", "score_topk")
     rows = []
     for frac in I.SWEEP_FRACS:
         res = {"topk_frac": frac}
@@ -563,7 +563,7 @@ def main():
     fwd_ms = sum(v for kname, v in stages.items()
                  if kname in ("summaries_mfma", "summaries_reduce", "fused_mfma", "lin_gemm"))
     route_ms = sum(v for kname, v in stages.items()
-                   if kname in ("pool_project", "score", "topk_select"))
+                   if kname in ("pool_project", "score", "topk_select", "score_topk"))
 
     achieved = (fl_sparse + fl_apply) / (fused_ms * 1e-3) / 1e12
     traffic = None

@@ -361,6 +361,197 @@ __global__ __launch_bounds__(256) void topk_kernel(const double* __restrict__ S,
     }
 }
 
+// Scores and hard top-k in one pass, the score rows kept in LDS (S never
+// reaches memory): one work-group per 16 query blocks of a head.
+//
+// Scores: the 8 waves take turns over the 16-column tiles of the row block;
+// every 16 x 16 tile is the same chain of fp64 matrix-core products as a
+// quarter of score_kernel's 32 x 32 (same operand split, same order over the
+// channels), so the scores are bit for bit those of score_kernel.  They are
+// stored as order-preserving keys.
+//
+// Selection: wave w takes rows w and w + 8.  Per row a radix
+// select on a wave-private 256-bin histogram finds the k-th largest key; its
+// digits start at the highest bit where the row's keys differ (the bits above
+// are common to all keys, and the first 8-bit digit would otherwise put every
+// key in one bin).  Then every larger key and the lowest-index keys equal to
+// it are kept, as in topk_kernel, indices ascending.
+constexpr int kStRows = 16;
+constexpr int kStMaxTkv = 1200;  // 16 rows of keys + 8 histograms fit 160 KiB of LDS
+
+// LDS operations of one wave are done in order; this also keeps the compiler
+// from moving them across (the histogram is written by other lanes)
+__device__ inline void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+}
+
+__device__ inline unsigned long long wave_or64(unsigned long long v) {
+    unsigned lo = (unsigned)v, hi = (unsigned)(v >> 32);
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        lo |= __shfl_xor(lo, o);
+        hi |= __shfl_xor(hi, o);
+    }
+    return ((unsigned long long)hi << 32) | lo;
+}
+
+template <int d>
+__global__ __launch_bounds__(512) void score_topk_kernel(const double* __restrict__ qt,
+                                                         const double* __restrict__ kt, int Tq,
+                                                         int Tkv, int k,
+                                                         int32_t* __restrict__ idx,
+                                                         uint8_t* __restrict__ mask) {
+    __shared__ unsigned long long keys[kStRows * kStMaxTkv];  // [row][Tkv]
+    __shared__ unsigned hist[8][256];
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int r16 = lane & 15, kq = lane >> 4;
+    const long bh = blockIdx.y;
+    const int i0 = blockIdx.x * kStRows;
+
+    // ---- scores: A operand (16 query rows) held for the whole row block
+    {
+        const double* ar = qt + ((size_t)bh * Tq + min(i0 + r16, Tq - 1)) * d + 2 * kq;
+        double2 a[d / 8];
+#pragma unroll
+        for (int s = 0; s < d / 8; ++s) a[s] = *reinterpret_cast<const double2*>(ar + 8 * s);
+        const double* B = kt + (size_t)bh * Tkv * d + 2 * kq;
+        const int ntiles = (Tkv + 15) >> 4;
+        for (int t = w; t < ntiles; t += 16) {  // two tiles in flight: t and t + 8
+            const int ja = 16 * t + r16, jb = ja + 128;
+            const double* ba = B + (size_t)min(ja, Tkv - 1) * d;
+            const double* bb = B + (size_t)min(jb, Tkv - 1) * d;
+            f64x4 ca = {0.0, 0.0, 0.0, 0.0}, cb = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+            for (int s = 0; s < d / 8; ++s) {
+                const double2 x = *reinterpret_cast<const double2*>(ba + 8 * s);
+                const double2 y = *reinterpret_cast<const double2*>(bb + 8 * s);
+                ca = __builtin_amdgcn_mfma_f64_16x16x4f64(a[s].x, x.x, ca, 0, 0, 0);
+                cb = __builtin_amdgcn_mfma_f64_16x16x4f64(a[s].x, y.x, cb, 0, 0, 0);
+                ca = __builtin_amdgcn_mfma_f64_16x16x4f64(a[s].y, x.y, ca, 0, 0, 0);
+                cb = __builtin_amdgcn_mfma_f64_16x16x4f64(a[s].y, y.y, cb, 0, 0, 0);
+            }
+            // element r of lane (kq, r16): row kq + 4 r, column r16 of the tile
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                if (ja < Tkv) keys[(kq + 4 * r) * Tkv + ja] = score_key(ca[r]);
+                if (jb < Tkv) keys[(kq + 4 * r) * Tkv + jb] = score_key(cb[r]);
+            }
+        }
+    }
+    __syncthreads();
+
+    // ---- selection, one row at a time per wave, the row's keys in registers
+    // (key j in lane j % 64, slot j / 64)
+    constexpr int kSlots = (kStMaxTkv + 63) / 64;
+    unsigned* h = hist[w];
+    const unsigned long long below = (1ull << lane) - 1ull;
+    for (int rr = w; rr < kStRows; rr += 8) {
+        const int i = i0 + rr;
+        if (i >= Tq) break;
+        const size_t row = (size_t)bh * Tq + i;
+        int32_t* irow = idx + row * k;
+        uint8_t* mrow = mask ? mask + row * Tkv : nullptr;
+        if (k == Tkv) {  // everything selected
+            for (int j = lane; j < Tkv; j += 64) {
+                if (mrow) mrow[j] = 1;
+                irow[j] = j;
+            }
+            continue;
+        }
+        unsigned long long kv[kSlots];
+#pragma unroll
+        for (int t = 0; t < kSlots; ++t) {
+            const int j = lane + 64 * t;
+            kv[t] = j < Tkv ? keys[rr * Tkv + j] : 0ull;
+        }
+        const unsigned long long key0 = keys[rr * Tkv];
+        unsigned long long diff = 0;
+#pragma unroll
+        for (int t = 0; t < kSlots; ++t)
+            if (lane + 64 * t < Tkv) diff |= kv[t] ^ key0;
+        diff = wave_or64(diff);
+        int hi = diff ? 63 - __clzll((long long)diff) : -1;
+        // bits above hi are common: the prefix starts as those bits of any key
+        unsigned long long pmask = hi < 0 ? ~0ull : hi == 63 ? 0ull : ~((2ull << hi) - 1ull);
+        unsigned long long prefix = key0 & pmask;
+        int kr = k;
+        for (; hi >= 0; hi -= 8) {
+            const int lo = hi >= 7 ? hi - 7 : 0;
+            *reinterpret_cast<uint4*>(h + 4 * lane) = make_uint4(0u, 0u, 0u, 0u);
+            wave_lds_sync();
+#pragma unroll
+            for (int t = 0; t < kSlots; ++t)
+                if (lane + 64 * t < Tkv && (kv[t] & pmask) == prefix)
+                    atomicAdd(&h[(unsigned)(kv[t] >> lo) & 255u], 1u);
+            wave_lds_sync();
+            // lane l holds bins 255 - 4 l - q (descending); inclusive scan
+            unsigned c[4], tot = 0;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                c[q] = h[255 - 4 * lane - q];
+                tot += c[q];
+            }
+            unsigned incl = tot;
+#pragma unroll
+            for (int off = 1; off < 64; off <<= 1) {
+                const unsigned o = __shfl_up(incl, off);
+                if (lane >= off) incl += o;
+            }
+            const unsigned excl = incl - tot;
+            const bool found = excl < (unsigned)kr && (unsigned)kr <= incl;
+            int digit = 0, nkr = 0, done = 0;
+            if (found) {
+                unsigned run = excl;
+                digit = -1;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    if (digit < 0) {
+                        if (run + c[q] >= (unsigned)kr) {
+                            digit = 255 - 4 * lane - q;
+                            nkr = kr - (int)run;
+                            // the bin holds exactly the keys still wanted
+                            done = c[q] == (unsigned)nkr;
+                        } else {
+                            run += c[q];
+                        }
+                    }
+                }
+            }
+            const int src = __ffsll((unsigned long long)__ballot(found)) - 1;
+            digit = __shfl(digit, src);
+            nkr = __shfl(nkr, src);
+            done = __shfl(done, src);
+            // a last digit narrower than 8 bits also carries bits above hi,
+            // which equal the prefix's there
+            prefix |= (unsigned long long)(unsigned)digit << lo;
+            pmask |= (unsigned long long)((2u << (hi - lo)) - 1u) << lo;
+            kr = nkr;
+            wave_lds_sync();  // the bins are read before the next clear
+            if (done) break;
+        }
+        const unsigned long long thr = prefix;
+        int eq_base = 0, out_base = 0;
+#pragma unroll
+        for (int t = 0; t < kSlots; ++t) {
+            const int j = lane + 64 * t;
+            const bool in = j < Tkv;
+            const unsigned long long key = kv[t] & pmask;
+            const bool gt = in && key > thr;
+            const bool eq = in && key == thr;
+            const unsigned long long be = __ballot(eq);
+            const bool sel = gt || (eq && eq_base + __popcll(be & below) < kr);
+            const unsigned long long bs = __ballot(sel);
+            if (in) {
+                if (mrow) mrow[j] = sel ? 1 : 0;
+                if (sel) irow[out_base + __popcll(bs & below)] = j;
+            }
+            eq_base += __popcll(be);
+            out_base += __popcll(bs);
+        }
+    }
+}
+
 __global__ void zero_mask_kernel(uint8_t* __restrict__ mask, size_t n) {
     for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
          i += (size_t)gridDim.x * blockDim.x)
@@ -441,6 +632,18 @@ hipError_t launch_route(const Dims& D, const void* Q, const void* K, const float
             zero_mask_kernel<<<dim3((unsigned)(nb < 65535 ? nb : 65535)), 256, 0, s>>>(mask, n);
             timing_after(s, K_TOPK);
         }
+        return hipGetLastError();
+    }
+    if (D.Tkv <= kStMaxTkv) {  // scores and selection in one pass
+        hipError_t e = launch_pool_project(D, Q, K, Wq, Wk, ws, s, pooled);
+        if (e != hipSuccess) return e;
+        const dim3 g((D.Tq + kStRows - 1) / kStRows, (unsigned)D.BH);
+        timing_before(s, K_SCORE_TOPK);
+        if (D.d == 128)
+            score_topk_kernel<128><<<g, 512, 0, s>>>(ws.qt, ws.kt, D.Tq, D.Tkv, D.k, idx, mask);
+        else
+            score_topk_kernel<64><<<g, 512, 0, s>>>(ws.qt, ws.kt, D.Tq, D.Tkv, D.k, idx, mask);
+        timing_after(s, K_SCORE_TOPK);
         return hipGetLastError();
     }
     hipError_t e = launch_scores(D, Q, K, Wq, Wk, ws, s, pooled);

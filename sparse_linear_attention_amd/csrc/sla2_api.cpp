@@ -255,7 +255,7 @@ const char* kKindNames[K_NUM_KINDS] = {
     "quant_i8",     "fused_i8",    "fused_sla1",  "bwd_rows",
     "bwd_dh",       "bwd_keys",    "bwd_lin_rows", "bwd_lin_keys",
     "bwd_rows_mfma", "bwd_keys_mfma", "bwd_blk_summ", "bwd_sum_parts", "pool_quant",
-    "lin_gemm",
+    "lin_gemm",     "score_topk",
 };
 }  // namespace
 

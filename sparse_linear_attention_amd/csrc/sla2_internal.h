@@ -39,6 +39,7 @@ enum KernelKind {
     K_BWD_SUM_PARTS,
     K_POOL_QUANT,
     K_LIN_GEMM,
+    K_SCORE_TOPK,
     K_NUM_KINDS
 };
 

@@ -206,6 +206,37 @@ def test_tie_breaking_on_duplicated_blocks(orc, dev):
     assert np.array_equal(mask.cpu().numpy(), omask)
 
 
+@pytest.mark.parametrize("N", [1200 * 64, 1200 * 64 + 1])
+def test_route_at_the_one_pass_limit(orc, dev, N):
+    """Selection and mask exact at T_kv = 1200, the most KV blocks whose 16
+    score rows the one-pass score + top-k kernel keeps in LDS, and at 1201,
+    where the scores go through memory to the separate top-k kernel."""
+    w = wl("tkv-limit", "bf16", N, 128, 128, 0.03, H=2)
+    say(f"case route at T_kv limit: N={N}")
+    x = I.make_inputs(w)
+    p = problem_of(x)
+    q, k, v, wq, wk, al = to_dev(x, dev)
+    idx, mask = S.route(p, q, k, wq, wk)
+    torch.cuda.synchronize()
+    check_route(orc, x, idx, mask)
+
+
+def test_route_all_scores_equal(orc, dev):
+    """Every key block the same: all scores of a row tie, and the selection
+    is the k lowest block indices (ties to the lower index)."""
+    w = wl("all-equal", "bf16", 3000, 128, 128, 0.1, H=2)
+    x = I.make_inputs(w)
+    x.k = np.ascontiguousarray(np.broadcast_to(x.k[:, :, :1, :], x.k.shape))
+    p = problem_of(x)
+    q, k, v, wq, wk, al = to_dev(x, dev)
+    idx, mask = S.route(p, q, k, wq, wk)
+    torch.cuda.synchronize()
+    kk = S.topk(p)
+    gi = idx.cpu().numpy()
+    assert (gi == np.arange(kk, dtype=np.int32)).all()
+    check_route(orc, x, idx, mask)
+
+
 def test_per_head_projections(orc, dev):
     w = wl("per-head", "bf16", 900, 128, 128, 0.2, H=3)
     x = I.make_inputs(w)
