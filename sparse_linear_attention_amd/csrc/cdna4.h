@@ -50,7 +50,13 @@ __device__ inline f32x16 zero16() {
 // +inf.  fmaxf quiets each operand with an extra instruction first; written
 // as a builtin (not inline asm) so that the compiler keeps the wait states
 // between a matrix instruction and the reads of its result.
-__device__ inline float max2f(float a, float b) { return __builtin_amdgcn_fmed3f(a, b, INFINITY); }
+__device__ inline float max2f(float a, float b) {
+    // +inf hidden from the compiler, which would otherwise turn the med3 into
+    // a max with a canonicalising max per operand (IEEE mode)
+    float inf = INFINITY;
+    __asm__("" : "+v"(inf));
+    return __builtin_amdgcn_fmed3f(a, b, inf);
+}
 
 __device__ inline float bf16_bits(unsigned short b) { return __uint_as_float((unsigned)b << 16); }
 

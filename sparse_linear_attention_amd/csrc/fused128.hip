@@ -316,15 +316,17 @@ __global__ __launch_bounds__(256, 2) void fused128_kernel(
                     if (jx * 64 + 32 * mt + 8 * (i >> 2) + 4 * hl + (i & 3) >= N)
                         s[mt][i] = -INFINITY;
         }
-        // pairwise maxima in a tree (no NaN reaches here)
+        // pairwise maxima of the two m-tiles (one v_med3 each), then four
+        // chains over them, whose links of two become three-input maxima (the
+        // med3 results need no canonicalising); no NaN reaches here
         float m[16];
 #pragma unroll
         for (int i = 0; i < 16; ++i) m[i] = max2f(s[0][i], s[1][i]);
+        float c4[4];
 #pragma unroll
-        for (int w2 = 8; w2 >= 1; w2 >>= 1)
-#pragma unroll
-            for (int i = 0; i < w2; ++i) m[i] = max2f(m[i], m[i + w2]);
-        return update_ref(m[0], ct);
+        for (int j = 0; j < 4; ++j)
+            c4[j] = fmaxf(fmaxf(fmaxf(m[j], m[j + 4]), m[j + 8]), m[j + 12]);
+        return update_ref(fmaxf(fmaxf(fmaxf(c4[0], c4[1]), c4[2]), c4[3]), ct);
     };
     auto ctile = [&](int jx) { return LOWBIT ? c_base * sk_h[jx] : c_base; };
     // the query block's row of the linear-branch product into LDS by
@@ -375,7 +377,8 @@ __global__ __launch_bounds__(256, 2) void fused128_kernel(
     // rescale follow once its S is complete.  K tile x sits in stage x % 3,
     // V tile x in stage x % 2.  The last three steps are peeled off the loop,
     // so that inside it every load is unconditional.
-    auto step = [&](int r, int ks_r, auto more1_c, auto more2_c, auto more3_c) {
+    auto step = [&](int r, int ks_r, f32x16 (&sc)[2], f32x16 (&sn)[2], auto more1_c,
+                    auto more2_c, auto more3_c, auto copy_c) {
         constexpr bool MORE1 = decltype(more1_c)::value;
         constexpr bool MORE2 = decltype(more2_c)::value;
         constexpr bool MORE3 = decltype(more3_c)::value;
@@ -390,7 +393,6 @@ __global__ __launch_bounds__(256, 2) void fused128_kernel(
         if (MORE3)
             issue_k<LOWBIT>(kbase + ks_r * P::kStage, rk, sel[r + 3], N, w, lane, koff, toff, rp);
         if constexpr (kEarlyH && !MORE1) issue_h();
-        f32x16 sn[2];
         if (MORE1) compute_s(kbase + (ks_r == 2 ? 0 : ks_r + 1) * P::kStage, sn);
         const char* vst = vbase + (r & 1) * kVT;
         const char* v8st = v8base + (r & 1) * kV8;
@@ -480,22 +482,39 @@ __global__ __launch_bounds__(256, 2) void fused128_kernel(
             const int jn = sel[r + 1];
             cur_ct = ctile(jn);
             cur_ref = finish_s(sn, jn, cur_ct, std::integral_constant<bool, !MORE2>{});
-            sc[0] = sn[0];
-            sc[1] = sn[1];
+            if constexpr (decltype(copy_c)::value) {
+                sc[0] = sn[0];
+                sc[1] = sn[1];
+            }
         }
     };
+    // Tile steps in pairs, the next tile's S alternating between sc and sn
+    // (no register copies); the steps after the pairs keep the current S in
+    // sc.
+    f32x16 sn[2];
+    const std::true_type T{};
+    const std::false_type F{};
+    auto adv = [](int x) { return x == 2 ? 0 : x + 1; };
     int r = 0, ks = 0;
-    for (; r + 3 < k; ++r, ks = ks == 2 ? 0 : ks + 1)
-        step(r, ks, std::true_type{}, std::true_type{}, std::true_type{});
+    for (; r + 4 < k; r += 2) {
+        step(r, ks, sc, sn, T, T, T, F);
+        ks = adv(ks);
+        step(r + 1, ks, sn, sc, T, T, T, F);
+        ks = adv(ks);
+    }
+    if (r + 3 < k) {
+        step(r++, ks, sc, sn, T, T, T, T);
+        ks = adv(ks);
+    }
     if (r + 2 < k) {
-        step(r++, ks, std::true_type{}, std::true_type{}, std::false_type{});
-        ks = ks == 2 ? 0 : ks + 1;
+        step(r++, ks, sc, sn, T, T, F, T);
+        ks = adv(ks);
     }
     if (r + 1 < k) {
-        step(r++, ks, std::true_type{}, std::false_type{}, std::false_type{});
-        ks = ks == 2 ? 0 : ks + 1;
+        step(r++, ks, sc, sn, T, F, F, T);
+        ks = adv(ks);
     }
-    if (r < k) step(r, ks, std::false_type{}, std::false_type{}, std::false_type{});
+    if (r < k) step(r, ks, sc, sn, F, F, F, T);
 
     // ---- epilogue
     const float l_all = LOWV ? lacc[0] : l_part + __shfl_xor(l_part, 32);
