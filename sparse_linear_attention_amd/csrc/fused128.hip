@@ -411,7 +411,9 @@ __global__ __launch_bounds__(256, 2) void fused128_kernel(
         if (LOWV) {
             // codes of 256 P~ as the k operand of the e4m3 P V product: byte
             // 16 mt + i of this lane is the code of sc[mt][i]; the row sum is
-            // taken over the decoded values
+            // taken over the decoded values.  The low-bit reference moves on
+            // every new maximum (update_ref), so 256 P~ <= 256 (at most half
+            // an ulp of the logit above it) and needs no clamp to e4m3's 448
             const float bias = 8.0f - mref;
             i32x8 pc;
 #pragma unroll
@@ -421,8 +423,7 @@ __global__ __launch_bounds__(256, 2) void fused128_kernel(
                     float p4[4];
 #pragma unroll
                     for (int c = 0; c < 4; ++c)
-                        p4[c] = fminf(__builtin_amdgcn_exp2f(fmaf(sc[mt][4 * q + c], c_tile, bias)),
-                                      448.0f);
+                        p4[c] = __builtin_amdgcn_exp2f(fmaf(sc[mt][4 * q + c], c_tile, bias));
                     int wv = __builtin_amdgcn_cvt_pk_fp8_f32(p4[0], p4[1], 0, false);
                     wv = __builtin_amdgcn_cvt_pk_fp8_f32(p4[2], p4[3], wv, true);
                     pc[4 * mt + q] = wv;
@@ -458,8 +459,7 @@ __global__ __launch_bounds__(256, 2) void fused128_kernel(
                     for (int e = 0; e < 8; e += 2) {
                         const float p0 = __builtin_amdgcn_exp2f(fmaf(sc[kq >> 1][8 * (kq & 1) + e], c_tile, bias));
                         const float p1 = __builtin_amdgcn_exp2f(fmaf(sc[kq >> 1][8 * (kq & 1) + e + 1], c_tile, bias));
-                        const int code = __builtin_amdgcn_cvt_pk_fp8_f32(fminf(p0, 448.0f),
-                                                                         fminf(p1, 448.0f), 0, false);
+                        const int code = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, 0, false);
                         const auto back = __builtin_amdgcn_cvt_pk_f32_fp8(code, false);
                         pf[e] = (_Float16)back[0];
                         pf[e + 1] = (_Float16)back[1];
