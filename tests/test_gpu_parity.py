@@ -221,6 +221,25 @@ def test_route_at_the_one_pass_limit(orc, dev, N):
     check_route(orc, x, idx, mask)
 
 
+@pytest.mark.parametrize("d", [64, 128])
+def test_route_batches_per_head_projections(orc, dev, d):
+    """Two batch entries, per-head projections, a ragged last block and a row
+    block count that is not a multiple of 16 (the one-pass score + top-k
+    kernel takes 16 query blocks per work-group): selection and mask exact."""
+    B, H, N = 2, 3, 2500  # T_q = 20, T_kv = 40
+    w = I.Workload("route-b2", B, H, N, d, 128, 64, 0.15, "bf16", "smooth", seed=5)
+    x = I.make_inputs(w)
+    rng = np.random.default_rng(12)
+    x.wq = (rng.standard_normal((H, d, d)) / np.sqrt(d)).astype(np.float32)
+    x.wk = (rng.standard_normal((H, d, d)) / np.sqrt(d)).astype(np.float32)
+    say(f"case route B={B} H={H} N={N} d={d} per-head W")
+    p = problem_of(x)
+    q, k, v, wq, wk, al = to_dev(x, dev)
+    idx, mask = S.route(p, q, k, wq, wk)
+    torch.cuda.synchronize()
+    check_route(orc, x, idx, mask)
+
+
 def test_route_all_scores_equal(orc, dev):
     """Every key block the same: all scores of a row tie, and the selection
     is the k lowest block indices (ties to the lower index)."""
