@@ -424,7 +424,10 @@ __global__ __launch_bounds__(256, 2) void fused128_kernel(
 #pragma unroll
                     for (int c = 0; c < 4; ++c)
                         p4[c] = __builtin_amdgcn_exp2f(fmaf(sc[mt][4 * q + c], c_tile, bias));
-                    int wv = __builtin_amdgcn_cvt_pk_fp8_f32(p4[0], p4[1], 0, false);
+                    // the low half first, into any live register (the high
+                    // half is written next): no zeroed word per code group
+                    int wv = __builtin_amdgcn_cvt_pk_fp8_f32(p4[0], p4[1], __float_as_int(p4[0]),
+                                                             false);
                     wv = __builtin_amdgcn_cvt_pk_fp8_f32(p4[2], p4[3], wv, true);
                     pc[4 * mt + q] = wv;
                 }
@@ -459,7 +462,10 @@ __global__ __launch_bounds__(256, 2) void fused128_kernel(
                     for (int e = 0; e < 8; e += 2) {
                         const float p0 = __builtin_amdgcn_exp2f(fmaf(sc[kq >> 1][8 * (kq & 1) + e], c_tile, bias));
                         const float p1 = __builtin_amdgcn_exp2f(fmaf(sc[kq >> 1][8 * (kq & 1) + e + 1], c_tile, bias));
-                        const int code = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, 0, false);
+                        // only the low half is decoded: the high half's
+                        // source is any live register
+                        const int code =
+                            __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, __float_as_int(p0), false);
                         const auto back = __builtin_amdgcn_cvt_pk_f32_fp8(code, false);
                         pf[e] = (_Float16)back[0];
                         pf[e + 1] = (_Float16)back[1];
