@@ -620,11 +620,14 @@ hipError_t launch_summaries_mfma(const Dims& D, const void* K, const void* V,
     timing_before(s, K_SUMM_MFMA);
     if (hz_path(D)) {
         // (stage switches: no V^T without the sparse branch, no h_j, z_j
-        // without the linear one).  Blocks per work-group: up to 16, fewer
-        // when that leaves under 2048 work-groups (short sequences or few
-        // heads), so that the pass still fills the GPU
+        // without the linear one).  Blocks per work-group: up to 8 (at the
+        // 14B shape 5,920 work-groups, about six rounds of the 1,024 that are
+        // resident at once, against three with 16: a shorter last round),
+        // fewer when that leaves under 2048 work-groups (short sequences or
+        // few heads), so that the pass still fills the GPU
+        constexpr long kMaxBlocksPerGroup = 8;
         const long blocks = (long)D.Tkv * D.BH;
-        const int bpc = (int)std::max(1L, std::min((long)kSummBlocksPerChunk, blocks / 2048));
+        const int bpc = (int)std::max(1L, std::min(kMaxBlocksPerGroup, blocks / 2048));
         dim3 gh((D.Tkv + bpc - 1) / bpc, (unsigned)D.BH);
         summaries_mfma_kernel<128, true><<<gh, 256, 0, s>>>(
             (const uint16_t*)K, (const uint16_t*)V, D.skip_sparse ? nullptr : ws.vt, nullptr,
