@@ -147,6 +147,48 @@ __device__ inline void sub_bf16_8(float (&acc)[8][8], const uint16_t* src, int t
         }
     }
 }
+// acc -= src(0), .., src(n - 1) (bf16 d x d matrices) in that order, the
+// loads of four matrices issued together: the subtraction itself is cheap
+// and the loop is bound by the latency of the gathers
+template <typename F>
+__device__ inline void sub_bf16_8_seq(float (&acc)[8][8], int n, F src, int t) {
+    int r = 0;
+    for (; r + 4 <= n; r += 4) {
+        uint4 u[4][8];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const uint16_t* p = src(r + q);
+#pragma unroll
+            for (int m = 0; m < 8; ++m) u[q][m] = *reinterpret_cast<const uint4*>(p + 8 * (t + 256 * m));
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+            for (int m = 0; m < 8; ++m) {
+                const uint32_t wv[4] = {u[q][m].x, u[q][m].y, u[q][m].z, u[q][m].w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    acc[m][2 * e] -= __uint_as_float(wv[e] << 16);
+                    acc[m][2 * e + 1] -= __uint_as_float(wv[e] & 0xffff0000u);
+                }
+            }
+    }
+    for (; r < n; ++r) sub_bf16_8(acc, src(r), t);
+}
+// z - src(0) - .. - src(n - 1), in that order, four loads at a time
+template <typename F>
+__device__ inline float sub_seq(float z, int n, F src) {
+    int r = 0;
+    for (; r + 4 <= n; r += 4) {
+        const float a = src(r), b = src(r + 1), c = src(r + 2), d = src(r + 3);
+        z -= a;
+        z -= b;
+        z -= c;
+        z -= d;
+    }
+    for (; r < n; ++r) z -= src(r);
+    return z;
+}
 __device__ inline void put_dd8(float* dst, const float (&acc)[8][8], int t) {
 #pragma unroll
     for (int m = 0; m < 8; ++m) {
@@ -182,14 +224,13 @@ __global__ __launch_bounds__(256) void bwd_lin_rows_kernel(
     {
         float acc[8][8];
         load_base8(acc, htot + (size_t)bh * kD * kD, t);
-        for (int r = 0; r < k; ++r)
-            sub_bf16_8(acc, hb16 + ((size_t)bh * Tkv + sel[r]) * kD * kD, t);
+        sub_bf16_8_seq(acc, k, [&](int r) { return hb16 + ((size_t)bh * Tkv + sel[r]) * kD * kD; },
+                       t);
         put_dd8(sH, acc, t);
-        if (t < kD) {
-            float z = ztot[(size_t)bh * kD + t];
-            for (int r = 0; r < k; ++r) z -= zblk[((size_t)bh * Tkv + sel[r]) * kD + t];
-            sZ[t] = z;
-        }
+        if (t < kD)
+            sZ[t] = sub_seq(ztot[(size_t)bh * kD + t], k, [&](int r) {
+                return zblk[((size_t)bh * Tkv + sel[r]) * kD + t];
+            });
     }
     const float a = alpha_of(alpha, bh, H, qb, Tq, alpha_qblock);
     const float om = 1.0f - a;
@@ -317,14 +358,13 @@ __global__ __launch_bounds__(256) void bwd_lin_keys_kernel(
     {
         float acc[8][8];
         load_base8(acc, dHt + (size_t)bh * kD * kD, t);
-        for (int n = n0; n < n1; ++n)
-            sub_bf16_8(acc, dHb16 + ((size_t)bh * Tq + L[n]) * kD * kD, t);
+        sub_bf16_8_seq(acc, n1 - n0,
+                       [&](int r) { return dHb16 + ((size_t)bh * Tq + L[n0 + r]) * kD * kD; }, t);
         put_dd8(sH, acc, t);
-        if (t < kD) {
-            float z = dZt[(size_t)bh * kD + t];
-            for (int n = n0; n < n1; ++n) z -= dZq[((size_t)bh * Tq + L[n]) * kD + t];
-            sZ[t] = z;
-        }
+        if (t < kD)
+            sZ[t] = sub_seq(dZt[(size_t)bh * kD + t], n1 - n0, [&](int r) {
+                return dZq[((size_t)bh * Tq + L[n0 + r]) * kD + t];
+            });
     }
     fill64<false>(sA, V + hb, st.t, j * 64, N, t);
     fill64<true>(sB, K + hb, st.t, j * 64, N, t);
