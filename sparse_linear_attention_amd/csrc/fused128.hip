@@ -463,12 +463,13 @@ __global__ __launch_bounds__(256, 2) void fused128_kernel(
                         const float p0 = __builtin_amdgcn_exp2f(fmaf(sc[kq >> 1][8 * (kq & 1) + e], c_tile, bias));
                         const float p1 = __builtin_amdgcn_exp2f(fmaf(sc[kq >> 1][8 * (kq & 1) + e + 1], c_tile, bias));
                         // only the low half is decoded: the high half's
-                        // source is any live register
+                        // source is any live register.  Decoded straight to
+                        // fp16 (scale 1; every e4m3 value is an fp16 value)
                         const int code =
                             __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, __float_as_int(p0), false);
-                        const auto back = __builtin_amdgcn_cvt_pk_f32_fp8(code, false);
-                        pf[e] = (_Float16)back[0];
-                        pf[e + 1] = (_Float16)back[1];
+                        const f16x2 back = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(code, 1.0f, false);
+                        pf[e] = back[0];
+                        pf[e + 1] = back[1];
                     }
                 } else {
     #pragma unroll
