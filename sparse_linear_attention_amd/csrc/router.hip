@@ -375,7 +375,9 @@ __global__ __launch_bounds__(256) void topk_kernel(const double* __restrict__ S,
 // digits start at the highest bit where the row's keys differ (the bits above
 // are common to all keys, and the first 8-bit digit would otherwise put every
 // key in one bin).  Then every larger key and the lowest-index keys equal to
-// it are kept, as in topk_kernel, indices ascending.
+// it are kept, as in topk_kernel, indices ascending.  For SLA v1 (kl > 0) a
+// second selection takes the kl smallest scores, ties to the higher index
+// (topk_kernel's low pass), and marks them 0xFF in the mask.
 constexpr int kStRows = 16;
 constexpr int kStMaxTkv = 1200;  // 16 rows of keys + 8 histograms fit 160 KiB of LDS
 
@@ -396,12 +398,119 @@ __device__ inline unsigned long long wave_or64(unsigned long long v) {
     return ((unsigned long long)hi << 32) | lo;
 }
 
+constexpr int kStSlots = (kStMaxTkv + 63) / 64;
+
+// Radix select over one row's keys held by a wave (the key of position
+// p = lane + 64 t in kv[t], positions below n, 0 < kk < n): the kk largest
+// keys are those above thr on the bits pmask, and the first kr keys (lowest
+// positions) equal to it there.  Digits of 8 bits start at the highest bit
+// where the keys differ; h is the wave's 256-bin histogram in LDS.
+__device__ inline void wave_radix_select(const unsigned long long (&kv)[kStSlots], int n, int kk,
+                                         unsigned* h, int lane, unsigned long long& thr,
+                                         unsigned long long& pmask_out, int& kr_out) {
+    const unsigned long long key0 =
+        ((unsigned long long)(unsigned)__shfl((int)(kv[0] >> 32), 0) << 32) |
+        (unsigned)__shfl((int)(unsigned)kv[0], 0);
+    unsigned long long diff = 0;
+#pragma unroll
+    for (int t = 0; t < kStSlots; ++t)
+        if (lane + 64 * t < n) diff |= kv[t] ^ key0;
+    diff = wave_or64(diff);
+    int hi = diff ? 63 - __clzll((long long)diff) : -1;
+    // bits above hi are common: the prefix starts as those bits of any key
+    unsigned long long pmask = hi < 0 ? ~0ull : hi == 63 ? 0ull : ~((2ull << hi) - 1ull);
+    unsigned long long prefix = key0 & pmask;
+    int kr = kk;
+    for (; hi >= 0; hi -= 8) {
+        const int lo = hi >= 7 ? hi - 7 : 0;
+        *reinterpret_cast<uint4*>(h + 4 * lane) = make_uint4(0u, 0u, 0u, 0u);
+        wave_lds_sync();
+#pragma unroll
+        for (int t = 0; t < kStSlots; ++t)
+            if (lane + 64 * t < n && (kv[t] & pmask) == prefix)
+                atomicAdd(&h[(unsigned)(kv[t] >> lo) & 255u], 1u);
+        wave_lds_sync();
+        // lane l holds bins 255 - 4 l - q (descending); inclusive scan
+        unsigned c[4], tot = 0;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            c[q] = h[255 - 4 * lane - q];
+            tot += c[q];
+        }
+        unsigned incl = tot;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const unsigned o = __shfl_up(incl, off);
+            if (lane >= off) incl += o;
+        }
+        const unsigned excl = incl - tot;
+        const bool found = excl < (unsigned)kr && (unsigned)kr <= incl;
+        int digit = 0, nkr = 0, done = 0;
+        if (found) {
+            unsigned run = excl;
+            digit = -1;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                if (digit < 0) {
+                    if (run + c[q] >= (unsigned)kr) {
+                        digit = 255 - 4 * lane - q;
+                        nkr = kr - (int)run;
+                        // the bin holds exactly the keys still wanted
+                        done = c[q] == (unsigned)nkr;
+                    } else {
+                        run += c[q];
+                    }
+                }
+            }
+        }
+        const int src = __ffsll((unsigned long long)__ballot(found)) - 1;
+        digit = __shfl(digit, src);
+        nkr = __shfl(nkr, src);
+        done = __shfl(done, src);
+        // a last digit narrower than 8 bits also carries bits above hi,
+        // which equal the prefix's there
+        prefix |= (unsigned long long)(unsigned)digit << lo;
+        pmask |= (unsigned long long)((2u << (hi - lo)) - 1u) << lo;
+        kr = nkr;
+        wave_lds_sync();  // the bins are read before the next clear
+        if (done) break;
+    }
+    thr = prefix;
+    pmask_out = pmask;
+    kr_out = kr;
+}
+
+// f(p, selected, rank among the selected) for every position p < n, in
+// ascending order, after wave_radix_select
+template <typename F>
+__device__ inline void wave_emit(const unsigned long long (&kv)[kStSlots], int n,
+                                 unsigned long long thr, unsigned long long pmask, int kr,
+                                 int lane, F f) {
+    const unsigned long long below = (1ull << lane) - 1ull;
+    int eq_base = 0, out_base = 0;
+#pragma unroll
+    for (int t = 0; t < kStSlots; ++t) {
+        const int p = lane + 64 * t;
+        const bool in = p < n;
+        const unsigned long long key = kv[t] & pmask;
+        const bool gt = in && key > thr;
+        const bool eq = in && key == thr;
+        const unsigned long long be = __ballot(eq);
+        const bool sel = gt || (eq && eq_base + __popcll(be & below) < kr);
+        const unsigned long long bs = __ballot(sel);
+        if (in) f(p, sel, out_base + __popcll(bs & below));
+        eq_base += __popcll(be);
+        out_base += __popcll(bs);
+    }
+}
+
 template <int d>
 __global__ __launch_bounds__(512) void score_topk_kernel(const double* __restrict__ qt,
                                                          const double* __restrict__ kt, int Tq,
                                                          int Tkv, int k,
                                                          int32_t* __restrict__ idx,
-                                                         uint8_t* __restrict__ mask) {
+                                                         uint8_t* __restrict__ mask, int kl,
+                                                         int32_t* __restrict__ negl) {
     __shared__ unsigned long long keys[kStRows * kStMaxTkv];  // [row][Tkv]
     __shared__ unsigned hist[8][256];
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -442,112 +551,67 @@ __global__ __launch_bounds__(512) void score_topk_kernel(const double* __restric
     __syncthreads();
 
     // ---- selection, one row at a time per wave, the row's keys in registers
-    // (key j in lane j % 64, slot j / 64)
-    constexpr int kSlots = (kStMaxTkv + 63) / 64;
+    // (position p in lane p % 64, slot p / 64)
     unsigned* h = hist[w];
-    const unsigned long long below = (1ull << lane) - 1ull;
     for (int rr = w; rr < kStRows; rr += 8) {
         const int i = i0 + rr;
         if (i >= Tq) break;
         const size_t row = (size_t)bh * Tq + i;
-        int32_t* irow = idx + row * k;
         uint8_t* mrow = mask ? mask + row * Tkv : nullptr;
-        if (k == Tkv) {  // everything selected
-            for (int j = lane; j < Tkv; j += 64) {
-                if (mrow) mrow[j] = 1;
-                irow[j] = j;
-            }
-            continue;
-        }
-        unsigned long long kv[kSlots];
-#pragma unroll
-        for (int t = 0; t < kSlots; ++t) {
-            const int j = lane + 64 * t;
-            kv[t] = j < Tkv ? keys[rr * Tkv + j] : 0ull;
-        }
-        const unsigned long long key0 = keys[rr * Tkv];
-        unsigned long long diff = 0;
-#pragma unroll
-        for (int t = 0; t < kSlots; ++t)
-            if (lane + 64 * t < Tkv) diff |= kv[t] ^ key0;
-        diff = wave_or64(diff);
-        int hi = diff ? 63 - __clzll((long long)diff) : -1;
-        // bits above hi are common: the prefix starts as those bits of any key
-        unsigned long long pmask = hi < 0 ? ~0ull : hi == 63 ? 0ull : ~((2ull << hi) - 1ull);
-        unsigned long long prefix = key0 & pmask;
-        int kr = k;
-        for (; hi >= 0; hi -= 8) {
-            const int lo = hi >= 7 ? hi - 7 : 0;
-            *reinterpret_cast<uint4*>(h + 4 * lane) = make_uint4(0u, 0u, 0u, 0u);
-            wave_lds_sync();
-#pragma unroll
-            for (int t = 0; t < kSlots; ++t)
-                if (lane + 64 * t < Tkv && (kv[t] & pmask) == prefix)
-                    atomicAdd(&h[(unsigned)(kv[t] >> lo) & 255u], 1u);
-            wave_lds_sync();
-            // lane l holds bins 255 - 4 l - q (descending); inclusive scan
-            unsigned c[4], tot = 0;
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                c[q] = h[255 - 4 * lane - q];
-                tot += c[q];
-            }
-            unsigned incl = tot;
-#pragma unroll
-            for (int off = 1; off < 64; off <<= 1) {
-                const unsigned o = __shfl_up(incl, off);
-                if (lane >= off) incl += o;
-            }
-            const unsigned excl = incl - tot;
-            const bool found = excl < (unsigned)kr && (unsigned)kr <= incl;
-            int digit = 0, nkr = 0, done = 0;
-            if (found) {
-                unsigned run = excl;
-                digit = -1;
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    if (digit < 0) {
-                        if (run + c[q] >= (unsigned)kr) {
-                            digit = 255 - 4 * lane - q;
-                            nkr = kr - (int)run;
-                            // the bin holds exactly the keys still wanted
-                            done = c[q] == (unsigned)nkr;
-                        } else {
-                            run += c[q];
-                        }
-                    }
+        const unsigned long long* krow = keys + rr * Tkv;
+        unsigned long long kv[kStSlots];
+        if (k > 0) {  // the k largest, ties to the lower index; mask 1 / 0
+            int32_t* irow = idx + row * k;
+            if (k == Tkv) {  // everything selected
+                for (int j = lane; j < Tkv; j += 64) {
+                    if (mrow) mrow[j] = 1;
+                    irow[j] = j;
                 }
-            }
-            const int src = __ffsll((unsigned long long)__ballot(found)) - 1;
-            digit = __shfl(digit, src);
-            nkr = __shfl(nkr, src);
-            done = __shfl(done, src);
-            // a last digit narrower than 8 bits also carries bits above hi,
-            // which equal the prefix's there
-            prefix |= (unsigned long long)(unsigned)digit << lo;
-            pmask |= (unsigned long long)((2u << (hi - lo)) - 1u) << lo;
-            kr = nkr;
-            wave_lds_sync();  // the bins are read before the next clear
-            if (done) break;
-        }
-        const unsigned long long thr = prefix;
-        int eq_base = 0, out_base = 0;
+            } else {
 #pragma unroll
-        for (int t = 0; t < kSlots; ++t) {
-            const int j = lane + 64 * t;
-            const bool in = j < Tkv;
-            const unsigned long long key = kv[t] & pmask;
-            const bool gt = in && key > thr;
-            const bool eq = in && key == thr;
-            const unsigned long long be = __ballot(eq);
-            const bool sel = gt || (eq && eq_base + __popcll(be & below) < kr);
-            const unsigned long long bs = __ballot(sel);
-            if (in) {
-                if (mrow) mrow[j] = sel ? 1 : 0;
-                if (sel) irow[out_base + __popcll(bs & below)] = j;
+                for (int t = 0; t < kStSlots; ++t) {
+                    const int j = lane + 64 * t;
+                    kv[t] = j < Tkv ? krow[j] : 0ull;
+                }
+                unsigned long long thr, pm;
+                int kr;
+                wave_radix_select(kv, Tkv, k, h, lane, thr, pm, kr);
+                wave_emit(kv, Tkv, thr, pm, kr, lane, [&](int j, bool sel, int rank) {
+                    if (mrow) mrow[j] = sel ? 1 : 0;
+                    if (sel) irow[rank] = j;
+                });
             }
-            eq_base += __popcll(be);
-            out_base += __popcll(bs);
+        } else if (mrow) {
+            for (int j = lane; j < Tkv; j += 64) mrow[j] = 0;
+        }
+        if (kl > 0) {
+            // SLA v1: the kl LAST blocks of the order (score descending, index
+            // ascending), i.e. the smallest scores with ties to the higher
+            // index: the inverted keys at reversed positions p = Tkv - 1 - j,
+            // selected like the k largest; the mask gets 0xFF there (the
+            // stores above come first in this wave's order) and the indices
+            // leave ascending
+            int32_t* nrow = negl + row * kl;
+            if (kl == Tkv) {
+                for (int j = lane; j < Tkv; j += 64) {
+                    if (mrow) mrow[j] = 0xFF;
+                    nrow[j] = j;
+                }
+            } else {
+#pragma unroll
+                for (int t = 0; t < kStSlots; ++t) {
+                    const int p = lane + 64 * t;
+                    kv[t] = p < Tkv ? ~krow[Tkv - 1 - p] : 0ull;
+                }
+                unsigned long long thr, pm;
+                int kr;
+                wave_radix_select(kv, Tkv, kl, h, lane, thr, pm, kr);
+                wave_emit(kv, Tkv, thr, pm, kr, lane, [&](int p, bool sel, int rank) {
+                    if (!sel) return;
+                    if (mrow) mrow[Tkv - 1 - p] = 0xFF;
+                    nrow[kl - 1 - rank] = Tkv - 1 - p;
+                });
+            }
         }
     }
 }
@@ -640,9 +704,11 @@ hipError_t launch_route(const Dims& D, const void* Q, const void* K, const float
         const dim3 g((D.Tq + kStRows - 1) / kStRows, (unsigned)D.BH);
         timing_before(s, K_SCORE_TOPK);
         if (D.d == 128)
-            score_topk_kernel<128><<<g, 512, 0, s>>>(ws.qt, ws.kt, D.Tq, D.Tkv, D.k, idx, mask);
+            score_topk_kernel<128><<<g, 512, 0, s>>>(ws.qt, ws.kt, D.Tq, D.Tkv, D.k, idx, mask, 0,
+                                                     nullptr);
         else
-            score_topk_kernel<64><<<g, 512, 0, s>>>(ws.qt, ws.kt, D.Tq, D.Tkv, D.k, idx, mask);
+            score_topk_kernel<64><<<g, 512, 0, s>>>(ws.qt, ws.kt, D.Tq, D.Tkv, D.k, idx, mask, 0,
+                                                    nullptr);
         timing_after(s, K_SCORE_TOPK);
         return hipGetLastError();
     }
@@ -680,6 +746,18 @@ hipError_t launch_route_v1(const Dims& D, const void* Q, const void* K, int kl, 
             (const uint16_t*)Q, (const uint16_t*)K, nullptr, nullptr, ws.qt, ws.kt, D.N, D.d,
             D.bq, D.bkv, D.Tq, D.Tkv, D.H, D.w_heads, D.st);
     timing_after(s, K_POOL_PROJECT);
+    if (D.Tkv <= kStMaxTkv) {  // scores, both selections and the mask in one pass
+        const dim3 g((D.Tq + kStRows - 1) / kStRows, (unsigned)D.BH);
+        timing_before(s, K_SCORE_TOPK);
+        if (D.d == 128)
+            score_topk_kernel<128><<<g, 512, 0, s>>>(ws.qt, ws.kt, D.Tq, D.Tkv, D.k, crit, mask,
+                                                     kl, negl);
+        else
+            score_topk_kernel<64><<<g, 512, 0, s>>>(ws.qt, ws.kt, D.Tq, D.Tkv, D.k, crit, mask,
+                                                    kl, negl);
+        timing_after(s, K_SCORE_TOPK);
+        return hipGetLastError();
+    }
     timing_before(s, K_SCORE);
     launch_score_kernel(D, ws, s);
     timing_after(s, K_SCORE);

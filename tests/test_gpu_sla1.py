@@ -90,6 +90,33 @@ def test_sla1_parity(orc, dev, case):
     compare_v1(orc, x, O, oc, on, wp, phi, low, orc.all_blocks(oracle_problem(orc, w, phi)), wh)
 
 
+def test_sla1_route_all_scores_equal(orc, dev):
+    """Every key block the same, so every score of a row ties: the critical
+    blocks are the k_h lowest indices (ties to the lower index) and the
+    negligible ones the k_l highest (the order's last blocks)."""
+    w = I.Workload("v1-ties", 1, 2, 3000, 128, 128, 64, 0.1, "bf16", "smooth", seed=5)
+    x = I.make_inputs(w)
+    x.k = np.ascontiguousarray(np.broadcast_to(x.k[:, :, :1, :], x.k.shape))
+    q, k, v, _, _, _ = to_dev(x, dev)
+    low = 0.2
+    crit, negl, oc, on = route_both(orc, x, q, k, low)
+    kh, kl, T = crit.shape[-1], negl.shape[-1], w.Tkv
+    assert (crit.cpu().numpy() == np.arange(kh)).all()
+    assert (negl.cpu().numpy() == np.arange(T - kl, T)).all()
+
+
+@pytest.mark.parametrize("N", [1200 * 64, 1200 * 64 + 1])
+def test_sla1_route_at_the_one_pass_limit(orc, dev, N):
+    """Critical and negligible indices and the ternary mask exact at 1200 KV
+    blocks (scores and both selections in one pass) and at 1201 (scores
+    through memory, two top-k passes)."""
+    say(f"case sla1 route at T_kv limit: N={N}")
+    w = I.Workload("v1-limit", 1, 2, N, 128, 128, 64, 0.05, "bf16", "smooth", seed=7)
+    x = I.make_inputs(w)
+    q, k, v, _, _, _ = to_dev(x, dev)
+    route_both(orc, x, q, k, 0.1)
+
+
 # the vector-ALU kernels: b_q = 64 (the SLA notes' b_q = b_kv = 64), d = 64, fp32
 VALU_CASES = [  # name, N, H, d, b_q, dtype, k_h frac, k_l frac, phi, w_heads
     ("b64-ragged", 700, 2, 128, 64, "bf16", 0.2, 0.3, S.PHI_SOFTMAX, 1),
