@@ -404,8 +404,9 @@ sla2_status sla2_backward(const sla2_problem* p, const void* Q, const void* K, c
  *   S of sla2_route (same pooling, projections and fp64 arithmetic), with
  *   lambda_i found by bisection so that sum_j M_ij = k (k = sla2_topk(p)):
  *   f(lambda) = sum_j sigma(S_ij / tau + lambda) - k over the bracket
- *   [-max_j S_ij / tau - 50, -min_j S_ij / tau + 50], 100 halvings, lambda =
- *   the final midpoint.  k = 0 gives M = 0 (lambda = -inf), k = T_kv M = 1
+ *   [-max_j S_ij / tau - 50, -min_j S_ij / tau + 50], 100 halvings (stopped
+ *   early once the midpoint equals an end of the bracket, after which no
+ *   halving can move it), lambda = the final midpoint.  k = 0 gives M = 0 (lambda = -inf), k = T_kv M = 1
  *   (lambda = +inf).  The pages use tau = 0.1.
  * Out: M [B,H,T_q,T_kv] fp32; lambda [B,H,T_q] fp64, or NULL.
  * ws : sla2_workspace_bytes(p, SLA2_OP_ROUTE) bytes.  tau <= 0 or not finite:

@@ -63,6 +63,9 @@ __global__ __launch_bounds__(256) void soft_topk_kernel(const double* __restrict
     double lo = -mx - 50.0, hi = -mn + 50.0;
     for (int it = 0; it < kSoftIters; ++it) {
         const double mid = 0.5 * (lo + hi);
+        // once the midpoint equals an end, no halving can move lambda (the
+        // final midpoint) any more: the rest of the 100 would be no-ops
+        if (mid == lo || mid == hi) break;
         double f = 0.0;
         for (int j = t; j < Tkv; j += 256) f += sigmoid(x[j] + mid);
         f = block_sum(f, red) - (double)k;
@@ -72,6 +75,67 @@ __global__ __launch_bounds__(256) void soft_topk_kernel(const double* __restrict
     const double lam = 0.5 * (lo + hi);
     for (int j = t; j < Tkv; j += 256) mrow[j] = (float)sigmoid(x[j] + lam);
     if (t == 0 && lambda) lambda[row] = lam;
+}
+
+// The same bisection with one wave per score row (four rows per work-group
+// of 256), for rows of at most 64 SLOTS blocks: the row's S / tau stays in
+// registers (block j in lane j % 64, slot j / 64) and the sums are wave
+// reductions, so no work-group barrier is needed.
+__device__ inline double wave_sum_f64(double v) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+    return v;
+}
+template <int SLOTS>
+__global__ __launch_bounds__(256) void soft_topk_wave_kernel(const double* __restrict__ S,
+                                                             long rows, int Tkv, int k,
+                                                             double tau, float* __restrict__ M,
+                                                             double* __restrict__ lambda) {
+    const int lane = threadIdx.x & 63;
+    const long row = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (row >= rows) return;  // the whole wave
+    float* mrow = M + (size_t)row * Tkv;
+    if (k <= 0 || k >= Tkv) {
+        for (int j = lane; j < Tkv; j += 64) mrow[j] = k <= 0 ? 0.0f : 1.0f;
+        if (lane == 0 && lambda) lambda[row] = k <= 0 ? -INFINITY : INFINITY;
+        return;
+    }
+    double x[SLOTS];
+    double mx = -INFINITY, mn = INFINITY;
+#pragma unroll
+    for (int t = 0; t < SLOTS; ++t) {
+        const int j = lane + 64 * t;
+        x[t] = 0.0;
+        if (j < Tkv) {
+            x[t] = S[(size_t)row * Tkv + j] / tau;
+            mx = fmax(mx, x[t]);
+            mn = fmin(mn, x[t]);
+        }
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+        mx = fmax(mx, __shfl_xor(mx, off));
+        mn = fmin(mn, __shfl_xor(mn, off));
+    }
+    double lo = -mx - 50.0, hi = -mn + 50.0;
+    for (int it = 0; it < kSoftIters; ++it) {
+        const double mid = 0.5 * (lo + hi);
+        if (mid == lo || mid == hi) break;  // (as in soft_topk_kernel)
+        double f = 0.0;
+#pragma unroll
+        for (int t = 0; t < SLOTS; ++t)
+            if (lane + 64 * t < Tkv) f += sigmoid(x[t] + mid);
+        f = wave_sum_f64(f) - (double)k;
+        if (f > 0.0) hi = mid;
+        else lo = mid;
+    }
+    const double lam = 0.5 * (lo + hi);
+#pragma unroll
+    for (int t = 0; t < SLOTS; ++t) {
+        const int j = lane + 64 * t;
+        if (j < Tkv) mrow[j] = (float)sigmoid(x[t] + lam);
+    }
+    if (lane == 0 && lambda) lambda[row] = lam;
 }
 
 // dS = s / tau (dM - sum dM s / sum s), s = M (1 - M); grid (Tq, BH)
@@ -196,8 +260,15 @@ hipError_t launch_soft_topk(const Dims& D, const void* Q, const void* K, const f
                             const RouteWS& ws, hipStream_t s) {
     hipError_t e = launch_scores(D, Q, K, Wq, Wk, ws, s);
     if (e != hipSuccess) return e;
-    soft_topk_kernel<<<dim3(D.Tq, (unsigned)D.BH), 256, sizeof(double) * D.Tkv, s>>>(
-        ws.S, D.Tq, D.Tkv, D.k, tau, M, lambda);
+    constexpr int kWaveSlots = 19;  // rows of up to 1216 blocks: one wave each
+    if (D.Tkv <= 64 * kWaveSlots) {
+        const long rows = D.BH * (long)D.Tq;
+        soft_topk_wave_kernel<kWaveSlots><<<dim3((unsigned)((rows + 3) / 4)), 256, 0, s>>>(
+            ws.S, rows, D.Tkv, D.k, tau, M, lambda);
+    } else {
+        soft_topk_kernel<<<dim3(D.Tq, (unsigned)D.BH), 256, sizeof(double) * D.Tkv, s>>>(
+            ws.S, D.Tq, D.Tkv, D.k, tau, M, lambda);
+    }
     return hipGetLastError();
 }
 
