@@ -399,6 +399,9 @@ __device__ inline unsigned long long wave_or64(unsigned long long v) {
 }
 
 constexpr int kStSlots = (kStMaxTkv + 63) / 64;
+// the filtered selection is tried for k up to this (on the Wan-shape scores
+// about 46 keys pass the filter at k = 36 and 130 at k = 60)
+constexpr int kFilterMaxK = 48;
 
 // Radix select over one row's keys held by a wave (the key of position
 // p = lane + 64 t in kv[t], positions below n, 0 < kk < n): the kk largest
@@ -478,6 +481,85 @@ __device__ inline void wave_radix_select(const unsigned long long (&kv)[kStSlots
     thr = prefix;
     pmask_out = pmask;
     kr_out = kr;
+}
+
+__device__ inline unsigned long long shfl_xor64(unsigned long long v, int m) {
+    const unsigned lo = (unsigned)__shfl_xor((int)(unsigned)v, m);
+    const unsigned hi = (unsigned)__shfl_xor((int)(unsigned)(v >> 32), m);
+    return ((unsigned long long)hi << 32) | lo;
+}
+__device__ inline unsigned long long umax64(unsigned long long a, unsigned long long b) {
+    return a > b ? a : b;
+}
+__device__ inline unsigned long long umin64(unsigned long long a, unsigned long long b) {
+    return a < b ? a : b;
+}
+
+// The same result as wave_radix_select (thr on all 64 bits, kr) for kk <= 64,
+// by a filter: every lane's largest key is an element of the row, so at
+// least kk keys are >= tau, the kk-th largest of the 64 lane maxima, and so
+// is the kk-th largest key of the row.  The keys >= tau (at most 128 of them)
+// are gathered through the wave's LDS scratch sc (128 entries), sorted
+// descending by a bitonic network over two slots per lane, and the kk-th of
+// them is thr; kr counts the keys equal to thr among the first kk.  Returns
+// false (nothing decided) when more than 128 keys pass the filter.
+__device__ inline bool wave_filter_select(const unsigned long long (&kv)[kStSlots], int n,
+                                          int kk, unsigned long long* sc, int lane,
+                                          unsigned long long& thr, int& kr_out) {
+    unsigned long long m = 0ull;  // below every key of a real score
+#pragma unroll
+    for (int t = 0; t < kStSlots; ++t)
+        if (lane + 64 * t < n) m = umax64(m, kv[t]);
+    // lane maxima sorted descending (bitonic; blocks with lane & size clear
+    // run descending, the lower lane of a pair keeping the larger key)
+#pragma unroll
+    for (int size = 2; size <= 64; size <<= 1)
+#pragma unroll
+        for (int j = size >> 1; j > 0; j >>= 1) {
+            const unsigned long long o = shfl_xor64(m, j);
+            const bool keep_max = ((lane & j) == 0) == ((lane & size) == 0);
+            m = keep_max ? umax64(m, o) : umin64(m, o);
+        }
+    const unsigned long long tau = ((unsigned long long)(unsigned)__shfl((int)(m >> 32), kk - 1)
+                                    << 32) |
+                                   (unsigned)__shfl((int)(unsigned)m, kk - 1);
+    // gather the keys >= tau (their order does not matter)
+    const unsigned long long below = (1ull << lane) - 1ull;
+    int c = 0;
+#pragma unroll
+    for (int t = 0; t < kStSlots; ++t) {
+        const bool in = lane + 64 * t < n && kv[t] >= tau;
+        const unsigned long long b = __ballot(in);
+        const int r = c + __popcll(b & below);
+        if (in && r < 128) sc[r] = kv[t];
+        c += __popcll(b);
+    }
+    wave_lds_sync();
+    if (c > 128) return false;
+    unsigned long long a = lane < c ? sc[lane] : 0ull;        // element lane
+    unsigned long long b = lane + 64 < c ? sc[lane + 64] : 0ull;  // element lane + 64
+    wave_lds_sync();  // read before the scratch is written again
+    // 128 elements (index lane and lane + 64) sorted descending
+#pragma unroll
+    for (int size = 2; size <= 128; size <<= 1)
+#pragma unroll
+        for (int j = size >> 1; j > 0; j >>= 1) {
+            if (j == 64) {  // partners in the same lane; one descending block
+                const unsigned long long x = umax64(a, b), y = umin64(a, b);
+                a = x;
+                b = y;
+            } else {
+                const unsigned long long oa = shfl_xor64(a, j), ob = shfl_xor64(b, j);
+                const bool low = (lane & j) == 0;
+                const bool da = (lane & size) == 0, db = ((lane + 64) & size) == 0;
+                a = (low == da) ? umax64(a, oa) : umin64(a, oa);
+                b = (low == db) ? umax64(b, ob) : umin64(b, ob);
+            }
+        }
+    thr = ((unsigned long long)(unsigned)__shfl((int)(a >> 32), kk - 1) << 32) |
+          (unsigned)__shfl((int)(unsigned)a, kk - 1);
+    kr_out = __popcll(__ballot(lane < kk && a == thr));
+    return true;
 }
 
 // f(p, selected, rank among the selected) for every position p < n, in
@@ -573,9 +655,12 @@ __global__ __launch_bounds__(512) void score_topk_kernel(const double* __restric
                     const int j = lane + 64 * t;
                     kv[t] = j < Tkv ? krow[j] : 0ull;
                 }
-                unsigned long long thr, pm;
+                unsigned long long thr, pm = ~0ull;
                 int kr;
-                wave_radix_select(kv, Tkv, k, h, lane, thr, pm, kr);
+                if (k > kFilterMaxK ||
+                    !wave_filter_select(kv, Tkv, k, reinterpret_cast<unsigned long long*>(h),
+                                        lane, thr, kr))
+                    wave_radix_select(kv, Tkv, k, h, lane, thr, pm, kr);
                 wave_emit(kv, Tkv, thr, pm, kr, lane, [&](int j, bool sel, int rank) {
                     if (mrow) mrow[j] = sel ? 1 : 0;
                     if (sel) irow[rank] = j;
