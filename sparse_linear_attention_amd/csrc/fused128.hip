@@ -330,18 +330,24 @@ __global__ __launch_bounds__(256, 2) void fused128_kernel(
     };
     auto ctile = [&](int jx) { return LOWBIT ? c_base * sk_h[jx] : c_base; };
     // the query block's row of the linear-branch product into LDS by
-    // direct loads: H_i^T (bf16, entry e * 128 + c) as [128 e rows][256 B]
-    // with chunk c' of row e at c' ^ (e & 15) (the K tile layout, 8 pieces of
-    // 1 KB per wave), Z_i (fp32) after it.  Issued at the start of the last
-    // tile step, into the K stages (free from then on; 32.5 KB of the 48),
-    // so that the loads run under the last P V (bf16 path).
+    // direct loads: H_i^T (bf16) as [128 e rows][256 B] with chunk c' (c =
+    // 8 c' ..) of row e at c' ^ (e & 15) (the K tile layout, 8 pieces of 1 KB
+    // per wave), Z_i (fp32) after it.  The row holds the chunk at hz_unit(e,
+    // c'); for the rows e = 16 i + r of piece i that unit is 512 (i / 2) +
+    // 16 (i % 2) plus a part that depends on (r, c') only, so the lane's
+    // offset is set once and the piece adds a uniform one.  Issued at the
+    // start of the last tile step, into the K stages (free from then on; 32.5
+    // KB of the 48), so that the loads run under the last P V (bf16 path).
     constexpr bool kEarlyH = LIN && !LOWBIT;
     auto issue_h = [&]() {
         const rsrc_t rh = head_rsrc(HZ + (size_t)bh * Tq * kHzRowBytes);
-        const uint32_t hoff = k_lane_off(w, lane, 256u);
+        const int hr = 4 * w + (lane >> 4), hc = (lane & 15) ^ hr;
+        const uint32_t hoff = 16u * (uint32_t)hz_unit(hr, hc);
         const uint32_t row0 = (uint32_t)qb * kHzRowBytes;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) load_lds16(rh, hoff, row0 + 4096 * i, s_lds + (4 * i + w) * 1024);
+        for (int i = 0; i < 8; ++i)
+            load_lds16(rh, hoff, row0 + 8192 * (i >> 1) + 256 * (i & 1),
+                       s_lds + (4 * i + w) * 1024);
         if (w < 2)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rh, SLA2_LDS(s_lds + 32768 + 256 * w), 4,
                                                      (uint32_t)lane * 4,
@@ -531,7 +537,7 @@ __global__ __launch_bounds__(256, 2) void fused128_kernel(
     for (int i = 0; i < 4; ++i) ol[i] = zero16();
     float inv_den = 0.0f;
     if (LIN) {
-        // H_i^T (bf16 row of the product: entry e * 128 + c) in LDS as
+        // H_i^T (bf16 row of the product, units at hz_unit) in LDS as
         // [128 d rows][256 B], chunk c' of row e at c' ^ (e & 15); Z_i fp32
         char* sH = s_lds;
         float* sZ = reinterpret_cast<float*>(s_lds + 32768);
@@ -545,7 +551,7 @@ __global__ __launch_bounds__(256, 2) void fused128_kernel(
             const int he = t >> 1, hc = 8 * (t & 1);  // row e, 16-byte chunks hc .. hc + 7
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
-                const uint4 v = *reinterpret_cast<const uint4*>(hrow + he * 256 + (hc + i) * 16);
+                const uint4 v = *reinterpret_cast<const uint4*>(hrow + 16 * hz_unit(he, hc + i));
                 *reinterpret_cast<uint4*>(sH + he * 256 + (((hc + i) ^ (he & 15)) << 4)) = v;
             }
             if (t < 128) sZ[t] = reinterpret_cast<const float*>(hrow + 2 * 128 * 128)[t];

@@ -38,6 +38,11 @@ namespace {
 using namespace cdna4;
 
 __device__ inline float bf16_lo(unsigned w) { return __uint_as_float(w << 16); }
+// two floats as bf16 (nearest even), a in the low half
+__device__ inline uint32_t pack_bf16x2(float a, float b) {
+    return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)a) |
+           ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)b) << 16);
+}
 __device__ inline float bf16_hi(unsigned w) { return __uint_as_float(w & 0xffff0000u); }
 
 // Cross-lane steps of the fp64 column sums (pooled keys).  Half-exchange:
@@ -94,8 +99,8 @@ constexpr int kTPitch = 64 * 2 + 16;  // bytes per row of a [d][64] fp16 tile in
 
 // HZ: instead of phi(K)^T tiles, z_j and chunk partials, write every block's
 // summaries for the linear-branch product (linear.hip): row j of hz holds
-// h_j^T (V channel e major, phi channel c minor: entry e * D + c) and then
-// z_j, in bf16; V^T tiles only if vt is not null.  With xk not null the pass
+// h_j^T (V channel e, phi channel c; 16-byte units in the order hz_unit
+// gives) and then z_j, in bf16; V^T tiles only if vt is not null.  With xk not null the pass
 // also writes the router's pooled keys ("SLA2 深度解读" 03: the mean of each
 // KV block, [BH][Tkv][D] fp64), from the K rows it holds anyway: each wave
 // sums its channels over the 64 tokens (one per lane) in fp64 by a
@@ -259,8 +264,7 @@ __global__ __launch_bounds__(256, 4) void summaries_mfma_kernel(
         }
         if constexpr (HZ) {
             // h_j (phi channels c x V channels e) = phi(K_j)^T V_j; lane holds
-            // column e and four consecutive rows c per group, stored as
-            // entry e * D + c of h_j^T (8 bytes per group)
+            // column e and four consecutive rows c per group of its tiles
             f32x16 hj[TPW];
 #pragma unroll
             for (int s = 0; s < TPW; ++s) hj[s] = zero16();
@@ -276,17 +280,34 @@ __global__ __launch_bounds__(256, 4) void summaries_mfma_kernel(
                     hj[s] = mfma_f16(a, b, hj[s]);
                 }
             }
-            const int e = 32 * nt_w + l32;
+            // bf16 (nearest even), then units of 8 consecutive c: the lane
+            // pair (l32, l32 + 32) holds c = 8 g + 0..3 and 8 g + 4..7 of
+            // group g; one lane-half swap gives the lower lane group 2 q
+            // whole and the upper lane group 2 q + 1.  With D = 128 wave w
+            // holds e = 32 w + l32 and tile s rows c = 32 s + .., so its
+            // unit is (e, 4 s + 2 q + hl), at hz_unit = ((w * 4 + s) * 2 +
+            // q) * 64 + lane: each store is 1 KB of the row, contiguous
+            static_assert(!HZ || (NT == 4 && MT_STEP == 1), "unit order: D = 128");
 #pragma unroll
             for (int s = 0; s < TPW; ++s) {
-                const int mt = mt_w0 + s * MT_STEP;
+                uint32_t dw[4][2];
 #pragma unroll
                 for (int g4 = 0; g4 < 4; ++g4) {
-                    typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
-                    bf16x4_t b4;
+                    dw[g4][0] = pack_bf16x2(hj[s][4 * g4], hj[s][4 * g4 + 1]);
+                    dw[g4][1] = pack_bf16x2(hj[s][4 * g4 + 2], hj[s][4 * g4 + 3]);
+                }
 #pragma unroll
-                    for (int c = 0; c < 4; ++c) b4[c] = (__bf16)hj[s][4 * g4 + c];
-                    *reinterpret_cast<bf16x4_t*>(hzj + e * D + 32 * mt + 8 * g4 + 4 * hl) = b4;
+                for (int q = 0; q < 2; ++q) {
+                    uint32_t r[2];
+#pragma unroll
+                    for (int h2 = 0; h2 < 2; ++h2) {
+                        const uint32_t send = hl ? dw[2 * q][h2] : dw[2 * q + 1][h2];
+                        const auto x = __builtin_amdgcn_permlane32_swap(send, send, false, false);
+                        r[h2] = hl ? x[0] : x[1];
+                    }
+                    const uint4 u = hl ? make_uint4(r[0], r[1], dw[2 * q + 1][0], dw[2 * q + 1][1])
+                                       : make_uint4(dw[2 * q][0], dw[2 * q][1], r[0], r[1]);
+                    *reinterpret_cast<uint4*>(hzj + (((w * TPW + s) * 2 + q) * 64 + lane) * 8) = u;
                 }
             }
             continue;
