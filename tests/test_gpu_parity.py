@@ -206,6 +206,35 @@ def test_tie_breaking_on_duplicated_blocks(orc, dev):
     assert np.array_equal(mask.cpu().numpy(), omask)
 
 
+def test_selection_paths_with_equal_keys(orc, dev):
+    """The one-pass top-k first keeps the keys at or above the k-th largest of
+    the 64 lane maxima (at most 128, sorted two per lane) and falls back to
+    the radix select when more pass.  Head 0: every key row of the head the
+    same, so all T_kv scores of a row tie (the fallback; the first k blocks).
+    Head 1: two groups of 100 blocks, equal within the group (100 candidates
+    in two slots, ties at the k-th place).  Head 2: the usual keys.  Indices
+    and masks bit-exact against the oracle (ties to the lower index)."""
+    w = wl("equal-keys", "bf16", 200 * 64, 128, 128, 0.17, H=3)
+    say("case selection paths: N=12800 k=34 of 200, equal key groups")
+    x = I.make_inputs(w)
+    nb = w.N // 64
+    x.k[0, 0] = x.k[0, 0, :1]
+    hot = np.random.default_rng(7).choice(nb, 100, replace=False)
+    rows = np.repeat(np.isin(np.arange(nb), hot), 64)
+    ka, kb = x.k[0, 1, 0].copy(), x.k[0, 1, 64 * 100 + 5].copy()
+    x.k[0, 1, rows] = ka
+    x.k[0, 1, ~rows] = kb
+    p, idx, mask, O = run_gpu(x, dev)
+    oidx = check_route(orc, x, idx, mask)
+    k = oidx.shape[-1]
+    assert k <= 48  # the filtered selection is tried
+    assert (oidx[0, 0] == np.arange(k)).all()
+    grp = np.isin(np.arange(nb), hot)
+    # head 1: the first k blocks of one group
+    for r in oidx[0, 1]:
+        assert len(set(grp[r])) == 1
+
+
 @pytest.mark.parametrize("N", [1200 * 64, 1200 * 64 + 1])
 def test_route_at_the_one_pass_limit(orc, dev, N):
     """Selection and mask exact at T_kv = 1200, the most KV blocks whose 16
