@@ -189,6 +189,22 @@ __device__ inline float sub_seq(float z, int n, F src) {
     for (; r < n; ++r) z -= src(r);
     return z;
 }
+// acc -= the fp32 d x d matrix src (the same entries as load_base8)
+__device__ inline void sub_f32_8(float (&acc)[8][8], const float* src, int t) {
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+        const float4 a = *reinterpret_cast<const float4*>(src + 8 * (t + 256 * m));
+        const float4 b = *reinterpret_cast<const float4*>(src + 8 * (t + 256 * m) + 4);
+        acc[m][0] -= a.x;
+        acc[m][1] -= a.y;
+        acc[m][2] -= a.z;
+        acc[m][3] -= a.w;
+        acc[m][4] -= b.x;
+        acc[m][5] -= b.y;
+        acc[m][6] -= b.z;
+        acc[m][7] -= b.w;
+    }
+}
 __device__ inline void put_dd8(float* dst, const float (&acc)[8][8], int t) {
 #pragma unroll
     for (int m = 0; m < 8; ++m) {
@@ -201,7 +217,10 @@ __device__ inline void put_dd8(float* dst, const float (&acc)[8][8], int t) {
 // ---------------------------------------------------------------------------
 // Linear rows pass: one work-group per (head, query block), 256 threads.
 // Writes dQ (the phi chain; the first writer of dQ), dH_i, dZ_i and g . O_l
-// per row into gol.
+// per row into gol.  H_i = h_tot - S_i with S_i the sum of the bf16 h_j of
+// the selected blocks: from ssel (row i of the selection product, fp32; it
+// may be the row of dHq that this work-group overwrites at its end) or, when
+// ssel is null, gathered here.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void bwd_lin_rows_kernel(
     const uint16_t* __restrict__ Q, const float* __restrict__ dO,
@@ -210,7 +229,7 @@ __global__ __launch_bounds__(256) void bwd_lin_rows_kernel(
     const uint16_t* __restrict__ hb16, const float* __restrict__ zblk, float* __restrict__ dQ,
     float* __restrict__ dHq, uint16_t* __restrict__ dHb16, float* __restrict__ dZq,
     float* __restrict__ gol, int N, int Tq, int Tkv, int k, int H, Strides st,
-    int alpha_qblock) {
+    int alpha_qblock, const float* ssel) {
     __shared__ float sH[kD * kLd];  // H_i [c][e]
     __shared__ float sA[64 * kLd];  // phi(q) of 64 rows [m][c]
     __shared__ float sB[64 * kLd];  // dn of the same rows [m][e]
@@ -224,8 +243,11 @@ __global__ __launch_bounds__(256) void bwd_lin_rows_kernel(
     {
         float acc[8][8];
         load_base8(acc, htot + (size_t)bh * kD * kD, t);
-        sub_bf16_8_seq(acc, k, [&](int r) { return hb16 + ((size_t)bh * Tkv + sel[r]) * kD * kD; },
-                       t);
+        if (ssel)
+            sub_f32_8(acc, ssel + ((size_t)bh * Tq + qb) * kD * kD, t);
+        else
+            sub_bf16_8_seq(acc, k,
+                           [&](int r) { return hb16 + ((size_t)bh * Tkv + sel[r]) * kD * kD; }, t);
         put_dd8(sH, acc, t);
         if (t < kD)
             sZ[t] = sub_seq(ztot[(size_t)bh * kD + t], k, [&](int r) {
@@ -333,16 +355,19 @@ __global__ __launch_bounds__(256) void bwd_lin_rows_kernel(
 
 // ---------------------------------------------------------------------------
 // Linear keys pass: one work-group per (head, KV block j), 256 threads.
-// dh_j = dH_tot - sum over the query blocks selecting j of dH_i (ascending),
-// dz_j likewise; writes dK = (dh_j v_u + dz_j) phi'(k_u) and dV = phi(k_u)
-// dh_j (the first writers of dK and dV).
+// dh_j = dH_tot - sum over the query blocks selecting j of dH_i (bf16; from
+// dsel, row j of the transposed selection product, fp32, or gathered here
+// in ascending order when dsel is null), dz_j likewise (gathered); writes
+// dK = (dh_j v_u + dz_j) phi'(k_u) and dV = phi(k_u) dh_j (the first writers
+// of dK and dV).
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void bwd_lin_keys_kernel(
     const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const float* __restrict__ dHt, const float* __restrict__ dZt,
     const uint16_t* __restrict__ dHb16, const float* __restrict__ dZq,
     const int32_t* __restrict__ off, const int32_t* __restrict__ list, float* __restrict__ dK,
-    float* __restrict__ dV, int N, int Tq, int Tkv, int k, int H, Strides st) {
+    float* __restrict__ dV, int N, int Tq, int Tkv, int k, int H, Strides st,
+    const float* __restrict__ dsel) {
     __shared__ float sH[kD * kLd];  // dh_j [c][e]
     __shared__ float sA[64 * kLd];  // V_j [u][e]
     __shared__ float sB[64 * kLd];  // phi(K_j) [u][c]
@@ -358,8 +383,12 @@ __global__ __launch_bounds__(256) void bwd_lin_keys_kernel(
     {
         float acc[8][8];
         load_base8(acc, dHt + (size_t)bh * kD * kD, t);
-        sub_bf16_8_seq(acc, n1 - n0,
-                       [&](int r) { return dHb16 + ((size_t)bh * Tq + L[n0 + r]) * kD * kD; }, t);
+        if (dsel)
+            sub_f32_8(acc, dsel + ((size_t)bh * Tkv + j) * kD * kD, t);
+        else
+            sub_bf16_8_seq(
+                acc, n1 - n0,
+                [&](int r) { return dHb16 + ((size_t)bh * Tq + L[n0 + r]) * kD * kD; }, t);
         put_dd8(sH, acc, t);
         if (t < kD)
             sZ[t] = sub_seq(dZt[(size_t)bh * kD + t], n1 - n0, [&](int r) {
@@ -1062,6 +1091,8 @@ hipError_t launch_backward_mfma(const Dims& D, const void* Q, const void* K, con
                                 float* dQ, float* dK, float* dV, const FwdWS& ws,
                                 const BwdWS& bw, hipStream_t s) {
     const bool lin = D.k < D.Tkv;
+    // the selected sums by dense products (else gathered per row)
+    const bool prod = lin && D.k > 0 && sel_product_fits(D);
     const uint16_t* q = static_cast<const uint16_t*>(Q);
     const uint16_t* kk = static_cast<const uint16_t*>(K);
     const uint16_t* v = static_cast<const uint16_t*>(V);
@@ -1074,20 +1105,30 @@ hipError_t launch_backward_mfma(const Dims& D, const void* Q, const void* K, con
         if ((e = hipGetLastError()) != hipSuccess) return e;
         if ((e = sum_parts(D, bw.hblk, bw.zblk, ws.htot, ws.ztot, D.Tkv, s)) != hipSuccess)
             return e;
+        // S_i (the selected h_j summed) as a dense 0/1 product into dHq,
+        // which the rows pass reads and then overwrites row by row
+        if (prod && (e = launch_sel_product(D, false, idx, nullptr, nullptr, bw.sbits, bw.hb16,
+                                            bw.dHq, s)) != hipSuccess)
+            return e;
         timing_before(s, K_BWD_LIN_ROWS);
         bwd_lin_rows_kernel<<<head_major_grid(D.BH, D.Tq), 256, 0, s>>>(
             q, dO, idx, alpha, ws.htot, ws.ztot, bw.hb16, bw.zblk, dQ, bw.dHq, bw.dHb16, bw.dZq,
-            bw.da, D.N, D.Tq, D.Tkv, D.k, D.H, D.st, D.alpha_qblock);
+            bw.da, D.N, D.Tq, D.Tkv, D.k, D.H, D.st, D.alpha_qblock, prod ? bw.dHq : nullptr);
         timing_after(s, K_BWD_LIN_ROWS);
         if ((e = hipGetLastError()) != hipSuccess) return e;
         if ((e = sum_parts(D, bw.dHq, bw.dZq, bw.dHt, bw.dZt, D.Tq, s)) != hipSuccess) return e;
     }
     if (D.k > 0 && (e = launch_invert(D, idx, bw, s)) != hipSuccess) return e;
     if (lin) {
+        // the selecting query blocks' dH_i summed per KV block, into hblk
+        // (free once h_tot is formed)
+        if (prod && (e = launch_sel_product(D, true, nullptr, bw.off, bw.list, bw.sbits,
+                                            bw.dHb16, bw.hblk, s)) != hipSuccess)
+            return e;
         timing_before(s, K_BWD_LIN_KEYS);
         bwd_lin_keys_kernel<<<head_major_grid(D.BH, D.Tkv), 256, 0, s>>>(
             kk, v, bw.dHt, bw.dZt, bw.dHb16, bw.dZq, bw.off, bw.list, dK, dV, D.N, D.Tq, D.Tkv,
-            D.k, D.H, D.st);
+            D.k, D.H, D.st, prod ? bw.hblk : nullptr);
         timing_after(s, K_BWD_LIN_KEYS);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }

@@ -65,10 +65,11 @@ static_assert(4 * 2 * kWSt + kTbl <= 80 * 1024, "LDS budget: two work-groups per
 // the padded row count, are all zero).  Bit b of byte g of the row is KV
 // block 8 g + b.  Stored k-step major, [BH][Tkvp / 64][rows][8 bytes], so
 // that a product tile's 320 rows of one k-step are contiguous.
+// sel: bits of the selected blocks instead (the backward's products).
 __global__ __launch_bounds__(256) void unsel_kernel(const int32_t* __restrict__ idx, int k,
                                                     const int32_t* __restrict__ negl, int kl,
                                                     uint8_t* __restrict__ U, int Tq, int Tkv,
-                                                    int Tkvp, int rows) {
+                                                    int Tkvp, int rows, int sel) {
     __shared__ uint32_t row[kMaxTkvPad / 32];
     const int t = threadIdx.x;
     const long bh = blockIdx.x / rows;
@@ -77,7 +78,8 @@ __global__ __launch_bounds__(256) void unsel_kernel(const int32_t* __restrict__ 
     for (int x = t; x < nw; x += 256) {
         const int lo = 32 * x;
         uint32_t v = 0;
-        if (i < Tq) v = Tkv >= lo + 32 ? 0xffffffffu : (Tkv > lo ? (1u << (Tkv - lo)) - 1u : 0u);
+        if (i < Tq && !sel)
+            v = Tkv >= lo + 32 ? 0xffffffffu : (Tkv > lo ? (1u << (Tkv - lo)) - 1u : 0u);
         row[x] = v;
     }
     __syncthreads();
@@ -85,7 +87,10 @@ __global__ __launch_bounds__(256) void unsel_kernel(const int32_t* __restrict__ 
         const size_t r = (size_t)bh * Tq + i;
         for (int x = t; x < k; x += 256) {
             const int j = idx[r * k + x];
-            if ((unsigned)j < (unsigned)Tkv) atomicAnd(&row[j >> 5], ~(1u << (j & 31)));
+            if ((unsigned)j < (unsigned)Tkv) {
+                if (sel) atomicOr(&row[j >> 5], 1u << (j & 31));
+                else atomicAnd(&row[j >> 5], ~(1u << (j & 31)));
+            }
         }
         for (int x = t; x < kl; x += 256) {
             const int j = negl[r * kl + x];
@@ -96,6 +101,36 @@ __global__ __launch_bounds__(256) void unsel_kernel(const int32_t* __restrict__ 
     const int nks = Tkvp / 64;
     for (int x = t; x < nks; x += 256)
         *reinterpret_cast<uint2*>(U + (((size_t)bh * nks + x) * rows + i) * 8) =
+            make_uint2(row[2 * x], row[2 * x + 1]);
+}
+
+// The transposed selection as product rows: row j (a KV block) has bit i
+// set for every query block i in list[off[j] .. off[j + 1]) (the query
+// blocks that select j; off per head [Tkv + 1], list per head [Tq * k]).
+// Same layout as unsel_kernel's, with the query blocks as the k dimension.
+__global__ __launch_bounds__(256) void csr_bits_kernel(const int32_t* __restrict__ off,
+                                                       const int32_t* __restrict__ list, int k,
+                                                       uint8_t* __restrict__ U, int Tq, int Tkv,
+                                                       int Tqp, int rows) {
+    __shared__ uint32_t row[kMaxTkvPad / 32];
+    const int t = threadIdx.x;
+    const long bh = blockIdx.x / rows;
+    const int j = blockIdx.x % rows;
+    const int nw = Tqp / 32;
+    for (int x = t; x < nw; x += 256) row[x] = 0u;
+    __syncthreads();
+    if (j < Tkv) {
+        const int32_t* o = off + (size_t)bh * (Tkv + 1);
+        const int32_t* L = list + (size_t)bh * Tq * k;
+        for (int x = o[j] + t; x < o[j + 1]; x += 256) {
+            const int i = L[x];
+            if ((unsigned)i < (unsigned)Tq) atomicOr(&row[i >> 5], 1u << (i & 31));
+        }
+    }
+    __syncthreads();
+    const int nks = Tqp / 64;
+    for (int x = t; x < nks; x += 256)
+        *reinterpret_cast<uint2*>(U + (((size_t)bh * nks + x) * rows + j) * 8) =
             make_uint2(row[2 * x], row[2 * x + 1]);
 }
 
@@ -169,10 +204,15 @@ __device__ inline void load_lds4(rsrc_t r, uint32_t voff, uint32_t soff, char* d
 // Each wave stages its own operands (no barrier in the loop): waves of a
 // work-group and the two work-groups of a compute unit run unsynchronised,
 // so one wave's load and LDS waits are covered by the others' products.
+// F32: the backward's form: B rows bp elements apart, nt column tiles, every
+// output column in fp32 (rows of nt * 128 floats); otherwise the forward's
+// summaries rows (kHzPitch, kNT tiles) and H_i bf16 / Z_i fp32 output rows.
+template <bool F32>
 __global__ __launch_bounds__(256, 2) void lin_gemm_kernel(const uint8_t* __restrict__ U,
                                                          const uint16_t* __restrict__ hz,
                                                          char* __restrict__ HZ, int Tq, int Tkv,
-                                                         int Tkvp, int nM, int rows) {
+                                                         int Tkvp, int nM, int rows, int nt,
+                                                         int bp) {
     __shared__ __attribute__((aligned(1024))) char lds[4 * 2 * kWSt + kTbl];
     const int t = threadIdx.x, lane = t & 63, l32 = lane & 31, hl = lane >> 5;
     const int w = __builtin_amdgcn_readfirstlane(t >> 6);
@@ -180,13 +220,13 @@ __global__ __launch_bounds__(256, 2) void lin_gemm_kernel(const uint8_t* __restr
     int g = blockIdx.x;
     const int mi = g % nM;
     g /= nM;
-    const int ni = g % kNT;
-    const long bh = g / kNT;
+    const int ni = g % nt;
+    const long bh = g / nt;
     const int m0 = mi * kGemmM + 160 * wm;  // this wave's first row
     const int n0 = ni * kGN + 64 * wn;      // this wave's first column
     const int nk = Tkvp / kGK;
     const rsrc_t ru = head_rsrc(U + (size_t)bh * nk * rows * 8);
-    const rsrc_t rh = head_rsrc(hz + (size_t)bh * Tkv * kHzPitch);
+    const rsrc_t rh = head_rsrc(hz + (size_t)bh * Tkv * bp);
 
     // byte table: entry v holds the 8 bf16 values bit e of v (0 or 1)
     char* const tbl = lds + 4 * 2 * kWSt;
@@ -209,7 +249,7 @@ __global__ __launch_bounds__(256, 2) void lin_gemm_kernel(const uint8_t* __restr
     // (row & 3) of the wave's 64 columns
     const int brow = lane >> 3;  // + 8 q (row & 3 does not depend on q)
     const int bcol = n0 + 16 * (((lane & 7) >> 1) ^ (brow & 3)) + 8 * (lane & 1);
-    const uint32_t boff = (uint32_t)(brow * kHzPitch + bcol) * 2;
+    const uint32_t boff = (uint32_t)(brow * bp + bcol) * 2;
     char* const wbase = lds + w * 2 * kWSt;
     auto issue = [&](int stage, int kk) {
         char* A = wbase + stage * kWSt;
@@ -221,12 +261,12 @@ __global__ __launch_bounds__(256, 2) void lin_gemm_kernel(const uint8_t* __restr
         if (j0 + kGK <= Tkv) {
 #pragma unroll
             for (int q = 0; q < 8; ++q)
-                load_lds16(rh, boff, (uint32_t)(j0 + 8 * q) * kHzPitch * 2, B + 1024 * q);
+                load_lds16(rh, boff, (uint32_t)(j0 + 8 * q) * bp * 2, B + 1024 * q);
         } else {  // rows past T_kv repeat row T_kv - 1, whose U bits are 0
 #pragma unroll
             for (int q = 0; q < 8; ++q) {
                 const int jr = min(j0 + 8 * q + brow, Tkv - 1);
-                load_lds16(rh, (uint32_t)(jr * kHzPitch + bcol) * 2, 0, B + 1024 * q);
+                load_lds16(rh, (uint32_t)(jr * bp + bcol) * 2, 0, B + 1024 * q);
             }
         }
     };
@@ -316,6 +356,19 @@ __global__ __launch_bounds__(256, 2) void lin_gemm_kernel(const uint8_t* __restr
     // region (free now: no other wave reads it), so that the global stores
     // are whole 128-byte row pieces: rows of m-tiles 0-2, then 3-4.  The Z
     // columns (one column tile) go out in fp32 directly.
+    if constexpr (F32) {
+        float* of = reinterpret_cast<float*>(HZ) + (size_t)bh * Tq * nt * 128;
+#pragma unroll
+        for (int m = 0; m < 5; ++m)
+#pragma unroll
+            for (int n = 0; n < 2; ++n)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int qb = m0 + 32 * m + 8 * (r >> 2) + 4 * hl + (r & 3);
+                    if (qb < Tq) of[(size_t)qb * nt * 128 + n0 + 32 * n + l32] = acc[m][n][r];
+                }
+        return;
+    }
     char* out = HZ + (size_t)bh * Tq * kHzRowBytes;
     if (n0 >= 128 * 128) {
 #pragma unroll
@@ -368,15 +421,50 @@ hipError_t launch_unsel(const Dims& D, const int32_t* idx, const int32_t* negl, 
     if (tp > kMaxTkvPad) return hipErrorInvalidValue;
     const int rows = ubit_rows(D);
     unsel_kernel<<<dim3((unsigned)(D.BH * rows)), 256, 0, s>>>(idx, D.k, negl, kl, ws.usel, D.Tq,
-                                                               D.Tkv, tp, rows);
+                                                               D.Tkv, tp, rows, 0);
+    return hipGetLastError();
+}
+
+size_t sel_product_bits_bytes(const Dims& D) {
+    const size_t a = (size_t)D.BH * (tkv_pad(D) / 64) * ubit_rows(D) * 8;
+    const int tqp = (D.Tq + 63) & ~63;
+    const int rt = (D.Tkv + kGemmM - 1) / kGemmM * kGemmM + 64;
+    const size_t b = (size_t)D.BH * (tqp / 64) * rt * 8;
+    return a > b ? a : b;
+}
+
+hipError_t launch_sel_product(const Dims& D, bool keys, const int32_t* idx, const int32_t* off,
+                              const int32_t* list, uint8_t* bits, const uint16_t* B, float* out,
+                              hipStream_t s) {
+    // rows: query blocks (keys = false: the KV blocks each selects, B = per-
+    // KV-block matrices) or KV blocks (keys = true: the query blocks selecting
+    // each, B = per-query-block matrices); the k dimension is the other side
+    const int nr = keys ? D.Tkv : D.Tq, nk = keys ? D.Tq : D.Tkv;
+    const int nkp = (nk + 63) & ~63;
+    if (nkp > kMaxTkvPad) return hipErrorInvalidValue;
+    const int nM = (nr + kGemmM - 1) / kGemmM;
+    const int rows = nM * kGemmM + 64;
+    if (keys)
+        csr_bits_kernel<<<dim3((unsigned)(D.BH * rows)), 256, 0, s>>>(off, list, D.k, bits, D.Tq,
+                                                                    D.Tkv, nkp, rows);
+    else
+        unsel_kernel<<<dim3((unsigned)(D.BH * rows)), 256, 0, s>>>(idx, D.k, nullptr, 0, bits,
+                                                                   D.Tq, D.Tkv, nkp, rows, 1);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    constexpr int kNT32 = 128 * 128 / kGN;  // d x d matrices: 128 column tiles
+    timing_before(s, K_BWD_LIN_PRODUCT);
+    lin_gemm_kernel<true><<<dim3((unsigned)(D.BH * kNT32 * nM)), 256, 0, s>>>(
+        bits, B, reinterpret_cast<char*>(out), nr, nk, nkp, nM, rows, kNT32, 128 * 128);
+    timing_after(s, K_BWD_LIN_PRODUCT);
     return hipGetLastError();
 }
 
 hipError_t launch_lin_gemm(const Dims& D, const FwdWS& ws, hipStream_t s) {
     const int nM = (D.Tq + kGemmM - 1) / kGemmM;
     timing_before(s, K_LIN_GEMM);
-    lin_gemm_kernel<<<dim3((unsigned)(D.BH * kNT * nM)), 256, 0, s>>>(
-        ws.usel, ws.hz, ws.HZ, D.Tq, D.Tkv, tkv_pad(D), nM, ubit_rows(D));
+    lin_gemm_kernel<false><<<dim3((unsigned)(D.BH * kNT * nM)), 256, 0, s>>>(
+        ws.usel, ws.hz, ws.HZ, D.Tq, D.Tkv, tkv_pad(D), nM, ubit_rows(D), kNT, kHzPitch);
     timing_after(s, K_LIN_GEMM);
     return hipGetLastError();
 }

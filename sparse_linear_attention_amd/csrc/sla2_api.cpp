@@ -141,6 +141,7 @@ size_t layout_backward(const Dims& D, char* base, FwdWS* ws, BwdWS* bw) {
         b.gl = carve<uint16_t>(base, off, 2 * bh * np * d);
         b.lse = carve<float>(base, off, 4 * bh * np);
         b.D = carve<float>(base, off, 4 * bh * np);
+        b.sbits = carve<uint8_t>(base, off, sel_product_bits_bytes(D));
     } else {
         const int nch = summ_chunks(D);
         w.hpart = carve<float>(base, off, 4 * bh * nch * d * d);
@@ -255,7 +256,7 @@ const char* kKindNames[K_NUM_KINDS] = {
     "quant_i8",     "fused_i8",    "fused_sla1",  "bwd_rows",
     "bwd_dh",       "bwd_keys",    "bwd_lin_rows", "bwd_lin_keys",
     "bwd_rows_mfma", "bwd_keys_mfma", "bwd_blk_summ", "bwd_sum_parts", "pool_quant",
-    "lin_gemm",     "score_topk",
+    "lin_gemm",     "score_topk",  "bwd_lin_product",
 };
 }  // namespace
 

@@ -40,6 +40,7 @@ enum KernelKind {
     K_POOL_QUANT,
     K_LIN_GEMM,
     K_SCORE_TOPK,
+    K_BWD_LIN_PRODUCT,
     K_NUM_KINDS
 };
 
@@ -202,6 +203,7 @@ struct BwdWS {
     uint16_t* dHb16;// [BH][Tq][d][d]  dH_i rounded to bf16
     uint16_t* gh;   // [BH][Tq * 128][d] bf16 high part of alpha dO (rows past N: 0)
     uint16_t* gl;   // [BH][Tq * 128][d] bf16 rest of alpha dO
+    uint8_t* sbits; // 0/1 rows of the selection products (sel_product_bits_bytes)
 };
 // the backward runs on the matrix cores for bf16 inputs with d = b_q = 128
 // (b_kv = 64) and phi = elu + 1; other problems take the vector-ALU kernels
@@ -344,6 +346,19 @@ hipError_t launch_fused128(const Dims& D, const void* Q, const void* K, const in
 hipError_t launch_unsel(const Dims& D, const int32_t* idx, const int32_t* negl, int kl,
                         const FwdWS& ws, hipStream_t s);
 hipError_t launch_lin_gemm(const Dims& D, const FwdWS& ws, hipStream_t s);
+// backward (d = b_q = 128): out = sum of the bf16 d x d matrices B selected
+// per row, fp32: keys = false: rows = query blocks, S_i = sum over the KV
+// blocks i selects of B_j; keys = true: rows = KV blocks, D_j = sum over the
+// query blocks selecting j (off / list) of B_i.  bits: the 0/1 rows
+// (sel_product_bits_bytes); out: [BH][rows][d * d] fp32.
+size_t sel_product_bits_bytes(const Dims& D);
+// the products' bit rows hold at most 7680 blocks of the k dimension
+inline bool sel_product_fits(const Dims& D) {
+    return ((D.Tkv + 63) & ~63) <= 7680 && ((D.Tq + 63) & ~63) <= 7680;
+}
+hipError_t launch_sel_product(const Dims& D, bool keys, const int32_t* idx, const int32_t* off,
+                              const int32_t* list, uint8_t* bits, const uint16_t* B, float* out,
+                              hipStream_t s);
 // diagnostic: C[t] = A[t] B[t]^T, 32 x 128 e4m3 tiles, fp8 matrix cores
 hipError_t launch_fp8_dot(const uint8_t* A, const uint8_t* B, float* C, int ntiles,
                           hipStream_t s);
