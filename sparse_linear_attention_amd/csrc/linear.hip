@@ -211,8 +211,10 @@ template <bool F32>
 __global__ __launch_bounds__(256, 2) void lin_gemm_kernel(const uint8_t* __restrict__ U,
                                                          const uint16_t* __restrict__ hz,
                                                          char* __restrict__ HZ, int Tq, int Tkv,
-                                                         int Tkvp, int nM, int rows, int nt,
-                                                         int bp) {
+                                                         int Tkvp, int nM, int rows, int nt_,
+                                                         int bp_) {
+    // the forward's form keeps its sizes as constants
+    const int nt = F32 ? nt_ : kNT, bp = F32 ? bp_ : kHzPitch;
     __shared__ __attribute__((aligned(1024))) char lds[4 * 2 * kWSt + kTbl];
     const int t = threadIdx.x, lane = t & 63, l32 = lane & 31, hl = lane >> 5;
     const int w = __builtin_amdgcn_readfirstlane(t >> 6);
