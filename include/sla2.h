@@ -209,9 +209,10 @@ sla2_status sla2_forward(const sla2_problem* p, const void* Q, const void* K,
 /*
  * sla2_attention -- sla2_route followed by sla2_forward in one call (same
  *   kernels, bit-identical O and topk_idx).  On the bf16 bq = 128 path the
- *   block summaries (which read only K and V) run on a helper stream,
- *   concurrently with the router (Q and K), joined before the fused kernel
- *   with events; other paths run in sequence.  The helper stream and its
+ *   block summaries (which read only K and V, and also write the router's
+ *   pooled keys) run on a helper stream, concurrently with the pooling of
+ *   the queries; the projections, scores and top-k follow once they are
+ *   joined (events); other paths run in sequence.  The helper stream and its
  *   events are created once per device on first use (default priority) and
  *   kept until the process ends.  Calls from several host threads (on
  *   different streams, with different workspaces) are safe: a lock keeps
@@ -382,9 +383,12 @@ const char* sla2_kernel_name(int32_t kind);
  *   the rows alpha applies to.  Through phi (SLA notes, key design 4):
  *   dx = dphi * phi'(x) for elu + 1; for the row softmax p = phi(x), dx =
  *   p * (dphi - p . dphi).  bf16 inputs with d = bq = 128 and phi = elu + 1
- *   run on the matrix cores (bf16 / fp16 operands as in sla2_forward's bf16
- *   path, fp32 accumulation); every other problem (softmax phi included) in
- *   fp32 on the vector ALU.
+ *   run on the matrix cores: the sparse passes with bf16 Q, K, V and every
+ *   fp32 operand split into a bf16 high part and the bf16 rounding of the
+ *   rest; the selected blocks' bf16 summaries (and the selecting query
+ *   blocks' bf16 dH_i) summed by dense 0/1 products, fp32 accumulation; the
+ *   linear passes' own products in fp32.  Every other problem (softmax phi
+ *   included) in fp32 on the vector ALU.
  * In : Q, K, V, topk_idx, alpha as sla2_forward; dO fp32 in problem.layout.
  * Out: dQ, dK, dV fp32 in problem.layout; dalpha [H] or [H][T_q] fp32
  *      (problem.alpha_mode).  All overwritten.
