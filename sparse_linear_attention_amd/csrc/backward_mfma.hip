@@ -421,42 +421,60 @@ __global__ __launch_bounds__(256) void bwd_lin_keys_kernel(
 
 // ---------------------------------------------------------------------------
 // Per-KV-block summaries on the fp32 matrix cores: h_j = phi(K_j)^T V_j
-// ([c][e], over the block's tokens below N) and z_j = colsum phi(K_j).  One
-// work-group per (head, block), 256 threads.
+// ([c][e], over the block's tokens below N; written rounded to bf16) and
+// z_j = colsum phi(K_j) (fp32).  One work-group per (head, chunk of
+// kBlkChunk blocks), 256 threads; the chunk's h_j and z_j summed in fp32
+// (ascending j) into hpart / zpart[bh][chunk], from which sum_parts forms
+// the head's totals.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void blk_summ_kernel(const uint16_t* __restrict__ K,
+constexpr int kBlkChunk = 8;
+
+__global__ __launch_bounds__(256, 2) void blk_summ_kernel(const uint16_t* __restrict__ K,
                                                        const uint16_t* __restrict__ V,
-                                                       float* __restrict__ hblk,
+                                                       float* __restrict__ hpart,
+                                                       float* __restrict__ zpart,
                                                        uint16_t* __restrict__ hb16,
                                                        float* __restrict__ zblk, int N, int Tkv,
-                                                       int H, Strides st) {
+                                                       int nch, int H, Strides st) {
     __shared__ float sP[64 * kLd];  // phi(K_j) [u][c]
     __shared__ float sV[64 * kLd];  // V_j [u][e]
     const int t = threadIdx.x, lane = t & 63, w = t >> 6, l32 = lane & 31;
     long bh;
-    int j;
-    if (!head_major_map(blockIdx.x, Tkv, &bh, &j)) return;
+    int ch;
+    if (!head_major_map(blockIdx.x, nch, &bh, &ch)) return;
     const long hb = head_base(st, bh, H);
-    fill64<true>(sP, K + hb, st.t, j * 64, N, t);
-    fill64<false>(sV, V + hb, st.t, j * 64, N, t);
-    __syncthreads();
-    f32x16 h[4] = {zero16(), zero16(), zero16(), zero16()};
-    mfma_f32_row<4>(h, sP, 1, kLd, sV, kLd, 1, 32 * w, 0, 64, lane);
-    float* ho = hblk + ((size_t)bh * Tkv + j) * kD * kD;
-    uint16_t* ho16 = hb16 + ((size_t)bh * Tkv + j) * kD * kD;
+    f32x16 hs[4] = {zero16(), zero16(), zero16(), zero16()};
+    float zs = 0.0f;
+    const int j1 = min(Tkv, (ch + 1) * kBlkChunk);
+    for (int j = ch * kBlkChunk; j < j1; ++j) {
+        __syncthreads();  // the previous block's reads of sP, sV are done
+        fill64<true>(sP, K + hb, st.t, j * 64, N, t);
+        fill64<false>(sV, V + hb, st.t, j * 64, N, t);
+        __syncthreads();
+        f32x16 h[4] = {zero16(), zero16(), zero16(), zero16()};
+        mfma_f32_row<4>(h, sP, 1, kLd, sV, kLd, 1, 32 * w, 0, 64, lane);
+        uint16_t* ho16 = hb16 + ((size_t)bh * Tkv + j) * kD * kD;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int o = (32 * w + acc_row(r, lane)) * kD + 32 * i + l32;
+                ho16[o] = __builtin_bit_cast(uint16_t, (__bf16)h[i][r]);
+                hs[i][r] += h[i][r];
+            }
+        if (t < kD) {
+            float z = 0.0f;
+            for (int u = 0; u < 64; ++u) z += sP[u * kLd + t];
+            zblk[((size_t)bh * Tkv + j) * kD + t] = z;
+            zs += z;
+        }
+    }
+    float* ho = hpart + ((size_t)bh * nch + ch) * kD * kD;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int o = (32 * w + acc_row(r, lane)) * kD + 32 * i + l32;
-            ho[o] = h[i][r];
-            ho16[o] = __builtin_bit_cast(uint16_t, (__bf16)h[i][r]);
-        }
-    if (t < kD) {
-        float z = 0.0f;
-        for (int u = 0; u < 64; ++u) z += sP[u * kLd + t];
-        zblk[((size_t)bh * Tkv + j) * kD + t] = z;
-    }
+        for (int r = 0; r < 16; ++r) ho[(32 * w + acc_row(r, lane)) * kD + 32 * i + l32] = hs[i][r];
+    if (t < kD) zpart[((size_t)bh * nch + ch) * kD + t] = zs;
 }
 
 // tot[bh][e] = sum over c < nch of part[bh][c][e] for the d*d entries of the
@@ -1098,12 +1116,13 @@ hipError_t launch_backward_mfma(const Dims& D, const void* Q, const void* K, con
     const uint16_t* v = static_cast<const uint16_t*>(V);
     hipError_t e = hipSuccess;
     if (lin) {
+        const int nch = bwd_summ_chunks(D);
         timing_before(s, K_BWD_BLK_SUMM);
-        blk_summ_kernel<<<head_major_grid(D.BH, D.Tkv), 256, 0, s>>>(
-            kk, v, bw.hblk, bw.hb16, bw.zblk, D.N, D.Tkv, D.H, D.st);
+        blk_summ_kernel<<<head_major_grid(D.BH, nch), 256, 0, s>>>(
+            kk, v, bw.hblk, bw.zpart, bw.hb16, bw.zblk, D.N, D.Tkv, nch, D.H, D.st);
         timing_after(s, K_BWD_BLK_SUMM);
         if ((e = hipGetLastError()) != hipSuccess) return e;
-        if ((e = sum_parts(D, bw.hblk, bw.zblk, ws.htot, ws.ztot, D.Tkv, s)) != hipSuccess)
+        if ((e = sum_parts(D, bw.hblk, bw.zpart, ws.htot, ws.ztot, nch, s)) != hipSuccess)
             return e;
         // S_i (the selected h_j summed) as a dense 0/1 product into dHq,
         // which the rows pass reads and then overwrites row by row

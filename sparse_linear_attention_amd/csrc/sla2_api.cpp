@@ -142,6 +142,7 @@ size_t layout_backward(const Dims& D, char* base, FwdWS* ws, BwdWS* bw) {
         b.lse = carve<float>(base, off, 4 * bh * np);
         b.D = carve<float>(base, off, 4 * bh * np);
         b.sbits = carve<uint8_t>(base, off, sel_product_bits_bytes(D));
+        b.zpart = carve<float>(base, off, 4 * bh * bwd_summ_chunks(D) * d);
     } else {
         const int nch = summ_chunks(D);
         w.hpart = carve<float>(base, off, 4 * bh * nch * d * d);

@@ -195,7 +195,8 @@ struct BwdWS {
     int32_t* list;  // [BH][Tq * k]  and the lists (ascending)
     // matrix-core path only (bwd_mfma_path): per-block summaries and the
     // per-query-block gradients of H_i, Z_i
-    float* hblk;    // [BH][Tkv][d][d] h_j
+    float* hblk;    // [BH][Tkv][d][d]: the per-chunk h partials, then the keys
+                    //                product's rows
     float* zblk;    // [BH][Tkv][d]    z_j
     float* dHq;     // [BH][Tq][d][d]  dL/dH_i
     float* dZq;     // [BH][Tq][d]     dL/dZ_i
@@ -204,7 +205,11 @@ struct BwdWS {
     uint16_t* gh;   // [BH][Tq * 128][d] bf16 high part of alpha dO (rows past N: 0)
     uint16_t* gl;   // [BH][Tq * 128][d] bf16 rest of alpha dO
     uint8_t* sbits; // 0/1 rows of the selection products (sel_product_bits_bytes)
+    float* zpart;   // [BH][bwd_summ_chunks][d] z summed per chunk of KV blocks
+                    // (the h partials go to the front of hblk)
 };
+// chunks of 8 KV blocks of the matrix-core backward's block summaries
+inline int bwd_summ_chunks(const Dims& D) { return (D.Tkv + 7) / 8; }
 // the backward runs on the matrix cores for bf16 inputs with d = b_q = 128
 // (b_kv = 64) and phi = elu + 1; other problems take the vector-ALU kernels
 inline bool bwd_mfma_path(const Dims& D) {
