@@ -59,7 +59,7 @@ def log(*a):
 def kernel_source_sha() -> str:
     """Hash of the fused kernel's sources (counters are void once it changes)."""
     h = hashlib.sha256()
-    for f in ("fused128.hip", "cdna4.h", "sla2_internal.h"):
+    for f in ("fused128.hip", "cdna4.h", "hz_layout.h"):
         h.update(open(os.path.join(ROOT, "sparse_linear_attention_amd", "csrc", f), "rb").read())
     return h.hexdigest()[:16]
 

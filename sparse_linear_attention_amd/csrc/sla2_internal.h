@@ -8,6 +8,7 @@
 #include <stdint.h>
 
 #include "sla2.h"
+#include "hz_layout.h"
 
 namespace sla2 {
 
@@ -110,16 +111,6 @@ inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 // U[i][j] (h_j, z_j), U the 0/1 indicator of the blocks query block i leaves
 // to the linear branch (linear.hip).  Rows of the block summaries and of the
 // products hold the d*d entries of h^T (V channel major) and then the d of z.
-// The h_j^T part of a summaries row (and the H_i^T part of a product row)
-// is stored in the order in which the block-summaries pass's matrix
-// accumulators hold it, so that every store there is a contiguous 1 KB: the
-// 16-byte unit of entries (e, 8 u .. 8 u + 7) (V channel e, phi channels c =
-// 8 u ..) is unit ((e / 32 * 4 + u / 4) * 2 + (u / 2) % 2) * 64 + e % 32 +
-// 32 (u % 2) of the row.  The product is indifferent to the column order;
-// the fused kernel fetches each unit from here.
-__host__ __device__ inline int hz_unit(int e, int u) {
-    return (((e >> 5) * 4 + (u >> 2)) * 2 + ((u >> 1) & 1)) * 64 + (e & 31) + 32 * (u & 1);
-}
 constexpr int kHzCols = 128 * 128 + 128;  // entries of a row
 // bytes of a product row: H_i^T in bf16 (the fp32 exponent range, so no
 // scaling), then Z_i in fp32
