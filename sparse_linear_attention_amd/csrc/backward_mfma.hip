@@ -135,46 +135,6 @@ __device__ inline void load_base8(float (&acc)[8][8], const float* base, int t) 
         acc[m][7] = b.w;
     }
 }
-__device__ inline void sub_bf16_8(float (&acc)[8][8], const uint16_t* src, int t) {
-#pragma unroll
-    for (int m = 0; m < 8; ++m) {
-        const uint4 u = *reinterpret_cast<const uint4*>(src + 8 * (t + 256 * m));
-        const uint32_t wv[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            acc[m][2 * q] -= __uint_as_float(wv[q] << 16);
-            acc[m][2 * q + 1] -= __uint_as_float(wv[q] & 0xffff0000u);
-        }
-    }
-}
-// acc -= src(0), .., src(n - 1) (bf16 d x d matrices) in that order, the
-// loads of four matrices issued together: the subtraction itself is cheap
-// and the loop is bound by the latency of the gathers
-template <typename F>
-__device__ inline void sub_bf16_8_seq(float (&acc)[8][8], int n, F src, int t) {
-    int r = 0;
-    for (; r + 4 <= n; r += 4) {
-        uint4 u[4][8];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const uint16_t* p = src(r + q);
-#pragma unroll
-            for (int m = 0; m < 8; ++m) u[q][m] = *reinterpret_cast<const uint4*>(p + 8 * (t + 256 * m));
-        }
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-#pragma unroll
-            for (int m = 0; m < 8; ++m) {
-                const uint32_t wv[4] = {u[q][m].x, u[q][m].y, u[q][m].z, u[q][m].w};
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    acc[m][2 * e] -= __uint_as_float(wv[e] << 16);
-                    acc[m][2 * e + 1] -= __uint_as_float(wv[e] & 0xffff0000u);
-                }
-            }
-    }
-    for (; r < n; ++r) sub_bf16_8(acc, src(r), t);
-}
 // z - src(0) - .. - src(n - 1), in that order, four loads at a time
 template <typename F>
 __device__ inline float sub_seq(float z, int n, F src) {
@@ -218,15 +178,14 @@ __device__ inline void put_dd8(float* dst, const float (&acc)[8][8], int t) {
 // Linear rows pass: one work-group per (head, query block), 256 threads.
 // Writes dQ (the phi chain; the first writer of dQ), dH_i, dZ_i and g . O_l
 // per row into gol.  H_i = h_tot - S_i with S_i the sum of the bf16 h_j of
-// the selected blocks: from ssel (row i of the selection product, fp32; it
-// may be the row of dHq that this work-group overwrites at its end) or, when
-// ssel is null, gathered here.
+// the selected blocks, row i of the selection product (fp32; k > 0 only;
+// it may be the row of dHq that this work-group overwrites at its end).
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void bwd_lin_rows_kernel(
     const uint16_t* __restrict__ Q, const float* __restrict__ dO,
     const int32_t* __restrict__ idx, const float* __restrict__ alpha,
     const float* __restrict__ htot, const float* __restrict__ ztot,
-    const uint16_t* __restrict__ hb16, const float* __restrict__ zblk, float* __restrict__ dQ,
+    const float* __restrict__ zblk, float* __restrict__ dQ,
     float* __restrict__ dHq, uint16_t* __restrict__ dHb16, float* __restrict__ dZq,
     float* __restrict__ gol, int N, int Tq, int Tkv, int k, int H, Strides st,
     int alpha_qblock, const float* ssel) {
@@ -243,11 +202,7 @@ __global__ __launch_bounds__(256) void bwd_lin_rows_kernel(
     {
         float acc[8][8];
         load_base8(acc, htot + (size_t)bh * kD * kD, t);
-        if (ssel)
-            sub_f32_8(acc, ssel + ((size_t)bh * Tq + qb) * kD * kD, t);
-        else
-            sub_bf16_8_seq(acc, k,
-                           [&](int r) { return hb16 + ((size_t)bh * Tkv + sel[r]) * kD * kD; }, t);
+        if (k > 0) sub_f32_8(acc, ssel + ((size_t)bh * Tq + qb) * kD * kD, t);
         put_dd8(sH, acc, t);
         if (t < kD)
             sZ[t] = sub_seq(ztot[(size_t)bh * kD + t], k, [&](int r) {
@@ -355,24 +310,24 @@ __global__ __launch_bounds__(256) void bwd_lin_rows_kernel(
 
 // ---------------------------------------------------------------------------
 // Linear keys pass: one work-group per (head, KV block j), 256 threads.
-// dh_j = dH_tot - sum over the query blocks selecting j of dH_i (bf16; from
-// dsel, row j of the transposed selection product, fp32, or gathered here
-// in ascending order when dsel is null), dz_j likewise (gathered); writes
+// dh_j = dH_tot - sum over the query blocks selecting j of dH_i (bf16; row j
+// of the transposed selection product dsel, fp32; k > 0 only), dz_j
+// likewise (gathered, fp32); writes
 // dK = (dh_j v_u + dz_j) phi'(k_u) and dV = phi(k_u) dh_j (the first writers
 // of dK and dV).
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void bwd_lin_keys_kernel(
     const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const float* __restrict__ dHt, const float* __restrict__ dZt,
-    const uint16_t* __restrict__ dHb16, const float* __restrict__ dZq,
-    const int32_t* __restrict__ off, const int32_t* __restrict__ list, float* __restrict__ dK,
+    const float* __restrict__ dZq, const int32_t* __restrict__ off,
+    const int32_t* __restrict__ list, float* __restrict__ dK,
     float* __restrict__ dV, int N, int Tq, int Tkv, int k, int H, Strides st,
     const float* __restrict__ dsel) {
     __shared__ float sH[kD * kLd];  // dh_j [c][e]
     __shared__ float sA[64 * kLd];  // V_j [u][e]
     __shared__ float sB[64 * kLd];  // phi(K_j) [u][c]
     __shared__ float sZ[kD];
-    const int t = threadIdx.x, ty = t >> 4, tx = t & 15;
+    const int t = threadIdx.x;
     long bh;
     int j;
     if (!head_interleaved_map(blockIdx.x, Tkv, &bh, &j)) return;
@@ -383,12 +338,7 @@ __global__ __launch_bounds__(256) void bwd_lin_keys_kernel(
     {
         float acc[8][8];
         load_base8(acc, dHt + (size_t)bh * kD * kD, t);
-        if (dsel)
-            sub_f32_8(acc, dsel + ((size_t)bh * Tkv + j) * kD * kD, t);
-        else
-            sub_bf16_8_seq(
-                acc, n1 - n0,
-                [&](int r) { return dHb16 + ((size_t)bh * Tq + L[n0 + r]) * kD * kD; }, t);
+        if (k > 0) sub_f32_8(acc, dsel + ((size_t)bh * Tkv + j) * kD * kD, t);
         put_dd8(sH, acc, t);
         if (t < kD)
             sZ[t] = sub_seq(dZt[(size_t)bh * kD + t], n1 - n0, [&](int r) {
@@ -1109,8 +1059,9 @@ hipError_t launch_backward_mfma(const Dims& D, const void* Q, const void* K, con
                                 float* dQ, float* dK, float* dV, const FwdWS& ws,
                                 const BwdWS& bw, hipStream_t s) {
     const bool lin = D.k < D.Tkv;
-    // the selected sums by dense products (else gathered per row)
-    const bool prod = lin && D.k > 0 && sel_product_fits(D);
+    // the selected sums by dense products (every valid problem fits them)
+    const bool prod = lin && D.k > 0;
+    if (prod && !sel_product_fits(D)) return hipErrorInvalidValue;
     const uint16_t* q = static_cast<const uint16_t*>(Q);
     const uint16_t* kk = static_cast<const uint16_t*>(K);
     const uint16_t* v = static_cast<const uint16_t*>(V);
@@ -1131,7 +1082,7 @@ hipError_t launch_backward_mfma(const Dims& D, const void* Q, const void* K, con
             return e;
         timing_before(s, K_BWD_LIN_ROWS);
         bwd_lin_rows_kernel<<<head_major_grid(D.BH, D.Tq), 256, 0, s>>>(
-            q, dO, idx, alpha, ws.htot, ws.ztot, bw.hb16, bw.zblk, dQ, bw.dHq, bw.dHb16, bw.dZq,
+            q, dO, idx, alpha, ws.htot, ws.ztot, bw.zblk, dQ, bw.dHq, bw.dHb16, bw.dZq,
             bw.da, D.N, D.Tq, D.Tkv, D.k, D.H, D.st, D.alpha_qblock, prod ? bw.dHq : nullptr);
         timing_after(s, K_BWD_LIN_ROWS);
         if ((e = hipGetLastError()) != hipSuccess) return e;
@@ -1146,7 +1097,7 @@ hipError_t launch_backward_mfma(const Dims& D, const void* Q, const void* K, con
             return e;
         timing_before(s, K_BWD_LIN_KEYS);
         bwd_lin_keys_kernel<<<head_major_grid(D.BH, D.Tkv), 256, 0, s>>>(
-            kk, v, bw.dHt, bw.dZt, bw.dHb16, bw.dZq, bw.off, bw.list, dK, dV, D.N, D.Tq, D.Tkv,
+            kk, v, bw.dHt, bw.dZt, bw.dZq, bw.off, bw.list, dK, dV, D.N, D.Tq, D.Tkv,
             D.k, D.H, D.st, prod ? bw.hblk : nullptr);
         timing_after(s, K_BWD_LIN_KEYS);
         if ((e = hipGetLastError()) != hipSuccess) return e;

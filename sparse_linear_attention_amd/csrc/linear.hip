@@ -48,7 +48,7 @@ __device__ inline void load_lds16(rsrc_t r, uint32_t voff, uint32_t soff, char* 
 }
 __device__ inline uint32_t lds_addr(const void* p) { return (uint32_t)(uintptr_t)SLA2_LDS(p); }
 
-constexpr int kMaxTkvPad = 7680;
+constexpr int kMaxTkvPad = kMaxBitBlocks;
 constexpr int kGN = 128;                 // columns per tile
 constexpr int kGK = 64;                  // KV blocks per stage
 constexpr int kNT = kHzPitch / kGN;      // column tiles (130)

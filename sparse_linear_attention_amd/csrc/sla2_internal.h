@@ -348,9 +348,11 @@ hipError_t launch_lin_gemm(const Dims& D, const FwdWS& ws, hipStream_t s);
 // query blocks selecting j (off / list) of B_i.  bits: the 0/1 rows
 // (sel_product_bits_bytes); out: [BH][rows][d * d] fp32.
 size_t sel_product_bits_bytes(const Dims& D);
-// the products' bit rows hold at most 7680 blocks of the k dimension
+// blocks of the k dimension that a 0/1 product row (unsel_kernel,
+// csr_bits_kernel) holds at most
+constexpr int kMaxBitBlocks = 7680;
 inline bool sel_product_fits(const Dims& D) {
-    return ((D.Tkv + 63) & ~63) <= 7680 && ((D.Tq + 63) & ~63) <= 7680;
+    return ((D.Tkv + 63) & ~63) <= kMaxBitBlocks && ((D.Tq + 63) & ~63) <= kMaxBitBlocks;
 }
 hipError_t launch_sel_product(const Dims& D, bool keys, const int32_t* idx, const int32_t* off,
                               const int32_t* list, uint8_t* bits, const uint16_t* B, float* out,
