@@ -131,6 +131,31 @@ def test_backward_wan13b_one_head(orc, dev):
     _check("dalpha", da.cpu().numpy(), ra)
 
 
+def test_backward_ragged_product_tiles(orc, dev):
+    """One head with N = 41003 (k = 20 of 641 KV blocks): the selected
+    summaries are summed by 0/1 products of 320-row tiles, here two row tiles
+    over the 321 query blocks (the second holding one) and three over the
+    641 KV blocks (the last holding one), and the last KV block is ragged.
+    Every gradient entry against the oracle."""
+    w = I.WAN13B.with_(H=1, N=41003)
+    say("case backward ragged product tiles: N=41003 H=1")
+    x = I.make_inputs(w)
+    q, k, v, wq, wk, al = to_dev(x, dev)
+    p = S.problem(1, 1, w.N, w.d, w.bq, w.bkv, w.topk_frac, 1, w.dtype)
+    assert (S.num_q_blocks(p), S.num_kv_blocks(p)) == (321, 641)
+    idx, _ = S.route(p, q, k, wq, wk, want_mask=False)
+    dO = np.random.default_rng(5).normal(0, 1, (1, 1, w.N, w.d)).astype(np.float32)
+    dQ, dK, dV, da = S.backward(p, q, k, v, idx, al, torch.from_numpy(dO).to(dev))
+    torch.cuda.synchronize()
+    op = orc.problem(1, 1, w.N, w.d, w.bq, w.bkv, w.topk_frac, 1, w.dtype)
+    rQ, rK, rV, ra = orc.backward(op, x.q, x.k, x.v, idx.cpu().numpy(), x.alpha,
+                                  dO.astype(np.float64))
+    _check("dQ", dQ.cpu().numpy(), rQ)
+    _check("dK", dK.cpu().numpy(), rK)
+    _check("dV", dV.cpu().numpy(), rV)
+    _check("dalpha", da.cpu().numpy(), ra)
+
+
 @pytest.mark.parametrize("dtype,bq,frac", [("bf16", 128, 0.2), ("bf16", 128, 1.0), ("f32", 64, 0.25)],
                          ids=["matrix-core", "matrix-core-all-selected", "valu"])
 def test_backward_ignores_workspace_contents(dev, dtype, bq, frac):
