@@ -164,12 +164,12 @@ __global__ __launch_bounds__(256) void proj_kernel(const double* __restrict__ xq
                                                    const float* __restrict__ Wq,
                                                    const float* __restrict__ Wk,
                                                    double* __restrict__ qt, double* __restrict__ kt,
-                                                   int Tq, int Tkv, int H, int w_heads) {
+                                                   int Tq, int Tkv, int H, int w_heads, int side0) {
     constexpr int ct = d / 64;
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int r16 = lane & 15, kq = lane >> 4;
     const long bh = blockIdx.z;
-    const int side = (int)blockIdx.y / ct;
+    const int side = side0 + (int)blockIdx.y / ct;  // 0: queries, 1: keys
     const int rows = side ? Tkv : Tq;
     const int iw = blockIdx.x * 64 + 32 * (w >> 1);
     const int ew = ((int)blockIdx.y % ct) * 64 + 32 * (w & 1);
@@ -717,8 +717,25 @@ void launch_score_kernel(const Dims& D, const RouteWS& ws, hipStream_t s) {
 
 }  // namespace
 
+namespace {
+// the projection product over the queries (sides = 1), the keys (2) or both (3)
+void launch_proj(const Dims& D, const float* Wq, const float* Wk, const RouteWS& ws, int sides,
+                 hipStream_t s) {
+    const int rows = sides == 1 ? D.Tq : sides == 2 ? D.Tkv : max(D.Tq, D.Tkv);
+    const int ns = sides == 3 ? 2 : 1, side0 = sides == 2 ? 1 : 0;
+    dim3 gp((rows + 63) / 64, ns * (D.d / 64), (unsigned)D.BH);
+    if (D.d == 128)
+        proj_kernel<128><<<gp, 256, 0, s>>>(ws.xq, ws.xk, Wq, Wk, ws.qt, ws.kt, D.Tq, D.Tkv, D.H,
+                                            D.w_heads, side0);
+    else
+        proj_kernel<64><<<gp, 256, 0, s>>>(ws.xq, ws.xk, Wq, Wk, ws.qt, ws.kt, D.Tq, D.Tkv, D.H,
+                                           D.w_heads, side0);
+}
+}  // namespace
+
 hipError_t launch_pool_project(const Dims& D, const void* Q, const void* K, const float* Wq,
-                               const float* Wk, const RouteWS& ws, hipStream_t s, bool pooled) {
+                               const float* Wk, const RouteWS& ws, hipStream_t s, bool pooled,
+                               bool q_projected) {
     // pool (means into ws.xq / ws.xk), then project them with a tiled product
     dim3 g1(D.Tq + D.Tkv, (unsigned)D.BH);
     timing_before(s, K_POOL_PROJECT);
@@ -732,18 +749,13 @@ hipError_t launch_pool_project(const Dims& D, const void* Q, const void* K, cons
         pool_project_kernel<uint16_t><<<g1, 256, 0, s>>>(
             (const uint16_t*)Q, (const uint16_t*)K, nullptr, nullptr, ws.xq, ws.xk, D.N, D.d,
             D.bq, D.bkv, D.Tq, D.Tkv, D.H, D.w_heads, D.st);
-    dim3 gp((max(D.Tq, D.Tkv) + 63) / 64, 2 * (D.d / 64), (unsigned)D.BH);
-    if (D.d == 128)
-        proj_kernel<128><<<gp, 256, 0, s>>>(ws.xq, ws.xk, Wq, Wk, ws.qt, ws.kt, D.Tq, D.Tkv, D.H,
-                                            D.w_heads);
-    else
-        proj_kernel<64><<<gp, 256, 0, s>>>(ws.xq, ws.xk, Wq, Wk, ws.qt, ws.kt, D.Tq, D.Tkv, D.H,
-                                           D.w_heads);
+    launch_proj(D, Wq, Wk, ws, q_projected ? 2 : 3, s);
     timing_after(s, K_POOL_PROJECT);
     return hipGetLastError();
 }
 
-hipError_t launch_pool_queries(const Dims& D, const void* Q, const RouteWS& ws, hipStream_t s) {
+hipError_t launch_pool_queries(const Dims& D, const void* Q, const RouteWS& ws, hipStream_t s,
+                               const float* Wq) {
     if (D.k == 0) return hipSuccess;
     // work-groups [0, Tq) of the pooling grid: the query blocks
     dim3 g1(D.Tq, (unsigned)D.BH);
@@ -756,13 +768,15 @@ hipError_t launch_pool_queries(const Dims& D, const void* Q, const RouteWS& ws, 
         pool_project_kernel<uint16_t><<<g1, 256, 0, s>>>(
             (const uint16_t*)Q, nullptr, nullptr, nullptr, ws.xq, ws.xk, D.N, D.d, D.bq,
             D.bkv, D.Tq, D.Tkv, D.H, D.w_heads, D.st);
+    if (Wq) launch_proj(D, Wq, nullptr, ws, 1, s);
     timing_after(s, K_POOL_PROJECT);
     return hipGetLastError();
 }
 
 hipError_t launch_scores(const Dims& D, const void* Q, const void* K, const float* Wq,
-                         const float* Wk, const RouteWS& ws, hipStream_t s, bool pooled) {
-    hipError_t e = launch_pool_project(D, Q, K, Wq, Wk, ws, s, pooled);
+                         const float* Wk, const RouteWS& ws, hipStream_t s, bool pooled,
+                         bool q_projected) {
+    hipError_t e = launch_pool_project(D, Q, K, Wq, Wk, ws, s, pooled, q_projected);
     if (e != hipSuccess) return e;
     timing_before(s, K_SCORE);
     launch_score_kernel(D, ws, s);
@@ -772,7 +786,7 @@ hipError_t launch_scores(const Dims& D, const void* Q, const void* K, const floa
 
 hipError_t launch_route(const Dims& D, const void* Q, const void* K, const float* Wq,
                         const float* Wk, int32_t* idx, uint8_t* mask, const RouteWS& ws,
-                        hipStream_t s, bool pooled) {
+                        hipStream_t s, bool pooled, bool q_projected) {
     if (D.k == 0) {  // nothing is selected: only the mask (if wanted) is written
         if (mask) {
             const size_t n = (size_t)D.BH * D.Tq * D.Tkv;
@@ -784,7 +798,7 @@ hipError_t launch_route(const Dims& D, const void* Q, const void* K, const float
         return hipGetLastError();
     }
     if (D.Tkv <= kStMaxTkv) {  // scores and selection in one pass
-        hipError_t e = launch_pool_project(D, Q, K, Wq, Wk, ws, s, pooled);
+        hipError_t e = launch_pool_project(D, Q, K, Wq, Wk, ws, s, pooled, q_projected);
         if (e != hipSuccess) return e;
         const dim3 g((D.Tq + kStRows - 1) / kStRows, (unsigned)D.BH);
         timing_before(s, K_SCORE_TOPK);
@@ -797,7 +811,7 @@ hipError_t launch_route(const Dims& D, const void* Q, const void* K, const float
         timing_after(s, K_SCORE_TOPK);
         return hipGetLastError();
     }
-    hipError_t e = launch_scores(D, Q, K, Wq, Wk, ws, s, pooled);
+    hipError_t e = launch_scores(D, Q, K, Wq, Wk, ws, s, pooled, q_projected);
     if (e != hipSuccess) return e;
 
     dim3 g3(D.Tq, (unsigned)D.BH);

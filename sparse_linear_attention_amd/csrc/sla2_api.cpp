@@ -464,12 +464,14 @@ SLA2_API sla2_status sla2_attention(const sla2_problem* p, const void* Q, const 
     if (hz_path(D)) {
         // K is read once: the block-summaries pass (helper stream) also
         // writes the router's pooled keys, while the caller's stream pools
-        // the queries; the projections, scores and top-k follow the join
+        // and projects the queries; the keys' projections, the scores and
+        // top-k follow the join
         e = launch_summaries_mfma(D, K, V, fw, sd->s, D.k > 0 ? rw.xk : nullptr);
         if (e == hipSuccess) e = hipEventRecord(sd->join, sd->s);
-        if (e == hipSuccess) e = launch_pool_queries(D, Q, rw, s);
+        if (e == hipSuccess) e = launch_pool_queries(D, Q, rw, s, Wq);
         if (e == hipSuccess) e = hipStreamWaitEvent(s, sd->join, 0);
-        if (e == hipSuccess) e = launch_route(D, Q, K, Wq, Wk, topk_idx, nullptr, rw, s, true);
+        if (e == hipSuccess)
+            e = launch_route(D, Q, K, Wq, Wk, topk_idx, nullptr, rw, s, true, true);
         const bool lin = D.k < D.Tkv && !D.skip_lin;
         if (e == hipSuccess && lin) e = launch_unsel(D, topk_idx, nullptr, 0, fw, s);
         if (e == hipSuccess && lin) e = launch_lin_gemm(D, fw, s);

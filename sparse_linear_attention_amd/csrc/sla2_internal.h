@@ -232,23 +232,27 @@ void timing_after(hipStream_t s, int kind);
 // launchers (each returns hipGetLastError() after its launches)
 // ---------------------------------------------------------------------------
 // pooled: ws.xq / ws.xk already hold the pooled means (launch_pool_quant),
-// so the pooling pass is skipped
+// so the pooling pass is skipped; q_projected: ws.qt holds the queries'
+// projections as well (launch_pool_queries with Wq), only the keys are
+// projected
 hipError_t launch_route(const Dims& D, const void* Q, const void* K, const float* Wq,
                         const float* Wk, int32_t* idx, uint8_t* mask, const RouteWS& ws,
-                        hipStream_t s, bool pooled = false);
+                        hipStream_t s, bool pooled = false, bool q_projected = false);
 
 // the pooling pass over the query blocks only (ws.xq), for a caller that
-// has the key blocks' means from the block-summaries pass
-hipError_t launch_pool_queries(const Dims& D, const void* Q, const RouteWS& ws, hipStream_t s);
+// has the key blocks' means from the block-summaries pass; with Wq also
+// their projections (ws.qt)
+hipError_t launch_pool_queries(const Dims& D, const void* Q, const RouteWS& ws, hipStream_t s,
+                               const float* Wq = nullptr);
 
 // router stages: pooled rows and their projections (ws.xq/xk, ws.qt/kt);
 // then the scores (ws.S)
 hipError_t launch_pool_project(const Dims& D, const void* Q, const void* K, const float* Wq,
                                const float* Wk, const RouteWS& ws, hipStream_t s,
-                               bool pooled = false);
+                               bool pooled = false, bool q_projected = false);
 hipError_t launch_scores(const Dims& D, const void* Q, const void* K, const float* Wq,
                          const float* Wk, const RouteWS& ws, hipStream_t s,
-                         bool pooled = false);
+                         bool pooled = false, bool q_projected = false);
 
 // training-time router: SoftTop-k, its gradient, the projections' gradient
 hipError_t launch_soft_topk(const Dims& D, const void* Q, const void* K, const float* Wq,
