@@ -773,6 +773,15 @@ hipError_t launch_pool_queries(const Dims& D, const void* Q, const RouteWS& ws, 
     return hipGetLastError();
 }
 
+hipError_t launch_project_queries(const Dims& D, const float* Wq, const RouteWS& ws,
+                                  hipStream_t s) {
+    if (D.k == 0) return hipSuccess;
+    timing_before(s, K_POOL_PROJECT);
+    launch_proj(D, Wq, nullptr, ws, 1, s);
+    timing_after(s, K_POOL_PROJECT);
+    return hipGetLastError();
+}
+
 hipError_t launch_scores(const Dims& D, const void* Q, const void* K, const float* Wq,
                          const float* Wk, const RouteWS& ws, hipStream_t s, bool pooled,
                          bool q_projected) {

@@ -582,8 +582,9 @@ SLA2_API sla2_status sla2_attention_fp8(const sla2_problem* p, const void* Q, co
     if ((e = side_stream(&sd)) != hipSuccess) return SLA2_EHIP;
     // K is read by the block-summaries pass (helper stream), which also
     // writes the router's pooled keys and each KV block's column sums; the
-    // caller's stream pools the queries and writes their codes, then (once
-    // the summaries are done) runs the projections, scores and top-k while
+    // caller's stream pools the queries, writes their codes and projects
+    // them, then (once the summaries are done) runs the keys' projections,
+    // the scores and top-k while
     // the helper stream takes the K mean from the block sums and writes the
     // key codes (and the V codes).  The same codes as sla2_quantize_fp8
     // (exact fp64 sums).
@@ -594,8 +595,10 @@ SLA2_API sla2_status sla2_attention_fp8(const sla2_problem* p, const void* Q, co
     if (e == hipSuccess) e = launch_quantize_k(D, K, V, fw, sd->s);
     if (e == hipSuccess) e = hipEventRecord(sd->join, sd->s);
     if (e == hipSuccess) e = launch_pool_quant(D, Q, K, rw, fw, s, true);
+    if (e == hipSuccess) e = launch_project_queries(D, Wq, rw, s);
     if (e == hipSuccess) e = hipStreamWaitEvent(s, sd->pooled, 0);
-    if (e == hipSuccess) e = launch_route(D, Q, K, Wq, Wk, topk_idx, nullptr, rw, s, true);
+    if (e == hipSuccess)
+        e = launch_route(D, Q, K, Wq, Wk, topk_idx, nullptr, rw, s, true, true);
     const bool lin = D.k < D.Tkv && !D.skip_lin;
     if (e == hipSuccess && lin) e = launch_unsel(D, topk_idx, nullptr, 0, fw, s);
     if (e == hipSuccess) e = hipStreamWaitEvent(s, sd->join, 0);

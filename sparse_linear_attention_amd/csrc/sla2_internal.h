@@ -244,6 +244,9 @@ hipError_t launch_route(const Dims& D, const void* Q, const void* K, const float
 // their projections (ws.qt)
 hipError_t launch_pool_queries(const Dims& D, const void* Q, const RouteWS& ws, hipStream_t s,
                                const float* Wq = nullptr);
+// the queries' projections alone (ws.xq -> ws.qt), e.g. after launch_pool_quant
+hipError_t launch_project_queries(const Dims& D, const float* Wq, const RouteWS& ws,
+                                  hipStream_t s);
 
 // router stages: pooled rows and their projections (ws.xq/xk, ws.qt/kt);
 // then the scores (ws.S)
