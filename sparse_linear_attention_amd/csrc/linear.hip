@@ -16,7 +16,10 @@
 // lin_gemm_kernel multiplies it with the per-block summaries written by the
 // block-summaries pass (bf16 rows of h_j^T, then z_j) on the bf16 matrix
 // cores (32x32x16, fp32 accumulation) into rows of H_i^T (rounded to bf16)
-// and Z_i (fp32) that the fused kernel's epilogue reads.
+// and Z_i (fp32) that the fused kernel's epilogue reads.  The backward uses
+// the same product in an fp32-output form (lin_gemm_kernel<true>) over the
+// selection's bits (unsel_kernel with sel set) or over the bits of its
+// transpose (csr_bits_kernel), summing bf16 d x d matrices per row.
 //
 // Product tiles: 320 query blocks x 128 columns per work-group of 4 waves
 // (2 x 2: each wave 5 x 2 tiles of 32 x 32, 160 rows x 64 columns), 64 KV
